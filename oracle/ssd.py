@@ -1,0 +1,243 @@
+"""Self-speculative decoding loop, accept rule and matchness scoring (oracle).
+
+Notation: committed tokens t[0..n-1]; the KV cache is valid for positions
+0..n-2 at every layer; y0 = t[n-1]; drafts y1..yd'.  b = reuse boundary (first
+layer with a skipped sub-layer).
+
+Readings of the pages (each also listed in the design notes):
+  * Exit at E runs layers 0..E-1 and verify continues at layer E (LayerSkip
+    blog §3.1 prose "run only the first E layers", §3.2 "layers E+1..L, L-E in
+    all"; its listing's range(E+1) is taken as an off-by-one).
+  * The KV cache accumulates across draft steps (LayerSkip blog §3.1 comment);
+    the listing's per-step reset is not taken.
+  * Verify reuses, for the draft rows, the hidden state entering layer b (the
+    listing reads "layer E's hidden state" out of a KV-cache entry; LayerSkip
+    blog §3.2).  The last draft token runs layers < b itself.
+  * At temperature 0 the draft is argmax and the accept rule reduces to
+    "accept while equal, then emit the target's argmax"; at T > 0 the draft
+    samples y ~ q so that min(1, p/q) with the norm(max(0, p - q)) correction
+    is distribution-preserving (LayerSkip blog §3.3 rule; §3 "lossless").
+  * Confidence = max_v q(v) of the draft distribution (SWIFT digest §4.2; the
+    SpecEE notes' AdaInfer "top prob" feature); the low-confidence token is
+    kept and drafting stops after it, so 1 <= d' <= d.
+  * The prefill's token counts toward the number generated.
+"""
+import numpy as np
+
+from . import model as mdl
+from . import philox
+from .numerics import argmax_lowest, softmax
+
+
+# --------------------------------------------------------------------------
+# Sampling primitives
+
+
+def race_sample(keys_f32):
+    """Exponential race / Gumbel-max: index of the largest key (lowest on ties).
+    keys_v = log(weight_v) + Gumbel_v samples v with probability weight_v / sum."""
+    return argmax_lowest(keys_f32)
+
+
+def sample_logits(z, T, seed, it, row, purpose):
+    """Sample from softmax(z / T) by the race over float32 keys z/T + Gumbel."""
+    g = philox.gumbel(seed, it, row, purpose, z.shape[-1])
+    keys = (np.asarray(z, np.float64) / T).astype(np.float32) + g
+    return race_sample(keys)
+
+
+def pick(z, T, seed, it, row, purpose):
+    """Greedy argmax at T == 0, otherwise a sample from softmax(z / T)."""
+    if T == 0:
+        return argmax_lowest(z)
+    return sample_logits(z, T, seed, it, row, purpose)
+
+
+def log_softmax(z, T):
+    zz = np.asarray(z, np.float64) / (T if T > 0 else 1.0)
+    m = np.max(zz)
+    return zz - (m + np.log(np.sum(np.exp(zz - m))))
+
+
+def confidence(z, T):
+    """max_v softmax(z / T)_v (softmax at T = 1 when decoding greedily)."""
+    return float(np.exp(np.max(log_softmax(z, T))))
+
+
+def accept_probability(p, q, y):
+    """min(1, p(y) / q(y)) (LayerSkip blog §3.3)."""
+    return min(1.0, p[y] / q[y])
+
+
+def residual_distribution(p, q):
+    """norm(max(0, p - q)); falls back to p when the positive part sums to 0
+    (only possible when p == q, where no rejection can occur)."""
+    r = np.maximum(0.0, p - q)
+    s = r.sum()
+    return p.copy() if s == 0 else r / s
+
+
+def accept_greedy(p_logits, drafts):
+    """T = 0: accept drafts while each equals the target argmax; then emit the
+    target's argmax at the first mismatch (or the bonus after d' matches)."""
+    k = 0
+    while k < len(drafts) and argmax_lowest(p_logits[k]) == drafts[k]:
+        k += 1
+    return [int(t) for t in drafts[:k]] + [argmax_lowest(p_logits[k])]
+
+
+def accept_sampled(p_logits, q_logits, drafts, T, seed, it):
+    """T > 0 accept/reject (LayerSkip blog §3.3): for i = 1..d', accept y_i when
+    u_i * q_i(y_i) < p_i(y_i) (probability min(1, p/q)); at the first rejection
+    emit a sample of norm(max(0, p_i - q_i)); if all are accepted, emit a bonus
+    sample of p_{d'+1}.  Decisions are taken on float32 quantities."""
+    dp = len(drafts)
+    for i in range(dp):
+        y = int(drafts[i])
+        lp = log_softmax(p_logits[i], T).astype(np.float32)
+        lq = log_softmax(q_logits[i], T).astype(np.float32)
+        u = philox.uniforms(seed, it, i, philox.PURPOSE_ACCEPT, 1)[0]
+        if np.log(u) + lq[y] < lp[y]:
+            continue
+        p32 = np.exp(lp)
+        q32 = np.exp(lq)
+        r = np.maximum(np.float32(0), p32 - q32)
+        g = philox.gumbel(seed, it, i, philox.PURPOSE_SAMPLE, r.shape[0])
+        if np.any(r > 0):
+            with np.errstate(divide="ignore"):
+                keys = np.log(r) + g
+        else:
+            keys = lp + g
+        return [int(t) for t in drafts[:i]] + [race_sample(keys)]
+    return [int(t) for t in drafts] + [sample_logits(p_logits[dp], T, seed, it, dp, philox.PURPOSE_SAMPLE)]
+
+
+# --------------------------------------------------------------------------
+# Prefill, draft, verify
+
+
+def prefill(model, kv, prompt):
+    """All prompt rows through the full model at positions 0..P-1; logits of the last row."""
+    z = mdl.forward(model, prompt, range(len(prompt)), kv)
+    return z[-1]
+
+
+def draft(model, kv, y0, n, mask, d, tau, T, seed, it):
+    """Draft phase (LayerSkip blog §3.1; SWIFT digest §3.1, §4.2).
+
+    Feeds y0 at position n-1, then each new draft token at the next position,
+    through the sub-layers the plan keeps, the shared final norm and LM head.
+    Stops after step j when confidence < tau (or at j = d).  Returns
+    (drafts, draft logits [d', V], hidden states entering layer b [d', D]).
+    """
+    b = mdl.first_skipped_layer(mask, model.L)
+    drafts, zs, hb = [], [], []
+    y = int(y0)
+    for j in range(1, d + 1):
+        pos = [n - 2 + j]
+        h = mdl.embed(model, [y])
+        h = mdl.run_layers(model, h, pos, kv, None, 0, b)
+        hb.append(h[0].copy())
+        h = mdl.run_layers(model, h, pos, kv, mask, b, model.L)
+        z = mdl.final_logits(model, h)[0]
+        y = pick(z, T, seed, it, j - 1, philox.PURPOSE_DRAFT)
+        drafts.append(y)
+        zs.append(z)
+        if np.float32(confidence(z, T)) < np.float32(tau):
+            break
+    return drafts, np.array(zs), np.array(hb)
+
+
+def verify(model, kv, y0, drafts, n, b, hb=None):
+    """Verify phase (LayerSkip blog §3.2): rows y0..yd' at positions n-1..n-1+d'.
+
+    With hb (the draft's hidden states entering layer b) only the last row runs
+    layers < b; otherwise every row does (no reuse).  Layers >= b run in full
+    for every row, overwriting the draft's keys/values there.  Returns the full
+    model's logits [d'+1, V]; row i scores the token at position n+i.
+    """
+    dp = len(drafts)
+    rows = [int(y0)] + [int(t) for t in drafts]
+    positions = list(range(n - 1, n + dp))
+    if hb is None:
+        h = mdl.embed(model, rows)
+        h = mdl.run_layers(model, h, positions, kv, None, 0, b)
+    else:
+        hl = mdl.embed(model, rows[-1:])
+        hl = mdl.run_layers(model, hl, positions[-1:], kv, None, 0, b)
+        h = np.concatenate([np.asarray(hb).reshape(dp, -1), hl], axis=0)
+    h = mdl.run_layers(model, h, positions, kv, None, b, model.L)
+    return mdl.final_logits(model, h)
+
+
+# --------------------------------------------------------------------------
+# Generation loops
+
+
+def ar_generate(model, prompt, n_gen, T=0.0, seed=3, capacity=None):
+    """Plain autoregressive decoding with the full model: the lossless reference."""
+    P = len(prompt)
+    kv = mdl.KVCache(model.shape, capacity or (P + n_gen + 1))
+    out = [pick(prefill(model, kv, prompt), T, seed, 0, 0, philox.PURPOSE_SAMPLE)]
+    it = 1
+    while len(out) < n_gen:
+        n = P + len(out)
+        z = mdl.forward(model, [out[-1]], [n - 1], kv)[0]
+        out.append(pick(z, T, seed, it, 0, philox.PURPOSE_SAMPLE))
+        it += 1
+    return out, kv
+
+
+def ssd_generate(model, prompt, n_gen, mask, d, tau=0.0, T=0.0, seed=3, reuse=True, capacity=None,
+                 on_iteration=None):
+    """Self-speculative decoding loop (LayerSkip blog §3.3): draft, verify, accept,
+    append the emitted tokens; output truncated to exactly n_gen tokens."""
+    P = len(prompt)
+    L = model.L
+    b = mdl.first_skipped_layer(mask, L)
+    kv = mdl.KVCache(model.shape, capacity or (P + n_gen + d + 2))
+    out = [pick(prefill(model, kv, prompt), T, seed, 0, 0, philox.PURPOSE_SAMPLE)]
+    stats = {"drafted": [], "accepted": [], "emitted": []}
+    it = 1
+    while len(out) < n_gen:
+        n = P + len(out)
+        y0 = out[-1]
+        drafts, zq, hb = draft(model, kv, y0, n, mask, d, tau, T, seed, it)
+        zp = verify(model, kv, y0, drafts, n, b, hb if reuse else None)
+        if T == 0:
+            emitted = accept_greedy(zp, drafts)
+        else:
+            emitted = accept_sampled(zp, zq, drafts, T, seed, it)
+        stats["drafted"].append(len(drafts))
+        stats["accepted"].append(len(emitted) - 1)
+        stats["emitted"].append(len(emitted))
+        if on_iteration is not None:
+            on_iteration(it, n, drafts, zq, zp, emitted, kv)
+        out.extend(emitted)
+        it += 1
+    return out[:n_gen], stats, kv
+
+
+def score_masks(model, kv, window, pos0, masks):
+    """SWIFT matchness scoring (SWIFT digest §4.1, §4.1.2, §5.3).
+
+    window = gamma+1 committed tokens at positions pos0..pos0+gamma; the cache
+    holds the full model's keys/values for positions < pos0.  Each candidate
+    plan runs ONE causal draft forward over rows window[0..gamma-1] (its own
+    keys/values at the window positions, the full model's before them) and
+    predicts every next token by argmax; its score is the fraction of rows whose
+    prediction equals window[i+1].  Returns (scores, index of the best plan,
+    lowest index on ties).
+    """
+    gamma = len(window) - 1
+    rows = [int(t) for t in window[:-1]]
+    targets = np.asarray(window[1:], dtype=np.int64)
+    positions = list(range(pos0, pos0 + gamma))
+    scores = []
+    for mask in masks:
+        kvm = kv.copy()
+        z = mdl.forward(model, rows, positions, kvm, mask)
+        pred = np.array([argmax_lowest(r) for r in z])
+        scores.append(float(np.sum(pred == targets)) / gamma)
+    scores = np.array(scores)
+    return scores, int(np.argmax(scores))
