@@ -1,0 +1,257 @@
+/*
+ * ssd.h — C ABI of the MI355X self-speculative decoding library (libssd.so).
+ *
+ * One self-speculative decoding (SSD) step of a Llama-style decoder at batch 1:
+ *   draft  — up to d tokens through the sub-layers a skip plan keeps (a SWIFT
+ *            skip mask or a LayerSkip exit layer E), stopping early when the
+ *            draft's confidence falls below a threshold;
+ *   verify — one full-depth pass over the d'+1 draft positions that reuses the
+ *            draft's state below the first skipped layer, then the shared LM head;
+ *   accept — min(1, p/q) accept/reject with resampling from norm(max(0, p - q))
+ *            and a bonus token when every draft is accepted;
+ * plus SWIFT's matchness scoring of candidate skip plans against committed context.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [SWIFT]     "SWIFT: On-the-Fly Self-Speculative Decoding for LLM Inference
+ *               Acceleration" (paper digest, arXiv 2410.06916v2)
+ *   [LayerSkip] "ACL'24 | LayerSkip: Meta 把 Self-Speculative Decoding 从头训到尾"
+ *               (blog post)
+ *   [SpecEE]    "SpecEE: Accelerating Large Language Model Inference with
+ *               Speculative Early Exiting" (study notes)
+ *
+ * Conventions
+ *   - Every pointer named *_dev is device memory of the GPU current when the
+ *     object was created; the caller allocates and owns it (the library never
+ *     allocates device memory).  *_host pointers are host memory, read during
+ *     the call only.
+ *   - Weights are row-major [out_features, in_features] ("[N, K]"), in the
+ *     model dtype (SSD_DTYPE_F32: float, SSD_DTYPE_BF16: bfloat16 bits).  Norm
+ *     gains are float32.
+ *   - Calls taking a hipStream_t enqueue work on that stream and return without
+ *     waiting, except where stated.  One sequence must not be used from two
+ *     streams at once; calls on one sequence are ordered by its stream.
+ *   - Return value: SSD_OK (0) or a negative ssd_status.  ssd_last_error()
+ *     gives a message for the calling thread's last failure.  Nothing aborts
+ *     and nothing throws across this boundary.  Conditions found on the device
+ *     (KV capacity exceeded, non-finite logits) set a sticky flag in the
+ *     sequence, reported by ssd_read_state() / ssd_sync().
+ *
+ * Sequence state kept on the device (so that a whole iteration can be enqueued
+ * without a host round trip, and captured in a HIP graph):
+ *   kvlen      number of positions whose keys/values are committed (= n - 1 for
+ *              n committed tokens: the newest token is not yet in the cache);
+ *   last_token the newest committed token (the next draft's input y0);
+ *   iteration  SSD iteration counter (0 = the prefill's token), used to address
+ *              the random draws;
+ *   n_out      total tokens committed to the output log (the prefill's token
+ *              counts).
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum ssd_status {
+  SSD_OK = 0,
+  SSD_ERR_ARG = -1,          /* null pointer, negative size, value out of range */
+  SSD_ERR_SHAPE = -2,        /* shape unsupported by the kernels (see ssd_model_create) */
+  SSD_ERR_CAPACITY = -3,     /* KV pages, workspace or row limits exceeded */
+  SSD_ERR_HIP = -4,          /* a HIP runtime call failed */
+  SSD_ERR_UNSUPPORTED = -5,  /* option not implemented for this dtype/shape */
+  SSD_ERR_NUMERIC = -6       /* non-finite logits were seen on the device */
+} ssd_status;
+
+typedef enum ssd_dtype { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
+
+typedef struct ssd_model ssd_model;
+typedef struct ssd_seq ssd_seq;
+
+/* Weights of one decoder layer. */
+typedef struct ssd_layer_weights {
+  const float* attn_norm;   /* [D] float32 RMSNorm gain before attention */
+  const void* w_qkv;        /* [(H + 2*KVH) * hd, D]: rows 0..H*hd-1 = Wq,
+                               then KVH*hd rows of Wk, then KVH*hd rows of Wv */
+  const void* w_o;          /* [D, H * hd] */
+  const float* mlp_norm;    /* [D] float32 RMSNorm gain before the MLP */
+  const void* w_gate_up;    /* [2F, D]: rows 0..F-1 = Wgate, rows F..2F-1 = Wup */
+  const void* w_down;       /* [D, F] */
+} ssd_layer_weights;
+
+/* Llama-2 style decoder ([SWIFT] §5.1 LLaMA-2 backbones; [LayerSkip] §2 one LM
+ * head shared by every exit): h = Emb[t]; per layer h += Wo·Attn(RoPE(Wq x),
+ * RoPE(Wk x), Wv x) with x = RMSNorm(h), then h += Wdown·(silu(Wgate x) * Wup x)
+ * with x = RMSNorm(h); logits = LMhead·RMSNorm_final(h).  No biases, RoPE with
+ * rotate-half pairing (i, i + hd/2), grouped-query attention (query head j uses
+ * KV head j / (H / KVH)), attention scale hd^-1/2.
+ * Supported: head_dim 64 or 128; D, F multiples of 64; H % KVH == 0. */
+typedef struct ssd_model_desc {
+  int n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  float rms_eps;            /* e.g. 1e-5 */
+  float rope_theta;         /* e.g. 10000 */
+  int dtype;                /* ssd_dtype: storage of weights, activations and the KV cache */
+  const void* embed;        /* [V, D] */
+  const float* final_norm;  /* [D] float32 */
+  const void* lm_head;      /* [V, D] */
+  const ssd_layer_weights* layers;  /* host array of n_layers entries (copied) */
+} ssd_model_desc;
+
+/* Per-row softmax statistics of a logits row z (row a3 of the path;
+ * [LayerSkip] §3.1 softmax/argmax of the draft; [SpecEE] AdaInfer §1 "top
+ * prob" and the top-2 gap). */
+typedef struct ssd_row_stat {
+  float max;        /* max_v z_v */
+  int32_t argmax;   /* lowest index attaining max */
+  float max2;       /* second largest value (z at another index); -inf if V == 1 */
+  float lse;        /* log sum_v exp(z_v / T) (T = 1 when temperature is 0) */
+  float conf;       /* max_v softmax(z / T)_v */
+  int32_t sample;   /* argmax at T = 0, else a draw from softmax(z / T) */
+} ssd_row_stat;
+
+/* Host-visible copy of the sequence's device state (ssd_read_state). */
+typedef struct ssd_state {
+  int32_t kvlen, last_token, iteration, n_out, error_flags;
+  int32_t last_n_drafted, last_n_emitted;
+} ssd_state;
+
+/* ---- model ---------------------------------------------------------------- */
+
+/* Validates the shape and records the weight pointers (which must stay valid
+ * until ssd_model_destroy).  Builds nothing on the device. */
+int ssd_model_create(const ssd_model_desc* desc, ssd_model** out_model);
+int ssd_model_destroy(ssd_model* model);
+
+/* Bytes of the KV pool for n_pages pages of page_size positions.
+ * Pool layout: [n_pages][L][2 (K, V)][KVH][page_size][hd] in the model dtype. */
+int ssd_kv_pool_bytes(const ssd_model* model, int n_pages, int page_size, size_t* bytes);
+
+/* Bytes of the per-sequence device workspace.
+ *   max_rows   largest row block processed at once: prefill chunk, d + 1 for
+ *              verify, n_masks * gamma for scoring (<= 1024);
+ *   max_draft  largest d passed to ssd_draft (<= 32);
+ *   max_ctx    page_size * n_logical_pages of the sequence. */
+int ssd_workspace_bytes(const ssd_model* model, int max_rows, int max_draft, int max_ctx,
+                        size_t* bytes);
+
+/* ---- sequence --------------------------------------------------------------- */
+
+/* Creates a sequence over a caller-owned KV pool and workspace.
+ *   page_table_host[n_logical_pages]: logical page i (positions
+ *   i*page_size .. (i+1)*page_size-1) lives in physical pool page
+ *   page_table_host[i] (each < n_pages).  Copied to the workspace (synchronous).
+ *   page_size: 16, 32 or 64.  The sequence starts empty (kvlen 0). */
+int ssd_seq_create(const ssd_model* model, void* kv_pool_dev, int n_pages, int page_size,
+                   const int32_t* page_table_host, int n_logical_pages, void* workspace_dev,
+                   size_t workspace_bytes, int max_rows, int max_draft, hipStream_t stream,
+                   ssd_seq** out_seq);
+int ssd_seq_destroy(ssd_seq* seq);
+
+/* Prefill (row a7): the n prompt tokens tokens_dev[0..n-1] at positions 0..n-1
+ * through the full model (in chunks of max_rows rows); then the first
+ * generated token is picked from the last row's logits (argmax at temperature
+ * 0, else a draw with iteration 0) and committed.  After it: kvlen = n,
+ * n_out = 1.  last_logits_dev[V] (nullable) receives the last row's logits. */
+int ssd_prefill(ssd_seq* seq, const int32_t* tokens_dev, int n, float temperature, uint64_t seed,
+                float* last_logits_dev, hipStream_t stream);
+
+/* One plain autoregressive step with the full model (row a7; the lossless
+ * reference of [SWIFT] §2): feeds last_token at position kvlen, picks the next
+ * token (argmax, or a draw addressed by the current iteration) and commits it.
+ * logits_dev[V] (nullable) receives the logits. */
+int ssd_decode_ar(ssd_seq* seq, float temperature, uint64_t seed, float* logits_dev,
+                  hipStream_t stream);
+
+/* Draft phase (row a1; [LayerSkip] §3.1, [SWIFT] §3.1 and §4.2).
+ * Plan: skip_mask_host[2L] (entry 2l = skip the attention sub-layer of layer
+ * l, entry 2l+1 = skip its MLP sub-layer; [SWIFT] Appendix A Fig. 10), or, when
+ * skip_mask_host is NULL, exit_layer E in 0..L: run layers 0..E-1 only.
+ * Step j = 1..d feeds y_{j-1} (y_0 = last_token) at position kvlen + j - 1
+ * through the kept sub-layers (writing their K/V at that position), the shared
+ * final norm and LM head; y_j = argmax (temperature 0) or a draw from
+ * softmax(z / T) (purpose "draft"); conf_j = max softmax.  Drafting stops after
+ * step j when conf_j < conf_thresh or j = d; d' = j.
+ * Outputs: draft_tokens_dev[d] (first d' valid), draft_logits_dev[d * V]
+ * (rows 0..d'-1 valid: the q logits), n_drafted_dev[1] = d'.
+ * Also saves, for each step, the residual entering the reuse boundary b (the
+ * first layer with a skipped sub-layer) for ssd_verify. */
+int ssd_draft(ssd_seq* seq, const uint8_t* skip_mask_host, int exit_layer, int d, float conf_thresh,
+              float temperature, uint64_t seed, int32_t* draft_tokens_dev, float* draft_logits_dev,
+              int32_t* n_drafted_dev, hipStream_t stream);
+
+/* Verify pass (row a2; [LayerSkip] §3.2).  Rows i = 0..d' carry y_0..y_d' at
+ * positions kvlen + i.  With reuse != 0 only row d' runs the layers below the
+ * plan's boundary b; rows < d' take the residual the draft saved there (the
+ * draft's keys/values below b are the full model's).  With reuse == 0 every
+ * row runs every layer.  Layers >= b run in full for all rows, overwriting the
+ * draft's keys/values; attention is causal inside the block.
+ * The plan must be the one of the preceding ssd_draft; d is its d.
+ * Output: logits_dev[(d + 1) * V]; rows 0..d' valid; row i is the full model's
+ * logits for position kvlen + i + 1. */
+int ssd_verify(ssd_seq* seq, const uint8_t* skip_mask_host, int exit_layer, int d,
+               const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, int reuse,
+               float* logits_dev, hipStream_t stream);
+
+/* Accept / reject (row a4; [LayerSkip] §3.3).
+ * Temperature 0: k = number of leading drafts equal to the argmax of the
+ * corresponding verify row; emits y_1..y_k then argmax of verify row k.
+ * Temperature T > 0: p_i = softmax(p_logits row i-1 / T), q_i = softmax(q row
+ * i-1 / T); y_i is accepted when u_i * q_i(y_i) < p_i(y_i) (u_i uniform,
+ * purpose "accept"), taken as log u + log q < log p in float32; at the first
+ * rejection a draw from norm(max(0, p_i - q_i)) (purpose "sample", row i-1) is
+ * emitted; when all d' are accepted a bonus draw from p_{d'+1} (row d').
+ * Outputs: out_tokens_dev[d + 1] (first n_out valid), n_out_dev[1] = k + 1.
+ * Does not change the sequence (see ssd_commit). */
+int ssd_accept(ssd_seq* seq, const float* p_logits_dev, const float* q_logits_dev,
+               const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, int d, float temperature,
+               uint64_t seed, int32_t* out_tokens_dev, int32_t* n_out_dev, hipStream_t stream);
+
+/* Commit (row a5): appends out_tokens_dev[0..n_out-1] to the output log,
+ * kvlen += n_out, last_token = the last emitted token, iteration += 1.  Keys and
+ * values at positions >= the new kvlen are dead (rejected drafts) and are
+ * overwritten by later steps: roll-back is this metadata update only. */
+int ssd_commit(ssd_seq* seq, const int32_t* out_tokens_dev, const int32_t* n_out_dev,
+               hipStream_t stream);
+
+/* SWIFT matchness scoring (row a6; [SWIFT] §4.1, §4.1.2, §5.3, §D.2).
+ * window_dev[gamma + 1] are committed tokens at positions pos0..pos0+gamma, and
+ * the cache must hold the full model's keys/values for positions < pos0
+ * (pos0 <= kvlen).  For each candidate plan c (masks_host[c * 2L .. +2L]) one
+ * causal draft forward runs rows window[0..gamma-1] at positions pos0.. with
+ * the candidate's own keys/values at the window positions (kept in the
+ * workspace; the cache is not modified); row i predicts argmax of its logits.
+ * scores_dev[c] = #(prediction i == window[i+1]) / gamma; best_dev[0] = the
+ * highest-scoring candidate (lowest index on ties).
+ * Requires n_masks * gamma <= max_rows. */
+int ssd_score_masks(ssd_seq* seq, const uint8_t* masks_host, int n_masks, const int32_t* window_dev,
+                    int pos0, int gamma, float* scores_dev, int32_t* best_dev, hipStream_t stream);
+
+/* Row statistics (row a3) of rows logits rows of length V, as used inside
+ * draft/verify/accept; exposed for tests.  Draws use (seed, iteration, row
+ * index, purpose "draft"). */
+int ssd_row_stats(const float* logits_dev, int rows, int V, float temperature, uint64_t seed,
+                  int32_t iteration, ssd_row_stat* stats_dev, hipStream_t stream);
+
+/* ---- host synchronisation ------------------------------------------------------ */
+
+/* Waits for the stream, then copies the device state.  Returns
+ * SSD_ERR_CAPACITY / SSD_ERR_NUMERIC if the device flagged such a condition. */
+int ssd_read_state(ssd_seq* seq, ssd_state* out, hipStream_t stream);
+
+/* Waits for the stream, then copies min(n_out, max_tokens) committed tokens
+ * of the output log to tokens_host; *n_tokens = that count. */
+int ssd_read_output(ssd_seq* seq, int32_t* tokens_host, int max_tokens, int* n_tokens,
+                    hipStream_t stream);
+
+/* Thread-local message describing this thread's last failure ("" if none). */
+const char* ssd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_H */

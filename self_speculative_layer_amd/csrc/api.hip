@@ -1,0 +1,528 @@
+// C ABI of the self-speculative decoding library: model and sequence handles,
+// workspace carving, and the launch sequences of draft / verify / accept /
+// commit / prefill / AR decode / matchness scoring.  All per-iteration values
+// (positions, tokens, draft length) are read by the kernels from the
+// sequence's device state, so a whole iteration is enqueued without any
+// device-to-host traffic.
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace ssd;
+
+// ---------------------------------------------------------------------------
+// errors
+
+static thread_local std::string g_err;
+
+static int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define CHECK_ARG(cond, msg) \
+  do {                       \
+    if (!(cond)) return fail(SSD_ERR_ARG, msg); \
+  } while (0)
+
+#define TRY(expr)                                                              \
+  do {                                                                         \
+    int _rc = (expr);                                                          \
+    if (_rc != 0) return fail(_rc, std::string("launch failed: ") + #expr);    \
+  } while (0)
+
+extern "C" const char* ssd_last_error(void) { return g_err.c_str(); }
+
+// ---------------------------------------------------------------------------
+// handles
+
+struct ssd_model {
+  ssd_model_desc d;
+  std::vector<ssd_layer_weights> layers;
+  int q_dim, kv_dim, qkv_dim;
+  size_t elt;
+};
+
+struct Workspace {
+  DevState* st;
+  int* page_table;
+  double* inv_freq;
+  int *pos, *tok, *pos1, *tok1, *vpos, *vtok;
+  float *h, *h1, *qkv, *part, *hb, *logits1, *logits_rows;
+  void *x, *x2, *qb, *local_kv;
+  ssd_row_stat* stats;
+  int *dec, *corr, *rowmaps;
+  int32_t* log;
+};
+
+struct ssd_seq {
+  const ssd_model* m;
+  KvView kv;
+  int max_rows, max_draft, max_ctx, log_cap;
+  Workspace w;
+};
+
+namespace {
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Carves the workspace; with base == nullptr only computes the size.
+size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char* base, Workspace* w) {
+  const ssd_model_desc& d = m->d;
+  const int R = max_rows, D = d.d_model, F = d.ffn_dim, V = d.vocab, L = d.n_layers;
+  const int xw = std::max(D, m->q_dim);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  Workspace t{};
+  t.st = (DevState*)take(sizeof(DevState));
+  t.page_table = (int*)take(sizeof(int) * (size_t)((max_ctx + 15) / 16 + 1));
+  t.inv_freq = (double*)take(sizeof(double) * d.head_dim / 2);
+  t.pos = (int*)take(sizeof(int) * R);
+  t.tok = (int*)take(sizeof(int) * R);
+  t.pos1 = (int*)take(sizeof(int) * 4);
+  t.tok1 = (int*)take(sizeof(int) * 4);
+  t.vpos = (int*)take(sizeof(int) * (max_draft + 1));
+  t.vtok = (int*)take(sizeof(int) * (max_draft + 1));
+  t.h = (float*)take(sizeof(float) * (size_t)R * D);
+  t.h1 = (float*)take(sizeof(float) * D);
+  t.qkv = (float*)take(sizeof(float) * (size_t)R * m->qkv_dim);
+  t.part = (float*)take(sizeof(float) * attention_partial_floats(R, d.n_heads, d.head_dim, max_ctx));
+  t.hb = (float*)take(sizeof(float) * (size_t)max_draft * D);
+  t.logits1 = (float*)take(sizeof(float) * V);
+  t.logits_rows = (float*)take(sizeof(float) * (size_t)R * V);
+  t.x = take(m->elt * (size_t)R * xw);
+  t.x2 = take(m->elt * (size_t)R * F);
+  t.qb = take(m->elt * (size_t)R * m->q_dim);
+  t.local_kv = take(m->elt * (size_t)R * 2 * m->kv_dim);
+  t.stats = (ssd_row_stat*)take(sizeof(ssd_row_stat) * R);
+  t.dec = (int*)take(sizeof(int) * (max_draft + 1));
+  t.corr = (int*)take(sizeof(int) * (max_draft + 1));
+  t.rowmaps = (int*)take(sizeof(int) * (size_t)2 * L * R);
+  t.log = (int32_t*)take(sizeof(int32_t) * (size_t)max_ctx);
+  if (w) *w = t;
+  return off;
+}
+
+// A block of rows whose residuals live in h (row i of the block at residual
+// row hmap[i], or i).
+struct Block {
+  float* h;
+  RowBlock rb;            // rb.ymap doubles as hmap for the residual stream
+  void* local_kv;         // scoring: the candidates' own keys/values
+  int local_start;
+  int group_rows;
+};
+
+int attn_sublayer(ssd_seq* q, int l, const Block& b, hipStream_t s) {
+  const ssd_model* m = q->m;
+  const ssd_model_desc& d = m->d;
+  const ssd_layer_weights& lw = m->layers[l];
+  const Workspace& w = q->w;
+  const RowBlock& rb = b.rb;
+  const int D = d.d_model;
+  TRY(launch_rmsnorm(d.dtype, b.h, D, lw.attn_norm, w.x, D, rb.M, D, d.rms_eps, rb.nrows, rb.ymap, rb.stop, s));
+  TRY(launch_linear(d.dtype, EPI_STORE, lw.w_qkv, w.x, D, rb.M, m->qkv_dim, D, w.qkv, m->qkv_dim, nullptr, 0,
+                    rb.nrows, nullptr, rb.stop, s));
+  TRY(launch_rope_kv(d.dtype, d.head_dim, w.qkv, m->qkv_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads,
+                     d.n_kv_heads, rb, w.inv_freq, b.local_kv, &w.st->error_flags, s));
+  TRY(launch_attention(d.dtype, d.head_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads, d.n_kv_heads, rb,
+                       q->max_ctx, b.local_kv, b.local_start, b.group_rows, w.part, w.x, m->q_dim, s));
+  TRY(launch_linear(d.dtype, EPI_RESID, lw.w_o, w.x, m->q_dim, rb.M, D, m->q_dim, b.h, D, nullptr, 0, rb.nrows,
+                    rb.ymap, rb.stop, s));
+  return 0;
+}
+
+int mlp_sublayer(ssd_seq* q, int l, const Block& b, hipStream_t s) {
+  const ssd_model* m = q->m;
+  const ssd_model_desc& d = m->d;
+  const ssd_layer_weights& lw = m->layers[l];
+  const Workspace& w = q->w;
+  const RowBlock& rb = b.rb;
+  const int D = d.d_model, F = d.ffn_dim;
+  TRY(launch_rmsnorm(d.dtype, b.h, D, lw.mlp_norm, w.x, D, rb.M, D, d.rms_eps, rb.nrows, rb.ymap, rb.stop, s));
+  TRY(launch_linear(d.dtype, EPI_SWIGLU, lw.w_gate_up, w.x, D, rb.M, F, D, nullptr, 0, w.x2, F, rb.nrows, nullptr,
+                    rb.stop, s));
+  TRY(launch_linear(d.dtype, EPI_RESID, lw.w_down, w.x2, F, rb.M, D, F, b.h, D, nullptr, 0, rb.nrows, rb.ymap,
+                    rb.stop, s));
+  return 0;
+}
+
+bool skip_attn(const uint8_t* mask, int l) { return mask && mask[2 * l]; }
+bool skip_mlp(const uint8_t* mask, int l) { return mask && mask[2 * l + 1]; }
+
+int run_layers(ssd_seq* q, const Block& b, int l0, int l1, const uint8_t* mask, hipStream_t s) {
+  for (int l = l0; l < l1; ++l) {
+    if (!skip_attn(mask, l)) TRY(attn_sublayer(q, l, b, s));
+    if (!skip_mlp(mask, l)) TRY(mlp_sublayer(q, l, b, s));
+  }
+  return 0;
+}
+
+// Final RMSNorm + LM head of M rows of h into logits [M, V].
+int final_logits(ssd_seq* q, const float* h, int M, const int* nrows, float* logits, const int* stop,
+                 hipStream_t s) {
+  const ssd_model* m = q->m;
+  const ssd_model_desc& d = m->d;
+  TRY(launch_rmsnorm(d.dtype, h, d.d_model, d.final_norm, q->w.x, d.d_model, M, d.d_model, d.rms_eps, nrows,
+                     nullptr, stop, s));
+  TRY(launch_linear(d.dtype, EPI_STORE, d.lm_head, q->w.x, d.d_model, M, d.vocab, d.d_model, logits, d.vocab,
+                    nullptr, 0, nrows, nullptr, stop, s));
+  return 0;
+}
+
+// The plan as a mask of 2L entries (exit_layer -> suffix mask).  Returns the
+// reuse boundary b, or -1 on a bad plan.
+int plan_mask(const ssd_model* m, const uint8_t* mask_in, int exit_layer, std::vector<uint8_t>& mask) {
+  const int L = m->d.n_layers;
+  mask.assign(2 * L, 0);
+  if (mask_in) {
+    for (int i = 0; i < 2 * L; ++i) mask[i] = mask_in[i] ? 1 : 0;
+  } else {
+    if (exit_layer < 0 || exit_layer > L) return -1;
+    for (int l = exit_layer; l < L; ++l) mask[2 * l] = mask[2 * l + 1] = 1;
+  }
+  for (int l = 0; l < L; ++l)
+    if (mask[2 * l] || mask[2 * l + 1]) return l;
+  return L;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// model
+
+extern "C" int ssd_model_create(const ssd_model_desc* desc, ssd_model** out_model) {
+  CHECK_ARG(desc && out_model, "null argument");
+  const ssd_model_desc& d = *desc;
+  CHECK_ARG(d.n_layers > 0 && d.d_model > 0 && d.n_heads > 0 && d.n_kv_heads > 0 && d.vocab > 0 && d.ffn_dim > 0,
+            "non-positive model dimension");
+  if (d.head_dim != 64 && d.head_dim != 128) return fail(SSD_ERR_SHAPE, "head_dim must be 64 or 128");
+  if (d.n_heads % d.n_kv_heads != 0) return fail(SSD_ERR_SHAPE, "n_heads must be a multiple of n_kv_heads");
+  if (64 / (d.n_heads / d.n_kv_heads) < 1) return fail(SSD_ERR_SHAPE, "more than 64 query heads per KV head");
+  if (d.dtype != SSD_DTYPE_F32 && d.dtype != SSD_DTYPE_BF16) return fail(SSD_ERR_ARG, "bad dtype");
+  if (d.dtype == SSD_DTYPE_BF16 &&
+      (d.d_model % 64 != 0 || d.ffn_dim % 64 != 0 || (d.n_heads * d.head_dim) % 64 != 0))
+    return fail(SSD_ERR_SHAPE, "bf16 models need d_model, ffn_dim and n_heads*head_dim multiples of 64");
+  CHECK_ARG(d.embed && d.final_norm && d.lm_head && d.layers, "null weight pointer");
+  for (int l = 0; l < d.n_layers; ++l) {
+    const ssd_layer_weights& lw = d.layers[l];
+    CHECK_ARG(lw.attn_norm && lw.w_qkv && lw.w_o && lw.mlp_norm && lw.w_gate_up && lw.w_down,
+              "null layer weight pointer");
+  }
+  ssd_model* m = new (std::nothrow) ssd_model;
+  if (!m) return fail(SSD_ERR_CAPACITY, "out of host memory");
+  m->d = d;
+  m->layers.assign(d.layers, d.layers + d.n_layers);
+  m->d.layers = m->layers.data();
+  m->q_dim = d.n_heads * d.head_dim;
+  m->kv_dim = d.n_kv_heads * d.head_dim;
+  m->qkv_dim = m->q_dim + 2 * m->kv_dim;
+  m->elt = d.dtype == SSD_DTYPE_BF16 ? 2 : 4;
+  *out_model = m;
+  return SSD_OK;
+}
+
+extern "C" int ssd_model_destroy(ssd_model* model) {
+  delete model;
+  return SSD_OK;
+}
+
+extern "C" int ssd_kv_pool_bytes(const ssd_model* m, int n_pages, int page_size, size_t* bytes) {
+  CHECK_ARG(m && bytes && n_pages > 0 && page_size > 0, "bad argument");
+  *bytes = (size_t)n_pages * m->d.n_layers * 2 * m->kv_dim * page_size * m->elt;
+  return SSD_OK;
+}
+
+extern "C" int ssd_workspace_bytes(const ssd_model* m, int max_rows, int max_draft, int max_ctx, size_t* bytes) {
+  CHECK_ARG(m && bytes, "null argument");
+  CHECK_ARG(max_rows >= 1 && max_rows <= 1024, "max_rows must be in 1..1024");
+  CHECK_ARG(max_draft >= 1 && max_draft <= 32, "max_draft must be in 1..32");
+  CHECK_ARG(max_ctx >= 1, "max_ctx must be positive");
+  *bytes = carve(m, std::max(max_rows, max_draft + 1), max_draft, max_ctx, nullptr, nullptr);
+  return SSD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// sequence
+
+extern "C" int ssd_seq_create(const ssd_model* m, void* kv_pool_dev, int n_pages, int page_size,
+                              const int32_t* page_table_host, int n_logical_pages, void* workspace_dev,
+                              size_t workspace_bytes, int max_rows, int max_draft, hipStream_t stream,
+                              ssd_seq** out_seq) {
+  CHECK_ARG(m && kv_pool_dev && page_table_host && workspace_dev && out_seq, "null argument");
+  CHECK_ARG(page_size == 16 || page_size == 32 || page_size == 64, "page_size must be 16, 32 or 64");
+  CHECK_ARG(n_pages > 0 && n_logical_pages > 0, "no pages");
+  CHECK_ARG(max_rows >= 1 && max_rows <= 1024 && max_draft >= 1 && max_draft <= 32, "bad row limits");
+  for (int i = 0; i < n_logical_pages; ++i)
+    CHECK_ARG(page_table_host[i] >= 0 && page_table_host[i] < n_pages, "page table entry out of range");
+  const int R = std::max(max_rows, max_draft + 1);
+  const int max_ctx = n_logical_pages * page_size;
+  const size_t need = carve(m, R, max_draft, max_ctx, nullptr, nullptr);
+  if (workspace_bytes < need) return fail(SSD_ERR_CAPACITY, "workspace too small");
+  ssd_seq* q = new (std::nothrow) ssd_seq;
+  if (!q) return fail(SSD_ERR_CAPACITY, "out of host memory");
+  q->m = m;
+  q->max_rows = R;
+  q->max_draft = max_draft;
+  q->max_ctx = max_ctx;
+  q->log_cap = max_ctx;
+  carve(m, R, max_draft, max_ctx, (char*)workspace_dev, &q->w);
+  q->kv.pool = kv_pool_dev;
+  q->kv.page_table = q->w.page_table;
+  q->kv.n_lpages = n_logical_pages;
+  q->kv.page_size = page_size;
+  // RoPE inverse frequencies theta^(-2i/hd), computed in fp64
+  std::vector<double> inv(m->d.head_dim / 2);
+  for (int i = 0; i < m->d.head_dim / 2; ++i)
+    inv[i] = std::pow((double)m->d.rope_theta, -2.0 * i / (double)m->d.head_dim);
+  hipError_t e = hipMemcpy(q->w.page_table, page_table_host, sizeof(int32_t) * n_logical_pages,
+                           hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(q->w.inv_freq, inv.data(), sizeof(double) * inv.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    delete q;
+    return fail(SSD_ERR_HIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
+  }
+  int rc = launch_state_init(q->w.st, stream);
+  if (rc == 0 && hipStreamSynchronize(stream) != hipSuccess) rc = SSD_ERR_HIP;
+  if (rc != 0) {
+    delete q;
+    return fail(SSD_ERR_HIP, "state init failed");
+  }
+  *out_seq = q;
+  return SSD_OK;
+}
+
+extern "C" int ssd_seq_destroy(ssd_seq* seq) {
+  delete seq;
+  return SSD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// prefill and AR decode
+
+extern "C" int ssd_prefill(ssd_seq* q, const int32_t* tokens_dev, int n, float temperature, uint64_t seed,
+                           float* last_logits_dev, hipStream_t s) {
+  CHECK_ARG(q && tokens_dev, "null argument");
+  CHECK_ARG(n >= 1, "empty prompt");
+  CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
+  if (n >= q->max_ctx) return fail(SSD_ERR_CAPACITY, "prompt does not fit the KV pages");
+  const ssd_model_desc& d = q->m->d;
+  const Workspace& w = q->w;
+  TRY(launch_state_init(w.st, s));
+  int last_rows = 0;
+  for (int c0 = 0; c0 < n; c0 += q->max_rows) {
+    const int M = std::min(q->max_rows, n - c0);
+    TRY(launch_fill_positions(w.pos, M, c0, s));
+    TRY(launch_embed(d.dtype, d.embed, tokens_dev + c0, d.vocab, w.h, d.d_model, M, d.d_model, nullptr, nullptr,
+                     s));
+    Block b{w.h, RowBlock{M, nullptr, w.pos, nullptr, nullptr}, nullptr, 0, 0};
+    TRY(run_layers(q, b, 0, d.n_layers, nullptr, s));
+    last_rows = M;
+  }
+  float* lg = last_logits_dev ? last_logits_dev : w.logits1;
+  TRY(final_logits(q, w.h + (size_t)(last_rows - 1) * d.d_model, 1, nullptr, lg, nullptr, s));
+  TRY(launch_row_stats(lg, d.vocab, 1, d.vocab, temperature, seed, nullptr, 0, 0, PURPOSE_SAMPLE, w.stats, nullptr,
+                       s));
+  TRY(launch_pick_commit(w.stats, w.st, w.log, q->log_cap, 1, n, s));
+  return SSD_OK;
+}
+
+extern "C" int ssd_decode_ar(ssd_seq* q, float temperature, uint64_t seed, float* logits_dev, hipStream_t s) {
+  CHECK_ARG(q, "null argument");
+  CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
+  const ssd_model_desc& d = q->m->d;
+  const Workspace& w = q->w;
+  TRY(launch_single_row_prep(w.st, w.pos1, w.tok1, q->max_ctx, s));
+  TRY(launch_embed(d.dtype, d.embed, w.tok1, d.vocab, w.h1, d.d_model, 1, d.d_model, nullptr, nullptr, s));
+  Block b{w.h1, RowBlock{1, nullptr, w.pos1, nullptr, nullptr}, nullptr, 0, 0};
+  TRY(run_layers(q, b, 0, d.n_layers, nullptr, s));
+  float* lg = logits_dev ? logits_dev : w.logits1;
+  TRY(final_logits(q, w.h1, 1, nullptr, lg, nullptr, s));
+  TRY(launch_row_stats(lg, d.vocab, 1, d.vocab, temperature, seed, &w.st->iteration, 0, 0, PURPOSE_SAMPLE, w.stats,
+                       nullptr, s));
+  TRY(launch_pick_commit(w.stats, w.st, w.log, q->log_cap, 0, 0, s));
+  return SSD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// draft / verify / accept / commit
+
+extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_layer, int d_max, float conf_thresh,
+                         float temperature, uint64_t seed, int32_t* draft_tokens_dev, float* draft_logits_dev,
+                         int32_t* n_drafted_dev, hipStream_t s) {
+  CHECK_ARG(q && draft_tokens_dev && draft_logits_dev && n_drafted_dev, "null argument");
+  CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
+  CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
+  const ssd_model_desc& d = q->m->d;
+  const Workspace& w = q->w;
+  std::vector<uint8_t> mask;
+  const int b = plan_mask(q->m, skip_mask_host, exit_layer, mask);
+  CHECK_ARG(b >= 0, "exit_layer out of range");
+  const int* stop = &w.st->stop;
+  TRY(launch_draft_begin(w.st, s));
+  Block blk{w.h1, RowBlock{1, nullptr, w.pos1, nullptr, stop}, nullptr, 0, 0};
+  for (int j = 1; j <= d_max; ++j) {
+    TRY(launch_draft_step_prep(w.st, draft_tokens_dev, j, w.pos1, w.tok1, q->max_ctx, n_drafted_dev, s));
+    TRY(launch_embed(d.dtype, d.embed, w.tok1, d.vocab, w.h1, d.d_model, 1, d.d_model, nullptr, stop, s));
+    TRY(run_layers(q, blk, 0, b, nullptr, s));
+    TRY(launch_copy_rows(w.h1, w.hb + (size_t)(j - 1) * d.d_model, 1, d.d_model, nullptr, nullptr, stop, s));
+    TRY(run_layers(q, blk, b, d.n_layers, mask.data(), s));
+    float* lg = draft_logits_dev + (size_t)(j - 1) * d.vocab;
+    TRY(final_logits(q, w.h1, 1, nullptr, lg, stop, s));
+    TRY(launch_draft_stats(lg, d.vocab, temperature, seed, w.st, j, d_max, conf_thresh, draft_tokens_dev,
+                           n_drafted_dev, s));
+  }
+  return SSD_OK;
+}
+
+extern "C" int ssd_verify(ssd_seq* q, const uint8_t* skip_mask_host, int exit_layer, int d_max,
+                          const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, int reuse,
+                          float* logits_dev, hipStream_t s) {
+  CHECK_ARG(q && draft_tokens_dev && n_drafted_dev && logits_dev, "null argument");
+  CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
+  const ssd_model_desc& d = q->m->d;
+  const Workspace& w = q->w;
+  std::vector<uint8_t> mask;
+  const int b = plan_mask(q->m, skip_mask_host, exit_layer, mask);
+  CHECK_ARG(b >= 0, "exit_layer out of range");
+  const int M = d_max + 1;
+  const int* rows = &w.st->verify_rows;
+  TRY(launch_verify_prep(w.st, draft_tokens_dev, n_drafted_dev, d_max, w.vpos, w.vtok, w.pos1, w.tok1, q->max_ctx,
+                         s));
+  Block full{w.h, RowBlock{M, rows, w.vpos, nullptr, nullptr}, nullptr, 0, 0};
+  if (reuse) {
+    // rows < d' take the residual saved by the draft at the boundary
+    TRY(launch_copy_rows(w.hb, w.h, d_max, d.d_model, n_drafted_dev, nullptr, nullptr, s));
+    // the last row (y_d') runs the layers below the boundary
+    TRY(launch_embed(d.dtype, d.embed, w.tok1, d.vocab, w.h1, d.d_model, 1, d.d_model, nullptr, nullptr, s));
+    Block one{w.h1, RowBlock{1, nullptr, w.pos1, nullptr, nullptr}, nullptr, 0, 0};
+    TRY(run_layers(q, one, 0, b, nullptr, s));
+    TRY(launch_copy_rows(w.h1, w.h, 1, d.d_model, nullptr, n_drafted_dev, nullptr, s));
+  } else {
+    TRY(launch_embed(d.dtype, d.embed, w.vtok, d.vocab, w.h, d.d_model, M, d.d_model, rows, nullptr, s));
+    TRY(run_layers(q, full, 0, b, nullptr, s));
+  }
+  TRY(run_layers(q, full, b, d.n_layers, nullptr, s));
+  TRY(final_logits(q, w.h, M, rows, logits_dev, nullptr, s));
+  return SSD_OK;
+}
+
+extern "C" int ssd_accept(ssd_seq* q, const float* p_logits_dev, const float* q_logits_dev,
+                          const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, int d_max, float temperature,
+                          uint64_t seed, int32_t* out_tokens_dev, int32_t* n_out_dev, hipStream_t s) {
+  CHECK_ARG(q && p_logits_dev && q_logits_dev && draft_tokens_dev && n_drafted_dev && out_tokens_dev && n_out_dev,
+            "null argument");
+  CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
+  CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
+  TRY(launch_accept(p_logits_dev, q_logits_dev, q->m->d.vocab, draft_tokens_dev, n_drafted_dev, d_max, temperature,
+                    seed, q->w.st, q->w.dec, q->w.corr, out_tokens_dev, n_out_dev, s));
+  return SSD_OK;
+}
+
+extern "C" int ssd_commit(ssd_seq* q, const int32_t* out_tokens_dev, const int32_t* n_out_dev, hipStream_t s) {
+  CHECK_ARG(q && out_tokens_dev && n_out_dev, "null argument");
+  TRY(launch_commit(q->w.st, out_tokens_dev, n_out_dev, q->w.log, q->log_cap, s));
+  return SSD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// SWIFT matchness scoring
+
+extern "C" int ssd_score_masks(ssd_seq* q, const uint8_t* masks_host, int n_masks, const int32_t* window_dev,
+                               int pos0, int gamma, float* scores_dev, int32_t* best_dev, hipStream_t s) {
+  CHECK_ARG(q && masks_host && window_dev && scores_dev && best_dev, "null argument");
+  CHECK_ARG(n_masks >= 1 && gamma >= 1, "empty scoring problem");
+  CHECK_ARG(pos0 >= 0, "negative pos0");
+  const ssd_model_desc& d = q->m->d;
+  const int L = d.n_layers;
+  const int R = n_masks * gamma;
+  if (R > q->max_rows) return fail(SSD_ERR_CAPACITY, "n_masks * gamma exceeds max_rows");
+  if (pos0 + gamma > q->max_ctx) return fail(SSD_ERR_CAPACITY, "window beyond the KV pages");
+  const Workspace& w = q->w;
+  // compact row lists per sub-layer: rows of the candidates that run it
+  std::vector<int> maps((size_t)2 * L * R);
+  std::vector<int> counts(2 * L);
+  for (int sl = 0; sl < 2 * L; ++sl) {
+    int n = 0;
+    for (int c = 0; c < n_masks; ++c)
+      if (!masks_host[(size_t)c * 2 * L + sl])
+        for (int i = 0; i < gamma; ++i) maps[(size_t)sl * R + n++] = c * gamma + i;
+    counts[sl] = n;
+  }
+  hipError_t e = hipMemcpyAsync(w.rowmaps, maps.data(), sizeof(int) * maps.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "rowmap upload");
+  TRY(launch_window_rows(window_dev, R, gamma, pos0, w.pos, w.tok, s));
+  TRY(launch_embed(d.dtype, d.embed, w.tok, d.vocab, w.h, d.d_model, R, d.d_model, nullptr, nullptr, s));
+  for (int l = 0; l < L; ++l) {
+    for (int sub = 0; sub < 2; ++sub) {
+      const int sl = 2 * l + sub;
+      const int M = counts[sl];
+      if (M == 0) continue;
+      // compact row j is window row j % gamma: positions come from w.pos (filled for all R rows)
+      Block b{w.h, RowBlock{M, nullptr, w.pos, w.rowmaps + (size_t)sl * R, nullptr}, w.local_kv, pos0, gamma};
+      if (sub == 0) TRY(attn_sublayer(q, l, b, s));
+      else TRY(mlp_sublayer(q, l, b, s));
+    }
+  }
+  TRY(final_logits(q, w.h, R, nullptr, w.logits_rows, nullptr, s));
+  TRY(launch_row_stats(w.logits_rows, d.vocab, R, d.vocab, 0.f, 0, nullptr, 0, 0, PURPOSE_DRAFT, w.stats, nullptr,
+                       s));
+  TRY(launch_score(w.stats, window_dev, n_masks, gamma, scores_dev, best_dev, s));
+  // the host row lists must outlive the copy
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "stream sync");
+  return SSD_OK;
+}
+
+extern "C" int ssd_row_stats(const float* logits_dev, int rows, int V, float temperature, uint64_t seed,
+                             int32_t iteration, ssd_row_stat* stats_dev, hipStream_t s) {
+  CHECK_ARG(logits_dev && stats_dev && rows >= 1 && V >= 1, "bad argument");
+  CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
+  TRY(launch_row_stats(logits_dev, V, rows, V, temperature, seed, nullptr, iteration, 0, PURPOSE_DRAFT, stats_dev,
+                       nullptr, s));
+  return SSD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// host synchronisation
+
+extern "C" int ssd_read_state(ssd_seq* q, ssd_state* out, hipStream_t s) {
+  CHECK_ARG(q && out, "null argument");
+  DevState st;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(&st, q->w.st, sizeof(st), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, std::string("read state: ") + hipGetErrorString(e));
+  out->kvlen = st.kvlen;
+  out->last_token = st.last_token;
+  out->iteration = st.iteration;
+  out->n_out = st.n_out;
+  out->error_flags = st.error_flags;
+  out->last_n_drafted = st.n_drafted;
+  out->last_n_emitted = st.n_emitted;
+  if (st.error_flags & ERRF_CAPACITY) return fail(SSD_ERR_CAPACITY, "KV pages or output log exhausted on the device");
+  if (st.error_flags & ERRF_NUMERIC) return fail(SSD_ERR_NUMERIC, "non-finite logits seen on the device");
+  return SSD_OK;
+}
+
+extern "C" int ssd_read_output(ssd_seq* q, int32_t* tokens_host, int max_tokens, int* n_tokens, hipStream_t s) {
+  CHECK_ARG(q && tokens_host && n_tokens && max_tokens >= 0, "bad argument");
+  ssd_state st;
+  int rc = ssd_read_state(q, &st, s);
+  if (rc != SSD_OK && rc != SSD_ERR_CAPACITY && rc != SSD_ERR_NUMERIC) return rc;
+  const int n = std::min(std::min(st.n_out, max_tokens), q->log_cap);
+  hipError_t e = n > 0 ? hipMemcpy(tokens_host, q->w.log, sizeof(int32_t) * n, hipMemcpyDeviceToHost) : hipSuccess;
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "read output");
+  *n_tokens = n;
+  return rc;
+}

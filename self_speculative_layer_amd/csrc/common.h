@@ -1,0 +1,117 @@
+// Shared device/host definitions of the self-speculative decoding library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+// Flags in DevState::error_flags.
+constexpr int ERRF_CAPACITY = 1;
+constexpr int ERRF_NUMERIC = 2;
+
+// Per-sequence state that lives on the device, so that the host can enqueue
+// a whole decode iteration without reading anything back.
+struct DevState {
+  int32_t kvlen;        // positions with committed K/V (= committed tokens - 1)
+  int32_t last_token;   // newest committed token (input of the next step)
+  int32_t iteration;    // random-draw address: 0 = prefill's token, SSD iterations from 1
+  int32_t n_out;        // tokens in the output log
+  int32_t error_flags;  // ERRF_* (sticky)
+  int32_t n_drafted;    // d' of the last draft
+  int32_t stop;         // draft early-stop flag (kernels of later draft steps exit at once)
+  int32_t n_emitted;    // tokens emitted by the last commit
+  int32_t verify_rows;  // d' + 1 of the current verify
+  int32_t pad[7];
+};
+
+// ---------------------------------------------------------------------------
+// Conversions
+
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bfloat16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float ld(const float* p) { return *p; }
+__device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
+__device__ __forceinline__ void st(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+
+// ---------------------------------------------------------------------------
+// Wave / block reductions (64-lane wavefronts)
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// (value, index) maximum with the lowest index winning ties.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v2 = __shfl_xor(v, o, WAVE);
+    int i2 = __shfl_xor(i, o, WAVE);
+    argmax_merge(v, i, v2, i2);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): the random draws of the
+// accept rule.  key = (seed lo, seed hi); counter = (iteration, row, purpose,
+// element / 4); word element % 4.
+
+constexpr uint32_t PURPOSE_DRAFT = 0;
+constexpr uint32_t PURPOSE_ACCEPT = 1;
+constexpr uint32_t PURPOSE_SAMPLE = 2;
+
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                            uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0;
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0;
+    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
+// Uniform in (0, 1), exact in float32: (2 * (x >> 9) + 1) * 2^-24.
+__device__ __forceinline__ float word_to_uniform(uint32_t x) {
+  return (float)(2u * (x >> 9) + 1u) * 5.9604644775390625e-08f;
+}
+
+// Gumbel(0, 1) noise -log(-log u), float32.
+__device__ __forceinline__ float word_to_gumbel(uint32_t x) {
+  return -logf(-logf(word_to_uniform(x)));
+}
+
+}  // namespace ssd

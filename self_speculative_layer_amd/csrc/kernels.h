@@ -1,0 +1,95 @@
+// Host-side launchers of the library's HIP kernels (kernels.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "../../include/ssd.h"
+
+namespace ssd {
+
+// GEMM epilogues: Y = X . W^T then
+enum Epilogue {
+  EPI_STORE = 0,    // Y[m, n] = acc                          (float)
+  EPI_RESID = 1,    // Y[m, n] += acc                         (float residual stream)
+  EPI_SWIGLU = 2    // A[m, f] = act(silu(acc_gate) * acc_up) (act dtype; W rows f and f + up_rows)
+};
+
+// Description of a block of rows that flows through the decoder layers.
+struct RowBlock {
+  int M;               // static row count (grid size)
+  const int* nrows;    // device: active rows (nullable -> M)
+  const int* pos;      // device: absolute position of each row [M]
+  const int* ymap;     // device: residual row of each compact row (nullable -> identity)
+  const int* stop;     // device: early-exit flag (nullable)
+};
+
+struct KvView {
+  void* pool;          // [pages][L][2][KVH][PS][HD]
+  const int* page_table;
+  int n_lpages, page_size;
+};
+
+// Linear layer: X [M, K] (row stride ldx, act dtype) times W [N, K]^T.
+// For EPI_SWIGLU, N = F (output features) and W holds 2F rows (gate, then up).
+int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
+                  float* Y, int ldy, void* A, int lda, const int* nrows, const int* ymap,
+                  const int* stop, hipStream_t s);
+
+int launch_rmsnorm(int dtype, const float* h, int ldh, const float* gain, void* x, int ldx, int M, int D,
+                   float eps, const int* nrows, const int* hmap, const int* stop, hipStream_t s);
+
+int launch_embed(int dtype, const void* emb, const int* tokens, int V, float* h, int ldh, int M, int D,
+                 const int* nrows, const int* stop, hipStream_t s);
+
+// RoPE on q and k, bf16/f32 storage of q into qout and of k, v into the cache
+// (or, when local_kv != nullptr, into local_kv[row][2][KVH][HD]).
+int launch_rope_kv(int dtype, int head_dim, const float* qkv, int ldqkv, void* qout, int ldq,
+                   const KvView& kv, int L, int layer, int H, int KVH, const RowBlock& rb,
+                   const double* inv_freq, void* local_kv, int* err_flags, hipStream_t s);
+
+// Attention of every row over cached keys at positions <= its own (keys at
+// positions >= local_start come from local_kv rows of the row's own group of
+// `group_rows` consecutive rows).  Output act dtype [M, H*HD].
+int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer,
+                     int H, int KVH, const RowBlock& rb, int max_ctx, const void* local_kv,
+                     int local_start, int group_rows, float* part, void* out, int ldo, hipStream_t s);
+size_t attention_partial_floats(int max_rows, int H, int head_dim, int max_ctx);
+
+// Row statistics (a3).  purpose/rowid_base address the random draws.
+int launch_row_stats(const float* z, int ldz, int rows, int V, float T, uint64_t seed,
+                     const int* iter_ptr, int iter_const, int rowid_base, uint32_t purpose,
+                     ssd_row_stat* out, const int* stop, hipStream_t s);
+
+// Draft step j: stats of one row + draft token + early stop.
+int launch_draft_stats(const float* z, int V, float T, uint64_t seed, DevState* st, int j, int d,
+                       float tau, int32_t* draft_tokens, int32_t* n_drafted_out, hipStream_t s);
+
+int launch_accept(const float* zp, const float* zq, int V, const int32_t* drafts, const int32_t* n_drafted,
+                  int d, float T, uint64_t seed, const DevState* st, int* dec, int* corr,
+                  int32_t* out_tokens, int32_t* n_out, hipStream_t s);
+
+int launch_commit(DevState* st, const int32_t* out_tokens, const int32_t* n_out, int32_t* log,
+                  int log_cap, hipStream_t s);
+
+// Pick one token from a row's stats and commit it (prefill / AR step).
+int launch_pick_commit(const ssd_row_stat* stat, DevState* st, int32_t* log, int log_cap, int set_kvlen,
+                       int kvlen_value, hipStream_t s);
+
+// Small control kernels.
+int launch_state_init(DevState* st, hipStream_t s);
+int launch_fill_positions(int* pos, int M, int start, hipStream_t s);
+int launch_window_rows(const int32_t* window, int R, int gamma, int pos0, int* pos, int* tok, hipStream_t s);
+int launch_single_row_prep(DevState* st, int* pos1, int* tok1, int max_ctx, hipStream_t s);
+int launch_draft_begin(DevState* st, hipStream_t s);
+int launch_draft_step_prep(DevState* st, const int32_t* drafts, int j, int* pos1, int* tok1, int max_ctx,
+                           int32_t* n_drafted_out, hipStream_t s);
+int launch_verify_prep(DevState* st, const int32_t* drafts, const int32_t* n_drafted, int d, int* vpos,
+                       int* vtok, int* pos1, int* tok1, int max_ctx, hipStream_t s);
+// Copies rows r < (count ? *count : rows) of src [.., D] to dst row r + (dst_off ? *dst_off : 0).
+int launch_copy_rows(const float* src, float* dst, int rows, int D, const int* count, const int* dst_off,
+                     const int* stop, hipStream_t s);
+int launch_score(const ssd_row_stat* stats, const int32_t* window, int n_masks, int gamma, float* scores,
+                 int32_t* best, hipStream_t s);
+
+}  // namespace ssd

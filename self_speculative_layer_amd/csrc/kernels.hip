@@ -1,0 +1,1040 @@
+// HIP kernels of the self-speculative decoding path, written for gfx950
+// (CDNA4: 64-lane wavefronts, bf16 MFMA 16x16x32, 160 KB LDS per CU).
+#include <math.h>
+
+#include "kernels.h"
+
+namespace ssd {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+static inline int hip_ok(hipError_t e) { return e == hipSuccess ? 0 : SSD_ERR_HIP; }
+static inline int last_launch() { return hip_ok(hipGetLastError()); }
+
+__device__ __forceinline__ int active_rows(int M, const int* nrows) {
+  return nrows ? min(M, *nrows) : M;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// ===========================================================================
+// Linear layers, bf16: Y[M, N] = X[M, K] . W[N, K]^T with fp32 accumulation on
+// the matrix cores.  Weight-streaming design for few rows: a workgroup owns 16
+// output features for a 16-row block and all of K; its NW waves split K into
+// contiguous 64-element slices (each weight row is read as whole 128-byte
+// lines by one wave), accumulate with v_mfma_f32_16x16x32_bf16 (weights as
+// the A operand: 16 features x 32 k; activations as B: 32 k x 16 rows), then
+// reduce the per-wave tiles through LDS in a fixed order.  The reduction order
+// of an output element never depends on M, so a row's result is the same
+// whatever rows it is batched with.
+// ===========================================================================
+
+constexpr int GEMM_NW = 8;
+constexpr int GEMM_U = 8;
+
+template <int EPI>
+__global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_rows16(
+    const bf16_t* __restrict__ W, const bf16_t* __restrict__ X, int ldx, int M, int N, int K,
+    float* __restrict__ Y, int ldy, bf16_t* __restrict__ A, int lda, int n_rb,
+    const int* __restrict__ nrows, const int* __restrict__ ymap, const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int Ma = active_rows(M, nrows);
+  const int rb = blockIdx.x % n_rb;
+  const int tile = blockIdx.x / n_rb;
+  const int m0 = rb * 16;
+  if (m0 >= Ma) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = tile * 16;
+  const int nrow = n0 + r;
+  const bool wv = nrow < N;
+  const bf16_t* wp = W + (size_t)(wv ? nrow : 0) * K + g * 8;
+  const bf16_t* wp2 = wp + (size_t)N * K;   // up rows (EPI_SWIGLU)
+  const int m = m0 + r;
+  const bool xv = m < Ma;
+  const bf16_t* xp = X + (size_t)(xv ? m : 0) * ldx + g * 8;
+
+  const int nu = K >> 6;                       // 64-element units of K
+  const int kb_beg = 2 * ((nu * wave) / GEMM_NW);
+  const int kb_end = 2 * ((nu * (wave + 1)) / GEMM_NW);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+  int kb = kb_beg;
+  for (; kb + GEMM_U <= kb_end; kb += GEMM_U) {
+    u32x4 wa[GEMM_U], wb[GEMM_U], xa[GEMM_U];
+#pragma unroll
+    for (int u = 0; u < GEMM_U; ++u) {
+      wa[u] = wv ? *(const u32x4*)(wp + (kb + u) * 32) : zero;
+      if (EPI == EPI_SWIGLU) wb[u] = wv ? *(const u32x4*)(wp2 + (kb + u) * 32) : zero;
+      xa[u] = xv ? *(const u32x4*)(xp + (kb + u) * 32) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < GEMM_U; ++u) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[u]),
+                                                    __builtin_bit_cast(bf16x8, xa[u]), acc, 0, 0, 0);
+      if (EPI == EPI_SWIGLU)
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb[u]),
+                                                       __builtin_bit_cast(bf16x8, xa[u]), acc2, 0, 0, 0);
+    }
+  }
+  for (; kb < kb_end; ++kb) {
+    u32x4 wa = wv ? *(const u32x4*)(wp + kb * 32) : zero;
+    u32x4 xa = xv ? *(const u32x4*)(xp + kb * 32) : zero;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa),
+                                                  __builtin_bit_cast(bf16x8, xa), acc, 0, 0, 0);
+    if (EPI == EPI_SWIGLU) {
+      u32x4 wb = wv ? *(const u32x4*)(wp2 + kb * 32) : zero;
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb),
+                                                     __builtin_bit_cast(bf16x8, xa), acc2, 0, 0, 0);
+    }
+  }
+  // acc[i] holds D[feature 4g + i][row r].
+  constexpr int NT = (EPI == EPI_SWIGLU) ? 2 : 1;
+  __shared__ float red[NT][GEMM_NW][16][17];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    red[0][wave][4 * g + i][r] = acc[i];
+    if (EPI == EPI_SWIGLU) red[NT - 1][wave][4 * g + i][r] = acc2[i];
+  }
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int mm = threadIdx.x >> 4, nn = threadIdx.x & 15;
+    const int row = m0 + mm, col = n0 + nn;
+    if (row < Ma && col < N) {
+      float s = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int w = 0; w < GEMM_NW; ++w) {
+        s += red[0][w][nn][mm];
+        if (EPI == EPI_SWIGLU) s2 += red[NT - 1][w][nn][mm];
+      }
+      const int yrow = ymap ? ymap[row] : row;
+      if (EPI == EPI_STORE) Y[(size_t)yrow * ldy + col] = s;
+      else if (EPI == EPI_RESID) Y[(size_t)yrow * ldy + col] += s;
+      else A[(size_t)row * lda + col] = f2bf(silu(s) * s2);
+    }
+  }
+}
+
+// fp32 linear layer (the fp32 workload): plain FMAs.  A workgroup owns 16
+// output features (4 per wave) and a 16-row block; lanes stride K, each lane
+// sums its k in order, then a fixed butterfly reduces across lanes.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_rows16(
+    const float* __restrict__ W, const float* __restrict__ X, int ldx, int M, int N, int K,
+    float* __restrict__ Y, int ldy, float* __restrict__ A, int lda, int n_rb,
+    const int* __restrict__ nrows, const int* __restrict__ ymap, const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int Ma = active_rows(M, nrows);
+  const int rb = blockIdx.x % n_rb;
+  const int tile = blockIdx.x / n_rb;
+  const int m0 = rb * 16;
+  if (m0 >= Ma) return;
+  const int mcount = min(16, Ma - m0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int c = 0; c < 4; ++c) {
+    const int col = tile * 16 + wave * 4 + c;
+    if (col >= N) break;
+    float acc[16], acc2[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { acc[i] = 0.f; acc2[i] = 0.f; }
+    const float* w = W + (size_t)col * K;
+    const float* w2 = w + (size_t)N * K;
+    for (int k = lane; k < K; k += 64) {
+      const float a = w[k];
+      const float a2 = (EPI == EPI_SWIGLU) ? w2[k] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < mcount) {
+          const float xv = X[(size_t)(m0 + i) * ldx + k];
+          acc[i] = fmaf(a, xv, acc[i]);
+          if (EPI == EPI_SWIGLU) acc2[i] = fmaf(a2, xv, acc2[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < mcount) {
+        const float s = wave_sum(acc[i]);
+        const float s2 = (EPI == EPI_SWIGLU) ? wave_sum(acc2[i]) : 0.f;
+        if (lane == 0) {
+          const int row = m0 + i;
+          const int yrow = ymap ? ymap[row] : row;
+          if (EPI == EPI_STORE) Y[(size_t)yrow * ldy + col] = s;
+          else if (EPI == EPI_RESID) Y[(size_t)yrow * ldy + col] += s;
+          else A[(size_t)row * lda + col] = silu(s) * s2;
+        }
+      }
+    }
+  }
+}
+
+int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
+                  float* Y, int ldy, void* A, int lda, const int* nrows, const int* ymap,
+                  const int* stop, hipStream_t s) {
+  if (M <= 0 || N <= 0) return 0;
+  const int n_rb = (M + 15) / 16;
+  const int n_tiles = (N + 15) / 16;
+  const dim3 grid(n_rb * n_tiles);
+  if (dtype == SSD_DTYPE_BF16) {
+    if (K % 64 != 0) return SSD_ERR_SHAPE;
+    const bf16_t* w = (const bf16_t*)W;
+    const bf16_t* x = (const bf16_t*)X;
+    switch (epi) {
+      case EPI_STORE:
+        hipLaunchKernelGGL(gemm_bf16_rows16<EPI_STORE>, grid, dim3(GEMM_NW * 64), 0, s, w, x, ldx, M, N, K, Y,
+                           ldy, (bf16_t*)A, lda, n_rb, nrows, ymap, stop);
+        break;
+      case EPI_RESID:
+        hipLaunchKernelGGL(gemm_bf16_rows16<EPI_RESID>, grid, dim3(GEMM_NW * 64), 0, s, w, x, ldx, M, N, K, Y,
+                           ldy, (bf16_t*)A, lda, n_rb, nrows, ymap, stop);
+        break;
+      default:
+        hipLaunchKernelGGL(gemm_bf16_rows16<EPI_SWIGLU>, grid, dim3(GEMM_NW * 64), 0, s, w, x, ldx, M, N, K, Y,
+                           ldy, (bf16_t*)A, lda, n_rb, nrows, ymap, stop);
+    }
+  } else {
+    const float* w = (const float*)W;
+    const float* x = (const float*)X;
+    switch (epi) {
+      case EPI_STORE:
+        hipLaunchKernelGGL(gemm_f32_rows16<EPI_STORE>, grid, dim3(256), 0, s, w, x, ldx, M, N, K, Y, ldy,
+                           (float*)A, lda, n_rb, nrows, ymap, stop);
+        break;
+      case EPI_RESID:
+        hipLaunchKernelGGL(gemm_f32_rows16<EPI_RESID>, grid, dim3(256), 0, s, w, x, ldx, M, N, K, Y, ldy,
+                           (float*)A, lda, n_rb, nrows, ymap, stop);
+        break;
+      default:
+        hipLaunchKernelGGL(gemm_f32_rows16<EPI_SWIGLU>, grid, dim3(256), 0, s, w, x, ldx, M, N, K, Y, ldy,
+                           (float*)A, lda, n_rb, nrows, ymap, stop);
+    }
+  }
+  return last_launch();
+}
+
+// ===========================================================================
+// RMSNorm: x[m] = act(h[hmap[m]] / sqrt(mean(h^2) + eps) * gain), fp32 sums.
+// ===========================================================================
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h, int ldh,
+                                                      const float* __restrict__ gain, T* __restrict__ x,
+                                                      int ldx, int M, int D, float eps,
+                                                      const int* __restrict__ nrows,
+                                                      const int* __restrict__ hmap, const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int row = blockIdx.x;
+  if (row >= active_rows(M, nrows)) return;
+  const float* hr = h + (size_t)(hmap ? hmap[row] : row) * ldh;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) ss = fmaf(hr[i], hr[i], ss);
+  ss = wave_sum(ss);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)D + eps);
+  T* xr = x + (size_t)row * ldx;
+  for (int i = threadIdx.x; i < D; i += 256) st(xr + i, hr[i] * inv * gain[i]);
+}
+
+int launch_rmsnorm(int dtype, const float* h, int ldh, const float* gain, void* x, int ldx, int M, int D,
+                   float eps, const int* nrows, const int* hmap, const int* stop, hipStream_t s) {
+  if (M <= 0) return 0;
+  if (dtype == SSD_DTYPE_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, s, h, ldh, gain, (bf16_t*)x, ldx, M, D,
+                       eps, nrows, hmap, stop);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, s, h, ldh, gain, (float*)x, ldx, M, D, eps,
+                       nrows, hmap, stop);
+  return last_launch();
+}
+
+// ===========================================================================
+// Embedding gather into the fp32 residual stream.
+// ===========================================================================
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ emb, const int* __restrict__ tokens,
+                                                    int V, float* __restrict__ h, int ldh, int M, int D,
+                                                    const int* __restrict__ nrows, const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int row = blockIdx.x;
+  if (row >= active_rows(M, nrows)) return;
+  const int t = min(max(tokens[row], 0), V - 1);   // ids are produced in range; clamp keeps reads in bounds
+  const T* e = emb + (size_t)t * D;
+  float* hr = h + (size_t)row * ldh;
+  for (int i = threadIdx.x; i < D; i += 256) hr[i] = ld(e + i);
+}
+
+int launch_embed(int dtype, const void* emb, const int* tokens, int V, float* h, int ldh, int M, int D,
+                 const int* nrows, const int* stop, hipStream_t s) {
+  if (M <= 0) return 0;
+  if (dtype == SSD_DTYPE_BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, s, (const bf16_t*)emb, tokens, V, h, ldh, M,
+                       D, nrows, stop);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, s, (const float*)emb, tokens, V, h, ldh, M, D,
+                       nrows, stop);
+  return last_launch();
+}
+
+// ===========================================================================
+// RoPE + KV append.  One workgroup (HD/2 threads) per (row, head slot):
+// slots 0..H-1 rotate q, H..H+KVH-1 rotate k into the cache, the rest copy v.
+// Angles pos * theta^(-2i/hd) are formed and reduced in fp64, cos/sin rounded
+// to fp32, the rotation itself in fp32.
+// ===========================================================================
+
+__device__ __forceinline__ size_t kv_index(int page, int L, int layer, int kv, int KVH, int g, int PS, int slot,
+                                           int HD) {
+  return (((((size_t)page * L + layer) * 2 + kv) * KVH + g) * PS + slot) * (size_t)HD;
+}
+
+template <typename T, int HD>
+__global__ void rope_kv_kernel(const float* __restrict__ qkv, int ldqkv, T* __restrict__ qout, int ldq,
+                               T* __restrict__ pool, const int* __restrict__ page_table, int n_lpages, int PS,
+                               int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
+                               const int* __restrict__ pos, const double* __restrict__ inv_freq,
+                               T* __restrict__ local_kv, int* __restrict__ err, const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int row = blockIdx.x;
+  if (row >= active_rows(M, nrows)) return;
+  const int slot = blockIdx.y;
+  const int i = threadIdx.x;                  // pair index 0..HD/2-1
+  const int p = pos[row];
+  const float* src = qkv + (size_t)row * ldqkv + (size_t)slot * HD;
+  T* dst;
+  if (slot < H) {
+    dst = qout + (size_t)row * ldq + (size_t)slot * HD;
+  } else {
+    const int kvsel = slot < H + KVH ? 0 : 1;
+    const int g = slot - H - kvsel * KVH;
+    if (local_kv) {
+      dst = local_kv + (((size_t)row * 2 + kvsel) * KVH + g) * HD;
+    } else {
+      const int lp = p / PS;
+      if (lp >= n_lpages || p < 0) {
+        if (i == 0) atomicOr(err, ERRF_CAPACITY);
+        return;
+      }
+      dst = pool + kv_index(page_table[lp], L, layer, kvsel, KVH, g, PS, p % PS, HD);
+    }
+  }
+  const float x1 = src[i], x2 = src[i + HD / 2];
+  if (slot < H + KVH) {
+    const double a = (double)p * inv_freq[i];
+    const float c = (float)cos(a), sn = (float)sin(a);
+    st(dst + i, x1 * c - x2 * sn);
+    st(dst + i + HD / 2, x2 * c + x1 * sn);
+  } else {
+    st(dst + i, x1);
+    st(dst + i + HD / 2, x2);
+  }
+}
+
+int launch_rope_kv(int dtype, int head_dim, const float* qkv, int ldqkv, void* qout, int ldq,
+                   const KvView& kv, int L, int layer, int H, int KVH, const RowBlock& rb,
+                   const double* inv_freq, void* local_kv, int* err_flags, hipStream_t s) {
+  if (rb.M <= 0) return 0;
+  const dim3 grid(rb.M, H + 2 * KVH);
+#define ROPE_LAUNCH(T, HD)                                                                                     \
+  hipLaunchKernelGGL((rope_kv_kernel<T, HD>), grid, dim3(HD / 2), 0, s, qkv, ldqkv, (T*)qout, ldq, (T*)kv.pool, \
+                     kv.page_table, kv.n_lpages, kv.page_size, L, layer, H, KVH, rb.M, rb.nrows, rb.pos,        \
+                     inv_freq, (T*)local_kv, err_flags, rb.stop)
+  if (dtype == SSD_DTYPE_BF16) {
+    if (head_dim == 128) ROPE_LAUNCH(bf16_t, 128); else ROPE_LAUNCH(bf16_t, 64);
+  } else {
+    if (head_dim == 128) ROPE_LAUNCH(float, 128); else ROPE_LAUNCH(float, 64);
+  }
+#undef ROPE_LAUNCH
+  return last_launch();
+}
+
+// ===========================================================================
+// Attention over the paged cache, split over keys.  Split s covers absolute
+// key positions [256 s, 256 s + 256); a workgroup handles one KV head, one
+// split and a block of rows with all their query heads (grouped-query), stages
+// 64 keys at a time in LDS as fp32 (K transposed so lanes read consecutive
+// words) and keeps an online softmax per query.  Partial (m, l, o) go to a
+// buffer; a combine kernel merges the splits of a row in split order.  Split
+// boundaries are fixed positions, so a row's result does not depend on the
+// rows batched with it.
+// ===========================================================================
+
+constexpr int ATT_SPLIT = 256;
+constexpr int ATT_CHUNK = 64;
+constexpr int ATT_MAXQ = 64;     // queries (rows x heads of a group) per workgroup
+
+size_t attention_partial_floats(int max_rows, int H, int head_dim, int max_ctx) {
+  const int nsplit = (max_ctx + ATT_SPLIT - 1) / ATT_SPLIT;
+  return (size_t)max_rows * H * nsplit * (head_dim + 2);
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_partial_kernel(
+    const T* __restrict__ q, int ldq, const T* __restrict__ pool, const int* __restrict__ page_table, int PS,
+    int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows, const int* __restrict__ pos, int RB,
+    int nsplit, const T* __restrict__ local_kv, int local_start, int group_rows, float* __restrict__ part,
+    const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int g = blockIdx.x, s = blockIdx.y, rbk = blockIdx.z;
+  const int Ma = active_rows(M, nrows);
+  const int r0 = rbk * RB;
+  if (r0 >= Ma) return;
+  const int r1 = min(r0 + RB, Ma);
+  const int G = H / KVH;
+  const int nq = (r1 - r0) * G;
+  const int key_beg = s * ATT_SPLIT;
+  const int maxpos = pos[r1 - 1];
+  if (key_beg > maxpos) return;
+  const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
+  const float scale = 1.0f / sqrtf((float)HD);
+
+  __shared__ float Kt[HD][ATT_CHUNK + 1];
+  __shared__ float Vs[ATT_CHUNK][HD];
+  __shared__ float Qs[ATT_MAXQ][HD];
+  __shared__ float Os[ATT_MAXQ][HD];
+  __shared__ float Ms[ATT_MAXQ], Ls[ATT_MAXQ];
+  __shared__ float Pw[4][ATT_CHUNK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < nq * HD; e += 256) {
+    const int qi = e / HD, d = e % HD;
+    const int row = r0 + qi / G, head = g * G + qi % G;
+    Qs[qi][d] = ld(q + (size_t)row * ldq + (size_t)head * HD + d);
+    Os[qi][d] = 0.f;
+  }
+  for (int qi = tid; qi < nq; qi += 256) { Ms[qi] = -INFINITY; Ls[qi] = 0.f; }
+  // the group of the block's rows (scoring: candidates of group_rows rows each)
+  const int grp_base = group_rows > 0 ? (r0 / group_rows) * group_rows : 0;
+
+  for (int kc = key_beg; kc < key_end; kc += ATT_CHUNK) {
+    __syncthreads();
+    // stage keys kc .. kc+63 (masked past key_end)
+    for (int e = tid; e < ATT_CHUNK * HD; e += 256) {
+      const int t = e / HD, d = e % HD;
+      const int kp = kc + t;
+      float kval = 0.f, vval = 0.f;
+      if (kp < key_end) {
+        if (local_kv && kp >= local_start) {
+          const size_t base = ((size_t)(grp_base + (kp - local_start)) * 2) * KVH * HD;
+          kval = ld(local_kv + base + (size_t)g * HD + d);
+          vval = ld(local_kv + base + (size_t)KVH * HD + (size_t)g * HD + d);
+        } else {
+          const int page = page_table[kp / PS];
+          kval = ld(pool + kv_index(page, L, layer, 0, KVH, g, PS, kp % PS, HD) + d);
+          vval = ld(pool + kv_index(page, L, layer, 1, KVH, g, PS, kp % PS, HD) + d);
+        }
+      }
+      Kt[d][t] = kval;
+      Vs[t][d] = vval;
+    }
+    __syncthreads();
+    for (int qi = wave; qi < nq; qi += 4) {
+      const int row = r0 + qi / G;
+      const int prow = pos[row];
+      const int kp = kc + lane;
+      const bool valid = kp < key_end && kp <= prow;
+      float sc = -INFINITY;
+      if (valid) {
+        float acc = 0.f;
+#pragma unroll 16
+        for (int d = 0; d < HD; ++d) acc = fmaf(Qs[qi][d], Kt[d][lane], acc);
+        sc = acc * scale;
+      }
+      const float mx = wave_max(sc);
+      if (mx == -INFINITY) continue;            // no visible key in this chunk (wave-uniform)
+      const float m_old = Ms[qi];
+      const float m_new = fmaxf(m_old, mx);
+      const float alpha = expf(m_old - m_new);   // 0 when m_old = -inf
+      const float pexp = valid ? expf(sc - m_new) : 0.f;
+      const float psum = wave_sum(pexp);
+      Pw[wave][lane] = pexp;
+      __builtin_amdgcn_wave_barrier();
+      for (int d = lane; d < HD; d += 64) {
+        float o = Os[qi][d] * alpha;
+        for (int t = 0; t < ATT_CHUNK; ++t) o = fmaf(Pw[wave][t], Vs[t][d], o);
+        Os[qi][d] = o;
+      }
+      if (lane == 0) { Ms[qi] = m_new; Ls[qi] = Ls[qi] * alpha + psum; }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < nq * (HD + 2); e += 256) {
+    const int qi = e / (HD + 2), c = e % (HD + 2);
+    const int row = r0 + qi / G, head = g * G + qi % G;
+    if (s * ATT_SPLIT > pos[row]) continue;     // the row sees no key of this split
+    float* dstp = part + (((size_t)row * H + head) * nsplit + s) * (HD + 2);
+    dstp[c] = c < HD ? Os[qi][c] : (c == HD ? Ms[qi] : Ls[qi]);
+  }
+}
+
+template <typename T, int HD>
+__global__ void attn_combine_kernel(const float* __restrict__ part, int nsplit, int M, const int* __restrict__ nrows,
+                                    const int* __restrict__ pos, int H, T* __restrict__ out, int ldo,
+                                    const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int row = blockIdx.x, head = blockIdx.y, d = threadIdx.x;
+  if (row >= active_rows(M, nrows)) return;
+  const int ns = pos[row] / ATT_SPLIT + 1;
+  const float* pr = part + ((size_t)row * H + head) * nsplit * (HD + 2);
+  float m = -INFINITY;
+  for (int s = 0; s < ns; ++s) m = fmaxf(m, pr[s * (HD + 2) + HD]);
+  float l = 0.f, o = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = expf(pr[s * (HD + 2) + HD] - m);
+    l = fmaf(pr[s * (HD + 2) + HD + 1], w, l);
+    o = fmaf(pr[s * (HD + 2) + d], w, o);
+  }
+  st(out + (size_t)row * ldo + (size_t)head * HD + d, o / l);
+}
+
+int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer,
+                     int H, int KVH, const RowBlock& rb, int max_ctx, const void* local_kv,
+                     int local_start, int group_rows, float* part, void* out, int ldo, hipStream_t s) {
+  if (rb.M <= 0) return 0;
+  const int G = H / KVH;
+  int RB = ATT_MAXQ / G;
+  if (RB < 1) return SSD_ERR_SHAPE;
+  if (group_rows > 0) {
+    // a row block must not straddle two groups
+    while (RB > 1 && group_rows % RB != 0) --RB;
+  }
+  const int nsplit = (max_ctx + ATT_SPLIT - 1) / ATT_SPLIT;
+  const dim3 grid(KVH, nsplit, (rb.M + RB - 1) / RB);
+#define ATT_LAUNCH(T, HD)                                                                                        \
+  do {                                                                                                           \
+    hipLaunchKernelGGL((attn_partial_kernel<T, HD>), grid, dim3(256), 0, s, (const T*)q, ldq, (const T*)kv.pool, \
+                       kv.page_table, kv.page_size, L, layer, H, KVH, rb.M, rb.nrows, rb.pos, RB, nsplit,        \
+                       (const T*)local_kv, local_start, group_rows, part, rb.stop);                              \
+    hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(rb.M, H), dim3(HD), 0, s, part, nsplit, rb.M, rb.nrows, \
+                       rb.pos, H, (T*)out, ldo, rb.stop);                                                        \
+  } while (0)
+  if (dtype == SSD_DTYPE_BF16) {
+    if (head_dim == 128) ATT_LAUNCH(bf16_t, 128); else ATT_LAUNCH(bf16_t, 64);
+  } else {
+    if (head_dim == 128) ATT_LAUNCH(float, 128); else ATT_LAUNCH(float, 64);
+  }
+#undef ATT_LAUNCH
+  return last_launch();
+}
+
+// ===========================================================================
+// Row statistics: max, argmax (lowest index), second max, log-sum-exp of z/T,
+// confidence and a draw.  One 1024-thread workgroup per row.
+// ===========================================================================
+
+struct Top2 { float v1; int i1; float v2; };
+
+__device__ __forceinline__ void top2_push(Top2& t, float v, int i) {
+  if (v > t.v1 || (v == t.v1 && i < t.i1)) { t.v2 = fmaxf(t.v2, t.v1); t.v1 = v; t.i1 = i; }
+  else t.v2 = fmaxf(t.v2, v);
+}
+
+__device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
+  Top2 r;
+  if (b.v1 > a.v1 || (b.v1 == a.v1 && b.i1 < a.i1)) { r.v1 = b.v1; r.i1 = b.i1; r.v2 = fmaxf(b.v2, a.v1); }
+  else { r.v1 = a.v1; r.i1 = a.i1; r.v2 = fmaxf(a.v2, b.v1); }
+  return r;
+}
+
+// Block-wide statistics of z[0..V).  All 1024 threads must call it.
+__device__ ssd_row_stat block_row_stats(const float* __restrict__ z, int V, float T, uint64_t seed, int iter,
+                                        int rowid, uint32_t purpose, bool* bad) {
+  __shared__ Top2 sh_t[16];
+  __shared__ float sh_f[16];
+  __shared__ int sh_i[16];
+  __shared__ Top2 sh_res;
+  __shared__ float sh_sum;
+  __shared__ int sh_bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) sh_bad = 0;
+  Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+  int nonfinite = 0;
+  for (int v = tid; v < V; v += 1024) {
+    const float zv = z[v];
+    if (!isfinite(zv)) nonfinite = 1;
+    top2_push(t, zv, v);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Top2 u{__shfl_xor(t.v1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.v2, o, 64)};
+    t = top2_merge(t, u);
+  }
+  __syncthreads();
+  if (nonfinite) sh_bad = 1;
+  if (lane == 0) sh_t[wave] = t;
+  __syncthreads();
+  if (tid == 0) {
+    Top2 r = sh_t[0];
+    for (int w = 1; w < 16; ++w) r = top2_merge(r, sh_t[w]);
+    sh_res = r;
+  }
+  __syncthreads();
+  const Top2 res = sh_res;
+  const float invT = T > 0.f ? 1.0f / T : 1.0f;
+  // sum exp((z - max) / T) and the race over z/T + Gumbel
+  float se = 0.f;
+  float kbest = -INFINITY;
+  int ibest = 0x7fffffff;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  for (int v4 = tid * 4; v4 < V; v4 += 4096) {
+    U4 w{0, 0, 0, 0};
+    if (T > 0.f) w = philox4x32_10((uint32_t)iter, (uint32_t)rowid, purpose, (uint32_t)(v4 >> 2), k0, k1);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = v4 + e;
+      if (v < V) {
+        const float zv = z[v];
+        se += expf((zv - res.v1) * invT);
+        if (T > 0.f) argmax_merge(kbest, ibest, zv / T + word_to_gumbel(ws[e]), v);
+      }
+    }
+  }
+  se = wave_sum(se);
+  wave_argmax(kbest, ibest);
+  if (lane == 0) { sh_f[wave] = se; sh_i[wave] = ibest; }
+  __shared__ float sh_k[16];
+  if (lane == 0) sh_k[wave] = kbest;
+  __syncthreads();
+  ssd_row_stat out;
+  if (tid == 0) {
+    float tot = 0.f;
+    for (int w = 0; w < 16; ++w) tot += sh_f[w];
+    float kb = sh_k[0];
+    int ib = sh_i[0];
+    for (int w = 1; w < 16; ++w) argmax_merge(kb, ib, sh_k[w], sh_i[w]);
+    sh_sum = tot;
+    sh_i[0] = ib;
+  }
+  __syncthreads();
+  out.max = res.v1;
+  out.argmax = res.i1;
+  out.max2 = res.v2;
+  out.lse = res.v1 * invT + logf(sh_sum);
+  out.conf = 1.0f / sh_sum;
+  out.sample = T > 0.f ? sh_i[0] : res.i1;
+  *bad = sh_bad != 0;
+  __syncthreads();
+  return out;
+}
+
+__global__ __launch_bounds__(1024) void row_stats_kernel(const float* __restrict__ z, int ldz, int V, float T,
+                                                         uint64_t seed, const int* iter_ptr, int iter_const,
+                                                         int rowid_base, uint32_t purpose,
+                                                         ssd_row_stat* __restrict__ out,
+                                                         const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int row = blockIdx.x;
+  const int iter = iter_ptr ? *iter_ptr : iter_const;
+  bool bad;
+  ssd_row_stat r = block_row_stats(z + (size_t)row * ldz, V, T, seed, iter, rowid_base + row, purpose, &bad);
+  if (threadIdx.x == 0) out[row] = r;
+}
+
+int launch_row_stats(const float* z, int ldz, int rows, int V, float T, uint64_t seed, const int* iter_ptr,
+                     int iter_const, int rowid_base, uint32_t purpose, ssd_row_stat* out, const int* stop,
+                     hipStream_t s) {
+  if (rows <= 0) return 0;
+  hipLaunchKernelGGL(row_stats_kernel, dim3(rows), dim3(1024), 0, s, z, ldz, V, T, seed, iter_ptr, iter_const,
+                     rowid_base, purpose, out, stop);
+  return last_launch();
+}
+
+// Draft step j: the draft token y_j, and the confidence stop.
+__global__ __launch_bounds__(1024) void draft_stats_kernel(const float* __restrict__ z, int V, float T,
+                                                           uint64_t seed, DevState* st, int j, int d, float tau,
+                                                           int32_t* __restrict__ draft_tokens,
+                                                           int32_t* __restrict__ n_drafted_out) {
+  if (st->stop) return;
+  bool bad;
+  ssd_row_stat r = block_row_stats(z, V, T, seed, st->iteration, j - 1, PURPOSE_DRAFT, &bad);
+  if (threadIdx.x == 0) {
+    draft_tokens[j - 1] = r.sample;
+    if (bad) atomicOr(&st->error_flags, ERRF_NUMERIC);
+    if (r.conf < tau || j == d) {
+      st->stop = 1;
+      st->n_drafted = j;
+      *n_drafted_out = j;
+    }
+  }
+}
+
+int launch_draft_stats(const float* z, int V, float T, uint64_t seed, DevState* st, int j, int d, float tau,
+                       int32_t* draft_tokens, int32_t* n_drafted_out, hipStream_t s) {
+  hipLaunchKernelGGL(draft_stats_kernel, dim3(1), dim3(1024), 0, s, z, V, T, seed, st, j, d, tau, draft_tokens,
+                     n_drafted_out);
+  return last_launch();
+}
+
+// ===========================================================================
+// Accept / reject.  One workgroup per verify row i = 0..d' computes its
+// decision and its correction (or, for i = d', the bonus); a one-wave kernel
+// then scans the decisions in order.
+// ===========================================================================
+
+__device__ float block_sum_1024(float v) {
+  __shared__ float sh[16];
+  __shared__ float tot;
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < 16; ++w) t += sh[w];
+    tot = t;
+  }
+  __syncthreads();
+  const float r = tot;
+  __syncthreads();
+  return r;
+}
+
+__device__ int block_argmax_1024(float v, int i) {
+  __shared__ float shv[16];
+  __shared__ int shi[16];
+  __shared__ int res;
+  wave_argmax(v, i);
+  if ((threadIdx.x & 63) == 0) { shv[threadIdx.x >> 6] = v; shi[threadIdx.x >> 6] = i; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float bv = shv[0];
+    int bi = shi[0];
+    for (int w = 1; w < 16; ++w) argmax_merge(bv, bi, shv[w], shi[w]);
+    res = bi;
+  }
+  __syncthreads();
+  const int r = res;
+  __syncthreads();
+  return r;
+}
+
+__device__ float block_max_1024(float v) {
+  __shared__ float sh[16];
+  __shared__ float tot;
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = sh[0];
+    for (int w = 1; w < 16; ++w) t = fmaxf(t, sh[w]);
+    tot = t;
+  }
+  __syncthreads();
+  const float r = tot;
+  __syncthreads();
+  return r;
+}
+
+// log-sum-exp of z/T over the row (T > 0)
+__device__ float block_lse(const float* z, int V, float T) {
+  float m = -INFINITY;
+  for (int v = threadIdx.x; v < V; v += 1024) m = fmaxf(m, z[v]);
+  m = block_max_1024(m);
+  float se = 0.f;
+  for (int v = threadIdx.x; v < V; v += 1024) se += expf((z[v] - m) / T);
+  se = block_sum_1024(se);
+  return m / T + logf(se);
+}
+
+__global__ __launch_bounds__(1024) void accept_rows_kernel(const float* __restrict__ zp, const float* __restrict__ zq,
+                                                           int V, const int32_t* __restrict__ drafts,
+                                                           const int32_t* __restrict__ n_drafted, float T,
+                                                           uint64_t seed, const DevState* __restrict__ st,
+                                                           int* __restrict__ dec, int* __restrict__ corr) {
+  const int i = blockIdx.x;
+  const int dp = *n_drafted;
+  if (i > dp) return;
+  const float* p = zp + (size_t)i * V;
+  const int tid = threadIdx.x;
+  if (T == 0.f) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int v = tid; v < V; v += 1024) argmax_merge(bv, bi, p[v], v);
+    const int am = block_argmax_1024(bv, bi);
+    if (tid == 0) { corr[i] = am; dec[i] = (i < dp) && (am == drafts[i]); }
+    return;
+  }
+  const int iter = st->iteration;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const float lse_p = block_lse(p, V, T);
+  float kbest = -INFINITY;
+  int ibest = 0x7fffffff;
+  if (i == dp) {
+    // bonus: a draw from p_{d'+1}
+    for (int v4 = tid * 4; v4 < V; v4 += 4096) {
+      const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)i, PURPOSE_SAMPLE, (uint32_t)(v4 >> 2), k0, k1);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      for (int e = 0; e < 4; ++e)
+        if (v4 + e < V) argmax_merge(kbest, ibest, p[v4 + e] / T + word_to_gumbel(ws[e]), v4 + e);
+    }
+    const int b = block_argmax_1024(kbest, ibest);
+    if (tid == 0) { corr[i] = b; dec[i] = 0; }
+    return;
+  }
+  const float* q = zq + (size_t)i * V;
+  const float lse_q = block_lse(q, V, T);
+  // residual norm(max(0, p - q)) as a race over log(r) + Gumbel
+  int any_pos = 0;
+  for (int v4 = tid * 4; v4 < V; v4 += 4096) {
+    const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)i, PURPOSE_SAMPLE, (uint32_t)(v4 >> 2), k0, k1);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    for (int e = 0; e < 4; ++e) {
+      const int v = v4 + e;
+      if (v < V) {
+        const float r = expf(p[v] / T - lse_p) - expf(q[v] / T - lse_q);
+        if (r > 0.f) { any_pos = 1; argmax_merge(kbest, ibest, logf(r) + word_to_gumbel(ws[e]), v); }
+      }
+    }
+  }
+  const int anyp = block_sum_1024((float)any_pos) > 0.f;
+  int c;
+  if (anyp) {
+    c = block_argmax_1024(kbest, ibest);
+  } else {
+    kbest = -INFINITY; ibest = 0x7fffffff;
+    for (int v4 = tid * 4; v4 < V; v4 += 4096) {
+      const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)i, PURPOSE_SAMPLE, (uint32_t)(v4 >> 2), k0, k1);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      for (int e = 0; e < 4; ++e)
+        if (v4 + e < V) argmax_merge(kbest, ibest, (p[v4 + e] / T - lse_p) + word_to_gumbel(ws[e]), v4 + e);
+    }
+    c = block_argmax_1024(kbest, ibest);
+  }
+  if (tid == 0) {
+    const int y = drafts[i];
+    const float lp = p[y] / T - lse_p;
+    const float lq = q[y] / T - lse_q;
+    const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)i, PURPOSE_ACCEPT, 0u, k0, k1);
+    const float u = word_to_uniform(w.x);
+    dec[i] = (logf(u) + lq) < lp;
+    corr[i] = c;
+  }
+}
+
+__global__ void accept_emit_kernel(const int32_t* __restrict__ drafts, const int32_t* __restrict__ n_drafted,
+                                   const int* __restrict__ dec, const int* __restrict__ corr,
+                                   int32_t* __restrict__ out, int32_t* __restrict__ n_out) {
+  if (threadIdx.x != 0) return;
+  const int dp = *n_drafted;
+  int k = 0;
+  while (k < dp && dec[k]) { out[k] = drafts[k]; ++k; }
+  out[k] = corr[k];
+  *n_out = k + 1;
+}
+
+int launch_accept(const float* zp, const float* zq, int V, const int32_t* drafts, const int32_t* n_drafted, int d,
+                  float T, uint64_t seed, const DevState* st, int* dec, int* corr, int32_t* out_tokens,
+                  int32_t* n_out, hipStream_t s) {
+  hipLaunchKernelGGL(accept_rows_kernel, dim3(d + 1), dim3(1024), 0, s, zp, zq, V, drafts, n_drafted, T, seed, st,
+                     dec, corr);
+  hipLaunchKernelGGL(accept_emit_kernel, dim3(1), dim3(64), 0, s, drafts, n_drafted, dec, corr, out_tokens, n_out);
+  return last_launch();
+}
+
+// ===========================================================================
+// Commit and control kernels (single wave).
+// ===========================================================================
+
+__global__ void commit_kernel(DevState* st, const int32_t* __restrict__ out_tokens, const int32_t* __restrict__ n_out,
+                              int32_t* __restrict__ log, int log_cap) {
+  if (threadIdx.x != 0) return;
+  const int n = *n_out;
+  for (int t = 0; t < n; ++t) {
+    const int idx = st->n_out + t;
+    if (idx < log_cap) log[idx] = out_tokens[t];
+    else st->error_flags |= ERRF_CAPACITY;
+  }
+  st->n_out += n;
+  st->kvlen += n;
+  st->last_token = out_tokens[n - 1];
+  st->iteration += 1;
+  st->n_emitted = n;
+}
+
+int launch_commit(DevState* st, const int32_t* out_tokens, const int32_t* n_out, int32_t* log, int log_cap,
+                  hipStream_t s) {
+  hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, s, st, out_tokens, n_out, log, log_cap);
+  return last_launch();
+}
+
+__global__ void pick_commit_kernel(const ssd_row_stat* __restrict__ stat, DevState* st, int32_t* __restrict__ log,
+                                   int log_cap, int set_kvlen, int kvlen_value) {
+  if (threadIdx.x != 0) return;
+  const int tok = stat->sample;
+  if (!isfinite(stat->max) || !isfinite(stat->lse)) st->error_flags |= ERRF_NUMERIC;
+  if (st->n_out < log_cap) log[st->n_out] = tok;
+  else st->error_flags |= ERRF_CAPACITY;
+  st->n_out += 1;
+  st->kvlen = set_kvlen ? kvlen_value : st->kvlen + 1;
+  st->last_token = tok;
+  st->iteration += 1;
+  st->n_emitted = 1;
+}
+
+int launch_pick_commit(const ssd_row_stat* stat, DevState* st, int32_t* log, int log_cap, int set_kvlen,
+                       int kvlen_value, hipStream_t s) {
+  hipLaunchKernelGGL(pick_commit_kernel, dim3(1), dim3(64), 0, s, stat, st, log, log_cap, set_kvlen, kvlen_value);
+  return last_launch();
+}
+
+__global__ void state_init_kernel(DevState* st) {
+  if (threadIdx.x == 0) {
+    st->kvlen = 0; st->last_token = 0; st->iteration = 0; st->n_out = 0; st->error_flags = 0;
+    st->n_drafted = 0; st->stop = 0; st->n_emitted = 0; st->verify_rows = 0;
+  }
+}
+
+int launch_state_init(DevState* st, hipStream_t s) {
+  hipLaunchKernelGGL(state_init_kernel, dim3(1), dim3(64), 0, s, st);
+  return last_launch();
+}
+
+__global__ void fill_positions_kernel(int* pos, int M, int start) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < M) pos[i] = start + i;
+}
+
+int launch_fill_positions(int* pos, int M, int start, hipStream_t s) {
+  hipLaunchKernelGGL(fill_positions_kernel, dim3((M + 255) / 256), dim3(256), 0, s, pos, M, start);
+  return last_launch();
+}
+
+// Scoring rows j = c * gamma + i: token window[i] at position pos0 + i.
+__global__ void window_rows_kernel(const int32_t* __restrict__ window, int R, int gamma, int pos0, int* pos,
+                                   int* tok) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < R) { pos[j] = pos0 + j % gamma; tok[j] = window[j % gamma]; }
+}
+
+int launch_window_rows(const int32_t* window, int R, int gamma, int pos0, int* pos, int* tok, hipStream_t s) {
+  hipLaunchKernelGGL(window_rows_kernel, dim3((R + 255) / 256), dim3(256), 0, s, window, R, gamma, pos0, pos, tok);
+  return last_launch();
+}
+
+// AR step: the newest token at position kvlen.
+__global__ void single_row_prep_kernel(DevState* st, int* pos1, int* tok1, int max_ctx) {
+  if (threadIdx.x != 0) return;
+  const int p = st->kvlen;
+  if (p >= max_ctx) st->error_flags |= ERRF_CAPACITY;
+  pos1[0] = min(p, max_ctx - 1);
+  tok1[0] = st->last_token;
+}
+
+int launch_single_row_prep(DevState* st, int* pos1, int* tok1, int max_ctx, hipStream_t s) {
+  hipLaunchKernelGGL(single_row_prep_kernel, dim3(1), dim3(64), 0, s, st, pos1, tok1, max_ctx);
+  return last_launch();
+}
+
+__global__ void draft_begin_kernel(DevState* st) {
+  if (threadIdx.x == 0) { st->stop = 0; st->n_drafted = 0; }
+}
+
+int launch_draft_begin(DevState* st, hipStream_t s) {
+  hipLaunchKernelGGL(draft_begin_kernel, dim3(1), dim3(64), 0, s, st);
+  return last_launch();
+}
+
+// Draft step j feeds y_{j-1} at position kvlen + j - 1.
+__global__ void draft_step_prep_kernel(DevState* st, const int32_t* __restrict__ drafts, int j, int* pos1,
+                                       int* tok1, int max_ctx, int32_t* __restrict__ n_drafted_out) {
+  if (threadIdx.x != 0 || st->stop) return;
+  const int p = st->kvlen + j - 1;
+  if (p + 1 >= max_ctx) {
+    // out of KV pages: end the draft (verify needs position kvlen + d' too)
+    st->error_flags |= ERRF_CAPACITY;
+    st->stop = 1;
+    st->n_drafted = max(j - 1, 0);
+    *n_drafted_out = max(j - 1, 0);
+    return;
+  }
+  pos1[0] = p;
+  tok1[0] = j == 1 ? st->last_token : drafts[j - 2];
+}
+
+int launch_draft_step_prep(DevState* st, const int32_t* drafts, int j, int* pos1, int* tok1, int max_ctx,
+                           int32_t* n_drafted_out, hipStream_t s) {
+  hipLaunchKernelGGL(draft_step_prep_kernel, dim3(1), dim3(64), 0, s, st, drafts, j, pos1, tok1, max_ctx,
+                     n_drafted_out);
+  return last_launch();
+}
+
+// Verify rows i = 0..d': tokens y_0..y_d' at positions kvlen + i; pos1/tok1 = the last row.
+__global__ void verify_prep_kernel(DevState* st, const int32_t* __restrict__ drafts,
+                                   const int32_t* __restrict__ n_drafted, int d, int* vpos, int* vtok, int* pos1,
+                                   int* tok1, int max_ctx) {
+  const int i = threadIdx.x;
+  const int dp = min(*n_drafted, d);
+  const int kv = st->kvlen;
+  if (i <= d) {
+    const int p = min(kv + i, max_ctx - 1);
+    vpos[i] = p;
+    vtok[i] = i == 0 ? st->last_token : drafts[i - 1];
+  }
+  __syncthreads();
+  if (i == 0) {
+    if (kv + dp >= max_ctx) st->error_flags |= ERRF_CAPACITY;
+    st->verify_rows = dp + 1;
+    pos1[0] = vpos[dp];
+    tok1[0] = vtok[dp];
+  }
+}
+
+int launch_verify_prep(DevState* st, const int32_t* drafts, const int32_t* n_drafted, int d, int* vpos, int* vtok,
+                       int* pos1, int* tok1, int max_ctx, hipStream_t s) {
+  hipLaunchKernelGGL(verify_prep_kernel, dim3(1), dim3(64), 0, s, st, drafts, n_drafted, d, vpos, vtok, pos1, tok1,
+                     max_ctx);
+  return last_launch();
+}
+
+__global__ void copy_rows_kernel(const float* __restrict__ src, float* __restrict__ dst, int rows, int D,
+                                 const int* __restrict__ count, const int* __restrict__ dst_off,
+                                 const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int r = blockIdx.x;
+  const int n = count ? min(rows, *count) : rows;
+  if (r >= n) return;
+  const int off = dst_off ? *dst_off : 0;
+  for (int i = threadIdx.x; i < D; i += 256) dst[(size_t)(r + off) * D + i] = src[(size_t)r * D + i];
+}
+
+int launch_copy_rows(const float* src, float* dst, int rows, int D, const int* count, const int* dst_off,
+                     const int* stop, hipStream_t s) {
+  if (rows <= 0) return 0;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(rows), dim3(256), 0, s, src, dst, rows, D, count, dst_off, stop);
+  return last_launch();
+}
+
+// Matchness: per candidate the fraction of rows whose argmax equals the next
+// window token; best = highest score, lowest index on ties.
+__global__ void score_kernel(const ssd_row_stat* __restrict__ stats, const int32_t* __restrict__ window,
+                             int n_masks, int gamma, float* __restrict__ scores, int32_t* __restrict__ best) {
+  __shared__ int hits[1024];
+  const int c = threadIdx.x;
+  if (c < n_masks) {
+    int h = 0;
+    for (int i = 0; i < gamma; ++i) h += stats[c * gamma + i].argmax == window[i + 1];
+    hits[c] = h;
+    scores[c] = (float)h / (float)gamma;
+  }
+  __syncthreads();
+  if (c == 0) {
+    int b = 0;
+    for (int k = 1; k < n_masks; ++k)
+      if (hits[k] > hits[b]) b = k;
+    *best = b;
+  }
+}
+
+int launch_score(const ssd_row_stat* stats, const int32_t* window, int n_masks, int gamma, float* scores,
+                 int32_t* best, hipStream_t s) {
+  if (n_masks > 1024) return SSD_ERR_CAPACITY;
+  hipLaunchKernelGGL(score_kernel, dim3(1), dim3(1024), 0, s, stats, window, n_masks, gamma, scores, best);
+  return last_launch();
+}
+
+}  // namespace ssd

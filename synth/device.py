@@ -1,0 +1,39 @@
+"""Device copies of the synthetic model, in the layout the C ABI takes.
+
+Layout only (no arithmetic of the method): w_qkv stacks Wq, Wk, Wv row blocks;
+w_gate_up stacks Wgate then Wup; norm gains are ones (float32).
+"""
+import torch
+
+from . import KIND_WDOWN, KIND_WGATE, KIND_WK, KIND_WO, KIND_WQ, KIND_WUP, KIND_WV, TID_EMBED, TID_LM_HEAD
+from . import SEED_WEIGHTS, layer_tid, weight_dev
+
+
+def build_weights(shape, seed=SEED_WEIGHTS, device="cuda", n_layers=None):
+    dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    D, F = shape.d_model, shape.ffn_dim
+    qd, kd = shape.q_dim, shape.kv_dim
+
+    def fill_rows(t, row0, rows, tid):
+        weight_dev(t.view(-1)[row0 * t.shape[1]:(row0 + rows) * t.shape[1]], tid, seed=seed)
+
+    layers = []
+    for l in range(shape.n_layers if n_layers is None else n_layers):
+        wqkv = torch.empty(qd + 2 * kd, D, dtype=dt, device=device)
+        fill_rows(wqkv, 0, qd, layer_tid(l, KIND_WQ))
+        fill_rows(wqkv, qd, kd, layer_tid(l, KIND_WK))
+        fill_rows(wqkv, qd + kd, kd, layer_tid(l, KIND_WV))
+        wo = weight_dev(torch.empty(D, qd, dtype=dt, device=device), layer_tid(l, KIND_WO), seed=seed)
+        wgu = torch.empty(2 * F, D, dtype=dt, device=device)
+        fill_rows(wgu, 0, F, layer_tid(l, KIND_WGATE))
+        fill_rows(wgu, F, F, layer_tid(l, KIND_WUP))
+        wd = weight_dev(torch.empty(D, F, dtype=dt, device=device), layer_tid(l, KIND_WDOWN), seed=seed)
+        layers.append({"attn_norm": torch.ones(D, dtype=torch.float32, device=device), "w_qkv": wqkv, "w_o": wo,
+                       "mlp_norm": torch.ones(D, dtype=torch.float32, device=device), "w_gate_up": wgu,
+                       "w_down": wd})
+    return {
+        "embed": weight_dev(torch.empty(shape.vocab, D, dtype=dt, device=device), TID_EMBED, seed=seed),
+        "lm_head": weight_dev(torch.empty(shape.vocab, D, dtype=dt, device=device), TID_LM_HEAD, seed=seed),
+        "final_norm": torch.ones(D, dtype=torch.float32, device=device),
+        "layers": layers,
+    }

@@ -1,0 +1,286 @@
+"""GPU path (through the C ABI) against the CPU oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from self_speculative_layer_amd import binding as B
+from oracle import model as omodel
+from oracle import philox as ophilox
+from oracle import ssd as ossd
+
+from gpu_util import (BF16_HD64, BF16_HD128, F32_GQA, check_greedy_tokens, dev, gpu_model, logit_tol,
+                      oracle_ar_with_logits)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [synth.TINY, F32_GQA, BF16_HD64, BF16_HD128]
+
+
+@pytest.fixture(scope="module", params=SHAPES, ids=lambda s: s.name)
+def pair(request):
+    shape = request.param
+    print("[gpu] building %s" % shape.name, flush=True)
+    g = gpu_model(shape)
+    o = omodel.Model.synthetic(shape)
+    yield shape, g, o
+    g.close()
+
+
+def test_device_weights_equal_host_weights(pair):
+    shape, g, o = pair
+    t = g.tensors
+    emb = t["embed"].float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(emb, o.embed)
+    wqkv = t["layers"][1]["w_qkv"].float().cpu().numpy()
+    assert np.array_equal(wqkv[shape.q_dim: shape.q_dim + shape.kv_dim], o.layers[1].wk)
+    wgu = t["layers"][0]["w_gate_up"].float().cpu().numpy()
+    assert np.array_equal(wgu[shape.ffn_dim:], o.layers[0].wup)
+
+
+def test_prefill_logits(pair):
+    shape, g, o = pair
+    P = 300 if shape.dtype == "bf16" else 40          # bf16: spans two 256-key attention splits
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    # a non-identity page table: logical page i in physical page (3 i + 1) mod n
+    n_lp = (P + 64 + 63) // 64
+    pt = [(3 * i + 1) % (n_lp + 1) for i in range(n_lp)]
+    seq = B.Sequence(g, max_ctx=n_lp * 64, max_rows=64, max_draft=4, page_table=pt)
+    lg = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
+    B.ssd_prefill(seq.handle, dev(prompt), 0.0, 0, lg)
+    st = B.ssd_read_state(seq.handle)
+    assert st.kvlen == P and st.n_out == 1 and st.iteration == 1
+    z = ossd.prefill(o, omodel.KVCache(shape, P + 1), prompt)
+    err = np.abs(lg.cpu().numpy() - z).max()
+    print("prefill max |dz| = %.3g" % err)
+    assert err < logit_tol(shape)
+    seq.close()
+
+
+PLANS = {
+    "tiny-f32": dict(skip_mask=synth.mask_from_layers(4, [2]), d=4),
+    "f32-gqa": dict(exit_layer=1, d=3),
+    "bf16-hd64-gqa": dict(skip_mask=synth.mask_from_layers(4, [1, 3]), d=5),
+    "bf16-hd128": dict(exit_layer=1, d=6),
+}
+
+
+def _mask_of(shape, plan):
+    if plan.get("skip_mask") is not None:
+        return plan["skip_mask"]
+    return synth.mask_exit(shape.n_layers, plan["exit_layer"])
+
+
+def test_greedy_ssd_matches_oracle_and_ar(pair):
+    """GPU SSD tokens == oracle AR tokens (margin rule) and == GPU AR tokens."""
+    shape, g, o = pair
+    plan = PLANS[shape.name]
+    P, n_gen = 32, 48
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    ref, ref_z = oracle_ar_with_logits(o, prompt, n_gen)
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * plan["d"] + 8, max_rows=64, max_draft=8)
+    out, stats = seq.generate_ssd(dev(prompt), n_gen, skip_mask=plan.get("skip_mask"),
+                                  exit_layer=plan.get("exit_layer"), d=plan["d"])
+    print("iterations %d, mean emitted %.2f" % (len(stats), np.mean([e for _, e in stats])))
+    assert all(1 <= e <= dp + 1 for dp, e in stats)
+    check_greedy_tokens(out, ref, ref_z)
+    ar = seq.generate_ar(dev(prompt), n_gen)
+    assert [int(x) for x in ar] == [int(x) for x in out]
+    seq.close()
+
+
+def test_verify_logits_match_oracle_per_iteration(pair):
+    """Each iteration's verify logits (rows 0..d') against the oracle's verify."""
+    shape, g, o = pair
+    plan = PLANS[shape.name]
+    mask = _mask_of(shape, plan)
+    d = plan["d"]
+    P, n_gen = 24, 30
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    records = []
+    ossd.ssd_generate(o, prompt, n_gen, mask, d,
+                      on_iteration=lambda it, n, dr, zq, zp, em, kv: records.append((list(dr), zq, zp, em)))
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=64, max_draft=8)
+    B.ssd_prefill(seq.handle, dev(prompt))
+    V = shape.vocab
+    worst = 0.0
+    compared = 0
+    for dr, zq, zp, em in records:
+        seq.ssd_iteration(plan.get("skip_mask"), plan.get("exit_layer"), d)
+        st = B.ssd_read_state(seq.handle)
+        dp = st.last_n_drafted
+        gd = seq.draft_tokens[:dp].cpu().numpy().tolist()
+        if gd != dr:
+            break          # a near-tie changed the path; later states are not comparable
+        gz = seq.verify_logits[: (dp + 1) * V].view(dp + 1, V).cpu().numpy()
+        gq = seq.draft_logits[: dp * V].view(dp, V).cpu().numpy()
+        worst = max(worst, np.abs(gz - zp).max(), np.abs(gq - zq).max())
+        compared += 1
+        ge = seq.out_tokens[: st.last_n_emitted].cpu().numpy().tolist()
+        if ge != em:
+            break
+    print("worst |dz| over %d of %d iterations %.3g" % (compared, len(records), worst))
+    assert compared >= min(3, len(records))
+    assert worst < logit_tol(shape)
+    seq.close()
+
+
+def test_reuse_equals_no_reuse(pair):
+    """verify with the draft's saved state == verify recomputing every row, bitwise."""
+    shape, g, o = pair
+    plan = PLANS[shape.name]
+    d = plan["d"]
+    P = 20
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    outs = []
+    for reuse in (True, False):
+        seq = B.Sequence(g, max_ctx=P + 4 * d + 8, max_rows=64, max_draft=8)
+        B.ssd_prefill(seq.handle, dev(prompt))
+        B.ssd_draft(seq.handle, plan.get("skip_mask"), plan.get("exit_layer"), d, 0.0, 0.0, 0, seq.draft_tokens,
+                    seq.draft_logits, seq.n_drafted)
+        B.ssd_verify(seq.handle, plan.get("skip_mask"), plan.get("exit_layer"), d, seq.draft_tokens, seq.n_drafted,
+                     reuse, seq.verify_logits)
+        torch.cuda.synchronize()
+        outs.append(seq.verify_logits[: (d + 1) * shape.vocab].clone())
+        seq.close()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_empty_plan_accepts_everything(pair):
+    shape, g, o = pair
+    P, n_gen, d = 16, 30, 4
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=64, max_draft=8)
+    out, stats = seq.generate_ssd(dev(prompt), n_gen, skip_mask=np.zeros(2 * shape.n_layers, np.uint8), d=d)
+    assert all(e == dp + 1 for dp, e in stats)
+    seq.close()
+
+
+def test_sampled_ssd_matches_oracle(pair):
+    """T = 1 with a confidence stop: same Philox draws on both sides, so the emitted
+    tokens agree except at decisions within 1e-2 (log units) of flipping."""
+    shape, g, o = pair
+    plan = PLANS[shape.name]
+    mask = _mask_of(shape, plan)
+    d, tau, T, seed = plan["d"], 0.002, 1.0, 12345
+    P, n_gen = 24, 40
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    ref, ost, _ = ossd.ssd_generate(o, prompt, n_gen, mask, d, tau=tau, T=T, seed=seed)
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=64, max_draft=8)
+    out, stats = seq.generate_ssd(dev(prompt), n_gen, skip_mask=plan.get("skip_mask"),
+                                  exit_layer=plan.get("exit_layer"), d=d, conf_thresh=tau, temperature=T, seed=seed)
+    got = [int(x) for x in out]
+    n_match = next((i for i, (a, b) in enumerate(zip(got, ref)) if a != b), len(ref))
+    print("sampled: %d/%d tokens match before the first divergence; oracle drafted %s, gpu %s" %
+          (n_match, n_gen, ost["drafted"][:8], [s[0] for s in stats[:8]]))
+    assert n_match >= n_gen // 2
+    seq.close()
+
+
+def test_row_stats_match_oracle():
+    rng = np.random.default_rng(7)
+    V, rows = 32000, 6
+    z = (rng.standard_normal((rows, V)) * 2.0).astype(np.float32)
+    z[2, 77] = z[2].max() + 1.0
+    z[2, 78] = z[2, 77]                     # a tie: lowest index wins, margin 0
+    zt = dev(z.reshape(-1), torch.float32)
+    st = torch.zeros(rows * 6, dtype=torch.int32, device="cuda")
+    for T in (0.0, 0.7):
+        B.ssd_row_stats(zt, rows, V, T, 99, 5, st)
+        torch.cuda.synchronize()
+        raw = st.cpu().numpy()
+        fl = raw.view(np.float32).reshape(rows, 6)
+        it = raw.reshape(rows, 6)
+        for r in range(rows):
+            zz = z[r].astype(np.float64)
+            assert it[r, 1] == int(np.argmax(zz))
+            assert fl[r, 0] == z[r].max()
+            s = np.sort(zz)
+            assert fl[r, 2] == np.float32(s[-2])
+            lse = ossd.log_softmax(zz, T)
+            assert abs(fl[r, 3] - (np.max(zz / (T or 1.0)) - np.max(lse))) < 1e-4
+            assert abs(fl[r, 4] - ossd.confidence(zz, T)) < 1e-5
+            if T > 0:
+                assert it[r, 5] == ossd.sample_logits(zz, T, 99, 5, r, ophilox.PURPOSE_DRAFT)
+            else:
+                assert it[r, 5] == it[r, 1]
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0, 0.6])
+def test_accept_matches_oracle(T):
+    """ssd_accept on constructed verify/draft logits vs the oracle's accept rule."""
+    shape = BF16_HD64
+    g = gpu_model(shape, n_layers=1)
+    V, d = shape.vocab, 6
+    rng = np.random.default_rng(11)
+    seq = B.Sequence(g, max_ctx=128, max_rows=16, max_draft=8)
+    B.ssd_prefill(seq.handle, dev(synth.prompt_tokens(4, V)))     # iteration becomes 1
+    agree = 0
+    for trial in range(12):
+        zp = (rng.standard_normal((d + 1, V)) * 3).astype(np.float32)
+        zq = zp[:d] + (rng.standard_normal((d, V)) * 0.5).astype(np.float32)
+        drafts = [int(ossd.sample_logits(zq[i].astype(np.float64), T or 1.0, 5, trial, i, 0)) for i in range(d)]
+        if T == 0:
+            drafts = [int(np.argmax(zp[i])) if i < trial % (d + 1) else int(np.argmax(zq[i])) for i in range(d)]
+        dp = d - trial % 3
+        seq.verify_logits[: (d + 1) * V].copy_(dev(zp.reshape(-1), torch.float32))
+        seq.draft_logits[: d * V].copy_(dev(zq.reshape(-1), torch.float32))
+        seq.draft_tokens[:d].copy_(dev(drafts))
+        seq.n_drafted.fill_(dp)
+        B.ssd_accept(seq.handle, seq.verify_logits, seq.draft_logits, seq.draft_tokens, seq.n_drafted, d, T, 777,
+                     seq.out_tokens, seq.n_out)
+        torch.cuda.synchronize()
+        n = int(seq.n_out.item())
+        got = seq.out_tokens[:n].cpu().numpy().tolist()
+        if T == 0:
+            ref = ossd.accept_greedy(zp[: dp + 1].astype(np.float64), drafts[:dp])
+        else:
+            ref = ossd.accept_sampled(zp[: dp + 1].astype(np.float64), zq[:dp].astype(np.float64), drafts[:dp], T,
+                                      777, 1)
+        assert 1 <= n <= dp + 1
+        agree += got == ref
+    assert agree == 12
+    seq.close()
+    g.close()
+
+
+def test_score_masks_match_oracle():
+    shape = BF16_HD64
+    g = gpu_model(shape)
+    o = omodel.Model.synthetic(shape)
+    P, gamma = 40, 32
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    ref, kv = ossd.ar_generate(o, prompt, gamma)
+    window = (list(prompt) + ref)[P - 1: P + gamma]
+    masks = [np.zeros(8, np.uint8), synth.mask_from_layers(4, [1]), synth.mask_from_layers(4, [0, 2]),
+             synth.mask_exit(4, 2), np.array([0, 1, 1, 0, 0, 0, 0, 1], np.uint8)]
+    oscores, obest = ossd.score_masks(o, kv, window, P - 1, masks)
+    seq = B.Sequence(g, max_ctx=P + gamma + 64, max_rows=len(masks) * gamma, max_draft=4)
+    gout = seq.generate_ar(dev(prompt), gamma)
+    assert [int(x) for x in gout] == ref
+    scores = torch.zeros(len(masks), dtype=torch.float32, device="cuda")
+    best = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.ssd_score_masks(seq.handle, np.stack(masks), dev(window), P - 1, gamma, scores, best)
+    torch.cuda.synchronize()
+    gs = scores.cpu().numpy()
+    print("scores gpu %s oracle %s" % (gs, oscores))
+    assert gs[0] == 1.0
+    assert np.abs(gs - oscores).max() <= 2.0 / gamma
+    assert int(best.item()) == int(np.argmax(gs))
+    seq.close()
+    g.close()
+
+
+def test_capacity_is_reported_not_faulted():
+    shape = synth.TINY
+    g = gpu_model(shape)
+    P = 50
+    seq = B.Sequence(g, max_ctx=64, max_rows=64, max_draft=8)
+    B.ssd_prefill(seq.handle, dev(synth.prompt_tokens(P, shape.vocab)))
+    with pytest.raises(B.SSDError) as e:
+        for _ in range(10):
+            seq.ssd_iteration(None, 2, 8)
+            B.ssd_read_state(seq.handle)
+    assert e.value.code == B.SSD_ERR_CAPACITY
+    seq.close()
+    g.close()
