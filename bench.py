@@ -1,0 +1,264 @@
+"""Benchmark of the self-speculative decoding hot path on one MI355X.
+
+A step is one SSD iteration of the workload: draft (up to d tokens through the
+plan's sub-layers, shared final norm + LM head, confidence stop), one verify
+pass over the d'+1 rows, accept/reject, commit.  Inputs (weights, prompt, KV
+cache after the prefill) are resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7b|tiny|13b|70b|score13b]
+                    [--no-cpu-baseline]
+
+Prints one JSON line.  value = committed tokens per second over the K timed
+steps.  roofline = the dominant kernel (the gate/up projection with its fused
+SwiGLU epilogue, 44 % of the weight bytes of an iteration), timed live with HIP
+events around each of its launches in the timed region.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+WORKLOADS = {
+    "7b": dict(shape="llama2-7b-shape", prompt=512, n_gen=256, exit_layer=8, d=12, tau=0.0, T=0.0,
+               desc="LLaMA-2-7B-shaped bf16 decoder, LayerSkip early-exit draft E=8, d=12, greedy, "
+                    "512-token random prompt, 256 generated tokens, batch 1"),
+    "tiny": dict(shape="tiny-f32", prompt=32, n_gen=64, skip_layers=[2], d=4, tau=0.0, T=0.0,
+                 desc="tiny fp32 decoder (L4 D256 H4 F688 V1024), draft skips layer 2, d=4, greedy, "
+                      "32-token prompt, 64 tokens"),
+    "13b": dict(shape="llama2-13b-shape", prompt=1024, n_gen=256, random_skip=20, d=8, tau=0.8, T=1.0,
+                desc="LLaMA-2-13B-shaped bf16 decoder, SWIFT skip mask of 20 seeded layers, d<=8, confidence "
+                     "stop 0.8, T=1.0 sampling, 1024-token prompt, 256 tokens"),
+    "70b": dict(shape="llama2-70b-shape", prompt=4096, n_gen=128, random_skip=40, d=8, tau=0.0, T=0.0,
+                desc="LLaMA-2-70B-shaped bf16 decoder (GQA 64/8), SWIFT skip mask of 40 seeded layers, d=8, "
+                     "greedy, 4096-token prompt, 128 tokens"),
+}
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def plan_of(wl, shape):
+    import synth
+    if "exit_layer" in wl:
+        return None, wl["exit_layer"], synth.mask_exit(shape.n_layers, wl["exit_layer"])
+    if "skip_layers" in wl:
+        m = synth.mask_from_layers(shape.n_layers, wl["skip_layers"])
+        return m, None, m
+    layers = synth.random_skip_layers(shape.n_layers, wl["random_skip"], synth.SEED_MASKS, 0)
+    m = synth.mask_from_layers(shape.n_layers, layers)
+    return m, None, m
+
+
+def verify_bytes(shape, kvlen, rows, b):
+    """Algorithmic HBM bytes of one verify pass: every layer's weights once, the
+    LM head once, each layer's cached keys/values once, the new K/V written."""
+    elt = 2 if shape.dtype == "bf16" else 4
+    w = shape.n_layers * shape.layer_param_count() * elt + shape.vocab * shape.d_model * elt
+    kv_tok = 2 * shape.kv_dim * elt
+    kv = shape.n_layers * (kvlen + rows) * kv_tok + shape.n_layers * rows * kv_tok
+    return w + kv
+
+
+def cpu_baseline(shape, wl, mask, max_seconds=20.0):
+    """The oracle as it stands on a bounded sample: SSD iterations of the same
+    model after a 16-token prompt (weights float64 on the host)."""
+    import numpy as np
+    import synth
+    from oracle import model as omodel
+    from oracle import ssd as ossd
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    t0 = time.time()
+    om = omodel.Model.synthetic(shape)
+    log("oracle weights built in %.1fs" % (time.time() - t0))
+    P = 16
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    kv = omodel.KVCache(shape, P + 64 * (wl["d"] + 2))
+    out = [ossd.pick(ossd.prefill(om, kv, prompt), wl["T"], synth.SEED_SAMPLING, 0, 0, 2)]
+    b = omodel.first_skipped_layer(mask, shape.n_layers)
+    tokens, iters = 0, 0
+    t0 = time.time()
+    while True:
+        n = P + len(out)
+        drafts, zq, hb = ossd.draft(om, kv, out[-1], n, mask, wl["d"], wl["tau"], wl["T"], synth.SEED_SAMPLING,
+                                    iters + 1)
+        zp = ossd.verify(om, kv, out[-1], drafts, n, b, hb)
+        em = ossd.accept_greedy(zp, drafts) if wl["T"] == 0 else ossd.accept_sampled(zp, zq, drafts, wl["T"],
+                                                                                     synth.SEED_SAMPLING, iters + 1)
+        out.extend(em)
+        tokens += len(em)
+        iters += 1
+        if time.time() - t0 > max_seconds or iters >= 64:
+            break
+    dt = time.time() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d SSD iterations (%d committed tokens) of the same %s model and plan after a 16-token "
+                      "prompt, float64 NumPy oracle, %.1f s" % (iters, tokens, shape.name, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ar-steps", type=int, default=16)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4}))
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path runs a single sequence on one MI355X; "
+              "--gpus %d is not supported (multi-GPU sharding is described in DESIGN.md only)" % args.gpus)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import device as sdev
+    from self_speculative_layer_amd import binding as B
+
+    wl = WORKLOADS[args.workload]
+    shape = synth.SHAPES[wl["shape"]]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    tensors = sdev.build_weights(shape)
+    torch.cuda.synchronize()
+    log("weights on device in %.1fs (%.2f GB)" % (time.time() - t0, shape.param_count() * (2 if shape.dtype == "bf16" else 4) / 1e9))
+    model = B.Model(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
+                    shape.vocab, shape.dtype, tensors)
+    skip_mask, exit_layer, mask = plan_of(wl, shape)
+    d = wl["d"]
+    K, W = args.steps, args.warmup
+    max_ctx = wl["prompt"] + (K + W + 2) * (d + 1) + 64
+    seq = B.Sequence(model, max_ctx=max_ctx, max_rows=512, max_draft=max(d, 1), device=dev)
+    prompt = torch.from_numpy(synth.prompt_tokens(wl["prompt"], shape.vocab)).to(dev)
+    seed = synth.SEED_SAMPLING
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    B.ssd_prefill(seq.handle, prompt, wl["T"], seed)
+    ev1.record()
+    torch.cuda.synchronize()
+    prefill_ms = ev0.elapsed_time(ev1)
+    log("prefill %d tokens: %.1f ms" % (wl["prompt"], prefill_ms))
+
+    def iteration(vev=None):
+        h = seq.handle
+        B.ssd_draft(h, skip_mask, exit_layer, d, wl["tau"], wl["T"], seed, seq.draft_tokens, seq.draft_logits,
+                    seq.n_drafted)
+        if vev is not None:
+            vev[0].record()
+        B.ssd_verify(h, skip_mask, exit_layer, d, seq.draft_tokens, seq.n_drafted, True, seq.verify_logits)
+        if vev is not None:
+            vev[1].record()
+        B.ssd_accept(h, seq.verify_logits, seq.draft_logits, seq.draft_tokens, seq.n_drafted, d, wl["T"], seed,
+                     seq.out_tokens, seq.n_out)
+        B.ssd_commit(h, seq.out_tokens, seq.n_out)
+
+    for _ in range(W):
+        iteration()
+    st0 = B.ssd_read_state(seq.handle)
+    vevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    per_iter_swiglu = d * shape.n_layers + shape.n_layers
+    B.ssd_profile_enable(B.SSD_PROF_GEMM_SWIGLU, K * per_iter_swiglu + 8)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record()
+    for k in range(K):
+        iteration(vevs[k])
+    ev1.record()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    B.ssd_profile_disable()
+    st1 = B.ssd_read_state(seq.handle)
+    elapsed_ms = ev0.elapsed_time(ev1)
+    wall_ms = (t_end - t_start) * 1e3
+    tokens = st1.n_out - st0.n_out
+    value = tokens / (elapsed_ms / 1e3)
+    prof_ms, prof_n, prof_bytes = B.ssd_profile_read()
+    verify_ms = [a.elapsed_time(b) for a, b in vevs]
+    # context during the timed steps (for the verify byte count): its mean kvlen
+    kv_mid = (st0.kvlen + st1.kvlen) / 2.0
+    b = int(np.argmax(mask.reshape(-1, 2).any(axis=1))) if mask.any() else shape.n_layers
+    vb = verify_bytes(shape, kv_mid, d + 1, b)
+    vmed = float(np.median(verify_ms))
+    log("timed %d steps: %.1f ms (wall %.1f ms), %d tokens -> %.1f tok/s; verify median %.3f ms" %
+        (K, elapsed_ms, wall_ms, tokens, value, vmed))
+    achieved = prof_bytes / (prof_ms / 1e3) / 1e9 if prof_ms > 0 else 0.0
+
+    # same-kernel AR decode baseline
+    ar_tps = None
+    if args.ar_steps > 0:
+        seq2 = B.Sequence(model, max_ctx=wl["prompt"] + args.ar_steps + 64, max_rows=512, max_draft=1, device=dev)
+        B.ssd_prefill(seq2.handle, prompt, wl["T"], seed)
+        for _ in range(2):
+            B.ssd_decode_ar(seq2.handle, wl["T"], seed)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.ar_steps):
+            B.ssd_decode_ar(seq2.handle, wl["T"], seed)
+        ev1.record()
+        torch.cuda.synchronize()
+        ar_tps = args.ar_steps / (ev0.elapsed_time(ev1) / 1e3)
+        seq2.close()
+
+    result = {
+        "metric": "accepted tokens/s (batch 1) + verify-pass HBM GB/s vs MI355X peak",
+        "value": round(value, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded random-init weights and uniform random prompt)",
+        "config": {"workload": wl["desc"], "prompt_len": wl["prompt"], "d": d, "conf_thresh": wl["tau"],
+                   "temperature": wl["T"], "batch": 1, "step": "one SSD iteration (draft + verify + accept + commit)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "gemm_bf16_rows16<EPI_SWIGLU> (gate/up projection + SwiGLU)",
+                     "launches": prof_n, "avg_launch_us": round(prof_ms / max(prof_n, 1) * 1e3, 3),
+                     "bytes_per_launch": round(prof_bytes / max(prof_n, 1))},
+        "verify": {"median_ms": round(vmed, 4), "algorithmic_GB": round(vb / 1e9, 4),
+                   "GBps": round(vb / (vmed / 1e3) / 1e9, 1),
+                   "frac_of_peak": round(vb / (vmed / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "mean_tokens_per_step": round(tokens / K, 4),
+        "ar_tokens_per_s": None if ar_tps is None else round(ar_tps, 3),
+        "prefill_ms": round(prefill_ms, 2),
+        "wall_ms_timed": round(wall_ms, 2),
+    }
+    seq.close()
+    model.close()
+    del tensors
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(shape, wl, mask)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

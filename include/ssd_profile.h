@@ -1,0 +1,39 @@
+/*
+ * ssd_profile.h — kernel-timing hooks of libssd.so, for measurement.
+ *
+ * While a kernel class is enabled, the library records a HIP event on the
+ * launch stream immediately before and after each launch of that class (up to
+ * max_launches launches), and accumulates the algorithmic bytes each launch
+ * must move (weights + activations read + results written, each once).
+ * ssd_profile_read waits for the recorded events and returns the summed
+ * durations.  Process-wide; not thread-safe; events are created by
+ * ssd_profile_enable (host-side objects, no device memory).
+ */
+#ifndef SSD_PROFILE_H
+#define SSD_PROFILE_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_profile_class {
+  SSD_PROF_GEMM_STORE = 0,   /* linear layers with a plain store epilogue (QKV, LM head) */
+  SSD_PROF_GEMM_RESID = 1,   /* linear layers adding into the residual stream (O, down) */
+  SSD_PROF_GEMM_SWIGLU = 2   /* gate/up projection with the fused SwiGLU epilogue */
+} ssd_profile_class;
+
+/* Start recording launches of `kernel_class` (discarding earlier records).
+ * Returns 0, SSD_ERR_ARG (-1) or SSD_ERR_HIP (-4). */
+int ssd_profile_enable(int kernel_class, int max_launches);
+
+/* Stop recording (records are kept for ssd_profile_read). */
+int ssd_profile_disable(void);
+
+/* Synchronises the recorded events.  *total_ms = sum of launch durations,
+ * *n_launches = launches recorded, *total_bytes = their algorithmic bytes. */
+int ssd_profile_read(double* total_ms, int* n_launches, double* total_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

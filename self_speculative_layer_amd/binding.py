@@ -15,7 +15,8 @@ ERROR_NAMES = {-1: "SSD_ERR_ARG", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_CAPACITY", -
 # Every symbol include/ssd.h declares.
 EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_kv_pool_bytes", "ssd_workspace_bytes", "ssd_seq_create",
            "ssd_seq_destroy", "ssd_prefill", "ssd_decode_ar", "ssd_draft", "ssd_verify", "ssd_accept", "ssd_commit",
-           "ssd_score_masks", "ssd_row_stats", "ssd_read_state", "ssd_read_output", "ssd_last_error"]
+           "ssd_score_masks", "ssd_row_stats", "ssd_read_state", "ssd_read_output", "ssd_last_error",
+           "ssd_profile_enable", "ssd_profile_disable", "ssd_profile_read"]
 
 
 class SSDError(RuntimeError):
@@ -80,6 +81,9 @@ def lib():
             "ssd_row_stats": [P, I, I, F, U64, ctypes.c_int32, P, P],
             "ssd_read_state": [P, ctypes.POINTER(ssd_state), P],
             "ssd_read_output": [P, P, I, ctypes.POINTER(I), P],
+            "ssd_profile_enable": [I, I],
+            "ssd_profile_disable": [],
+            "ssd_profile_read": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I), ctypes.POINTER(ctypes.c_double)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -211,6 +215,24 @@ def ssd_read_output(seq, max_tokens, stream=None):
     check(lib().ssd_read_output(seq, out.ctypes.data_as(ctypes.c_void_p), max_tokens, ctypes.byref(n),
                                 _stream(stream)))
     return out[: n.value]
+
+
+SSD_PROF_GEMM_STORE, SSD_PROF_GEMM_RESID, SSD_PROF_GEMM_SWIGLU = 0, 1, 2
+
+
+def ssd_profile_enable(kernel_class, max_launches):
+    check(lib().ssd_profile_enable(kernel_class, max_launches))
+
+
+def ssd_profile_disable():
+    check(lib().ssd_profile_disable())
+
+
+def ssd_profile_read():
+    ms, by = ctypes.c_double(), ctypes.c_double()
+    n = ctypes.c_int()
+    check(lib().ssd_profile_read(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(by)))
+    return ms.value, n.value, by.value
 
 
 # ---------------------------------------------------------------------------

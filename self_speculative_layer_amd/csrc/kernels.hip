@@ -169,6 +169,13 @@ __global__ __launch_bounds__(256) void gemm_f32_rows16(
   }
 }
 
+bool profile_wants(int cls);
+void profile_before(hipStream_t s);
+void profile_after(hipStream_t s, double bytes);
+static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
+                              float* Y, int ldy, void* A, int lda, int n_rb, dim3 grid, const int* nrows,
+                              const int* ymap, const int* stop, hipStream_t s);
+
 int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
                   float* Y, int ldy, void* A, int lda, const int* nrows, const int* ymap,
                   const int* stop, hipStream_t s) {
@@ -176,6 +183,23 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
   const int n_rb = (M + 15) / 16;
   const int n_tiles = (N + 15) / 16;
   const dim3 grid(n_rb * n_tiles);
+  const bool prof = profile_wants(epi);
+  if (prof) profile_before(s);
+  const int rc = launch_linear_impl(dtype, epi, W, X, ldx, M, N, K, Y, ldy, A, lda, n_rb, grid, nrows, ymap, stop, s);
+  if (prof) {
+    // algorithmic bytes: weights once, activations in once, results out once (residual: read + write)
+    const double elt = dtype == SSD_DTYPE_BF16 ? 2.0 : 4.0;
+    const double wrows = epi == EPI_SWIGLU ? 2.0 * N : (double)N;
+    double by = wrows * K * elt + (double)M * K * elt;
+    by += epi == EPI_STORE ? 4.0 * M * N : (epi == EPI_RESID ? 8.0 * M * N : elt * M * N);
+    profile_after(s, by);
+  }
+  return rc;
+}
+
+static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
+                              float* Y, int ldy, void* A, int lda, int n_rb, dim3 grid, const int* nrows,
+                              const int* ymap, const int* stop, hipStream_t s) {
   if (dtype == SSD_DTYPE_BF16) {
     if (K % 64 != 0) return SSD_ERR_SHAPE;
     const bf16_t* w = (const bf16_t*)W;
@@ -227,16 +251,54 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const int row = blockIdx.x;
   if (row >= active_rows(M, nrows)) return;
   const float* hr = h + (size_t)(hmap ? hmap[row] : row) * ldh;
+  T* xr = x + (size_t)row * ldx;
+  constexpr int MAXV = 8;                 // float4 per thread: rows up to 8192 wide
+  float4 v[MAXV];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < D; i += 256) ss = fmaf(hr[i], hr[i], ss);
+  const bool vec = (D % 4 == 0) && (ldh % 4 == 0);
+  if (vec) {
+    const int nv = D / 4;
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      v[j] = i < nv ? ((const float4*)hr)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      ss = fmaf(v[j].x, v[j].x, ss); ss = fmaf(v[j].y, v[j].y, ss);
+      ss = fmaf(v[j].z, v[j].z, ss); ss = fmaf(v[j].w, v[j].w, ss);
+    }
+    for (int i = threadIdx.x + 256 * MAXV; i < nv; i += 256) {
+      const float4 a = ((const float4*)hr)[i];
+      ss = fmaf(a.x, a.x, ss); ss = fmaf(a.y, a.y, ss); ss = fmaf(a.z, a.z, ss); ss = fmaf(a.w, a.w, ss);
+    }
+  } else {
+    for (int i = threadIdx.x; i < D; i += 256) ss = fmaf(hr[i], hr[i], ss);
+  }
   ss = wave_sum(ss);
   __shared__ float part[4];
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = (part[0] + part[1]) + (part[2] + part[3]);
   const float inv = 1.0f / sqrtf(tot / (float)D + eps);
-  T* xr = x + (size_t)row * ldx;
-  for (int i = threadIdx.x; i < D; i += 256) st(xr + i, hr[i] * inv * gain[i]);
+  if (vec) {
+    const int nv = D / 4;
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      if (i < nv) {
+        const float4 gg = ((const float4*)gain)[i];
+        st(xr + 4 * i + 0, v[j].x * inv * gg.x);
+        st(xr + 4 * i + 1, v[j].y * inv * gg.y);
+        st(xr + 4 * i + 2, v[j].z * inv * gg.z);
+        st(xr + 4 * i + 3, v[j].w * inv * gg.w);
+      }
+    }
+    for (int i = threadIdx.x + 256 * MAXV; i < nv; i += 256)
+      for (int c = 0; c < 4; ++c) st(xr + 4 * i + c, hr[4 * i + c] * inv * gain[4 * i + c]);
+  } else {
+    for (int i = threadIdx.x; i < D; i += 256) st(xr + i, hr[i] * inv * gain[i]);
+  }
 }
 
 int launch_rmsnorm(int dtype, const float* h, int ldh, const float* gain, void* x, int ldx, int M, int D,
@@ -392,8 +454,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
   const float scale = 1.0f / sqrtf((float)HD);
 
-  __shared__ float Kt[HD][ATT_CHUNK + 1];
-  __shared__ float Vs[ATT_CHUNK][HD];
+  // K and V chunks in LDS in the storage type; rows padded by 4 bytes so that
+  // lanes reading different keys hit different banks.
+  constexpr int EPW = 4 / (int)sizeof(T);            // elements per 32-bit word
+  constexpr int KST = HD + EPW;                       // padded row stride (elements)
+  constexpr int VEC = 16 / (int)sizeof(T);            // elements per 16-byte load
+  constexpr int VPR = HD / VEC;                       // 16-byte vectors per row
+  constexpr int NLD = ATT_CHUNK * VPR / 256;          // vectors per thread per matrix
+  __shared__ __align__(16) T Ks[ATT_CHUNK * KST];
+  __shared__ __align__(16) T Vs[ATT_CHUNK * KST];
   __shared__ float Qs[ATT_MAXQ][HD];
   __shared__ float Os[ATT_MAXQ][HD];
   __shared__ float Ms[ATT_MAXQ], Ls[ATT_MAXQ];
@@ -407,29 +476,44 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     Os[qi][d] = 0.f;
   }
   for (int qi = tid; qi < nq; qi += 256) { Ms[qi] = -INFINITY; Ls[qi] = 0.f; }
-  // the group of the block's rows (scoring: candidates of group_rows rows each)
   const int grp_base = group_rows > 0 ? (r0 / group_rows) * group_rows : 0;
 
   for (int kc = key_beg; kc < key_end; kc += ATT_CHUNK) {
-    __syncthreads();
-    // stage keys kc .. kc+63 (masked past key_end)
-    for (int e = tid; e < ATT_CHUNK * HD; e += 256) {
-      const int t = e / HD, d = e % HD;
+    // issue every load of the chunk first, then store to LDS
+    u32x4 kreg[NLD], vreg[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int e = tid + 256 * j;
+      const int t = e / VPR, vc = e % VPR;
       const int kp = kc + t;
-      float kval = 0.f, vval = 0.f;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      kreg[j] = z;
+      vreg[j] = z;
       if (kp < key_end) {
+        const T* kr;
+        const T* vr;
         if (local_kv && kp >= local_start) {
-          const size_t base = ((size_t)(grp_base + (kp - local_start)) * 2) * KVH * HD;
-          kval = ld(local_kv + base + (size_t)g * HD + d);
-          vval = ld(local_kv + base + (size_t)KVH * HD + (size_t)g * HD + d);
+          const size_t base = ((size_t)(grp_base + (kp - local_start)) * 2) * KVH * HD + (size_t)g * HD;
+          kr = local_kv + base;
+          vr = local_kv + base + (size_t)KVH * HD;
         } else {
           const int page = page_table[kp / PS];
-          kval = ld(pool + kv_index(page, L, layer, 0, KVH, g, PS, kp % PS, HD) + d);
-          vval = ld(pool + kv_index(page, L, layer, 1, KVH, g, PS, kp % PS, HD) + d);
+          kr = pool + kv_index(page, L, layer, 0, KVH, g, PS, kp % PS, HD);
+          vr = pool + kv_index(page, L, layer, 1, KVH, g, PS, kp % PS, HD);
         }
+        kreg[j] = *(const u32x4*)(kr + vc * VEC);
+        vreg[j] = *(const u32x4*)(vr + vc * VEC);
       }
-      Kt[d][t] = kval;
-      Vs[t][d] = vval;
+    }
+    __syncthreads();      // previous chunk's readers are done
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int e = tid + 256 * j;
+      const int t = e / VPR, vc = e % VPR;
+      uint32_t* kd = (uint32_t*)(Ks + t * KST + vc * VEC);
+      uint32_t* vd = (uint32_t*)(Vs + t * KST + vc * VEC);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) { kd[w] = kreg[j][w]; vd[w] = vreg[j][w]; }
     }
     __syncthreads();
     for (int qi = wave; qi < nq; qi += 4) {
@@ -440,8 +524,18 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
       float sc = -INFINITY;
       if (valid) {
         float acc = 0.f;
+        const T* kr = Ks + lane * KST;
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll 16
-        for (int d = 0; d < HD; ++d) acc = fmaf(Qs[qi][d], Kt[d][lane], acc);
+          for (int d = 0; d < HD; d += 2) {
+            const uint32_t w2 = *(const uint32_t*)(kr + d);
+            acc = fmaf(Qs[qi][d], __uint_as_float(w2 << 16), acc);
+            acc = fmaf(Qs[qi][d + 1], __uint_as_float(w2 & 0xFFFF0000u), acc);
+          }
+        } else {
+#pragma unroll 16
+          for (int d = 0; d < HD; ++d) acc = fmaf(Qs[qi][d], ld(kr + d), acc);
+        }
         sc = acc * scale;
       }
       const float mx = wave_max(sc);
@@ -455,7 +549,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
       __builtin_amdgcn_wave_barrier();
       for (int d = lane; d < HD; d += 64) {
         float o = Os[qi][d] * alpha;
-        for (int t = 0; t < ATT_CHUNK; ++t) o = fmaf(Pw[wave][t], Vs[t][d], o);
+#pragma unroll 8
+        for (int t = 0; t < ATT_CHUNK; ++t) o = fmaf(Pw[wave][t], ld(Vs + t * KST + d), o);
         Os[qi][d] = o;
       }
       if (lane == 0) { Ms[qi] = m_new; Ls[qi] = Ls[qi] * alpha + psum; }
