@@ -17,18 +17,23 @@ layers are marked separately): uint8[2L], entry 2l = skip the attention
 sub-layer of layer l, entry 2l+1 = skip its MLP sub-layer.  A LayerSkip exit at
 E (LayerSkip blog §3.1) is the plan that skips every sub-layer of layers E..L-1.
 
+RMSNorm before a projection is applied as  y = (rnd(h * gain) . W^T) / rms(h)
+with rms(h) = sqrt(mean(h^2) + eps): the same function as
+rnd(h / rms(h) * gain) . W^T before rounding, with the 1/rms scale applied to
+the projection's output.
+
 Precision (bf16 models): the model stores bf16 tensors at these points and
 rounds to nearest-even there; everything else is float64 here —
-RMSNorm outputs entering a projection, RoPE'd q, the cached k and v, the
-attention output entering Wo, the SwiGLU product entering Wdown.  fp32 models
-are computed in float64 with no rounding.
+the gain-scaled residual entering a projection, RoPE'd q, the cached k and v,
+the attention output entering Wo, the SwiGLU product entering Wdown.  fp32
+models are computed in float64 with no rounding.
 """
 import dataclasses
 
 import numpy as np
 
 import synth
-from .numerics import bf16_round, rmsnorm, rope, silu, softmax
+from .numerics import bf16_round, rms, rope, silu, softmax
 
 
 @dataclasses.dataclass
@@ -126,10 +131,11 @@ def attention_sublayer(model, l, h, positions, kv):
     lw = model.layers[l]
     M = h.shape[0]
     H, KVH, hd = s.n_heads, s.n_kv_heads, s.head_dim
-    x = model.rnd(rmsnorm(h, lw.attn_norm, s.rms_eps))
-    q = (x @ lw.wq.T).reshape(M, H, hd)
-    k = (x @ lw.wk.T).reshape(M, KVH, hd)
-    v = (x @ lw.wv.T).reshape(M, KVH, hd)
+    x = model.rnd(h * lw.attn_norm)
+    r = rms(h, s.rms_eps)
+    q = ((x @ lw.wq.T) / r).reshape(M, H, hd)
+    k = ((x @ lw.wk.T) / r).reshape(M, KVH, hd)
+    v = ((x @ lw.wv.T) / r).reshape(M, KVH, hd)
     q = model.rnd(rope(q, positions, s.rope_theta))
     k = model.rnd(rope(k, positions, s.rope_theta))
     v = model.rnd(v)
@@ -153,8 +159,9 @@ def attention_sublayer(model, l, h, positions, kv):
 def mlp_sublayer(model, l, h):
     s = model.shape
     lw = model.layers[l]
-    x = model.rnd(rmsnorm(h, lw.mlp_norm, s.rms_eps))
-    a = model.rnd(silu(x @ lw.wgate.T) * (x @ lw.wup.T))
+    x = model.rnd(h * lw.mlp_norm)
+    r = rms(h, s.rms_eps)
+    a = model.rnd(silu((x @ lw.wgate.T) / r) * ((x @ lw.wup.T) / r))
     return h + a @ lw.wdown.T
 
 
@@ -176,7 +183,7 @@ def embed(model, tokens):
 def final_logits(model, h):
     """Shared final RMSNorm and shared LM head: logits [M, V] (LayerSkip blog §2)."""
     s = model.shape
-    return model.rnd(rmsnorm(h, model.final_norm, s.rms_eps)) @ model.lm_head.T
+    return (model.rnd(h * model.final_norm) @ model.lm_head.T) / rms(h, s.rms_eps)
 
 
 def forward(model, tokens, positions, kv, mask=None):

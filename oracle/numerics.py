@@ -31,10 +31,14 @@ def bf16_round(x):
     return out
 
 
+def rms(h, eps):
+    """Per-row root mean square with the RMSNorm epsilon: sqrt(mean(h^2) + eps), shape [M, 1]."""
+    return np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+
+
 def rmsnorm(h, gain, eps):
     """RMSNorm: h / sqrt(mean(h^2) + eps) * gain, per row."""
-    ms = np.mean(h * h, axis=-1, keepdims=True)
-    return h / np.sqrt(ms + eps) * gain
+    return h / rms(h, eps) * gain
 
 
 def rope_angles(positions, head_dim, theta):

@@ -54,7 +54,7 @@ struct Workspace {
   int* page_table;
   double* inv_freq;
   int *pos, *tok, *pos1, *tok1, *vpos, *vtok;
-  float *h, *h1, *qkv, *part, *hb, *logits1, *logits_rows;
+  float *h, *h1, *qkv, *part, *hb, *logits1, *logits_rows, *inv;
   void *x, *x2, *qb, *local_kv;
   ssd_row_stat* stats;
   int *dec, *corr, *rowmaps;
@@ -95,6 +95,7 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.vtok = (int*)take(sizeof(int) * (max_draft + 1));
   t.h = (float*)take(sizeof(float) * (size_t)R * D);
   t.h1 = (float*)take(sizeof(float) * D);
+  t.inv = (float*)take(sizeof(float) * R);
   t.qkv = (float*)take(sizeof(float) * (size_t)R * m->qkv_dim);
   t.part = (float*)take(sizeof(float) * attention_partial_floats(R, d.n_heads, d.head_dim, max_ctx));
   t.hb = (float*)take(sizeof(float) * (size_t)max_draft * D);
@@ -130,15 +131,16 @@ int attn_sublayer(ssd_seq* q, int l, const Block& b, hipStream_t s) {
   const Workspace& w = q->w;
   const RowBlock& rb = b.rb;
   const int D = d.d_model;
-  TRY(launch_rmsnorm(d.dtype, b.h, D, lw.attn_norm, w.x, D, rb.M, D, d.rms_eps, rb.nrows, rb.ymap, rb.stop, s));
-  TRY(launch_linear(d.dtype, EPI_STORE, lw.w_qkv, w.x, D, rb.M, m->qkv_dim, D, w.qkv, m->qkv_dim, nullptr, 0,
+  TRY(launch_rowprep(d.dtype, b.h, D, lw.attn_norm, w.x, D, w.inv, rb.M, D, d.rms_eps, rb.nrows, rb.ymap, rb.stop,
+                     s));
+  TRY(launch_linear(d.dtype, EPI_STORE, lw.w_qkv, w.x, D, rb.M, m->qkv_dim, D, w.qkv, m->qkv_dim, nullptr, 0, w.inv,
                     rb.nrows, nullptr, rb.stop, s));
   TRY(launch_rope_kv(d.dtype, d.head_dim, w.qkv, m->qkv_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads,
                      d.n_kv_heads, rb, w.inv_freq, b.local_kv, &w.st->error_flags, s));
   TRY(launch_attention(d.dtype, d.head_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads, d.n_kv_heads, rb,
                        q->max_ctx, b.local_kv, b.local_start, b.group_rows, w.part, w.x, m->q_dim, s));
-  TRY(launch_linear(d.dtype, EPI_RESID, lw.w_o, w.x, m->q_dim, rb.M, D, m->q_dim, b.h, D, nullptr, 0, rb.nrows,
-                    rb.ymap, rb.stop, s));
+  TRY(launch_linear(d.dtype, EPI_RESID, lw.w_o, w.x, m->q_dim, rb.M, D, m->q_dim, b.h, D, nullptr, 0, nullptr,
+                    rb.nrows, rb.ymap, rb.stop, s));
   return 0;
 }
 
@@ -149,11 +151,12 @@ int mlp_sublayer(ssd_seq* q, int l, const Block& b, hipStream_t s) {
   const Workspace& w = q->w;
   const RowBlock& rb = b.rb;
   const int D = d.d_model, F = d.ffn_dim;
-  TRY(launch_rmsnorm(d.dtype, b.h, D, lw.mlp_norm, w.x, D, rb.M, D, d.rms_eps, rb.nrows, rb.ymap, rb.stop, s));
-  TRY(launch_linear(d.dtype, EPI_SWIGLU, lw.w_gate_up, w.x, D, rb.M, F, D, nullptr, 0, w.x2, F, rb.nrows, nullptr,
-                    rb.stop, s));
-  TRY(launch_linear(d.dtype, EPI_RESID, lw.w_down, w.x2, F, rb.M, D, F, b.h, D, nullptr, 0, rb.nrows, rb.ymap,
-                    rb.stop, s));
+  TRY(launch_rowprep(d.dtype, b.h, D, lw.mlp_norm, w.x, D, w.inv, rb.M, D, d.rms_eps, rb.nrows, rb.ymap, rb.stop,
+                     s));
+  TRY(launch_linear(d.dtype, EPI_SWIGLU, lw.w_gate_up, w.x, D, rb.M, F, D, nullptr, 0, w.x2, F, w.inv, rb.nrows,
+                    nullptr, rb.stop, s));
+  TRY(launch_linear(d.dtype, EPI_RESID, lw.w_down, w.x2, F, rb.M, D, F, b.h, D, nullptr, 0, nullptr, rb.nrows,
+                    rb.ymap, rb.stop, s));
   return 0;
 }
 
@@ -173,10 +176,10 @@ int final_logits(ssd_seq* q, const float* h, int M, const int* nrows, float* log
                  hipStream_t s) {
   const ssd_model* m = q->m;
   const ssd_model_desc& d = m->d;
-  TRY(launch_rmsnorm(d.dtype, h, d.d_model, d.final_norm, q->w.x, d.d_model, M, d.d_model, d.rms_eps, nrows,
-                     nullptr, stop, s));
+  TRY(launch_rowprep(d.dtype, h, d.d_model, d.final_norm, q->w.x, d.d_model, q->w.inv, M, d.d_model, d.rms_eps,
+                     nrows, nullptr, stop, s));
   TRY(launch_linear(d.dtype, EPI_STORE, d.lm_head, q->w.x, d.d_model, M, d.vocab, d.d_model, logits, d.vocab,
-                    nullptr, 0, nrows, nullptr, stop, s));
+                    nullptr, 0, q->w.inv, nrows, nullptr, stop, s));
   return 0;
 }
 

@@ -1,0 +1,179 @@
+// Attention over the paged KV cache (device functions shared by the
+// standalone attention kernels and the persistent decode kernel).
+//
+// Keys are split at fixed absolute positions: split s covers [256 s, 256 s + 256).
+// A work item handles one KV head g, one split and a block of rows with all
+// their query heads (grouped-query attention); it stages 64 keys at a time in
+// LDS (16-byte vector loads, all in flight) in the storage type, keeps an
+// online softmax per query in fp32 and writes a partial (o[HD], m, l).  The
+// combine merges a row's partials in split order.  Split and chunk boundaries
+// are fixed positions, so a row's result does not depend on the rows batched
+// with it.
+#pragma once
+#include "common.h"
+
+namespace ssd {
+
+constexpr int ATT_SPLIT = 256;
+constexpr int ATT_CHUNK = 64;
+constexpr int ATT_MAXQ = 64;     // queries (rows x heads of a group) per work item
+
+__device__ __forceinline__ size_t kv_index(int page, int L, int layer, int kv, int KVH, int g, int PS, int slot,
+                                           int HD) {
+  return (((((size_t)page * L + layer) * 2 + kv) * KVH + g) * PS + slot) * (size_t)HD;
+}
+
+template <typename T, int HD, int NW>
+struct AttnSmem {
+  static constexpr int EPW = 4 / (int)sizeof(T);   // elements per 32-bit word
+  static constexpr int KST = HD + EPW;              // padded row stride: lanes on different keys hit different banks
+  T Ks[ATT_CHUNK * KST];
+  T Vs[ATT_CHUNK * KST];
+  float Qs[ATT_MAXQ][HD];
+  float Os[ATT_MAXQ][HD];
+  float Ms[ATT_MAXQ], Ls[ATT_MAXQ];
+  float Pw[NW][ATT_CHUNK];
+};
+
+typedef uint32_t att_u32x4 __attribute__((ext_vector_type(4)));
+
+// One work item: KV head g, split s, rows r0..r1-1 (positions increasing).
+// Keys at positions >= local_start come from local_kv rows (scoring: the
+// candidate's own keys/values, rows grouped by group_rows).  Requires all
+// NW*64 threads of the block.
+template <typename T, int HD, int NW>
+__device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__ q, int ldq,
+                                  const T* __restrict__ pool, const int* __restrict__ page_table, int PS, int L,
+                                  int layer, int H, int KVH, const int* __restrict__ pos, int r0, int r1, int g,
+                                  int s, int nsplit, const T* __restrict__ local_kv, int local_start, int group_rows,
+                                  float* __restrict__ part) {
+  constexpr int NT = NW * 64;
+  constexpr int KST = AttnSmem<T, HD, NW>::KST;
+  constexpr int VEC = 16 / (int)sizeof(T);            // elements per 16-byte load
+  constexpr int VPR = HD / VEC;                       // 16-byte vectors per row
+  constexpr int NLD = ATT_CHUNK * VPR / NT;           // vectors per thread per matrix
+  static_assert(NLD >= 1 && ATT_CHUNK * VPR % NT == 0, "staging layout");
+  const int G = H / KVH;
+  const int nq = (r1 - r0) * G;
+  const int key_beg = s * ATT_SPLIT;
+  const int maxpos = pos[r1 - 1];
+  const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
+  const float scale = 1.0f / sqrtf((float)HD);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int e = tid; e < nq * HD; e += NT) {
+    const int qi = e / HD, d = e % HD;
+    const int row = r0 + qi / G, head = g * G + qi % G;
+    sm.Qs[qi][d] = ld(q + (size_t)row * ldq + (size_t)head * HD + d);
+    sm.Os[qi][d] = 0.f;
+  }
+  for (int qi = tid; qi < nq; qi += NT) { sm.Ms[qi] = -INFINITY; sm.Ls[qi] = 0.f; }
+  const int grp_base = group_rows > 0 ? (r0 / group_rows) * group_rows : 0;
+
+  for (int kc = key_beg; kc < key_end; kc += ATT_CHUNK) {
+    att_u32x4 kreg[NLD], vreg[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int e = tid + NT * j;
+      const int t = e / VPR, vc = e % VPR;
+      const int kp = kc + t;
+      const att_u32x4 z = {0u, 0u, 0u, 0u};
+      kreg[j] = z;
+      vreg[j] = z;
+      if (kp < key_end) {
+        const T* kr;
+        const T* vr;
+        if (local_kv && kp >= local_start) {
+          const size_t base = ((size_t)(grp_base + (kp - local_start)) * 2) * KVH * HD + (size_t)g * HD;
+          kr = local_kv + base;
+          vr = local_kv + base + (size_t)KVH * HD;
+        } else {
+          const int page = page_table[kp / PS];
+          kr = pool + kv_index(page, L, layer, 0, KVH, g, PS, kp % PS, HD);
+          vr = pool + kv_index(page, L, layer, 1, KVH, g, PS, kp % PS, HD);
+        }
+        kreg[j] = *(const att_u32x4*)(kr + vc * VEC);
+        vreg[j] = *(const att_u32x4*)(vr + vc * VEC);
+      }
+    }
+    __syncthreads();      // the previous chunk's readers are done
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int e = tid + NT * j;
+      const int t = e / VPR, vc = e % VPR;
+      uint32_t* kd = (uint32_t*)(sm.Ks + t * KST + vc * VEC);
+      uint32_t* vd = (uint32_t*)(sm.Vs + t * KST + vc * VEC);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) { kd[w] = kreg[j][w]; vd[w] = vreg[j][w]; }
+    }
+    __syncthreads();
+    for (int qi = wave; qi < nq; qi += NW) {
+      const int row = r0 + qi / G;
+      const int prow = pos[row];
+      const int kp = kc + lane;
+      const bool valid = kp < key_end && kp <= prow;
+      float sc = -INFINITY;
+      if (valid) {
+        float acc = 0.f;
+        const T* kr = sm.Ks + lane * KST;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll 16
+          for (int d = 0; d < HD; d += 2) {
+            const uint32_t w2 = *(const uint32_t*)(kr + d);
+            acc = fmaf(sm.Qs[qi][d], __uint_as_float(w2 << 16), acc);
+            acc = fmaf(sm.Qs[qi][d + 1], __uint_as_float(w2 & 0xFFFF0000u), acc);
+          }
+        } else {
+#pragma unroll 16
+          for (int d = 0; d < HD; ++d) acc = fmaf(sm.Qs[qi][d], ld(kr + d), acc);
+        }
+        sc = __fmul_rn(acc, scale);
+      }
+      const float mx = wave_max(sc);
+      if (mx == -INFINITY) continue;            // no visible key in this chunk (wave-uniform)
+      const float m_old = sm.Ms[qi];
+      const float m_new = fmaxf(m_old, mx);
+      const float alpha = expf(__fsub_rn(m_old, m_new));   // 0 when m_old = -inf
+      const float pexp = valid ? expf(__fsub_rn(sc, m_new)) : 0.f;
+      const float psum = wave_sum(pexp);
+      sm.Pw[wave][lane] = pexp;
+      __builtin_amdgcn_wave_barrier();
+      for (int d = lane; d < HD; d += 64) {
+        float o = __fmul_rn(sm.Os[qi][d], alpha);
+#pragma unroll 8
+        for (int t = 0; t < ATT_CHUNK; ++t) o = fmaf(sm.Pw[wave][t], ld(sm.Vs + t * KST + d), o);
+        sm.Os[qi][d] = o;
+      }
+      if (lane == 0) { sm.Ms[qi] = m_new; sm.Ls[qi] = __fadd_rn(__fmul_rn(sm.Ls[qi], alpha), psum); }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < nq * (HD + 2); e += NT) {
+    const int qi = e / (HD + 2), c = e % (HD + 2);
+    const int row = r0 + qi / G, head = g * G + qi % G;
+    if (s * ATT_SPLIT > pos[row]) continue;     // the row sees no key of this split
+    float* dstp = part + (((size_t)row * H + head) * nsplit + s) * (HD + 2);
+    dstp[c] = c < HD ? sm.Os[qi][c] : (c == HD ? sm.Ms[qi] : sm.Ls[qi]);
+  }
+  __syncthreads();
+}
+
+// Merge the splits of (row, head) in split order; component d of the output.
+template <typename T, int HD>
+__device__ __forceinline__ void attn_combine_elem(const float* __restrict__ part, int nsplit, int row, int head,
+                                                  int H, int p, int d, T* __restrict__ out, int ldo) {
+  const int ns = p / ATT_SPLIT + 1;
+  const float* pr = part + ((size_t)row * H + head) * nsplit * (HD + 2);
+  float m = -INFINITY;
+  for (int s = 0; s < ns; ++s) m = fmaxf(m, pr[s * (HD + 2) + HD]);
+  float l = 0.f, o = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = expf(__fsub_rn(pr[s * (HD + 2) + HD], m));
+    l = fmaf(pr[s * (HD + 2) + HD + 1], w, l);
+    o = fmaf(pr[s * (HD + 2) + d], w, o);
+  }
+  st(out + (size_t)row * ldo + (size_t)head * HD + d, __fdiv_rn(o, l));
+}
+
+}  // namespace ssd

@@ -115,3 +115,52 @@ __device__ __forceinline__ float word_to_gumbel(uint32_t x) {
 }
 
 }  // namespace ssd
+
+namespace ssd {
+
+// ---------------------------------------------------------------------------
+// Canonical RMS reductions.  The residual stream's sum of squares is formed
+// as (1) per group of 16 consecutive features, a butterfly over 16 lanes
+// (xor 8, 4, 2, 1), then (2) over the groups: lane j of one wave adds groups
+// j, j + 64, j + 128, ... in order, then a butterfly over 64 lanes.  Every
+// kernel that needs a row's RMS uses these functions, so the result is the
+// same bits whichever kernel produced or consumes it.
+
+// (1) with the 16 values held by 16 consecutive lanes; every lane gets the sum.
+__device__ __forceinline__ float tile16_ss_lanes(float v) {
+  float s = __fmul_rn(v, v);
+  s += __shfl_xor(s, 8, 16);
+  s += __shfl_xor(s, 4, 16);
+  s += __shfl_xor(s, 2, 16);
+  s += __shfl_xor(s, 1, 16);
+  return s;
+}
+
+// (2) by one full wave over ntiles group sums at tiles[t * stride]; every lane gets the total.
+__device__ __forceinline__ float row_ss_total(const float* tiles, int stride, int ntiles) {
+  const int lane = threadIdx.x & 63;
+  float acc = 0.f;
+  for (int t = lane; t < ntiles; t += 64) acc += tiles[(size_t)t * stride];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, WAVE);
+  return acc;
+}
+
+__device__ __forceinline__ float inv_rms(float ss_total, int D, float eps) {
+  return __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(ss_total, (float)D), eps)));
+}
+
+// Elementwise steps shared by every kernel that performs them, with explicit
+// round-to-nearest operations so that no kernel contracts them differently.
+__device__ __forceinline__ void rope_rotate(float x1, float x2, int pos, double inv_freq, float& y1, float& y2) {
+  const double a = (double)pos * inv_freq;
+  const float c = (float)cos(a), s = (float)sin(a);
+  y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, s));
+  y2 = __fadd_rn(__fmul_rn(x2, c), __fmul_rn(x1, s));
+}
+
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return __fmul_rn(__fdiv_rn(g, __fadd_rn(1.0f, expf(-g))), u);
+}
+
+}  // namespace ssd

@@ -32,11 +32,14 @@ struct KvView {
 
 // Linear layer: X [M, K] (row stride ldx, act dtype) times W [N, K]^T.
 // For EPI_SWIGLU, N = F (output features) and W holds 2F rows (gate, then up).
+// rscale (nullable): per-row factor applied to the product before the
+// epilogue (not for EPI_RESID).
 int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
-                  float* Y, int ldy, void* A, int lda, const int* nrows, const int* ymap,
+                  float* Y, int ldy, void* A, int lda, const float* rscale, const int* nrows, const int* ymap,
                   const int* stop, hipStream_t s);
 
-int launch_rmsnorm(int dtype, const float* h, int ldh, const float* gain, void* x, int ldx, int M, int D,
+// x[m] = act(h[hmap[m]] * gain), inv[m] = 1 / sqrt(mean(h^2) + eps).
+int launch_rowprep(int dtype, const float* h, int ldh, const float* gain, void* x, int ldx, float* inv, int M, int D,
                    float eps, const int* nrows, const int* hmap, const int* stop, hipStream_t s);
 
 int launch_embed(int dtype, const void* emb, const int* tokens, int V, float* h, int ldh, int M, int D,

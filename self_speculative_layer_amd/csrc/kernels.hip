@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include "kernels.h"
+#include "attn.h"
 
 namespace ssd {
 
@@ -15,7 +16,6 @@ __device__ __forceinline__ int active_rows(int M, const int* nrows) {
   return nrows ? min(M, *nrows) : M;
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // ===========================================================================
 // Linear layers, bf16: Y[M, N] = X[M, K] . W[N, K]^T with fp32 accumulation on
@@ -35,7 +35,7 @@ constexpr int GEMM_U = 8;
 template <int EPI>
 __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_rows16(
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ X, int ldx, int M, int N, int K,
-    float* __restrict__ Y, int ldy, bf16_t* __restrict__ A, int lda, int n_rb,
+    float* __restrict__ Y, int ldy, bf16_t* __restrict__ A, int lda, int n_rb, const float* __restrict__ rscale,
     const int* __restrict__ nrows, const int* __restrict__ ymap, const int* __restrict__ stop) {
   if (stop && *stop) return;
   const int Ma = active_rows(M, nrows);
@@ -108,10 +108,11 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_rows16(
         s += red[0][w][nn][mm];
         if (EPI == EPI_SWIGLU) s2 += red[NT - 1][w][nn][mm];
       }
+      if (rscale && EPI != EPI_RESID) { s = __fmul_rn(s, rscale[row]); s2 = __fmul_rn(s2, rscale[row]); }
       const int yrow = ymap ? ymap[row] : row;
       if (EPI == EPI_STORE) Y[(size_t)yrow * ldy + col] = s;
-      else if (EPI == EPI_RESID) Y[(size_t)yrow * ldy + col] += s;
-      else A[(size_t)row * lda + col] = f2bf(silu(s) * s2);
+      else if (EPI == EPI_RESID) Y[(size_t)yrow * ldy + col] = __fadd_rn(Y[(size_t)yrow * ldy + col], s);
+      else A[(size_t)row * lda + col] = f2bf(swiglu(s, s2));
     }
   }
 }
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_rows16(
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_rows16(
     const float* __restrict__ W, const float* __restrict__ X, int ldx, int M, int N, int K,
-    float* __restrict__ Y, int ldy, float* __restrict__ A, int lda, int n_rb,
+    float* __restrict__ Y, int ldy, float* __restrict__ A, int lda, int n_rb, const float* __restrict__ rscale,
     const int* __restrict__ nrows, const int* __restrict__ ymap, const int* __restrict__ stop) {
   if (stop && *stop) return;
   const int Ma = active_rows(M, nrows);
@@ -155,14 +156,15 @@ __global__ __launch_bounds__(256) void gemm_f32_rows16(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i < mcount) {
-        const float s = wave_sum(acc[i]);
-        const float s2 = (EPI == EPI_SWIGLU) ? wave_sum(acc2[i]) : 0.f;
+        float s = wave_sum(acc[i]);
+        float s2 = (EPI == EPI_SWIGLU) ? wave_sum(acc2[i]) : 0.f;
         if (lane == 0) {
           const int row = m0 + i;
+          if (rscale && EPI != EPI_RESID) { s = __fmul_rn(s, rscale[row]); s2 = __fmul_rn(s2, rscale[row]); }
           const int yrow = ymap ? ymap[row] : row;
           if (EPI == EPI_STORE) Y[(size_t)yrow * ldy + col] = s;
-          else if (EPI == EPI_RESID) Y[(size_t)yrow * ldy + col] += s;
-          else A[(size_t)row * lda + col] = silu(s) * s2;
+          else if (EPI == EPI_RESID) Y[(size_t)yrow * ldy + col] = __fadd_rn(Y[(size_t)yrow * ldy + col], s);
+          else A[(size_t)row * lda + col] = swiglu(s, s2);
         }
       }
     }
@@ -173,11 +175,11 @@ bool profile_wants(int cls);
 void profile_before(hipStream_t s);
 void profile_after(hipStream_t s, double bytes);
 static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
-                              float* Y, int ldy, void* A, int lda, int n_rb, dim3 grid, const int* nrows,
-                              const int* ymap, const int* stop, hipStream_t s);
+                              float* Y, int ldy, void* A, int lda, int n_rb, dim3 grid, const float* rscale,
+                              const int* nrows, const int* ymap, const int* stop, hipStream_t s);
 
 int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
-                  float* Y, int ldy, void* A, int lda, const int* nrows, const int* ymap,
+                  float* Y, int ldy, void* A, int lda, const float* rscale, const int* nrows, const int* ymap,
                   const int* stop, hipStream_t s) {
   if (M <= 0 || N <= 0) return 0;
   const int n_rb = (M + 15) / 16;
@@ -185,7 +187,8 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
   const dim3 grid(n_rb * n_tiles);
   const bool prof = profile_wants(epi);
   if (prof) profile_before(s);
-  const int rc = launch_linear_impl(dtype, epi, W, X, ldx, M, N, K, Y, ldy, A, lda, n_rb, grid, nrows, ymap, stop, s);
+  const int rc = launch_linear_impl(dtype, epi, W, X, ldx, M, N, K, Y, ldy, A, lda, n_rb, grid, rscale, nrows, ymap,
+                                    stop, s);
   if (prof) {
     // algorithmic bytes: weights once, activations in once, results out once (residual: read + write)
     const double elt = dtype == SSD_DTYPE_BF16 ? 2.0 : 4.0;
@@ -198,8 +201,8 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
 }
 
 static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
-                              float* Y, int ldy, void* A, int lda, int n_rb, dim3 grid, const int* nrows,
-                              const int* ymap, const int* stop, hipStream_t s) {
+                              float* Y, int ldy, void* A, int lda, int n_rb, dim3 grid, const float* rscale,
+                              const int* nrows, const int* ymap, const int* stop, hipStream_t s) {
   if (dtype == SSD_DTYPE_BF16) {
     if (K % 64 != 0) return SSD_ERR_SHAPE;
     const bf16_t* w = (const bf16_t*)W;
@@ -207,15 +210,15 @@ static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, 
     switch (epi) {
       case EPI_STORE:
         hipLaunchKernelGGL(gemm_bf16_rows16<EPI_STORE>, grid, dim3(GEMM_NW * 64), 0, s, w, x, ldx, M, N, K, Y,
-                           ldy, (bf16_t*)A, lda, n_rb, nrows, ymap, stop);
+                           ldy, (bf16_t*)A, lda, n_rb, rscale, nrows, ymap, stop);
         break;
       case EPI_RESID:
         hipLaunchKernelGGL(gemm_bf16_rows16<EPI_RESID>, grid, dim3(GEMM_NW * 64), 0, s, w, x, ldx, M, N, K, Y,
-                           ldy, (bf16_t*)A, lda, n_rb, nrows, ymap, stop);
+                           ldy, (bf16_t*)A, lda, n_rb, rscale, nrows, ymap, stop);
         break;
       default:
         hipLaunchKernelGGL(gemm_bf16_rows16<EPI_SWIGLU>, grid, dim3(GEMM_NW * 64), 0, s, w, x, ldx, M, N, K, Y,
-                           ldy, (bf16_t*)A, lda, n_rb, nrows, ymap, stop);
+                           ldy, (bf16_t*)A, lda, n_rb, rscale, nrows, ymap, stop);
     }
   } else {
     const float* w = (const float*)W;
@@ -223,15 +226,15 @@ static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, 
     switch (epi) {
       case EPI_STORE:
         hipLaunchKernelGGL(gemm_f32_rows16<EPI_STORE>, grid, dim3(256), 0, s, w, x, ldx, M, N, K, Y, ldy,
-                           (float*)A, lda, n_rb, nrows, ymap, stop);
+                           (float*)A, lda, n_rb, rscale, nrows, ymap, stop);
         break;
       case EPI_RESID:
         hipLaunchKernelGGL(gemm_f32_rows16<EPI_RESID>, grid, dim3(256), 0, s, w, x, ldx, M, N, K, Y, ldy,
-                           (float*)A, lda, n_rb, nrows, ymap, stop);
+                           (float*)A, lda, n_rb, rscale, nrows, ymap, stop);
         break;
       default:
         hipLaunchKernelGGL(gemm_f32_rows16<EPI_SWIGLU>, grid, dim3(256), 0, s, w, x, ldx, M, N, K, Y, ldy,
-                           (float*)A, lda, n_rb, nrows, ymap, stop);
+                           (float*)A, lda, n_rb, rscale, nrows, ymap, stop);
     }
   }
   return last_launch();
@@ -241,10 +244,13 @@ static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, 
 // RMSNorm: x[m] = act(h[hmap[m]] / sqrt(mean(h^2) + eps) * gain), fp32 sums.
 // ===========================================================================
 
+// Row preparation for a projection: x[m] = act(h[hmap[m]] * gain) and
+// inv[m] = 1 / sqrt(mean(h^2) + eps) (the RMS scale is applied to the
+// projection's output).  One workgroup per row.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h, int ldh,
+__global__ __launch_bounds__(256) void rowprep_kernel(const float* __restrict__ h, int ldh,
                                                       const float* __restrict__ gain, T* __restrict__ x,
-                                                      int ldx, int M, int D, float eps,
+                                                      int ldx, float* __restrict__ inv, int M, int D, float eps,
                                                       const int* __restrict__ nrows,
                                                       const int* __restrict__ hmap, const int* __restrict__ stop) {
   if (stop && *stop) return;
@@ -252,64 +258,34 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   if (row >= active_rows(M, nrows)) return;
   const float* hr = h + (size_t)(hmap ? hmap[row] : row) * ldh;
   T* xr = x + (size_t)row * ldx;
-  constexpr int MAXV = 8;                 // float4 per thread: rows up to 8192 wide
-  float4 v[MAXV];
-  float ss = 0.f;
-  const bool vec = (D % 4 == 0) && (ldh % 4 == 0);
-  if (vec) {
-    const int nv = D / 4;
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      const int i = threadIdx.x + 256 * j;
-      v[j] = i < nv ? ((const float4*)hr)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  __shared__ float tss[1024];                  // group sums, D <= 16384
+  const int ntiles = D / 16;
+  for (int base = 0; base < ntiles * 16; base += 256) {
+    const int i = base + threadIdx.x;
+    const float v = i < D ? hr[i] : 0.f;
+    const float s = tile16_ss_lanes(v);
+    if (i < D) {
+      if ((threadIdx.x & 15) == 0) tss[i >> 4] = s;
+      st(xr + i, __fmul_rn(v, gain[i]));
     }
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      ss = fmaf(v[j].x, v[j].x, ss); ss = fmaf(v[j].y, v[j].y, ss);
-      ss = fmaf(v[j].z, v[j].z, ss); ss = fmaf(v[j].w, v[j].w, ss);
-    }
-    for (int i = threadIdx.x + 256 * MAXV; i < nv; i += 256) {
-      const float4 a = ((const float4*)hr)[i];
-      ss = fmaf(a.x, a.x, ss); ss = fmaf(a.y, a.y, ss); ss = fmaf(a.z, a.z, ss); ss = fmaf(a.w, a.w, ss);
-    }
-  } else {
-    for (int i = threadIdx.x; i < D; i += 256) ss = fmaf(hr[i], hr[i], ss);
   }
-  ss = wave_sum(ss);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float inv = 1.0f / sqrtf(tot / (float)D + eps);
-  if (vec) {
-    const int nv = D / 4;
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      const int i = threadIdx.x + 256 * j;
-      if (i < nv) {
-        const float4 gg = ((const float4*)gain)[i];
-        st(xr + 4 * i + 0, v[j].x * inv * gg.x);
-        st(xr + 4 * i + 1, v[j].y * inv * gg.y);
-        st(xr + 4 * i + 2, v[j].z * inv * gg.z);
-        st(xr + 4 * i + 3, v[j].w * inv * gg.w);
-      }
-    }
-    for (int i = threadIdx.x + 256 * MAXV; i < nv; i += 256)
-      for (int c = 0; c < 4; ++c) st(xr + 4 * i + c, hr[4 * i + c] * inv * gain[4 * i + c]);
-  } else {
-    for (int i = threadIdx.x; i < D; i += 256) st(xr + i, hr[i] * inv * gain[i]);
+  if (threadIdx.x < 64) {
+    const float tot = row_ss_total(tss, 1, ntiles);
+    if (threadIdx.x == 0) inv[row] = inv_rms(tot, D, eps);
   }
 }
 
-int launch_rmsnorm(int dtype, const float* h, int ldh, const float* gain, void* x, int ldx, int M, int D,
+int launch_rowprep(int dtype, const float* h, int ldh, const float* gain, void* x, int ldx, float* inv, int M, int D,
                    float eps, const int* nrows, const int* hmap, const int* stop, hipStream_t s) {
   if (M <= 0) return 0;
+  if (D % 16 != 0 || D > 16384) return SSD_ERR_SHAPE;
   if (dtype == SSD_DTYPE_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, s, h, ldh, gain, (bf16_t*)x, ldx, M, D,
+    hipLaunchKernelGGL(rowprep_kernel<bf16_t>, dim3(M), dim3(256), 0, s, h, ldh, gain, (bf16_t*)x, ldx, inv, M, D,
                        eps, nrows, hmap, stop);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, s, h, ldh, gain, (float*)x, ldx, M, D, eps,
-                       nrows, hmap, stop);
+    hipLaunchKernelGGL(rowprep_kernel<float>, dim3(M), dim3(256), 0, s, h, ldh, gain, (float*)x, ldx, inv, M, D,
+                       eps, nrows, hmap, stop);
   return last_launch();
 }
 
@@ -349,10 +325,6 @@ int launch_embed(int dtype, const void* emb, const int* tokens, int V, float* h,
 // to fp32, the rotation itself in fp32.
 // ===========================================================================
 
-__device__ __forceinline__ size_t kv_index(int page, int L, int layer, int kv, int KVH, int g, int PS, int slot,
-                                           int HD) {
-  return (((((size_t)page * L + layer) * 2 + kv) * KVH + g) * PS + slot) * (size_t)HD;
-}
 
 template <typename T, int HD>
 __global__ void rope_kv_kernel(const float* __restrict__ qkv, int ldqkv, T* __restrict__ qout, int ldq,
@@ -386,10 +358,10 @@ __global__ void rope_kv_kernel(const float* __restrict__ qkv, int ldqkv, T* __re
   }
   const float x1 = src[i], x2 = src[i + HD / 2];
   if (slot < H + KVH) {
-    const double a = (double)p * inv_freq[i];
-    const float c = (float)cos(a), sn = (float)sin(a);
-    st(dst + i, x1 * c - x2 * sn);
-    st(dst + i + HD / 2, x2 * c + x1 * sn);
+    float y1, y2;
+    rope_rotate(x1, x2, p, inv_freq[i], y1, y2);
+    st(dst + i, y1);
+    st(dst + i + HD / 2, y2);
   } else {
     st(dst + i, x1);
     st(dst + i + HD / 2, x2);
@@ -415,19 +387,8 @@ int launch_rope_kv(int dtype, int head_dim, const float* qkv, int ldqkv, void* q
 }
 
 // ===========================================================================
-// Attention over the paged cache, split over keys.  Split s covers absolute
-// key positions [256 s, 256 s + 256); a workgroup handles one KV head, one
-// split and a block of rows with all their query heads (grouped-query), stages
-// 64 keys at a time in LDS as fp32 (K transposed so lanes read consecutive
-// words) and keeps an online softmax per query.  Partial (m, l, o) go to a
-// buffer; a combine kernel merges the splits of a row in split order.  Split
-// boundaries are fixed positions, so a row's result does not depend on the
-// rows batched with it.
+// Attention over the paged cache (device functions in attn.h).
 // ===========================================================================
-
-constexpr int ATT_SPLIT = 256;
-constexpr int ATT_CHUNK = 64;
-constexpr int ATT_MAXQ = 64;     // queries (rows x heads of a group) per workgroup
 
 size_t attention_partial_floats(int max_rows, int H, int head_dim, int max_ctx) {
   const int nsplit = (max_ctx + ATT_SPLIT - 1) / ATT_SPLIT;
@@ -446,125 +407,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   const int r0 = rbk * RB;
   if (r0 >= Ma) return;
   const int r1 = min(r0 + RB, Ma);
-  const int G = H / KVH;
-  const int nq = (r1 - r0) * G;
-  const int key_beg = s * ATT_SPLIT;
-  const int maxpos = pos[r1 - 1];
-  if (key_beg > maxpos) return;
-  const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
-  const float scale = 1.0f / sqrtf((float)HD);
-
-  // K and V chunks in LDS in the storage type; rows padded by 4 bytes so that
-  // lanes reading different keys hit different banks.
-  constexpr int EPW = 4 / (int)sizeof(T);            // elements per 32-bit word
-  constexpr int KST = HD + EPW;                       // padded row stride (elements)
-  constexpr int VEC = 16 / (int)sizeof(T);            // elements per 16-byte load
-  constexpr int VPR = HD / VEC;                       // 16-byte vectors per row
-  constexpr int NLD = ATT_CHUNK * VPR / 256;          // vectors per thread per matrix
-  __shared__ __align__(16) T Ks[ATT_CHUNK * KST];
-  __shared__ __align__(16) T Vs[ATT_CHUNK * KST];
-  __shared__ float Qs[ATT_MAXQ][HD];
-  __shared__ float Os[ATT_MAXQ][HD];
-  __shared__ float Ms[ATT_MAXQ], Ls[ATT_MAXQ];
-  __shared__ float Pw[4][ATT_CHUNK];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < nq * HD; e += 256) {
-    const int qi = e / HD, d = e % HD;
-    const int row = r0 + qi / G, head = g * G + qi % G;
-    Qs[qi][d] = ld(q + (size_t)row * ldq + (size_t)head * HD + d);
-    Os[qi][d] = 0.f;
-  }
-  for (int qi = tid; qi < nq; qi += 256) { Ms[qi] = -INFINITY; Ls[qi] = 0.f; }
-  const int grp_base = group_rows > 0 ? (r0 / group_rows) * group_rows : 0;
-
-  for (int kc = key_beg; kc < key_end; kc += ATT_CHUNK) {
-    // issue every load of the chunk first, then store to LDS
-    u32x4 kreg[NLD], vreg[NLD];
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int e = tid + 256 * j;
-      const int t = e / VPR, vc = e % VPR;
-      const int kp = kc + t;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[j] = z;
-      vreg[j] = z;
-      if (kp < key_end) {
-        const T* kr;
-        const T* vr;
-        if (local_kv && kp >= local_start) {
-          const size_t base = ((size_t)(grp_base + (kp - local_start)) * 2) * KVH * HD + (size_t)g * HD;
-          kr = local_kv + base;
-          vr = local_kv + base + (size_t)KVH * HD;
-        } else {
-          const int page = page_table[kp / PS];
-          kr = pool + kv_index(page, L, layer, 0, KVH, g, PS, kp % PS, HD);
-          vr = pool + kv_index(page, L, layer, 1, KVH, g, PS, kp % PS, HD);
-        }
-        kreg[j] = *(const u32x4*)(kr + vc * VEC);
-        vreg[j] = *(const u32x4*)(vr + vc * VEC);
-      }
-    }
-    __syncthreads();      // previous chunk's readers are done
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int e = tid + 256 * j;
-      const int t = e / VPR, vc = e % VPR;
-      uint32_t* kd = (uint32_t*)(Ks + t * KST + vc * VEC);
-      uint32_t* vd = (uint32_t*)(Vs + t * KST + vc * VEC);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) { kd[w] = kreg[j][w]; vd[w] = vreg[j][w]; }
-    }
-    __syncthreads();
-    for (int qi = wave; qi < nq; qi += 4) {
-      const int row = r0 + qi / G;
-      const int prow = pos[row];
-      const int kp = kc + lane;
-      const bool valid = kp < key_end && kp <= prow;
-      float sc = -INFINITY;
-      if (valid) {
-        float acc = 0.f;
-        const T* kr = Ks + lane * KST;
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll 16
-          for (int d = 0; d < HD; d += 2) {
-            const uint32_t w2 = *(const uint32_t*)(kr + d);
-            acc = fmaf(Qs[qi][d], __uint_as_float(w2 << 16), acc);
-            acc = fmaf(Qs[qi][d + 1], __uint_as_float(w2 & 0xFFFF0000u), acc);
-          }
-        } else {
-#pragma unroll 16
-          for (int d = 0; d < HD; ++d) acc = fmaf(Qs[qi][d], ld(kr + d), acc);
-        }
-        sc = acc * scale;
-      }
-      const float mx = wave_max(sc);
-      if (mx == -INFINITY) continue;            // no visible key in this chunk (wave-uniform)
-      const float m_old = Ms[qi];
-      const float m_new = fmaxf(m_old, mx);
-      const float alpha = expf(m_old - m_new);   // 0 when m_old = -inf
-      const float pexp = valid ? expf(sc - m_new) : 0.f;
-      const float psum = wave_sum(pexp);
-      Pw[wave][lane] = pexp;
-      __builtin_amdgcn_wave_barrier();
-      for (int d = lane; d < HD; d += 64) {
-        float o = Os[qi][d] * alpha;
-#pragma unroll 8
-        for (int t = 0; t < ATT_CHUNK; ++t) o = fmaf(Pw[wave][t], ld(Vs + t * KST + d), o);
-        Os[qi][d] = o;
-      }
-      if (lane == 0) { Ms[qi] = m_new; Ls[qi] = Ls[qi] * alpha + psum; }
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < nq * (HD + 2); e += 256) {
-    const int qi = e / (HD + 2), c = e % (HD + 2);
-    const int row = r0 + qi / G, head = g * G + qi % G;
-    if (s * ATT_SPLIT > pos[row]) continue;     // the row sees no key of this split
-    float* dstp = part + (((size_t)row * H + head) * nsplit + s) * (HD + 2);
-    dstp[c] = c < HD ? Os[qi][c] : (c == HD ? Ms[qi] : Ls[qi]);
-  }
+  if (s * ATT_SPLIT > pos[r1 - 1]) return;
+  __shared__ AttnSmem<T, HD, 4> sm;
+  attn_partial_item<T, HD, 4>(sm, q, ldq, pool, page_table, PS, L, layer, H, KVH, pos, r0, r1, g, s, nsplit,
+                              local_kv, local_start, group_rows, part);
 }
 
 template <typename T, int HD>
@@ -572,19 +418,9 @@ __global__ void attn_combine_kernel(const float* __restrict__ part, int nsplit, 
                                     const int* __restrict__ pos, int H, T* __restrict__ out, int ldo,
                                     const int* __restrict__ stop) {
   if (stop && *stop) return;
-  const int row = blockIdx.x, head = blockIdx.y, d = threadIdx.x;
+  const int row = blockIdx.x, head = blockIdx.y;
   if (row >= active_rows(M, nrows)) return;
-  const int ns = pos[row] / ATT_SPLIT + 1;
-  const float* pr = part + ((size_t)row * H + head) * nsplit * (HD + 2);
-  float m = -INFINITY;
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, pr[s * (HD + 2) + HD]);
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = expf(pr[s * (HD + 2) + HD] - m);
-    l = fmaf(pr[s * (HD + 2) + HD + 1], w, l);
-    o = fmaf(pr[s * (HD + 2) + d], w, o);
-  }
-  st(out + (size_t)row * ldo + (size_t)head * HD + d, o / l);
+  attn_combine_elem<T, HD>(part, nsplit, row, head, H, pos[row], threadIdx.x, out, ldo);
 }
 
 int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer,

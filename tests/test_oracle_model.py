@@ -6,6 +6,7 @@ import torch
 import synth
 from oracle import model as mdl
 from oracle import ssd
+from oracle.numerics import rmsnorm
 
 GQA_SMALL = synth.ModelShape("gqa-small-f32", 2, 128, 4, 2, 32, 96, 100, "f32")
 BF16_SMALL = synth.ModelShape("bf16-small", 3, 128, 4, 2, 32, 160, 300, "bf16")
@@ -99,7 +100,7 @@ def test_attention_single_key_returns_value():
     kv = mdl.KVCache(s, 4)
     h = mdl.embed(m, [5])
     out = mdl.attention_sublayer(m, 0, h, [0], kv)
-    x = mdl.rmsnorm(h, lw.attn_norm, s.rms_eps)
+    x = rmsnorm(h, lw.attn_norm, s.rms_eps)                # the textbook RMSNorm form
     v = (x @ lw.wv.T).reshape(s.n_kv_heads, s.head_dim)
     G = s.n_heads // s.n_kv_heads
     o = np.repeat(v, G, axis=0).reshape(-1)
