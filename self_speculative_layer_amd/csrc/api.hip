@@ -52,13 +52,32 @@ struct ssd_model {
 struct Workspace {
   DevState* st;
   int* page_table;
-  double* inv_freq;
+  float2* rope_cs;
   int *pos, *tok, *pos1, *tok1, *vpos, *vtok;
   float *h, *h1, *qkv, *part, *hb, *logits1, *logits_rows, *inv;
   void *x, *x2, *qb, *local_kv;
   ssd_row_stat* stats;
   int *dec, *corr, *rowmaps;
   int32_t* log;
+  // persistent decode pass
+  FzLayer* fz_layers;
+  bf16_t *fz_xg, *fz_ob;
+  float* fz_ss;
+  unsigned* fz_counters;
+  int* fz_prog;          // FZ_SLOTS slots of [types | layers] ints
+  const float** fz_gain; // FZ_SLOTS slots of gain pointers
+};
+
+constexpr int FZ_SLOTS = 12;
+
+// A pass program: phase list of the persistent kernel.
+struct FzProgram {
+  std::vector<int> type, layer;
+  std::vector<const float*> gain;
+  int save_phase = -1;
+  bool operator==(const FzProgram& o) const {
+    return type == o.type && layer == o.layer && gain == o.gain && save_phase == o.save_phase;
+  }
 };
 
 struct ssd_seq {
@@ -66,6 +85,11 @@ struct ssd_seq {
   KvView kv;
   int max_rows, max_draft, max_ctx, log_cap;
   Workspace w;
+  int fz_nwg = 0;            // workgroups of the persistent pass (0: not available)
+  int path = SSD_PATH_KERNELS;
+  int fz_max_phase = 0;
+  FzProgram fz_cache[FZ_SLOTS];
+  int fz_next = 0;
 };
 
 namespace {
@@ -86,7 +110,7 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   Workspace t{};
   t.st = (DevState*)take(sizeof(DevState));
   t.page_table = (int*)take(sizeof(int) * (size_t)((max_ctx + 15) / 16 + 1));
-  t.inv_freq = (double*)take(sizeof(double) * d.head_dim / 2);
+  t.rope_cs = (float2*)take(sizeof(float2) * (size_t)max_ctx * (d.head_dim / 2));
   t.pos = (int*)take(sizeof(int) * R);
   t.tok = (int*)take(sizeof(int) * R);
   t.pos1 = (int*)take(sizeof(int) * 4);
@@ -110,6 +134,14 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.corr = (int*)take(sizeof(int) * (max_draft + 1));
   t.rowmaps = (int*)take(sizeof(int) * (size_t)2 * L * R);
   t.log = (int32_t*)take(sizeof(int32_t) * (size_t)max_ctx);
+  const int max_phase = 2 + 5 * L;
+  t.fz_layers = (FzLayer*)take(sizeof(FzLayer) * L);
+  t.fz_xg = (bf16_t*)take(2 * (size_t)16 * std::max(D, m->q_dim));
+  t.fz_ob = (bf16_t*)take(2 * (size_t)16 * m->q_dim);
+  t.fz_ss = (float*)take(sizeof(float) * (size_t)16 * (D / 16 + 1));
+  t.fz_counters = (unsigned*)take(sizeof(unsigned) * (size_t)(max_phase + 1 + L * d.n_kv_heads));
+  t.fz_prog = (int*)take(sizeof(int) * (size_t)FZ_SLOTS * 2 * max_phase);
+  t.fz_gain = (const float**)take(sizeof(float*) * (size_t)FZ_SLOTS * max_phase);
   if (w) *w = t;
   return off;
 }
@@ -136,7 +168,7 @@ int attn_sublayer(ssd_seq* q, int l, const Block& b, hipStream_t s) {
   TRY(launch_linear(d.dtype, EPI_STORE, lw.w_qkv, w.x, D, rb.M, m->qkv_dim, D, w.qkv, m->qkv_dim, nullptr, 0, w.inv,
                     rb.nrows, nullptr, rb.stop, s));
   TRY(launch_rope_kv(d.dtype, d.head_dim, w.qkv, m->qkv_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads,
-                     d.n_kv_heads, rb, w.inv_freq, b.local_kv, &w.st->error_flags, s));
+                     d.n_kv_heads, rb, w.rope_cs, b.local_kv, &w.st->error_flags, s));
   TRY(launch_attention(d.dtype, d.head_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads, d.n_kv_heads, rb,
                        q->max_ctx, b.local_kv, b.local_start, b.group_rows, w.part, w.x, m->q_dim, s));
   TRY(launch_linear(d.dtype, EPI_RESID, lw.w_o, w.x, m->q_dim, rb.M, D, m->q_dim, b.h, D, nullptr, 0, nullptr,
@@ -197,6 +229,106 @@ int plan_mask(const ssd_model* m, const uint8_t* mask_in, int exit_layer, std::v
   for (int l = 0; l < L; ++l)
     if (mask[2 * l] || mask[2 * l + 1]) return l;
   return L;
+}
+
+// Phase program of a pass over the sub-layer entries (2l + sub), optionally
+// followed by the LM head.  save_entry: WG 0 copies h before that entry's
+// first phase (entries.size(): before the LM head); -1: no copy.
+FzProgram fz_build(const ssd_model* m, const std::vector<int>& entries, bool final_lm, int save_entry) {
+  FzProgram pr;
+  const ssd_model_desc& d = m->d;
+  auto consumer_gain = [&](size_t e) -> const float* {
+    if (e < entries.size()) {
+      const int l = entries[e] / 2;
+      return (entries[e] % 2 == 0) ? d.layers[l].attn_norm : d.layers[l].mlp_norm;
+    }
+    return final_lm ? d.final_norm : nullptr;
+  };
+  pr.type.push_back(PH_INIT); pr.layer.push_back(0); pr.gain.push_back(consumer_gain(0));
+  for (size_t e = 0; e < entries.size(); ++e) {
+    const int l = entries[e] / 2;
+    if ((int)e == save_entry) pr.save_phase = (int)pr.type.size();
+    if (entries[e] % 2 == 0) {
+      pr.type.insert(pr.type.end(), {PH_QKV, PH_ATTN, PH_O});
+      pr.layer.insert(pr.layer.end(), {l, l, l});
+      pr.gain.insert(pr.gain.end(), {nullptr, nullptr, consumer_gain(e + 1)});
+    } else {
+      pr.type.insert(pr.type.end(), {PH_GU, PH_DOWN});
+      pr.layer.insert(pr.layer.end(), {l, l});
+      pr.gain.insert(pr.gain.end(), {nullptr, consumer_gain(e + 1)});
+    }
+  }
+  if (final_lm) {
+    if (save_entry == (int)entries.size()) pr.save_phase = (int)pr.type.size();
+    pr.type.push_back(PH_LM); pr.layer.push_back(0); pr.gain.push_back(nullptr);
+  }
+  return pr;
+}
+
+// Sub-layer entries of layers [l0, l1) that the plan keeps (mask == nullptr: all).
+void fz_entries(std::vector<int>& out, int l0, int l1, const uint8_t* mask) {
+  for (int l = l0; l < l1; ++l) {
+    if (!(mask && mask[2 * l])) out.push_back(2 * l);
+    if (!(mask && mask[2 * l + 1])) out.push_back(2 * l + 1);
+  }
+}
+
+// Runs one persistent pass.  The program is uploaded to a workspace slot the
+// first time it is seen (a synchronous copy; later passes reuse the slot).
+int fz_run(ssd_seq* q, const FzProgram& pr, int M, const int* nrows, const int* pos, const int* tokens,
+           const float* h_in, float* h, float* logits, float* save_h, const int* stop, hipStream_t s) {
+  const ssd_model* m = q->m;
+  const ssd_model_desc& d = m->d;
+  Workspace& w = q->w;
+  const int np = (int)pr.type.size();
+  if (np > q->fz_max_phase) return fail(SSD_ERR_CAPACITY, "pass program too long");
+  int slot = -1;
+  for (int i = 0; i < FZ_SLOTS; ++i)
+    if (q->fz_cache[i] == pr) { slot = i; break; }
+  if (slot < 0) {
+    slot = q->fz_next;
+    q->fz_next = (q->fz_next + 1) % FZ_SLOTS;
+    std::vector<int> ints(2 * q->fz_max_phase, 0);
+    std::copy(pr.type.begin(), pr.type.end(), ints.begin());
+    std::copy(pr.layer.begin(), pr.layer.end(), ints.begin() + q->fz_max_phase);
+    std::vector<const float*> gains(q->fz_max_phase, nullptr);
+    std::copy(pr.gain.begin(), pr.gain.end(), gains.begin());
+    // the slot may still be read by passes queued on the stream
+    if (hipStreamSynchronize(s) != hipSuccess) return fail(SSD_ERR_HIP, "stream sync");
+    if (hipMemcpy(w.fz_prog + (size_t)slot * 2 * q->fz_max_phase, ints.data(), sizeof(int) * ints.size(),
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(w.fz_gain + (size_t)slot * q->fz_max_phase, gains.data(), sizeof(float*) * gains.size(),
+                  hipMemcpyHostToDevice) != hipSuccess)
+      return fail(SSD_ERR_HIP, "program upload");
+    q->fz_cache[slot] = pr;
+  }
+  FzParams p{};
+  p.layers = w.fz_layers;
+  p.L = d.n_layers; p.D = d.d_model; p.H = d.n_heads; p.KVH = d.n_kv_heads; p.HD = d.head_dim;
+  p.F = d.ffn_dim; p.V = d.vocab; p.eps = d.rms_eps;
+  p.embed = (const bf16_t*)d.embed;
+  p.lm_head = (const bf16_t*)d.lm_head;
+  p.ph_type = w.fz_prog + (size_t)slot * 2 * q->fz_max_phase;
+  p.ph_layer = p.ph_type + q->fz_max_phase;
+  p.ph_gain = w.fz_gain + (size_t)slot * q->fz_max_phase;
+  p.n_phase = np;
+  p.save_phase = save_h ? pr.save_phase : -1;
+  p.M = M; p.nrows = nrows; p.pos = pos; p.tokens = tokens; p.h_in = h_in;
+  p.h = h; p.xg = w.fz_xg; p.qb = (bf16_t*)w.qb; p.ob = w.fz_ob; p.ab = (bf16_t*)w.x2; p.ss = w.fz_ss;
+  p.part = w.part;
+  p.nsplit_max = attention_nsplit(q->max_ctx);
+  p.logits = logits; p.save_h = save_h;
+  p.pool = (bf16_t*)q->kv.pool; p.page_table = q->kv.page_table; p.PS = q->kv.page_size; p.n_lpages = q->kv.n_lpages;
+  p.rope_cs = w.rope_cs;
+  p.counters = w.fz_counters;
+  p.err = &w.st->error_flags;
+  p.stop = stop;
+  TRY(launch_fused_pass(p, d.head_dim, q->fz_nwg, s));
+  return 0;
+}
+
+bool fz_usable(const ssd_seq* q, int rows) {
+  return q->path == SSD_PATH_PERSISTENT && q->fz_nwg > 0 && q->m->d.dtype == SSD_DTYPE_BF16 && rows <= 16;
 }
 
 }  // namespace
@@ -284,17 +416,41 @@ extern "C" int ssd_seq_create(const ssd_model* m, void* kv_pool_dev, int n_pages
   q->kv.page_table = q->w.page_table;
   q->kv.n_lpages = n_logical_pages;
   q->kv.page_size = page_size;
-  // RoPE inverse frequencies theta^(-2i/hd), computed in fp64
-  std::vector<double> inv(m->d.head_dim / 2);
-  for (int i = 0; i < m->d.head_dim / 2; ++i)
-    inv[i] = std::pow((double)m->d.rope_theta, -2.0 * i / (double)m->d.head_dim);
+  // RoPE table: (cos, sin)(pos * theta^(-2i/hd)) for every position of the sequence, in fp64, rounded to fp32
+  const int half = m->d.head_dim / 2;
+  std::vector<float2> cs((size_t)max_ctx * half);
+  for (int i = 0; i < half; ++i) {
+    const double inv = std::pow((double)m->d.rope_theta, -2.0 * i / (double)m->d.head_dim);
+    for (int pos = 0; pos < max_ctx; ++pos) {
+      const double a = (double)pos * inv;
+      cs[(size_t)pos * half + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+    }
+  }
   hipError_t e = hipMemcpy(q->w.page_table, page_table_host, sizeof(int32_t) * n_logical_pages,
                            hipMemcpyHostToDevice);
-  if (e == hipSuccess)
-    e = hipMemcpy(q->w.inv_freq, inv.data(), sizeof(double) * inv.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(q->w.rope_cs, cs.data(), sizeof(float2) * cs.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     delete q;
     return fail(SSD_ERR_HIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
+  }
+  // persistent decode pass: layer pointer table, zeroed counters, one workgroup per CU
+  q->fz_max_phase = 2 + 5 * m->d.n_layers;
+  if (m->d.dtype == SSD_DTYPE_BF16) {
+    std::vector<FzLayer> fl(m->d.n_layers);
+    for (int l = 0; l < m->d.n_layers; ++l) {
+      const ssd_layer_weights& lw = m->layers[l];
+      fl[l] = FzLayer{lw.attn_norm, (const bf16_t*)lw.w_qkv, (const bf16_t*)lw.w_o, lw.mlp_norm,
+                      (const bf16_t*)lw.w_gate_up, (const bf16_t*)lw.w_down};
+    }
+    int dev = 0, cus = 0, coop = 0, per_cu = 0;
+    const size_t nctr = (size_t)(q->fz_max_phase + 1 + m->d.n_layers * m->d.n_kv_heads);
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
+        fused_pass_max_blocks_per_cu(m->d.head_dim, &per_cu) == 0 && per_cu >= 1 &&
+        hipMemcpy(q->w.fz_layers, fl.data(), sizeof(FzLayer) * fl.size(), hipMemcpyHostToDevice) == hipSuccess &&
+        hipMemset(q->w.fz_counters, 0, sizeof(unsigned) * nctr) == hipSuccess)
+      q->fz_nwg = cus;
   }
   int rc = launch_state_init(q->w.st, stream);
   if (rc == 0 && hipStreamSynchronize(stream) != hipSuccess) rc = SSD_ERR_HIP;
@@ -347,11 +503,17 @@ extern "C" int ssd_decode_ar(ssd_seq* q, float temperature, uint64_t seed, float
   const ssd_model_desc& d = q->m->d;
   const Workspace& w = q->w;
   TRY(launch_single_row_prep(w.st, w.pos1, w.tok1, q->max_ctx, s));
-  TRY(launch_embed(d.dtype, d.embed, w.tok1, d.vocab, w.h1, d.d_model, 1, d.d_model, nullptr, nullptr, s));
-  Block b{w.h1, RowBlock{1, nullptr, w.pos1, nullptr, nullptr}, nullptr, 0, 0};
-  TRY(run_layers(q, b, 0, d.n_layers, nullptr, s));
   float* lg = logits_dev ? logits_dev : w.logits1;
-  TRY(final_logits(q, w.h1, 1, nullptr, lg, nullptr, s));
+  if (fz_usable(q, 1)) {
+    std::vector<int> ent;
+    fz_entries(ent, 0, d.n_layers, nullptr);
+    TRY(fz_run(q, fz_build(q->m, ent, true, -1), 1, nullptr, w.pos1, w.tok1, nullptr, w.h1, lg, nullptr, nullptr, s));
+  } else {
+    TRY(launch_embed(d.dtype, d.embed, w.tok1, d.vocab, w.h1, d.d_model, 1, d.d_model, nullptr, nullptr, s));
+    Block b{w.h1, RowBlock{1, nullptr, w.pos1, nullptr, nullptr}, nullptr, 0, 0};
+    TRY(run_layers(q, b, 0, d.n_layers, nullptr, s));
+    TRY(final_logits(q, w.h1, 1, nullptr, lg, nullptr, s));
+  }
   TRY(launch_row_stats(lg, d.vocab, 1, d.vocab, temperature, seed, &w.st->iteration, 0, 0, PURPOSE_SAMPLE, w.stats,
                        nullptr, s));
   TRY(launch_pick_commit(w.stats, w.st, w.log, q->log_cap, 0, 0, s));
@@ -374,6 +536,21 @@ extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_lay
   CHECK_ARG(b >= 0, "exit_layer out of range");
   const int* stop = &w.st->stop;
   TRY(launch_draft_begin(w.st, s));
+  if (fz_usable(q, 1)) {
+    std::vector<int> ent;
+    fz_entries(ent, 0, b, nullptr);
+    const int save_entry = (int)ent.size();
+    fz_entries(ent, b, d.n_layers, mask.data());
+    const FzProgram pr = fz_build(q->m, ent, true, save_entry);
+    for (int j = 1; j <= d_max; ++j) {
+      TRY(launch_draft_step_prep(w.st, draft_tokens_dev, j, w.pos1, w.tok1, q->max_ctx, n_drafted_dev, s));
+      float* lg = draft_logits_dev + (size_t)(j - 1) * d.vocab;
+      TRY(fz_run(q, pr, 1, nullptr, w.pos1, w.tok1, nullptr, w.h1, lg, w.hb + (size_t)(j - 1) * d.d_model, stop, s));
+      TRY(launch_draft_stats(lg, d.vocab, temperature, seed, w.st, j, d_max, conf_thresh, draft_tokens_dev,
+                             n_drafted_dev, s));
+    }
+    return SSD_OK;
+  }
   Block blk{w.h1, RowBlock{1, nullptr, w.pos1, nullptr, stop}, nullptr, 0, 0};
   for (int j = 1; j <= d_max; ++j) {
     TRY(launch_draft_step_prep(w.st, draft_tokens_dev, j, w.pos1, w.tok1, q->max_ctx, n_drafted_dev, s));
@@ -403,6 +580,27 @@ extern "C" int ssd_verify(ssd_seq* q, const uint8_t* skip_mask_host, int exit_la
   const int* rows = &w.st->verify_rows;
   TRY(launch_verify_prep(w.st, draft_tokens_dev, n_drafted_dev, d_max, w.vpos, w.vtok, w.pos1, w.tok1, q->max_ctx,
                          s));
+  if (fz_usable(q, M)) {
+    std::vector<int> suffix;
+    fz_entries(suffix, b, d.n_layers, nullptr);
+    if (reuse && b > 0) {
+      // rows < d' take the residual the draft saved at the boundary; the last row runs the layers below it
+      TRY(launch_copy_rows(w.hb, w.h, d_max, d.d_model, n_drafted_dev, nullptr, nullptr, s));
+      std::vector<int> prefix;
+      fz_entries(prefix, 0, b, nullptr);
+      TRY(fz_run(q, fz_build(q->m, prefix, false, -1), 1, nullptr, w.pos1, w.tok1, nullptr, w.h1, nullptr, nullptr,
+                 nullptr, s));
+      TRY(launch_copy_rows(w.h1, w.h, 1, d.d_model, nullptr, n_drafted_dev, nullptr, s));
+      TRY(fz_run(q, fz_build(q->m, suffix, true, -1), M, rows, w.vpos, nullptr, w.h, w.h, logits_dev, nullptr,
+                 nullptr, s));
+    } else {
+      std::vector<int> all;
+      fz_entries(all, 0, d.n_layers, nullptr);
+      TRY(fz_run(q, fz_build(q->m, all, true, -1), M, rows, w.vpos, w.vtok, nullptr, w.h, logits_dev, nullptr,
+                 nullptr, s));
+    }
+    return SSD_OK;
+  }
   Block full{w.h, RowBlock{M, rows, w.vpos, nullptr, nullptr}, nullptr, 0, 0};
   if (reuse) {
     // rows < d' take the residual saved by the draft at the boundary
@@ -500,6 +698,15 @@ extern "C" int ssd_row_stats(const float* logits_dev, int rows, int V, float tem
 // ---------------------------------------------------------------------------
 // host synchronisation
 
+extern "C" int ssd_seq_set_decode_path(ssd_seq* q, int path) {
+  CHECK_ARG(q, "null argument");
+  CHECK_ARG(path == SSD_PATH_KERNELS || path == SSD_PATH_PERSISTENT, "unknown decode path");
+  if (path == SSD_PATH_PERSISTENT && q->fz_nwg <= 0)
+    return fail(SSD_ERR_UNSUPPORTED, "persistent pass needs a bf16 model and cooperative launch");
+  q->path = path;
+  return SSD_OK;
+}
+
 extern "C" int ssd_read_state(ssd_seq* q, ssd_state* out, hipStream_t s) {
   CHECK_ARG(q && out, "null argument");
   DevState st;
@@ -515,6 +722,7 @@ extern "C" int ssd_read_state(ssd_seq* q, ssd_state* out, hipStream_t s) {
   out->last_n_emitted = st.n_emitted;
   if (st.error_flags & ERRF_CAPACITY) return fail(SSD_ERR_CAPACITY, "KV pages or output log exhausted on the device");
   if (st.error_flags & ERRF_NUMERIC) return fail(SSD_ERR_NUMERIC, "non-finite logits seen on the device");
+  if (st.error_flags & ERRF_TIMEOUT) return fail(SSD_ERR_HIP, "a bounded wait of the persistent pass gave up");
   return SSD_OK;
 }
 

@@ -1,7 +1,7 @@
 // Attention over the paged KV cache (device functions shared by the
 // standalone attention kernels and the persistent decode kernel).
 //
-// Keys are split at fixed absolute positions: split s covers [256 s, 256 s + 256).
+// Keys are split at fixed absolute positions: split s covers [64 s, 64 s + 64).
 // A work item handles one KV head g, one split and a block of rows with all
 // their query heads (grouped-query attention); it stages 64 keys at a time in
 // LDS (16-byte vector loads, all in flight) in the storage type, keeps an
@@ -14,7 +14,7 @@
 
 namespace ssd {
 
-constexpr int ATT_SPLIT = 256;
+constexpr int ATT_SPLIT = 64;
 constexpr int ATT_CHUNK = 64;
 constexpr int ATT_MAXQ = 64;     // queries (rows x heads of a group) per work item
 

@@ -14,6 +14,7 @@ constexpr int WAVE = 64;
 // Flags in DevState::error_flags.
 constexpr int ERRF_CAPACITY = 1;
 constexpr int ERRF_NUMERIC = 2;
+constexpr int ERRF_TIMEOUT = 4;   // a bounded wait of the persistent pass gave up
 
 // Per-sequence state that lives on the device, so that the host can enqueue
 // a whole decode iteration without reading anything back.
@@ -152,11 +153,12 @@ __device__ __forceinline__ float inv_rms(float ss_total, int D, float eps) {
 
 // Elementwise steps shared by every kernel that performs them, with explicit
 // round-to-nearest operations so that no kernel contracts them differently.
-__device__ __forceinline__ void rope_rotate(float x1, float x2, int pos, double inv_freq, float& y1, float& y2) {
-  const double a = (double)pos * inv_freq;
-  const float c = (float)cos(a), s = (float)sin(a);
-  y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, s));
-  y2 = __fadd_rn(__fmul_rn(x2, c), __fmul_rn(x1, s));
+// Rotation of the pair (x1, x2) by the angle whose (cos, sin) is cs.  The
+// table of (cos, sin)(pos * theta^(-2i/hd)) is formed in fp64 and rounded to
+// fp32 when a sequence is created.
+__device__ __forceinline__ void rope_apply(float x1, float x2, float2 cs, float& y1, float& y2) {
+  y1 = __fsub_rn(__fmul_rn(x1, cs.x), __fmul_rn(x2, cs.y));
+  y2 = __fadd_rn(__fmul_rn(x2, cs.x), __fmul_rn(x1, cs.y));
 }
 
 __device__ __forceinline__ float swiglu(float g, float u) {

@@ -49,7 +49,7 @@ int launch_embed(int dtype, const void* emb, const int* tokens, int V, float* h,
 // (or, when local_kv != nullptr, into local_kv[row][2][KVH][HD]).
 int launch_rope_kv(int dtype, int head_dim, const float* qkv, int ldqkv, void* qout, int ldq,
                    const KvView& kv, int L, int layer, int H, int KVH, const RowBlock& rb,
-                   const double* inv_freq, void* local_kv, int* err_flags, hipStream_t s);
+                   const float2* rope_cs, void* local_kv, int* err_flags, hipStream_t s);
 
 // Attention of every row over cached keys at positions <= its own (keys at
 // positions >= local_start come from local_kv rows of the row's own group of
@@ -58,6 +58,8 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
                      int H, int KVH, const RowBlock& rb, int max_ctx, const void* local_kv,
                      int local_start, int group_rows, float* part, void* out, int ldo, hipStream_t s);
 size_t attention_partial_floats(int max_rows, int H, int head_dim, int max_ctx);
+// Number of fixed key splits covering max_ctx positions (the partial buffer's split dimension).
+int attention_nsplit(int max_ctx);
 
 // Row statistics (a3).  purpose/rowid_base address the random draws.
 int launch_row_stats(const float* z, int ldz, int rows, int V, float T, uint64_t seed,
@@ -94,5 +96,61 @@ int launch_copy_rows(const float* src, float* dst, int rows, int D, const int* c
                      const int* stop, hipStream_t s);
 int launch_score(const ssd_row_stat* stats, const int32_t* window, int n_masks, int gamma, float* scores,
                  int32_t* best, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Persistent decode pass (fused.hip)
+
+enum PassPhase { PH_INIT = 0, PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_DOWN = 5, PH_LM = 6 };
+
+struct FzLayer {
+  const float* attn_norm;
+  const bf16_t* w_qkv;
+  const bf16_t* w_o;
+  const float* mlp_norm;
+  const bf16_t* w_gate_up;
+  const bf16_t* w_down;
+};
+
+struct FzParams {
+  const FzLayer* layers;
+  int L, D, H, KVH, HD, F, V;
+  float eps;
+  const bf16_t* embed;
+  const bf16_t* lm_head;
+  // program
+  const int* ph_type;
+  const int* ph_layer;
+  const float* const* ph_gain;
+  int n_phase;
+  int save_phase;            // phase before which WG 0 copies h (rows < Ma) to save_h; -1: none
+  // rows
+  int M;
+  const int* nrows;
+  const int* pos;
+  const int* tokens;         // INIT from the embedding (when h_in == nullptr)
+  const float* h_in;         // INIT from residual rows
+  // buffers
+  float* h;
+  bf16_t* xg;
+  bf16_t* qb;
+  bf16_t* ob;
+  bf16_t* ab;
+  float* ss;                 // [D/16][16] group sums of h^2
+  float* part;
+  int nsplit_max;
+  float* logits;
+  float* save_h;
+  // cache
+  bf16_t* pool;
+  const int* page_table;
+  int PS, n_lpages;
+  const float2* rope_cs;     // [position][HD/2] (cos, sin)
+  unsigned* counters;        // [n_phase] + exit + per-attention-phase head counters
+  int* err;
+  const int* stop;
+};
+
+int launch_fused_pass(const FzParams& p, int head_dim, int nwg, hipStream_t s);
+int fused_pass_max_blocks_per_cu(int head_dim, int* blocks);
 
 }  // namespace ssd

@@ -29,7 +29,7 @@ __device__ __forceinline__ int active_rows(int M, const int* nrows) {
 // whatever rows it is batched with.
 // ===========================================================================
 
-constexpr int GEMM_NW = 8;
+constexpr int GEMM_NW = 4;
 constexpr int GEMM_U = 8;
 
 template <int EPI>
@@ -330,7 +330,7 @@ template <typename T, int HD>
 __global__ void rope_kv_kernel(const float* __restrict__ qkv, int ldqkv, T* __restrict__ qout, int ldq,
                                T* __restrict__ pool, const int* __restrict__ page_table, int n_lpages, int PS,
                                int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
-                               const int* __restrict__ pos, const double* __restrict__ inv_freq,
+                               const int* __restrict__ pos, const float2* __restrict__ rope_cs,
                                T* __restrict__ local_kv, int* __restrict__ err, const int* __restrict__ stop) {
   if (stop && *stop) return;
   const int row = blockIdx.x;
@@ -359,7 +359,7 @@ __global__ void rope_kv_kernel(const float* __restrict__ qkv, int ldqkv, T* __re
   const float x1 = src[i], x2 = src[i + HD / 2];
   if (slot < H + KVH) {
     float y1, y2;
-    rope_rotate(x1, x2, p, inv_freq[i], y1, y2);
+    rope_apply(x1, x2, rope_cs[(size_t)p * (HD / 2) + i], y1, y2);
     st(dst + i, y1);
     st(dst + i + HD / 2, y2);
   } else {
@@ -370,13 +370,13 @@ __global__ void rope_kv_kernel(const float* __restrict__ qkv, int ldqkv, T* __re
 
 int launch_rope_kv(int dtype, int head_dim, const float* qkv, int ldqkv, void* qout, int ldq,
                    const KvView& kv, int L, int layer, int H, int KVH, const RowBlock& rb,
-                   const double* inv_freq, void* local_kv, int* err_flags, hipStream_t s) {
+                   const float2* rope_cs, void* local_kv, int* err_flags, hipStream_t s) {
   if (rb.M <= 0) return 0;
   const dim3 grid(rb.M, H + 2 * KVH);
 #define ROPE_LAUNCH(T, HD)                                                                                     \
   hipLaunchKernelGGL((rope_kv_kernel<T, HD>), grid, dim3(HD / 2), 0, s, qkv, ldqkv, (T*)qout, ldq, (T*)kv.pool, \
                      kv.page_table, kv.n_lpages, kv.page_size, L, layer, H, KVH, rb.M, rb.nrows, rb.pos,        \
-                     inv_freq, (T*)local_kv, err_flags, rb.stop)
+                     rope_cs, (T*)local_kv, err_flags, rb.stop)
   if (dtype == SSD_DTYPE_BF16) {
     if (head_dim == 128) ROPE_LAUNCH(bf16_t, 128); else ROPE_LAUNCH(bf16_t, 64);
   } else {
@@ -390,8 +390,10 @@ int launch_rope_kv(int dtype, int head_dim, const float* qkv, int ldqkv, void* q
 // Attention over the paged cache (device functions in attn.h).
 // ===========================================================================
 
+int attention_nsplit(int max_ctx) { return (max_ctx + ATT_SPLIT - 1) / ATT_SPLIT; }
+
 size_t attention_partial_floats(int max_rows, int H, int head_dim, int max_ctx) {
-  const int nsplit = (max_ctx + ATT_SPLIT - 1) / ATT_SPLIT;
+  const int nsplit = attention_nsplit(max_ctx);
   return (size_t)max_rows * H * nsplit * (head_dim + 2);
 }
 
@@ -434,7 +436,7 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
     // a row block must not straddle two groups
     while (RB > 1 && group_rows % RB != 0) --RB;
   }
-  const int nsplit = (max_ctx + ATT_SPLIT - 1) / ATT_SPLIT;
+  const int nsplit = attention_nsplit(max_ctx);
   const dim3 grid(KVH, nsplit, (rb.M + RB - 1) / RB);
 #define ATT_LAUNCH(T, HD)                                                                                        \
   do {                                                                                                           \
