@@ -90,6 +90,7 @@ struct ssd_seq {
   int fz_max_phase = 0;
   FzProgram fz_cache[FZ_SLOTS];
   int fz_next = 0;
+  uint64_t fz_epoch = 0;     // passes launched (selects the counter set)
 };
 
 namespace {
@@ -139,7 +140,7 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.fz_xg = (bf16_t*)take(2 * (size_t)16 * std::max(D, m->q_dim));
   t.fz_ob = (bf16_t*)take(2 * (size_t)16 * m->q_dim);
   t.fz_ss = (float*)take(sizeof(float) * (size_t)16 * (D / 16 + 1));
-  t.fz_counters = (unsigned*)take(sizeof(unsigned) * (size_t)(max_phase + 1 + L * d.n_kv_heads));
+  t.fz_counters = (unsigned*)take(sizeof(unsigned) * 2 * fz_counter_set_size(max_phase, L, d.n_kv_heads));
   t.fz_prog = (int*)take(sizeof(int) * (size_t)FZ_SLOTS * 2 * max_phase);
   t.fz_gain = (const float**)take(sizeof(float*) * (size_t)FZ_SLOTS * max_phase);
   if (w) *w = t;
@@ -232,8 +233,9 @@ int plan_mask(const ssd_model* m, const uint8_t* mask_in, int exit_layer, std::v
 }
 
 // Phase program of a pass over the sub-layer entries (2l + sub), optionally
-// followed by the LM head.  save_entry: WG 0 copies h before that entry's
-// first phase (entries.size(): before the LM head); -1: no copy.
+// followed by the LM head.  save_entry: the residual that enters that entry
+// (entries.size(): the LM head) is also written to the save buffer by the
+// phase that produces it; -1: none.
 FzProgram fz_build(const ssd_model* m, const std::vector<int>& entries, bool final_lm, int save_entry) {
   FzProgram pr;
   const ssd_model_desc& d = m->d;
@@ -247,7 +249,7 @@ FzProgram fz_build(const ssd_model* m, const std::vector<int>& entries, bool fin
   pr.type.push_back(PH_INIT); pr.layer.push_back(0); pr.gain.push_back(consumer_gain(0));
   for (size_t e = 0; e < entries.size(); ++e) {
     const int l = entries[e] / 2;
-    if ((int)e == save_entry) pr.save_phase = (int)pr.type.size();
+    if ((int)e == save_entry) pr.save_phase = (int)pr.type.size() - 1;
     if (entries[e] % 2 == 0) {
       pr.type.insert(pr.type.end(), {PH_QKV, PH_ATTN, PH_O});
       pr.layer.insert(pr.layer.end(), {l, l, l});
@@ -259,7 +261,7 @@ FzProgram fz_build(const ssd_model* m, const std::vector<int>& entries, bool fin
     }
   }
   if (final_lm) {
-    if (save_entry == (int)entries.size()) pr.save_phase = (int)pr.type.size();
+    if (save_entry == (int)entries.size()) pr.save_phase = (int)pr.type.size() - 1;
     pr.type.push_back(PH_LM); pr.layer.push_back(0); pr.gain.push_back(nullptr);
   }
   return pr;
@@ -320,7 +322,11 @@ int fz_run(ssd_seq* q, const FzProgram& pr, int M, const int* nrows, const int* 
   p.logits = logits; p.save_h = save_h;
   p.pool = (bf16_t*)q->kv.pool; p.page_table = q->kv.page_table; p.PS = q->kv.page_size; p.n_lpages = q->kv.n_lpages;
   p.rope_cs = w.rope_cs;
-  p.counters = w.fz_counters;
+  const size_t set = fz_counter_set_size(q->fz_max_phase, d.n_layers, d.n_kv_heads);
+  p.counters = w.fz_counters + (q->fz_epoch & 1) * set;
+  p.counters_next = w.fz_counters + ((q->fz_epoch + 1) & 1) * set;
+  p.n_counters = (int)set;
+  ++q->fz_epoch;
   p.err = &w.st->error_flags;
   p.stop = stop;
   TRY(launch_fused_pass(p, d.head_dim, q->fz_nwg, s));
@@ -443,7 +449,7 @@ extern "C" int ssd_seq_create(const ssd_model* m, void* kv_pool_dev, int n_pages
                       (const bf16_t*)lw.w_gate_up, (const bf16_t*)lw.w_down};
     }
     int dev = 0, cus = 0, coop = 0, per_cu = 0;
-    const size_t nctr = (size_t)(q->fz_max_phase + 1 + m->d.n_layers * m->d.n_kv_heads);
+    const size_t nctr = 2 * fz_counter_set_size(q->fz_max_phase, m->d.n_layers, m->d.n_kv_heads);
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&

@@ -61,16 +61,47 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
   const float scale = 1.0f / sqrtf((float)HD);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  for (int e = tid; e < nq * HD; e += NT) {
-    const int qi = e / HD, d = e % HD;
-    const int row = r0 + qi / G, head = g * G + qi % G;
-    sm.Qs[qi][d] = ld(q + (size_t)row * ldq + (size_t)head * HD + d);
-    sm.Os[qi][d] = 0.f;
+  // queries: 16-byte loads, all in flight, then fp32 into LDS
+  constexpr int QPER = (ATT_MAXQ * VPR + NT - 1) / NT;
+  {
+    att_u32x4 qreg[QPER];
+#pragma unroll
+    for (int j = 0; j < QPER; ++j) {
+      const int e = tid + NT * j;
+      qreg[j] = att_u32x4{0u, 0u, 0u, 0u};
+      if (e < nq * VPR) {
+        const int qi = e / VPR, vc = e % VPR;
+        const int row = r0 + qi / G, head = g * G + qi % G;
+        qreg[j] = *(const att_u32x4*)(q + (size_t)row * ldq + (size_t)head * HD + vc * VEC);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < QPER; ++j) {
+      const int e = tid + NT * j;
+      if (e < nq * VPR) {
+        const int qi = e / VPR, vc = e % VPR;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if constexpr (sizeof(T) == 2) {
+            sm.Qs[qi][vc * VEC + 2 * w] = __uint_as_float(qreg[j][w] << 16);
+            sm.Qs[qi][vc * VEC + 2 * w + 1] = __uint_as_float(qreg[j][w] & 0xFFFF0000u);
+          } else {
+            sm.Qs[qi][vc * VEC + w] = __uint_as_float(qreg[j][w]);
+          }
+        }
+      }
+    }
   }
+  for (int e = tid; e < nq * HD; e += NT) sm.Os[e / HD][e % HD] = 0.f;
   for (int qi = tid; qi < nq; qi += NT) { sm.Ms[qi] = -INFINITY; sm.Ls[qi] = 0.f; }
   const int grp_base = group_rows > 0 ? (r0 / group_rows) * group_rows : 0;
 
   for (int kc = key_beg; kc < key_end; kc += ATT_CHUNK) {
+    // physical pages of the chunk's cached keys (PS divides 64: at most 64 / PS), one per lane,
+    // so that every key and value load below is independent of any other load
+    const int pg0 = kc / PS;
+    const int cached_end = local_kv ? min(key_end, local_start) : key_end;
+    const int pg = (lane * PS < ATT_CHUNK && kc + lane * PS < cached_end) ? page_table[pg0 + lane] : 0;
     att_u32x4 kreg[NLD], vreg[NLD];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
@@ -80,6 +111,7 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
       const att_u32x4 z = {0u, 0u, 0u, 0u};
       kreg[j] = z;
       vreg[j] = z;
+      const int page = __shfl(pg, t / PS, 64);
       if (kp < key_end) {
         const T* kr;
         const T* vr;
@@ -88,7 +120,6 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
           kr = local_kv + base;
           vr = local_kv + base + (size_t)KVH * HD;
         } else {
-          const int page = page_table[kp / PS];
           kr = pool + kv_index(page, L, layer, 0, KVH, g, PS, kp % PS, HD);
           vr = pool + kv_index(page, L, layer, 1, KVH, g, PS, kp % PS, HD);
         }
@@ -140,8 +171,18 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
       __builtin_amdgcn_wave_barrier();
       for (int d = lane; d < HD; d += 64) {
         float o = __fmul_rn(sm.Os[qi][d], alpha);
-#pragma unroll 8
-        for (int t = 0; t < ATT_CHUNK; ++t) o = fmaf(sm.Pw[wave][t], ld(sm.Vs + t * KST + d), o);
+        // 16 keys' values are read before their 16 multiply-adds (one LDS round trip per 16 keys)
+#pragma unroll
+        for (int t0 = 0; t0 < ATT_CHUNK; t0 += 16) {
+          float vv[16], pw[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            vv[u] = ld(sm.Vs + (t0 + u) * KST + d);
+            pw[u] = sm.Pw[wave][t0 + u];
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u) o = fmaf(pw[u], vv[u], o);
+        }
         sm.Os[qi][d] = o;
       }
       if (lane == 0) { sm.Ms[qi] = m_new; sm.Ls[qi] = __fadd_rn(__fmul_rn(sm.Ls[qi], alpha), psum); }
@@ -160,20 +201,56 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
 }
 
 // Merge the splits of (row, head) in split order; component d of the output.
-template <typename T, int HD>
-__device__ __forceinline__ void attn_combine_elem(const float* __restrict__ part, int nsplit, int row, int head,
-                                                  int H, int p, int d, T* __restrict__ out, int ldo) {
+template <int HD>
+__device__ __forceinline__ float attn_combine_value(const float* __restrict__ part, int nsplit, int row, int head,
+                                                   int H, int p, int d) {
   const int ns = p / ATT_SPLIT + 1;
   const float* pr = part + ((size_t)row * H + head) * nsplit * (HD + 2);
+  constexpr int B = 16;
+  if (ns <= B) {
+    // one round of loads
+    float mv[B], lv[B], ov[B];
+#pragma unroll
+    for (int s = 0; s < B; ++s) {
+      mv[s] = -INFINITY;
+      lv[s] = ov[s] = 0.f;
+      if (s < ns) {
+        mv[s] = pr[s * (HD + 2) + HD];
+        lv[s] = pr[s * (HD + 2) + HD + 1];
+        ov[s] = pr[s * (HD + 2) + d];
+      }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < B; ++s) m = fmaxf(m, mv[s]);
+    float l = 0.f, o = 0.f;
+#pragma unroll
+    for (int s = 0; s < B; ++s) {
+      if (s < ns) {
+        const float w = expf(__fsub_rn(mv[s], m));
+        l = fmaf(lv[s], w, l);
+        o = fmaf(ov[s], w, o);
+      }
+    }
+    return __fdiv_rn(o, l);
+  }
   float m = -INFINITY;
+#pragma unroll 16
   for (int s = 0; s < ns; ++s) m = fmaxf(m, pr[s * (HD + 2) + HD]);
   float l = 0.f, o = 0.f;
+#pragma unroll 16
   for (int s = 0; s < ns; ++s) {
     const float w = expf(__fsub_rn(pr[s * (HD + 2) + HD], m));
     l = fmaf(pr[s * (HD + 2) + HD + 1], w, l);
     o = fmaf(pr[s * (HD + 2) + d], w, o);
   }
-  st(out + (size_t)row * ldo + (size_t)head * HD + d, __fdiv_rn(o, l));
+  return __fdiv_rn(o, l);
+}
+
+template <typename T, int HD>
+__device__ __forceinline__ void attn_combine_elem(const float* __restrict__ part, int nsplit, int row, int head,
+                                                  int H, int p, int d, T* __restrict__ out, int ldo) {
+  st(out + (size_t)row * ldo + (size_t)head * HD + d, attn_combine_value<HD>(part, nsplit, row, head, H, p, d));
 }
 
 }  // namespace ssd

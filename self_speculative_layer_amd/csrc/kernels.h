@@ -122,7 +122,7 @@ struct FzParams {
   const int* ph_layer;
   const float* const* ph_gain;
   int n_phase;
-  int save_phase;            // phase before which WG 0 copies h (rows < Ma) to save_h; -1: none
+  int save_phase;            // phase (INIT or residual) whose output h is also written to save_h; -1: none
   // rows
   int M;
   const int* nrows;
@@ -145,10 +145,20 @@ struct FzParams {
   const int* page_table;
   int PS, n_lpages;
   const float2* rope_cs;     // [position][HD/2] (cos, sin)
-  unsigned* counters;        // [n_phase] + exit + per-attention-phase head counters
+  unsigned* counters;        // counter set of this pass (see fz_counter_set_size); the other set is cleared
+  unsigned* counters_next;   // the counter set of the next pass, cleared by this pass
+  int n_counters;            // counters per set
   int* err;
   const int* stop;
 };
+
+// Phase counters of one pass: per phase one top counter and FZ_GROUPS group
+// counters, then per attention phase one counter per KV head.  Two sets
+// alternate between consecutive passes.
+constexpr int FZ_GROUPS = 8;
+inline size_t fz_counter_set_size(int max_phase, int n_layers, int n_kv_heads) {
+  return (size_t)max_phase * (1 + FZ_GROUPS) + (size_t)n_layers * n_kv_heads;
+}
 
 int launch_fused_pass(const FzParams& p, int head_dim, int nwg, hipStream_t s);
 int fused_pass_max_blocks_per_cu(int head_dim, int* blocks);

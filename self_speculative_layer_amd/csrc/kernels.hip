@@ -248,30 +248,38 @@ static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, 
 // inv[m] = 1 / sqrt(mean(h^2) + eps) (the RMS scale is applied to the
 // projection's output).  One workgroup per row.
 template <typename T>
-__global__ __launch_bounds__(256) void rowprep_kernel(const float* __restrict__ h, int ldh,
-                                                      const float* __restrict__ gain, T* __restrict__ x,
-                                                      int ldx, float* __restrict__ inv, int M, int D, float eps,
-                                                      const int* __restrict__ nrows,
-                                                      const int* __restrict__ hmap, const int* __restrict__ stop) {
+__global__ __launch_bounds__(1024) void rowprep_kernel(const float* __restrict__ h, int ldh,
+                                                       const float* __restrict__ gain, T* __restrict__ x,
+                                                       int ldx, float* __restrict__ inv, int M, int D, float eps,
+                                                       const int* __restrict__ nrows,
+                                                       const int* __restrict__ hmap, const int* __restrict__ stop) {
   if (stop && *stop) return;
   const int row = blockIdx.x;
   if (row >= active_rows(M, nrows)) return;
   const float* hr = h + (size_t)(hmap ? hmap[row] : row) * ldh;
   T* xr = x + (size_t)row * ldx;
   __shared__ float tss[1024];                  // group sums, D <= 16384
-  const int ntiles = D / 16;
-  for (int base = 0; base < ntiles * 16; base += 256) {
-    const int i = base + threadIdx.x;
-    const float v = i < D ? hr[i] : 0.f;
-    const float s = tile16_ss_lanes(v);
+  constexpr int PER = 16;                      // D / 1024 elements per thread at most
+  float v[PER], gv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {              // every load in flight before the first use
+    const int i = j * 1024 + threadIdx.x;
+    v[j] = i < D ? hr[i] : 0.f;
+    gv[j] = i < D ? gain[i] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = j * 1024 + threadIdx.x;
+    if (j * 1024 >= D) break;                  // uniform: D is a multiple of 16
+    const float s = tile16_ss_lanes(v[j]);
     if (i < D) {
       if ((threadIdx.x & 15) == 0) tss[i >> 4] = s;
-      st(xr + i, __fmul_rn(v, gain[i]));
+      st(xr + i, __fmul_rn(v[j], gv[j]));
     }
   }
   __syncthreads();
   if (threadIdx.x < 64) {
-    const float tot = row_ss_total(tss, 1, ntiles);
+    const float tot = row_ss_total(tss, 1, D / 16);
     if (threadIdx.x == 0) inv[row] = inv_rms(tot, D, eps);
   }
 }
@@ -281,10 +289,10 @@ int launch_rowprep(int dtype, const float* h, int ldh, const float* gain, void* 
   if (M <= 0) return 0;
   if (D % 16 != 0 || D > 16384) return SSD_ERR_SHAPE;
   if (dtype == SSD_DTYPE_BF16)
-    hipLaunchKernelGGL(rowprep_kernel<bf16_t>, dim3(M), dim3(256), 0, s, h, ldh, gain, (bf16_t*)x, ldx, inv, M, D,
+    hipLaunchKernelGGL(rowprep_kernel<bf16_t>, dim3(M), dim3(1024), 0, s, h, ldh, gain, (bf16_t*)x, ldx, inv, M, D,
                        eps, nrows, hmap, stop);
   else
-    hipLaunchKernelGGL(rowprep_kernel<float>, dim3(M), dim3(256), 0, s, h, ldh, gain, (float*)x, ldx, inv, M, D,
+    hipLaunchKernelGGL(rowprep_kernel<float>, dim3(M), dim3(1024), 0, s, h, ldh, gain, (float*)x, ldx, inv, M, D,
                        eps, nrows, hmap, stop);
   return last_launch();
 }
@@ -303,6 +311,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ emb, c
   const int t = min(max(tokens[row], 0), V - 1);   // ids are produced in range; clamp keeps reads in bounds
   const T* e = emb + (size_t)t * D;
   float* hr = h + (size_t)row * ldh;
+#pragma unroll 8
   for (int i = threadIdx.x; i < D; i += 256) hr[i] = ld(e + i);
 }
 
