@@ -66,6 +66,16 @@ typedef __attribute__((address_space(3))) void fz_lds_t;
 // scalar branches.
 __device__ __forceinline__ int fz_wave() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// A pointer or count that is the same in every lane (read from memory with a
+// vector load), moved to scalar registers so that buffer resources built from
+// it stay scalar.
+template <typename T>
+__device__ __forceinline__ T* fz_uniform(T* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
 template <int HD>
 struct FzAttnSmem {
   static constexpr int VPR = HD / 8;            // 16-byte chunks per key row
@@ -255,25 +265,35 @@ __device__ __forceinline__ bool fz_is_gemm(int type) {
   return type == PH_QKV || type == PH_O || type == PH_GU || type == PH_DOWN || type == PH_LM;
 }
 
+// The streaming waves read weights and activations with buffer loads to LDS:
+// a buffer resource per matrix (base, size in bytes), a per-lane 32-bit byte
+// offset and a wave-uniform offset for the k-block, so a k-block costs two
+// scalar adds and one load instruction.  A lane whose activation row is >= Ma
+// reads past the resource's end and receives zeros (bounds-checked buffer
+// access), which keeps those MFMA columns finite without an exec mask.
+constexpr int FZ_RSRC_WORD3 = 0x00020000;       // raw buffer, 32-bit data format
+
 struct FzGeo {
+  __amdgpu_buffer_rsrc_t rw, rx;
   const bf16_t* W;
-  const bf16_t* X;
   int type, K, nrow_w, ntiles;
   int kb0, nw;        // this streaming wave's k-blocks [kb0, kb0 + nw) of every tile
   int nit;            // tiles of this workgroup
   int total;          // units (k-blocks) of this wave in the phase: nit * nw
+  uint32_t voff_x;    // this lane's activation offset (bytes) at the slice start
 };
 
-__device__ __forceinline__ FzGeo fz_geo(const FzParams& p, int type, int layer, int wave) {
+__device__ __forceinline__ FzGeo fz_geo(const FzParams& p, int type, int layer, int wave, int Ma) {
   FzGeo g;
   const int qd = p.H * p.HD, kvd = p.KVH * p.HD;
+  const bf16_t* X;
   g.type = type;
   switch (type) {
-    case PH_QKV: g.W = p.layers[layer].w_qkv; g.X = p.xg; g.K = p.D; g.nrow_w = qd + 2 * kvd; break;
-    case PH_O: g.W = p.layers[layer].w_o; g.X = p.ob; g.K = qd; g.nrow_w = p.D; break;
-    case PH_GU: g.W = p.layers[layer].w_gate_up; g.X = p.xg; g.K = p.D; g.nrow_w = 2 * p.F; break;
-    case PH_DOWN: g.W = p.layers[layer].w_down; g.X = p.ab; g.K = p.F; g.nrow_w = p.D; break;
-    default: g.W = p.lm_head; g.X = p.xg; g.K = p.D; g.nrow_w = p.V; break;
+    case PH_QKV: g.W = p.layers[layer].w_qkv; X = p.xg; g.K = p.D; g.nrow_w = qd + 2 * kvd; break;
+    case PH_O: g.W = p.layers[layer].w_o; X = p.ob; g.K = qd; g.nrow_w = p.D; break;
+    case PH_GU: g.W = p.layers[layer].w_gate_up; X = p.xg; g.K = p.D; g.nrow_w = 2 * p.F; break;
+    case PH_DOWN: g.W = p.layers[layer].w_down; X = p.ab; g.K = p.F; g.nrow_w = p.D; break;
+    default: g.W = p.lm_head; X = p.xg; g.K = p.D; g.nrow_w = p.V; break;
   }
   g.ntiles = fz_ntiles(p, type);
   const int nu = g.K >> 6;
@@ -282,56 +302,57 @@ __device__ __forceinline__ FzGeo fz_geo(const FzParams& p, int type, int layer, 
   const int wg = blockIdx.x, NWG = gridDim.x;
   g.nit = wg < g.ntiles ? (g.ntiles - wg + NWG - 1) / NWG : 0;
   g.total = g.nit * g.nw;
+  g.W = fz_uniform(g.W);
+  g.rw = __builtin_amdgcn_make_buffer_rsrc((void*)g.W, (short)0, (int)min((size_t)g.nrow_w * g.K * 2, (size_t)0x7FFFFFFF),
+                                           FZ_RSRC_WORD3);
+  g.rx = __builtin_amdgcn_make_buffer_rsrc((void*)fz_uniform(X), (short)0,
+                                           __builtin_amdgcn_readfirstlane(Ma * g.K * 2), FZ_RSRC_WORD3);
+  const int lane = threadIdx.x & 63;
+  g.voff_x = (uint32_t)((lane & 15) * g.K * 2 + (lane >> 4) * 16 + g.kb0 * 64);
   return g;
 }
 
 // A streaming wave's position in its unit sequence: unit u = item j (tile
-// wg + j * NWG), k-block kb.
+// wg + j * NWG), k-block kbi of the wave's slice.
 struct FzCur {
-  int u, j, kb;
-  const bf16_t* wp;   // this lane's weight row (+ its 8-column group) of the current tile
+  int u, j, kbi;
+  uint32_t voff;      // this lane's weight offset (bytes): its row of the current tile at the slice start
 };
 
-__device__ __forceinline__ const bf16_t* fz_wptr(const FzGeo& g, int tile, int HD, int F) {
+__device__ __forceinline__ uint32_t fz_wvoff(const FzGeo& g, int tile, int HD, int F) {
   const int lane = threadIdx.x & 63;
   const int row = fz_wrow(g.type, tile, lane & 15, HD, F);
-  // a row past the matrix (last LM tile) reads row 0: it only feeds discarded outputs
-  return g.W + (size_t)(row < g.nrow_w ? row : 0) * g.K + (lane >> 4) * 8;
+  // a row past the matrix (last LM tile) reads past the resource: zeros, discarded outputs
+  if (row >= g.nrow_w) return 0xFFFFF000u;
+  return (uint32_t)row * (uint32_t)g.K * 2u + (uint32_t)((lane >> 4) * 16 + g.kb0 * 64);
 }
 
 __device__ __forceinline__ void fz_cur_init(FzCur& c, const FzGeo& g, int HD, int F) {
   c.u = 0;
   c.j = 0;
-  c.kb = g.kb0;
-  c.wp = fz_wptr(g, blockIdx.x, HD, F);
+  c.kbi = 0;
+  c.voff = fz_wvoff(g, blockIdx.x, HD, F);
 }
 
 __device__ __forceinline__ void fz_cur_next(FzCur& c, const FzGeo& g, int HD, int F) {
   ++c.u;
-  if (++c.kb == g.kb0 + g.nw) {
-    c.kb = g.kb0;
+  if (++c.kbi == g.nw) {
+    c.kbi = 0;
     ++c.j;
     const int tile = blockIdx.x + c.j * gridDim.x;
-    if (tile < g.ntiles) c.wp = fz_wptr(g, tile, HD, F);
+    if (tile < g.ntiles) c.voff = fz_wvoff(g, tile, HD, F);
   }
 }
 
-template <int HD>
-__device__ __forceinline__ void fz_issue_w(FzSmem<HD>& sm, unsigned slot, const FzCur& c) {
-  const int wave = fz_wave();
-  __builtin_amdgcn_global_load_lds((const void*)(c.wp + c.kb * 32), (fz_lds_t*)&sm.ring[wave][slot][0][0], 16, 0,
-                                   FZ_CPOL_NT);
+// ring: this wave's ring in LDS, FZ_S slots of (weights 1 KB, activations 1 KB)
+__device__ __forceinline__ void fz_issue_w(unsigned char* ring, unsigned slot, const FzGeo& g, const FzCur& c) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rw, (fz_lds_t*)(ring + slot * 2048), 16, c.voff, c.kbi * 64, 0,
+                                           FZ_CPOL_NT);
 }
 
-// Activation block of the unit: lane l reads row l % 16, only for rows < Ma
-// (the other lanes' bytes keep stale values, which only reach output columns
-// that the epilogue discards).
-template <int HD>
-__device__ __forceinline__ void fz_issue_x(FzSmem<HD>& sm, unsigned slot, const FzGeo& g, const FzCur& c, int Ma) {
-  const int lane = threadIdx.x & 63, wave = fz_wave();
-  if ((lane & 15) < Ma)
-    __builtin_amdgcn_global_load_lds((const void*)(g.X + (size_t)(lane & 15) * g.K + (lane >> 4) * 8 + c.kb * 32),
-                                     (fz_lds_t*)&sm.ring[wave][slot][1][0], 16, 0, 0);
+__device__ __forceinline__ void fz_issue_x(unsigned char* ring, unsigned slot, const FzGeo& g, const FzCur& c) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rx, (fz_lds_t*)(ring + slot * 2048 + 1024), 16, g.voff_x, c.kbi * 64, 0,
+                                           0);
 }
 
 // ---------------------------------------------------------------------------
@@ -763,13 +784,14 @@ __global__ __launch_bounds__(FZ_NT, 1) void fused_pass_kernel(FzParams p) {
       const int ntiles = fz_ntiles(p, type);
       const int nit = wg < ntiles ? (ntiles - wg + NWG - 1) / NWG : 0;
       if (!ctrl) {
-        const FzGeo g = fz_geo(p, type, layer, wave);
+        const FzGeo g = fz_geo(p, type, layer, wave, Ma);
+        unsigned char* const ring = &sm.ring[wave][0][0][0];
         const int k = min(FZ_S, g.total);
         FzCur ci;
         fz_cur_init(ci, g, HD, p.F);
         for (int i = 0; i < pre; ++i) fz_cur_next(ci, g, HD, p.F);
         for (; ci.u < k; fz_cur_next(ci, g, HD, p.F)) {
-          fz_issue_w(sm, (gpos + ci.u) % FZ_S, ci);
+          fz_issue_w(ring, (gpos + ci.u) % FZ_S, g, ci);
           ++n_iss;
         }
         // the cached keys/values of this workgroup's first item of the coming attention phase
@@ -786,7 +808,7 @@ __global__ __launch_bounds__(FZ_NT, 1) void fused_pass_kernel(FzParams p) {
           FzCur cx;
           fz_cur_init(cx, g, HD, p.F);
           for (; cx.u < k; fz_cur_next(cx, g, HD, p.F)) {
-            fz_issue_x(sm, (gpos + cx.u) % FZ_S, g, cx, Ma);
+            fz_issue_x(ring, (gpos + cx.u) % FZ_S, g, cx);
             ++n_iss;
           }
         }
@@ -799,11 +821,11 @@ __global__ __launch_bounds__(FZ_NT, 1) void fused_pass_kernel(FzParams p) {
         FzCur cn{};
         int kn = 0;
         if (has_next) {
-          gn = fz_geo(p, p.ph_type[nph], p.ph_layer[nph], wave);
+          gn = fz_geo(p, p.ph_type[nph], p.ph_layer[nph], wave, Ma);
           kn = min(FZ_S, gn.total);
           fz_cur_init(cn, gn, HD, p.F);
           for (; cn.u < kn && g.total + cn.u - FZ_S < 0; fz_cur_next(cn, gn, HD, p.F)) {
-            fz_issue_w(sm, (gpos + g.total + cn.u) % FZ_S, cn);
+            fz_issue_w(ring, (gpos + g.total + cn.u) % FZ_S, gn, cn);
             ++n_iss;
           }
         }
@@ -813,22 +835,40 @@ __global__ __launch_bounds__(FZ_NT, 1) void fused_pass_kernel(FzParams p) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           int left = g.nw;                                 // units left in the current item
           unsigned slot = gpos % FZ_S;
-          for (int u = 0; u < g.total; ++u, slot = slot + 1 == FZ_S ? 0 : slot + 1) {
-            const unsigned seqx = u < k ? xs0 + (unsigned)u : rs0 + 2u * (unsigned)(u - k) + 1u;
-            fz_wait_vm((int)(n_iss - seqx - 1u));
-            const fz_u32x4 a = *(const fz_u32x4*)&sm.ring[wave][slot][0][lane * 16];
-            const fz_u32x4 b = *(const fz_u32x4*)&sm.ring[wave][slot][1][lane * 16];
+          // main part: every unit's slot is refilled with unit u + S of this phase.  The wait for
+          // unit u: its activation load was issued in the prologue batch (u < S: at least S - 1
+          // loads issued after it) or as a refill pair S units ago (exactly 2 (S - 1) after it).
+          const int main_end = g.total - FZ_S;             // < 0 when the phase has fewer than S units
+          int u = 0;
+          for (; u < main_end; ++u, slot = slot + 1 == FZ_S ? 0 : slot + 1) {
+            if (u < FZ_S) fz_vmcnt<FZ_S - 1>();
+            else fz_vmcnt<2 * FZ_S - 2>();
+            const fz_u32x4 a = *(const fz_u32x4*)(ring + slot * 2048 + lane * 16);
+            const fz_u32x4 b = *(const fz_u32x4*)(ring + slot * 2048 + 1024 + lane * 16);
             fz_lgkm_drain();                               // the slot is read before it is refilled
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                           __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-            if (ci.u < g.total) {
-              fz_issue_w(sm, slot, ci);
-              fz_issue_x(sm, slot, g, ci, Ma);
-              n_iss += 2;
-              fz_cur_next(ci, g, HD, p.F);
+            fz_issue_w(ring, slot, g, ci);
+            fz_issue_x(ring, slot, g, ci);
+            fz_cur_next(ci, g, HD, p.F);
+            if (--left == 0) {
+              left = g.nw;
+              fz_deposit(sm, ib++, wave, acc, p.err);
+              acc = f32x4{0.f, 0.f, 0.f, 0.f};
             }
+          }
+          n_iss += 2u * (unsigned)max(main_end, 0);
+          // tail: no refill of this phase; the freed slots take the next phase's weights
+          for (; u < g.total; ++u, slot = slot + 1 == FZ_S ? 0 : slot + 1) {
+            const unsigned seqx = u < k ? xs0 + (unsigned)u : rs0 + 2u * (unsigned)(u - k) + 1u;
+            fz_wait_vm((int)(n_iss - seqx - 1u));
+            const fz_u32x4 a = *(const fz_u32x4*)(ring + slot * 2048 + lane * 16);
+            const fz_u32x4 b = *(const fz_u32x4*)(ring + slot * 2048 + 1024 + lane * 16);
+            fz_lgkm_drain();
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
             for (; cn.u < kn && g.total + cn.u - FZ_S <= u; fz_cur_next(cn, gn, HD, p.F)) {
-              fz_issue_w(sm, (gpos + g.total + cn.u) % FZ_S, cn);
+              fz_issue_w(ring, (gpos + g.total + cn.u) % FZ_S, gn, cn);
               ++n_iss;
             }
             if (--left == 0) {
@@ -839,7 +879,7 @@ __global__ __launch_bounds__(FZ_NT, 1) void fused_pass_kernel(FzParams p) {
           }
         }
         for (; cn.u < kn; fz_cur_next(cn, gn, HD, p.F)) {
-          fz_issue_w(sm, (gpos + g.total + cn.u) % FZ_S, cn);
+          fz_issue_w(ring, (gpos + g.total + cn.u) % FZ_S, gn, cn);
           ++n_iss;
         }
         gpos += g.total;
@@ -847,11 +887,12 @@ __global__ __launch_bounds__(FZ_NT, 1) void fused_pass_kernel(FzParams p) {
       } else {
         // control wave: every workgroup has finished the previous phase
         fz_wait_phase(p, ph - 1);
+        fz_lds_barrier();                                  // GO: the streaming waves start now
+        // the 1/rms of the rows and the first epilogue's inputs load while the first tile streams
         const bool scaled = type == PH_QKV || type == PH_GU || type == PH_LM;
         if (scaled) fz_row_inv(p, Ma, sm.inv);
         FzPre pf;
         if (nit > 0) fz_epi_prefetch(p, sm, type, wg, Ma, gain, pf);
-        fz_lds_barrier();                                  // GO
         const bool save = ph == p.save_phase;
         for (int it = 0; it < nit; ++it, ++ib) {
           const int tile = wg + it * NWG;
