@@ -29,22 +29,26 @@ struct AttnSmem {
   static constexpr int KST = HD + EPW;              // padded row stride: lanes on different keys hit different banks
   T Ks[ATT_CHUNK * KST];
   T Vs[ATT_CHUNK * KST];
-  float Qs[ATT_MAXQ][HD];
-  float Os[ATT_MAXQ][HD];
-  float Ms[ATT_MAXQ], Ls[ATT_MAXQ];
+  alignas(16) T Qs[ATT_MAXQ * HD];
   float Pw[NW][ATT_CHUNK];
+  int Rpos[ATT_MAXQ];
 };
 
 typedef uint32_t att_u32x4 __attribute__((ext_vector_type(4)));
 
-// One work item: KV head g, split s, rows r0..r1-1 (positions increasing).
-// Keys at positions >= local_start come from local_kv rows (scoring: the
-// candidate's own keys/values, rows grouped by group_rows).  Requires all
-// NW*64 threads of the block.
+// One work item: KV head g, split s, the rows r0 .. min(r0 + RB, Ma) - 1 with
+// Ma = min(M, *nrows) (positions increasing).  Keys at positions >= local_start
+// come from local_kv rows (scoring: the candidate's own keys/values, rows
+// grouped by group_rows).  Requires all NW*64 threads of the block.
+//
+// Loads take two rounds: (1) the active-row count, the rows' positions, the
+// chunk's page ids and the queries; (2) every key and value of the chunk.
+// Items whose split starts past the block's last position return after (1).
 template <typename T, int HD, int NW>
 __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__ q, int ldq,
-                                  const T* __restrict__ pool, const int* __restrict__ page_table, int PS, int L,
-                                  int layer, int H, int KVH, const int* __restrict__ pos, int r0, int r1, int g,
+                                  const T* __restrict__ pool, const int* __restrict__ page_table, int PS,
+                                  int n_lpages, int L, int layer, int H, int KVH, int M,
+                                  const int* __restrict__ nrows, const int* __restrict__ pos, int r0, int RB, int g,
                                   int s, int nsplit, const T* __restrict__ local_kv, int local_start, int group_rows,
                                   float* __restrict__ part) {
   constexpr int NT = NW * 64;
@@ -54,77 +58,63 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
   constexpr int NLD = ATT_CHUNK * VPR / NT;           // vectors per thread per matrix
   static_assert(NLD >= 1 && ATT_CHUNK * VPR % NT == 0, "staging layout");
   const int G = H / KVH;
-  const int nq = (r1 - r0) * G;
   const int key_beg = s * ATT_SPLIT;
-  const int maxpos = pos[r1 - 1];
-  const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
   const float scale = 1.0f / sqrtf((float)HD);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rmax = min(r0 + RB, M);                   // rows of the block if every row is active
 
-  // queries: 16-byte loads, all in flight, then fp32 into LDS
+  // ---- round 1
+  const int na = nrows ? *nrows : M;
+  int rp = 0;
+  if (tid < rmax - r0) rp = pos[r0 + tid];
+  const int pg0 = key_beg / PS;
+  const int pg = (lane * PS < ATT_CHUNK && pg0 + lane < n_lpages) ? page_table[pg0 + lane] : 0;
   constexpr int QPER = (ATT_MAXQ * VPR + NT - 1) / NT;
-  {
-    att_u32x4 qreg[QPER];
+  const int nq_max = (rmax - r0) * G;
+  att_u32x4 qreg[QPER];
 #pragma unroll
-    for (int j = 0; j < QPER; ++j) {
-      const int e = tid + NT * j;
-      qreg[j] = att_u32x4{0u, 0u, 0u, 0u};
-      if (e < nq * VPR) {
-        const int qi = e / VPR, vc = e % VPR;
-        const int row = r0 + qi / G, head = g * G + qi % G;
-        qreg[j] = *(const att_u32x4*)(q + (size_t)row * ldq + (size_t)head * HD + vc * VEC);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < QPER; ++j) {
-      const int e = tid + NT * j;
-      if (e < nq * VPR) {
-        const int qi = e / VPR, vc = e % VPR;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          if constexpr (sizeof(T) == 2) {
-            sm.Qs[qi][vc * VEC + 2 * w] = __uint_as_float(qreg[j][w] << 16);
-            sm.Qs[qi][vc * VEC + 2 * w + 1] = __uint_as_float(qreg[j][w] & 0xFFFF0000u);
-          } else {
-            sm.Qs[qi][vc * VEC + w] = __uint_as_float(qreg[j][w]);
-          }
-        }
-      }
-    }
+  for (int j = 0; j < QPER; ++j) {
+    const int e = min(tid + NT * j, nq_max * VPR - 1);      // clamped: every lane loads a valid address
+    const int qi = e / VPR, vc = e % VPR;
+    const int row = r0 + qi / G, head = g * G + qi % G;
+    qreg[j] = *(const att_u32x4*)(q + (size_t)row * ldq + (size_t)head * HD + vc * VEC);
   }
-  for (int e = tid; e < nq * HD; e += NT) sm.Os[e / HD][e % HD] = 0.f;
-  for (int qi = tid; qi < nq; qi += NT) { sm.Ms[qi] = -INFINITY; sm.Ls[qi] = 0.f; }
+  if (tid < rmax - r0) sm.Rpos[tid] = rp;
+  __syncthreads();
+  const int Ma = min(M, na);
+  const int r1 = min(r0 + RB, Ma);
+  if (r1 <= r0) return;                               // uniform
+  const int maxpos = sm.Rpos[r1 - 1 - r0];
+  if (key_beg > maxpos) return;                       // uniform: no row sees a key of this split
+  const int nq = (r1 - r0) * G;
+  const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
+#pragma unroll
+  for (int j = 0; j < QPER; ++j) {
+    const int e = tid + NT * j;
+    if (e < nq * VPR) *(att_u32x4*)(sm.Qs + e * VEC) = qreg[j];
+  }
   const int grp_base = group_rows > 0 ? (r0 / group_rows) * group_rows : 0;
-
-  for (int kc = key_beg; kc < key_end; kc += ATT_CHUNK) {
-    // physical pages of the chunk's cached keys (PS divides 64: at most 64 / PS), one per lane,
-    // so that every key and value load below is independent of any other load
-    const int pg0 = kc / PS;
-    const int cached_end = local_kv ? min(key_end, local_start) : key_end;
-    const int pg = (lane * PS < ATT_CHUNK && kc + lane * PS < cached_end) ? page_table[pg0 + lane] : 0;
+  static_assert(ATT_SPLIT == ATT_CHUNK, "one chunk per split");
+  {
+    const int kc = key_beg;
+    // ---- round 2: every key and value of the chunk (clamped addresses, zero past the end)
     att_u32x4 kreg[NLD], vreg[NLD];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int e = tid + NT * j;
       const int t = e / VPR, vc = e % VPR;
       const int kp = kc + t;
-      const att_u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[j] = z;
-      vreg[j] = z;
-      const int page = __shfl(pg, t / PS, 64);
-      if (kp < key_end) {
-        const T* kr;
-        const T* vr;
-        if (local_kv && kp >= local_start) {
-          const size_t base = ((size_t)(grp_base + (kp - local_start)) * 2) * KVH * HD + (size_t)g * HD;
-          kr = local_kv + base;
-          vr = local_kv + base + (size_t)KVH * HD;
-        } else {
-          kr = pool + kv_index(page, L, layer, 0, KVH, g, PS, kp % PS, HD);
-          vr = pool + kv_index(page, L, layer, 1, KVH, g, PS, kp % PS, HD);
-        }
-        kreg[j] = *(const att_u32x4*)(kr + vc * VEC);
-        vreg[j] = *(const att_u32x4*)(vr + vc * VEC);
+      const int kq = min(kp, key_end - 1);
+      const int page = __shfl(pg, (kq - kc) / PS, 64);
+      const bool local = local_kv && kq >= local_start;
+      const size_t lbase = ((size_t)(grp_base + (kq - local_start)) * 2) * KVH * HD + (size_t)g * HD;
+      const T* kr = local ? local_kv + lbase : pool + kv_index(page, L, layer, 0, KVH, g, PS, kq % PS, HD);
+      const T* vr = local ? local_kv + lbase + (size_t)KVH * HD : pool + kv_index(page, L, layer, 1, KVH, g, PS, kq % PS, HD);
+      kreg[j] = *(const att_u32x4*)(kr + vc * VEC);
+      vreg[j] = *(const att_u32x4*)(vr + vc * VEC);
+      if (kp >= key_end) {
+        kreg[j] = att_u32x4{0u, 0u, 0u, 0u};
+        vreg[j] = att_u32x4{0u, 0u, 0u, 0u};
       }
     }
     __syncthreads();      // the previous chunk's readers are done
@@ -138,41 +128,43 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
       for (int w = 0; w < 4; ++w) { kd[w] = kreg[j][w]; vd[w] = vreg[j][w]; }
     }
     __syncthreads();
+    // one split = one chunk: each query's partial (o, m, l) follows from an empty online-softmax
+    // state (o = 0 * 0 + sum p v, m = max, l = 0 * 0 + sum p) and is written directly
     for (int qi = wave; qi < nq; qi += NW) {
-      const int row = r0 + qi / G;
-      const int prow = pos[row];
+      const int row = r0 + qi / G, head = g * G + qi % G;
+      const int prow = sm.Rpos[row - r0];
+      if (key_beg > prow) continue;             // the row sees no key of this split (wave-uniform)
       const int kp = kc + lane;
       const bool valid = kp < key_end && kp <= prow;
       float sc = -INFINITY;
       if (valid) {
         float acc = 0.f;
         const T* kr = sm.Ks + lane * KST;
+        const T* qr = sm.Qs + qi * HD;
         if constexpr (sizeof(T) == 2) {
 #pragma unroll 16
           for (int d = 0; d < HD; d += 2) {
             const uint32_t w2 = *(const uint32_t*)(kr + d);
-            acc = fmaf(sm.Qs[qi][d], __uint_as_float(w2 << 16), acc);
-            acc = fmaf(sm.Qs[qi][d + 1], __uint_as_float(w2 & 0xFFFF0000u), acc);
+            const uint32_t q2 = *(const uint32_t*)(qr + d);
+            acc = fmaf(__uint_as_float(q2 << 16), __uint_as_float(w2 << 16), acc);
+            acc = fmaf(__uint_as_float(q2 & 0xFFFF0000u), __uint_as_float(w2 & 0xFFFF0000u), acc);
           }
         } else {
 #pragma unroll 16
-          for (int d = 0; d < HD; ++d) acc = fmaf(sm.Qs[qi][d], ld(kr + d), acc);
+          for (int d = 0; d < HD; ++d) acc = fmaf(ld(qr + d), ld(kr + d), acc);
         }
         sc = __fmul_rn(acc, scale);
       }
       const float mx = wave_max(sc);
-      if (mx == -INFINITY) continue;            // no visible key in this chunk (wave-uniform)
-      const float m_old = sm.Ms[qi];
-      const float m_new = fmaxf(m_old, mx);
-      const float alpha = expf(__fsub_rn(m_old, m_new));   // 0 when m_old = -inf
-      const float pexp = valid ? expf(__fsub_rn(sc, m_new)) : 0.f;
+      const float pexp = valid ? expf(__fsub_rn(sc, mx)) : 0.f;
       const float psum = wave_sum(pexp);
       sm.Pw[wave][lane] = pexp;
       __builtin_amdgcn_wave_barrier();
+      float* dstp = part + (((size_t)row * H + head) * nsplit + s) * (HD + 2);
       for (int d = lane; d < HD; d += 64) {
-        float o = __fmul_rn(sm.Os[qi][d], alpha);
+        float o = 0.f;
         // 16 keys' values are read before their 16 multiply-adds (one LDS round trip per 16 keys)
-#pragma unroll
+#pragma unroll 1
         for (int t0 = 0; t0 < ATT_CHUNK; t0 += 16) {
           float vv[16], pw[16];
 #pragma unroll
@@ -183,19 +175,14 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
 #pragma unroll
           for (int u = 0; u < 16; ++u) o = fmaf(pw[u], vv[u], o);
         }
-        sm.Os[qi][d] = o;
+        dstp[d] = o;
       }
-      if (lane == 0) { sm.Ms[qi] = m_new; sm.Ls[qi] = __fadd_rn(__fmul_rn(sm.Ls[qi], alpha), psum); }
+      if (lane == 0) {
+        dstp[HD] = mx;
+        dstp[HD + 1] = psum;
+      }
       __builtin_amdgcn_wave_barrier();
     }
-  }
-  __syncthreads();
-  for (int e = tid; e < nq * (HD + 2); e += NT) {
-    const int qi = e / (HD + 2), c = e % (HD + 2);
-    const int row = r0 + qi / G, head = g * G + qi % G;
-    if (s * ATT_SPLIT > pos[row]) continue;     // the row sees no key of this split
-    float* dstp = part + (((size_t)row * H + head) * nsplit + s) * (HD + 2);
-    dstp[c] = c < HD ? sm.Os[qi][c] : (c == HD ? sm.Ms[qi] : sm.Ls[qi]);
   }
   __syncthreads();
 }

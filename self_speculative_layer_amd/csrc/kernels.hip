@@ -409,19 +409,14 @@ size_t attention_partial_floats(int max_rows, int H, int head_dim, int max_ctx) 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_partial_kernel(
     const T* __restrict__ q, int ldq, const T* __restrict__ pool, const int* __restrict__ page_table, int PS,
-    int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows, const int* __restrict__ pos, int RB,
-    int nsplit, const T* __restrict__ local_kv, int local_start, int group_rows, float* __restrict__ part,
-    const int* __restrict__ stop) {
+    int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
+    const int* __restrict__ pos, int RB, int nsplit, const T* __restrict__ local_kv, int local_start, int group_rows,
+    float* __restrict__ part, const int* __restrict__ stop) {
   if (stop && *stop) return;
   const int g = blockIdx.x, s = blockIdx.y, rbk = blockIdx.z;
-  const int Ma = active_rows(M, nrows);
-  const int r0 = rbk * RB;
-  if (r0 >= Ma) return;
-  const int r1 = min(r0 + RB, Ma);
-  if (s * ATT_SPLIT > pos[r1 - 1]) return;
   __shared__ AttnSmem<T, HD, 4> sm;
-  attn_partial_item<T, HD, 4>(sm, q, ldq, pool, page_table, PS, L, layer, H, KVH, pos, r0, r1, g, s, nsplit,
-                              local_kv, local_start, group_rows, part);
+  attn_partial_item<T, HD, 4>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, rbk * RB,
+                              RB, g, s, nsplit, local_kv, local_start, group_rows, part);
 }
 
 template <typename T, int HD>
@@ -450,8 +445,8 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
 #define ATT_LAUNCH(T, HD)                                                                                        \
   do {                                                                                                           \
     hipLaunchKernelGGL((attn_partial_kernel<T, HD>), grid, dim3(256), 0, s, (const T*)q, ldq, (const T*)kv.pool, \
-                       kv.page_table, kv.page_size, L, layer, H, KVH, rb.M, rb.nrows, rb.pos, RB, nsplit,        \
-                       (const T*)local_kv, local_start, group_rows, part, rb.stop);                              \
+                       kv.page_table, kv.page_size, kv.n_lpages, L, layer, H, KVH, rb.M, rb.nrows, rb.pos, RB,    \
+                       nsplit, (const T*)local_kv, local_start, group_rows, part, rb.stop);                      \
     hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(rb.M, H), dim3(HD), 0, s, part, nsplit, rb.M, rb.nrows, \
                        rb.pos, H, (T*)out, ldo, rb.stop);                                                        \
   } while (0)
