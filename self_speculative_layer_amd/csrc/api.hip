@@ -66,6 +66,8 @@ struct Workspace {
   unsigned* fz_counters;
   int* fz_prog;          // FZ_SLOTS slots of [types | layers] ints
   const float** fz_gain; // FZ_SLOTS slots of gain pointers
+  // decode mode (xg / ss above are shared with it)
+  unsigned* dec_ctr;     // attention merge counters [16][KVH], zero between launches
 };
 
 constexpr int FZ_SLOTS = 12;
@@ -143,6 +145,7 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.fz_counters = (unsigned*)take(sizeof(unsigned) * 2 * fz_counter_set_size(max_phase, L, d.n_kv_heads));
   t.fz_prog = (int*)take(sizeof(int) * (size_t)FZ_SLOTS * 2 * max_phase);
   t.fz_gain = (const float**)take(sizeof(float*) * (size_t)FZ_SLOTS * max_phase);
+  t.dec_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)16 * d.n_kv_heads);
   if (w) *w = t;
   return off;
 }
@@ -337,6 +340,94 @@ bool fz_usable(const ssd_seq* q, int rows) {
   return q->path == SSD_PATH_PERSISTENT && q->fz_nwg > 0 && q->m->d.dtype == SSD_DTYPE_BF16 && rows <= 16;
 }
 
+// ---------------------------------------------------------------------------
+// Decode mode: a block of at most 16 rows through a list of sub-layer entries
+// (2l: attention of layer l, 2l + 1: its MLP) with the kernels of decode.hip.
+// Each residual update also writes the input of the next RMSNorm consumer
+// (xg, ss), so the entry list fixes every gain in advance.
+
+bool dec_usable(const ssd_seq* q, int rows) {
+  return q->path == SSD_PATH_KERNELS && q->m->d.dtype == SSD_DTYPE_BF16 && rows <= 16;
+}
+
+// Gain of the RMSNorm that consumes the residual entering entry e (past the
+// end: the final norm when the LM head follows, else none).
+const float* dec_gain(const ssd_model* m, const std::vector<int>& ent, size_t e, bool final_lm) {
+  if (e < ent.size()) {
+    const ssd_layer_weights& lw = m->layers[ent[e] / 2];
+    return ent[e] % 2 == 0 ? lw.attn_norm : lw.mlp_norm;
+  }
+  return final_lm ? m->d.final_norm : nullptr;
+}
+
+DecGemm dec_base(const ssd_seq* q, int M, const int* nrows, const int* stop) {
+  DecGemm a{};
+  a.M = M; a.nrows = nrows; a.stop = stop;
+  a.ss = q->w.fz_ss; a.eps = q->m->d.rms_eps;
+  return a;
+}
+
+// Entries [e0, e1) of ent on the residual rows h[0, M).
+int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, const std::vector<int>& ent, size_t e0,
+               size_t e1, bool final_lm, const int* stop, hipStream_t s) {
+  const ssd_model* m = q->m;
+  const ssd_model_desc& d = m->d;
+  const Workspace& w = q->w;
+  const int D = d.d_model, F = d.ffn_dim;
+  for (size_t e = e0; e < e1; ++e) {
+    const int l = ent[e] / 2;
+    const ssd_layer_weights& lw = m->layers[l];
+    DecGemm r = dec_base(q, M, nrows, stop);
+    r.Y = h; r.ldy = D; r.N = D;
+    r.gain_next = dec_gain(m, ent, e + 1, final_lm);
+    r.xg_next = w.fz_xg; r.ss_next = w.fz_ss;
+    if (ent[e] % 2 == 0) {
+      DecGemm a = dec_base(q, M, nrows, stop);
+      a.W = (const bf16_t*)lw.w_qkv; a.N = m->qkv_dim; a.K = D;
+      a.X = w.fz_xg; a.ldx = D;
+      a.q = (bf16_t*)w.qb; a.ldq = m->q_dim;
+      a.pool = (bf16_t*)q->kv.pool; a.page_table = q->kv.page_table; a.PS = q->kv.page_size;
+      a.n_lpages = q->kv.n_lpages; a.L = d.n_layers; a.layer = l;
+      a.H = d.n_heads; a.KVH = d.n_kv_heads; a.HD = d.head_dim;
+      a.pos = pos; a.rope_cs = w.rope_cs; a.err = &w.st->error_flags;
+      TRY(launch_dec_gemm(DEC_QKV, a, s));
+      TRY(launch_attention_dec(d.head_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads, d.n_kv_heads, M, nrows,
+                               pos, q->max_ctx, w.part, w.x, m->q_dim, w.dec_ctr, stop, s));
+      r.W = (const bf16_t*)lw.w_o; r.K = m->q_dim; r.X = (const bf16_t*)w.x; r.ldx = m->q_dim;
+      TRY(launch_dec_gemm(DEC_RESID, r, s));
+    } else {
+      DecGemm a = dec_base(q, M, nrows, stop);
+      a.W = (const bf16_t*)lw.w_gate_up; a.N = F; a.K = D;
+      a.X = w.fz_xg; a.ldx = D;
+      a.A = (bf16_t*)w.x2; a.lda = F;
+      TRY(launch_dec_gemm(DEC_SWIGLU, a, s));
+      r.W = (const bf16_t*)lw.w_down; r.K = F; r.X = (const bf16_t*)w.x2; r.ldx = F;
+      TRY(launch_dec_gemm(DEC_RESID, r, s));
+    }
+  }
+  return 0;
+}
+
+// LM head of the block's rows (their final-norm input is in xg / ss).
+int dec_logits(ssd_seq* q, int M, const int* nrows, float* logits, const int* stop, hipStream_t s) {
+  const ssd_model_desc& d = q->m->d;
+  DecGemm a = dec_base(q, M, nrows, stop);
+  a.W = (const bf16_t*)d.lm_head; a.N = d.vocab; a.K = d.d_model;
+  a.X = q->w.fz_xg; a.ldx = d.d_model;
+  a.Y = logits; a.ldy = d.vocab;
+  TRY(launch_dec_gemm(DEC_STORE, a, s));
+  return 0;
+}
+
+// Rows entering a pass: h[dst] from tokens (embedding) or src rows, with the first consumer's input.
+int dec_entry(ssd_seq* q, const int* tokens, const float* src, int rows, const int* count, const int* dst_off,
+              float* h, const float* gain, const int* stop, hipStream_t s) {
+  const ssd_model_desc& d = q->m->d;
+  TRY(launch_dec_entry(d.embed, tokens, d.vocab, src, rows, count, dst_off, h, d.d_model, gain, q->w.fz_xg,
+                       q->w.fz_ss, stop, s));
+  return 0;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -459,6 +550,8 @@ extern "C" int ssd_seq_create(const ssd_model* m, void* kv_pool_dev, int n_pages
       q->fz_nwg = cus;
   }
   int rc = launch_state_init(q->w.st, stream);
+  if (rc == 0 && hipMemset(q->w.dec_ctr, 0, sizeof(unsigned) * 16 * (size_t)m->d.n_kv_heads) != hipSuccess)
+    rc = SSD_ERR_HIP;
   if (rc == 0 && hipStreamSynchronize(stream) != hipSuccess) rc = SSD_ERR_HIP;
   if (rc != 0) {
     delete q;
@@ -514,6 +607,12 @@ extern "C" int ssd_decode_ar(ssd_seq* q, float temperature, uint64_t seed, float
     std::vector<int> ent;
     fz_entries(ent, 0, d.n_layers, nullptr);
     TRY(fz_run(q, fz_build(q->m, ent, true, -1), 1, nullptr, w.pos1, w.tok1, nullptr, w.h1, lg, nullptr, nullptr, s));
+  } else if (dec_usable(q, 1)) {
+    std::vector<int> ent;
+    fz_entries(ent, 0, d.n_layers, nullptr);
+    TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, dec_gain(q->m, ent, 0, true), nullptr, s));
+    TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, ent, 0, ent.size(), true, nullptr, s));
+    TRY(dec_logits(q, 1, nullptr, lg, nullptr, s));
   } else {
     TRY(launch_embed(d.dtype, d.embed, w.tok1, d.vocab, w.h1, d.d_model, 1, d.d_model, nullptr, nullptr, s));
     Block b{w.h1, RowBlock{1, nullptr, w.pos1, nullptr, nullptr}, nullptr, 0, 0};
@@ -552,6 +651,25 @@ extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_lay
       TRY(launch_draft_step_prep(w.st, draft_tokens_dev, j, w.pos1, w.tok1, q->max_ctx, n_drafted_dev, s));
       float* lg = draft_logits_dev + (size_t)(j - 1) * d.vocab;
       TRY(fz_run(q, pr, 1, nullptr, w.pos1, w.tok1, nullptr, w.h1, lg, w.hb + (size_t)(j - 1) * d.d_model, stop, s));
+      TRY(launch_draft_stats(lg, d.vocab, temperature, seed, w.st, j, d_max, conf_thresh, draft_tokens_dev,
+                             n_drafted_dev, s));
+    }
+    return SSD_OK;
+  }
+  if (dec_usable(q, 1)) {
+    std::vector<int> ent;
+    fz_entries(ent, 0, b, nullptr);
+    const size_t save = ent.size();
+    fz_entries(ent, b, d.n_layers, mask.data());
+    const float* g0 = dec_gain(q->m, ent, 0, true);
+    for (int j = 1; j <= d_max; ++j) {
+      TRY(launch_draft_step_prep(w.st, draft_tokens_dev, j, w.pos1, w.tok1, q->max_ctx, n_drafted_dev, s));
+      TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, g0, stop, s));
+      TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, ent, 0, save, true, stop, s));
+      TRY(launch_copy_rows(w.h1, w.hb + (size_t)(j - 1) * d.d_model, 1, d.d_model, nullptr, nullptr, stop, s));
+      TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, ent, save, ent.size(), true, stop, s));
+      float* lg = draft_logits_dev + (size_t)(j - 1) * d.vocab;
+      TRY(dec_logits(q, 1, nullptr, lg, stop, s));
       TRY(launch_draft_stats(lg, d.vocab, temperature, seed, w.st, j, d_max, conf_thresh, draft_tokens_dev,
                              n_drafted_dev, s));
     }
@@ -605,6 +723,26 @@ extern "C" int ssd_verify(ssd_seq* q, const uint8_t* skip_mask_host, int exit_la
       TRY(fz_run(q, fz_build(q->m, all, true, -1), M, rows, w.vpos, w.vtok, nullptr, w.h, logits_dev, nullptr,
                  nullptr, s));
     }
+    return SSD_OK;
+  }
+  if (dec_usable(q, M)) {
+    std::vector<int> suffix;
+    fz_entries(suffix, reuse ? b : 0, d.n_layers, nullptr);
+    const float* g0 = dec_gain(q->m, suffix, 0, true);
+    if (reuse) {
+      // the last row (y_d') runs the layers below the boundary first (it uses row 0 of the block's
+      // normalised-input buffers); then the rows < d' take the residual the draft saved there
+      std::vector<int> prefix;
+      fz_entries(prefix, 0, b, nullptr);
+      TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, dec_gain(q->m, prefix, 0, false), nullptr, s));
+      TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, prefix, 0, prefix.size(), false, nullptr, s));
+      TRY(dec_entry(q, nullptr, w.hb, d_max, n_drafted_dev, nullptr, w.h, g0, nullptr, s));
+      TRY(dec_entry(q, nullptr, w.h1, 1, nullptr, n_drafted_dev, w.h, g0, nullptr, s));
+    } else {
+      TRY(dec_entry(q, w.vtok, nullptr, M, rows, nullptr, w.h, g0, nullptr, s));
+    }
+    TRY(dec_layers(q, w.h, M, rows, w.vpos, suffix, 0, suffix.size(), true, nullptr, s));
+    TRY(dec_logits(q, M, rows, logits_dev, nullptr, s));
     return SSD_OK;
   }
   Block full{w.h, RowBlock{M, rows, w.vpos, nullptr, nullptr}, nullptr, 0, 0};

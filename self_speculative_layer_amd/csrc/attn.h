@@ -36,6 +36,14 @@ struct AttnSmem {
 
 typedef uint32_t att_u32x4 __attribute__((ext_vector_type(4)));
 
+// Partial results are stored either plainly (read by a later kernel) or with
+// device-scope stores (read by another workgroup of the same kernel).
+template <bool DEV>
+__device__ __forceinline__ void part_store(float* p, float v) {
+  if constexpr (DEV) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
 // One work item: KV head g, split s, the rows r0 .. min(r0 + RB, Ma) - 1 with
 // Ma = min(M, *nrows) (positions increasing).  Keys at positions >= local_start
 // come from local_kv rows (scoring: the candidate's own keys/values, rows
@@ -44,7 +52,8 @@ typedef uint32_t att_u32x4 __attribute__((ext_vector_type(4)));
 // Loads take two rounds: (1) the active-row count, the rows' positions, the
 // chunk's page ids and the queries; (2) every key and value of the chunk.
 // Items whose split starts past the block's last position return after (1).
-template <typename T, int HD, int NW>
+// DEV: partials are written with device-scope stores.
+template <typename T, int HD, int NW, bool DEV = false>
 __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__ q, int ldq,
                                   const T* __restrict__ pool, const int* __restrict__ page_table, int PS,
                                   int n_lpages, int L, int layer, int H, int KVH, int M,
@@ -175,11 +184,11 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
 #pragma unroll
           for (int u = 0; u < 16; ++u) o = fmaf(pw[u], vv[u], o);
         }
-        dstp[d] = o;
+        part_store<DEV>(dstp + d, o);
       }
       if (lane == 0) {
-        dstp[HD] = mx;
-        dstp[HD + 1] = psum;
+        part_store<DEV>(dstp + HD, mx);
+        part_store<DEV>(dstp + HD + 1, psum);
       }
       __builtin_amdgcn_wave_barrier();
     }

@@ -1,0 +1,410 @@
+// Decode-mode kernels: a block of at most 16 rows (one draft token, or the
+// d' + 1 rows of a verify pass) through the decoder with the small steps
+// folded into the projections, so that a layer takes five launches:
+//
+//   QKV projection    row scale from the RMSNorm tile sums, RoPE, q store and
+//                     K/V append to the paged cache in the epilogue
+//   attention         split partials; the last split of a (row block, KV head)
+//                     to finish merges them
+//   O projection      residual add, then the next RMSNorm consumer's input
+//                     (x = bf16(h * gain) and the 16-feature tile sums of h^2)
+//   gate/up           row scale, SwiGLU
+//   down projection   residual add, next consumer's input
+//
+// The arithmetic of every output element is the same as in the general
+// kernels (kernels.hip), step for step: same K slices per wave, same
+// reduction order, same rounding of the epilogues, same canonical RMS sums.
+// A row's result never depends on the other rows of its block.
+#include <math.h>
+
+#include "kernels.h"
+#include "attn.h"
+
+namespace ssd {
+
+typedef uint32_t dec_u32x4 __attribute__((ext_vector_type(4)));
+
+static inline int dec_ok(hipError_t e) { return e == hipSuccess ? 0 : SSD_ERR_HIP; }
+
+constexpr int DEC_U = 8;      // 32-element K steps each wave keeps in flight
+// Waves per workgroup.  Each wave owns a contiguous quarter of K, as in the general projection kernel
+// (GEMM_NW), so the two give the same bits for a row; measured against 8 and 16 waves per tile on the
+// 7B shapes, 4 was fastest for every matrix.
+constexpr int DEC_NW = 4;
+constexpr int DEC_SSP = 8;    // RMS tile sums per lane and row: K <= 64 * 16 * DEC_SSP
+
+// ===========================================================================
+// Projection Y[M, N] = X[M, K] . W[N, K]^T for M <= 16, bf16 operands, fp32
+// accumulation on the matrix cores (v_mfma_f32_16x16x32_bf16: weights as A,
+// 16 features x 32 k; activations as B, 32 k x 16 rows).
+//
+// A workgroup owns one tile of 16 output features (two row sets of W for the
+// SwiGLU and QKV epilogues) and all of K.  Its NW waves take contiguous
+// 64-element slices of K; each wave keeps DEC_U steps (16 rows x 64 bytes of
+// each weight set per step) in flight in registers and reloads a step's
+// registers as soon as its MFMA has been issued.  The per-wave tiles are
+// reduced through LDS in wave order.  Rows >= M repeat the last row's
+// activations (no masking on the load path); their outputs are not stored.
+// ===========================================================================
+
+template <int EPI, int NW, bool HALF>
+__global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
+  if (a.stop && *a.stop) return;
+  const int Ma = a.nrows ? min(a.M, *a.nrows) : a.M;
+  if (Ma <= 0) return;
+  constexpr bool TWO = EPI == DEC_SWIGLU || EPI == DEC_QKV;   // outputs combine two W row sets
+  constexpr bool DUAL = TWO && !HALF;                           // 16 + 16 rows: two accumulators
+  static_assert(!HALF || TWO, "half tiles pair two row sets");
+  constexpr bool NORM = EPI != DEC_RESID;
+  constexpr int NT = DUAL ? 2 : 1;
+  constexpr int RPW = (16 + NW - 1) / NW;       // rows whose scale one wave computes
+  const int K = a.K;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int tile = blockIdx.x;
+
+  // W rows of this tile.  Two-set epilogues pair row f0 + i with row f1 + i: DUAL tiles take 16 of
+  // each (two accumulators), HALF tiles 8 of each in one accumulator (MFMA rows 0-7 and 8-15).
+  constexpr int SET = HALF ? 8 : 16;
+  int f0, f1, slot = 0, d0 = 0;
+  if (EPI == DEC_QKV) {
+    const int per = a.HD / (2 * SET);           // tiles per head slot: pairs (i, i + HD/2), i in [d0, d0 + SET)
+    slot = tile / per;
+    d0 = (tile % per) * SET;
+    f0 = slot * a.HD + d0;
+    f1 = f0 + a.HD / 2;
+  } else {
+    f0 = tile * SET;
+    f1 = a.N + f0;                              // SwiGLU: the up rows follow the N gate rows
+  }
+  int wrow = f0 + r;
+  if (HALF) wrow = (r < 8 ? f0 : f1) + (r & 7);
+  if (EPI == DEC_STORE) wrow = min(wrow, a.N - 1);   // tiles past N repeat the last W row; not stored
+  const bf16_t* wp = a.W + (size_t)wrow * K + g * 8;
+  const bf16_t* wp2 = a.W + (size_t)(f1 + r) * K + g * 8;
+  const bf16_t* xp = a.X + (size_t)min(r, Ma - 1) * a.ldx + g * 8;
+
+  // RMS tile sums of the rows this wave scales: loaded first, summed after the weight loads are issued
+  __shared__ float sinv[16];
+  const int nts = K / 16;
+  float ssv[RPW][DEC_SSP];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int row = min(wave + i * NW, Ma - 1);
+#pragma unroll
+      for (int j = 0; j < DEC_SSP; ++j) ssv[i][j] = a.ss[(size_t)row * nts + min(lane + 64 * j, nts - 1)];
+    }
+  }
+
+  const int nu = K >> 6;
+  const int s0 = 2 * ((nu * wave) / NW);
+  const int n = 2 * ((nu * (wave + 1)) / NW) - s0;   // 32-element steps of this wave (>= 2)
+  dec_u32x4 wa[DEC_U], wb[DEC_U], xa[DEC_U];
+#pragma unroll
+  for (int u = 0; u < DEC_U; ++u) {
+    const int k = (s0 + min(u, n - 1)) * 32;
+    wa[u] = *(const dec_u32x4*)(wp + k);
+    if (DUAL) wb[u] = *(const dec_u32x4*)(wp2 + k);
+    xa[u] = *(const dec_u32x4*)(xp + k);
+    __builtin_amdgcn_sched_barrier(0);       // same load order as the steady loop
+  }
+
+  if constexpr (NORM) {
+    // canonical order: lane j adds tiles j, j + 64, ... then a butterfly over the wave
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int row = wave + i * NW;
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < DEC_SSP; ++j)   // tiles past the row end add an exact 0 (keeps every load unconditional)
+        acc += __fmul_rn(ssv[i][j], lane + 64 * j < nts ? 1.f : 0.f);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, WAVE);
+      if (row < Ma && lane == 0) sinv[row] = inv_rms(acc, K, a.eps);
+    }
+  }
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+  // steps are consumed in increasing order; the steady loop has no branches, so the compiler's
+  // wait before each step's MFMA leaves the later steps' loads in flight
+  auto consume = [&](int u) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[u]),
+                                                  __builtin_bit_cast(bf16x8, xa[u]), acc, 0, 0, 0);
+    if (DUAL)
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb[u]),
+                                                     __builtin_bit_cast(bf16x8, xa[u]), acc2, 0, 0, 0);
+  };
+  auto reload = [&](int u, int step) {
+    const int k = (s0 + step) * 32;
+    wa[u] = *(const dec_u32x4*)(wp + k);
+    if (DUAL) wb[u] = *(const dec_u32x4*)(wp2 + k);
+    xa[u] = *(const dec_u32x4*)(xp + k);
+  };
+  const int nfull = n / DEC_U, rem = n - nfull * DEC_U;
+  for (int b = 1; b < nfull; ++b) {
+#pragma unroll
+    for (int u = 0; u < DEC_U; ++u) {
+      consume(u);
+      reload(u, b * DEC_U + u);
+      __builtin_amdgcn_sched_barrier(0);     // keep the issue order: one step's MFMA, then its reload
+    }
+  }
+  if (nfull > 0) {
+    if (rem > 0) {
+#pragma unroll
+      for (int u = 0; u < DEC_U; ++u) {
+        consume(u);
+        reload(u, min(nfull * DEC_U + u, n - 1));
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < DEC_U; ++u) consume(u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < DEC_U; ++u)
+    if (u < rem) consume(u);
+
+  // acc[i] holds D[feature 4g + i][row r]
+  __shared__ float red[NT][NW][16][17];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    red[0][wave][4 * g + i][r] = acc[i];
+    if (DUAL) red[NT - 1][wave][4 * g + i][r] = acc2[i];
+  }
+  __syncthreads();
+  if (threadIdx.x >= 256) return;
+  const int row = threadIdx.x >> 4, nn = threadIdx.x & 15;
+  if (row >= Ma) return;                        // uniform over each group of 16 lanes
+  if (HALF && nn >= 8) return;
+  float s = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    s += red[0][w][nn][row];
+    if (DUAL) s2 += red[NT - 1][w][nn][row];
+    if (HALF) s2 += red[0][w][nn + 8][row];
+  }
+
+  if constexpr (EPI == DEC_STORE) {
+    if (f0 + nn < a.N) a.Y[(size_t)row * a.ldy + f0 + nn] = __fmul_rn(s, sinv[row]);
+  } else if constexpr (EPI == DEC_RESID) {
+    const int col = f0 + nn;
+    float* hp = a.Y + (size_t)row * a.ldy + col;
+    const float hn = __fadd_rn(*hp, s);
+    *hp = hn;
+    if (a.gain_next) {
+      st(a.xg_next + (size_t)row * a.N + col, __fmul_rn(hn, a.gain_next[col]));
+      const float t = tile16_ss_lanes(hn);
+      if (nn == 0) a.ss_next[(size_t)row * (a.N / 16) + col / 16] = t;
+    }
+  } else if constexpr (EPI == DEC_SWIGLU) {
+    const float inv = sinv[row];
+    st(a.A + (size_t)row * a.lda + f0 + nn, swiglu(__fmul_rn(s, inv), __fmul_rn(s2, inv)));
+  } else {
+    const float inv = sinv[row];
+    const float x1 = __fmul_rn(s, inv), x2 = __fmul_rn(s2, inv);
+    const int HD = a.HD, H = a.H, KVH = a.KVH;
+    const int i = d0 + nn;                      // pair index
+    const int p = a.pos[row];
+    const int lp = p / a.PS;
+    if (p < 0 || lp >= a.n_lpages) {
+      if (nn == 0) atomicOr(a.err, ERRF_CAPACITY);
+      return;
+    }
+    bf16_t* dst;
+    if (slot < H) {
+      dst = a.q + (size_t)row * a.ldq + (size_t)slot * HD;
+    } else {
+      const int kvsel = slot < H + KVH ? 0 : 1;
+      const int gg = slot - H - kvsel * KVH;
+      dst = a.pool + kv_index(a.page_table[lp], a.L, a.layer, kvsel, KVH, gg, a.PS, p % a.PS, HD);
+    }
+    if (slot < H + KVH) {
+      float y1, y2;
+      rope_apply(x1, x2, a.rope_cs[(size_t)p * (HD / 2) + i], y1, y2);
+      st(dst + i, y1);
+      st(dst + i + HD / 2, y2);
+    } else {
+      st(dst + i, x1);
+      st(dst + i + HD / 2, x2);
+    }
+  }
+}
+
+bool profile_wants(int cls);
+void profile_before(hipStream_t s);
+void profile_after(hipStream_t s, double bytes);
+
+// Tile shapes of the two-set projections (HALF: 8 + 8 rows per workgroup, twice the workgroups).
+constexpr bool DEC_HALF_QKV = true;
+constexpr bool DEC_HALF_SWIGLU = false;
+
+static int dec_tiles(int epi, int N, int HD) {
+  (void)HD;
+  if (epi == DEC_QKV) return DEC_HALF_QKV ? N / 16 : N / 32;
+  if (epi == DEC_SWIGLU) return DEC_HALF_SWIGLU ? N / 8 : N / 16;
+  return (N + 15) / 16;
+}
+
+int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return 0;
+  if (a.M > 16 || (epi != DEC_STORE && a.N % 16 != 0) || a.K % 64 != 0) return SSD_ERR_SHAPE;
+  if (epi != DEC_RESID && a.K > 64 * 16 * DEC_SSP) return SSD_ERR_SHAPE;
+  if (epi == DEC_QKV && (a.HD % 32 != 0 || a.N % a.HD != 0)) return SSD_ERR_SHAPE;
+  if (a.K / 64 < DEC_NW) return SSD_ERR_SHAPE;
+  if (epi == DEC_SWIGLU && a.N % (DEC_HALF_SWIGLU ? 8 : 16) != 0) return SSD_ERR_SHAPE;
+  const dim3 grid(dec_tiles(epi, a.N, a.HD));
+  // profile classes: 0 plain-store projections (QKV, LM head), 1 residual, 2 gate/up
+  const int cls = epi == DEC_RESID ? 1 : (epi == DEC_SWIGLU ? 2 : 0);
+  const bool prof = profile_wants(cls);
+  if (prof) profile_before(s);
+  const dim3 block(DEC_NW * 64);
+  switch (epi) {
+    case DEC_STORE: hipLaunchKernelGGL((dec_gemm_kernel<DEC_STORE, DEC_NW, false>), grid, block, 0, s, a); break;
+    case DEC_RESID: hipLaunchKernelGGL((dec_gemm_kernel<DEC_RESID, DEC_NW, false>), grid, block, 0, s, a); break;
+    case DEC_SWIGLU:
+      hipLaunchKernelGGL((dec_gemm_kernel<DEC_SWIGLU, DEC_NW, DEC_HALF_SWIGLU>), grid, block, 0, s, a);
+      break;
+    default: hipLaunchKernelGGL((dec_gemm_kernel<DEC_QKV, DEC_NW, DEC_HALF_QKV>), grid, block, 0, s, a);
+  }
+  if (prof) {
+    // algorithmic bytes: weights once, activations in once, results out once (residual: read + write)
+    const double M = a.M, N = a.N, K = a.K;
+    const double wrows = epi == DEC_SWIGLU ? 2.0 * N : N;
+    double by = wrows * K * 2.0 + M * K * 2.0;
+    by += epi == DEC_STORE ? 4.0 * M * N : (epi == DEC_RESID ? 8.0 * M * N : 2.0 * M * N);
+    profile_after(s, by);
+  }
+  return dec_ok(hipGetLastError());
+}
+
+// ===========================================================================
+// Attention of a decode block with the split merge folded in: every work item
+// writes its partial with device-scope stores and counts itself on the
+// (row block, KV head) counter; the item that completes the count merges the
+// rows' partials (in split order) and resets the counter for the next launch.
+// ===========================================================================
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_dec_kernel(
+    const T* __restrict__ q, int ldq, const T* __restrict__ pool, const int* __restrict__ page_table, int PS,
+    int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
+    const int* __restrict__ pos, int RB, int nsplit, float* __restrict__ part, T* __restrict__ out, int ldo,
+    unsigned* __restrict__ counters, const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int g = blockIdx.x, s = blockIdx.y, rbk = blockIdx.z;
+  const int Ma = nrows ? min(M, *nrows) : M;
+  const int r0 = rbk * RB, r1 = min(r0 + RB, Ma);
+  if (r1 <= r0) return;
+  const int n_act = pos[r1 - 1] / ATT_SPLIT + 1;     // splits holding a key some row of the block sees
+  if (s >= n_act) return;
+  __shared__ AttnSmem<T, HD, 4> sm;
+  __shared__ int is_last;
+  attn_partial_item<T, HD, 4, true>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0,
+                                    RB, g, s, nsplit, nullptr, 0, 0, part);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* c = counters + (size_t)rbk * KVH + g;
+    const unsigned old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = old + 1 == (unsigned)n_act;
+    if (is_last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int G = H / KVH;
+  const int n = (r1 - r0) * G * HD;
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int d = e % HD, qi = e / HD;
+    const int row = r0 + qi / G, head = g * G + qi % G;
+    attn_combine_elem<T, HD>(part, nsplit, row, head, H, pos[row], d, out, ldo);
+  }
+}
+
+int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer, int H, int KVH,
+                         int M, const int* nrows, const int* pos, int max_ctx, float* part, void* out, int ldo,
+                         unsigned* counters, const int* stop, hipStream_t s) {
+  if (M <= 0) return 0;
+  const int G = H / KVH;
+  const int RB = ATT_MAXQ / G;
+  if (RB < 1 || M > 16) return SSD_ERR_SHAPE;
+  const int nsplit = attention_nsplit(max_ctx);
+  const dim3 grid(KVH, nsplit, (M + RB - 1) / RB);
+#define ATT_DEC(HD)                                                                                             \
+  hipLaunchKernelGGL((attn_dec_kernel<bf16_t, HD>), grid, dim3(256), 0, s, (const bf16_t*)q, ldq,                \
+                     (const bf16_t*)kv.pool, kv.page_table, kv.page_size, kv.n_lpages, L, layer, H, KVH, M, nrows, \
+                     pos, RB, nsplit, part, (bf16_t*)out, ldo, counters, stop)
+  if (head_dim == 128) ATT_DEC(128); else ATT_DEC(64);
+#undef ATT_DEC
+  return dec_ok(hipGetLastError());
+}
+
+// ===========================================================================
+// Rows entering a decode pass: h from the embedding (tokens) or from saved
+// residual rows, plus the first RMSNorm consumer's input.
+// ===========================================================================
+
+template <bool EMB, bool NORM>
+__global__ __launch_bounds__(256) void dec_entry_kernel(const bf16_t* __restrict__ emb, const int* __restrict__ tokens,
+                                                        int V, const float* __restrict__ src, int rows,
+                                                        const int* __restrict__ count, const int* __restrict__ dst_off,
+                                                        float* __restrict__ h, int D, const float* __restrict__ gain,
+                                                        bf16_t* __restrict__ xg, float* __restrict__ ss,
+                                                        const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int r = blockIdx.x;
+  const int n = count ? min(rows, *count) : rows;
+  if (r >= n) return;
+  const int dr = r + (dst_off ? *dst_off : 0);
+  const bf16_t* e = EMB ? emb + (size_t)min(max(tokens[r], 0), V - 1) * D : nullptr;   // ids are produced in range
+  const float* sr = EMB ? nullptr : src + (size_t)r * D;
+  float* hr = h + (size_t)dr * D;
+  // D % 16 == 0: each group of 16 lanes is entirely inside or outside the row.  Loads are issued in
+  // batches of 8 per thread before their first use.
+  constexpr int PER = 8;
+  for (int i0 = 0; i0 < D; i0 += 256 * PER) {
+    float v[PER], gv[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = min(i0 + j * 256 + (int)threadIdx.x, D - 1);
+      v[j] = EMB ? bf2f(e[i]) : sr[i];
+      if (NORM) gv[j] = gain[i];
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = i0 + j * 256 + threadIdx.x;
+      if (i0 + j * 256 >= D) break;           // uniform
+      if (i < D) hr[i] = v[j];
+      if (NORM) {
+        const float t = tile16_ss_lanes(v[j]);
+        if (i < D) {
+          st(xg + (size_t)dr * D + i, __fmul_rn(v[j], gv[j]));
+          if ((threadIdx.x & 15) == 0) ss[(size_t)dr * (D / 16) + i / 16] = t;
+        }
+      }
+    }
+  }
+}
+
+int launch_dec_entry(const void* emb, const int* tokens, int V, const float* src, int rows, const int* count,
+                     const int* dst_off, float* h, int D, const float* gain, void* xg, float* ss, const int* stop,
+                     hipStream_t s) {
+  if (rows <= 0) return 0;
+  if (D % 16 != 0) return SSD_ERR_SHAPE;
+#define ENTRY(E, N)                                                                                              \
+  hipLaunchKernelGGL((dec_entry_kernel<E, N>), dim3(rows), dim3(256), 0, s, (const bf16_t*)emb, tokens, V, src,  \
+                     rows, count, dst_off, h, D, gain, (bf16_t*)xg, ss, stop)
+  if (tokens) {
+    if (gain) ENTRY(true, true); else ENTRY(true, false);
+  } else {
+    if (gain) ENTRY(false, true); else ENTRY(false, false);
+  }
+#undef ENTRY
+  return dec_ok(hipGetLastError());
+}
+
+}  // namespace ssd

@@ -98,6 +98,45 @@ int launch_score(const ssd_row_stat* stats, const int32_t* window, int n_masks, 
                  int32_t* best, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Decode mode (decode.hip): blocks of at most 16 rows, bf16.
+
+enum DecEpilogue {
+  DEC_STORE = 0,    // Y[m, n] = acc * inv[m]                                  (LM head, fp32 logits)
+  DEC_RESID = 1,    // Y[m, n] += acc; then xg_next, ss_next of the new row (when gain_next)
+  DEC_SWIGLU = 2,   // A[m, f] = bf16(silu(acc_gate * inv[m]) * acc_up * inv[m])
+  DEC_QKV = 3       // (acc * inv[m]) rotated (q, k), stored to q / the paged cache
+};
+
+// inv[m] = 1 / sqrt(mean(h^2) + eps) from the rows' 16-feature tile sums ss[m][K/16].
+struct DecGemm {
+  const bf16_t* W; int N, K;        // W [N rows (SWIGLU: 2N), K]
+  const bf16_t* X; int ldx;         // activations [M, K]
+  int M; const int* nrows; const int* stop;
+  const float* ss; float eps;       // STORE, SWIGLU, QKV: tile sums of the normalised rows
+  float* Y; int ldy;                // STORE: output; RESID: residual stream
+  bf16_t* A; int lda;               // SWIGLU output
+  const float* gain_next;           // RESID: gain of the next RMSNorm consumer (nullable: none)
+  bf16_t* xg_next;                  //   its input bf16(h * gain) [M, N]
+  float* ss_next;                   //   tile sums of h^2 [M, N/16]
+  bf16_t* q; int ldq;               // QKV: rotated queries [M, H*HD]
+  bf16_t* pool; const int* page_table;
+  int PS, n_lpages, L, layer, H, KVH, HD;
+  const int* pos; const float2* rope_cs; int* err;
+};
+int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s);
+
+// Attention with the split merge folded in; counters[n_row_blocks][KVH] start at zero and are left at zero.
+int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer, int H, int KVH,
+                         int M, const int* nrows, const int* pos, int max_ctx, float* part, void* out, int ldo,
+                         unsigned* counters, const int* stop, hipStream_t s);
+
+// h[dst] = embedding row of tokens[r] (tokens != nullptr) or src[r], for r < (count ? *count : rows),
+// dst = r + (dst_off ? *dst_off : 0); with gain, also xg[dst] = bf16(h * gain) and ss[dst] tile sums.
+int launch_dec_entry(const void* emb, const int* tokens, int V, const float* src, int rows, const int* count,
+                     const int* dst_off, float* h, int D, const float* gain, void* xg, float* ss, const int* stop,
+                     hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // Persistent decode pass (fused.hip)
 
 enum PassPhase { PH_INIT = 0, PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_DOWN = 5, PH_LM = 6 };
