@@ -67,25 +67,26 @@ class Model:
 
     @staticmethod
     def synthetic(shape, seed=synth.SEED_WEIGHTS, n_layers=None):
-        """Weights from the shared seeded generator (norm gains 1)."""
+        """Weights from the shared seeded generator (norm gains 1 + w, float32)."""
         s = shape
         bf = s.dtype == "bf16"
         W = lambda rows, cols, tid: synth.weight_host((rows, cols), tid, "f64", bf16=bf, seed=seed)
+        G = lambda tid: synth.norm_gain_host(s.d_model, tid, seed=seed).astype(np.float64)
         layers = []
         for l in range(s.n_layers if n_layers is None else n_layers):
             layers.append(LayerWeights(
-                attn_norm=np.ones(s.d_model),
+                attn_norm=G(synth.layer_tid(l, synth.KIND_ATTN_NORM)),
                 wq=W(s.q_dim, s.d_model, synth.layer_tid(l, synth.KIND_WQ)),
                 wk=W(s.kv_dim, s.d_model, synth.layer_tid(l, synth.KIND_WK)),
                 wv=W(s.kv_dim, s.d_model, synth.layer_tid(l, synth.KIND_WV)),
                 wo=W(s.d_model, s.q_dim, synth.layer_tid(l, synth.KIND_WO)),
-                mlp_norm=np.ones(s.d_model),
+                mlp_norm=G(synth.layer_tid(l, synth.KIND_MLP_NORM)),
                 wgate=W(s.ffn_dim, s.d_model, synth.layer_tid(l, synth.KIND_WGATE)),
                 wup=W(s.ffn_dim, s.d_model, synth.layer_tid(l, synth.KIND_WUP)),
                 wdown=W(s.d_model, s.ffn_dim, synth.layer_tid(l, synth.KIND_WDOWN)),
             ))
         return Model(shape=s, embed=W(s.vocab, s.d_model, synth.TID_EMBED), layers=layers,
-                     final_norm=np.ones(s.d_model), lm_head=W(s.vocab, s.d_model, synth.TID_LM_HEAD))
+                     final_norm=G(synth.TID_FINAL_NORM), lm_head=W(s.vocab, s.d_model, synth.TID_LM_HEAD))
 
 
 class KVCache:

@@ -119,8 +119,17 @@ def tokens_dev(tensor, stream_id, vocab, seed=SEED_PROMPT, stream=0):
 # ---------------------------------------------------------------------------
 # Tensor ids.  Logical layouts are row-major [out, in] ("N x K").
 KIND_WQ, KIND_WK, KIND_WV, KIND_WO, KIND_WGATE, KIND_WUP, KIND_WDOWN = 1, 2, 3, 4, 6, 7, 8
+KIND_ATTN_NORM, KIND_MLP_NORM = 9, 10
 TID_EMBED = 0xFFFF0001
 TID_LM_HEAD = 0xFFFF0002
+TID_FINAL_NORM = 0xFFFF0003
+GAIN_STD = 0.1        # RMSNorm gains: 1 + w, w of the weight law with this deviation (fp32 add)
+
+
+def norm_gain_host(n, tensor_id, seed=SEED_WEIGHTS):
+    """float32 RMSNorm gain vector 1 + w (one fp32 addition per element)."""
+    w = weight_host((n,), tensor_id, "f32", seed=seed, std=GAIN_STD)
+    return (np.float32(1.0) + w).astype(np.float32)
 STREAM_PROMPT = 0x50000001
 
 

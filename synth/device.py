@@ -1,12 +1,18 @@
 """Device copies of the synthetic model, in the layout the C ABI takes.
 
 Layout only (no arithmetic of the method): w_qkv stacks Wq, Wk, Wv row blocks;
-w_gate_up stacks Wgate then Wup; norm gains are ones (float32).
+w_gate_up stacks Wgate then Wup; norm gains are float32 1 + w (the same
+single fp32 addition as norm_gain_host).
 """
 import torch
 
 from . import KIND_WDOWN, KIND_WGATE, KIND_WK, KIND_WO, KIND_WQ, KIND_WUP, KIND_WV, TID_EMBED, TID_LM_HEAD
-from . import SEED_WEIGHTS, layer_tid, weight_dev
+from . import GAIN_STD, KIND_ATTN_NORM, KIND_MLP_NORM, SEED_WEIGHTS, TID_FINAL_NORM, layer_tid, weight_dev
+
+
+def norm_gain_dev(n, tensor_id, seed=SEED_WEIGHTS, device="cuda"):
+    w = weight_dev(torch.empty(n, dtype=torch.float32, device=device), tensor_id, seed=seed, std=GAIN_STD)
+    return w + 1.0
 
 
 def build_weights(shape, seed=SEED_WEIGHTS, device="cuda", n_layers=None):
@@ -28,12 +34,12 @@ def build_weights(shape, seed=SEED_WEIGHTS, device="cuda", n_layers=None):
         fill_rows(wgu, 0, F, layer_tid(l, KIND_WGATE))
         fill_rows(wgu, F, F, layer_tid(l, KIND_WUP))
         wd = weight_dev(torch.empty(D, F, dtype=dt, device=device), layer_tid(l, KIND_WDOWN), seed=seed)
-        layers.append({"attn_norm": torch.ones(D, dtype=torch.float32, device=device), "w_qkv": wqkv, "w_o": wo,
-                       "mlp_norm": torch.ones(D, dtype=torch.float32, device=device), "w_gate_up": wgu,
-                       "w_down": wd})
+        layers.append({"attn_norm": norm_gain_dev(D, layer_tid(l, KIND_ATTN_NORM), seed, device), "w_qkv": wqkv,
+                       "w_o": wo, "mlp_norm": norm_gain_dev(D, layer_tid(l, KIND_MLP_NORM), seed, device),
+                       "w_gate_up": wgu, "w_down": wd})
     return {
         "embed": weight_dev(torch.empty(shape.vocab, D, dtype=dt, device=device), TID_EMBED, seed=seed),
         "lm_head": weight_dev(torch.empty(shape.vocab, D, dtype=dt, device=device), TID_LM_HEAD, seed=seed),
-        "final_norm": torch.ones(D, dtype=torch.float32, device=device),
+        "final_norm": norm_gain_dev(D, TID_FINAL_NORM, seed, device),
         "layers": layers,
     }

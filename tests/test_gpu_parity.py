@@ -47,6 +47,11 @@ def test_device_weights_equal_host_weights(pair):
     assert np.array_equal(wqkv[shape.q_dim: shape.q_dim + shape.kv_dim], o.layers[1].wk)
     wgu = t["layers"][0]["w_gate_up"].float().cpu().numpy()
     assert np.array_equal(wgu[shape.ffn_dim:], o.layers[0].wup)
+    for l in range(shape.n_layers):
+        assert np.array_equal(t["layers"][l]["attn_norm"].cpu().numpy().astype(np.float64), o.layers[l].attn_norm)
+        assert np.array_equal(t["layers"][l]["mlp_norm"].cpu().numpy().astype(np.float64), o.layers[l].mlp_norm)
+    assert np.array_equal(t["final_norm"].cpu().numpy().astype(np.float64), o.final_norm)
+    assert not np.array_equal(o.layers[0].attn_norm, o.layers[0].mlp_norm)
 
 
 def test_prefill_logits(pair):

@@ -25,12 +25,15 @@ def hf_model(m):
     with torch.no_grad():
         hf.model.embed_tokens.weight.copy_(T(m.embed))
         hf.lm_head.weight.copy_(T(m.lm_head))
+        hf.model.norm.weight.copy_(T(m.final_norm))
         for l, lw in enumerate(m.layers):
             L = hf.model.layers[l]
             L.self_attn.q_proj.weight.copy_(T(lw.wq)); L.self_attn.k_proj.weight.copy_(T(lw.wk))
             L.self_attn.v_proj.weight.copy_(T(lw.wv)); L.self_attn.o_proj.weight.copy_(T(lw.wo))
             L.mlp.gate_proj.weight.copy_(T(lw.wgate)); L.mlp.up_proj.weight.copy_(T(lw.wup))
             L.mlp.down_proj.weight.copy_(T(lw.wdown))
+            L.input_layernorm.weight.copy_(T(lw.attn_norm))
+            L.post_attention_layernorm.weight.copy_(T(lw.mlp_norm))
     return hf
 
 

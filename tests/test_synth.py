@@ -64,3 +64,15 @@ def test_random_skip_layers():
     assert len(a) == 20 and len(set(a)) == 20 and all(0 <= x < 40 for x in a)
     assert a == synth.random_skip_layers(40, 20, 2, 0)
     assert a != synth.random_skip_layers(40, 20, 2, 1)
+
+
+def test_norm_gain_law():
+    """RMSNorm gains: float32 1 + w with w of the weight law at GAIN_STD; distinct per tensor id."""
+    g = synth.norm_gain_host(4096, synth.layer_tid(3, synth.KIND_ATTN_NORM))
+    assert g.dtype == np.float32
+    w = synth.weight_host((4096,), synth.layer_tid(3, synth.KIND_ATTN_NORM), "f32", std=synth.GAIN_STD)
+    assert np.array_equal(g, np.float32(1.0) + w)
+    assert abs(float(g.mean()) - 1.0) < 4 * synth.GAIN_STD / 64
+    assert abs(float(g.std()) - synth.GAIN_STD) < 0.01
+    g2 = synth.norm_gain_host(4096, synth.layer_tid(3, synth.KIND_MLP_NORM))
+    assert not np.array_equal(g, g2)
