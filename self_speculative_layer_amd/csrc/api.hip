@@ -128,8 +128,9 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.hb = (float*)take(sizeof(float) * (size_t)max_draft * D);
   t.logits1 = (float*)take(sizeof(float) * V);
   t.logits_rows = (float*)take(sizeof(float) * (size_t)R * V);
-  t.x = take(m->elt * (size_t)R * xw);
-  t.x2 = take(m->elt * (size_t)R * F);
+  // (decode blocks use these two in the 16-row block layout)
+  t.x = take(m->elt * (size_t)std::max(R, 16) * xw);
+  t.x2 = take(m->elt * (size_t)std::max(R, 16) * F);
   t.qb = take(m->elt * (size_t)R * m->q_dim);
   t.local_kv = take(m->elt * (size_t)R * 2 * m->kv_dim);
   t.stats = (ssd_row_stat*)take(sizeof(ssd_row_stat) * R);
@@ -384,7 +385,7 @@ int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, co
     if (ent[e] % 2 == 0) {
       DecGemm a = dec_base(q, M, nrows, stop);
       a.W = (const bf16_t*)lw.w_qkv; a.N = m->qkv_dim; a.K = D;
-      a.X = w.fz_xg; a.ldx = D;
+      a.X = w.fz_xg;
       a.q = (bf16_t*)w.qb; a.ldq = m->q_dim;
       a.pool = (bf16_t*)q->kv.pool; a.page_table = q->kv.page_table; a.PS = q->kv.page_size;
       a.n_lpages = q->kv.n_lpages; a.L = d.n_layers; a.layer = l;
@@ -393,15 +394,15 @@ int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, co
       TRY(launch_dec_gemm(DEC_QKV, a, s));
       TRY(launch_attention_dec(d.head_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads, d.n_kv_heads, M, nrows,
                                pos, q->max_ctx, w.part, w.x, m->q_dim, w.dec_ctr, stop, s));
-      r.W = (const bf16_t*)lw.w_o; r.K = m->q_dim; r.X = (const bf16_t*)w.x; r.ldx = m->q_dim;
+      r.W = (const bf16_t*)lw.w_o; r.K = m->q_dim; r.X = (const bf16_t*)w.x;
       TRY(launch_dec_gemm(DEC_RESID, r, s));
     } else {
       DecGemm a = dec_base(q, M, nrows, stop);
       a.W = (const bf16_t*)lw.w_gate_up; a.N = F; a.K = D;
-      a.X = w.fz_xg; a.ldx = D;
-      a.A = (bf16_t*)w.x2; a.lda = F;
+      a.X = w.fz_xg;
+      a.A = (bf16_t*)w.x2;
       TRY(launch_dec_gemm(DEC_SWIGLU, a, s));
-      r.W = (const bf16_t*)lw.w_down; r.K = F; r.X = (const bf16_t*)w.x2; r.ldx = F;
+      r.W = (const bf16_t*)lw.w_down; r.K = F; r.X = (const bf16_t*)w.x2;
       TRY(launch_dec_gemm(DEC_RESID, r, s));
     }
   }
@@ -413,7 +414,7 @@ int dec_logits(ssd_seq* q, int M, const int* nrows, float* logits, const int* st
   const ssd_model_desc& d = q->m->d;
   DecGemm a = dec_base(q, M, nrows, stop);
   a.W = (const bf16_t*)d.lm_head; a.N = d.vocab; a.K = d.d_model;
-  a.X = q->w.fz_xg; a.ldx = d.d_model;
+  a.X = q->w.fz_xg;
   a.Y = logits; a.ldy = d.vocab;
   TRY(launch_dec_gemm(DEC_STORE, a, s));
   return 0;

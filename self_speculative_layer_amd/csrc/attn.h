@@ -1,14 +1,19 @@
 // Attention over the paged KV cache (device functions shared by the
-// standalone attention kernels and the persistent decode kernel).
+// standalone attention kernels and the decode-mode attention kernel).
 //
 // Keys are split at fixed absolute positions: split s covers [64 s, 64 s + 64).
 // A work item handles one KV head g, one split and a block of rows with all
-// their query heads (grouped-query attention); it stages 64 keys at a time in
-// LDS (16-byte vector loads, all in flight) in the storage type, keeps an
-// online softmax per query in fp32 and writes a partial (o[HD], m, l).  The
-// combine merges a row's partials in split order.  Split and chunk boundaries
-// are fixed positions, so a row's result does not depend on the rows batched
-// with it.
+// their query heads (grouped-query attention); it stages the split's 64 keys
+// and values in LDS (16-byte vector loads, all in flight) in the storage type
+// and writes, per query, a partial (o[HD], m, l) of the softmax restricted to
+// the split.  The merge combines a row's partials in split order.  Split
+// boundaries are fixed positions and every reduction runs in a fixed order,
+// so a row's result does not depend on the rows batched with it.
+//
+// bf16 items form the scores on the matrix cores (v_mfma_f32_16x16x32_bf16:
+// 16 keys x 32 dims of K as A, 32 dims x 16 queries as B), the softmax in
+// fp32 registers, and P.V as fp32 FMAs over keys in order.  fp32 items use
+// FMAs throughout.
 #pragma once
 #include "common.h"
 
@@ -17,6 +22,7 @@ namespace ssd {
 constexpr int ATT_SPLIT = 64;
 constexpr int ATT_CHUNK = 64;
 constexpr int ATT_MAXQ = 64;     // queries (rows x heads of a group) per work item
+constexpr int ATT_MAXW = 32;     // splits a block merge can hold (contexts up to 2048 positions)
 
 __device__ __forceinline__ size_t kv_index(int page, int L, int layer, int kv, int KVH, int g, int PS, int slot,
                                            int HD) {
@@ -34,6 +40,22 @@ struct AttnSmem {
   int Rpos[ATT_MAXQ];
 };
 
+// bf16 items: K rows give way to the probabilities P[key][query] once the
+// scores are formed, and to the merge weights in a block merge.
+template <int HD, int NW>
+struct AttnSmem<bf16_t, HD, NW> {
+  static constexpr int KST = HD + 8;                // 16-byte aligned rows
+  union alignas(16) {
+    bf16_t Ks[ATT_CHUNK * KST];
+    float P[ATT_CHUNK * ATT_MAXQ];
+    float Wm[2 * ATT_MAXQ * ATT_MAXW];              // merge: [query][split] weights, then l values
+  };
+  alignas(16) bf16_t Vs[ATT_CHUNK * KST];
+  alignas(16) bf16_t Qs[ATT_MAXQ * KST];
+  int Rpos[ATT_MAXQ];
+  float Mx[ATT_MAXQ], Ls[ATT_MAXQ];
+};
+
 typedef uint32_t att_u32x4 __attribute__((ext_vector_type(4)));
 
 // Partial results are stored either plainly (read by a later kernel) or with
@@ -44,17 +66,185 @@ __device__ __forceinline__ void part_store(float* p, float v) {
   else *p = v;
 }
 
-// One work item: KV head g, split s, the rows r0 .. min(r0 + RB, Ma) - 1 with
-// Ma = min(M, *nrows) (positions increasing).  Keys at positions >= local_start
-// come from local_kv rows (scoring: the candidate's own keys/values, rows
-// grouped by group_rows).  Requires all NW*64 threads of the block.
-//
-// Loads take two rounds: (1) the active-row count, the rows' positions, the
-// chunk's page ids and the queries; (2) every key and value of the chunk.
-// Items whose split starts past the block's last position return after (1).
-// DEV: partials are written with device-scope stores.
-template <typename T, int HD, int NW, bool DEV = false>
-__device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__ q, int ldq,
+// bf16 work item (same contract as attn_partial_item below).
+template <int HD, int NW, bool DEV>
+__device__ void attn_item_bf16(AttnSmem<bf16_t, HD, NW>& sm, const bf16_t* __restrict__ q, int ldq,
+                               const bf16_t* __restrict__ pool, const int* __restrict__ page_table, int PS,
+                               int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
+                               const int* __restrict__ pos, int r0, int RB, int g, int s, int nsplit,
+                               const bf16_t* __restrict__ local_kv, int local_start, int group_rows,
+                               float* __restrict__ part) {
+  static_assert(NW == 4, "four waves: one 16-query tile each");
+  constexpr int NT = NW * 64;
+  constexpr int KST = AttnSmem<bf16_t, HD, NW>::KST;
+  constexpr int VEC = 8;                              // bf16 per 16-byte load
+  constexpr int VPR = HD / VEC;
+  constexpr int NLD = ATT_CHUNK * VPR / NT;
+  static_assert(NLD >= 1 && ATT_CHUNK * VPR % NT == 0 && HD % 32 == 0, "staging layout");
+  const int G = H / KVH;
+  const int key_beg = s * ATT_SPLIT;
+  const float scale = 1.0f / sqrtf((float)HD);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rmax = min(r0 + RB, M);
+
+  // ---- round 1: active rows, positions, the split's page ids, the queries
+  const int na = nrows ? *nrows : M;
+  int rp = 0;
+  if (tid < rmax - r0) rp = pos[r0 + tid];
+  const int pg0 = key_beg / PS;
+  const int pg = (lane * PS < ATT_CHUNK && pg0 + lane < n_lpages) ? page_table[pg0 + lane] : 0;
+  constexpr int QPER = (ATT_MAXQ * VPR + NT - 1) / NT;
+  const int nq_max = (rmax - r0) * G;
+  att_u32x4 qreg[QPER];
+#pragma unroll
+  for (int j = 0; j < QPER; ++j) {
+    const int e = min(tid + NT * j, nq_max * VPR - 1);
+    const int qi = e / VPR, vc = e % VPR;
+    const int row = r0 + qi / G, head = g * G + qi % G;
+    qreg[j] = *(const att_u32x4*)(q + (size_t)row * ldq + (size_t)head * HD + vc * VEC);
+  }
+  if (tid < rmax - r0) sm.Rpos[tid] = rp;
+  __syncthreads();
+  const int Ma = min(M, na);
+  const int r1 = min(r0 + RB, Ma);
+  if (r1 <= r0) return;
+  const int maxpos = sm.Rpos[r1 - 1 - r0];
+  if (key_beg > maxpos) return;
+  const int nq = (r1 - r0) * G;
+  const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
+  const int grp_base = group_rows > 0 ? (r0 / group_rows) * group_rows : 0;
+
+  // ---- round 2: the split's keys and values (clamped addresses, zero past the end)
+  att_u32x4 kreg[NLD], vreg[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int e = tid + NT * j;
+    const int t = e / VPR, vc = e % VPR;
+    const int kp = key_beg + t;
+    const int kq = min(kp, key_end - 1);
+    const int page = __shfl(pg, (kq - key_beg) / PS, 64);
+    const bool local = local_kv && kq >= local_start;
+    const size_t lbase = ((size_t)(grp_base + (kq - local_start)) * 2) * KVH * HD + (size_t)g * HD;
+    const bf16_t* kr = local ? local_kv + lbase : pool + kv_index(page, L, layer, 0, KVH, g, PS, kq % PS, HD);
+    const bf16_t* vr = local ? local_kv + lbase + (size_t)KVH * HD
+                            : pool + kv_index(page, L, layer, 1, KVH, g, PS, kq % PS, HD);
+    kreg[j] = *(const att_u32x4*)(kr + vc * VEC);
+    vreg[j] = *(const att_u32x4*)(vr + vc * VEC);
+    if (kp >= key_end) {
+      kreg[j] = att_u32x4{0u, 0u, 0u, 0u};
+      vreg[j] = att_u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < QPER; ++j) {
+    const int e = tid + NT * j;
+    if (e < nq * VPR) *(att_u32x4*)(sm.Qs + (e / VPR) * KST + (e % VPR) * VEC) = qreg[j];
+  }
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int e = tid + NT * j;
+    const int t = e / VPR, vc = e % VPR;
+    *(att_u32x4*)(sm.Ks + t * KST + vc * VEC) = kreg[j];
+    *(att_u32x4*)(sm.Vs + t * KST + vc * VEC) = vreg[j];
+  }
+  __syncthreads();
+
+  // ---- scores: wave w forms S[key][query] for queries [16 w, 16 w + 16) and all 64 keys;
+  // acc[kt][i] = S[key 16 kt + 4 (lane >> 4) + i][query 16 w + (lane & 15)]
+  const bool qwork = 16 * wave < nq;                  // wave-uniform
+  const int ql = lane & 15, g4 = lane >> 4;
+  f32x4 acc[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (qwork) {
+#pragma unroll
+    for (int ds = 0; ds < HD / 32; ++ds) {
+      const bf16x8 bq = *(const bf16x8*)(sm.Qs + (16 * wave + ql) * KST + 32 * ds + 8 * g4);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const bf16x8 ak = *(const bf16x8*)(sm.Ks + (16 * kt + ql) * KST + 32 * ds + 8 * g4);
+        acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bq, acc[kt], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();                                    // K is no longer read: P takes its place
+
+  // ---- softmax of each query over the split's keys it sees (causal: key position <= its row's)
+  if (qwork) {
+    const int qq = 16 * wave + ql;
+    const bool qv = qq < nq;
+    const int prow = qv ? sm.Rpos[qq / G] : -1;
+    float sc[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kp = key_beg + 16 * kt + 4 * g4 + i;
+        const bool valid = kp < key_end && kp <= prow;
+        sc[kt][i] = valid ? __fmul_rn(acc[kt][i], scale) : -INFINITY;
+        mx = fmaxf(mx, sc[kt][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float ps = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pe = sc[kt][i] == -INFINITY ? 0.f : expf(__fsub_rn(sc[kt][i], mx));
+        sm.P[(16 * kt + 4 * g4 + i) * ATT_MAXQ + qq] = pe;
+        ps += pe;
+      }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    if (g4 == 0) {
+      sm.Mx[qq] = mx;
+      sm.Ls[qq] = ps;
+    }
+  }
+  __syncthreads();
+
+  // ---- o[query][d] = sum over keys in order of p * v (fp32); thread: dims 2 dp, 2 dp + 1 of query quads
+  constexpr int DP = HD / 2, QG = NT / DP;
+  const int dp = tid % DP, qg = tid / DP;
+  for (int quad = qg; 4 * quad < nq; quad += QG) {
+    float o[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j][0] = o[j][1] = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < ATT_CHUNK; ++k) {
+      const uint32_t v2 = *(const uint32_t*)(sm.Vs + k * KST + 2 * dp);
+      const f32x4 p4 = *(const f32x4*)(sm.P + k * ATT_MAXQ + 4 * quad);
+      const float vlo = __uint_as_float(v2 << 16), vhi = __uint_as_float(v2 & 0xFFFF0000u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[j][0] = fmaf(p4[j], vlo, o[j][0]);
+        o[j][1] = fmaf(p4[j], vhi, o[j][1]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int qq = 4 * quad + j;
+      if (qq >= nq) break;
+      if (key_beg > sm.Rpos[qq / G]) continue;        // the row sees no key of this split
+      const int row = r0 + qq / G, head = g * G + qq % G;
+      float* dstp = part + (((size_t)row * H + head) * nsplit + s) * (HD + 2);
+      part_store<DEV>(dstp + 2 * dp, o[j][0]);
+      part_store<DEV>(dstp + 2 * dp + 1, o[j][1]);
+      if (dp == 0) {
+        part_store<DEV>(dstp + HD, sm.Mx[qq]);
+        part_store<DEV>(dstp + HD + 1, sm.Ls[qq]);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// fp32 work item (FMAs throughout).
+template <typename T, int HD, int NW, bool DEV>
+__device__ void attn_item_scalar(AttnSmem<T, HD, NW>& sm, const T* __restrict__ q, int ldq,
                                   const T* __restrict__ pool, const int* __restrict__ page_table, int PS,
                                   int n_lpages, int L, int layer, int H, int KVH, int M,
                                   const int* __restrict__ nrows, const int* __restrict__ pos, int r0, int RB, int g,
@@ -196,6 +386,30 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
   __syncthreads();
 }
 
+// One work item: KV head g, split s, the rows r0 .. min(r0 + RB, Ma) - 1 with
+// Ma = min(M, *nrows) (positions increasing).  Keys at positions >= local_start
+// come from local_kv rows (scoring: the candidate's own keys/values, rows
+// grouped by group_rows).  Requires all NW*64 threads of the block.
+//
+// Loads take two rounds: (1) the active-row count, the rows' positions, the
+// chunk's page ids and the queries; (2) every key and value of the chunk.
+// Items whose split starts past the block's last position return after (1).
+// DEV: partials are written with device-scope stores.
+template <typename T, int HD, int NW, bool DEV = false>
+__device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__ q, int ldq,
+                                  const T* __restrict__ pool, const int* __restrict__ page_table, int PS,
+                                  int n_lpages, int L, int layer, int H, int KVH, int M,
+                                  const int* __restrict__ nrows, const int* __restrict__ pos, int r0, int RB, int g,
+                                  int s, int nsplit, const T* __restrict__ local_kv, int local_start, int group_rows,
+                                  float* __restrict__ part) {
+  if constexpr (sizeof(T) == 2)
+    attn_item_bf16<HD, NW, DEV>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0, RB,
+                                g, s, nsplit, local_kv, local_start, group_rows, part);
+  else
+    attn_item_scalar<T, HD, NW, DEV>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0,
+                                     RB, g, s, nsplit, local_kv, local_start, group_rows, part);
+}
+
 // Merge the splits of (row, head) in split order; component d of the output.
 template <int HD>
 __device__ __forceinline__ float attn_combine_value(const float* __restrict__ part, int nsplit, int row, int head,
@@ -243,10 +457,135 @@ __device__ __forceinline__ float attn_combine_value(const float* __restrict__ pa
   return __fdiv_rn(o, l);
 }
 
+// Merge by one block of the partials of rows r0 .. r1 - 1 (all G query heads
+// of KV head g), once every split has stored its partial (positions from
+// sm.Rpos, at most ATT_MAXW splits).  Same arithmetic as attn_combine_value,
+// with each (query, split) weight formed once: (1) every pair's m and l,
+// (2) per query the maximum, the weights and l in split order, (3) per output
+// element the weighted sum of the splits' o in split order over l.  The o
+// values of the first MP dim pairs per thread are loaded together with (1).
+// The output is in the decode block layout.
+template <int HD, int NW>
+__device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __restrict__ part, int nsplit, int r0,
+                                 int r1, int G, int g, int H, bf16_t* __restrict__ out) {
+  constexpr int NT = NW * 64;
+  constexpr int REC = HD + 2;
+  constexpr int PR = HD / 2;                          // dim pairs per query
+  constexpr int CH = 16;                              // splits per load round of (3)
+  constexpr int MP = 4;                               // dim pairs per thread in the first round
+  constexpr int P1 = ATT_MAXQ * ATT_MAXW / NT;
+  const int tid = threadIdx.x;
+  const int nq = (r1 - r0) * G;
+  const int npair = nq * PR;
+  float* Wt = sm.Wm;                                  // [query][split]: m, then the weight
+  float* Lv = sm.Wm + ATT_MAXQ * ATT_MAXW;            // [query][split]: l
+  auto rec = [&](int qq, int sp) -> const float* {
+    return part + (((size_t)(r0 + qq / G) * H + g * G + qq % G) * nsplit + sp) * REC;
+  };
+  auto nsplits = [&](int qq) { return sm.Rpos[qq / G] / ATT_SPLIT + 1; };
+
+  // loads of (1) and of the first round of (3)
+  float mv[P1], lv[P1];
+#pragma unroll
+  for (int j = 0; j < P1; ++j) {
+    const int idx = tid + NT * j;
+    const int qq = idx / ATT_MAXW, sp = idx % ATT_MAXW;
+    if (qq < nq && sp < nsplits(qq)) {
+      const float* pr = rec(qq, sp);
+      mv[j] = pr[HD];
+      lv[j] = pr[HD + 1];
+    }
+  }
+  float2 ov[MP][CH];
+#pragma unroll
+  for (int x = 0; x < MP; ++x) {
+    const int pi = tid + NT * x;
+    if (pi < npair) {
+      const int qq = pi / PR, d2 = (pi % PR) * 2, ns = nsplits(qq);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) ov[x][c] = *(const float2*)(rec(qq, min(c, ns - 1)) + d2);
+    }
+  }
+  // (1)
+#pragma unroll
+  for (int j = 0; j < P1; ++j) {
+    const int idx = tid + NT * j;
+    const int qq = idx / ATT_MAXW, sp = idx % ATT_MAXW;
+    if (qq < nq && sp < nsplits(qq)) {
+      Wt[idx] = mv[j];
+      Lv[idx] = lv[j];
+    }
+  }
+  __syncthreads();
+  // (2)
+  if (tid < nq) {
+    const int ns = nsplits(tid);
+    float m = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, Wt[tid * ATT_MAXW + sp]);
+    float l = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float w = expf(__fsub_rn(Wt[tid * ATT_MAXW + sp], m));
+      Wt[tid * ATT_MAXW + sp] = w;
+      l = fmaf(Lv[tid * ATT_MAXW + sp], w, l);
+    }
+    sm.Ls[tid] = l;
+  }
+  __syncthreads();
+  // (3): splits [c0, ns) of one dim pair, accumulated into o; then the store
+  auto rest = [&](int qq, int d2, int ns, int c0, float2& o) {
+    const float* w = Wt + qq * ATT_MAXW;
+    for (; c0 < ns; c0 += CH) {
+      float2 v[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) v[c] = *(const float2*)(rec(qq, min(c0 + c, ns - 1)) + d2);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c0 + c < ns) {
+          o.x = fmaf(v[c].x, w[c0 + c], o.x);
+          o.y = fmaf(v[c].y, w[c0 + c], o.y);
+        }
+      }
+    }
+  };
+  auto store = [&](int qq, int d2, float2 o) {
+    const int row = r0 + qq / G, head = g * G + qq % G;
+    const float l = sm.Ls[qq];
+    bf16_t* dst = out + dec_act_index(row, head * HD + d2);   // d2 even: d2 + 1 is the next element
+    st(dst, __fdiv_rn(o.x, l));
+    st(dst + 1, __fdiv_rn(o.y, l));
+  };
+#pragma unroll
+  for (int x = 0; x < MP; ++x) {
+    const int pi = tid + NT * x;
+    if (pi < npair) {
+      const int qq = pi / PR, d2 = (pi % PR) * 2, ns = nsplits(qq);
+      const float* w = Wt + qq * ATT_MAXW;
+      float2 o = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c < ns) {
+          o.x = fmaf(ov[x][c].x, w[c], o.x);
+          o.y = fmaf(ov[x][c].y, w[c], o.y);
+        }
+      }
+      rest(qq, d2, ns, CH, o);
+      store(qq, d2, o);
+    }
+  }
+  for (int pi = tid + NT * MP; pi < npair; pi += NT) {
+    const int qq = pi / PR, d2 = (pi % PR) * 2;
+    float2 o = make_float2(0.f, 0.f);
+    rest(qq, d2, nsplits(qq), 0, o);
+    store(qq, d2, o);
+  }
+}
+
+// blocked: out in the decode block layout (ldo unused), else rows of stride ldo.
 template <typename T, int HD>
 __device__ __forceinline__ void attn_combine_elem(const float* __restrict__ part, int nsplit, int row, int head,
-                                                  int H, int p, int d, T* __restrict__ out, int ldo) {
-  st(out + (size_t)row * ldo + (size_t)head * HD + d, attn_combine_value<HD>(part, nsplit, row, head, H, p, d));
+                                                  int H, int p, int d, T* __restrict__ out, int ldo, bool blocked) {
+  const size_t o = blocked ? dec_act_index(row, head * HD + d) : (size_t)row * ldo + (size_t)head * HD + d;
+  st(out + o, attn_combine_value<HD>(part, nsplit, row, head, H, p, d));
 }
 
 }  // namespace ssd

@@ -161,6 +161,13 @@ __device__ __forceinline__ void rope_apply(float x1, float x2, float2 cs, float&
   y2 = __fadd_rn(__fmul_rn(x2, cs.x), __fmul_rn(x1, cs.y));
 }
 
+// Activation layout of a decode block (at most 16 rows): blocks of 32
+// columns, each holding the 16 rows' 32 values contiguously, so that one
+// matrix-core step's activations (16 rows x 32 columns) are one 1 KB run.
+__device__ __forceinline__ size_t dec_act_index(int row, int col) {
+  return (size_t)(col >> 5) * 512 + (size_t)row * 32 + (col & 31);
+}
+
 __device__ __forceinline__ float swiglu(float g, float u) {
   return __fmul_rn(__fdiv_rn(g, __fadd_rn(1.0f, expf(-g))), u);
 }

@@ -47,7 +47,33 @@ constexpr int DEC_SSP = 8;    // RMS tile sums per lane and row: K <= 64 * 16 * 
 // activations (no masking on the load path); their outputs are not stored.
 // ===========================================================================
 
-template <int EPI, int NW, bool HALF>
+// Per-tile output rows: f0 + i (and f1 + i for the two-set epilogues); for QKV also the head slot and
+// the pair index base d0.
+struct DecTile {
+  int f0, f1, slot, d0;
+};
+
+template <int EPI, bool HALF>
+__device__ __forceinline__ DecTile dec_tile(const DecGemm& a, int tile) {
+  constexpr int SET = HALF ? 8 : 16;
+  DecTile t{0, 0, 0, 0};
+  if (EPI == DEC_QKV) {
+    const int per = a.HD / (2 * SET);           // tiles per head slot: pairs (i, i + HD/2), i in [d0, d0 + SET)
+    t.slot = tile / per;
+    t.d0 = (tile % per) * SET;
+    t.f0 = t.slot * a.HD + t.d0;
+    t.f1 = t.f0 + a.HD / 2;
+  } else {
+    t.f0 = tile * SET;
+    t.f1 = a.N + t.f0;                          // SwiGLU: the up rows follow the N gate rows
+  }
+  return t;
+}
+
+// TPW tiles per workgroup share each activation load (fewer activation reads
+// per weight byte when M > 1); the arithmetic of an output element does not
+// depend on TPW.
+template <int EPI, int NW, bool HALF, int TPW>
 __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   if (a.stop && *a.stop) return;
   const int Ma = a.nrows ? min(a.M, *a.nrows) : a.M;
@@ -56,34 +82,29 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   constexpr bool DUAL = TWO && !HALF;                           // 16 + 16 rows: two accumulators
   static_assert(!HALF || TWO, "half tiles pair two row sets");
   constexpr bool NORM = EPI != DEC_RESID;
-  constexpr int NT = DUAL ? 2 : 1;
+  constexpr int SPT = DUAL ? 2 : 1;             // accumulators (16-row W sets) per tile
+  constexpr int NS = TPW * SPT;
+  constexpr int U = NS <= 2 ? DEC_U : DEC_U / 2;
   constexpr int RPW = (16 + NW - 1) / NW;       // rows whose scale one wave computes
   const int K = a.K;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int tile = blockIdx.x;
+  const int ntiles = (int)gridDim.x * TPW;      // grid covers the tiles; a tile past the last one
+  (void)ntiles;                                 // repeats the last (its outputs are not stored)
 
-  // W rows of this tile.  Two-set epilogues pair row f0 + i with row f1 + i: DUAL tiles take 16 of
-  // each (two accumulators), HALF tiles 8 of each in one accumulator (MFMA rows 0-7 and 8-15).
-  constexpr int SET = HALF ? 8 : 16;
-  int f0, f1, slot = 0, d0 = 0;
-  if (EPI == DEC_QKV) {
-    const int per = a.HD / (2 * SET);           // tiles per head slot: pairs (i, i + HD/2), i in [d0, d0 + SET)
-    slot = tile / per;
-    d0 = (tile % per) * SET;
-    f0 = slot * a.HD + d0;
-    f1 = f0 + a.HD / 2;
-  } else {
-    f0 = tile * SET;
-    f1 = a.N + f0;                              // SwiGLU: the up rows follow the N gate rows
+  // W rows: set (j, 0) = f0 + r (HALF: f0 + r for r < 8, f1 + r - 8 after), set (j, 1) = f1 + r
+  const bf16_t* wp[NS];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const DecTile t = dec_tile<EPI, HALF>(a, min((int)blockIdx.x * TPW + j, a.n_tiles - 1));
+    int wrow = t.f0 + r;
+    if (HALF) wrow = (r < 8 ? t.f0 : t.f1) + (r & 7);
+    if (EPI == DEC_STORE) wrow = min(wrow, a.N - 1);   // rows past N repeat the last W row; not stored
+    wp[j * SPT] = a.W + (size_t)wrow * K + g * 8;
+    if (DUAL) wp[j * SPT + 1] = a.W + (size_t)(t.f1 + r) * K + g * 8;
   }
-  int wrow = f0 + r;
-  if (HALF) wrow = (r < 8 ? f0 : f1) + (r & 7);
-  if (EPI == DEC_STORE) wrow = min(wrow, a.N - 1);   // tiles past N repeat the last W row; not stored
-  const bf16_t* wp = a.W + (size_t)wrow * K + g * 8;
-  const bf16_t* wp2 = a.W + (size_t)(f1 + r) * K + g * 8;
-  const bf16_t* xp = a.X + (size_t)min(r, Ma - 1) * a.ldx + g * 8;
+  const bf16_t* xp = a.X + dec_act_index(min(r, Ma - 1), g * 8);   // step t: xp + 512 t
 
   // RMS tile sums of the rows this wave scales: loaded first, summed after the weight loads are issued
   __shared__ float sinv[16];
@@ -101,13 +122,16 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   const int nu = K >> 6;
   const int s0 = 2 * ((nu * wave) / NW);
   const int n = 2 * ((nu * (wave + 1)) / NW) - s0;   // 32-element steps of this wave (>= 2)
-  dec_u32x4 wa[DEC_U], wb[DEC_U], xa[DEC_U];
+  dec_u32x4 w[NS][U], xa[U];
+  auto reload = [&](int u, int step) {
+    const int k = (s0 + step) * 32;
 #pragma unroll
-  for (int u = 0; u < DEC_U; ++u) {
-    const int k = (s0 + min(u, n - 1)) * 32;
-    wa[u] = *(const dec_u32x4*)(wp + k);
-    if (DUAL) wb[u] = *(const dec_u32x4*)(wp2 + k);
-    xa[u] = *(const dec_u32x4*)(xp + k);
+    for (int j = 0; j < NS; ++j) w[j][u] = *(const dec_u32x4*)(wp[j] + k);
+    xa[u] = *(const dec_u32x4*)(xp + (size_t)(s0 + step) * 512);
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    reload(u, min(u, n - 1));
     __builtin_amdgcn_sched_barrier(0);       // same load order as the steady loop
   }
 
@@ -126,110 +150,108 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
     }
   }
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // steps are consumed in increasing order; the steady loop has no branches, so the compiler's
-  // wait before each step's MFMA leaves the later steps' loads in flight
+  // wait before each step's MFMAs leaves the later steps' loads in flight
   auto consume = [&](int u) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[u]),
-                                                  __builtin_bit_cast(bf16x8, xa[u]), acc, 0, 0, 0);
-    if (DUAL)
-      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb[u]),
-                                                     __builtin_bit_cast(bf16x8, xa[u]), acc2, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[j][u]),
+                                                       __builtin_bit_cast(bf16x8, xa[u]), acc[j], 0, 0, 0);
   };
-  auto reload = [&](int u, int step) {
-    const int k = (s0 + step) * 32;
-    wa[u] = *(const dec_u32x4*)(wp + k);
-    if (DUAL) wb[u] = *(const dec_u32x4*)(wp2 + k);
-    xa[u] = *(const dec_u32x4*)(xp + k);
-  };
-  const int nfull = n / DEC_U, rem = n - nfull * DEC_U;
+  const int nfull = n / U, rem = n - nfull * U;
   for (int b = 1; b < nfull; ++b) {
 #pragma unroll
-    for (int u = 0; u < DEC_U; ++u) {
+    for (int u = 0; u < U; ++u) {
       consume(u);
-      reload(u, b * DEC_U + u);
-      __builtin_amdgcn_sched_barrier(0);     // keep the issue order: one step's MFMA, then its reload
+      reload(u, b * U + u);
+      __builtin_amdgcn_sched_barrier(0);     // keep the issue order: one step's MFMAs, then its reload
     }
   }
   if (nfull > 0) {
     if (rem > 0) {
 #pragma unroll
-      for (int u = 0; u < DEC_U; ++u) {
+      for (int u = 0; u < U; ++u) {
         consume(u);
-        reload(u, min(nfull * DEC_U + u, n - 1));
+        reload(u, min(nfull * U + u, n - 1));
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < DEC_U; ++u) consume(u);
+      for (int u = 0; u < U; ++u) consume(u);
     }
   }
 #pragma unroll
-  for (int u = 0; u < DEC_U; ++u)
+  for (int u = 0; u < U; ++u)
     if (u < rem) consume(u);
 
-  // acc[i] holds D[feature 4g + i][row r]
-  __shared__ float red[NT][NW][16][17];
+  // acc[j][i] holds D[feature 4g + i][row r] of set j
+  __shared__ float red[NS][NW][16][17];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    red[0][wave][4 * g + i][r] = acc[i];
-    if (DUAL) red[NT - 1][wave][4 * g + i][r] = acc2[i];
-  }
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[j][wave][4 * g + i][r] = acc[j][i];
   __syncthreads();
   if (threadIdx.x >= 256) return;
   const int row = threadIdx.x >> 4, nn = threadIdx.x & 15;
   if (row >= Ma) return;                        // uniform over each group of 16 lanes
-  if (HALF && nn >= 8) return;
-  float s = 0.f, s2 = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    s += red[0][w][nn][row];
-    if (DUAL) s2 += red[NT - 1][w][nn][row];
-    if (HALF) s2 += red[0][w][nn + 8][row];
-  }
-
-  if constexpr (EPI == DEC_STORE) {
-    if (f0 + nn < a.N) a.Y[(size_t)row * a.ldy + f0 + nn] = __fmul_rn(s, sinv[row]);
-  } else if constexpr (EPI == DEC_RESID) {
-    const int col = f0 + nn;
-    float* hp = a.Y + (size_t)row * a.ldy + col;
-    const float hn = __fadd_rn(*hp, s);
-    *hp = hn;
-    if (a.gain_next) {
-      st(a.xg_next + (size_t)row * a.N + col, __fmul_rn(hn, a.gain_next[col]));
-      const float t = tile16_ss_lanes(hn);
-      if (nn == 0) a.ss_next[(size_t)row * (a.N / 16) + col / 16] = t;
+  for (int j = 0; j < TPW; ++j) {
+    const int tile = (int)blockIdx.x * TPW + j;
+    if (tile >= a.n_tiles) break;
+    if (HALF && nn >= 8) break;
+    const DecTile t = dec_tile<EPI, HALF>(a, tile);
+    float s = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      s += red[j * SPT][ww][nn][row];
+      if (DUAL) s2 += red[j * SPT + 1][ww][nn][row];
+      if (HALF) s2 += red[j][ww][nn + 8][row];
     }
-  } else if constexpr (EPI == DEC_SWIGLU) {
-    const float inv = sinv[row];
-    st(a.A + (size_t)row * a.lda + f0 + nn, swiglu(__fmul_rn(s, inv), __fmul_rn(s2, inv)));
-  } else {
-    const float inv = sinv[row];
-    const float x1 = __fmul_rn(s, inv), x2 = __fmul_rn(s2, inv);
-    const int HD = a.HD, H = a.H, KVH = a.KVH;
-    const int i = d0 + nn;                      // pair index
-    const int p = a.pos[row];
-    const int lp = p / a.PS;
-    if (p < 0 || lp >= a.n_lpages) {
-      if (nn == 0) atomicOr(a.err, ERRF_CAPACITY);
-      return;
-    }
-    bf16_t* dst;
-    if (slot < H) {
-      dst = a.q + (size_t)row * a.ldq + (size_t)slot * HD;
+    if constexpr (EPI == DEC_STORE) {
+      if (t.f0 + nn < a.N) a.Y[(size_t)row * a.ldy + t.f0 + nn] = __fmul_rn(s, sinv[row]);
+    } else if constexpr (EPI == DEC_RESID) {
+      const int col = t.f0 + nn;
+      float* hp = a.Y + (size_t)row * a.ldy + col;
+      const float hn = __fadd_rn(*hp, s);
+      *hp = hn;
+      if (a.gain_next) {
+        st(a.xg_next + dec_act_index(row, col), __fmul_rn(hn, a.gain_next[col]));
+        const float tt = tile16_ss_lanes(hn);
+        if (nn == 0) a.ss_next[(size_t)row * (a.N / 16) + col / 16] = tt;
+      }
+    } else if constexpr (EPI == DEC_SWIGLU) {
+      const float inv = sinv[row];
+      st(a.A + dec_act_index(row, t.f0 + nn), swiglu(__fmul_rn(s, inv), __fmul_rn(s2, inv)));
     } else {
-      const int kvsel = slot < H + KVH ? 0 : 1;
-      const int gg = slot - H - kvsel * KVH;
-      dst = a.pool + kv_index(a.page_table[lp], a.L, a.layer, kvsel, KVH, gg, a.PS, p % a.PS, HD);
-    }
-    if (slot < H + KVH) {
-      float y1, y2;
-      rope_apply(x1, x2, a.rope_cs[(size_t)p * (HD / 2) + i], y1, y2);
-      st(dst + i, y1);
-      st(dst + i + HD / 2, y2);
-    } else {
-      st(dst + i, x1);
-      st(dst + i + HD / 2, x2);
+      const float inv = sinv[row];
+      const float x1 = __fmul_rn(s, inv), x2 = __fmul_rn(s2, inv);
+      const int HD = a.HD, H = a.H, KVH = a.KVH;
+      const int i = t.d0 + nn;                  // pair index
+      const int p = a.pos[row];
+      const int lp = p / a.PS;
+      if (p < 0 || lp >= a.n_lpages) {
+        if (nn == 0) atomicOr(a.err, ERRF_CAPACITY);
+        continue;
+      }
+      bf16_t* dst;
+      if (t.slot < H) {
+        dst = a.q + (size_t)row * a.ldq + (size_t)t.slot * HD;
+      } else {
+        const int kvsel = t.slot < H + KVH ? 0 : 1;
+        const int gg = t.slot - H - kvsel * KVH;
+        dst = a.pool + kv_index(a.page_table[lp], a.L, a.layer, kvsel, KVH, gg, a.PS, p % a.PS, HD);
+      }
+      if (t.slot < H + KVH) {
+        float y1, y2;
+        rope_apply(x1, x2, a.rope_cs[(size_t)p * (HD / 2) + i], y1, y2);
+        st(dst + i, y1);
+        st(dst + i + HD / 2, y2);
+      } else {
+        st(dst + i, x1);
+        st(dst + i + HD / 2, x2);
+      }
     }
   }
 }
@@ -238,15 +260,30 @@ bool profile_wants(int cls);
 void profile_before(hipStream_t s);
 void profile_after(hipStream_t s, double bytes);
 
-// Tile shapes of the two-set projections (HALF: 8 + 8 rows per workgroup, twice the workgroups).
+// Tile shapes of the two-set projections (HALF: 8 + 8 rows per tile, twice the tiles).
 constexpr bool DEC_HALF_QKV = true;
 constexpr bool DEC_HALF_SWIGLU = false;
 
-static int dec_tiles(int epi, int N, int HD) {
-  (void)HD;
+static int dec_tiles(int epi, int N) {
   if (epi == DEC_QKV) return DEC_HALF_QKV ? N / 16 : N / 32;
   if (epi == DEC_SWIGLU) return DEC_HALF_SWIGLU ? N / 8 : N / 16;
   return (N + 15) / 16;
+}
+
+// Tiles per workgroup: one (most workgroups in flight), except for the LM head
+// with several rows: its 2000 tiles keep the chip busy at two per workgroup,
+// and each activation load then feeds twice the weights.
+static int dec_tpw(int epi, int M) {
+  return epi == DEC_STORE && M > 1 ? 2 : 1;
+}
+
+template <int EPI, bool HALF>
+static void dec_launch(const DecGemm& a, int tpw, hipStream_t s) {
+  const dim3 block(DEC_NW * 64);
+  if (tpw == 2)
+    hipLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 2>), dim3((a.n_tiles + 1) / 2), block, 0, s, a);
+  else
+    hipLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 1>), dim3(a.n_tiles), block, 0, s, a);
 }
 
 int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
@@ -256,19 +293,18 @@ int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
   if (epi == DEC_QKV && (a.HD % 32 != 0 || a.N % a.HD != 0)) return SSD_ERR_SHAPE;
   if (a.K / 64 < DEC_NW) return SSD_ERR_SHAPE;
   if (epi == DEC_SWIGLU && a.N % (DEC_HALF_SWIGLU ? 8 : 16) != 0) return SSD_ERR_SHAPE;
-  const dim3 grid(dec_tiles(epi, a.N, a.HD));
+  DecGemm b = a;
+  b.n_tiles = dec_tiles(epi, a.N);
+  const int tpw = dec_tpw(epi, a.M);
   // profile classes: 0 plain-store projections (QKV, LM head), 1 residual, 2 gate/up
   const int cls = epi == DEC_RESID ? 1 : (epi == DEC_SWIGLU ? 2 : 0);
   const bool prof = profile_wants(cls);
   if (prof) profile_before(s);
-  const dim3 block(DEC_NW * 64);
   switch (epi) {
-    case DEC_STORE: hipLaunchKernelGGL((dec_gemm_kernel<DEC_STORE, DEC_NW, false>), grid, block, 0, s, a); break;
-    case DEC_RESID: hipLaunchKernelGGL((dec_gemm_kernel<DEC_RESID, DEC_NW, false>), grid, block, 0, s, a); break;
-    case DEC_SWIGLU:
-      hipLaunchKernelGGL((dec_gemm_kernel<DEC_SWIGLU, DEC_NW, DEC_HALF_SWIGLU>), grid, block, 0, s, a);
-      break;
-    default: hipLaunchKernelGGL((dec_gemm_kernel<DEC_QKV, DEC_NW, DEC_HALF_QKV>), grid, block, 0, s, a);
+    case DEC_STORE: dec_launch<DEC_STORE, false>(b, tpw, s); break;
+    case DEC_RESID: dec_launch<DEC_RESID, false>(b, tpw, s); break;
+    case DEC_SWIGLU: dec_launch<DEC_SWIGLU, DEC_HALF_SWIGLU>(b, tpw, s); break;
+    default: dec_launch<DEC_QKV, DEC_HALF_QKV>(b, tpw, s);
   }
   if (prof) {
     // algorithmic bytes: weights once, activations in once, results out once (residual: read + write)
@@ -316,13 +352,7 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int G = H / KVH;
-  const int n = (r1 - r0) * G * HD;
-  for (int e = threadIdx.x; e < n; e += 256) {
-    const int d = e % HD, qi = e / HD;
-    const int row = r0 + qi / G, head = g * G + qi % G;
-    attn_combine_elem<T, HD>(part, nsplit, row, head, H, pos[row], d, out, ldo);
-  }
+  attn_merge_block<HD, 4>(sm, part, nsplit, r0, r1, H / KVH, g, H, out);
 }
 
 int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer, int H, int KVH,
@@ -333,6 +363,12 @@ int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv,
   const int RB = ATT_MAXQ / G;
   if (RB < 1 || M > 16) return SSD_ERR_SHAPE;
   const int nsplit = attention_nsplit(max_ctx);
+  if (nsplit > ATT_MAXW) {
+    // longer contexts: partials, then one merge block per (row, head) (the general kernels)
+    const RowBlock rb{M, nrows, pos, nullptr, stop};
+    return launch_attention(SSD_DTYPE_BF16, head_dim, q, ldq, kv, L, layer, H, KVH, rb, max_ctx, nullptr, 0, 0, part,
+                            out, ldo, s, true);
+  }
   const dim3 grid(KVH, nsplit, (M + RB - 1) / RB);
 #define ATT_DEC(HD)                                                                                             \
   hipLaunchKernelGGL((attn_dec_kernel<bf16_t, HD>), grid, dim3(256), 0, s, (const bf16_t*)q, ldq,                \
@@ -382,7 +418,7 @@ __global__ __launch_bounds__(256) void dec_entry_kernel(const bf16_t* __restrict
       if (NORM) {
         const float t = tile16_ss_lanes(v[j]);
         if (i < D) {
-          st(xg + (size_t)dr * D + i, __fmul_rn(v[j], gv[j]));
+          st(xg + dec_act_index(dr, i), __fmul_rn(v[j], gv[j]));
           if ((threadIdx.x & 15) == 0) ss[(size_t)dr * (D / 16) + i / 16] = t;
         }
       }

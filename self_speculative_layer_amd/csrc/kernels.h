@@ -54,9 +54,11 @@ int launch_rope_kv(int dtype, int head_dim, const float* qkv, int ldqkv, void* q
 // Attention of every row over cached keys at positions <= its own (keys at
 // positions >= local_start come from local_kv rows of the row's own group of
 // `group_rows` consecutive rows).  Output act dtype [M, H*HD].
+// out_blocked: the output in the decode block layout (M <= 16) instead of rows of stride ldo.
 int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer,
                      int H, int KVH, const RowBlock& rb, int max_ctx, const void* local_kv,
-                     int local_start, int group_rows, float* part, void* out, int ldo, hipStream_t s);
+                     int local_start, int group_rows, float* part, void* out, int ldo, hipStream_t s,
+                     bool out_blocked = false);
 size_t attention_partial_floats(int max_rows, int H, int head_dim, int max_ctx);
 // Number of fixed key splits covering max_ctx positions (the partial buffer's split dimension).
 int attention_nsplit(int max_ctx);
@@ -108,20 +110,23 @@ enum DecEpilogue {
 };
 
 // inv[m] = 1 / sqrt(mean(h^2) + eps) from the rows' 16-feature tile sums ss[m][K/16].
+// Activations (X, and the A / xg_next outputs) are in the decode block layout
+// (dec_act_index in common.h).
 struct DecGemm {
   const bf16_t* W; int N, K;        // W [N rows (SWIGLU: 2N), K]
-  const bf16_t* X; int ldx;         // activations [M, K]
+  const bf16_t* X;                  // activations [M <= 16, K], decode block layout
   int M; const int* nrows; const int* stop;
   const float* ss; float eps;       // STORE, SWIGLU, QKV: tile sums of the normalised rows
   float* Y; int ldy;                // STORE: output; RESID: residual stream
-  bf16_t* A; int lda;               // SWIGLU output
+  bf16_t* A;                        // SWIGLU output [M, N], decode block layout
   const float* gain_next;           // RESID: gain of the next RMSNorm consumer (nullable: none)
-  bf16_t* xg_next;                  //   its input bf16(h * gain) [M, N]
+  bf16_t* xg_next;                  //   its input bf16(h * gain) [M, N], decode block layout
   float* ss_next;                   //   tile sums of h^2 [M, N/16]
   bf16_t* q; int ldq;               // QKV: rotated queries [M, H*HD]
   bf16_t* pool; const int* page_table;
   int PS, n_lpages, L, layer, H, KVH, HD;
   const int* pos; const float2* rope_cs; int* err;
+  int n_tiles;                      // set by the launcher
 };
 int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s);
 

@@ -421,18 +421,20 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 
 template <typename T, int HD>
 __global__ void attn_combine_kernel(const float* __restrict__ part, int nsplit, int M, const int* __restrict__ nrows,
-                                    const int* __restrict__ pos, int H, T* __restrict__ out, int ldo,
+                                    const int* __restrict__ pos, int H, T* __restrict__ out, int ldo, int blocked,
                                     const int* __restrict__ stop) {
   if (stop && *stop) return;
   const int row = blockIdx.x, head = blockIdx.y;
   if (row >= active_rows(M, nrows)) return;
-  attn_combine_elem<T, HD>(part, nsplit, row, head, H, pos[row], threadIdx.x, out, ldo);
+  attn_combine_elem<T, HD>(part, nsplit, row, head, H, pos[row], threadIdx.x, out, ldo, blocked != 0);
 }
 
 int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer,
                      int H, int KVH, const RowBlock& rb, int max_ctx, const void* local_kv,
-                     int local_start, int group_rows, float* part, void* out, int ldo, hipStream_t s) {
+                     int local_start, int group_rows, float* part, void* out, int ldo, hipStream_t s,
+                     bool out_blocked) {
   if (rb.M <= 0) return 0;
+  if (out_blocked && rb.M > 16) return SSD_ERR_SHAPE;
   const int G = H / KVH;
   int RB = ATT_MAXQ / G;
   if (RB < 1) return SSD_ERR_SHAPE;
@@ -448,7 +450,7 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
                        kv.page_table, kv.page_size, kv.n_lpages, L, layer, H, KVH, rb.M, rb.nrows, rb.pos, RB,    \
                        nsplit, (const T*)local_kv, local_start, group_rows, part, rb.stop);                      \
     hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(rb.M, H), dim3(HD), 0, s, part, nsplit, rb.M, rb.nrows, \
-                       rb.pos, H, (T*)out, ldo, rb.stop);                                                        \
+                       rb.pos, H, (T*)out, ldo, out_blocked ? 1 : 0, rb.stop);                                  \
   } while (0)
   if (dtype == SSD_DTYPE_BF16) {
     if (head_dim == 128) ATT_LAUNCH(bf16_t, 128); else ATT_LAUNCH(bf16_t, 64);
@@ -464,11 +466,81 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
 // confidence and a draw.  One 1024-thread workgroup per row.
 // ===========================================================================
 
+// Loops over a row of logits with the loads of several iterations in flight
+// before their first use.  Each thread visits its elements in the same order
+// as the plain loops they replace: v = tid, tid + NT, ... (strided), or the
+// quads v4 = 4 tid, 4 tid + 4 NT, ... with their elements v4 .. v4 + 3.
+template <int NT, typename F>
+__device__ __forceinline__ void for_strided(const float* __restrict__ z, int V, F f) {
+  constexpr int B = 8;
+  const int tid = threadIdx.x;
+  for (int base = 0; base < V; base += NT * B) {
+    float zv[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) zv[u] = z[min(base + u * NT + tid, V - 1)];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int v = base + u * NT + tid;
+      if (v < V) f(v, zv[u]);
+    }
+  }
+}
+
+// f(v4, a[4], b[4]) for each quad of the thread (b: a second row, or a again); elements >= V are
+// clamped copies that f must skip.
+template <int NT, typename F>
+__device__ __forceinline__ void for_quads(const float* __restrict__ za, const float* __restrict__ zb, int V, F f) {
+  constexpr int B = 4;
+  const int tid = threadIdx.x;
+  for (int base = 0; base < V; base += NT * 4 * B) {
+    float a[B][4], b[B][4];
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = min(base + (u * NT + tid) * 4 + e, V - 1);
+        a[u][e] = za[v];
+        b[u][e] = zb[v];
+      }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int v4 = base + (u * NT + tid) * 4;
+      if (v4 < V) f(v4, a[u], b[u]);
+    }
+  }
+}
+
+// Rows up to ROWREG * 1024 elements are read once into registers (one round
+// of loads), in either element order: strided r[k] = z[tid + 1024 k], or
+// quads r[4 i + e] = z[4 tid + 4096 i + e].
+constexpr int ROWREG = 32;
+
+__device__ __forceinline__ void load_row_strided(const float* __restrict__ z, int V, float (&r)[ROWREG]) {
+#pragma unroll
+  for (int k = 0; k < ROWREG; ++k) r[k] = z[min((int)threadIdx.x + 1024 * k, V - 1)];
+}
+
+__device__ __forceinline__ void load_row_quads(const float* __restrict__ z, int V, float (&r)[ROWREG]) {
+#pragma unroll
+  for (int i = 0; i < ROWREG / 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[4 * i + e] = z[min(4 * (int)threadIdx.x + 4096 * i + e, V - 1)];
+}
+
 struct Top2 { float v1; int i1; float v2; };
 
 __device__ __forceinline__ void top2_push(Top2& t, float v, int i) {
   if (v > t.v1 || (v == t.v1 && i < t.i1)) { t.v2 = fmaxf(t.v2, t.v1); t.v1 = v; t.i1 = i; }
   else t.v2 = fmaxf(t.v2, v);
+}
+
+// The same update as selects (no branches); a push with take == false changes nothing.
+__device__ __forceinline__ void top2_push_sel(Top2& t, float v, int i, bool take) {
+  const bool better = take && (v > t.v1 || (v == t.v1 && i < t.i1));
+  const float v2 = better ? fmaxf(t.v2, t.v1) : (take ? fmaxf(t.v2, v) : t.v2);
+  t.v1 = better ? v : t.v1;
+  t.i1 = better ? i : t.i1;
+  t.v2 = v2;
 }
 
 __device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
@@ -491,10 +563,23 @@ __device__ ssd_row_stat block_row_stats(const float* __restrict__ z, int V, floa
   if (tid == 0) sh_bad = 0;
   Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
   int nonfinite = 0;
-  for (int v = tid; v < V; v += 1024) {
-    const float zv = z[v];
-    if (!isfinite(zv)) nonfinite = 1;
-    top2_push(t, zv, v);
+  const bool in_regs = V <= 1024 * ROWREG;          // uniform
+  float rq[ROWREG];
+  if (in_regs) {
+    load_row_quads(z, V, rq);
+#pragma unroll
+    for (int i = 0; i < ROWREG / 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * tid + 4096 * i + e;
+        nonfinite |= (v < V) & !isfinite(rq[4 * i + e]);
+        top2_push_sel(t, rq[4 * i + e], v, v < V);
+      }
+  } else {
+    for_strided<1024>(z, V, [&](int v, float zv) {
+      if (!isfinite(zv)) nonfinite = 1;
+      top2_push(t, zv, v);
+    });
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -518,7 +603,7 @@ __device__ ssd_row_stat block_row_stats(const float* __restrict__ z, int V, floa
   float kbest = -INFINITY;
   int ibest = 0x7fffffff;
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-  for (int v4 = tid * 4; v4 < V; v4 += 4096) {
+  auto quad = [&](int v4, const float* zq) {
     U4 w{0, 0, 0, 0};
     if (T > 0.f) w = philox4x32_10((uint32_t)iter, (uint32_t)rowid, purpose, (uint32_t)(v4 >> 2), k0, k1);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -526,11 +611,34 @@ __device__ ssd_row_stat block_row_stats(const float* __restrict__ z, int V, floa
     for (int e = 0; e < 4; ++e) {
       const int v = v4 + e;
       if (v < V) {
-        const float zv = z[v];
+        const float zv = zq[e];
         se += expf((zv - res.v1) * invT);
         if (T > 0.f) argmax_merge(kbest, ibest, zv / T + word_to_gumbel(ws[e]), v);
       }
     }
+  };
+  if (in_regs) {
+    // sum in quad order; elements past the row add an exact 0
+#pragma unroll
+    for (int i = 0; i < ROWREG / 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = expf((rq[4 * i + e] - res.v1) * invT);
+        se += 4 * tid + 4096 * i + e < V ? x : 0.f;
+      }
+    if (T > 0.f) {
+      for (int i = 0; i < ROWREG / 4; ++i) {
+        const int v4 = 4 * tid + 4096 * i;
+        if (v4 >= V) break;
+        const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)rowid, purpose, (uint32_t)(v4 >> 2), k0, k1);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (v4 + e < V) argmax_merge(kbest, ibest, rq[4 * i + e] / T + word_to_gumbel(ws[e]), v4 + e);
+      }
+    }
+  } else {
+    for_quads<1024>(z, z, V, [&](int v4, const float* zq, const float*) { quad(v4, zq); });
   }
   se = wave_sum(se);
   wave_argmax(kbest, ibest);
@@ -670,10 +778,22 @@ __device__ float block_max_1024(float v) {
 // log-sum-exp of z/T over the row (T > 0)
 __device__ float block_lse(const float* z, int V, float T) {
   float m = -INFINITY;
-  for (int v = threadIdx.x; v < V; v += 1024) m = fmaxf(m, z[v]);
-  m = block_max_1024(m);
   float se = 0.f;
-  for (int v = threadIdx.x; v < V; v += 1024) se += expf((z[v] - m) / T);
+  if (V <= 1024 * ROWREG) {
+    float r[ROWREG];
+    load_row_strided(z, V, r);
+#pragma unroll
+    for (int k = 0; k < ROWREG; ++k)
+      if ((int)threadIdx.x + 1024 * k < V) m = fmaxf(m, r[k]);
+    m = block_max_1024(m);
+#pragma unroll
+    for (int k = 0; k < ROWREG; ++k)
+      if ((int)threadIdx.x + 1024 * k < V) se += expf((r[k] - m) / T);
+  } else {
+    for_strided<1024>(z, V, [&](int, float zv) { m = fmaxf(m, zv); });
+    m = block_max_1024(m);
+    for_strided<1024>(z, V, [&](int, float zv) { se += expf((zv - m) / T); });
+  }
   se = block_sum_1024(se);
   return m / T + logf(se);
 }
@@ -691,7 +811,15 @@ __global__ __launch_bounds__(1024) void accept_rows_kernel(const float* __restri
   if (T == 0.f) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int v = tid; v < V; v += 1024) argmax_merge(bv, bi, p[v], v);
+    if (V <= 1024 * ROWREG) {
+      float r[ROWREG];
+      load_row_strided(p, V, r);
+#pragma unroll
+      for (int k = 0; k < ROWREG; ++k)
+        if (tid + 1024 * k < V) argmax_merge(bv, bi, r[k], tid + 1024 * k);
+    } else {
+      for_strided<1024>(p, V, [&](int v, float pv) { argmax_merge(bv, bi, pv, v); });
+    }
     const int am = block_argmax_1024(bv, bi);
     if (tid == 0) { corr[i] = am; dec[i] = (i < dp) && (am == drafts[i]); }
     return;
@@ -703,12 +831,13 @@ __global__ __launch_bounds__(1024) void accept_rows_kernel(const float* __restri
   int ibest = 0x7fffffff;
   if (i == dp) {
     // bonus: a draw from p_{d'+1}
-    for (int v4 = tid * 4; v4 < V; v4 += 4096) {
+    for_quads<1024>(p, p, V, [&](int v4, const float* pq, const float*) {
       const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)i, PURPOSE_SAMPLE, (uint32_t)(v4 >> 2), k0, k1);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (v4 + e < V) argmax_merge(kbest, ibest, p[v4 + e] / T + word_to_gumbel(ws[e]), v4 + e);
-    }
+        if (v4 + e < V) argmax_merge(kbest, ibest, pq[e] / T + word_to_gumbel(ws[e]), v4 + e);
+    });
     const int b = block_argmax_1024(kbest, ibest);
     if (tid == 0) { corr[i] = b; dec[i] = 0; }
     return;
@@ -717,29 +846,31 @@ __global__ __launch_bounds__(1024) void accept_rows_kernel(const float* __restri
   const float lse_q = block_lse(q, V, T);
   // residual norm(max(0, p - q)) as a race over log(r) + Gumbel
   int any_pos = 0;
-  for (int v4 = tid * 4; v4 < V; v4 += 4096) {
+  for_quads<1024>(p, q, V, [&](int v4, const float* pq, const float* qq) {
     const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)i, PURPOSE_SAMPLE, (uint32_t)(v4 >> 2), k0, k1);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int v = v4 + e;
       if (v < V) {
-        const float r = expf(p[v] / T - lse_p) - expf(q[v] / T - lse_q);
+        const float r = expf(pq[e] / T - lse_p) - expf(qq[e] / T - lse_q);
         if (r > 0.f) { any_pos = 1; argmax_merge(kbest, ibest, logf(r) + word_to_gumbel(ws[e]), v); }
       }
     }
-  }
+  });
   const int anyp = block_sum_1024((float)any_pos) > 0.f;
   int c;
   if (anyp) {
     c = block_argmax_1024(kbest, ibest);
   } else {
     kbest = -INFINITY; ibest = 0x7fffffff;
-    for (int v4 = tid * 4; v4 < V; v4 += 4096) {
+    for_quads<1024>(p, p, V, [&](int v4, const float* pq, const float*) {
       const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)i, PURPOSE_SAMPLE, (uint32_t)(v4 >> 2), k0, k1);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (v4 + e < V) argmax_merge(kbest, ibest, (p[v4 + e] / T - lse_p) + word_to_gumbel(ws[e]), v4 + e);
-    }
+        if (v4 + e < V) argmax_merge(kbest, ibest, (pq[e] / T - lse_p) + word_to_gumbel(ws[e]), v4 + e);
+    });
     c = block_argmax_1024(kbest, ibest);
   }
   if (tid == 0) {

@@ -303,9 +303,10 @@ def test_capacity_is_reported_not_faulted():
 
 
 @pytest.mark.parametrize("shape", [BF16_HD64, BF16_HD128], ids=lambda s: s.name)
-def test_persistent_pass_equals_standalone_kernels(shape):
-    """An AR step gives the same logits, bit for bit, on both decode paths and as
-    the last row of a prefill (standalone kernels, many rows) at that position."""
+def test_decode_paths_agree_with_prefill(shape):
+    """An AR step on the kernels path gives the same logits, bit for bit, as the
+    last row of a prefill (general kernels, many rows) at that position; the
+    persistent pass (its own attention arithmetic) agrees within the bf16 bound."""
     g = gpu_model(shape)
     P = 70
     prompt = synth.prompt_tokens(P, shape.vocab)
@@ -323,8 +324,8 @@ def test_persistent_pass_equals_standalone_kernels(shape):
     lg2 = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
     B.ssd_prefill(seq2.handle, dev(list(prompt) + [t_p]), 0.0, 0, lg2)
     torch.cuda.synchronize()
-    assert torch.equal(logits["persistent"], logits["kernels"])
-    assert torch.equal(logits["persistent"], lg2)
+    assert torch.equal(logits["kernels"], lg2)
+    assert (logits["persistent"] - logits["kernels"]).abs().max().item() < logit_tol(shape)
     seq2.close()
     g.close()
 
