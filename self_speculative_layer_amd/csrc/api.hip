@@ -68,6 +68,8 @@ struct Workspace {
   const float** fz_gain; // FZ_SLOTS slots of gain pointers
   // decode mode (xg / ss above are shared with it)
   unsigned* dec_ctr;     // attention merge counters [16][KVH], zero between launches
+  StatRec* stat_recs;    // row statistics: segment records [rows][segments]
+  unsigned* stat_ctr;    //   and per-row counters, zero between launches
 };
 
 constexpr int FZ_SLOTS = 12;
@@ -147,6 +149,8 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.fz_prog = (int*)take(sizeof(int) * (size_t)FZ_SLOTS * 2 * max_phase);
   t.fz_gain = (const float**)take(sizeof(float*) * (size_t)FZ_SLOTS * max_phase);
   t.dec_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)16 * d.n_kv_heads);
+  t.stat_recs = (StatRec*)take(sizeof(StatRec) * (size_t)R * stat_segments(V));
+  t.stat_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)R);
   if (w) *w = t;
   return off;
 }
@@ -553,6 +557,7 @@ extern "C" int ssd_seq_create(const ssd_model* m, void* kv_pool_dev, int n_pages
   int rc = launch_state_init(q->w.st, stream);
   if (rc == 0 && hipMemset(q->w.dec_ctr, 0, sizeof(unsigned) * 16 * (size_t)m->d.n_kv_heads) != hipSuccess)
     rc = SSD_ERR_HIP;
+  if (rc == 0 && hipMemset(q->w.stat_ctr, 0, sizeof(unsigned) * (size_t)R) != hipSuccess) rc = SSD_ERR_HIP;
   if (rc == 0 && hipStreamSynchronize(stream) != hipSuccess) rc = SSD_ERR_HIP;
   if (rc != 0) {
     delete q;
@@ -591,8 +596,8 @@ extern "C" int ssd_prefill(ssd_seq* q, const int32_t* tokens_dev, int n, float t
   }
   float* lg = last_logits_dev ? last_logits_dev : w.logits1;
   TRY(final_logits(q, w.h + (size_t)(last_rows - 1) * d.d_model, 1, nullptr, lg, nullptr, s));
-  TRY(launch_row_stats(lg, d.vocab, 1, d.vocab, temperature, seed, nullptr, 0, 0, PURPOSE_SAMPLE, w.stats, nullptr,
-                       s));
+  TRY(launch_row_stats_seg(lg, d.vocab, 1, d.vocab, temperature, seed, nullptr, 0, 0, PURPOSE_SAMPLE, w.stats,
+                           w.stat_recs, w.stat_ctr, nullptr, DraftStep{}, s));
   TRY(launch_pick_commit(w.stats, w.st, w.log, q->log_cap, 1, n, s));
   return SSD_OK;
 }
@@ -620,8 +625,8 @@ extern "C" int ssd_decode_ar(ssd_seq* q, float temperature, uint64_t seed, float
     TRY(run_layers(q, b, 0, d.n_layers, nullptr, s));
     TRY(final_logits(q, w.h1, 1, nullptr, lg, nullptr, s));
   }
-  TRY(launch_row_stats(lg, d.vocab, 1, d.vocab, temperature, seed, &w.st->iteration, 0, 0, PURPOSE_SAMPLE, w.stats,
-                       nullptr, s));
+  TRY(launch_row_stats_seg(lg, d.vocab, 1, d.vocab, temperature, seed, &w.st->iteration, 0, 0, PURPOSE_SAMPLE,
+                           w.stats, w.stat_recs, w.stat_ctr, nullptr, DraftStep{}, s));
   TRY(launch_pick_commit(w.stats, w.st, w.log, q->log_cap, 0, 0, s));
   return SSD_OK;
 }
@@ -652,8 +657,9 @@ extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_lay
       TRY(launch_draft_step_prep(w.st, draft_tokens_dev, j, w.pos1, w.tok1, q->max_ctx, n_drafted_dev, s));
       float* lg = draft_logits_dev + (size_t)(j - 1) * d.vocab;
       TRY(fz_run(q, pr, 1, nullptr, w.pos1, w.tok1, nullptr, w.h1, lg, w.hb + (size_t)(j - 1) * d.d_model, stop, s));
-      TRY(launch_draft_stats(lg, d.vocab, temperature, seed, w.st, j, d_max, conf_thresh, draft_tokens_dev,
-                             n_drafted_dev, s));
+      TRY(launch_row_stats_seg(lg, d.vocab, 1, d.vocab, temperature, seed, nullptr, 0, 0, PURPOSE_DRAFT, nullptr,
+                               w.stat_recs, w.stat_ctr, nullptr,
+                               DraftStep{w.st, j, d_max, conf_thresh, draft_tokens_dev, n_drafted_dev}, s));
     }
     return SSD_OK;
   }
@@ -671,8 +677,9 @@ extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_lay
       TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, ent, save, ent.size(), true, stop, s));
       float* lg = draft_logits_dev + (size_t)(j - 1) * d.vocab;
       TRY(dec_logits(q, 1, nullptr, lg, stop, s));
-      TRY(launch_draft_stats(lg, d.vocab, temperature, seed, w.st, j, d_max, conf_thresh, draft_tokens_dev,
-                             n_drafted_dev, s));
+      TRY(launch_row_stats_seg(lg, d.vocab, 1, d.vocab, temperature, seed, nullptr, 0, 0, PURPOSE_DRAFT, nullptr,
+                               w.stat_recs, w.stat_ctr, nullptr,
+                               DraftStep{w.st, j, d_max, conf_thresh, draft_tokens_dev, n_drafted_dev}, s));
     }
     return SSD_OK;
   }
@@ -685,8 +692,9 @@ extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_lay
     TRY(run_layers(q, blk, b, d.n_layers, mask.data(), s));
     float* lg = draft_logits_dev + (size_t)(j - 1) * d.vocab;
     TRY(final_logits(q, w.h1, 1, nullptr, lg, stop, s));
-    TRY(launch_draft_stats(lg, d.vocab, temperature, seed, w.st, j, d_max, conf_thresh, draft_tokens_dev,
-                           n_drafted_dev, s));
+    TRY(launch_row_stats_seg(lg, d.vocab, 1, d.vocab, temperature, seed, nullptr, 0, 0, PURPOSE_DRAFT, nullptr,
+                             w.stat_recs, w.stat_ctr, nullptr,
+                             DraftStep{w.st, j, d_max, conf_thresh, draft_tokens_dev, n_drafted_dev}, s));
   }
   return SSD_OK;
 }
@@ -822,8 +830,8 @@ extern "C" int ssd_score_masks(ssd_seq* q, const uint8_t* masks_host, int n_mask
     }
   }
   TRY(final_logits(q, w.h, R, nullptr, w.logits_rows, nullptr, s));
-  TRY(launch_row_stats(w.logits_rows, d.vocab, R, d.vocab, 0.f, 0, nullptr, 0, 0, PURPOSE_DRAFT, w.stats, nullptr,
-                       s));
+  TRY(launch_row_stats_seg(w.logits_rows, d.vocab, R, d.vocab, 0.f, 0, nullptr, 0, 0, PURPOSE_DRAFT, w.stats,
+                           w.stat_recs, w.stat_ctr, nullptr, DraftStep{}, s));
   TRY(launch_score(w.stats, window_dev, n_masks, gamma, scores_dev, best_dev, s));
   // the host row lists must outlive the copy
   e = hipStreamSynchronize(s);

@@ -68,9 +68,25 @@ int launch_row_stats(const float* z, int ldz, int rows, int V, float T, uint64_t
                      const int* iter_ptr, int iter_const, int rowid_base, uint32_t purpose,
                      ssd_row_stat* out, const int* stop, hipStream_t s);
 
-// Draft step j: stats of one row + draft token + early stop.
-int launch_draft_stats(const float* z, int V, float T, uint64_t seed, DevState* st, int j, int d,
-                       float tau, int32_t* draft_tokens, int32_t* n_drafted_out, hipStream_t s);
+// Row statistics over segments of STAT_SEG logits with a merge by the last
+// segment (recs: rows x stat_segments(V) records; ctr: rows counters, zero
+// between launches).  With ds.st set, row 0 is draft step ds.j: the merge
+// writes the draft token and applies the confidence stop instead of out.
+constexpr int STAT_SEG = 2048;
+constexpr int STAT_MAXSEG = 64;
+struct StatRec { float v1; int i1; float v2; float s; float kv; int ki; int bad; int pad; };
+struct DraftStep {
+  DevState* st;            // nullptr: plain row statistics
+  int j, d;
+  float tau;
+  int32_t* draft_tokens;
+  int32_t* n_drafted_out;
+};
+int stat_segments(int V);
+int launch_row_stats_seg(const float* z, int ldz, int rows, int V, float T, uint64_t seed, const int* iter_ptr,
+                         int iter_const, int rowid_base, uint32_t purpose, ssd_row_stat* out, StatRec* recs,
+                         unsigned* ctr, const int* stop, const DraftStep& ds, hipStream_t s);
+
 
 int launch_accept(const float* zp, const float* zq, int V, const int32_t* drafts, const int32_t* n_drafted,
                   int d, float T, uint64_t seed, const DevState* st, int* dec, int* corr,

@@ -690,31 +690,160 @@ int launch_row_stats(const float* z, int ldz, int rows, int V, float T, uint64_t
   return last_launch();
 }
 
-// Draft step j: the draft token y_j, and the confidence stop.
-__global__ __launch_bounds__(1024) void draft_stats_kernel(const float* __restrict__ z, int V, float T,
-                                                           uint64_t seed, DevState* st, int j, int d, float tau,
-                                                           int32_t* __restrict__ draft_tokens,
-                                                           int32_t* __restrict__ n_drafted_out) {
-  if (st->stop) return;
-  bool bad;
-  ssd_row_stat r = block_row_stats(z, V, T, seed, st->iteration, j - 1, PURPOSE_DRAFT, &bad);
-  if (threadIdx.x == 0) {
-    draft_tokens[j - 1] = r.sample;
-    if (bad) atomicOr(&st->error_flags, ERRF_NUMERIC);
-    if (r.conf < tau || j == d) {
-      st->stop = 1;
-      st->n_drafted = j;
-      *n_drafted_out = j;
+// ===========================================================================
+// Row statistics spread over segments of STAT_SEG logits, one 256-thread
+// workgroup each with all of its loads in one round (a single workgroup
+// reading a whole row is bound by one CU's outstanding misses).  Each
+// segment stores a record; the segment that completes the row's count
+// merges the records in segment order and resets the count.
+// ===========================================================================
+
+__global__ __launch_bounds__(256) void row_stats_seg_kernel(const float* __restrict__ z, int ldz, int V, float T,
+                                                            uint64_t seed, const int* iter_ptr, int iter_const,
+                                                            int rowid_base, uint32_t purpose,
+                                                            ssd_row_stat* __restrict__ out, StatRec* __restrict__ recs,
+                                                            unsigned* __restrict__ ctr, const int* __restrict__ stop,
+                                                            DraftStep ds) {
+  if (stop && *stop) return;
+  if (ds.st && ds.st->stop) return;
+  const int seg = blockIdx.x, row = blockIdx.y, nseg = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* zr = z + (size_t)row * ldz;
+  const int iter = ds.st ? ds.st->iteration : (iter_ptr ? *iter_ptr : iter_const);
+  const int rowid = ds.st ? ds.j - 1 : rowid_base + row;
+  const float invT = T > 0.f ? 1.0f / T : 1.0f;
+  __shared__ Top2 sh_t[4];
+  __shared__ float sh_s[4], sh_k[4];
+  __shared__ int sh_i[4], sh_bad[4], sh_last;
+  __shared__ StatRec sh_rec[STAT_MAXSEG];
+  // elements 4 q + e of the quads q = seg * STAT_SEG / 4 + tid + 256 h
+  float x[8];
+  int vv[8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vv[4 * h + e] = 4 * (seg * (STAT_SEG / 4) + tid + 256 * h) + e;
+      x[4 * h + e] = zr[min(vv[4 * h + e], V - 1)];
     }
+  Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+  int bad = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    bad |= (vv[k] < V) & !isfinite(x[k]);
+    top2_push_sel(t, x[k], vv[k], vv[k] < V);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Top2 u{__shfl_xor(t.v1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.v2, o, 64)};
+    t = top2_merge(t, u);
+  }
+  bad = __any(bad) ? 1 : 0;
+  if (lane == 0) { sh_t[wave] = t; sh_bad[wave] = bad; }
+  __syncthreads();
+  t = sh_t[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) t = top2_merge(t, sh_t[w]);
+  // sum of exp((z - m) / T) over the segment (m its maximum), in a fixed order
+  float se = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float ex = expf((x[k] - t.v1) * invT);
+    se += vv[k] < V ? ex : 0.f;
+  }
+  se = wave_sum(se);
+  float kbest = -INFINITY;
+  int ibest = 0x7fffffff;
+  if (T > 0.f) {
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v4 = vv[4 * h];
+      if (v4 < V) {
+        const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)rowid, purpose, (uint32_t)(v4 >> 2), k0, k1);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (v4 + e < V) argmax_merge(kbest, ibest, x[4 * h + e] / T + word_to_gumbel(ws[e]), v4 + e);
+      }
+    }
+    wave_argmax(kbest, ibest);
+  }
+  if (lane == 0) { sh_s[wave] = se; sh_k[wave] = kbest; sh_i[wave] = ibest; }
+  __syncthreads();
+  if (tid == 0) {
+    float ss = sh_s[0];
+    float kb = sh_k[0];
+    int ib = sh_i[0];
+    int bb = sh_bad[0];
+    for (int w = 1; w < 4; ++w) {
+      ss += sh_s[w];
+      argmax_merge(kb, ib, sh_k[w], sh_i[w]);
+      bb |= sh_bad[w];
+    }
+    StatRec* rc = recs + (size_t)row * nseg + seg;
+    __hip_atomic_store(&rc->v1, t.v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&rc->i1, t.i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&rc->v2, t.v2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&rc->s, ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&rc->kv, kb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&rc->ki, ib, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&rc->bad, bb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the record is stored before the count
+    const unsigned old = __hip_atomic_fetch_add(ctr + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = old + 1 == (unsigned)nseg;
+    if (sh_last) __hip_atomic_store(ctr + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!sh_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (tid < nseg) sh_rec[tid] = recs[(size_t)row * nseg + tid];
+  __syncthreads();
+  if (tid != 0) return;
+  Top2 r{sh_rec[0].v1, sh_rec[0].i1, sh_rec[0].v2};
+  for (int k = 1; k < nseg; ++k) r = top2_merge(r, Top2{sh_rec[k].v1, sh_rec[k].i1, sh_rec[k].v2});
+  float S = 0.f;
+  float kb = -INFINITY;
+  int ib = 0x7fffffff;
+  int bb = 0;
+  for (int k = 0; k < nseg; ++k) {
+    S = fmaf(sh_rec[k].s, expf((sh_rec[k].v1 - r.v1) * invT), S);
+    argmax_merge(kb, ib, sh_rec[k].kv, sh_rec[k].ki);
+    bb |= sh_rec[k].bad;
+  }
+  ssd_row_stat o;
+  o.max = r.v1;
+  o.argmax = r.i1;
+  o.max2 = r.v2;
+  o.lse = r.v1 * invT + logf(S);
+  o.conf = 1.0f / S;
+  o.sample = T > 0.f ? ib : r.i1;
+  if (ds.st) {
+    ds.draft_tokens[ds.j - 1] = o.sample;
+    if (bb) atomicOr(&ds.st->error_flags, ERRF_NUMERIC);
+    if (o.conf < ds.tau || ds.j == ds.d) {
+      ds.st->stop = 1;
+      ds.st->n_drafted = ds.j;
+      *ds.n_drafted_out = ds.j;
+    }
+  } else {
+    out[row] = o;
   }
 }
 
-int launch_draft_stats(const float* z, int V, float T, uint64_t seed, DevState* st, int j, int d, float tau,
-                       int32_t* draft_tokens, int32_t* n_drafted_out, hipStream_t s) {
-  hipLaunchKernelGGL(draft_stats_kernel, dim3(1), dim3(1024), 0, s, z, V, T, seed, st, j, d, tau, draft_tokens,
-                     n_drafted_out);
+int stat_segments(int V) { return (V + STAT_SEG - 1) / STAT_SEG; }
+
+int launch_row_stats_seg(const float* z, int ldz, int rows, int V, float T, uint64_t seed, const int* iter_ptr,
+                         int iter_const, int rowid_base, uint32_t purpose, ssd_row_stat* out, StatRec* recs,
+                         unsigned* ctr, const int* stop, const DraftStep& ds, hipStream_t s) {
+  if (rows <= 0) return 0;
+  const int nseg = stat_segments(V);
+  if (nseg > STAT_MAXSEG) return SSD_ERR_SHAPE;
+  hipLaunchKernelGGL(row_stats_seg_kernel, dim3(nseg, rows), dim3(256), 0, s, z, ldz, V, T, seed, iter_ptr,
+                     iter_const, rowid_base, purpose, out, recs, ctr, stop, ds);
   return last_launch();
 }
+
 
 // ===========================================================================
 // Accept / reject.  One workgroup per verify row i = 0..d' computes its
