@@ -1,11 +1,12 @@
 /*
  * ssd_profile.h — kernel-timing hooks of libssd.so, for measurement.
  *
- * While a kernel class is enabled, the library records a HIP event on the
- * launch stream immediately before and after each launch of that class (up to
- * max_launches launches), and accumulates the algorithmic bytes each launch
- * must move (weights + activations read + results written, each once).
- * ssd_profile_read waits for the recorded events and returns the summed
+ * While a kernel class is enabled, each launch of that class (up to
+ * max_launches launches) goes out with a pair of HIP events that take the
+ * dispatch's own begin and end timestamps (hipExtLaunchKernel: no marker is
+ * queued around the kernel), and the library accumulates the algorithmic
+ * bytes each launch must move (weights + activations read + results written,
+ * each once).  ssd_profile_read waits for the events and returns the summed
  * durations.  Process-wide; not thread-safe; events are created by
  * ssd_profile_enable (host-side objects, no device memory).
  */

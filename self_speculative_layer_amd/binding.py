@@ -246,6 +246,7 @@ def ssd_profile_read():
     return ms.value, n.value, by.value
 
 
+
 # ---------------------------------------------------------------------------
 # convenience owners of device memory
 

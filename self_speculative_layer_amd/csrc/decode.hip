@@ -15,6 +15,7 @@
 // kernels (kernels.hip), step for step: same K slices per wave, same
 // reduction order, same rounding of the epilogues, same canonical RMS sums.
 // A row's result never depends on the other rows of its block.
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "kernels.h"
@@ -256,9 +257,8 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   }
 }
 
-bool profile_wants(int cls);
-void profile_before(hipStream_t s);
-void profile_after(hipStream_t s, double bytes);
+bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop);
+void profile_done(double bytes);
 
 // Tile shapes of the two-set projections (HALF: 8 + 8 rows per tile, twice the tiles).
 constexpr bool DEC_HALF_QKV = true;
@@ -277,13 +277,15 @@ static int dec_tpw(int epi, int M) {
   return epi == DEC_STORE && M > 1 ? 2 : 1;
 }
 
+// e0, e1: events taking the dispatch's begin and end timestamps (profiling), or null.
 template <int EPI, bool HALF>
-static void dec_launch(const DecGemm& a, int tpw, hipStream_t s) {
+static void dec_launch(const DecGemm& a, int tpw, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
   const dim3 block(DEC_NW * 64);
   if (tpw == 2)
-    hipLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 2>), dim3((a.n_tiles + 1) / 2), block, 0, s, a);
+    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 2>), dim3((a.n_tiles + 1) / 2), block, 0, s, e0, e1, 0,
+                          a);
   else
-    hipLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 1>), dim3(a.n_tiles), block, 0, s, a);
+    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 1>), dim3(a.n_tiles), block, 0, s, e0, e1, 0, a);
 }
 
 int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
@@ -298,13 +300,13 @@ int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
   const int tpw = dec_tpw(epi, a.M);
   // profile classes: 0 plain-store projections (QKV, LM head), 1 residual, 2 gate/up
   const int cls = epi == DEC_RESID ? 1 : (epi == DEC_SWIGLU ? 2 : 0);
-  const bool prof = profile_wants(cls);
-  if (prof) profile_before(s);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  const bool prof = profile_next(cls, &e0, &e1);
   switch (epi) {
-    case DEC_STORE: dec_launch<DEC_STORE, false>(b, tpw, s); break;
-    case DEC_RESID: dec_launch<DEC_RESID, false>(b, tpw, s); break;
-    case DEC_SWIGLU: dec_launch<DEC_SWIGLU, DEC_HALF_SWIGLU>(b, tpw, s); break;
-    default: dec_launch<DEC_QKV, DEC_HALF_QKV>(b, tpw, s);
+    case DEC_STORE: dec_launch<DEC_STORE, false>(b, tpw, e0, e1, s); break;
+    case DEC_RESID: dec_launch<DEC_RESID, false>(b, tpw, e0, e1, s); break;
+    case DEC_SWIGLU: dec_launch<DEC_SWIGLU, DEC_HALF_SWIGLU>(b, tpw, e0, e1, s); break;
+    default: dec_launch<DEC_QKV, DEC_HALF_QKV>(b, tpw, e0, e1, s);
   }
   if (prof) {
     // algorithmic bytes: weights once, activations in once, results out once (residual: read + write)
@@ -312,7 +314,7 @@ int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
     const double wrows = epi == DEC_SWIGLU ? 2.0 * N : N;
     double by = wrows * K * 2.0 + M * K * 2.0;
     by += epi == DEC_STORE ? 4.0 * M * N : (epi == DEC_RESID ? 8.0 * M * N : 2.0 * M * N);
-    profile_after(s, by);
+    profile_done(by);
   }
   return dec_ok(hipGetLastError());
 }

@@ -1,5 +1,6 @@
 // HIP kernels of the self-speculative decoding path, written for gfx950
 // (CDNA4: 64-lane wavefronts, bf16 MFMA 16x16x32, 160 KB LDS per CU).
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "kernels.h"
@@ -171,12 +172,12 @@ __global__ __launch_bounds__(256) void gemm_f32_rows16(
   }
 }
 
-bool profile_wants(int cls);
-void profile_before(hipStream_t s);
-void profile_after(hipStream_t s, double bytes);
+bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop);
+void profile_done(double bytes);
 static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
                               float* Y, int ldy, void* A, int lda, int n_rb, dim3 grid, const float* rscale,
-                              const int* nrows, const int* ymap, const int* stop, hipStream_t s);
+                              const int* nrows, const int* ymap, const int* stop, hipEvent_t e0, hipEvent_t e1,
+                              hipStream_t s);
 
 int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
                   float* Y, int ldy, void* A, int lda, const float* rscale, const int* nrows, const int* ymap,
@@ -185,39 +186,40 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
   const int n_rb = (M + 15) / 16;
   const int n_tiles = (N + 15) / 16;
   const dim3 grid(n_rb * n_tiles);
-  const bool prof = profile_wants(epi);
-  if (prof) profile_before(s);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  const bool prof = profile_next(epi, &e0, &e1);
   const int rc = launch_linear_impl(dtype, epi, W, X, ldx, M, N, K, Y, ldy, A, lda, n_rb, grid, rscale, nrows, ymap,
-                                    stop, s);
+                                    stop, e0, e1, s);
   if (prof) {
     // algorithmic bytes: weights once, activations in once, results out once (residual: read + write)
     const double elt = dtype == SSD_DTYPE_BF16 ? 2.0 : 4.0;
     const double wrows = epi == EPI_SWIGLU ? 2.0 * N : (double)N;
     double by = wrows * K * elt + (double)M * K * elt;
     by += epi == EPI_STORE ? 4.0 * M * N : (epi == EPI_RESID ? 8.0 * M * N : elt * M * N);
-    profile_after(s, by);
+    profile_done(by);
   }
   return rc;
 }
 
 static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
                               float* Y, int ldy, void* A, int lda, int n_rb, dim3 grid, const float* rscale,
-                              const int* nrows, const int* ymap, const int* stop, hipStream_t s) {
+                              const int* nrows, const int* ymap, const int* stop, hipEvent_t e0, hipEvent_t e1,
+                              hipStream_t s) {
   if (dtype == SSD_DTYPE_BF16) {
     if (K % 64 != 0) return SSD_ERR_SHAPE;
     const bf16_t* w = (const bf16_t*)W;
     const bf16_t* x = (const bf16_t*)X;
     switch (epi) {
       case EPI_STORE:
-        hipLaunchKernelGGL(gemm_bf16_rows16<EPI_STORE>, grid, dim3(GEMM_NW * 64), 0, s, w, x, ldx, M, N, K, Y,
+        hipExtLaunchKernelGGL(gemm_bf16_rows16<EPI_STORE>, grid, dim3(GEMM_NW * 64), 0, s, e0, e1, 0, w, x, ldx, M, N, K, Y,
                            ldy, (bf16_t*)A, lda, n_rb, rscale, nrows, ymap, stop);
         break;
       case EPI_RESID:
-        hipLaunchKernelGGL(gemm_bf16_rows16<EPI_RESID>, grid, dim3(GEMM_NW * 64), 0, s, w, x, ldx, M, N, K, Y,
+        hipExtLaunchKernelGGL(gemm_bf16_rows16<EPI_RESID>, grid, dim3(GEMM_NW * 64), 0, s, e0, e1, 0, w, x, ldx, M, N, K, Y,
                            ldy, (bf16_t*)A, lda, n_rb, rscale, nrows, ymap, stop);
         break;
       default:
-        hipLaunchKernelGGL(gemm_bf16_rows16<EPI_SWIGLU>, grid, dim3(GEMM_NW * 64), 0, s, w, x, ldx, M, N, K, Y,
+        hipExtLaunchKernelGGL(gemm_bf16_rows16<EPI_SWIGLU>, grid, dim3(GEMM_NW * 64), 0, s, e0, e1, 0, w, x, ldx, M, N, K, Y,
                            ldy, (bf16_t*)A, lda, n_rb, rscale, nrows, ymap, stop);
     }
   } else {
@@ -225,15 +227,15 @@ static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, 
     const float* x = (const float*)X;
     switch (epi) {
       case EPI_STORE:
-        hipLaunchKernelGGL(gemm_f32_rows16<EPI_STORE>, grid, dim3(256), 0, s, w, x, ldx, M, N, K, Y, ldy,
+        hipExtLaunchKernelGGL(gemm_f32_rows16<EPI_STORE>, grid, dim3(256), 0, s, e0, e1, 0, w, x, ldx, M, N, K, Y, ldy,
                            (float*)A, lda, n_rb, rscale, nrows, ymap, stop);
         break;
       case EPI_RESID:
-        hipLaunchKernelGGL(gemm_f32_rows16<EPI_RESID>, grid, dim3(256), 0, s, w, x, ldx, M, N, K, Y, ldy,
+        hipExtLaunchKernelGGL(gemm_f32_rows16<EPI_RESID>, grid, dim3(256), 0, s, e0, e1, 0, w, x, ldx, M, N, K, Y, ldy,
                            (float*)A, lda, n_rb, rscale, nrows, ymap, stop);
         break;
       default:
-        hipLaunchKernelGGL(gemm_f32_rows16<EPI_SWIGLU>, grid, dim3(256), 0, s, w, x, ldx, M, N, K, Y, ldy,
+        hipExtLaunchKernelGGL(gemm_f32_rows16<EPI_SWIGLU>, grid, dim3(256), 0, s, e0, e1, 0, w, x, ldx, M, N, K, Y, ldy,
                            (float*)A, lda, n_rb, rscale, nrows, ymap, stop);
     }
   }

@@ -1,4 +1,7 @@
-// Kernel-timing hooks (include/ssd_profile.h).
+// Kernel-timing hooks (include/ssd_profile.h).  A profiled launch goes out
+// through hipExtLaunchKernel with a start and a stop event: the events take
+// the dispatch's own begin and end timestamps, so no marker is queued around
+// the kernel and the stream's timing is unchanged.
 #include <vector>
 
 #include "kernels.h"
@@ -18,12 +21,14 @@ struct ProfState {
 ProfState g_prof;
 }  // namespace
 
-bool profile_wants(int cls) { return g_prof.on && g_prof.cls == cls && g_prof.used < g_prof.max; }
+bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop) {
+  if (!(g_prof.on && g_prof.cls == cls && g_prof.used < g_prof.max)) return false;
+  *start = g_prof.ev[2 * g_prof.used];
+  *stop = g_prof.ev[2 * g_prof.used + 1];
+  return true;
+}
 
-void profile_before(hipStream_t s) { (void)hipEventRecord(g_prof.ev[2 * g_prof.used], s); }
-
-void profile_after(hipStream_t s, double bytes) {
-  (void)hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
+void profile_done(double bytes) {
   g_prof.bytes[g_prof.used] = bytes;
   ++g_prof.used;
 }
