@@ -138,8 +138,6 @@ def main():
     ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ar-steps", type=int, default=16)
-    ap.add_argument("--path", default="kernels", choices=["kernels", "persistent"],
-                    help="decode path of the steps of at most 16 rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -178,8 +176,7 @@ def main():
     d = wl["d"]
     K, W = args.steps, args.warmup
     max_ctx = wl["prompt"] + (2 * K + W + 2) * (d + 1) + 64
-    path = B.SSD_PATH_PERSISTENT if args.path == "persistent" else B.SSD_PATH_KERNELS
-    seq = B.Sequence(model, max_ctx=max_ctx, max_rows=512, max_draft=max(d, 1), device=dev, path=path)
+    seq = B.Sequence(model, max_ctx=max_ctx, max_rows=512, max_draft=max(d, 1), device=dev)
     prompt = torch.from_numpy(synth.prompt_tokens(wl["prompt"], shape.vocab)).to(dev)
     seed = synth.SEED_SAMPLING
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -245,8 +242,7 @@ def main():
     # same-kernel AR decode baseline
     ar_tps = None
     if args.ar_steps > 0:
-        seq2 = B.Sequence(model, max_ctx=wl["prompt"] + args.ar_steps + 64, max_rows=512, max_draft=1, device=dev,
-                          path=path)
+        seq2 = B.Sequence(model, max_ctx=wl["prompt"] + args.ar_steps + 64, max_rows=512, max_draft=1, device=dev)
         B.ssd_prefill(seq2.handle, prompt, wl["T"], seed)
         for _ in range(2):
             B.ssd_decode_ar(seq2.handle, wl["T"], seed)
@@ -259,7 +255,7 @@ def main():
         ar_tps = args.ar_steps / (ev0.elapsed_time(ev1) / 1e3)
         seq2.close()
 
-    traffic = pmc_traffic_bytes(DOMINANT) if args.path == "kernels" else None
+    traffic = pmc_traffic_bytes(DOMINANT)
     if traffic is not None:
         traffic = round(traffic)
     result = {

@@ -152,21 +152,6 @@ int ssd_seq_create(const ssd_model* model, void* kv_pool_dev, int n_pages, int p
                    ssd_seq** out_seq);
 int ssd_seq_destroy(ssd_seq* seq);
 
-/* Decode-path selection for the steps of at most 16 rows (draft steps, verify,
- * plain AR steps).  Both paths compute the same arithmetic in the same order
- * and give bitwise-equal results:
- *   SSD_PATH_KERNELS     one launch per operation (default);
- *   SSD_PATH_PERSISTENT  one cooperative launch per forward pass, one
- *                        workgroup per compute unit, grid-wide phase counters
- *                        with bounded waits (a wait that gives up sets a flag
- *                        that ssd_read_state reports as SSD_ERR_HIP).
- * Returns SSD_ERR_UNSUPPORTED for SSD_PATH_PERSISTENT on an fp32 model or a
- * device without cooperative launch; SSD_ERR_ARG for an unknown value.
- * Prefill, mask scoring and blocks of more than 16 rows always use the
- * kernels path. */
-typedef enum ssd_decode_path { SSD_PATH_KERNELS = 0, SSD_PATH_PERSISTENT = 1 } ssd_decode_path;
-int ssd_seq_set_decode_path(ssd_seq* seq, int path);
-
 /* Prefill (row a7): the n prompt tokens tokens_dev[0..n-1] at positions 0..n-1
  * through the full model (in chunks of max_rows rows); then the first
  * generated token is picked from the last row's logits (argmax at temperature

@@ -14,7 +14,7 @@ ERROR_NAMES = {-1: "SSD_ERR_ARG", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_CAPACITY", -
 
 # Every symbol include/ssd.h declares.
 EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_kv_pool_bytes", "ssd_workspace_bytes", "ssd_seq_create",
-           "ssd_seq_destroy", "ssd_seq_set_decode_path", "ssd_prefill", "ssd_decode_ar", "ssd_draft", "ssd_verify", "ssd_accept", "ssd_commit",
+           "ssd_seq_destroy", "ssd_prefill", "ssd_decode_ar", "ssd_draft", "ssd_verify", "ssd_accept", "ssd_commit",
            "ssd_score_masks", "ssd_row_stats", "ssd_read_state", "ssd_read_output", "ssd_last_error",
            "ssd_profile_enable", "ssd_profile_disable", "ssd_profile_read"]
 
@@ -71,7 +71,6 @@ def lib():
             "ssd_workspace_bytes": [P, I, I, I, SZ],
             "ssd_seq_create": [P, P, I, I, P, I, P, ctypes.c_size_t, I, I, P, ctypes.POINTER(P)],
             "ssd_seq_destroy": [P],
-            "ssd_seq_set_decode_path": [P, I],
             "ssd_prefill": [P, P, I, F, U64, P, P],
             "ssd_decode_ar": [P, F, U64, P, P],
             "ssd_draft": [P, P, I, I, F, F, U64, P, P, P, P],
@@ -159,12 +158,6 @@ def ssd_seq_destroy(seq):
     check(lib().ssd_seq_destroy(seq))
 
 
-SSD_PATH_KERNELS = 0
-SSD_PATH_PERSISTENT = 1
-
-
-def ssd_seq_set_decode_path(seq, path):
-    check(lib().ssd_seq_set_decode_path(seq, path))
 
 
 def ssd_prefill(seq, tokens, temperature=0.0, seed=0, last_logits=None, stream=None):
@@ -283,7 +276,7 @@ class Sequence:
     """A sequence with its own KV pool and workspace (torch device tensors)."""
 
     def __init__(self, model, max_ctx, max_rows=64, max_draft=16, page_size=64, page_table=None, device="cuda",
-                 stream=None, path=SSD_PATH_KERNELS):
+                 stream=None):
         import numpy as np
         import torch
         self.model = model
@@ -300,7 +293,6 @@ class Sequence:
         self.stream = stream
         self.handle = ssd_seq_create(model.handle, self.kv, n_pages, page_size, page_table, self.ws, max_rows,
                                      max_draft, stream)
-        ssd_seq_set_decode_path(self.handle, path)
         V = model.vocab
         self.draft_tokens = torch.zeros(max_draft, dtype=torch.int32, device=device)
         self.draft_logits = torch.zeros(max_draft * V, dtype=torch.float32, device=device)

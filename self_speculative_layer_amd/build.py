@@ -5,24 +5,24 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssd.so")
-SOURCES = ["kernels.hip", "decode.hip", "api.hip", "profile.hip", "fused.hip"]
+SOURCES = ["kernels.hip", "decode.hip", "api.hip", "profile.hip"]
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-# Kernels that must not use scratch (private) memory: the persistent decode
-# pass runs as one cooperative grid and keeps every value in registers/LDS.
-NO_SCRATCH = {"fused.hip": "fused_pass_kernel"}
+# Kernels that must not use scratch (private) memory: the decode-block
+# projections and attention keep every value in registers / LDS.
+NO_SCRATCH = {"decode.hip": ("dec_gemm_kernel", "attn_dec_kernel")}
 
 
 def _check_no_scratch(src, remarks):
     """Fail the build when a listed kernel spills to scratch."""
-    kernel = NO_SCRATCH[src]
+    kernels = NO_SCRATCH[src]
     current = None
     for line in remarks.splitlines():
         if "Function Name:" in line:
             current = line.split("Function Name:")[1].split()[0]
-        elif current and kernel in current and "ScratchSize [bytes/lane]:" in line:
+        elif current and any(k in current for k in kernels) and "ScratchSize [bytes/lane]:" in line:
             size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
             if size != 0:
                 raise RuntimeError("%s uses %d bytes/lane of scratch (register spills)" % (current, size))

@@ -59,29 +59,12 @@ struct Workspace {
   ssd_row_stat* stats;
   int *dec, *corr, *rowmaps;
   int32_t* log;
-  // persistent decode pass
-  FzLayer* fz_layers;
-  bf16_t *fz_xg, *fz_ob;
-  float* fz_ss;
-  unsigned* fz_counters;
-  int* fz_prog;          // FZ_SLOTS slots of [types | layers] ints
-  const float** fz_gain; // FZ_SLOTS slots of gain pointers
-  // decode mode (xg / ss above are shared with it)
+  // decode blocks (<= 16 rows)
+  bf16_t* xg;            // next RMSNorm consumer's input bf16(h * g), decode block layout [16][max(D, q_dim)]
+  float* ss;             // its 16-feature tile sums of h^2 [16][D / 16]
   unsigned* dec_ctr;     // attention merge counters [16][KVH], zero between launches
   StatRec* stat_recs;    // row statistics: segment records [rows][segments]
   unsigned* stat_ctr;    //   and per-row counters, zero between launches
-};
-
-constexpr int FZ_SLOTS = 12;
-
-// A pass program: phase list of the persistent kernel.
-struct FzProgram {
-  std::vector<int> type, layer;
-  std::vector<const float*> gain;
-  int save_phase = -1;
-  bool operator==(const FzProgram& o) const {
-    return type == o.type && layer == o.layer && gain == o.gain && save_phase == o.save_phase;
-  }
 };
 
 struct ssd_seq {
@@ -89,12 +72,6 @@ struct ssd_seq {
   KvView kv;
   int max_rows, max_draft, max_ctx, log_cap;
   Workspace w;
-  int fz_nwg = 0;            // workgroups of the persistent pass (0: not available)
-  int path = SSD_PATH_KERNELS;
-  int fz_max_phase = 0;
-  FzProgram fz_cache[FZ_SLOTS];
-  int fz_next = 0;
-  uint64_t fz_epoch = 0;     // passes launched (selects the counter set)
 };
 
 namespace {
@@ -140,14 +117,8 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.corr = (int*)take(sizeof(int) * (max_draft + 1));
   t.rowmaps = (int*)take(sizeof(int) * (size_t)2 * L * R);
   t.log = (int32_t*)take(sizeof(int32_t) * (size_t)max_ctx);
-  const int max_phase = 2 + 5 * L;
-  t.fz_layers = (FzLayer*)take(sizeof(FzLayer) * L);
-  t.fz_xg = (bf16_t*)take(2 * (size_t)16 * std::max(D, m->q_dim));
-  t.fz_ob = (bf16_t*)take(2 * (size_t)16 * m->q_dim);
-  t.fz_ss = (float*)take(sizeof(float) * (size_t)16 * (D / 16 + 1));
-  t.fz_counters = (unsigned*)take(sizeof(unsigned) * 2 * fz_counter_set_size(max_phase, L, d.n_kv_heads));
-  t.fz_prog = (int*)take(sizeof(int) * (size_t)FZ_SLOTS * 2 * max_phase);
-  t.fz_gain = (const float**)take(sizeof(float*) * (size_t)FZ_SLOTS * max_phase);
+  t.xg = (bf16_t*)take(2 * (size_t)16 * std::max(D, m->q_dim));
+  t.ss = (float*)take(sizeof(float) * (size_t)16 * (D / 16 + 1));
   t.dec_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)16 * d.n_kv_heads);
   t.stat_recs = (StatRec*)take(sizeof(StatRec) * (size_t)R * stat_segments(V));
   t.stat_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)R);
@@ -240,109 +211,12 @@ int plan_mask(const ssd_model* m, const uint8_t* mask_in, int exit_layer, std::v
   return L;
 }
 
-// Phase program of a pass over the sub-layer entries (2l + sub), optionally
-// followed by the LM head.  save_entry: the residual that enters that entry
-// (entries.size(): the LM head) is also written to the save buffer by the
-// phase that produces it; -1: none.
-FzProgram fz_build(const ssd_model* m, const std::vector<int>& entries, bool final_lm, int save_entry) {
-  FzProgram pr;
-  const ssd_model_desc& d = m->d;
-  auto consumer_gain = [&](size_t e) -> const float* {
-    if (e < entries.size()) {
-      const int l = entries[e] / 2;
-      return (entries[e] % 2 == 0) ? d.layers[l].attn_norm : d.layers[l].mlp_norm;
-    }
-    return final_lm ? d.final_norm : nullptr;
-  };
-  pr.type.push_back(PH_INIT); pr.layer.push_back(0); pr.gain.push_back(consumer_gain(0));
-  for (size_t e = 0; e < entries.size(); ++e) {
-    const int l = entries[e] / 2;
-    if ((int)e == save_entry) pr.save_phase = (int)pr.type.size() - 1;
-    if (entries[e] % 2 == 0) {
-      pr.type.insert(pr.type.end(), {PH_QKV, PH_ATTN, PH_O});
-      pr.layer.insert(pr.layer.end(), {l, l, l});
-      pr.gain.insert(pr.gain.end(), {nullptr, nullptr, consumer_gain(e + 1)});
-    } else {
-      pr.type.insert(pr.type.end(), {PH_GU, PH_DOWN});
-      pr.layer.insert(pr.layer.end(), {l, l});
-      pr.gain.insert(pr.gain.end(), {nullptr, consumer_gain(e + 1)});
-    }
-  }
-  if (final_lm) {
-    if (save_entry == (int)entries.size()) pr.save_phase = (int)pr.type.size() - 1;
-    pr.type.push_back(PH_LM); pr.layer.push_back(0); pr.gain.push_back(nullptr);
-  }
-  return pr;
-}
-
 // Sub-layer entries of layers [l0, l1) that the plan keeps (mask == nullptr: all).
-void fz_entries(std::vector<int>& out, int l0, int l1, const uint8_t* mask) {
+void plan_entries(std::vector<int>& out, int l0, int l1, const uint8_t* mask) {
   for (int l = l0; l < l1; ++l) {
     if (!(mask && mask[2 * l])) out.push_back(2 * l);
     if (!(mask && mask[2 * l + 1])) out.push_back(2 * l + 1);
   }
-}
-
-// Runs one persistent pass.  The program is uploaded to a workspace slot the
-// first time it is seen (a synchronous copy; later passes reuse the slot).
-int fz_run(ssd_seq* q, const FzProgram& pr, int M, const int* nrows, const int* pos, const int* tokens,
-           const float* h_in, float* h, float* logits, float* save_h, const int* stop, hipStream_t s) {
-  const ssd_model* m = q->m;
-  const ssd_model_desc& d = m->d;
-  Workspace& w = q->w;
-  const int np = (int)pr.type.size();
-  if (np > q->fz_max_phase) return fail(SSD_ERR_CAPACITY, "pass program too long");
-  int slot = -1;
-  for (int i = 0; i < FZ_SLOTS; ++i)
-    if (q->fz_cache[i] == pr) { slot = i; break; }
-  if (slot < 0) {
-    slot = q->fz_next;
-    q->fz_next = (q->fz_next + 1) % FZ_SLOTS;
-    std::vector<int> ints(2 * q->fz_max_phase, 0);
-    std::copy(pr.type.begin(), pr.type.end(), ints.begin());
-    std::copy(pr.layer.begin(), pr.layer.end(), ints.begin() + q->fz_max_phase);
-    std::vector<const float*> gains(q->fz_max_phase, nullptr);
-    std::copy(pr.gain.begin(), pr.gain.end(), gains.begin());
-    // the slot may still be read by passes queued on the stream
-    if (hipStreamSynchronize(s) != hipSuccess) return fail(SSD_ERR_HIP, "stream sync");
-    if (hipMemcpy(w.fz_prog + (size_t)slot * 2 * q->fz_max_phase, ints.data(), sizeof(int) * ints.size(),
-                  hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(w.fz_gain + (size_t)slot * q->fz_max_phase, gains.data(), sizeof(float*) * gains.size(),
-                  hipMemcpyHostToDevice) != hipSuccess)
-      return fail(SSD_ERR_HIP, "program upload");
-    q->fz_cache[slot] = pr;
-  }
-  FzParams p{};
-  p.layers = w.fz_layers;
-  p.L = d.n_layers; p.D = d.d_model; p.H = d.n_heads; p.KVH = d.n_kv_heads; p.HD = d.head_dim;
-  p.F = d.ffn_dim; p.V = d.vocab; p.eps = d.rms_eps;
-  p.embed = (const bf16_t*)d.embed;
-  p.lm_head = (const bf16_t*)d.lm_head;
-  p.ph_type = w.fz_prog + (size_t)slot * 2 * q->fz_max_phase;
-  p.ph_layer = p.ph_type + q->fz_max_phase;
-  p.ph_gain = w.fz_gain + (size_t)slot * q->fz_max_phase;
-  p.n_phase = np;
-  p.save_phase = save_h ? pr.save_phase : -1;
-  p.M = M; p.nrows = nrows; p.pos = pos; p.tokens = tokens; p.h_in = h_in;
-  p.h = h; p.xg = w.fz_xg; p.qb = (bf16_t*)w.qb; p.ob = w.fz_ob; p.ab = (bf16_t*)w.x2; p.ss = w.fz_ss;
-  p.part = w.part;
-  p.nsplit_max = attention_nsplit(q->max_ctx);
-  p.logits = logits; p.save_h = save_h;
-  p.pool = (bf16_t*)q->kv.pool; p.page_table = q->kv.page_table; p.PS = q->kv.page_size; p.n_lpages = q->kv.n_lpages;
-  p.rope_cs = w.rope_cs;
-  const size_t set = fz_counter_set_size(q->fz_max_phase, d.n_layers, d.n_kv_heads);
-  p.counters = w.fz_counters + (q->fz_epoch & 1) * set;
-  p.counters_next = w.fz_counters + ((q->fz_epoch + 1) & 1) * set;
-  p.n_counters = (int)set;
-  ++q->fz_epoch;
-  p.err = &w.st->error_flags;
-  p.stop = stop;
-  TRY(launch_fused_pass(p, d.head_dim, q->fz_nwg, s));
-  return 0;
-}
-
-bool fz_usable(const ssd_seq* q, int rows) {
-  return q->path == SSD_PATH_PERSISTENT && q->fz_nwg > 0 && q->m->d.dtype == SSD_DTYPE_BF16 && rows <= 16;
 }
 
 // ---------------------------------------------------------------------------
@@ -352,7 +226,7 @@ bool fz_usable(const ssd_seq* q, int rows) {
 // (xg, ss), so the entry list fixes every gain in advance.
 
 bool dec_usable(const ssd_seq* q, int rows) {
-  return q->path == SSD_PATH_KERNELS && q->m->d.dtype == SSD_DTYPE_BF16 && rows <= 16;
+  return q->m->d.dtype == SSD_DTYPE_BF16 && rows <= 16;
 }
 
 // Gain of the RMSNorm that consumes the residual entering entry e (past the
@@ -368,7 +242,7 @@ const float* dec_gain(const ssd_model* m, const std::vector<int>& ent, size_t e,
 DecGemm dec_base(const ssd_seq* q, int M, const int* nrows, const int* stop) {
   DecGemm a{};
   a.M = M; a.nrows = nrows; a.stop = stop;
-  a.ss = q->w.fz_ss; a.eps = q->m->d.rms_eps;
+  a.ss = q->w.ss; a.eps = q->m->d.rms_eps;
   return a;
 }
 
@@ -385,11 +259,11 @@ int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, co
     DecGemm r = dec_base(q, M, nrows, stop);
     r.Y = h; r.ldy = D; r.N = D;
     r.gain_next = dec_gain(m, ent, e + 1, final_lm);
-    r.xg_next = w.fz_xg; r.ss_next = w.fz_ss;
+    r.xg_next = w.xg; r.ss_next = w.ss;
     if (ent[e] % 2 == 0) {
       DecGemm a = dec_base(q, M, nrows, stop);
       a.W = (const bf16_t*)lw.w_qkv; a.N = m->qkv_dim; a.K = D;
-      a.X = w.fz_xg;
+      a.X = w.xg;
       a.q = (bf16_t*)w.qb; a.ldq = m->q_dim;
       a.pool = (bf16_t*)q->kv.pool; a.page_table = q->kv.page_table; a.PS = q->kv.page_size;
       a.n_lpages = q->kv.n_lpages; a.L = d.n_layers; a.layer = l;
@@ -403,7 +277,7 @@ int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, co
     } else {
       DecGemm a = dec_base(q, M, nrows, stop);
       a.W = (const bf16_t*)lw.w_gate_up; a.N = F; a.K = D;
-      a.X = w.fz_xg;
+      a.X = w.xg;
       a.A = (bf16_t*)w.x2;
       TRY(launch_dec_gemm(DEC_SWIGLU, a, s));
       r.W = (const bf16_t*)lw.w_down; r.K = F; r.X = (const bf16_t*)w.x2;
@@ -418,7 +292,7 @@ int dec_logits(ssd_seq* q, int M, const int* nrows, float* logits, const int* st
   const ssd_model_desc& d = q->m->d;
   DecGemm a = dec_base(q, M, nrows, stop);
   a.W = (const bf16_t*)d.lm_head; a.N = d.vocab; a.K = d.d_model;
-  a.X = q->w.fz_xg;
+  a.X = q->w.xg;
   a.Y = logits; a.ldy = d.vocab;
   TRY(launch_dec_gemm(DEC_STORE, a, s));
   return 0;
@@ -428,8 +302,8 @@ int dec_logits(ssd_seq* q, int M, const int* nrows, float* logits, const int* st
 int dec_entry(ssd_seq* q, const int* tokens, const float* src, int rows, const int* count, const int* dst_off,
               float* h, const float* gain, const int* stop, hipStream_t s) {
   const ssd_model_desc& d = q->m->d;
-  TRY(launch_dec_entry(d.embed, tokens, d.vocab, src, rows, count, dst_off, h, d.d_model, gain, q->w.fz_xg,
-                       q->w.fz_ss, stop, s));
+  TRY(launch_dec_entry(d.embed, tokens, d.vocab, src, rows, count, dst_off, h, d.d_model, gain, q->w.xg,
+                       q->w.ss, stop, s));
   return 0;
 }
 
@@ -535,25 +409,6 @@ extern "C" int ssd_seq_create(const ssd_model* m, void* kv_pool_dev, int n_pages
     delete q;
     return fail(SSD_ERR_HIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
   }
-  // persistent decode pass: layer pointer table, zeroed counters, one workgroup per CU
-  q->fz_max_phase = 2 + 5 * m->d.n_layers;
-  if (m->d.dtype == SSD_DTYPE_BF16) {
-    std::vector<FzLayer> fl(m->d.n_layers);
-    for (int l = 0; l < m->d.n_layers; ++l) {
-      const ssd_layer_weights& lw = m->layers[l];
-      fl[l] = FzLayer{lw.attn_norm, (const bf16_t*)lw.w_qkv, (const bf16_t*)lw.w_o, lw.mlp_norm,
-                      (const bf16_t*)lw.w_gate_up, (const bf16_t*)lw.w_down};
-    }
-    int dev = 0, cus = 0, coop = 0, per_cu = 0;
-    const size_t nctr = 2 * fz_counter_set_size(q->fz_max_phase, m->d.n_layers, m->d.n_kv_heads);
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
-        fused_pass_max_blocks_per_cu(m->d.head_dim, &per_cu) == 0 && per_cu >= 1 &&
-        hipMemcpy(q->w.fz_layers, fl.data(), sizeof(FzLayer) * fl.size(), hipMemcpyHostToDevice) == hipSuccess &&
-        hipMemset(q->w.fz_counters, 0, sizeof(unsigned) * nctr) == hipSuccess)
-      q->fz_nwg = cus;
-  }
   int rc = launch_state_init(q->w.st, stream);
   if (rc == 0 && hipMemset(q->w.dec_ctr, 0, sizeof(unsigned) * 16 * (size_t)m->d.n_kv_heads) != hipSuccess)
     rc = SSD_ERR_HIP;
@@ -609,13 +464,9 @@ extern "C" int ssd_decode_ar(ssd_seq* q, float temperature, uint64_t seed, float
   const Workspace& w = q->w;
   TRY(launch_single_row_prep(w.st, w.pos1, w.tok1, q->max_ctx, s));
   float* lg = logits_dev ? logits_dev : w.logits1;
-  if (fz_usable(q, 1)) {
+  if (dec_usable(q, 1)) {
     std::vector<int> ent;
-    fz_entries(ent, 0, d.n_layers, nullptr);
-    TRY(fz_run(q, fz_build(q->m, ent, true, -1), 1, nullptr, w.pos1, w.tok1, nullptr, w.h1, lg, nullptr, nullptr, s));
-  } else if (dec_usable(q, 1)) {
-    std::vector<int> ent;
-    fz_entries(ent, 0, d.n_layers, nullptr);
+    plan_entries(ent, 0, d.n_layers, nullptr);
     TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, dec_gain(q->m, ent, 0, true), nullptr, s));
     TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, ent, 0, ent.size(), true, nullptr, s));
     TRY(dec_logits(q, 1, nullptr, lg, nullptr, s));
@@ -647,27 +498,11 @@ extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_lay
   CHECK_ARG(b >= 0, "exit_layer out of range");
   const int* stop = &w.st->stop;
   TRY(launch_draft_begin(w.st, s));
-  if (fz_usable(q, 1)) {
-    std::vector<int> ent;
-    fz_entries(ent, 0, b, nullptr);
-    const int save_entry = (int)ent.size();
-    fz_entries(ent, b, d.n_layers, mask.data());
-    const FzProgram pr = fz_build(q->m, ent, true, save_entry);
-    for (int j = 1; j <= d_max; ++j) {
-      TRY(launch_draft_step_prep(w.st, draft_tokens_dev, j, w.pos1, w.tok1, q->max_ctx, n_drafted_dev, s));
-      float* lg = draft_logits_dev + (size_t)(j - 1) * d.vocab;
-      TRY(fz_run(q, pr, 1, nullptr, w.pos1, w.tok1, nullptr, w.h1, lg, w.hb + (size_t)(j - 1) * d.d_model, stop, s));
-      TRY(launch_row_stats_seg(lg, d.vocab, 1, d.vocab, temperature, seed, nullptr, 0, 0, PURPOSE_DRAFT, nullptr,
-                               w.stat_recs, w.stat_ctr, nullptr,
-                               DraftStep{w.st, j, d_max, conf_thresh, draft_tokens_dev, n_drafted_dev}, s));
-    }
-    return SSD_OK;
-  }
   if (dec_usable(q, 1)) {
     std::vector<int> ent;
-    fz_entries(ent, 0, b, nullptr);
+    plan_entries(ent, 0, b, nullptr);
     const size_t save = ent.size();
-    fz_entries(ent, b, d.n_layers, mask.data());
+    plan_entries(ent, b, d.n_layers, mask.data());
     const float* g0 = dec_gain(q->m, ent, 0, true);
     for (int j = 1; j <= d_max; ++j) {
       TRY(launch_draft_step_prep(w.st, draft_tokens_dev, j, w.pos1, w.tok1, q->max_ctx, n_drafted_dev, s));
@@ -713,36 +548,15 @@ extern "C" int ssd_verify(ssd_seq* q, const uint8_t* skip_mask_host, int exit_la
   const int* rows = &w.st->verify_rows;
   TRY(launch_verify_prep(w.st, draft_tokens_dev, n_drafted_dev, d_max, w.vpos, w.vtok, w.pos1, w.tok1, q->max_ctx,
                          s));
-  if (fz_usable(q, M)) {
-    std::vector<int> suffix;
-    fz_entries(suffix, b, d.n_layers, nullptr);
-    if (reuse && b > 0) {
-      // rows < d' take the residual the draft saved at the boundary; the last row runs the layers below it
-      TRY(launch_copy_rows(w.hb, w.h, d_max, d.d_model, n_drafted_dev, nullptr, nullptr, s));
-      std::vector<int> prefix;
-      fz_entries(prefix, 0, b, nullptr);
-      TRY(fz_run(q, fz_build(q->m, prefix, false, -1), 1, nullptr, w.pos1, w.tok1, nullptr, w.h1, nullptr, nullptr,
-                 nullptr, s));
-      TRY(launch_copy_rows(w.h1, w.h, 1, d.d_model, nullptr, n_drafted_dev, nullptr, s));
-      TRY(fz_run(q, fz_build(q->m, suffix, true, -1), M, rows, w.vpos, nullptr, w.h, w.h, logits_dev, nullptr,
-                 nullptr, s));
-    } else {
-      std::vector<int> all;
-      fz_entries(all, 0, d.n_layers, nullptr);
-      TRY(fz_run(q, fz_build(q->m, all, true, -1), M, rows, w.vpos, w.vtok, nullptr, w.h, logits_dev, nullptr,
-                 nullptr, s));
-    }
-    return SSD_OK;
-  }
   if (dec_usable(q, M)) {
     std::vector<int> suffix;
-    fz_entries(suffix, reuse ? b : 0, d.n_layers, nullptr);
+    plan_entries(suffix, reuse ? b : 0, d.n_layers, nullptr);
     const float* g0 = dec_gain(q->m, suffix, 0, true);
     if (reuse) {
       // the last row (y_d') runs the layers below the boundary first (it uses row 0 of the block's
       // normalised-input buffers); then the rows < d' take the residual the draft saved there
       std::vector<int> prefix;
-      fz_entries(prefix, 0, b, nullptr);
+      plan_entries(prefix, 0, b, nullptr);
       TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, dec_gain(q->m, prefix, 0, false), nullptr, s));
       TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, prefix, 0, prefix.size(), false, nullptr, s));
       TRY(dec_entry(q, nullptr, w.hb, d_max, n_drafted_dev, nullptr, w.h, g0, nullptr, s));
@@ -851,15 +665,6 @@ extern "C" int ssd_row_stats(const float* logits_dev, int rows, int V, float tem
 // ---------------------------------------------------------------------------
 // host synchronisation
 
-extern "C" int ssd_seq_set_decode_path(ssd_seq* q, int path) {
-  CHECK_ARG(q, "null argument");
-  CHECK_ARG(path == SSD_PATH_KERNELS || path == SSD_PATH_PERSISTENT, "unknown decode path");
-  if (path == SSD_PATH_PERSISTENT && q->fz_nwg <= 0)
-    return fail(SSD_ERR_UNSUPPORTED, "persistent pass needs a bf16 model and cooperative launch");
-  q->path = path;
-  return SSD_OK;
-}
-
 extern "C" int ssd_read_state(ssd_seq* q, ssd_state* out, hipStream_t s) {
   CHECK_ARG(q && out, "null argument");
   DevState st;
@@ -875,7 +680,6 @@ extern "C" int ssd_read_state(ssd_seq* q, ssd_state* out, hipStream_t s) {
   out->last_n_emitted = st.n_emitted;
   if (st.error_flags & ERRF_CAPACITY) return fail(SSD_ERR_CAPACITY, "KV pages or output log exhausted on the device");
   if (st.error_flags & ERRF_NUMERIC) return fail(SSD_ERR_NUMERIC, "non-finite logits seen on the device");
-  if (st.error_flags & ERRF_TIMEOUT) return fail(SSD_ERR_HIP, "a bounded wait of the persistent pass gave up");
   return SSD_OK;
 }
 

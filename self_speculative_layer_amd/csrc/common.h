@@ -14,7 +14,6 @@ constexpr int WAVE = 64;
 // Flags in DevState::error_flags.
 constexpr int ERRF_CAPACITY = 1;
 constexpr int ERRF_NUMERIC = 2;
-constexpr int ERRF_TIMEOUT = 4;   // a bounded wait of the persistent pass gave up
 
 // Per-sequence state that lives on the device, so that the host can enqueue
 // a whole decode iteration without reading anything back.

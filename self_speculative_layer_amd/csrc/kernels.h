@@ -157,70 +157,4 @@ int launch_dec_entry(const void* emb, const int* tokens, int V, const float* src
                      const int* dst_off, float* h, int D, const float* gain, void* xg, float* ss, const int* stop,
                      hipStream_t s);
 
-// ---------------------------------------------------------------------------
-// Persistent decode pass (fused.hip)
-
-enum PassPhase { PH_INIT = 0, PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_DOWN = 5, PH_LM = 6 };
-
-struct FzLayer {
-  const float* attn_norm;
-  const bf16_t* w_qkv;
-  const bf16_t* w_o;
-  const float* mlp_norm;
-  const bf16_t* w_gate_up;
-  const bf16_t* w_down;
-};
-
-struct FzParams {
-  const FzLayer* layers;
-  int L, D, H, KVH, HD, F, V;
-  float eps;
-  const bf16_t* embed;
-  const bf16_t* lm_head;
-  // program
-  const int* ph_type;
-  const int* ph_layer;
-  const float* const* ph_gain;
-  int n_phase;
-  int save_phase;            // phase (INIT or residual) whose output h is also written to save_h; -1: none
-  // rows
-  int M;
-  const int* nrows;
-  const int* pos;
-  const int* tokens;         // INIT from the embedding (when h_in == nullptr)
-  const float* h_in;         // INIT from residual rows
-  // buffers
-  float* h;
-  bf16_t* xg;
-  bf16_t* qb;
-  bf16_t* ob;
-  bf16_t* ab;
-  float* ss;                 // [D/16][16] group sums of h^2
-  float* part;
-  int nsplit_max;
-  float* logits;
-  float* save_h;
-  // cache
-  bf16_t* pool;
-  const int* page_table;
-  int PS, n_lpages;
-  const float2* rope_cs;     // [position][HD/2] (cos, sin)
-  unsigned* counters;        // counter set of this pass (see fz_counter_set_size); the other set is cleared
-  unsigned* counters_next;   // the counter set of the next pass, cleared by this pass
-  int n_counters;            // counters per set
-  int* err;
-  const int* stop;
-};
-
-// Phase counters of one pass: per phase one top counter and FZ_GROUPS group
-// counters, then per attention phase one counter per KV head.  Two sets
-// alternate between consecutive passes.
-constexpr int FZ_GROUPS = 8;
-inline size_t fz_counter_set_size(int max_phase, int n_layers, int n_kv_heads) {
-  return (size_t)max_phase * (1 + FZ_GROUPS) + (size_t)n_layers * n_kv_heads;
-}
-
-int launch_fused_pass(const FzParams& p, int head_dim, int nwg, hipStream_t s);
-int fused_pass_max_blocks_per_cu(int head_dim, int* blocks);
-
 }  // namespace ssd

@@ -27,17 +27,6 @@ def pair(request):
     g.close()
 
 
-PATHS = {"kernels": B.SSD_PATH_KERNELS, "persistent": B.SSD_PATH_PERSISTENT}
-
-
-@pytest.fixture(params=sorted(PATHS))
-def path(request, pair):
-    """Decode path of the sequence; the persistent pass exists for bf16 models."""
-    if request.param == "persistent" and pair[0].dtype != "bf16":
-        pytest.skip("the persistent decode pass is bf16 only")
-    return PATHS[request.param]
-
-
 def test_device_weights_equal_host_weights(pair):
     shape, g, o = pair
     t = g.tensors
@@ -87,14 +76,14 @@ def _mask_of(shape, plan):
     return synth.mask_exit(shape.n_layers, plan["exit_layer"])
 
 
-def test_greedy_ssd_matches_oracle_and_ar(pair, path):
+def test_greedy_ssd_matches_oracle_and_ar(pair):
     """GPU SSD tokens == oracle AR tokens (margin rule) and == GPU AR tokens."""
     shape, g, o = pair
     plan = PLANS[shape.name]
     P, n_gen = 32, 48
     prompt = synth.prompt_tokens(P, shape.vocab)
     ref, ref_z = oracle_ar_with_logits(o, prompt, n_gen)
-    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * plan["d"] + 8, max_rows=64, max_draft=8, path=path)
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * plan["d"] + 8, max_rows=64, max_draft=8)
     out, stats = seq.generate_ssd(dev(prompt), n_gen, skip_mask=plan.get("skip_mask"),
                                   exit_layer=plan.get("exit_layer"), d=plan["d"])
     print("iterations %d, mean emitted %.2f" % (len(stats), np.mean([e for _, e in stats])))
@@ -105,7 +94,7 @@ def test_greedy_ssd_matches_oracle_and_ar(pair, path):
     seq.close()
 
 
-def test_verify_logits_match_oracle_per_iteration(pair, path):
+def test_verify_logits_match_oracle_per_iteration(pair):
     """Each iteration's verify logits (rows 0..d') against the oracle's verify."""
     shape, g, o = pair
     plan = PLANS[shape.name]
@@ -116,7 +105,7 @@ def test_verify_logits_match_oracle_per_iteration(pair, path):
     records = []
     ossd.ssd_generate(o, prompt, n_gen, mask, d,
                       on_iteration=lambda it, n, dr, zq, zp, em, kv: records.append((list(dr), zq, zp, em)))
-    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=64, max_draft=8, path=path)
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=64, max_draft=8)
     B.ssd_prefill(seq.handle, dev(prompt))
     V = shape.vocab
     worst = 0.0
@@ -141,7 +130,7 @@ def test_verify_logits_match_oracle_per_iteration(pair, path):
     seq.close()
 
 
-def test_reuse_equals_no_reuse(pair, path):
+def test_reuse_equals_no_reuse(pair):
     """verify with the draft's saved state == verify recomputing every row, bitwise."""
     shape, g, o = pair
     plan = PLANS[shape.name]
@@ -150,7 +139,7 @@ def test_reuse_equals_no_reuse(pair, path):
     prompt = synth.prompt_tokens(P, shape.vocab)
     outs = []
     for reuse in (True, False):
-        seq = B.Sequence(g, max_ctx=P + 4 * d + 8, max_rows=64, max_draft=8, path=path)
+        seq = B.Sequence(g, max_ctx=P + 4 * d + 8, max_rows=64, max_draft=8)
         B.ssd_prefill(seq.handle, dev(prompt))
         B.ssd_draft(seq.handle, plan.get("skip_mask"), plan.get("exit_layer"), d, 0.0, 0.0, 0, seq.draft_tokens,
                     seq.draft_logits, seq.n_drafted)
@@ -162,17 +151,17 @@ def test_reuse_equals_no_reuse(pair, path):
     assert torch.equal(outs[0], outs[1])
 
 
-def test_empty_plan_accepts_everything(pair, path):
+def test_empty_plan_accepts_everything(pair):
     shape, g, o = pair
     P, n_gen, d = 16, 30, 4
     prompt = synth.prompt_tokens(P, shape.vocab)
-    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=64, max_draft=8, path=path)
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=64, max_draft=8)
     out, stats = seq.generate_ssd(dev(prompt), n_gen, skip_mask=np.zeros(2 * shape.n_layers, np.uint8), d=d)
     assert all(e == dp + 1 for dp, e in stats)
     seq.close()
 
 
-def test_sampled_ssd_matches_oracle(pair, path):
+def test_sampled_ssd_matches_oracle(pair):
     """T = 1 with a confidence stop: same Philox draws on both sides, so the emitted
     tokens agree except at decisions within 1e-2 (log units) of flipping."""
     shape, g, o = pair
@@ -182,7 +171,7 @@ def test_sampled_ssd_matches_oracle(pair, path):
     P, n_gen = 24, 40
     prompt = synth.prompt_tokens(P, shape.vocab)
     ref, ost, _ = ossd.ssd_generate(o, prompt, n_gen, mask, d, tau=tau, T=T, seed=seed)
-    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=64, max_draft=8, path=path)
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=64, max_draft=8)
     out, stats = seq.generate_ssd(dev(prompt), n_gen, skip_mask=plan.get("skip_mask"),
                                   exit_layer=plan.get("exit_layer"), d=d, conf_thresh=tau, temperature=T, seed=seed)
     got = [int(x) for x in out]
@@ -303,36 +292,24 @@ def test_capacity_is_reported_not_faulted():
 
 
 @pytest.mark.parametrize("shape", [BF16_HD64, BF16_HD128], ids=lambda s: s.name)
-def test_decode_paths_agree_with_prefill(shape):
-    """An AR step on the kernels path gives the same logits, bit for bit, as the
-    last row of a prefill (general kernels, many rows) at that position; the
-    persistent pass (its own attention arithmetic) agrees within the bf16 bound."""
+def test_decode_step_equals_prefill_row(shape):
+    """An AR step (decode-block kernels, one row) gives the same logits, bit for
+    bit, as the last row of a prefill (general kernels, many rows) at that
+    position."""
     g = gpu_model(shape)
     P = 70
     prompt = synth.prompt_tokens(P, shape.vocab)
-    logits = {}
-    for name, path in PATHS.items():
-        seq1 = B.Sequence(g, max_ctx=P + 64, max_rows=64, max_draft=4, path=path)
-        B.ssd_prefill(seq1.handle, dev(prompt))
-        lg1 = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
-        B.ssd_decode_ar(seq1.handle, 0.0, 0, lg1)
-        t_p = int(B.ssd_read_output(seq1.handle, 2)[0])
-        assert B.ssd_read_state(seq1.handle).error_flags == 0
-        logits[name] = lg1
-        seq1.close()
+    seq1 = B.Sequence(g, max_ctx=P + 64, max_rows=64, max_draft=4)
+    B.ssd_prefill(seq1.handle, dev(prompt))
+    lg1 = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
+    B.ssd_decode_ar(seq1.handle, 0.0, 0, lg1)
+    t_p = int(B.ssd_read_output(seq1.handle, 2)[0])
+    assert B.ssd_read_state(seq1.handle).error_flags == 0
+    seq1.close()
     seq2 = B.Sequence(g, max_ctx=P + 64, max_rows=32, max_draft=4)
     lg2 = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
     B.ssd_prefill(seq2.handle, dev(list(prompt) + [t_p]), 0.0, 0, lg2)
     torch.cuda.synchronize()
-    assert torch.equal(logits["kernels"], lg2)
-    assert (logits["persistent"] - logits["kernels"]).abs().max().item() < logit_tol(shape)
+    assert torch.equal(lg1, lg2)
     seq2.close()
-    g.close()
-
-
-def test_persistent_path_is_refused_for_fp32():
-    g = gpu_model(synth.TINY)
-    with pytest.raises(B.SSDError) as e:
-        B.Sequence(g, max_ctx=128, max_rows=16, max_draft=4, path=B.SSD_PATH_PERSISTENT)
-    assert e.value.code == B.SSD_ERR_UNSUPPORTED
     g.close()
