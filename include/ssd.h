@@ -73,6 +73,16 @@ typedef enum ssd_dtype { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
 typedef struct ssd_model ssd_model;
 typedef struct ssd_seq ssd_seq;
 
+/* Weight layouts.  Logical shapes below are [rows N, columns K] (y = W x).
+ * fp32 models: row-major, K contiguous.
+ * bf16 models: the projection weights (w_qkv, w_o, w_gate_up, w_down, lm_head)
+ * are packed in matrix-core tiles: 16-row groups, each split into 32-column
+ * steps of 16 x 32 elements stored contiguously (1 KB), i.e. element (n, k) at
+ *   ((n / 16) * (K / 32) + k / 32) * 512 + (n % 16) * 32 + k % 32,
+ * with N rounded up to a multiple of 16 (padding rows are never used for an
+ * output).  ssd_pack_bf16 converts a row-major matrix; ssd_packed_bf16_bytes
+ * gives the size.  The embedding stays row-major [V, D] (rows are gathered). */
+
 /* Weights of one decoder layer. */
 typedef struct ssd_layer_weights {
   const float* attn_norm;   /* [D] float32 RMSNorm gain before attention */
@@ -96,9 +106,9 @@ typedef struct ssd_model_desc {
   float rms_eps;            /* e.g. 1e-5 */
   float rope_theta;         /* e.g. 10000 */
   int dtype;                /* ssd_dtype: storage of weights, activations and the KV cache */
-  const void* embed;        /* [V, D] */
+  const void* embed;        /* [V, D] row-major */
   const float* final_norm;  /* [D] float32 */
-  const void* lm_head;      /* [V, D] */
+  const void* lm_head;      /* [V, D] (bf16: packed) */
   const ssd_layer_weights* layers;  /* host array of n_layers entries (copied) */
 } ssd_model_desc;
 
@@ -125,6 +135,15 @@ typedef struct ssd_state {
 /* Validates the shape and records the weight pointers (which must stay valid
  * until ssd_model_destroy).  Builds nothing on the device. */
 int ssd_model_create(const ssd_model_desc* desc, ssd_model** out_model);
+
+/* Bytes of a bf16 [N, K] weight in the packed tile layout (K a multiple of 32):
+ * ceil(N / 16) * 16 * K * 2.  SSD_ERR_SHAPE otherwise. */
+int ssd_packed_bf16_bytes(int N, int K, size_t* bytes);
+
+/* Packs a row-major bf16 [N, K] matrix (src, device) into the tile layout
+ * (dst, device, ssd_packed_bf16_bytes; caller-owned; must not overlap src);
+ * padding rows are zero.  Enqueued on stream; SSD_ERR_SHAPE if K % 32 != 0. */
+int ssd_pack_bf16(const void* src, void* dst, int N, int K, hipStream_t stream);
 int ssd_model_destroy(ssd_model* model);
 
 /* Bytes of the KV pool for n_pages pages of page_size positions.

@@ -13,7 +13,8 @@ ERROR_NAMES = {-1: "SSD_ERR_ARG", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_CAPACITY", -
                -5: "SSD_ERR_UNSUPPORTED", -6: "SSD_ERR_NUMERIC"}
 
 # Every symbol include/ssd.h declares.
-EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_kv_pool_bytes", "ssd_workspace_bytes", "ssd_seq_create",
+EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_packed_bf16_bytes", "ssd_pack_bf16", "ssd_kv_pool_bytes",
+           "ssd_workspace_bytes", "ssd_seq_create",
            "ssd_seq_destroy", "ssd_prefill", "ssd_decode_ar", "ssd_draft", "ssd_verify", "ssd_accept", "ssd_commit",
            "ssd_score_masks", "ssd_row_stats", "ssd_read_state", "ssd_read_output", "ssd_last_error",
            "ssd_profile_enable", "ssd_profile_disable", "ssd_profile_read"]
@@ -67,6 +68,8 @@ def lib():
         sig = {
             "ssd_model_create": [ctypes.POINTER(ssd_model_desc), ctypes.POINTER(P)],
             "ssd_model_destroy": [P],
+            "ssd_packed_bf16_bytes": [I, I, ctypes.POINTER(ctypes.c_size_t)],
+            "ssd_pack_bf16": [P, P, I, I, P],
             "ssd_kv_pool_bytes": [P, I, I, SZ],
             "ssd_workspace_bytes": [P, I, I, I, SZ],
             "ssd_seq_create": [P, P, I, I, P, I, P, ctypes.c_size_t, I, I, P, ctypes.POINTER(P)],
@@ -130,6 +133,16 @@ def ssd_model_create(desc):
 
 def ssd_model_destroy(model):
     check(lib().ssd_model_destroy(model))
+
+
+def ssd_packed_bf16_bytes(N, K):
+    b = ctypes.c_size_t()
+    check(lib().ssd_packed_bf16_bytes(N, K, ctypes.byref(b)))
+    return b.value
+
+
+def ssd_pack_bf16(src, dst, N, K, stream=None):
+    check(lib().ssd_pack_bf16(_ptr(src), _ptr(dst), N, K, _stream(stream)))
 
 
 def ssd_kv_pool_bytes(model, n_pages, page_size):

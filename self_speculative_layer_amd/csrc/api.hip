@@ -343,6 +343,20 @@ extern "C" int ssd_model_create(const ssd_model_desc* desc, ssd_model** out_mode
   return SSD_OK;
 }
 
+extern "C" int ssd_packed_bf16_bytes(int N, int K, size_t* bytes) {
+  CHECK_ARG(bytes && N > 0 && K > 0, "bad argument");
+  if (K % 32 != 0) return fail(SSD_ERR_SHAPE, "K must be a multiple of 32");
+  *bytes = (size_t)((N + 15) / 16) * 16 * (size_t)K * 2;
+  return SSD_OK;
+}
+
+extern "C" int ssd_pack_bf16(const void* src, void* dst, int N, int K, hipStream_t stream) {
+  CHECK_ARG(src && dst && N > 0 && K > 0, "bad argument");
+  if (K % 32 != 0) return fail(SSD_ERR_SHAPE, "K must be a multiple of 32");
+  TRY(launch_pack_bf16(src, dst, N, K, stream));
+  return SSD_OK;
+}
+
 extern "C" int ssd_model_destroy(ssd_model* model) {
   delete model;
   return SSD_OK;

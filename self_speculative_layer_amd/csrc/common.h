@@ -160,6 +160,13 @@ __device__ __forceinline__ void rope_apply(float x1, float x2, float2 cs, float&
   y2 = __fadd_rn(__fmul_rn(x2, cs.x), __fmul_rn(x1, cs.y));
 }
 
+// Packed bf16 projection weights: element (n, k) of an [N, K] matrix, in
+// 16-row groups of 32-column steps stored as 16 x 32 contiguous elements (one
+// matrix-core A operand per 1 KB).
+__device__ __forceinline__ size_t wpk_index(int n, int k, int K) {
+  return ((size_t)(n >> 4) * (size_t)(K >> 5) + (size_t)(k >> 5)) * 512 + (size_t)(n & 15) * 32 + (k & 31);
+}
+
 // Activation layout of a decode block (at most 16 rows): blocks of 32
 // columns, each holding the 16 rows' 32 values contiguously, so that one
 // matrix-core step's activations (16 rows x 32 columns) are one 1 KB run.

@@ -41,8 +41,9 @@ constexpr int DEC_SSP = 8;    // RMS tile sums per lane and row: K <= 64 * 16 * 
 //
 // A workgroup owns one tile of 16 output features (two row sets of W for the
 // SwiGLU and QKV epilogues) and all of K.  Its NW waves take contiguous
-// 64-element slices of K; each wave keeps DEC_U steps (16 rows x 64 bytes of
-// each weight set per step) in flight in registers and reloads a step's
+// 64-element slices of K; each wave keeps DEC_U steps (one contiguous 1 KB
+// tile of each weight set per step, packed layout) in flight in registers and
+// reloads a step's
 // registers as soon as its MFMA has been issued.  The per-wave tiles are
 // reduced through LDS in wave order.  Rows >= M repeat the last row's
 // activations (no masking on the load path); their outputs are not stored.
@@ -102,8 +103,8 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
     int wrow = t.f0 + r;
     if (HALF) wrow = (r < 8 ? t.f0 : t.f1) + (r & 7);
     if (EPI == DEC_STORE) wrow = min(wrow, a.N - 1);   // rows past N repeat the last W row; not stored
-    wp[j * SPT] = a.W + (size_t)wrow * K + g * 8;
-    if (DUAL) wp[j * SPT + 1] = a.W + (size_t)(t.f1 + r) * K + g * 8;
+    wp[j * SPT] = a.W + wpk_index(wrow, g * 8, K);                  // step t: + 512 t
+    if (DUAL) wp[j * SPT + 1] = a.W + wpk_index(t.f1 + r, g * 8, K);
   }
   const bf16_t* xp = a.X + dec_act_index(min(r, Ma - 1), g * 8);   // step t: xp + 512 t
 
@@ -125,9 +126,8 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   const int n = 2 * ((nu * (wave + 1)) / NW) - s0;   // 32-element steps of this wave (>= 2)
   dec_u32x4 w[NS][U], xa[U];
   auto reload = [&](int u, int step) {
-    const int k = (s0 + step) * 32;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) w[j][u] = *(const dec_u32x4*)(wp[j] + k);
+    for (int j = 0; j < NS; ++j) w[j][u] = *(const dec_u32x4*)(wp[j] + (size_t)(s0 + step) * 512);
     xa[u] = *(const dec_u32x4*)(xp + (size_t)(s0 + step) * 512);
   };
 #pragma unroll

@@ -38,6 +38,9 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
                   float* Y, int ldy, void* A, int lda, const float* rscale, const int* nrows, const int* ymap,
                   const int* stop, hipStream_t s);
 
+// Row-major bf16 [N, K] -> packed tile layout (K % 32 == 0).
+int launch_pack_bf16(const void* src, void* dst, int N, int K, hipStream_t s);
+
 // x[m] = act(h[hmap[m]] * gain), inv[m] = 1 / sqrt(mean(h^2) + eps).
 int launch_rowprep(int dtype, const float* h, int ldh, const float* gain, void* x, int ldx, float* inv, int M, int D,
                    float eps, const int* nrows, const int* hmap, const int* stop, hipStream_t s);

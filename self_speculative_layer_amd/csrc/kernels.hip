@@ -20,7 +20,7 @@ __device__ __forceinline__ int active_rows(int M, const int* nrows) {
 
 // ===========================================================================
 // Linear layers, bf16: Y[M, N] = X[M, K] . W[N, K]^T with fp32 accumulation on
-// the matrix cores.  Weight-streaming design for few rows: a workgroup owns 16
+// the matrix cores (W in the packed tile layout, wpk_index).  Weight-streaming design for few rows: a workgroup owns 16
 // output features for a 16-row block and all of K; its NW waves split K into
 // contiguous 64-element slices (each weight row is read as whole 128-byte
 // lines by one wave), accumulate with v_mfma_f32_16x16x32_bf16 (weights as
@@ -49,8 +49,8 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_rows16(
   const int n0 = tile * 16;
   const int nrow = n0 + r;
   const bool wv = nrow < N;
-  const bf16_t* wp = W + (size_t)(wv ? nrow : 0) * K + g * 8;
-  const bf16_t* wp2 = wp + (size_t)N * K;   // up rows (EPI_SWIGLU)
+  const bf16_t* wp = W + wpk_index(wv ? nrow : 0, g * 8, K);     // packed: step kb at + 512 kb
+  const bf16_t* wp2 = W + wpk_index((wv ? nrow : 0) + N, g * 8, K);   // up rows (EPI_SWIGLU)
   const int m = m0 + r;
   const bool xv = m < Ma;
   const bf16_t* xp = X + (size_t)(xv ? m : 0) * ldx + g * 8;
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_rows16(
     u32x4 wa[GEMM_U], wb[GEMM_U], xa[GEMM_U];
 #pragma unroll
     for (int u = 0; u < GEMM_U; ++u) {
-      wa[u] = wv ? *(const u32x4*)(wp + (kb + u) * 32) : zero;
-      if (EPI == EPI_SWIGLU) wb[u] = wv ? *(const u32x4*)(wp2 + (kb + u) * 32) : zero;
+      wa[u] = wv ? *(const u32x4*)(wp + (size_t)(kb + u) * 512) : zero;
+      if (EPI == EPI_SWIGLU) wb[u] = wv ? *(const u32x4*)(wp2 + (size_t)(kb + u) * 512) : zero;
       xa[u] = xv ? *(const u32x4*)(xp + (kb + u) * 32) : zero;
     }
 #pragma unroll
@@ -80,12 +80,12 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_rows16(
     }
   }
   for (; kb < kb_end; ++kb) {
-    u32x4 wa = wv ? *(const u32x4*)(wp + kb * 32) : zero;
+    u32x4 wa = wv ? *(const u32x4*)(wp + (size_t)kb * 512) : zero;
     u32x4 xa = xv ? *(const u32x4*)(xp + kb * 32) : zero;
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa),
                                                   __builtin_bit_cast(bf16x8, xa), acc, 0, 0, 0);
     if (EPI == EPI_SWIGLU) {
-      u32x4 wb = wv ? *(const u32x4*)(wp2 + kb * 32) : zero;
+      u32x4 wb = wv ? *(const u32x4*)(wp2 + (size_t)kb * 512) : zero;
       acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb),
                                                      __builtin_bit_cast(bf16x8, xa), acc2, 0, 0, 0);
     }
@@ -1205,6 +1205,32 @@ int launch_copy_rows(const float* src, float* dst, int rows, int D, const int* c
                      const int* stop, hipStream_t s) {
   if (rows <= 0) return 0;
   hipLaunchKernelGGL(copy_rows_kernel, dim3(rows), dim3(256), 0, s, src, dst, rows, D, count, dst_off, stop);
+  return last_launch();
+}
+
+// Row-major bf16 [N, K] -> packed tile layout (wpk_index); one thread per 16
+// bytes of the output, padding rows zero.
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
+                                                        int N, int K) {
+  const size_t total = (size_t)((N + 15) / 16) * 16 * K / 8;
+  const size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= total) return;
+  const size_t e = c * 8;
+  const size_t blk = e / 512;
+  const int within = (int)(e % 512);
+  const int ksteps = K / 32;
+  const int n = (int)(blk / ksteps) * 16 + within / 32;
+  const int k = (int)(blk % ksteps) * 32 + within % 32;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (n < N) v = *(const u32x4*)(src + (size_t)n * K + k);
+  *(u32x4*)(dst + e) = v;
+}
+
+int launch_pack_bf16(const void* src, void* dst, int N, int K, hipStream_t s) {
+  if (N <= 0 || K <= 0 || K % 32 != 0) return SSD_ERR_SHAPE;
+  const size_t total = (size_t)((N + 15) / 16) * 16 * K / 8;
+  hipLaunchKernelGGL(pack_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, (const bf16_t*)src,
+                     (bf16_t*)dst, N, K);
   return last_launch();
 }
 

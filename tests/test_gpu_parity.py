@@ -9,6 +9,7 @@ from oracle import model as omodel
 from oracle import philox as ophilox
 from oracle import ssd as ossd
 
+from synth import device as sdev
 from gpu_util import (BF16_HD64, BF16_HD128, F32_GQA, check_greedy_tokens, dev, gpu_model, logit_tol,
                       oracle_ar_with_logits)
 
@@ -27,15 +28,29 @@ def pair(request):
     g.close()
 
 
+def _logical(t, N, K, shape):
+    """A device weight as its [N, K] row-major float matrix (bf16 weights are packed)."""
+    if shape.dtype == "bf16":
+        t = sdev.unpack_bf16(t, N, K)
+    return t.float().cpu().numpy()
+
+
 def test_device_weights_equal_host_weights(pair):
     shape, g, o = pair
     t = g.tensors
     emb = t["embed"].float().cpu().numpy().astype(np.float64)
     assert np.array_equal(emb, o.embed)
-    wqkv = t["layers"][1]["w_qkv"].float().cpu().numpy()
+    D, F = shape.d_model, shape.ffn_dim
+    wqkv = _logical(t["layers"][1]["w_qkv"], shape.qkv_dim, D, shape)
+    assert np.array_equal(wqkv[:shape.q_dim], o.layers[1].wq)
     assert np.array_equal(wqkv[shape.q_dim: shape.q_dim + shape.kv_dim], o.layers[1].wk)
-    wgu = t["layers"][0]["w_gate_up"].float().cpu().numpy()
-    assert np.array_equal(wgu[shape.ffn_dim:], o.layers[0].wup)
+    assert np.array_equal(wqkv[shape.q_dim + shape.kv_dim:], o.layers[1].wv)
+    wgu = _logical(t["layers"][0]["w_gate_up"], 2 * F, D, shape)
+    assert np.array_equal(wgu[:F], o.layers[0].wgate)
+    assert np.array_equal(wgu[F:], o.layers[0].wup)
+    assert np.array_equal(_logical(t["layers"][0]["w_o"], D, shape.q_dim, shape), o.layers[0].wo)
+    assert np.array_equal(_logical(t["layers"][0]["w_down"], D, F, shape), o.layers[0].wdown)
+    assert np.array_equal(_logical(t["lm_head"], shape.vocab, D, shape), o.lm_head)
     for l in range(shape.n_layers):
         assert np.array_equal(t["layers"][l]["attn_norm"].cpu().numpy().astype(np.float64), o.layers[l].attn_norm)
         assert np.array_equal(t["layers"][l]["mlp_norm"].cpu().numpy().astype(np.float64), o.layers[l].mlp_norm)
@@ -313,3 +328,32 @@ def test_decode_step_equals_prefill_row(shape):
     assert torch.equal(lg1, lg2)
     seq2.close()
     g.close()
+
+
+@pytest.mark.parametrize("N,K", [(16, 32), (1000, 256), (2003, 512), (48, 4096)])
+def test_pack_bf16_layout(N, K):
+    """ssd_pack_bf16 (device kernel) against the layout definition (element (n, k) at
+    ((n / 16) * (K / 32) + k / 32) * 512 + (n % 16) * 32 + k % 32, padding rows zero)."""
+    src = torch.arange(N * K, dtype=torch.float32, device="cuda").remainder(251).to(torch.bfloat16).view(N, K)
+    nbytes = B.ssd_packed_bf16_bytes(N, K)
+    Np = (N + 15) // 16 * 16
+    assert nbytes == Np * K * 2
+    dst = torch.full((Np * K,), 7.0, dtype=torch.bfloat16, device="cuda")
+    B.ssd_pack_bf16(src, dst, N, K)
+    torch.cuda.synchronize()
+    d = dst.cpu().float().numpy()
+    sv = src.cpu().float().numpy()
+    n = np.arange(Np)[:, None]
+    k = np.arange(K)[None, :]
+    idx = ((n // 16) * (K // 32) + k // 32) * 512 + (n % 16) * 32 + k % 32
+    ref = np.zeros((Np, K), np.float32)
+    ref[:N] = sv
+    assert np.array_equal(d[idx], ref)
+    assert torch.equal(sdev.unpack_bf16(dst, N, K), src)
+
+
+def test_pack_bf16_rejects_bad_k():
+    src = torch.zeros(16, 48, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.SSDError) as e:
+        B.ssd_pack_bf16(src, torch.zeros_like(src), 16, 48)
+    assert e.value.code == B.SSD_ERR_SHAPE
