@@ -100,7 +100,8 @@ typedef struct ssd_layer_weights {
  * with x = RMSNorm(h); logits = LMhead·RMSNorm_final(h).  No biases, RoPE with
  * rotate-half pairing (i, i + hd/2), grouped-query attention (query head j uses
  * KV head j / (H / KVH)), attention scale hd^-1/2.
- * Supported: head_dim 64 or 128; D, F multiples of 64; H % KVH == 0. */
+ * Supported: head_dim 64 or 128; D, F multiples of 64; H % KVH == 0, with at
+ * most 64 (fp32) or 16 (bf16) query heads per KV head. */
 typedef struct ssd_model_desc {
   int n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   float rms_eps;            /* e.g. 1e-5 */

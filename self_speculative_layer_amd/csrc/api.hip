@@ -320,6 +320,8 @@ extern "C" int ssd_model_create(const ssd_model_desc* desc, ssd_model** out_mode
   if (d.head_dim != 64 && d.head_dim != 128) return fail(SSD_ERR_SHAPE, "head_dim must be 64 or 128");
   if (d.n_heads % d.n_kv_heads != 0) return fail(SSD_ERR_SHAPE, "n_heads must be a multiple of n_kv_heads");
   if (64 / (d.n_heads / d.n_kv_heads) < 1) return fail(SSD_ERR_SHAPE, "more than 64 query heads per KV head");
+  if (d.dtype == SSD_DTYPE_BF16 && d.n_heads / d.n_kv_heads > 16)
+    return fail(SSD_ERR_SHAPE, "bf16 models: at most 16 query heads per KV head");
   if (d.dtype != SSD_DTYPE_F32 && d.dtype != SSD_DTYPE_BF16) return fail(SSD_ERR_ARG, "bad dtype");
   if (d.dtype == SSD_DTYPE_BF16 &&
       (d.d_model % 64 != 0 || d.ffn_dim % 64 != 0 || (d.n_heads * d.head_dim) % 64 != 0))

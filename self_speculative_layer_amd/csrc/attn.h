@@ -21,8 +21,13 @@ namespace ssd {
 
 constexpr int ATT_SPLIT = 64;
 constexpr int ATT_CHUNK = 64;
-constexpr int ATT_MAXQ = 64;     // queries (rows x heads of a group) per work item
+constexpr int ATT_MAXQ = 64;     // queries (rows x heads of a group) per fp32 work item
+constexpr int ATTB_MAXQ = 16;    // queries per bf16 work item (one matrix-core query tile)
 constexpr int ATT_MAXW = 32;     // splits a block merge can hold (contexts up to 2048 positions)
+
+// Queries (rows x heads of a KV group) one work item takes for storage type T.
+template <typename T>
+constexpr int att_maxq() { return sizeof(T) == 2 ? ATTB_MAXQ : ATT_MAXQ; }
 
 __device__ __forceinline__ size_t kv_index(int page, int L, int layer, int kv, int KVH, int g, int PS, int slot,
                                            int HD) {
@@ -40,20 +45,22 @@ struct AttnSmem {
   int Rpos[ATT_MAXQ];
 };
 
-// bf16 items: K rows give way to the probabilities P[key][query] once the
+// bf16 items: K rows give way to the partial outputs of waves 1..3 once the
 // scores are formed, and to the merge weights in a block merge.
 template <int HD, int NW>
 struct AttnSmem<bf16_t, HD, NW> {
   static constexpr int KST = HD + 8;                // 16-byte aligned rows
   union alignas(16) {
     bf16_t Ks[ATT_CHUNK * KST];
-    float P[ATT_CHUNK * ATT_MAXQ];
-    float Wm[2 * ATT_MAXQ * ATT_MAXW];              // merge: [query][split] weights, then l values
+    float Op[NW][ATTB_MAXQ][HD];                    // each wave's P.V sums of the quads it hands over
+    float Wm[2 * ATTB_MAXQ * ATT_MAXW];             // merge: [query][split] weights, then l values
   };
   alignas(16) bf16_t Vs[ATT_CHUNK * KST];
-  alignas(16) bf16_t Qs[ATT_MAXQ * KST];
-  int Rpos[ATT_MAXQ];
-  float Mx[ATT_MAXQ], Ls[ATT_MAXQ];
+  alignas(16) bf16_t Qs[ATTB_MAXQ * KST];
+  alignas(16) float P[ATT_CHUNK * ATTB_MAXQ];       // probabilities [key][query]
+  float Mw[NW][ATTB_MAXQ], Sw[NW][ATTB_MAXQ];       // per-wave maximum and sum of each query
+  int Rpos[ATTB_MAXQ];
+  float Mx[ATTB_MAXQ], Ls[ATTB_MAXQ];
 };
 
 typedef uint32_t att_u32x4 __attribute__((ext_vector_type(4)));
@@ -74,7 +81,7 @@ __device__ void attn_item_bf16(AttnSmem<bf16_t, HD, NW>& sm, const bf16_t* __res
                                const int* __restrict__ pos, int r0, int RB, int g, int s, int nsplit,
                                const bf16_t* __restrict__ local_kv, int local_start, int group_rows,
                                float* __restrict__ part) {
-  static_assert(NW == 4, "four waves: one 16-query tile each");
+  static_assert(NW == 4, "four waves: 16 keys each");
   constexpr int NT = NW * 64;
   constexpr int KST = AttnSmem<bf16_t, HD, NW>::KST;
   constexpr int VEC = 8;                              // bf16 per 16-byte load
@@ -94,7 +101,7 @@ __device__ void attn_item_bf16(AttnSmem<bf16_t, HD, NW>& sm, const bf16_t* __res
   if (tid < rmax - r0) rp = pos[r0 + tid];
   const int pg0 = key_beg / PS;
   const int pg = (lane * PS < ATT_CHUNK && pg0 + lane < n_lpages) ? page_table[pg0 + lane] : 0;
-  constexpr int QPER = (ATT_MAXQ * VPR + NT - 1) / NT;
+  constexpr int QPER = (ATTB_MAXQ * VPR + NT - 1) / NT;
   const int nq_max = (rmax - r0) * G;
   att_u32x4 qreg[QPER];
 #pragma unroll
@@ -150,92 +157,110 @@ __device__ void attn_item_bf16(AttnSmem<bf16_t, HD, NW>& sm, const bf16_t* __res
   }
   __syncthreads();
 
-  // ---- scores: wave w forms S[key][query] for queries [16 w, 16 w + 16) and all 64 keys;
-  // acc[kt][i] = S[key 16 kt + 4 (lane >> 4) + i][query 16 w + (lane & 15)]
-  const bool qwork = 16 * wave < nq;                  // wave-uniform
+  // ---- scores: wave w forms S[key][query] for its 16 keys [16 w, 16 w + 16) and the (at most 16)
+  // queries; acc[i] = S[key 16 w + 4 (lane >> 4) + i][query lane & 15]
   const int ql = lane & 15, g4 = lane >> 4;
-  f32x4 acc[4];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (qwork) {
+  for (int ds = 0; ds < HD / 32; ++ds) {
+    const bf16x8 bq = *(const bf16x8*)(sm.Qs + ql * KST + 32 * ds + 8 * g4);
+    const bf16x8 ak = *(const bf16x8*)(sm.Ks + (16 * wave + ql) * KST + 32 * ds + 8 * g4);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bq, acc, 0, 0, 0);
+  }
+  // ---- softmax of each query over the split's keys it sees (causal: key position <= its row's):
+  // the maximum over the four waves' keys, then each wave's probabilities and their sum
+  const bool qv = ql < nq;
+  const int prow = qv ? sm.Rpos[ql / G] : -1;
+  float sc[4];
+  float mx = -INFINITY;
 #pragma unroll
-    for (int ds = 0; ds < HD / 32; ++ds) {
-      const bf16x8 bq = *(const bf16x8*)(sm.Qs + (16 * wave + ql) * KST + 32 * ds + 8 * g4);
+  for (int i = 0; i < 4; ++i) {
+    const int kp = key_beg + 16 * wave + 4 * g4 + i;
+    const bool valid = kp < key_end && kp <= prow;
+    sc[i] = valid ? __fmul_rn(acc[i], scale) : -INFINITY;
+    mx = fmaxf(mx, sc[i]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (g4 == 0) sm.Mw[wave][ql] = mx;
+  __syncthreads();                                    // also: every wave is done reading K
+  mx = fmaxf(fmaxf(sm.Mw[0][ql], sm.Mw[1][ql]), fmaxf(sm.Mw[2][ql], sm.Mw[3][ql]));
+  float ps = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8 ak = *(const bf16x8*)(sm.Ks + (16 * kt + ql) * KST + 32 * ds + 8 * g4);
-        acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bq, acc[kt], 0, 0, 0);
+  for (int i = 0; i < 4; ++i) {
+    const float pe = sc[i] == -INFINITY ? 0.f : expf(__fsub_rn(sc[i], mx));
+    sm.P[(16 * wave + 4 * g4 + i) * ATTB_MAXQ + ql] = pe;
+    ps += pe;
+  }
+  ps += __shfl_xor(ps, 16, 64);
+  ps += __shfl_xor(ps, 32, 64);
+  if (g4 == 0) sm.Sw[wave][ql] = ps;
+  if (wave == 0 && g4 == 0) sm.Mx[ql] = mx;
+  __syncthreads();
+
+  // ---- o[query][d]: wave w sums p * v over its 16 keys in order (fp32), lane: dims 2 dp, 2 dp + 1 of
+  // the query quads qh, qh + QS, ...; waves 1..3 hand their sums to wave 0, which adds them in wave order
+  constexpr int DP = HD / 2;                          // dim pairs
+  constexpr int QS = 64 / DP;                         // quad groups per wave (1 at hd 128, 2 at hd 64)
+  constexpr int NQ4 = ATTB_MAXQ / 4 / QS;             // quads per lane
+  const int dp = lane % DP, qh = lane / DP;
+  float o[NQ4][4][2];
+#pragma unroll
+  for (int a = 0; a < NQ4; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[a][j][0] = o[a][j][1] = 0.f;
+#pragma unroll 4
+  for (int kk = 0; kk < 16; ++kk) {
+    const int k = 16 * wave + kk;
+    const uint32_t v2 = *(const uint32_t*)(sm.Vs + k * KST + 2 * dp);
+    const float vlo = __uint_as_float(v2 << 16), vhi = __uint_as_float(v2 & 0xFFFF0000u);
+#pragma unroll
+    for (int a = 0; a < NQ4; ++a) {
+      const f32x4 p4 = *(const f32x4*)(sm.P + k * ATTB_MAXQ + 4 * (qh + QS * a));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[a][j][0] = fmaf(p4[j], vlo, o[a][j][0]);
+        o[a][j][1] = fmaf(p4[j], vhi, o[a][j][1]);
       }
     }
   }
-  __syncthreads();                                    // K is no longer read: P takes its place
-
-  // ---- softmax of each query over the split's keys it sees (causal: key position <= its row's)
-  if (qwork) {
-    const int qq = 16 * wave + ql;
-    const bool qv = qq < nq;
-    const int prow = qv ? sm.Rpos[qq / G] : -1;
-    float sc[4][4];
-    float mx = -INFINITY;
+  // each wave finalises the query quads q4 with q4 % NW == wave (sum in wave order), so every wave hands
+  // the other quads' sums over through LDS
+  float (*Opw)[ATTB_MAXQ][HD] = sm.Op;                // [NW][query][dim] (aliases K)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+  for (int a = 0; a < NQ4; ++a) {
+    const int q4 = qh + QS * a;
+    if ((q4 % NW) == wave) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kp = key_beg + 16 * kt + 4 * g4 + i;
-        const bool valid = kp < key_end && kp <= prow;
-        sc[kt][i] = valid ? __fmul_rn(acc[kt][i], scale) : -INFINITY;
-        mx = fmaxf(mx, sc[kt][i]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float ps = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pe = sc[kt][i] == -INFINITY ? 0.f : expf(__fsub_rn(sc[kt][i], mx));
-        sm.P[(16 * kt + 4 * g4 + i) * ATT_MAXQ + qq] = pe;
-        ps += pe;
-      }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    if (g4 == 0) {
-      sm.Mx[qq] = mx;
-      sm.Ls[qq] = ps;
+    for (int j = 0; j < 4; ++j) {
+      Opw[wave][4 * q4 + j][2 * dp] = o[a][j][0];
+      Opw[wave][4 * q4 + j][2 * dp + 1] = o[a][j][1];
     }
   }
   __syncthreads();
-
-  // ---- o[query][d] = sum over keys in order of p * v (fp32); thread: dims 2 dp, 2 dp + 1 of query quads
-  constexpr int DP = HD / 2, QG = NT / DP;
-  const int dp = tid % DP, qg = tid / DP;
-  for (int quad = qg; 4 * quad < nq; quad += QG) {
-    float o[4][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j][0] = o[j][1] = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < ATT_CHUNK; ++k) {
-      const uint32_t v2 = *(const uint32_t*)(sm.Vs + k * KST + 2 * dp);
-      const f32x4 p4 = *(const f32x4*)(sm.P + k * ATT_MAXQ + 4 * quad);
-      const float vlo = __uint_as_float(v2 << 16), vhi = __uint_as_float(v2 & 0xFFFF0000u);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o[j][0] = fmaf(p4[j], vlo, o[j][0]);
-        o[j][1] = fmaf(p4[j], vhi, o[j][1]);
-      }
-    }
+  for (int a = 0; a < NQ4; ++a) {
+    const int q4 = qh + QS * a;
+    if ((q4 % NW) != wave) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int qq = 4 * quad + j;
-      if (qq >= nq) break;
+      const int qq = 4 * q4 + j;
+      if (qq >= nq) continue;
       if (key_beg > sm.Rpos[qq / G]) continue;        // the row sees no key of this split
+      float olo = 0.f, ohi = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        olo += w == wave ? o[a][j][0] : Opw[w][qq][2 * dp];
+        ohi += w == wave ? o[a][j][1] : Opw[w][qq][2 * dp + 1];
+      }
       const int row = r0 + qq / G, head = g * G + qq % G;
       float* dstp = part + (((size_t)row * H + head) * nsplit + s) * (HD + 2);
-      part_store<DEV>(dstp + 2 * dp, o[j][0]);
-      part_store<DEV>(dstp + 2 * dp + 1, o[j][1]);
+      part_store<DEV>(dstp + 2 * dp, olo);
+      part_store<DEV>(dstp + 2 * dp + 1, ohi);
       if (dp == 0) {
+        const float l = ((sm.Sw[0][qq] + sm.Sw[1][qq]) + sm.Sw[2][qq]) + sm.Sw[3][qq];
         part_store<DEV>(dstp + HD, sm.Mx[qq]);
-        part_store<DEV>(dstp + HD + 1, sm.Ls[qq]);
+        part_store<DEV>(dstp + HD + 1, l);
       }
     }
   }
@@ -461,8 +486,8 @@ __device__ __forceinline__ float attn_combine_value(const float* __restrict__ pa
 // of KV head g), once every split has stored its partial (positions from
 // sm.Rpos, at most ATT_MAXW splits).  Same arithmetic as attn_combine_value,
 // with each (query, split) weight formed once: (1) every pair's m and l,
-// (2) per query the maximum, the weights and l in split order, (3) per output
-// element the weighted sum of the splits' o in split order over l.  The o
+// (2) per query the maximum and the weights, (3) per output element the
+// weighted sums of the splits' o and l in split order, and their quotient.  The o
 // values of the first MP dim pairs per thread are loaded together with (1).
 // The output is in the decode block layout.
 template <int HD, int NW>
@@ -473,12 +498,12 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
   constexpr int PR = HD / 2;                          // dim pairs per query
   constexpr int CH = 16;                              // splits per load round of (3)
   constexpr int MP = 4;                               // dim pairs per thread in the first round
-  constexpr int P1 = ATT_MAXQ * ATT_MAXW / NT;
+  constexpr int P1 = ATTB_MAXQ * ATT_MAXW / NT;
   const int tid = threadIdx.x;
   const int nq = (r1 - r0) * G;
   const int npair = nq * PR;
   float* Wt = sm.Wm;                                  // [query][split]: m, then the weight
-  float* Lv = sm.Wm + ATT_MAXQ * ATT_MAXW;            // [query][split]: l
+  float* Lv = sm.Wm + ATTB_MAXQ * ATT_MAXW;           // [query][split]: l
   auto rec = [&](int qq, int sp) -> const float* {
     return part + (((size_t)(r0 + qq / G) * H + g * G + qq % G) * nsplit + sp) * REC;
   };
@@ -517,23 +542,26 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
     }
   }
   __syncthreads();
-  // (2)
-  if (tid < nq) {
-    const int ns = nsplits(tid);
-    float m = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, Wt[tid * ATT_MAXW + sp]);
-    float l = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
-      const float w = expf(__fsub_rn(Wt[tid * ATT_MAXW + sp], m));
-      Wt[tid * ATT_MAXW + sp] = w;
-      l = fmaf(Lv[tid * ATT_MAXW + sp], w, l);
+  // (2) per query the maximum of its splits' m and the weights; a wave takes two queries at a time
+  // (lanes 0-31 and 32-63, lane = split).  l is accumulated in (3), next to o, in split order.
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    static_assert(ATT_MAXW <= 32, "one half-wave lane per split");
+    for (int q0 = 2 * wave; q0 < nq; q0 += 2 * NW) {
+      const int qq = q0 + (lane >> 5), sp = lane & 31;
+      const bool on = qq < nq && sp < nsplits(min(qq, nq - 1));
+      const float mv = on ? Wt[qq * ATT_MAXW + sp] : -INFINITY;
+      float m = mv;
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+      if (on) Wt[qq * ATT_MAXW + sp] = expf(__fsub_rn(mv, m));
     }
-    sm.Ls[tid] = l;
   }
   __syncthreads();
-  // (3): splits [c0, ns) of one dim pair, accumulated into o; then the store
-  auto rest = [&](int qq, int d2, int ns, int c0, float2& o) {
+  // (3): splits [c0, ns) of one dim pair accumulated into o, and l; then the store
+  auto rest = [&](int qq, int d2, int ns, int c0, float2& o, float& l) {
     const float* w = Wt + qq * ATT_MAXW;
+    const float* lw = Lv + qq * ATT_MAXW;
     for (; c0 < ns; c0 += CH) {
       float2 v[CH];
 #pragma unroll
@@ -541,15 +569,15 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         if (c0 + c < ns) {
+          l = fmaf(lw[c0 + c], w[c0 + c], l);
           o.x = fmaf(v[c].x, w[c0 + c], o.x);
           o.y = fmaf(v[c].y, w[c0 + c], o.y);
         }
       }
     }
   };
-  auto store = [&](int qq, int d2, float2 o) {
+  auto store = [&](int qq, int d2, float2 o, float l) {
     const int row = r0 + qq / G, head = g * G + qq % G;
-    const float l = sm.Ls[qq];
     bf16_t* dst = out + dec_act_index(row, head * HD + d2);   // d2 even: d2 + 1 is the next element
     st(dst, __fdiv_rn(o.x, l));
     st(dst + 1, __fdiv_rn(o.y, l));
@@ -560,23 +588,27 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
     if (pi < npair) {
       const int qq = pi / PR, d2 = (pi % PR) * 2, ns = nsplits(qq);
       const float* w = Wt + qq * ATT_MAXW;
+      const float* lw = Lv + qq * ATT_MAXW;
       float2 o = make_float2(0.f, 0.f);
+      float l = 0.f;
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         if (c < ns) {
+          l = fmaf(lw[c], w[c], l);
           o.x = fmaf(ov[x][c].x, w[c], o.x);
           o.y = fmaf(ov[x][c].y, w[c], o.y);
         }
       }
-      rest(qq, d2, ns, CH, o);
-      store(qq, d2, o);
+      rest(qq, d2, ns, CH, o, l);
+      store(qq, d2, o, l);
     }
   }
   for (int pi = tid + NT * MP; pi < npair; pi += NT) {
     const int qq = pi / PR, d2 = (pi % PR) * 2;
     float2 o = make_float2(0.f, 0.f);
-    rest(qq, d2, nsplits(qq), 0, o);
-    store(qq, d2, o);
+    float l = 0.f;
+    rest(qq, d2, nsplits(qq), 0, o, l);
+    store(qq, d2, o, l);
   }
 }
 

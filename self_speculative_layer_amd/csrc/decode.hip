@@ -362,7 +362,7 @@ int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv,
                          unsigned* counters, const int* stop, hipStream_t s) {
   if (M <= 0) return 0;
   const int G = H / KVH;
-  const int RB = ATT_MAXQ / G;
+  const int RB = ATTB_MAXQ / G;
   if (RB < 1 || M > 16) return SSD_ERR_SHAPE;
   const int nsplit = attention_nsplit(max_ctx);
   if (nsplit > ATT_MAXW) {

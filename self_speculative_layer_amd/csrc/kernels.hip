@@ -438,7 +438,7 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
   if (rb.M <= 0) return 0;
   if (out_blocked && rb.M > 16) return SSD_ERR_SHAPE;
   const int G = H / KVH;
-  int RB = ATT_MAXQ / G;
+  int RB = (dtype == SSD_DTYPE_BF16 ? ATTB_MAXQ : ATT_MAXQ) / G;
   if (RB < 1) return SSD_ERR_SHAPE;
   if (group_rows > 0) {
     // a row block must not straddle two groups
