@@ -23,7 +23,7 @@ constexpr int ATT_SPLIT = 64;
 constexpr int ATT_CHUNK = 64;
 constexpr int ATT_MAXQ = 64;     // queries (rows x heads of a group) per fp32 work item
 constexpr int ATTB_MAXQ = 16;    // queries per bf16 work item (one matrix-core query tile)
-constexpr int ATT_MAXW = 32;     // splits a block merge can hold (contexts up to 2048 positions)
+constexpr int ATT_MAXW = 64;     // splits a block merge can hold (contexts up to 4096 positions)
 
 // Queries (rows x heads of a KV group) one work item takes for storage type T.
 template <typename T>
@@ -507,7 +507,7 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
   auto rec = [&](int qq, int sp) -> const float* {
     return part + (((size_t)(r0 + qq / G) * H + g * G + qq % G) * nsplit + sp) * REC;
   };
-  auto nsplits = [&](int qq) { return sm.Rpos[qq / G] / ATT_SPLIT + 1; };
+  auto nsplits = [&](int qq) { return min(sm.Rpos[qq / G] / ATT_SPLIT + 1, nsplit); };
 
   // loads of (1) and of the first round of (3)
   float mv[P1], lv[P1];
@@ -542,19 +542,18 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
     }
   }
   __syncthreads();
-  // (2) per query the maximum of its splits' m and the weights; a wave takes two queries at a time
-  // (lanes 0-31 and 32-63, lane = split).  l is accumulated in (3), next to o, in split order.
+  // (2) per query the maximum of its splits' m and the weights; a wave takes one query at a time
+  // (lane = split).  l is accumulated in (3), next to o, in split order.
   {
     const int lane = tid & 63, wave = tid >> 6;
-    static_assert(ATT_MAXW <= 32, "one half-wave lane per split");
-    for (int q0 = 2 * wave; q0 < nq; q0 += 2 * NW) {
-      const int qq = q0 + (lane >> 5), sp = lane & 31;
-      const bool on = qq < nq && sp < nsplits(min(qq, nq - 1));
-      const float mv = on ? Wt[qq * ATT_MAXW + sp] : -INFINITY;
+    static_assert(ATT_MAXW <= 64, "one lane per split");
+    for (int qq = wave; qq < nq; qq += NW) {
+      const bool on = lane < nsplits(qq);
+      const float mv = on ? Wt[qq * ATT_MAXW + lane] : -INFINITY;
       float m = mv;
 #pragma unroll
-      for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
-      if (on) Wt[qq * ATT_MAXW + sp] = expf(__fsub_rn(mv, m));
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      if (on) Wt[qq * ATT_MAXW + lane] = expf(__fsub_rn(mv, m));
     }
   }
   __syncthreads();

@@ -108,6 +108,23 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   }
   const bf16_t* xp = a.X + dec_act_index(min(r, Ma - 1), g * 8);   // step t: xp + 512 t
 
+  // Epilogue operands that do not depend on the product (the residual element and the next gain; the
+  // row's position) are loaded ahead of the weight stream, so that the tail after the reduction holds
+  // no dependent global loads.  Thread (erow, enn) of the epilogue; clamped rows are not stored.
+  const int erow = min((int)threadIdx.x >> 4, Ma - 1), enn = threadIdx.x & 15;
+  float eh[TPW], eg[TPW];
+  int epos = 0;
+  if constexpr (EPI == DEC_RESID) {
+    const float* gsrc = a.gain_next ? a.gain_next : a.Y;     // unconditional load; unused without gain_next
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int col = dec_tile<EPI, HALF>(a, min((int)blockIdx.x * TPW + j, a.n_tiles - 1)).f0 + enn;
+      eh[j] = a.Y[(size_t)erow * a.ldy + col];
+      eg[j] = gsrc[col];
+    }
+  }
+  if constexpr (EPI == DEC_QKV) epos = a.pos[erow];
+
   // RMS tile sums of the rows this wave scales: loaded first, summed after the weight loads are issued
   __shared__ float sinv[16];
   const int nts = K / 16;
@@ -148,6 +165,20 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, WAVE);
       if (row < Ma && lane == 0) sinv[row] = inv_rms(acc, K, a.eps);
+    }
+  }
+  // QKV: the row's page and rotation, issued behind the first weight steps (only the position load
+  // is waited for here)
+  float2 ecs[TPW];
+  int epage = 0;
+  if constexpr (EPI == DEC_QKV) {
+    const int lp = epos / a.PS;
+    const bool ok = epos >= 0 && lp < a.n_lpages;
+    epage = a.page_table[ok ? lp : 0];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const DecTile t = dec_tile<EPI, HALF>(a, min((int)blockIdx.x * TPW + j, a.n_tiles - 1));
+      ecs[j] = a.rope_cs[(size_t)(ok ? epos : 0) * (a.HD / 2) + t.d0 + (HALF ? (enn & 7) : enn)];
     }
   }
 
@@ -214,11 +245,10 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       if (t.f0 + nn < a.N) a.Y[(size_t)row * a.ldy + t.f0 + nn] = __fmul_rn(s, sinv[row]);
     } else if constexpr (EPI == DEC_RESID) {
       const int col = t.f0 + nn;
-      float* hp = a.Y + (size_t)row * a.ldy + col;
-      const float hn = __fadd_rn(*hp, s);
-      *hp = hn;
+      const float hn = __fadd_rn(eh[j], s);
+      a.Y[(size_t)row * a.ldy + col] = hn;
       if (a.gain_next) {
-        st(a.xg_next + dec_act_index(row, col), __fmul_rn(hn, a.gain_next[col]));
+        st(a.xg_next + dec_act_index(row, col), __fmul_rn(hn, eg[j]));
         const float tt = tile16_ss_lanes(hn);
         if (nn == 0) a.ss_next[(size_t)row * (a.N / 16) + col / 16] = tt;
       }
@@ -230,7 +260,7 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       const float x1 = __fmul_rn(s, inv), x2 = __fmul_rn(s2, inv);
       const int HD = a.HD, H = a.H, KVH = a.KVH;
       const int i = t.d0 + nn;                  // pair index
-      const int p = a.pos[row];
+      const int p = epos;                       // row == erow here (row < Ma)
       const int lp = p / a.PS;
       if (p < 0 || lp >= a.n_lpages) {
         if (nn == 0) atomicOr(a.err, ERRF_CAPACITY);
@@ -242,11 +272,11 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       } else {
         const int kvsel = t.slot < H + KVH ? 0 : 1;
         const int gg = t.slot - H - kvsel * KVH;
-        dst = a.pool + kv_index(a.page_table[lp], a.L, a.layer, kvsel, KVH, gg, a.PS, p % a.PS, HD);
+        dst = a.pool + kv_index(epage, a.L, a.layer, kvsel, KVH, gg, a.PS, p % a.PS, HD);
       }
       if (t.slot < H + KVH) {
         float y1, y2;
-        rope_apply(x1, x2, a.rope_cs[(size_t)p * (HD / 2) + i], y1, y2);
+        rope_apply(x1, x2, ecs[j], y1, y2);
         st(dst + i, y1);
         st(dst + i + HD / 2, y2);
       } else {
@@ -337,7 +367,7 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(
   const int Ma = nrows ? min(M, *nrows) : M;
   const int r0 = rbk * RB, r1 = min(r0 + RB, Ma);
   if (r1 <= r0) return;
-  const int n_act = pos[r1 - 1] / ATT_SPLIT + 1;     // splits holding a key some row of the block sees
+  const int n_act = min(pos[r1 - 1] / ATT_SPLIT + 1, nsplit);   // splits holding a key some row of the block sees
   if (s >= n_act) return;
   __shared__ AttnSmem<T, HD, 4> sm;
   __shared__ int is_last;
