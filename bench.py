@@ -64,6 +64,14 @@ WORKLOADS = {
 }
 
 
+SCORING = {
+    "score13b": dict(shape="llama2-13b-shape", prompt=1024, gamma=32, n_masks=16, skip_lo=16, skip_hi=24,
+                     desc="LLaMA-2-13B-shaped bf16 decoder, SWIFT matchness scoring of 16 seeded candidate plans "
+                          "(16-24 of 40 layers skipped each) over a 32-token window greedily generated after a "
+                          "1024-token random prompt"),
+}
+
+
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
@@ -133,9 +141,9 @@ def cpu_baseline(shape, wl, mask, max_seconds=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=None, help="default 64 (SSD steps), 8 (scoring steps)")
+    ap.add_argument("--warmup", type=int, default=None, help="default 8 (SSD steps), 2 (scoring steps)")
+    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS) + sorted(SCORING))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ar-steps", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -162,6 +170,13 @@ def main():
     from synth import device as sdev
     from self_speculative_layer_amd import binding as B
 
+    if args.workload in SCORING:
+        args.steps = 8 if args.steps is None else args.steps
+        args.warmup = 2 if args.warmup is None else args.warmup
+        run_scoring(args)
+        return
+    args.steps = 64 if args.steps is None else args.steps
+    args.warmup = 8 if args.warmup is None else args.warmup
     wl = WORKLOADS[args.workload]
     shape = synth.SHAPES[wl["shape"]]
     torch.cuda.set_device(0)
@@ -294,6 +309,99 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shape, wl, mask)
+    print(json.dumps(result), flush=True)
+
+
+def run_scoring(args):
+    """One step = one ssd_score_masks call: every candidate plan's draft over the
+    window rows in one batched pass (rows of the candidates that keep a sub-layer
+    go through it together), the LM head, row statistics and the matchness
+    scores.  The dominant kernel is the batched gate/up projection; its
+    launches are timed with dispatch events in K further steps."""
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import device as sdev
+    from self_speculative_layer_amd import binding as B
+
+    wl = SCORING[args.workload]
+    shape = synth.SHAPES[wl["shape"]]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    tensors = sdev.build_weights(shape)
+    torch.cuda.synchronize()
+    log("weights on device in %.1fs" % (time.time() - t0))
+    model = B.Model(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
+                    shape.vocab, shape.dtype, tensors)
+    P, gamma, nm = wl["prompt"], wl["gamma"], wl["n_masks"]
+    masks = synth.scoring_masks(shape.n_layers, nm, wl["skip_lo"], wl["skip_hi"])
+    seq = B.Sequence(model, max_ctx=P + gamma + 64, max_rows=nm * gamma, max_draft=1, device=dev)
+    prompt = torch.from_numpy(synth.prompt_tokens(P, shape.vocab)).to(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    B.ssd_prefill(seq.handle, prompt)
+    ev1.record()
+    torch.cuda.synchronize()
+    prefill_ms = ev0.elapsed_time(ev1)
+    for _ in range(gamma - 1):
+        B.ssd_decode_ar(seq.handle, 0.0, 0)
+    gen = B.ssd_read_output(seq.handle, gamma)
+    window = torch.tensor([int(prompt[-1])] + [int(x) for x in gen], dtype=torch.int32, device=dev)
+    scores = torch.zeros(nm, dtype=torch.float32, device=dev)
+    best = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step():
+        B.ssd_score_masks(seq.handle, masks, window, P - 1, gamma, scores, best)
+
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(K):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / K
+    # measured region: the batched gate/up launches with dispatch events
+    keep_mlp = (masks[:, 1::2] == 0).sum(axis=0)           # candidates running each layer's MLP
+    n_gu = int((keep_mlp > 0).sum())
+    B.ssd_profile_enable(B.SSD_PROF_GEMM_SWIGLU, K * n_gu + 8)
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    B.ssd_profile_disable()
+    prof_ms, prof_n, prof_bytes = B.ssd_profile_read()
+    D, F = shape.d_model, shape.ffn_dim
+    flops = float(sum(2.0 * (c * gamma) * 2 * F * D for c in keep_mlp if c > 0)) * K
+    gu_ms = prof_ms
+    tflops = flops / (gu_ms / 1e3) / 1e12 if gu_ms > 0 else 0.0
+    gbps = prof_bytes / (gu_ms / 1e3) / 1e9 if gu_ms > 0 else 0.0
+    ai = flops / prof_bytes if prof_bytes > 0 else 0.0
+    mfma_bound = ai * HBM_PEAK_GBPS * 1e9 > 2.5e15          # above the bf16 ridge: compute-bound
+    log("scoring step %.2f ms; gate/up launches %d, %.1f us avg, %.1f TFLOP/s, %.0f GB/s (AI %.0f flop/B)"
+        % (ms, prof_n, prof_ms / max(prof_n, 1) * 1e3, tflops, gbps, ai))
+    roof = ({"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+             "frac": round(tflops / 2500.0, 4)} if mfma_bound else
+            {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+    roof.update({"traffic": None, "kernel": "gemm_bf16 gate/up + SwiGLU over the candidates' rows",
+                 "launches": prof_n, "avg_launch_us": round(prof_ms / max(prof_n, 1) * 1e3, 3),
+                 "flop_per_step": flops / K, "bytes_per_launch": round(prof_bytes / max(prof_n, 1)),
+                 "measured": "dispatch-timestamp events on every launch of the kernel in %d further steps" % K})
+    result = {
+        "metric": "mask-scoring steps/s (16 candidate plans x 32-token window)",
+        "value": round(1e3 / ms, 4), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded random-init weights, uniform random prompt, seeded masks)",
+        "config": {"workload": wl["desc"], "prompt_len": P, "gamma": gamma, "n_masks": nm},
+        "roofline": roof, "scores": [round(float(x), 5) for x in scores.cpu()], "best": int(best.item()),
+        "prefill_ms": round(prefill_ms, 2),
+    }
+    seq.close()
+    model.close()
     print(json.dumps(result), flush=True)
 
 

@@ -12,7 +12,7 @@ FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17", "-Wall", "-Wno-u
 
 # Kernels that must not use scratch (private) memory: the decode-block
 # projections and attention keep every value in registers / LDS.
-NO_SCRATCH = {"decode.hip": ("dec_gemm_kernel", "attn_dec_kernel")}
+NO_SCRATCH = {"decode.hip": ("dec_gemm_kernel", "attn_dec_kernel"), "kernels.hip": ("gemm_bf16_tiled",)}
 
 
 def _check_no_scratch(src, remarks):

@@ -172,6 +172,172 @@ __global__ __launch_bounds__(256) void gemm_f32_rows16(
   }
 }
 
+// ===========================================================================
+// Linear layers, bf16, for blocks of many rows (prefill, mask scoring): a
+// workgroup owns 128 W rows (SwiGLU: 64 gate rows and the same 64 up rows) and
+// 128 activation rows.  K goes through LDS in 64-element slabs, double
+// buffered (global loads of slab t + 1 in flight while slab t feeds the matrix
+// cores); W slabs keep the packed 16 x 32 tiles, activation slabs are stored in
+// the same tile shape, so every fragment read is one contiguous 1 KB tile.
+// Each wave forms a 64 x 64 quadrant: 4 x 4 v_mfma_f32_16x16x32_bf16 blocks.
+// The arithmetic of an output element is that of gemm_bf16_rows16 and of the
+// decode projections: the K quarters of the four-wave split (same boundaries)
+// are each accumulated from zero by the MFMA chain in k order, and the quarter
+// sums are added in quarter order.  A row's result is the same bits in all
+// three kernels.
+// ===========================================================================
+
+constexpr int TG_W = 128;            // W rows per workgroup
+constexpr int TG_M = 128;            // activation rows per workgroup
+constexpr int TG_KS = 64;            // K elements per LDS slab
+constexpr int TG_MIN_ROWS = 64;      // row counts from which launch_linear takes this kernel
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_tiled(
+    const bf16_t* __restrict__ W, const bf16_t* __restrict__ X, int ldx, int M, int N, int K,
+    float* __restrict__ Y, int ldy, bf16_t* __restrict__ A, int lda, int n_mb, const float* __restrict__ rscale,
+    const int* __restrict__ nrows, const int* __restrict__ ymap, const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  const int Ma = active_rows(M, nrows);
+  const int mb = blockIdx.x % n_mb, nb = blockIdx.x / n_mb;
+  const int m0 = mb * TG_M;
+  if (m0 >= Ma) return;
+  __shared__ alignas(16) bf16_t Ws[2][TG_W * TG_KS];     // [row tile 0..7][k tile 0..1][16][32]
+  __shared__ alignas(16) bf16_t Xs[2][TG_M * TG_KS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+  const int r = lane & 15, g = lane >> 4;
+  const int ktiles = K / 32;
+  const int n_wtiles = (N + 15) / 16;                     // packed tiles per W row set
+
+  // global packed tile (row tile index) of local W row tile t (0..7)
+  auto wtile = [&](int t) -> int {
+    if (SW) return t < 4 ? 4 * nb + t : n_wtiles + 4 * nb + (t - 4);   // gate f0.., then up N + f0..
+    return min(8 * nb + t, n_wtiles - 1);                               // tiles past N repeat the last
+  };
+  // staging: thread tid loads 4 x 16 B of W (tiles (tid >> 6) + 4 j, lane offset) and 4 x 16 B of X
+  // (rows (tid >> 3) + 32 j, chunk tid & 7)
+  const bf16_t* wsrc[4];
+  int wdst[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int id = (tid >> 6) + 4 * j;                    // local tile id = row tile * 2 + k tile
+    wsrc[j] = W + ((size_t)wtile(id >> 1) * ktiles + (id & 1)) * 512 + lane * 8;
+    wdst[j] = id * 512 + lane * 8;
+  }
+  const bf16_t* xsrc[4];
+  int xdst[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (tid >> 3) + 32 * j, c = tid & 7;
+    xsrc[j] = X + (size_t)min(m0 + row, Ma - 1) * ldx + 8 * c;
+    xdst[j] = (((row >> 4) * 2 + (c >> 2)) * 512) + (row & 15) * 32 + (c & 3) * 8;
+  }
+  u32x4 wreg[4], xreg[4];
+  auto gload = [&](int sl) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wreg[j] = *(const u32x4*)(wsrc[j] + (size_t)sl * 1024);     // slab sl = k tiles 2 sl, 2 sl + 1
+      xreg[j] = *(const u32x4*)(xsrc[j] + (size_t)sl * TG_KS);
+    }
+  };
+  auto lstore = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *(u32x4*)(Ws[b] + wdst[j]) = wreg[j];
+      *(u32x4*)(Xs[b] + xdst[j]) = xreg[j];
+    }
+  };
+
+  // this wave's W row tiles (A fragments) and activation row tiles (B fragments)
+  int at[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) at[i] = SW ? (i < 2 ? 2 * wn + i : 4 + 2 * wn + (i - 2)) : 4 * wn + i;
+  f32x4 acc[4][4], sum[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = sum[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nu = K / TG_KS;                               // slabs (= 64-element units)
+  int qend = nu / 4;                                      // end of quarter q: (nu (q + 1)) / 4
+  int q = 0;
+  auto close_quarters = [&](int sl) {                     // quarters ending at slab sl (empty ones add zero)
+    while (q < 4 && qend <= sl) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sum[i][j] += acc[i][j];
+          acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      ++q;
+      qend = (nu * (q + 1)) / 4;
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int sl = 0; sl < nu; ++sl) {
+    const int b = sl & 1;
+    if (sl + 1 < nu) gload(sl + 1);
+    close_quarters(sl);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(Ws[b] + (at[i] * 2 + kt) * 512 + r * 32 + g * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = *(const bf16x8*)(Xs[b] + ((4 * wm + j) * 2 + kt) * 512 + r * 32 + g * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (sl + 1 < nu) lstore(b ^ 1);
+    __syncthreads();
+  }
+  close_quarters(nu);
+
+  // acc layout: lane (r, g) holds D[feature 4 g + e][row r] of each 16 x 16 block
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = m0 + 16 * (4 * wm + j) + r;
+    if (row >= Ma) continue;
+    const float rs = (rscale && EPI != EPI_RESID) ? rscale[row] : 1.f;
+    const int yrow = ymap ? ymap[row] : row;
+    if constexpr (SW) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = 64 * nb + 16 * (2 * wn + i) + 4 * g + e;
+          float s1 = sum[i][j][e], s2 = sum[i + 2][j][e];
+          if (rscale) { s1 = __fmul_rn(s1, rs); s2 = __fmul_rn(s2, rs); }
+          A[(size_t)row * lda + col] = f2bf(swiglu(s1, s2));
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = 128 * nb + 16 * (4 * wn + i) + 4 * g + e;
+          if (col >= N) continue;
+          float v = sum[i][j][e];
+          if (EPI == EPI_STORE) {
+            if (rscale) v = __fmul_rn(v, rs);
+            Y[(size_t)yrow * ldy + col] = v;
+          } else {
+            Y[(size_t)yrow * ldy + col] = __fadd_rn(Y[(size_t)yrow * ldy + col], v);
+          }
+        }
+    }
+  }
+}
+
 bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop);
 void profile_done(double bytes);
 static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
@@ -183,13 +349,30 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
                   float* Y, int ldy, void* A, int lda, const float* rscale, const int* nrows, const int* ymap,
                   const int* stop, hipStream_t s) {
   if (M <= 0 || N <= 0) return 0;
-  const int n_rb = (M + 15) / 16;
-  const int n_tiles = (N + 15) / 16;
-  const dim3 grid(n_rb * n_tiles);
   hipEvent_t e0 = nullptr, e1 = nullptr;
   const bool prof = profile_next(epi, &e0, &e1);
-  const int rc = launch_linear_impl(dtype, epi, W, X, ldx, M, N, K, Y, ldy, A, lda, n_rb, grid, rscale, nrows, ymap,
-                                    stop, e0, e1, s);
+  int rc;
+  if (dtype == SSD_DTYPE_BF16 && M >= TG_MIN_ROWS && K % TG_KS == 0 && (epi != EPI_SWIGLU || N % 64 == 0)) {
+    const int n_mb = (M + TG_M - 1) / TG_M;
+    const int n_nb = epi == EPI_SWIGLU ? N / 64 : (N + TG_W - 1) / TG_W;
+    const dim3 grid(n_mb * n_nb);
+    const bf16_t* w = (const bf16_t*)W;
+    const bf16_t* x = (const bf16_t*)X;
+#define TILED(E)                                                                                                  \
+  hipExtLaunchKernelGGL(gemm_bf16_tiled<E>, grid, dim3(256), 0, s, e0, e1, 0, w, x, ldx, M, N, K, Y, ldy, (bf16_t*)A, \
+                        lda, n_mb, rscale, nrows, ymap, stop)
+    if (epi == EPI_STORE) TILED(EPI_STORE);
+    else if (epi == EPI_RESID) TILED(EPI_RESID);
+    else TILED(EPI_SWIGLU);
+#undef TILED
+    rc = last_launch();
+  } else {
+    const int n_rb = (M + 15) / 16;
+    const int n_tiles = (N + 15) / 16;
+    const dim3 grid(n_rb * n_tiles);
+    rc = launch_linear_impl(dtype, epi, W, X, ldx, M, N, K, Y, ldy, A, lda, n_rb, grid, rscale, nrows, ymap, stop,
+                            e0, e1, s);
+  }
   if (prof) {
     // algorithmic bytes: weights once, activations in once, results out once (residual: read + write)
     const double elt = dtype == SSD_DTYPE_BF16 ? 2.0 : 4.0;

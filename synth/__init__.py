@@ -199,6 +199,14 @@ def random_skip_layers(n_layers, n_skip, seed, index=0):
     return sorted(chosen)
 
 
+def scoring_masks(n_layers, n_masks, lo, hi, seed=SEED_MASKS):
+    """Candidate skip masks for mask scoring: candidate c skips a seeded uniform
+    subset of k_c layers, k_c uniform over [lo, hi]."""
+    ks = tokens_host(n_masks, 0x4E000000, hi - lo + 1, seed=seed) + lo
+    return np.stack([mask_from_layers(n_layers, random_skip_layers(n_layers, int(k), seed, index=c + 1))
+                     for c, k in enumerate(ks)])
+
+
 def mask_from_layers(n_layers, layers):
     """uint8[2L] skip mask: bit pair (2l, 2l+1) = (attention, MLP) of layer l skipped."""
     m = np.zeros(2 * n_layers, np.uint8)
