@@ -175,11 +175,12 @@ __global__ __launch_bounds__(256) void gemm_f32_rows16(
 // ===========================================================================
 // Linear layers, bf16, for blocks of many rows (prefill, mask scoring): a
 // workgroup owns 128 W rows (SwiGLU: 64 gate rows and the same 64 up rows) and
-// 128 activation rows.  K goes through LDS in 64-element slabs, double
-// buffered (global loads of slab t + 1 in flight while slab t feeds the matrix
-// cores); W slabs keep the packed 16 x 32 tiles, activation slabs are stored in
-// the same tile shape, so every fragment read is one contiguous 1 KB tile.
-// Each wave forms a 64 x 64 quadrant: 4 x 4 v_mfma_f32_16x16x32_bf16 blocks.
+// 128 activation rows.  K goes through LDS in 64-element slabs with TG_NST
+// slabs in flight: the loads write LDS directly (global_load_lds_dwordx4, one
+// 1 KB tile per wave instruction), so no registers hold data in transit.  W
+// slabs keep the packed 16 x 32 tiles and activation slabs are stored in the
+// same tile shape, so every fragment read is one contiguous 1 KB tile.  Each
+// wave forms a 64 x 64 quadrant: 4 x 4 v_mfma_f32_16x16x32_bf16 blocks.
 // The arithmetic of an output element is that of gemm_bf16_rows16 and of the
 // decode projections: the K quarters of the four-wave split (same boundaries)
 // are each accumulated from zero by the MFMA chain in k order, and the quarter
@@ -190,7 +191,18 @@ __global__ __launch_bounds__(256) void gemm_f32_rows16(
 constexpr int TG_W = 128;            // W rows per workgroup
 constexpr int TG_M = 128;            // activation rows per workgroup
 constexpr int TG_KS = 64;            // K elements per LDS slab
+constexpr int TG_NST = 2;            // slabs in flight (LDS buffers; 64 KB: two workgroups per CU)
 constexpr int TG_MIN_ROWS = 64;      // row counts from which launch_linear takes this kernel
+
+typedef __attribute__((address_space(3))) void tg_lds_t;
+typedef __attribute__((address_space(1))) const void tg_gbl_t;
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds wave-uniform).
+__device__ __forceinline__ void tg_load_lds(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((tg_gbl_t*)src, (tg_lds_t*)lds, 16, 0, 0);
+}
+// Workgroup barrier without a memory fence: the waits for the slab loads are explicit.
+__device__ __forceinline__ void tg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_tiled(
@@ -200,11 +212,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
   if (stop && *stop) return;
   constexpr bool SW = EPI == EPI_SWIGLU;
   const int Ma = active_rows(M, nrows);
-  const int mb = blockIdx.x % n_mb, nb = blockIdx.x / n_mb;
+  // workgroup i runs on XCD i % 8: consecutive logical blocks (the row blocks of one W tile) are placed
+  // on one XCD, so that they share its L2 for the W slabs
+  const int nblk = gridDim.x;
+  const int lb = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int mb = lb % n_mb, nb = lb / n_mb;
   const int m0 = mb * TG_M;
   if (m0 >= Ma) return;
-  __shared__ alignas(16) bf16_t Ws[2][TG_W * TG_KS];     // [row tile 0..7][k tile 0..1][16][32]
-  __shared__ alignas(16) bf16_t Xs[2][TG_M * TG_KS];
+  // per stage: W tiles [row tile 0..7][k tile 0..1][16][32], then the activation tiles in the same shape
+  __shared__ alignas(16) bf16_t Ls[TG_NST][2 * TG_W * TG_KS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
@@ -217,41 +233,27 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
     if (SW) return t < 4 ? 4 * nb + t : n_wtiles + 4 * nb + (t - 4);   // gate f0.., then up N + f0..
     return min(8 * nb + t, n_wtiles - 1);                               // tiles past N repeat the last
   };
-  // staging: thread tid loads 4 x 16 B of W (tiles (tid >> 6) + 4 j, lane offset) and 4 x 16 B of X
-  // (rows (tid >> 3) + 32 j, chunk tid & 7)
+  // wave w fills LDS tiles w + 4 j (j = 0..3) of W and of the activations per slab
   const bf16_t* wsrc[4];
-  int wdst[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int id = (tid >> 6) + 4 * j;                    // local tile id = row tile * 2 + k tile
-    wsrc[j] = W + ((size_t)wtile(id >> 1) * ktiles + (id & 1)) * 512 + lane * 8;
-    wdst[j] = id * 512 + lane * 8;
-  }
   const bf16_t* xsrc[4];
-  int xdst[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = (tid >> 3) + 32 * j, c = tid & 7;
-    xsrc[j] = X + (size_t)min(m0 + row, Ma - 1) * ldx + 8 * c;
-    xdst[j] = (((row >> 4) * 2 + (c >> 2)) * 512) + (row & 15) * 32 + (c & 3) * 8;
+    const int id = wave + 4 * j;                          // local tile id = row tile * 2 + k tile
+    wsrc[j] = W + ((size_t)wtile(id >> 1) * ktiles + (id & 1)) * 512 + lane * 8;
+    const int row = (id >> 1) * 16 + (lane >> 2);
+    xsrc[j] = X + (size_t)min(m0 + row, Ma - 1) * ldx + (id & 1) * 32 + (lane & 3) * 8;
   }
-  u32x4 wreg[4], xreg[4];
-  auto gload = [&](int sl) {
+  auto issue = [&](int sl) {                              // 8 loads per thread
+    bf16_t* st = Ls[sl % TG_NST];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      wreg[j] = *(const u32x4*)(wsrc[j] + (size_t)sl * 1024);     // slab sl = k tiles 2 sl, 2 sl + 1
-      xreg[j] = *(const u32x4*)(xsrc[j] + (size_t)sl * TG_KS);
-    }
-  };
-  auto lstore = [&](int b) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *(u32x4*)(Ws[b] + wdst[j]) = wreg[j];
-      *(u32x4*)(Xs[b] + xdst[j]) = xreg[j];
+      const int id = wave + 4 * j;
+      tg_load_lds(wsrc[j] + (size_t)sl * 1024, st + id * 512);
+      tg_load_lds(xsrc[j] + (size_t)sl * TG_KS, st + TG_W * TG_KS + id * 512);
     }
   };
 
-  // this wave's W row tiles (A fragments) and activation row tiles (B fragments)
+  // this wave's W row tiles (A fragments); activation row tiles 4 wm + j (B fragments)
   int at[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) at[i] = SW ? (i < 2 ? 2 * wn + i : 4 + 2 * wn + (i - 2)) : 4 * wn + i;
@@ -262,45 +264,47 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
     for (int j = 0; j < 4; ++j) acc[i][j] = sum[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nu = K / TG_KS;                               // slabs (= 64-element units)
-  int qend = nu / 4;                                      // end of quarter q: (nu (q + 1)) / 4
-  int q = 0;
-  auto close_quarters = [&](int sl) {                     // quarters ending at slab sl (empty ones add zero)
-    while (q < 4 && qend <= sl) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+  for (int p = 0; p < TG_NST - 1; ++p)
+    if (p < nu) issue(p);
+  int sl = 0;
+  for (int q = 0; q < 4; ++q) {
+    const int qe = (nu * (q + 1)) / 4;                    // quarter q: slabs [(nu q) / 4, qe)
+    for (; sl < qe; ++sl) {
+      if (sl + TG_NST - 1 < nu) {
+        issue(sl + TG_NST - 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (TG_NST - 1)) : "memory");   // slab sl has landed
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      tg_barrier();                                       // ... for every wave's share of it
+      const bf16_t* st = Ls[sl % TG_NST];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sum[i][j] += acc[i][j];
-          acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      ++q;
-      qend = (nu * (q + 1)) / 4;
+      for (int kt = 0; kt < 2; ++kt) {
+        bf16x8 af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + (at[i] * 2 + kt) * 512 + r * 32 + g * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bfr[j] = *(const bf16x8*)(st + TG_W * TG_KS + ((4 * wm + j) * 2 + kt) * 512 + r * 32 + g * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's reads of the stage are done
+      tg_barrier();                                         // before the stage is refilled
     }
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int sl = 0; sl < nu; ++sl) {
-    const int b = sl & 1;
-    if (sl + 1 < nu) gload(sl + 1);
-    close_quarters(sl);
+    // the quarter's sum joins the earlier quarters' (an empty quarter adds zero)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      bf16x8 af[4], bfr[4];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(Ws[b] + (at[i] * 2 + kt) * 512 + r * 32 + g * 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = *(const bf16x8*)(Xs[b] + ((4 * wm + j) * 2 + kt) * 512 + r * 32 + g * 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (sl + 1 < nu) lstore(b ^ 1);
-    __syncthreads();
+      for (int j = 0; j < 4; ++j) {
+        sum[i][j] += acc[i][j];
+        acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
   }
-  close_quarters(nu);
 
   // acc layout: lane (r, g) holds D[feature 4 g + e][row r] of each 16 x 16 block
 #pragma unroll
