@@ -76,3 +76,15 @@ def test_norm_gain_law():
     assert abs(float(g.std()) - synth.GAIN_STD) < 0.01
     g2 = synth.norm_gain_host(4096, synth.layer_tid(3, synth.KIND_MLP_NORM))
     assert not np.array_equal(g, g2)
+
+
+def test_scoring_masks_law():
+    """Scoring candidates: k_c skipped layers with k_c in [lo, hi], both
+    sub-layer bits of a skipped layer set, distinct seeded subsets, reproducible."""
+    m = synth.scoring_masks(40, 16, 16, 24)
+    assert m.shape == (16, 80) and m.dtype == np.uint8
+    assert np.array_equal(m[:, 0::2], m[:, 1::2])
+    k = m[:, 0::2].sum(axis=1)
+    assert k.min() >= 16 and k.max() <= 24 and len(set(k.tolist())) > 1
+    assert len({row.tobytes() for row in m}) == 16
+    assert np.array_equal(m, synth.scoring_masks(40, 16, 16, 24))
