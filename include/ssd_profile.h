@@ -7,8 +7,11 @@
  * queued around the kernel), and the library accumulates the algorithmic
  * bytes each launch must move (weights + activations read + results written,
  * each once).  ssd_profile_read waits for the events and returns the summed
- * durations.  Process-wide; not thread-safe; events are created by
- * ssd_profile_enable (host-side objects, no device memory).
+ * durations.  A launch that returned at once because a device stop flag was
+ * raised (a draft step after the confidence stop) moved no bytes; such
+ * launches are left out of the sums and of the count.  Process-wide; not
+ * thread-safe; ssd_profile_enable creates the events and a device array of
+ * max_launches flags (the only device memory the hooks use).
  */
 #ifndef SSD_PROFILE_H
 #define SSD_PROFILE_H
@@ -30,8 +33,9 @@ int ssd_profile_enable(int kernel_class, int max_launches);
 /* Stop recording (records are kept for ssd_profile_read). */
 int ssd_profile_disable(void);
 
-/* Synchronises the recorded events.  *total_ms = sum of launch durations,
- * *n_launches = launches recorded, *total_bytes = their algorithmic bytes. */
+/* Synchronises the device.  *total_ms = sum of the durations of the recorded
+ * launches that did their work, *n_launches = their number, *total_bytes =
+ * their algorithmic bytes. */
 int ssd_profile_read(double* total_ms, int* n_launches, double* total_bytes);
 
 #ifdef __cplusplus

@@ -80,6 +80,7 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   if (a.stop && *a.stop) return;
   const int Ma = a.nrows ? min(a.M, *a.nrows) : a.M;
   if (Ma <= 0) return;
+  if (a.prof_ran && blockIdx.x == 0 && threadIdx.x == 0) *a.prof_ran = 1;   // timing record: this launch ran
   constexpr bool TWO = EPI == DEC_SWIGLU || EPI == DEC_QKV;   // outputs combine two W row sets
   constexpr bool DUAL = TWO && !HALF;                           // 16 + 16 rows: two accumulators
   static_assert(!HALF || TWO, "half tiles pair two row sets");
@@ -287,8 +288,8 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   }
 }
 
-bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop);
-void profile_done(double bytes);
+bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop, int** ran);
+void profile_done(double bytes, const int* stop_flag, bool self_marked, hipStream_t s);
 
 // Tile shapes of the two-set projections (HALF: 8 + 8 rows per tile, twice the tiles).
 constexpr bool DEC_HALF_QKV = true;
@@ -331,7 +332,7 @@ int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
   // profile classes: 0 plain-store projections (QKV, LM head), 1 residual, 2 gate/up
   const int cls = epi == DEC_RESID ? 1 : (epi == DEC_SWIGLU ? 2 : 0);
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  const bool prof = profile_next(cls, &e0, &e1);
+  const bool prof = profile_next(cls, &e0, &e1, &b.prof_ran);
   switch (epi) {
     case DEC_STORE: dec_launch<DEC_STORE, false>(b, tpw, e0, e1, s); break;
     case DEC_RESID: dec_launch<DEC_RESID, false>(b, tpw, e0, e1, s); break;
@@ -344,7 +345,7 @@ int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
     const double wrows = epi == DEC_SWIGLU ? 2.0 * N : N;
     double by = wrows * K * 2.0 + M * K * 2.0;
     by += epi == DEC_STORE ? 4.0 * M * N : (epi == DEC_RESID ? 8.0 * M * N : 2.0 * M * N);
-    profile_done(by);
+    profile_done(by, a.stop, true, s);
   }
   return dec_ok(hipGetLastError());
 }

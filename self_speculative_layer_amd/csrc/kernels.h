@@ -146,6 +146,7 @@ struct DecGemm {
   int PS, n_lpages, L, layer, H, KVH, HD;
   const int* pos; const float2* rope_cs; int* err;
   int n_tiles;                      // set by the launcher
+  int* prof_ran;                    // set by the launcher: timing record of a profiled launch (or null)
 };
 int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s);
 

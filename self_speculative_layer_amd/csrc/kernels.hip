@@ -342,8 +342,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
   }
 }
 
-bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop);
-void profile_done(double bytes);
+bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop, int** ran);
+void profile_done(double bytes, const int* stop_flag, bool self_marked, hipStream_t s);
 static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
                               float* Y, int ldy, void* A, int lda, int n_rb, dim3 grid, const float* rscale,
                               const int* nrows, const int* ymap, const int* stop, hipEvent_t e0, hipEvent_t e1,
@@ -354,7 +354,8 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
                   const int* stop, hipStream_t s) {
   if (M <= 0 || N <= 0) return 0;
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  const bool prof = profile_next(epi, &e0, &e1);
+  int* ran = nullptr;
+  const bool prof = profile_next(epi, &e0, &e1, &ran);
   int rc;
   if (dtype == SSD_DTYPE_BF16 && M >= TG_MIN_ROWS && K % TG_KS == 0 && (epi != EPI_SWIGLU || N % 64 == 0)) {
     const int n_mb = (M + TG_M - 1) / TG_M;
@@ -383,7 +384,7 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
     const double wrows = epi == EPI_SWIGLU ? 2.0 * N : (double)N;
     double by = wrows * K * elt + (double)M * K * elt;
     by += epi == EPI_STORE ? 4.0 * M * N : (epi == EPI_RESID ? 8.0 * M * N : elt * M * N);
-    profile_done(by);
+    profile_done(by, stop, false, s);
   }
   return rc;
 }

@@ -1,7 +1,12 @@
 // Kernel-timing hooks (include/ssd_profile.h).  A profiled launch goes out
 // through hipExtLaunchKernel with a start and a stop event: the events take
 // the dispatch's own begin and end timestamps, so no marker is queued around
-// the kernel and the stream's timing is unchanged.
+// the kernel and the stream's timing is unchanged.  Each record also has a
+// device flag that says whether the launch did its work: a launch behind a
+// raised device stop flag (a draft step after the confidence stop) returns at
+// once and is left out of the sums.  Decode projections set the flag
+// themselves; other launches with a stop flag get a one-thread marker kernel
+// after them; launches without one always run.
 #include <vector>
 
 #include "kernels.h"
@@ -16,20 +21,29 @@ struct ProfState {
   bool on = false;
   std::vector<hipEvent_t> ev;   // 2 per launch
   std::vector<double> bytes;
+  std::vector<char> host_ran;   // launch without a stop flag: ran
+  int* ran_dev = nullptr;       // [max] set on the device by launches that ran
   int used = 0;
 };
 ProfState g_prof;
 }  // namespace
 
-bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop) {
+__global__ void prof_mark_kernel(int* ran, const int* stop) { *ran = *stop ? 0 : 1; }
+
+bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop, int** ran) {
   if (!(g_prof.on && g_prof.cls == cls && g_prof.used < g_prof.max)) return false;
   *start = g_prof.ev[2 * g_prof.used];
   *stop = g_prof.ev[2 * g_prof.used + 1];
+  *ran = g_prof.ran_dev + g_prof.used;
   return true;
 }
 
-void profile_done(double bytes) {
-  g_prof.bytes[g_prof.used] = bytes;
+// stop_flag: the launch's device stop flag (nullable); self_marked: the kernel writes its ran flag.
+void profile_done(double bytes, const int* stop_flag, bool self_marked, hipStream_t s) {
+  const int i = g_prof.used;
+  g_prof.bytes[i] = bytes;
+  g_prof.host_ran[i] = stop_flag == nullptr;
+  if (stop_flag && !self_marked) hipLaunchKernelGGL(prof_mark_kernel, dim3(1), dim3(1), 0, s, g_prof.ran_dev + i, stop_flag);
   ++g_prof.used;
 }
 
@@ -45,6 +59,11 @@ extern "C" int ssd_profile_enable(int kernel_class, int max_launches) {
   for (auto& e : g_prof.ev)
     if (hipEventCreate(&e) != hipSuccess) return SSD_ERR_HIP;
   g_prof.bytes.assign(max_launches, 0.0);
+  g_prof.host_ran.assign(max_launches, 0);
+  if (g_prof.ran_dev) (void)hipFree(g_prof.ran_dev);
+  g_prof.ran_dev = nullptr;
+  if (hipMalloc(&g_prof.ran_dev, sizeof(int) * (size_t)max_launches) != hipSuccess) return SSD_ERR_HIP;
+  if (hipMemset(g_prof.ran_dev, 0, sizeof(int) * (size_t)max_launches) != hipSuccess) return SSD_ERR_HIP;
   g_prof.cls = kernel_class;
   g_prof.max = max_launches;
   g_prof.used = 0;
@@ -60,15 +79,25 @@ extern "C" int ssd_profile_disable(void) {
 extern "C" int ssd_profile_read(double* total_ms, int* n_launches, double* total_bytes) {
   if (!total_ms || !n_launches || !total_bytes) return SSD_ERR_ARG;
   double ms = 0.0, by = 0.0;
+  int n = 0;
+  std::vector<int> ran(g_prof.used, 0);
+  if (g_prof.used > 0) {
+    if (hipEventSynchronize(g_prof.ev[2 * g_prof.used - 1]) != hipSuccess) return SSD_ERR_HIP;
+    if (hipDeviceSynchronize() != hipSuccess) return SSD_ERR_HIP;
+    if (hipMemcpy(ran.data(), g_prof.ran_dev, sizeof(int) * g_prof.used, hipMemcpyDeviceToHost) != hipSuccess)
+      return SSD_ERR_HIP;
+  }
   for (int i = 0; i < g_prof.used; ++i) {
+    if (!(g_prof.host_ran[i] || ran[i])) continue;
     if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) return SSD_ERR_HIP;
     float t = 0.f;
     if (hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) return SSD_ERR_HIP;
     ms += t;
     by += g_prof.bytes[i];
+    ++n;
   }
   *total_ms = ms;
-  *n_launches = g_prof.used;
+  *n_launches = n;
   *total_bytes = by;
   return SSD_OK;
 }
