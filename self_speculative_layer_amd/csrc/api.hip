@@ -247,8 +247,9 @@ DecGemm dec_base(const ssd_seq* q, int M, const int* nrows, const int* stop) {
 }
 
 // Entries [e0, e1) of ent on the residual rows h[0, M).
+// copy_last (nullable): the residual rows after the last entry are also written there.
 int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, const std::vector<int>& ent, size_t e0,
-               size_t e1, bool final_lm, const int* stop, hipStream_t s) {
+               size_t e1, bool final_lm, const int* stop, hipStream_t s, float* copy_last = nullptr) {
   const ssd_model* m = q->m;
   const ssd_model_desc& d = m->d;
   const Workspace& w = q->w;
@@ -260,6 +261,7 @@ int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, co
     r.Y = h; r.ldy = D; r.N = D;
     r.gain_next = dec_gain(m, ent, e + 1, final_lm);
     r.xg_next = w.xg; r.ss_next = w.ss;
+    r.y_copy = e + 1 == e1 ? copy_last : nullptr;
     if (ent[e] % 2 == 0) {
       DecGemm a = dec_base(q, M, nrows, stop);
       a.W = (const bf16_t*)lw.w_qkv; a.N = m->qkv_dim; a.K = D;
@@ -521,10 +523,12 @@ extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_lay
     plan_entries(ent, b, d.n_layers, mask.data());
     const float* g0 = dec_gain(q->m, ent, 0, true);
     for (int j = 1; j <= d_max; ++j) {
-      TRY(launch_draft_step_prep(w.st, draft_tokens_dev, j, w.pos1, w.tok1, q->max_ctx, n_drafted_dev, s));
-      TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, g0, stop, s));
-      TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, ent, 0, save, true, stop, s));
-      TRY(launch_copy_rows(w.h1, w.hb + (size_t)(j - 1) * d.d_model, 1, d.d_model, nullptr, nullptr, stop, s));
+      TRY(launch_dec_draft_entry(w.st, draft_tokens_dev, j, w.pos1, w.tok1, q->max_ctx, n_drafted_dev, d.embed,
+                                 d.vocab, w.h1, d.d_model, g0, w.xg, w.ss, s));
+      // the residual at the reuse boundary is saved for the verify by the last projection below it
+      float* hb = w.hb + (size_t)(j - 1) * d.d_model;
+      TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, ent, 0, save, true, stop, s, hb));
+      if (save == 0) TRY(launch_copy_rows(w.h1, hb, 1, d.d_model, nullptr, nullptr, stop, s));
       TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, ent, save, ent.size(), true, stop, s));
       float* lg = draft_logits_dev + (size_t)(j - 1) * d.vocab;
       TRY(dec_logits(q, 1, nullptr, lg, stop, s));

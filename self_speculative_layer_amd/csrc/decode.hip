@@ -248,6 +248,7 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       const int col = t.f0 + nn;
       const float hn = __fadd_rn(eh[j], s);
       a.Y[(size_t)row * a.ldy + col] = hn;
+      if (a.y_copy) a.y_copy[(size_t)row * a.ldy + col] = hn;
       if (a.gain_next) {
         st(a.xg_next + dec_act_index(row, col), __fmul_rn(hn, eg[j]));
         const float tt = tile16_ss_lanes(hn);
@@ -417,20 +418,12 @@ int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv,
 // residual rows, plus the first RMSNorm consumer's input.
 // ===========================================================================
 
+// Row r of the entry: h[dr] from the embedding row e (EMB) or from sr, and with NORM the first consumer's
+// input xg[dr] = bf16(h * gain) and the tile sums ss[dr].
 template <bool EMB, bool NORM>
-__global__ __launch_bounds__(256) void dec_entry_kernel(const bf16_t* __restrict__ emb, const int* __restrict__ tokens,
-                                                        int V, const float* __restrict__ src, int rows,
-                                                        const int* __restrict__ count, const int* __restrict__ dst_off,
-                                                        float* __restrict__ h, int D, const float* __restrict__ gain,
-                                                        bf16_t* __restrict__ xg, float* __restrict__ ss,
-                                                        const int* __restrict__ stop) {
-  if (stop && *stop) return;
-  const int r = blockIdx.x;
-  const int n = count ? min(rows, *count) : rows;
-  if (r >= n) return;
-  const int dr = r + (dst_off ? *dst_off : 0);
-  const bf16_t* e = EMB ? emb + (size_t)min(max(tokens[r], 0), V - 1) * D : nullptr;   // ids are produced in range
-  const float* sr = EMB ? nullptr : src + (size_t)r * D;
+__device__ __forceinline__ void dec_entry_row(const bf16_t* __restrict__ e, const float* __restrict__ sr, int dr,
+                                              float* __restrict__ h, int D, const float* __restrict__ gain,
+                                              bf16_t* __restrict__ xg, float* __restrict__ ss) {
   float* hr = h + (size_t)dr * D;
   // D % 16 == 0: each group of 16 lanes is entirely inside or outside the row.  Loads are issued in
   // batches of 8 per thread before their first use.
@@ -457,6 +450,71 @@ __global__ __launch_bounds__(256) void dec_entry_kernel(const bf16_t* __restrict
       }
     }
   }
+}
+
+template <bool EMB, bool NORM>
+__global__ __launch_bounds__(256) void dec_entry_kernel(const bf16_t* __restrict__ emb, const int* __restrict__ tokens,
+                                                        int V, const float* __restrict__ src, int rows,
+                                                        const int* __restrict__ count, const int* __restrict__ dst_off,
+                                                        float* __restrict__ h, int D, const float* __restrict__ gain,
+                                                        bf16_t* __restrict__ xg, float* __restrict__ ss,
+                                                        const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int r = blockIdx.x;
+  const int n = count ? min(rows, *count) : rows;
+  if (r >= n) return;
+  const int dr = r + (dst_off ? *dst_off : 0);
+  const bf16_t* e = EMB ? emb + (size_t)min(max(tokens[r], 0), V - 1) * D : nullptr;   // ids are produced in range
+  dec_entry_row<EMB, NORM>(e, EMB ? nullptr : src + (size_t)r * D, dr, h, D, gain, xg, ss);
+}
+
+// Draft step j (1-based): the row y_{j-1} at position kvlen + j - 1 (y_0 = the last committed token).
+// Out of KV pages (the verify needs position kvlen + d' as well) it ends the draft instead.  Writes
+// the row's position and token (pos1, tok1) for the step's kernels.
+template <bool NORM>
+__global__ __launch_bounds__(256) void dec_draft_entry_kernel(DevState* __restrict__ st,
+                                                              const int32_t* __restrict__ drafts, int j,
+                                                              int* __restrict__ pos1, int* __restrict__ tok1,
+                                                              int max_ctx, int32_t* __restrict__ n_drafted_out,
+                                                              const bf16_t* __restrict__ emb, int V,
+                                                              float* __restrict__ h, int D,
+                                                              const float* __restrict__ gain,
+                                                              bf16_t* __restrict__ xg, float* __restrict__ ss) {
+  __shared__ int s_tok, s_ok;
+  if (threadIdx.x == 0) {
+    int ok = !st->stop, tok = 0;
+    if (ok) {
+      const int p = st->kvlen + j - 1;
+      if (p + 1 >= max_ctx) {
+        st->error_flags |= ERRF_CAPACITY;
+        st->stop = 1;
+        st->n_drafted = max(j - 1, 0);
+        *n_drafted_out = max(j - 1, 0);
+        ok = 0;
+      } else {
+        tok = j == 1 ? st->last_token : drafts[j - 2];
+        pos1[0] = p;
+        tok1[0] = tok;
+      }
+    }
+    s_tok = tok;
+    s_ok = ok;
+  }
+  __syncthreads();
+  if (!s_ok) return;
+  dec_entry_row<true, NORM>(emb + (size_t)min(max(s_tok, 0), V - 1) * D, nullptr, 0, h, D, gain, xg, ss);
+}
+
+int launch_dec_draft_entry(DevState* st, const int32_t* drafts, int j, int* pos1, int* tok1, int max_ctx,
+                           int32_t* n_drafted_out, const void* emb, int V, float* h, int D, const float* gain,
+                           void* xg, float* ss, hipStream_t s) {
+  if (D % 16 != 0) return SSD_ERR_SHAPE;
+#define DENTRY(N)                                                                                                 \
+  hipLaunchKernelGGL((dec_draft_entry_kernel<N>), dim3(1), dim3(256), 0, s, st, drafts, j, pos1, tok1, max_ctx,  \
+                     n_drafted_out, (const bf16_t*)emb, V, h, D, gain, (bf16_t*)xg, ss)
+  if (gain) DENTRY(true); else DENTRY(false);
+#undef DENTRY
+  return dec_ok(hipGetLastError());
 }
 
 int launch_dec_entry(const void* emb, const int* tokens, int V, const float* src, int rows, const int* count,

@@ -141,6 +141,7 @@ struct DecGemm {
   const float* gain_next;           // RESID: gain of the next RMSNorm consumer (nullable: none)
   bf16_t* xg_next;                  //   its input bf16(h * gain) [M, N], decode block layout
   float* ss_next;                   //   tile sums of h^2 [M, N/16]
+  float* y_copy;                    //   (nullable) second destination of the new residual rows (stride ldy)
   bf16_t* q; int ldq;               // QKV: rotated queries [M, H*HD]
   bf16_t* pool; const int* page_table;
   int PS, n_lpages, L, layer, H, KVH, HD;
@@ -154,6 +155,12 @@ int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s);
 int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer, int H, int KVH,
                          int M, const int* nrows, const int* pos, int max_ctx, float* part, void* out, int ldo,
                          unsigned* counters, const int* stop, hipStream_t s);
+
+// Draft step j's entry row: position and token from the device state (or the end of the draft when the
+// KV pages are full), then the embedding row and the first consumer's input, as launch_dec_entry.
+int launch_dec_draft_entry(DevState* st, const int32_t* drafts, int j, int* pos1, int* tok1, int max_ctx,
+                           int32_t* n_drafted_out, const void* emb, int V, float* h, int D, const float* gain,
+                           void* xg, float* ss, hipStream_t s);
 
 // h[dst] = embedding row of tokens[r] (tokens != nullptr) or src[r], for r < (count ? *count : rows),
 // dst = r + (dst_off ? *dst_off : 0); with gain, also xg[dst] = bf16(h * gain) and ss[dst] tile sums.
