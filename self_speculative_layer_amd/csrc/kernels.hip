@@ -188,10 +188,8 @@ __global__ __launch_bounds__(256) void gemm_f32_rows16(
 // three kernels.
 // ===========================================================================
 
-constexpr int TG_W = 128;            // W rows per workgroup
-constexpr int TG_M = 128;            // activation rows per workgroup
 constexpr int TG_KS = 64;            // K elements per LDS slab
-constexpr int TG_NST = 2;            // slabs in flight (LDS buffers; 64 KB: two workgroups per CU)
+constexpr int TG_NST = 2;            // slabs in flight (LDS buffers)
 constexpr int TG_MIN_ROWS = 64;      // row counts from which launch_linear takes this kernel
 
 typedef __attribute__((address_space(3))) void tg_lds_t;
@@ -204,23 +202,30 @@ __device__ __forceinline__ void tg_load_lds(const void* src, void* lds) {
 // Workgroup barrier without a memory fence: the waits for the slab loads are explicit.
 __device__ __forceinline__ void tg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int EPI>
+// WI x WJ: MFMA blocks per wave (W row tiles x activation row tiles); the four waves form a 2 x 2 grid,
+// so a workgroup covers 32 WI W rows (SwiGLU: 16 WI gate rows and the same up rows) and 32 WJ
+// activation rows.  4 x 4 for large problems; 2 x 2 when the large tiles would leave CUs idle.
+template <int EPI, int WI, int WJ>
 __global__ __launch_bounds__(256) void gemm_bf16_tiled(
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ X, int ldx, int M, int N, int K,
     float* __restrict__ Y, int ldy, bf16_t* __restrict__ A, int lda, int n_mb, const float* __restrict__ rscale,
     const int* __restrict__ nrows, const int* __restrict__ ymap, const int* __restrict__ stop) {
   if (stop && *stop) return;
   constexpr bool SW = EPI == EPI_SWIGLU;
+  constexpr int WT = 2 * WI, XT = 2 * WJ;           // W / activation row tiles per workgroup
+  constexpr int WSZ = WT * 2 * 512, XSZ = XT * 2 * 512;   // elements of a stage's W / activation tiles
+  constexpr int H = WI / 2;
+  static_assert(!SW || WI % 2 == 0, "SwiGLU pairs gate and up tiles");
   const int Ma = active_rows(M, nrows);
   // workgroup i runs on XCD i % 8: consecutive logical blocks (the row blocks of one W tile) are placed
   // on one XCD, so that they share its L2 for the W slabs
   const int nblk = gridDim.x;
   const int lb = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
   const int mb = lb % n_mb, nb = lb / n_mb;
-  const int m0 = mb * TG_M;
+  const int m0 = mb * 16 * XT;
   if (m0 >= Ma) return;
-  // per stage: W tiles [row tile 0..7][k tile 0..1][16][32], then the activation tiles in the same shape
-  __shared__ alignas(16) bf16_t Ls[TG_NST][2 * TG_W * TG_KS];
+  // per stage: W tiles [row tile][k tile 0..1][16][32], then the activation tiles in the same shape
+  __shared__ alignas(16) bf16_t Ls[TG_NST][WSZ + XSZ];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
@@ -228,40 +233,42 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
   const int ktiles = K / 32;
   const int n_wtiles = (N + 15) / 16;                     // packed tiles per W row set
 
-  // global packed tile (row tile index) of local W row tile t (0..7)
+  // global packed tile (row tile index) of local W row tile t
   auto wtile = [&](int t) -> int {
-    if (SW) return t < 4 ? 4 * nb + t : n_wtiles + 4 * nb + (t - 4);   // gate f0.., then up N + f0..
-    return min(8 * nb + t, n_wtiles - 1);                               // tiles past N repeat the last
+    if (SW) return t < WI ? WI * nb + t : n_wtiles + WI * nb + (t - WI);   // gate f0.., then up N + f0..
+    return min(WT * nb + t, n_wtiles - 1);                                 // tiles past N repeat the last
   };
-  // wave w fills LDS tiles w + 4 j (j = 0..3) of W and of the activations per slab
-  const bf16_t* wsrc[4];
-  const bf16_t* xsrc[4];
+  // wave w fills the LDS tiles w + 4 j of W (j < WI) and of the activations (j < WJ) per slab
+  const bf16_t* wsrc[WI];
+  const bf16_t* xsrc[WJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < WI; ++j) {
     const int id = wave + 4 * j;                          // local tile id = row tile * 2 + k tile
     wsrc[j] = W + ((size_t)wtile(id >> 1) * ktiles + (id & 1)) * 512 + lane * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    const int id = wave + 4 * j;
     const int row = (id >> 1) * 16 + (lane >> 2);
     xsrc[j] = X + (size_t)min(m0 + row, Ma - 1) * ldx + (id & 1) * 32 + (lane & 3) * 8;
   }
-  auto issue = [&](int sl) {                              // 8 loads per thread
+  auto issue = [&](int sl) {                              // WI + WJ loads per thread
     bf16_t* st = Ls[sl % TG_NST];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int id = wave + 4 * j;
-      tg_load_lds(wsrc[j] + (size_t)sl * 1024, st + id * 512);
-      tg_load_lds(xsrc[j] + (size_t)sl * TG_KS, st + TG_W * TG_KS + id * 512);
-    }
+    for (int j = 0; j < WI; ++j) tg_load_lds(wsrc[j] + (size_t)sl * 1024, st + (wave + 4 * j) * 512);
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) tg_load_lds(xsrc[j] + (size_t)sl * TG_KS, st + WSZ + (wave + 4 * j) * 512);
   };
 
-  // this wave's W row tiles (A fragments); activation row tiles 4 wm + j (B fragments)
-  int at[4];
+  // this wave's W row tiles (A fragments); activation row tiles WJ wm + j (B fragments)
+  int at[WI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) at[i] = SW ? (i < 2 ? 2 * wn + i : 4 + 2 * wn + (i - 2)) : 4 * wn + i;
-  f32x4 acc[4][4], sum[4][4];
+  for (int i = 0; i < WI; ++i) at[i] = SW ? (i < H ? H * wn + i : WI + H * wn + (i - H)) : WI * wn + i;
+  f32x4 acc[WI][WJ], sum[WI][WJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = sum[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WJ; ++j) acc[i][j] = sum[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nu = K / TG_KS;                               // slabs (= 64-element units)
 #pragma unroll
@@ -273,7 +280,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
     for (; sl < qe; ++sl) {
       if (sl + TG_NST - 1 < nu) {
         issue(sl + TG_NST - 1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (TG_NST - 1)) : "memory");   // slab sl has landed
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((WI + WJ) * (TG_NST - 1)) : "memory");   // slab sl has landed
       } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
@@ -281,16 +288,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
       const bf16_t* st = Ls[sl % TG_NST];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        bf16x8 af[4], bfr[4];
+        bf16x8 af[WI], bfr[WJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + (at[i] * 2 + kt) * 512 + r * 32 + g * 8);
+        for (int i = 0; i < WI; ++i) af[i] = *(const bf16x8*)(st + (at[i] * 2 + kt) * 512 + r * 32 + g * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfr[j] = *(const bf16x8*)(st + TG_W * TG_KS + ((4 * wm + j) * 2 + kt) * 512 + r * 32 + g * 8);
+        for (int j = 0; j < WJ; ++j)
+          bfr[j] = *(const bf16x8*)(st + WSZ + ((WJ * wm + j) * 2 + kt) * 512 + r * 32 + g * 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WI; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < WJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's reads of the stage are done
@@ -298,9 +305,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
     }
     // the quarter's sum joins the earlier quarters' (an empty quarter adds zero)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < WJ; ++j) {
         sum[i][j] += acc[i][j];
         acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -308,27 +315,27 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
 
   // acc layout: lane (r, g) holds D[feature 4 g + e][row r] of each 16 x 16 block
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = m0 + 16 * (4 * wm + j) + r;
+  for (int j = 0; j < WJ; ++j) {
+    const int row = m0 + 16 * (WJ * wm + j) + r;
     if (row >= Ma) continue;
     const float rs = (rscale && EPI != EPI_RESID) ? rscale[row] : 1.f;
     const int yrow = ymap ? ymap[row] : row;
     if constexpr (SW) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < H; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int col = 64 * nb + 16 * (2 * wn + i) + 4 * g + e;
-          float s1 = sum[i][j][e], s2 = sum[i + 2][j][e];
+          const int col = 16 * WI * nb + 16 * (H * wn + i) + 4 * g + e;
+          float s1 = sum[i][j][e], s2 = sum[i + H][j][e];
           if (rscale) { s1 = __fmul_rn(s1, rs); s2 = __fmul_rn(s2, rs); }
           A[(size_t)row * lda + col] = f2bf(swiglu(s1, s2));
         }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WI; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int col = 128 * nb + 16 * (4 * wn + i) + 4 * g + e;
+          const int col = 16 * WT * nb + 16 * (WI * wn + i) + 4 * g + e;
           if (col >= N) continue;
           float v = sum[i][j][e];
           if (EPI == EPI_STORE) {
@@ -340,6 +347,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
         }
     }
   }
+}
+
+// Workgroups of the tiled projection with WI x WJ blocks per wave.
+static int tg_blocks(int epi, int M, int N, int WI, int WJ) {
+  const int n_mb = (M + 32 * WJ - 1) / (32 * WJ);
+  const int n_nb = epi == EPI_SWIGLU ? N / (16 * WI) : (N + 32 * WI - 1) / (32 * WI);
+  return n_mb * n_nb;
 }
 
 bool profile_next(int cls, hipEvent_t* start, hipEvent_t* stop, int** ran);
@@ -358,17 +372,25 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
   const bool prof = profile_next(epi, &e0, &e1, &ran);
   int rc;
   if (dtype == SSD_DTYPE_BF16 && M >= TG_MIN_ROWS && K % TG_KS == 0 && (epi != EPI_SWIGLU || N % 64 == 0)) {
-    const int n_mb = (M + TG_M - 1) / TG_M;
-    const int n_nb = epi == EPI_SWIGLU ? N / 64 : (N + TG_W - 1) / TG_W;
-    const dim3 grid(n_mb * n_nb);
+    // large tiles unless they would leave CUs idle
+    const bool big = tg_blocks(epi, M, N, 4, 4) >= 256;
+    const int WJ = big ? 4 : 2;
+    const int n_mb = (M + 32 * WJ - 1) / (32 * WJ);
+    const dim3 grid(big ? tg_blocks(epi, M, N, 4, 4) : tg_blocks(epi, M, N, 2, 2));
     const bf16_t* w = (const bf16_t*)W;
     const bf16_t* x = (const bf16_t*)X;
-#define TILED(E)                                                                                                  \
-  hipExtLaunchKernelGGL(gemm_bf16_tiled<E>, grid, dim3(256), 0, s, e0, e1, 0, w, x, ldx, M, N, K, Y, ldy, (bf16_t*)A, \
-                        lda, n_mb, rscale, nrows, ymap, stop)
-    if (epi == EPI_STORE) TILED(EPI_STORE);
-    else if (epi == EPI_RESID) TILED(EPI_RESID);
-    else TILED(EPI_SWIGLU);
+#define TILED(E, I, J)                                                                                            \
+  hipExtLaunchKernelGGL((gemm_bf16_tiled<E, I, J>), grid, dim3(256), 0, s, e0, e1, 0, w, x, ldx, M, N, K, Y, ldy,   \
+                        (bf16_t*)A, lda, n_mb, rscale, nrows, ymap, stop)
+    if (big) {
+      if (epi == EPI_STORE) TILED(EPI_STORE, 4, 4);
+      else if (epi == EPI_RESID) TILED(EPI_RESID, 4, 4);
+      else TILED(EPI_SWIGLU, 4, 4);
+    } else {
+      if (epi == EPI_STORE) TILED(EPI_STORE, 2, 2);
+      else if (epi == EPI_RESID) TILED(EPI_RESID, 2, 2);
+      else TILED(EPI_SWIGLU, 2, 2);
+    }
 #undef TILED
     rc = last_launch();
   } else {
