@@ -63,6 +63,21 @@ struct AttnSmem<bf16_t, HD, NW> {
   float Mx[ATTB_MAXQ], Ls[ATTB_MAXQ];
 };
 
+// bf16 items of QT > 1 query tiles (prefill, mask scoring): the keys stay in LDS for every tile, so the
+// hand-over buffer of the P.V sums has its own storage.
+template <int HD, int QT>
+struct AttnSmemQ {
+  static constexpr int KST = HD + 8;
+  alignas(16) bf16_t Ks[ATT_CHUNK * KST];
+  alignas(16) bf16_t Vs[ATT_CHUNK * KST];
+  alignas(16) bf16_t Qs[QT * ATTB_MAXQ * KST];
+  alignas(16) float P[ATT_CHUNK * ATTB_MAXQ];
+  float Op[4][ATTB_MAXQ][HD];
+  float Mw[4][ATTB_MAXQ], Sw[4][ATTB_MAXQ];
+  int Rpos[QT * ATTB_MAXQ];
+  float Mx[ATTB_MAXQ];
+};
+
 typedef uint32_t att_u32x4 __attribute__((ext_vector_type(4)));
 
 // Partial results are stored either plainly (read by a later kernel) or with
@@ -73,89 +88,21 @@ __device__ __forceinline__ void part_store(float* p, float v) {
   else *p = v;
 }
 
-// bf16 work item (same contract as attn_partial_item below).
-template <int HD, int NW, bool DEV>
-__device__ void attn_item_bf16(AttnSmem<bf16_t, HD, NW>& sm, const bf16_t* __restrict__ q, int ldq,
-                               const bf16_t* __restrict__ pool, const int* __restrict__ page_table, int PS,
-                               int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
-                               const int* __restrict__ pos, int r0, int RB, int g, int s, int nsplit,
-                               const bf16_t* __restrict__ local_kv, int local_start, int group_rows,
-                               float* __restrict__ part) {
-  static_assert(NW == 4, "four waves: 16 keys each");
-  constexpr int NT = NW * 64;
-  constexpr int KST = AttnSmem<bf16_t, HD, NW>::KST;
-  constexpr int VEC = 8;                              // bf16 per 16-byte load
-  constexpr int VPR = HD / VEC;
-  constexpr int NLD = ATT_CHUNK * VPR / NT;
-  static_assert(NLD >= 1 && ATT_CHUNK * VPR % NT == 0 && HD % 32 == 0, "staging layout");
-  const int G = H / KVH;
-  const int key_beg = s * ATT_SPLIT;
+// Scores, softmax partials, P.V and the partial stores of one tile of at most 16 queries: queries
+// qbase .. qbase + 15 of the item's nq (rows x heads of the group), on the split's keys and values
+// staged in sm.Ks / sm.Vs and the tile's queries at Qs.  Opw ([NW][16][HD] floats) takes the waves'
+// P.V sums handed over; it may alias sm.Ks when no later tile needs the keys (the scores are formed
+// before the barrier that precedes its first write).  Ends with a workgroup barrier.
+template <int HD, int NW, bool DEV, typename SM>
+__device__ __forceinline__ void attn_tile_bf16(SM& sm, const bf16_t* __restrict__ Qs,
+                                               float (*Opw)[ATTB_MAXQ][HD], int qbase, int nq, int G, int r0,
+                                               int g, int H, int s, int nsplit, int key_beg, int key_end,
+                                               float* __restrict__ part) {
+  constexpr int KST = SM::KST;
   const float scale = 1.0f / sqrtf((float)HD);
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rmax = min(r0 + RB, M);
-
-  // ---- round 1: active rows, positions, the split's page ids, the queries
-  const int na = nrows ? *nrows : M;
-  int rp = 0;
-  if (tid < rmax - r0) rp = pos[r0 + tid];
-  const int pg0 = key_beg / PS;
-  const int pg = (lane * PS < ATT_CHUNK && pg0 + lane < n_lpages) ? page_table[pg0 + lane] : 0;
-  constexpr int QPER = (ATTB_MAXQ * VPR + NT - 1) / NT;
-  const int nq_max = (rmax - r0) * G;
-  att_u32x4 qreg[QPER];
-#pragma unroll
-  for (int j = 0; j < QPER; ++j) {
-    const int e = min(tid + NT * j, nq_max * VPR - 1);
-    const int qi = e / VPR, vc = e % VPR;
-    const int row = r0 + qi / G, head = g * G + qi % G;
-    qreg[j] = *(const att_u32x4*)(q + (size_t)row * ldq + (size_t)head * HD + vc * VEC);
-  }
-  if (tid < rmax - r0) sm.Rpos[tid] = rp;
-  __syncthreads();
-  const int Ma = min(M, na);
-  const int r1 = min(r0 + RB, Ma);
-  if (r1 <= r0) return;
-  const int maxpos = sm.Rpos[r1 - 1 - r0];
-  if (key_beg > maxpos) return;
-  const int nq = (r1 - r0) * G;
-  const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
-  const int grp_base = group_rows > 0 ? (r0 / group_rows) * group_rows : 0;
-
-  // ---- round 2: the split's keys and values (clamped addresses, zero past the end)
-  att_u32x4 kreg[NLD], vreg[NLD];
-#pragma unroll
-  for (int j = 0; j < NLD; ++j) {
-    const int e = tid + NT * j;
-    const int t = e / VPR, vc = e % VPR;
-    const int kp = key_beg + t;
-    const int kq = min(kp, key_end - 1);
-    const int page = __shfl(pg, (kq - key_beg) / PS, 64);
-    const bool local = local_kv && kq >= local_start;
-    const size_t lbase = ((size_t)(grp_base + (kq - local_start)) * 2) * KVH * HD + (size_t)g * HD;
-    const bf16_t* kr = local ? local_kv + lbase : pool + kv_index(page, L, layer, 0, KVH, g, PS, kq % PS, HD);
-    const bf16_t* vr = local ? local_kv + lbase + (size_t)KVH * HD
-                            : pool + kv_index(page, L, layer, 1, KVH, g, PS, kq % PS, HD);
-    kreg[j] = *(const att_u32x4*)(kr + vc * VEC);
-    vreg[j] = *(const att_u32x4*)(vr + vc * VEC);
-    if (kp >= key_end) {
-      kreg[j] = att_u32x4{0u, 0u, 0u, 0u};
-      vreg[j] = att_u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < QPER; ++j) {
-    const int e = tid + NT * j;
-    if (e < nq * VPR) *(att_u32x4*)(sm.Qs + (e / VPR) * KST + (e % VPR) * VEC) = qreg[j];
-  }
-#pragma unroll
-  for (int j = 0; j < NLD; ++j) {
-    const int e = tid + NT * j;
-    const int t = e / VPR, vc = e % VPR;
-    *(att_u32x4*)(sm.Ks + t * KST + vc * VEC) = kreg[j];
-    *(att_u32x4*)(sm.Vs + t * KST + vc * VEC) = vreg[j];
-  }
-  __syncthreads();
+  (void)tid;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // ---- scores: wave w forms S[key][query] for its 16 keys [16 w, 16 w + 16) and the (at most 16)
   // queries; acc[i] = S[key 16 w + 4 (lane >> 4) + i][query lane & 15]
@@ -163,14 +110,14 @@ __device__ void attn_item_bf16(AttnSmem<bf16_t, HD, NW>& sm, const bf16_t* __res
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ds = 0; ds < HD / 32; ++ds) {
-    const bf16x8 bq = *(const bf16x8*)(sm.Qs + ql * KST + 32 * ds + 8 * g4);
+    const bf16x8 bq = *(const bf16x8*)(Qs + ql * KST + 32 * ds + 8 * g4);
     const bf16x8 ak = *(const bf16x8*)(sm.Ks + (16 * wave + ql) * KST + 32 * ds + 8 * g4);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bq, acc, 0, 0, 0);
   }
   // ---- softmax of each query over the split's keys it sees (causal: key position <= its row's):
   // the maximum over the four waves' keys, then each wave's probabilities and their sum
-  const bool qv = ql < nq;
-  const int prow = qv ? sm.Rpos[ql / G] : -1;
+  const bool qv = qbase + ql < nq;
+  const int prow = qv ? sm.Rpos[(qbase + ql) / G] : -1;
   float sc[4];
   float mx = -INFINITY;
 #pragma unroll
@@ -226,7 +173,6 @@ __device__ void attn_item_bf16(AttnSmem<bf16_t, HD, NW>& sm, const bf16_t* __res
   }
   // each wave finalises the query quads q4 with q4 % NW == wave (sum in wave order), so every wave hands
   // the other quads' sums over through LDS
-  float (*Opw)[ATTB_MAXQ][HD] = sm.Op;                // [NW][query][dim] (aliases K)
 #pragma unroll
   for (int a = 0; a < NQ4; ++a) {
     const int q4 = qh + QS * a;
@@ -244,16 +190,16 @@ __device__ void attn_item_bf16(AttnSmem<bf16_t, HD, NW>& sm, const bf16_t* __res
     if ((q4 % NW) != wave) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int qq = 4 * q4 + j;
-      if (qq >= nq) continue;
-      if (key_beg > sm.Rpos[qq / G]) continue;        // the row sees no key of this split
+      const int qq = 4 * q4 + j, qi = qbase + qq;    // query in the tile, in the item
+      if (qi >= nq) continue;
+      if (key_beg > sm.Rpos[qi / G]) continue;        // the row sees no key of this split
       float olo = 0.f, ohi = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         olo += w == wave ? o[a][j][0] : Opw[w][qq][2 * dp];
         ohi += w == wave ? o[a][j][1] : Opw[w][qq][2 * dp + 1];
       }
-      const int row = r0 + qq / G, head = g * G + qq % G;
+      const int row = r0 + qi / G, head = g * G + qi % G;
       float* dstp = part + (((size_t)row * H + head) * nsplit + s) * (HD + 2);
       part_store<DEV>(dstp + 2 * dp, olo);
       part_store<DEV>(dstp + 2 * dp + 1, ohi);
@@ -265,6 +211,95 @@ __device__ void attn_item_bf16(AttnSmem<bf16_t, HD, NW>& sm, const bf16_t* __res
     }
   }
   __syncthreads();
+}
+
+// bf16 work item (same contract as attn_partial_item below): QT tiles of at most 16 queries each, on
+// the split's keys and values staged once.
+template <int HD, int NW, bool DEV, int QT = 1, typename SM = AttnSmem<bf16_t, HD, NW>>
+__device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
+                               const bf16_t* __restrict__ pool, const int* __restrict__ page_table, int PS,
+                               int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
+                               const int* __restrict__ pos, int r0, int RB, int g, int s, int nsplit,
+                               const bf16_t* __restrict__ local_kv, int local_start, int group_rows,
+                               float* __restrict__ part) {
+  static_assert(NW == 4, "four waves: 16 keys each");
+  constexpr int NT = NW * 64;
+  constexpr int KST = SM::KST;
+  constexpr int VEC = 8;                              // bf16 per 16-byte load
+  constexpr int VPR = HD / VEC;
+  constexpr int NLD = ATT_CHUNK * VPR / NT;
+  static_assert(NLD >= 1 && ATT_CHUNK * VPR % NT == 0 && HD % 32 == 0, "staging layout");
+  const int G = H / KVH;
+  const int key_beg = s * ATT_SPLIT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rmax = min(r0 + RB, M);
+
+  // ---- round 1: active rows, positions, the split's page ids, the queries
+  const int na = nrows ? *nrows : M;
+  int rp = 0;
+  if (tid < rmax - r0) rp = pos[r0 + tid];
+  const int pg0 = key_beg / PS;
+  const int pg = (lane * PS < ATT_CHUNK && pg0 + lane < n_lpages) ? page_table[pg0 + lane] : 0;
+  constexpr int QPER = (QT * ATTB_MAXQ * VPR + NT - 1) / NT;
+  const int nq_max = (rmax - r0) * G;
+  att_u32x4 qreg[QPER];
+#pragma unroll
+  for (int j = 0; j < QPER; ++j) {
+    const int e = min(tid + NT * j, nq_max * VPR - 1);
+    const int qi = e / VPR, vc = e % VPR;
+    const int row = r0 + qi / G, head = g * G + qi % G;
+    qreg[j] = *(const att_u32x4*)(q + (size_t)row * ldq + (size_t)head * HD + vc * VEC);
+  }
+  if (tid < rmax - r0) sm.Rpos[tid] = rp;
+  __syncthreads();
+  const int Ma = min(M, na);
+  const int r1 = min(r0 + RB, Ma);
+  if (r1 <= r0) return;
+  const int maxpos = sm.Rpos[r1 - 1 - r0];
+  if (key_beg > maxpos) return;
+  const int nq = (r1 - r0) * G;
+  const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
+  const int grp_base = group_rows > 0 ? (r0 / group_rows) * group_rows : 0;
+
+  // ---- round 2: the split's keys and values (clamped addresses, zero past the end)
+  att_u32x4 kreg[NLD], vreg[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int e = tid + NT * j;
+    const int t = e / VPR, vc = e % VPR;
+    const int kp = key_beg + t;
+    const int kq = min(kp, key_end - 1);
+    const int page = __shfl(pg, (kq - key_beg) / PS, 64);
+    const bool local = local_kv && kq >= local_start;
+    const size_t lbase = ((size_t)(grp_base + (kq - local_start)) * 2) * KVH * HD + (size_t)g * HD;
+    const bf16_t* kr = local ? local_kv + lbase : pool + kv_index(page, L, layer, 0, KVH, g, PS, kq % PS, HD);
+    const bf16_t* vr = local ? local_kv + lbase + (size_t)KVH * HD
+                            : pool + kv_index(page, L, layer, 1, KVH, g, PS, kq % PS, HD);
+    kreg[j] = *(const att_u32x4*)(kr + vc * VEC);
+    vreg[j] = *(const att_u32x4*)(vr + vc * VEC);
+    if (kp >= key_end) {
+      kreg[j] = att_u32x4{0u, 0u, 0u, 0u};
+      vreg[j] = att_u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < QPER; ++j) {
+    const int e = tid + NT * j;
+    if (e < nq * VPR) *(att_u32x4*)(sm.Qs + (e / VPR) * KST + (e % VPR) * VEC) = qreg[j];
+  }
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int e = tid + NT * j;
+    const int t = e / VPR, vc = e % VPR;
+    *(att_u32x4*)(sm.Ks + t * KST + vc * VEC) = kreg[j];
+    *(att_u32x4*)(sm.Vs + t * KST + vc * VEC) = vreg[j];
+  }
+  __syncthreads();
+
+  for (int t = 0; t * ATTB_MAXQ < nq; ++t)
+    attn_tile_bf16<HD, NW, DEV>(sm, sm.Qs + t * ATTB_MAXQ * KST, sm.Op, t * ATTB_MAXQ, nq, G, r0, g, H, s, nsplit,
+                                key_beg, key_end, part);
 }
 
 // fp32 work item (FMAs throughout).

@@ -631,6 +631,21 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
                               RB, g, s, nsplit, local_kv, local_start, group_rows, part);
 }
 
+// bf16 items of QT query tiles (row blocks of QT * 16 / G rows): the split's keys and values are staged
+// once for all tiles.
+template <int HD, int QT>
+__global__ __launch_bounds__(256) void attn_partial_multi_kernel(
+    const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ pool, const int* __restrict__ page_table,
+    int PS, int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
+    const int* __restrict__ pos, int RB, int nsplit, const bf16_t* __restrict__ local_kv, int local_start,
+    int group_rows, float* __restrict__ part, const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int g = blockIdx.x, s = blockIdx.y, rbk = blockIdx.z;
+  __shared__ AttnSmemQ<HD, QT> sm;
+  attn_item_bf16<HD, 4, false, QT>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos,
+                                   rbk * RB, RB, g, s, nsplit, local_kv, local_start, group_rows, part);
+}
+
 template <typename T, int HD>
 __global__ void attn_combine_kernel(const float* __restrict__ part, int nsplit, int M, const int* __restrict__ nrows,
                                     const int* __restrict__ pos, int H, T* __restrict__ out, int ldo, int blocked,
@@ -650,17 +665,33 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
   const int G = H / KVH;
   int RB = (dtype == SSD_DTYPE_BF16 ? ATTB_MAXQ : ATT_MAXQ) / G;
   if (RB < 1) return SSD_ERR_SHAPE;
+  // bf16 rows beyond a decode block: several 16-query tiles per item (the rows of an item share one
+  // local-KV group when there is one)
+  int QT = 1;
+  if (dtype == SSD_DTYPE_BF16 && !out_blocked && rb.M > RB) {
+    QT = 2;
+    while (QT > 1 && local_kv && (group_rows % (QT * RB) != 0)) QT /= 2;
+    RB *= QT;
+  }
   if (group_rows > 0) {
     // a row block must not straddle two groups
     while (RB > 1 && group_rows % RB != 0) --RB;
   }
   const int nsplit = attention_nsplit(max_ctx);
   const dim3 grid(KVH, nsplit, (rb.M + RB - 1) / RB);
+#define ATT_MULTI(HD, Q)                                                                                         \
+  hipLaunchKernelGGL((attn_partial_multi_kernel<HD, Q>), grid, dim3(256), 0, s, (const bf16_t*)q, ldq,            \
+                     (const bf16_t*)kv.pool, kv.page_table, kv.page_size, kv.n_lpages, L, layer, H, KVH, rb.M,    \
+                     rb.nrows, rb.pos, RB, nsplit, (const bf16_t*)local_kv, local_start, group_rows, part, rb.stop)
 #define ATT_LAUNCH(T, HD)                                                                                        \
   do {                                                                                                           \
-    hipLaunchKernelGGL((attn_partial_kernel<T, HD>), grid, dim3(256), 0, s, (const T*)q, ldq, (const T*)kv.pool, \
-                       kv.page_table, kv.page_size, kv.n_lpages, L, layer, H, KVH, rb.M, rb.nrows, rb.pos, RB,    \
-                       nsplit, (const T*)local_kv, local_start, group_rows, part, rb.stop);                      \
+    if (QT == 4) ATT_MULTI(HD, 4);                                                                               \
+    else if (QT == 2) ATT_MULTI(HD, 2);                                                                          \
+    else                                                                                                         \
+      hipLaunchKernelGGL((attn_partial_kernel<T, HD>), grid, dim3(256), 0, s, (const T*)q, ldq,                  \
+                         (const T*)kv.pool, kv.page_table, kv.page_size, kv.n_lpages, L, layer, H, KVH, rb.M,    \
+                         rb.nrows, rb.pos, RB, nsplit, (const T*)local_kv, local_start, group_rows, part,        \
+                         rb.stop);                                                                               \
     hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(rb.M, H), dim3(HD), 0, s, part, nsplit, rb.M, rb.nrows, \
                        rb.pos, H, (T*)out, ldo, out_blocked ? 1 : 0, rb.stop);                                  \
   } while (0)
@@ -670,6 +701,7 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
     if (head_dim == 128) ATT_LAUNCH(float, 128); else ATT_LAUNCH(float, 64);
   }
 #undef ATT_LAUNCH
+#undef ATT_MULTI
   return last_launch();
 }
 
