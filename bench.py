@@ -31,7 +31,7 @@ HBM_PEAK_GBPS = 8000.0
 # reads on the same counters); valid only for the kernel source they were taken on.
 PMC_TRAFFIC = {
     "dec_gemm_kernel<DEC_SWIGLU>": {"source": "self_speculative_layer_amd/csrc/decode.hip",
-                                    "sha1_prefix": "4bd56e8f8523", "fetch_kib": 88427.1, "write_kib": 61.8,
+                                    "sha1_prefix": "559b8986cd02", "fetch_kib": 88425.7, "write_kib": 61.8,
                                     "fetch_scale": 2.0, "write_scale": 1.0},
 }
 DOMINANT = "dec_gemm_kernel<DEC_SWIGLU>"
