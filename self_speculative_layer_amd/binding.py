@@ -16,7 +16,8 @@ ERROR_NAMES = {-1: "SSD_ERR_ARG", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_CAPACITY", -
 EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_packed_bf16_bytes", "ssd_pack_bf16", "ssd_kv_pool_bytes",
            "ssd_workspace_bytes", "ssd_seq_create",
            "ssd_seq_destroy", "ssd_prefill", "ssd_decode_ar", "ssd_draft", "ssd_verify", "ssd_accept", "ssd_commit",
-           "ssd_score_masks", "ssd_row_stats", "ssd_read_state", "ssd_read_output", "ssd_last_error",
+           "ssd_score_masks", "ssd_uniform_mask", "ssd_swift_propose", "ssd_swift_search", "ssd_row_stats",
+           "ssd_read_state", "ssd_read_output", "ssd_last_error",
            "ssd_profile_enable", "ssd_profile_disable", "ssd_profile_read"]
 
 
@@ -81,6 +82,9 @@ def lib():
             "ssd_accept": [P, P, P, P, P, I, F, U64, P, P, P],
             "ssd_commit": [P, P, P, P],
             "ssd_score_masks": [P, P, I, P, I, I, P, P, P],
+            "ssd_uniform_mask": [I, I, P],
+            "ssd_swift_propose": [I, I, U64, I, I, P],
+            "ssd_swift_search": [P, P, I, I, P, I, I, I, I, F, U64, P, ctypes.POINTER(F), ctypes.POINTER(I), P],
             "ssd_row_stats": [P, I, I, F, U64, ctypes.c_int32, P, P],
             "ssd_read_state": [P, ctypes.POINTER(ssd_state), P],
             "ssd_read_output": [P, P, I, ctypes.POINTER(I), P],
@@ -209,6 +213,33 @@ def ssd_score_masks(seq, masks, window, pos0, gamma, scores, best, stream=None):
     m = np.ascontiguousarray(np.asarray(masks, dtype=np.uint8))
     check(lib().ssd_score_masks(seq, m.ctypes.data_as(ctypes.c_void_p), m.shape[0], _ptr(window), pos0, gamma,
                                 _ptr(scores), _ptr(best), _stream(stream)))
+
+
+def ssd_uniform_mask(n_layers, n_skip):
+    import numpy as np
+    m = np.zeros(2 * n_layers, np.uint8)
+    check(lib().ssd_uniform_mask(n_layers, n_skip, m.ctypes.data_as(ctypes.c_void_p)))
+    return m
+
+
+def ssd_swift_propose(n_layers, n_skip, seed, step, cand):
+    import numpy as np
+    m = np.zeros(2 * n_layers, np.uint8)
+    check(lib().ssd_swift_propose(n_layers, n_skip, seed, step, cand, m.ctypes.data_as(ctypes.c_void_p)))
+    return m
+
+
+def ssd_swift_search(seq, window, pos0, gamma, init_mask, n_skip, n_cand, max_steps, patience, target, seed,
+                     n_layers, stream=None):
+    """Returns (best mask, best score, steps run)."""
+    import numpy as np
+    im = np.ascontiguousarray(np.asarray(init_mask, dtype=np.uint8))
+    out = np.zeros(2 * n_layers, np.uint8)
+    sc, ns = F(0.0), I(0)
+    check(lib().ssd_swift_search(seq, _ptr(window), pos0, gamma, im.ctypes.data_as(ctypes.c_void_p), n_skip, n_cand,
+                                 max_steps, patience, target, seed, out.ctypes.data_as(ctypes.c_void_p),
+                                 ctypes.byref(sc), ctypes.byref(ns), _stream(stream)))
+    return out, float(sc.value), int(ns.value)
 
 
 def ssd_row_stats(logits, rows, V, temperature, seed, iteration, stats, stream=None):

@@ -65,6 +65,8 @@ struct Workspace {
   unsigned* dec_ctr;     // attention merge counters [16][KVH], zero between launches
   StatRec* stat_recs;    // row statistics: segment records [rows][segments]
   unsigned* stat_ctr;    //   and per-row counters, zero between launches
+  float* swift_scores;   // layer-set search: one step's scores [64]
+  int32_t* swift_best;   //   and its best index
 };
 
 struct ssd_seq {
@@ -122,6 +124,8 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.dec_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)16 * d.n_kv_heads);
   t.stat_recs = (StatRec*)take(sizeof(StatRec) * (size_t)R * stat_segments(V));
   t.stat_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)R);
+  t.swift_scores = (float*)take(sizeof(float) * 64);
+  t.swift_best = (int32_t*)take(sizeof(int32_t) * 4);
   if (w) *w = t;
   return off;
 }
@@ -670,6 +674,106 @@ extern "C" int ssd_score_masks(ssd_seq* q, const uint8_t* masks_host, int n_mask
   // the host row lists must outlive the copy
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(SSD_ERR_HIP, "stream sync");
+  return SSD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// SWIFT layer-set search (host driver over the batched scoring pass)
+
+namespace {
+
+// Philox4x32-10 (Salmon et al., SC'11), host side: the generator of the sampling draws.
+void philox_host(uint32_t c[4], uint32_t k0, uint32_t k1) {
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0], p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0, n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1, n3 = (uint32_t)p0;
+    c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+constexpr uint32_t PURPOSE_PROPOSE = 3;
+
+void propose_layers(int L, int n_skip, uint64_t seed, int step, int cand, uint8_t* mask) {
+  std::vector<int> idx(L);
+  for (int i = 0; i < L; ++i) idx[i] = i;
+  uint32_t w[4] = {0, 0, 0, 0};
+  for (int i = 0; i < n_skip; ++i) {
+    if (i % 4 == 0) {
+      w[0] = (uint32_t)step; w[1] = (uint32_t)cand; w[2] = PURPOSE_PROPOSE; w[3] = (uint32_t)(i / 4);
+      philox_host(w, (uint32_t)seed, (uint32_t)(seed >> 32));
+    }
+    const uint64_t x = w[i % 4];
+    const int r = (int)((x * (uint64_t)(L - i)) >> 32);
+    std::swap(idx[i], idx[i + r]);
+  }
+  std::fill(mask, mask + 2 * L, (uint8_t)0);
+  for (int i = 0; i < n_skip; ++i) mask[2 * idx[i]] = mask[2 * idx[i] + 1] = 1;
+}
+
+}  // namespace
+
+extern "C" int ssd_uniform_mask(int n_layers, int n_skip, uint8_t* mask_host) {
+  CHECK_ARG(mask_host && n_layers > 0 && n_skip >= 0 && n_skip <= n_layers, "bad argument");
+  std::fill(mask_host, mask_host + 2 * n_layers, (uint8_t)0);
+  for (int i = 0; i < n_skip; ++i) {
+    const int l = (int)(((int64_t)2 * i + 1) * n_layers / (2 * (int64_t)n_skip));
+    mask_host[2 * l] = mask_host[2 * l + 1] = 1;
+  }
+  return SSD_OK;
+}
+
+extern "C" int ssd_swift_propose(int n_layers, int n_skip, uint64_t seed, int step, int cand, uint8_t* mask_host) {
+  CHECK_ARG(mask_host && n_layers > 0 && n_skip >= 0 && n_skip <= n_layers && step >= 0 && cand >= 0,
+            "bad argument");
+  propose_layers(n_layers, n_skip, seed, step, cand, mask_host);
+  return SSD_OK;
+}
+
+extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0, int gamma,
+                                const uint8_t* init_mask_host, int n_skip, int n_cand, int max_steps, int patience,
+                                float target, uint64_t seed, uint8_t* best_mask_host, float* best_score,
+                                int* n_steps, hipStream_t s) {
+  CHECK_ARG(q && window_dev && init_mask_host && best_mask_host && best_score && n_steps, "null argument");
+  const int L = q->m->d.n_layers;
+  CHECK_ARG(n_skip >= 0 && n_skip <= L && n_cand >= 1 && n_cand + 1 <= 64 && max_steps >= 1 && patience >= 1,
+            "bad search parameters");
+  if ((n_cand + 1) * gamma > q->max_rows) return fail(SSD_ERR_CAPACITY, "(n_cand + 1) * gamma exceeds max_rows");
+  const size_t ML = 2 * (size_t)L;
+  std::vector<uint8_t> inc(init_mask_host, init_mask_host + ML), masks((n_cand + 1) * ML);
+  std::vector<float> sc(n_cand + 1);
+  float inc_score = 0.f;
+  int unimproved = 0, t = 0;
+  while (t < max_steps) {
+    int off = 0;
+    if (t == 0) {
+      std::copy(inc.begin(), inc.end(), masks.begin());
+      off = 1;
+    }
+    for (int c = 0; c < n_cand; ++c) propose_layers(L, n_skip, seed, t, c, masks.data() + (off + c) * ML);
+    const int nm = n_cand + off;
+    TRY(ssd_score_masks(q, masks.data(), nm, window_dev, pos0, gamma, q->w.swift_scores, q->w.swift_best, s));
+    if (hipMemcpy(sc.data(), q->w.swift_scores, sizeof(float) * nm, hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(SSD_ERR_HIP, "read scores");
+    if (t == 0) inc_score = sc[0];
+    int k = off;
+    for (int c = off + 1; c < nm; ++c)
+      if (sc[c] > sc[k]) k = c;
+    if (sc[k] > inc_score) {
+      std::copy(masks.begin() + k * ML, masks.begin() + (k + 1) * ML, inc.begin());
+      inc_score = sc[k];
+      unimproved = 0;
+    } else {
+      ++unimproved;
+    }
+    ++t;
+    if (inc_score > target || unimproved >= patience) break;
+  }
+  std::copy(inc.begin(), inc.end(), best_mask_host);
+  *best_score = inc_score;
+  *n_steps = t;
   return SSD_OK;
 }
 
