@@ -69,6 +69,10 @@ SCORING = {
                      desc="LLaMA-2-13B-shaped bf16 decoder, SWIFT matchness scoring of 16 seeded candidate plans "
                           "(16-24 of 40 layers skipped each) over a 32-token window greedily generated after a "
                           "1024-token random prompt"),
+    "swift13b": dict(shape="llama2-13b-shape", prompt=1024, gamma=32, n_masks=16, skip_lo=20, skip_hi=20, search=True,
+                     desc="LLaMA-2-13B-shaped bf16 decoder, SWIFT random search: 15 proposals of 20 skipped layers per "
+                          "step scored on a 32-token window greedily generated after a 1024-token random prompt, "
+                          "starting from the uniform plan"),
 }
 
 
@@ -352,8 +356,25 @@ def run_scoring(args):
     scores = torch.zeros(nm, dtype=torch.float32, device=dev)
     best = torch.zeros(1, dtype=torch.int32, device=dev)
 
+    search = wl.get("search", False)
+    n_skip = wl["skip_lo"]
+    init = B.ssd_uniform_mask(shape.n_layers, n_skip)
+    search_out = {}
+
+    used = []                                     # the masks each call scored
+
     def step():
-        B.ssd_score_masks(seq.handle, masks, window, P - 1, gamma, scores, best)
+        if search:
+            # one search step per call (its step 0: the starting plan and 15 proposals, a new seed each call)
+            sd = synth.SEED_MASKS + len(used)
+            bm, bs, ns = B.ssd_swift_search(seq.handle, window, P - 1, gamma, init, n_skip, nm - 1, 1, 1, 2.0, sd,
+                                            shape.n_layers)
+            search_out.update(best=bm, score=bs)
+            used.append(np.stack([init] + [B.ssd_swift_propose(shape.n_layers, n_skip, sd, 0, c)
+                                           for c in range(nm - 1)]))
+        else:
+            B.ssd_score_masks(seq.handle, masks, window, P - 1, gamma, scores, best)
+            used.append(masks)
 
     K, W = args.steps, args.warmup
     for _ in range(W):
@@ -366,16 +387,18 @@ def run_scoring(args):
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / K
     # measured region: the batched gate/up launches with dispatch events
-    keep_mlp = (masks[:, 1::2] == 0).sum(axis=0)           # candidates running each layer's MLP
-    n_gu = int((keep_mlp > 0).sum())
-    B.ssd_profile_enable(B.SSD_PROF_GEMM_SWIGLU, K * n_gu + 8)
+    B.ssd_profile_enable(B.SSD_PROF_GEMM_SWIGLU, K * shape.n_layers + 8)
+    n_before = len(used)
     for _ in range(K):
         step()
     torch.cuda.synchronize()
     B.ssd_profile_disable()
     prof_ms, prof_n, prof_bytes = B.ssd_profile_read()
     D, F = shape.d_model, shape.ffn_dim
-    flops = float(sum(2.0 * (c * gamma) * 2 * F * D for c in keep_mlp if c > 0)) * K
+    flops = 0.0
+    for mk in used[n_before:]:
+        keep_mlp = (mk[:, 1::2] == 0).sum(axis=0)         # candidates running each layer's MLP
+        flops += float(sum(2.0 * (c * gamma) * 2 * F * D for c in keep_mlp if c > 0))
     gu_ms = prof_ms
     tflops = flops / (gu_ms / 1e3) / 1e12 if gu_ms > 0 else 0.0
     gbps = prof_bytes / (gu_ms / 1e3) / 1e9 if gu_ms > 0 else 0.0
@@ -392,12 +415,15 @@ def run_scoring(args):
                  "flop_per_step": flops / K, "bytes_per_launch": round(prof_bytes / max(prof_n, 1)),
                  "measured": "dispatch-timestamp events on every launch of the kernel in %d further steps" % K})
     result = {
-        "metric": "mask-scoring steps/s (16 candidate plans x 32-token window)",
+        "metric": ("SWIFT search steps/s (15 proposals x 32-token window)" if search else
+                   "mask-scoring steps/s (16 candidate plans x 32-token window)"),
         "value": round(1e3 / ms, 4), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded random-init weights, uniform random prompt, seeded masks)",
         "config": {"workload": wl["desc"], "prompt_len": P, "gamma": gamma, "n_masks": nm},
-        "roofline": roof, "scores": [round(float(x), 5) for x in scores.cpu()], "best": int(best.item()),
+        "roofline": roof,
+        "scores": ([round(search_out.get("score", 0.0), 5)] if search else [round(float(x), 5) for x in scores.cpu()]),
+        "best": (np.nonzero(search_out["best"][::2])[0].tolist() if search else int(best.item())),
         "prefill_ms": round(prefill_ms, 2),
     }
     seq.close()
