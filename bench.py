@@ -147,7 +147,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="default 64 (SSD steps), 8 (scoring steps)")
     ap.add_argument("--warmup", type=int, default=None, help="default 8 (SSD steps), 2 (scoring steps)")
-    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS) + sorted(SCORING))
+    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS) + sorted(SCORING) + ["exit7b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ar-steps", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -174,6 +174,11 @@ def main():
     from synth import device as sdev
     from self_speculative_layer_amd import binding as B
 
+    if args.workload == "exit7b":
+        args.steps = 64 if args.steps is None else args.steps
+        args.warmup = 8 if args.warmup is None else args.warmup
+        run_exit(args)
+        return
     if args.workload in SCORING:
         args.steps = 8 if args.steps is None else args.steps
         args.warmup = 2 if args.warmup is None else args.warmup
@@ -313,6 +318,60 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shape, wl, mask)
+    print(json.dumps(result), flush=True)
+
+
+def run_exit(args):
+    """Lossy early-exit decoding (no verification): one step = one token through
+    layers 0..7 of the 7B shape, the shared final norm and LM head."""
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import device as sdev
+    from self_speculative_layer_amd import binding as B
+
+    shape = synth.LLAMA7B
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    tensors = sdev.build_weights(shape)
+    model = B.Model(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
+                    shape.vocab, shape.dtype, tensors)
+    K, W, E, P = args.steps, args.warmup, 8, 512
+    seq = B.Sequence(model, max_ctx=P + K + W + 64, max_rows=512, max_draft=1, device=dev)
+    B.ssd_prefill(seq.handle, torch.from_numpy(synth.prompt_tokens(P, shape.vocab)).to(dev))
+    for _ in range(W):
+        B.ssd_decode_exit(seq.handle, None, E)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(K):
+        B.ssd_decode_exit(seq.handle, None, E)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / K
+    B.ssd_profile_enable(B.SSD_PROF_GEMM_SWIGLU, K * E + 8)
+    for _ in range(K):
+        B.ssd_decode_exit(seq.handle, None, E)
+    torch.cuda.synchronize()
+    B.ssd_profile_disable()
+    prof_ms, prof_n, prof_bytes = B.ssd_profile_read()
+    achieved = prof_bytes / (prof_ms / 1e3) / 1e9 if prof_ms > 0 else 0.0
+    step_bytes = E * shape.layer_param_count() * 2 + shape.vocab * shape.d_model * 2
+    result = {
+        "metric": "lossy early-exit tokens/s (batch 1, exit at layer 8, no verification)",
+        "value": round(1e3 / ms, 3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded random-init weights and uniform random prompt)",
+        "config": {"workload": "LLaMA-2-7B-shaped bf16 decoder, lossy early exit at E=8, greedy, 512-token prompt"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": DOMINANT + " (decode-block gate/up projection + SwiGLU)", "launches": prof_n,
+                     "avg_launch_us": round(prof_ms / max(prof_n, 1) * 1e3, 3)},
+        "step_GBps": round(step_bytes / (ms / 1e3) / 1e9, 1),
+    }
+    seq.close()
+    model.close()
     print(json.dumps(result), flush=True)
 
 

@@ -187,6 +187,14 @@ int ssd_prefill(ssd_seq* seq, const int32_t* tokens_dev, int n, float temperatur
 int ssd_decode_ar(ssd_seq* seq, float temperature, uint64_t seed, float* logits_dev,
                   hipStream_t stream);
 
+/* Lossy early-exit decoding (next row f4; [LayerSkip] §3 first mode, §4): one step as ssd_decode_ar
+ * but through the plan's sub-layers only (skip_mask_host[2L], or exit_layer E when it is NULL) and the
+ * shared final norm and LM head; the token is committed without verification.  Keys and values are
+ * written for the kept sub-layers only (later steps of the same plan read nothing else).  The prompt is
+ * prefilled by ssd_prefill with the full model. */
+int ssd_decode_exit(ssd_seq* seq, const uint8_t* skip_mask_host, int exit_layer, float temperature,
+                    uint64_t seed, float* logits_dev, hipStream_t stream);
+
 /* Draft phase (row a1; [LayerSkip] §3.1, [SWIFT] §3.1 and §4.2).
  * Plan: skip_mask_host[2L] (entry 2l = skip the attention sub-layer of layer
  * l, entry 2l+1 = skip its MLP sub-layer; [SWIFT] Appendix A Fig. 10), or, when

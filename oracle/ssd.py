@@ -188,6 +188,28 @@ def ar_generate(model, prompt, n_gen, T=0.0, seed=3, capacity=None):
     return out, kv
 
 
+def exit_generate(model, prompt, n_gen, mask, T=0.0, seed=3, capacity=None):
+    """Lossy early-exit decoding (LayerSkip blog §3, first inference mode): after
+    the full-model prefill, every token comes from the plan's sub-layers alone
+    (with the shared final norm and LM head) and is kept without verification.
+    Reading: the prompt is processed by the full model (its keys/values below the
+    exit are the same either way); only the tokens after the first are
+    generated through the plan."""
+    P = len(prompt)
+    kv = mdl.KVCache(model.shape, capacity or (P + n_gen + 1))
+    z = prefill(model, kv, prompt)
+    out = [pick(z, T, seed, 0, 0, philox.PURPOSE_SAMPLE)]
+    zs = [z]
+    it = 1
+    while len(out) < n_gen:
+        n = P + len(out)
+        z = mdl.forward(model, [out[-1]], [n - 1], kv, mask)[0]
+        zs.append(z)
+        out.append(pick(z, T, seed, it, 0, philox.PURPOSE_SAMPLE))
+        it += 1
+    return out, np.array(zs)
+
+
 def ssd_generate(model, prompt, n_gen, mask, d, tau=0.0, T=0.0, seed=3, reuse=True, capacity=None,
                  on_iteration=None):
     """Self-speculative decoding loop (LayerSkip blog §3.3): draft, verify, accept,

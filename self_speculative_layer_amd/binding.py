@@ -15,7 +15,8 @@ ERROR_NAMES = {-1: "SSD_ERR_ARG", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_CAPACITY", -
 # Every symbol include/ssd.h declares.
 EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_packed_bf16_bytes", "ssd_pack_bf16", "ssd_kv_pool_bytes",
            "ssd_workspace_bytes", "ssd_seq_create",
-           "ssd_seq_destroy", "ssd_prefill", "ssd_decode_ar", "ssd_draft", "ssd_verify", "ssd_accept", "ssd_commit",
+           "ssd_seq_destroy", "ssd_prefill", "ssd_decode_ar", "ssd_decode_exit", "ssd_draft", "ssd_verify",
+           "ssd_accept", "ssd_commit",
            "ssd_score_masks", "ssd_uniform_mask", "ssd_swift_propose", "ssd_swift_search", "ssd_row_stats",
            "ssd_read_state", "ssd_read_output", "ssd_last_error",
            "ssd_profile_enable", "ssd_profile_disable", "ssd_profile_read"]
@@ -77,6 +78,7 @@ def lib():
             "ssd_seq_destroy": [P],
             "ssd_prefill": [P, P, I, F, U64, P, P],
             "ssd_decode_ar": [P, F, U64, P, P],
+            "ssd_decode_exit": [P, P, I, F, U64, P, P],
             "ssd_draft": [P, P, I, I, F, F, U64, P, P, P, P],
             "ssd_verify": [P, P, I, I, P, P, I, P, P],
             "ssd_accept": [P, P, P, P, P, I, F, U64, P, P, P],
@@ -183,6 +185,12 @@ def ssd_prefill(seq, tokens, temperature=0.0, seed=0, last_logits=None, stream=N
 
 def ssd_decode_ar(seq, temperature=0.0, seed=0, logits=None, stream=None):
     check(lib().ssd_decode_ar(seq, temperature, seed, _ptr(logits), _stream(stream)))
+
+
+def ssd_decode_exit(seq, skip_mask, exit_layer, temperature=0.0, seed=0, logits=None, stream=None):
+    keep, mp = _mask_arg(skip_mask)
+    check(lib().ssd_decode_exit(seq, mp, -1 if exit_layer is None else exit_layer, temperature, seed, _ptr(logits),
+                                _stream(stream)))
 
 
 def ssd_draft(seq, skip_mask, exit_layer, d, conf_thresh, temperature, seed, draft_tokens, draft_logits, n_drafted,

@@ -479,29 +479,47 @@ extern "C" int ssd_prefill(ssd_seq* q, const int32_t* tokens_dev, int n, float t
   return SSD_OK;
 }
 
-extern "C" int ssd_decode_ar(ssd_seq* q, float temperature, uint64_t seed, float* logits_dev, hipStream_t s) {
-  CHECK_ARG(q, "null argument");
-  CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
+namespace {
+
+// One committed token through the plan's sub-layers (mask == nullptr: the full model).
+int decode_one(ssd_seq* q, const uint8_t* mask, float temperature, uint64_t seed, float* logits_dev, hipStream_t s) {
   const ssd_model_desc& d = q->m->d;
   const Workspace& w = q->w;
   TRY(launch_single_row_prep(w.st, w.pos1, w.tok1, q->max_ctx, s));
   float* lg = logits_dev ? logits_dev : w.logits1;
   if (dec_usable(q, 1)) {
     std::vector<int> ent;
-    plan_entries(ent, 0, d.n_layers, nullptr);
+    plan_entries(ent, 0, d.n_layers, mask);
     TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, dec_gain(q->m, ent, 0, true), nullptr, s));
     TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, ent, 0, ent.size(), true, nullptr, s));
     TRY(dec_logits(q, 1, nullptr, lg, nullptr, s));
   } else {
     TRY(launch_embed(d.dtype, d.embed, w.tok1, d.vocab, w.h1, d.d_model, 1, d.d_model, nullptr, nullptr, s));
     Block b{w.h1, RowBlock{1, nullptr, w.pos1, nullptr, nullptr}, nullptr, 0, 0};
-    TRY(run_layers(q, b, 0, d.n_layers, nullptr, s));
+    TRY(run_layers(q, b, 0, d.n_layers, mask, s));
     TRY(final_logits(q, w.h1, 1, nullptr, lg, nullptr, s));
   }
   TRY(launch_row_stats_seg(lg, d.vocab, 1, d.vocab, temperature, seed, &w.st->iteration, 0, 0, PURPOSE_SAMPLE,
                            w.stats, w.stat_recs, w.stat_ctr, nullptr, DraftStep{}, s));
   TRY(launch_pick_commit(w.stats, w.st, w.log, q->log_cap, 0, 0, s));
   return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" int ssd_decode_ar(ssd_seq* q, float temperature, uint64_t seed, float* logits_dev, hipStream_t s) {
+  CHECK_ARG(q, "null argument");
+  CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
+  return decode_one(q, nullptr, temperature, seed, logits_dev, s);
+}
+
+extern "C" int ssd_decode_exit(ssd_seq* q, const uint8_t* skip_mask_host, int exit_layer, float temperature,
+                               uint64_t seed, float* logits_dev, hipStream_t s) {
+  CHECK_ARG(q, "null argument");
+  CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
+  std::vector<uint8_t> mask;
+  CHECK_ARG(plan_mask(q->m, skip_mask_host, exit_layer, mask) >= 0, "exit_layer out of range");
+  return decode_one(q, mask.data(), temperature, seed, logits_dev, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -423,3 +423,34 @@ def test_swift_search_matches_oracle(shape):
     assert abs(gscore - oscore) <= 2.0 / gamma
     seq.close()
     g.close()
+
+
+@pytest.mark.parametrize("shape", [BF16_HD64, BF16_HD128, F32_GQA], ids=lambda s: s.name)
+def test_decode_exit_matches_oracle(shape):
+    """Lossy early-exit decoding (ssd_decode_exit, exit at layer 1 and a skip mask)
+    against the oracle's exit_generate: tokens by the margin rule, each step's
+    logits within the logit tolerance up to the first excused mismatch."""
+    g = gpu_model(shape)
+    o = omodel.Model.synthetic(shape)
+    L, V = shape.n_layers, shape.vocab
+    P, n = 24, 16
+    prompt = synth.prompt_tokens(P, V)
+    for exit_layer, mask in ((1, None), (None, synth.mask_from_layers(L, [L - 2]))):
+        om = synth.mask_exit(L, exit_layer) if mask is None else mask
+        ref, ref_z = ossd.exit_generate(o, prompt, n, om)
+        seq = B.Sequence(g, max_ctx=P + n + 16, max_rows=64, max_draft=2)
+        B.ssd_prefill(seq.handle, dev(prompt))
+        zs = []
+        for _ in range(n - 1):
+            lg = torch.zeros(V, dtype=torch.float32, device="cuda")
+            B.ssd_decode_exit(seq.handle, mask, exit_layer, 0.0, 0, lg)
+            zs.append(lg)
+        out = [int(x) for x in B.ssd_read_output(seq.handle, n)]
+        assert B.ssd_read_state(seq.handle).error_flags == 0
+        stop = check_greedy_tokens(out, ref, ref_z)
+        upto = n - 1 if stop is None else stop - 1
+        for k in range(upto):
+            err = np.abs(zs[k].cpu().numpy() - ref_z[k + 1]).max()
+            assert err < logit_tol(shape), (k, err)
+        seq.close()
+    g.close()

@@ -1,5 +1,6 @@
 """Pins of the oracle's self-speculative loop: the pages' invariants, exact
 enumeration of the accept rule, and chi-square tests of the sampled output."""
+import dataclasses
 import itertools
 
 import numpy as np
@@ -379,3 +380,30 @@ def test_scoring_ties_pick_lowest_index(scoring_setup):
     mk = synth.mask_from_layers(4, [2])
     scores, best = ssd.score_masks(m, kv, window, pos0, [mk, mk, np.zeros(8, np.uint8), np.zeros(8, np.uint8)])
     assert best == 2
+
+
+# ---------------------------------------------------------------- lossy early exit
+def test_exit_generate_empty_plan_is_ar():
+    """With nothing skipped the lossy mode is plain AR (greedy and sampled)."""
+    m = _model(synth.TINY)
+    prompt = synth.prompt_tokens(16, synth.TINY.vocab)
+    for T in (0.0, 1.0):
+        ar, _ = ssd.ar_generate(m, prompt, 12, T=T)
+        ex, _ = ssd.exit_generate(m, prompt, 12, np.zeros(8, np.uint8), T=T)
+        assert ex == ar
+
+
+def test_exit_generate_equals_truncated_model():
+    """Exit at E: after the first token, each step's logits are those of a model
+    holding only layers 0..E-1 (same final norm and LM head), prefilled with the
+    prompt and the tokens generated so far."""
+    m = _model(synth.TINY)
+    E = 2
+    prompt = synth.prompt_tokens(16, synth.TINY.vocab)
+    ex, zs = ssd.exit_generate(m, prompt, 6, synth.mask_exit(4, E))
+    trunc = mdl.Model.synthetic(dataclasses.replace(synth.TINY, n_layers=E))   # layers 0..E-1, same tensors
+    for k in range(1, 6):
+        seq = list(prompt) + ex[:k]
+        z = ssd.prefill(trunc, mdl.KVCache(trunc.shape, len(seq) + 1), seq)
+        assert np.max(np.abs(z - zs[k])) < 1e-9
+        assert ex[k] == int(np.argmax(z))
