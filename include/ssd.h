@@ -264,8 +264,9 @@ int ssd_score_masks(ssd_seq* seq, const uint8_t* masks_host, int n_masks, const 
  * (with a periodic Bayesian step, not implemented here), scores them by
  * matchness on the last context window and keeps the best, stopping at a step
  * limit, after a run of steps without improvement, or above a matchness target.
- * Readings: candidates skip whole layers (both bits of a layer); a step proposes
- * n_cand uniformly random n_skip-subsets of the L layers; the incumbent is
+ * Readings: candidates skip n_skip whole layers (both bits of a layer) or, with
+ * sublayers != 0, n_skip of the 2L attention / MLP sub-layers ([SWIFT] Appendix
+ * A Fig. 10); a step proposes n_cand uniformly random such sets; the incumbent is
  * replaced by the best proposal of a step (lowest index on ties) only when its
  * score is strictly higher; the uniform starting plan skips layers
  * floor((2 i + 1) L / (2 n_skip)), i = 0..n_skip-1.  Host-only helpers below
@@ -274,20 +275,23 @@ int ssd_score_masks(ssd_seq* seq, const uint8_t* masks_host, int n_masks, const 
 /* mask_host[2L] = the uniform plan skipping n_skip of n_layers layers (0 <= n_skip <= n_layers). */
 int ssd_uniform_mask(int n_layers, int n_skip, uint8_t* mask_host);
 
-/* mask_host[2L] = proposal `cand` of search step `step`: a Fisher-Yates draw of n_skip layers, position i
- * taking (x_i * (L - i)) >> 32 from the Philox word x_i at key seed, counter (step, cand, 3, i / 4),
- * word i % 4 (the sampling draws' generator; purpose 3 = proposal). */
-int ssd_swift_propose(int n_layers, int n_skip, uint64_t seed, int step, int cand, uint8_t* mask_host);
+/* mask_host[2L] = proposal `cand` of search step `step`: a Fisher-Yates draw of n_skip of the N items
+ * (sublayers == 0: the N = L layers, both bits of a drawn layer set; otherwise the N = 2L sub-layers, bit i
+ * for item i), position i taking (x_i * (N - i)) >> 32 from the Philox word x_i at key seed, counter
+ * (step, cand, 3, i / 4), word i % 4 (the sampling draws' generator; purpose 3 = proposal). */
+int ssd_swift_propose(int n_layers, int n_skip, int sublayers, uint64_t seed, int step, int cand,
+                      uint8_t* mask_host);
 
 /* Random search on the window (same contract as ssd_score_masks: window_dev[gamma + 1] committed tokens
- * at positions pos0.., the cache holding the full model's keys/values before pos0).  Step t scores its
+ * at positions pos0.., the cache holding the full model's keys/values before pos0); proposals as
+ * ssd_swift_propose with the same sublayers flag.  Step t scores its
  * n_cand proposals (step 0 also the starting plan init_mask_host) in one batched scoring pass; the
  * search stops after max_steps steps, after `patience` consecutive steps without improvement, or as
  * soon as the incumbent's score exceeds `target`.  Requires (n_cand + 1) * gamma <= max_rows and
  * n_cand + 1 <= 64.  Out: best_mask_host[2L] (the incumbent), *best_score, *n_steps.  Synchronises
  * the stream once per step (the scores decide the next step). */
 int ssd_swift_search(ssd_seq* seq, const int32_t* window_dev, int pos0, int gamma, const uint8_t* init_mask_host,
-                     int n_skip, int n_cand, int max_steps, int patience, float target, uint64_t seed,
+                     int n_skip, int sublayers, int n_cand, int max_steps, int patience, float target, uint64_t seed,
                      uint8_t* best_mask_host, float* best_score, int* n_steps, hipStream_t stream);
 
 /* Row statistics (row a3) of rows logits rows of length V, as used inside

@@ -9,7 +9,9 @@ unimproved steps, 0.95).  The periodic Bayesian-optimisation step of the pages
 is not part of this search.
 
 Readings taken (the pages give no procedure beyond the above):
-  * a candidate skips whole layers (both sub-layers), n_skip of them;
+  * a candidate skips n_skip whole layers (both sub-layers), or n_skip of the
+    2L attention / MLP sub-layers when the search runs over sub-layers (SWIFT
+    digest Appendix A, Fig. 10: the two kinds are skipped separately);
   * the uniform starting plan (SWIFT digest §1, §4.1.1: "uniform layer
     skipping") skips layers floor((2 i + 1) L / (2 n_skip)), i = 0..n_skip-1,
     i.e. the centres of n_skip equal slices of the stack;
@@ -42,17 +44,26 @@ def uniform_skip_layers(L, n_skip):
     return [((2 * i + 1) * L) // (2 * n_skip) for i in range(n_skip)]
 
 
-def propose_layers(L, n_skip, seed, step, cand):
-    """A uniformly random n_skip-subset of range(L) (Fisher-Yates on Philox words)."""
+def propose_layers(N, n_skip, seed, step, cand):
+    """A uniformly random n_skip-subset of range(N) (Fisher-Yates on Philox words);
+    N = L layers or 2L sub-layers."""
     x = philox.words(seed, step, cand, PURPOSE_PROPOSE, n_skip)
-    idx = list(range(L))
+    idx = list(range(N))
     for i in range(n_skip):
-        r = (int(x[i]) * (L - i)) >> 32
+        r = (int(x[i]) * (N - i)) >> 32
         idx[i], idx[i + r] = idx[i + r], idx[i]
     return sorted(idx[:n_skip])
 
 
-def search(score_fn, L, init_mask, n_skip, n_cand, max_steps, patience, target, seed):
+def propose_mask(L, n_skip, seed, step, cand, sublayers=False):
+    if sublayers:
+        m = np.zeros(2 * L, np.uint8)
+        m[propose_layers(2 * L, n_skip, seed, step, cand)] = 1
+        return m
+    return layers_to_mask(L, propose_layers(L, n_skip, seed, step, cand))
+
+
+def search(score_fn, L, init_mask, n_skip, n_cand, max_steps, patience, target, seed, sublayers=False):
     """Random search.  score_fn(list of masks) -> scores.  Returns the final
     incumbent mask, its score, the number of steps run and the per-step
     history [(proposal masks, their scores, incumbent score after the step)]."""
@@ -62,7 +73,7 @@ def search(score_fn, L, init_mask, n_skip, n_cand, max_steps, patience, target, 
     history = []
     t = 0
     while t < max_steps:
-        props = [layers_to_mask(L, propose_layers(L, n_skip, seed, t, c)) for c in range(n_cand)]
+        props = [propose_mask(L, n_skip, seed, t, c, sublayers) for c in range(n_cand)]
         if t == 0:
             sc = list(score_fn([inc] + props))
             inc_score, sc = sc[0], sc[1:]

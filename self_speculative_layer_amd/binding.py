@@ -85,8 +85,8 @@ def lib():
             "ssd_commit": [P, P, P, P],
             "ssd_score_masks": [P, P, I, P, I, I, P, P, P],
             "ssd_uniform_mask": [I, I, P],
-            "ssd_swift_propose": [I, I, U64, I, I, P],
-            "ssd_swift_search": [P, P, I, I, P, I, I, I, I, F, U64, P, ctypes.POINTER(F), ctypes.POINTER(I), P],
+            "ssd_swift_propose": [I, I, I, U64, I, I, P],
+            "ssd_swift_search": [P, P, I, I, P, I, I, I, I, I, F, U64, P, ctypes.POINTER(F), ctypes.POINTER(I), P],
             "ssd_row_stats": [P, I, I, F, U64, ctypes.c_int32, P, P],
             "ssd_read_state": [P, ctypes.POINTER(ssd_state), P],
             "ssd_read_output": [P, P, I, ctypes.POINTER(I), P],
@@ -230,22 +230,24 @@ def ssd_uniform_mask(n_layers, n_skip):
     return m
 
 
-def ssd_swift_propose(n_layers, n_skip, seed, step, cand):
+def ssd_swift_propose(n_layers, n_skip, seed, step, cand, sublayers=False):
     import numpy as np
     m = np.zeros(2 * n_layers, np.uint8)
-    check(lib().ssd_swift_propose(n_layers, n_skip, seed, step, cand, m.ctypes.data_as(ctypes.c_void_p)))
+    check(lib().ssd_swift_propose(n_layers, n_skip, 1 if sublayers else 0, seed, step, cand,
+                                  m.ctypes.data_as(ctypes.c_void_p)))
     return m
 
 
 def ssd_swift_search(seq, window, pos0, gamma, init_mask, n_skip, n_cand, max_steps, patience, target, seed,
-                     n_layers, stream=None):
+                     n_layers, sublayers=False, stream=None):
     """Returns (best mask, best score, steps run)."""
     import numpy as np
     im = np.ascontiguousarray(np.asarray(init_mask, dtype=np.uint8))
     out = np.zeros(2 * n_layers, np.uint8)
     sc, ns = F(0.0), I(0)
-    check(lib().ssd_swift_search(seq, _ptr(window), pos0, gamma, im.ctypes.data_as(ctypes.c_void_p), n_skip, n_cand,
-                                 max_steps, patience, target, seed, out.ctypes.data_as(ctypes.c_void_p),
+    check(lib().ssd_swift_search(seq, _ptr(window), pos0, gamma, im.ctypes.data_as(ctypes.c_void_p), n_skip,
+                                 1 if sublayers else 0, n_cand, max_steps, patience, target, seed,
+                                 out.ctypes.data_as(ctypes.c_void_p),
                                  ctypes.byref(sc), ctypes.byref(ns), _stream(stream)))
     return out, float(sc.value), int(ns.value)
 

@@ -714,9 +714,11 @@ void philox_host(uint32_t c[4], uint32_t k0, uint32_t k1) {
 
 constexpr uint32_t PURPOSE_PROPOSE = 3;
 
-void propose_layers(int L, int n_skip, uint64_t seed, int step, int cand, uint8_t* mask) {
-  std::vector<int> idx(L);
-  for (int i = 0; i < L; ++i) idx[i] = i;
+// n_skip of the L layers (sublayers == 0: both bits of a layer) or of the 2L sub-layers (bit i).
+void propose_layers(int L, int n_skip, int sublayers, uint64_t seed, int step, int cand, uint8_t* mask) {
+  const int N = sublayers ? 2 * L : L;
+  std::vector<int> idx(N);
+  for (int i = 0; i < N; ++i) idx[i] = i;
   uint32_t w[4] = {0, 0, 0, 0};
   for (int i = 0; i < n_skip; ++i) {
     if (i % 4 == 0) {
@@ -724,11 +726,14 @@ void propose_layers(int L, int n_skip, uint64_t seed, int step, int cand, uint8_
       philox_host(w, (uint32_t)seed, (uint32_t)(seed >> 32));
     }
     const uint64_t x = w[i % 4];
-    const int r = (int)((x * (uint64_t)(L - i)) >> 32);
+    const int r = (int)((x * (uint64_t)(N - i)) >> 32);
     std::swap(idx[i], idx[i + r]);
   }
   std::fill(mask, mask + 2 * L, (uint8_t)0);
-  for (int i = 0; i < n_skip; ++i) mask[2 * idx[i]] = mask[2 * idx[i] + 1] = 1;
+  for (int i = 0; i < n_skip; ++i) {
+    if (sublayers) mask[idx[i]] = 1;
+    else mask[2 * idx[i]] = mask[2 * idx[i] + 1] = 1;
+  }
 }
 
 }  // namespace
@@ -743,20 +748,23 @@ extern "C" int ssd_uniform_mask(int n_layers, int n_skip, uint8_t* mask_host) {
   return SSD_OK;
 }
 
-extern "C" int ssd_swift_propose(int n_layers, int n_skip, uint64_t seed, int step, int cand, uint8_t* mask_host) {
-  CHECK_ARG(mask_host && n_layers > 0 && n_skip >= 0 && n_skip <= n_layers && step >= 0 && cand >= 0,
+extern "C" int ssd_swift_propose(int n_layers, int n_skip, int sublayers, uint64_t seed, int step, int cand,
+                                 uint8_t* mask_host) {
+  CHECK_ARG(mask_host && n_layers > 0 && n_skip >= 0 && n_skip <= (sublayers ? 2 : 1) * n_layers && step >= 0 &&
+                cand >= 0,
             "bad argument");
-  propose_layers(n_layers, n_skip, seed, step, cand, mask_host);
+  propose_layers(n_layers, n_skip, sublayers, seed, step, cand, mask_host);
   return SSD_OK;
 }
 
 extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0, int gamma,
-                                const uint8_t* init_mask_host, int n_skip, int n_cand, int max_steps, int patience,
-                                float target, uint64_t seed, uint8_t* best_mask_host, float* best_score,
-                                int* n_steps, hipStream_t s) {
+                                const uint8_t* init_mask_host, int n_skip, int sublayers, int n_cand, int max_steps,
+                                int patience, float target, uint64_t seed, uint8_t* best_mask_host,
+                                float* best_score, int* n_steps, hipStream_t s) {
   CHECK_ARG(q && window_dev && init_mask_host && best_mask_host && best_score && n_steps, "null argument");
   const int L = q->m->d.n_layers;
-  CHECK_ARG(n_skip >= 0 && n_skip <= L && n_cand >= 1 && n_cand + 1 <= 64 && max_steps >= 1 && patience >= 1,
+  CHECK_ARG(n_skip >= 0 && n_skip <= (sublayers ? 2 : 1) * L && n_cand >= 1 && n_cand + 1 <= 64 && max_steps >= 1 &&
+                patience >= 1,
             "bad search parameters");
   if ((n_cand + 1) * gamma > q->max_rows) return fail(SSD_ERR_CAPACITY, "(n_cand + 1) * gamma exceeds max_rows");
   const size_t ML = 2 * (size_t)L;
@@ -770,7 +778,7 @@ extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0,
       std::copy(inc.begin(), inc.end(), masks.begin());
       off = 1;
     }
-    for (int c = 0; c < n_cand; ++c) propose_layers(L, n_skip, seed, t, c, masks.data() + (off + c) * ML);
+    for (int c = 0; c < n_cand; ++c) propose_layers(L, n_skip, sublayers, seed, t, c, masks.data() + (off + c) * ML);
     const int nm = n_cand + off;
     TRY(ssd_score_masks(q, masks.data(), nm, window_dev, pos0, gamma, q->w.swift_scores, q->w.swift_best, s));
     if (hipMemcpy(sc.data(), q->w.swift_scores, sizeof(float) * nm, hipMemcpyDeviceToHost) != hipSuccess)

@@ -392,8 +392,9 @@ def test_long_context_attention_paths_agree(shape):
     g.close()
 
 
-@pytest.mark.parametrize("shape", [BF16_HD64, F32_GQA], ids=lambda s: s.name)
-def test_swift_search_matches_oracle(shape):
+@pytest.mark.parametrize("shape,sublayers", [(BF16_HD64, False), (F32_GQA, False), (BF16_HD64, True)],
+                         ids=["bf16-hd64-gqa-layers", "f32-gqa-layers", "bf16-hd64-gqa-sublayers"])
+def test_swift_search_matches_oracle(shape, sublayers):
     """SWIFT random search (ssd_swift_search: proposals on the host, one batched
     scoring pass per step) against the oracle's search with its own scoring:
     same number of steps, same final plan, score within the scoring tolerance.
@@ -409,14 +410,14 @@ def test_swift_search_matches_oracle(shape):
     n_skip = 2 if L >= 4 else 1
     init = swift.layers_to_mask(L, swift.uniform_skip_layers(L, n_skip))
     obest, oscore, osteps, hist = swift.search(lambda ms: ossd.score_masks(o, kv, window, P - 1, ms)[0], L, init,
-                                               n_skip, n_cand, 6, 3, 1.5, 5)
+                                               n_skip, n_cand, 6, 3, 1.5, 5, sublayers)
     print("oracle: %d steps, score %.4f, best %s; per step %s" % (osteps, oscore, obest[::2],
                                                                   [np.round(h[1], 3).tolist() for h in hist]))
     seq = B.Sequence(g, max_ctx=P + gamma + 64, max_rows=(n_cand + 1) * gamma, max_draft=4)
     gout = seq.generate_ar(dev(prompt), gamma)
     assert [int(x) for x in gout] == ref
     gbest, gscore, gsteps = B.ssd_swift_search(seq.handle, dev(window), P - 1, gamma, init, n_skip, n_cand, 6, 3,
-                                               1.5, 5, L)
+                                               1.5, 5, L, sublayers=sublayers)
     print("gpu: %d steps, score %.4f, best %s" % (gsteps, gscore, gbest[::2]))
     assert gsteps == osteps
     assert np.array_equal(gbest, obest)

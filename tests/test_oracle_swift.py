@@ -109,3 +109,18 @@ def test_library_helpers_equal_the_oracle():
             for c in range(6):
                 assert np.array_equal(B.ssd_swift_propose(L, n, 12345678901, t, c),
                                       swift.layers_to_mask(L, swift.propose_layers(L, n, 12345678901, t, c)))
+                assert np.array_equal(B.ssd_swift_propose(L, n, 99, t, c, sublayers=True),
+                                      swift.propose_mask(L, n, 99, t, c, sublayers=True))
+
+
+def test_sublayer_proposals_are_uniform():
+    """Sub-layer proposals: n_skip mask bits set, each of the 2L bits equally
+    likely (chi-square over 4000 proposals of 3 of 8 sub-layers)."""
+    L, n = 4, 3
+    counts = np.zeros(2 * L)
+    for t in range(400):
+        for c in range(10):
+            m = swift.propose_mask(L, n, 31, t, c, sublayers=True)
+            assert m.sum() == n
+            counts += m
+    assert stats.chisquare(counts).pvalue > 1e-3
