@@ -294,6 +294,16 @@ int ssd_swift_search(ssd_seq* seq, const int32_t* window_dev, int pos0, int gamm
                      int n_skip, int sublayers, int n_cand, int max_steps, int patience, float target, uint64_t seed,
                      uint8_t* best_mask_host, float* best_score, int* n_steps, hipStream_t stream);
 
+/* SpecEE exit features (next row f4; [SpecEE] §4.3.1) of rows hidden states h_dev [rows][D] (fp32, a
+ * layer's output in the residual stream) for k speculative tokens tokens_dev[k] (1 <= k <= 16):
+ * features_dev[r][0..k) = speculative-token logits z_j = bf16(h * g_final) . W_lm[t_j] / rms(h) (the shared
+ * final norm and LM head restricted to the k columns, with the LM head's own rounding points),
+ * [k..2k) = local probabilities softmax(z) over the k tokens, [2k..3k) = their variation against the
+ * previous layer's, prev_probs_dev[r][k] (0 when it is NULL).  The trained exit predictor that
+ * consumes them is not part of this library. */
+int ssd_specee_features(const ssd_model* model, const float* h_dev, int rows, const int32_t* tokens_dev, int k,
+                        const float* prev_probs_dev, float* features_dev, hipStream_t stream);
+
 /* Row statistics (row a3) of rows logits rows of length V, as used inside
  * draft/verify/accept; exposed for tests.  Draws use (seed, iteration, row
  * index, purpose "draft"). */

@@ -26,7 +26,7 @@ import numpy as np
 
 from . import model as mdl
 from . import philox
-from .numerics import argmax_lowest, softmax
+from .numerics import argmax_lowest, rms, softmax
 
 
 # --------------------------------------------------------------------------
@@ -263,3 +263,17 @@ def score_masks(model, kv, window, pos0, masks):
         scores.append(float(np.sum(pred == targets)) / gamma)
     scores = np.array(scores)
     return scores, int(np.argmax(scores))
+
+
+def specee_features(model, h, tokens, prev_probs=None):
+    """SpecEE exit features (SpecEE notes §4.3.1) of hidden states h [rows, D]
+    for the speculative tokens: the speculative-token logits (the shared final
+    norm and LM head restricted to those columns), their softmax (local
+    probabilities) and its change against the previous layer's (zero when there
+    is none).  Returns [rows, 3k]."""
+    h = np.atleast_2d(np.asarray(h, np.float64))
+    w = model.lm_head[[int(t) for t in tokens]]
+    z = (model.rnd(h * model.final_norm) @ w.T) / rms(h, model.shape.rms_eps)
+    p = softmax(z)
+    var = np.zeros_like(p) if prev_probs is None else p - np.asarray(prev_probs, np.float64)
+    return np.concatenate([z, p, var], axis=1)

@@ -17,7 +17,8 @@ EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_packed_bf16_bytes", "ss
            "ssd_workspace_bytes", "ssd_seq_create",
            "ssd_seq_destroy", "ssd_prefill", "ssd_decode_ar", "ssd_decode_exit", "ssd_draft", "ssd_verify",
            "ssd_accept", "ssd_commit",
-           "ssd_score_masks", "ssd_uniform_mask", "ssd_swift_propose", "ssd_swift_search", "ssd_row_stats",
+           "ssd_score_masks", "ssd_uniform_mask", "ssd_swift_propose", "ssd_swift_search", "ssd_specee_features",
+           "ssd_row_stats",
            "ssd_read_state", "ssd_read_output", "ssd_last_error",
            "ssd_profile_enable", "ssd_profile_disable", "ssd_profile_read"]
 
@@ -85,6 +86,7 @@ def lib():
             "ssd_commit": [P, P, P, P],
             "ssd_score_masks": [P, P, I, P, I, I, P, P, P],
             "ssd_uniform_mask": [I, I, P],
+            "ssd_specee_features": [P, P, I, P, I, P, P, P],
             "ssd_swift_propose": [I, I, I, U64, I, I, P],
             "ssd_swift_search": [P, P, I, I, P, I, I, I, I, I, F, U64, P, ctypes.POINTER(F), ctypes.POINTER(I), P],
             "ssd_row_stats": [P, I, I, F, U64, ctypes.c_int32, P, P],
@@ -250,6 +252,11 @@ def ssd_swift_search(seq, window, pos0, gamma, init_mask, n_skip, n_cand, max_st
                                  out.ctypes.data_as(ctypes.c_void_p),
                                  ctypes.byref(sc), ctypes.byref(ns), _stream(stream)))
     return out, float(sc.value), int(ns.value)
+
+
+def ssd_specee_features(model, h, rows, tokens, k, prev_probs, features, stream=None):
+    check(lib().ssd_specee_features(model, _ptr(h), rows, _ptr(tokens), k, _ptr(prev_probs), _ptr(features),
+                                    _stream(stream)))
 
 
 def ssd_row_stats(logits, rows, V, temperature, seed, iteration, stats, stream=None):

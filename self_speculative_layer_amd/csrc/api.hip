@@ -803,6 +803,16 @@ extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0,
   return SSD_OK;
 }
 
+extern "C" int ssd_specee_features(const ssd_model* m, const float* h_dev, int rows, const int32_t* tokens_dev, int k,
+                                   const float* prev_probs_dev, float* features_dev, hipStream_t s) {
+  CHECK_ARG(m && h_dev && tokens_dev && features_dev && rows >= 0, "bad argument");
+  if (k < 1 || k > 16) return fail(SSD_ERR_SHAPE, "k must be 1..16");
+  const ssd_model_desc& d = m->d;
+  TRY(launch_specee_features(d.dtype, h_dev, rows, d.d_model, d.rms_eps, d.final_norm, d.lm_head, d.vocab,
+                             tokens_dev, k, prev_probs_dev, features_dev, s));
+  return SSD_OK;
+}
+
 extern "C" int ssd_row_stats(const float* logits_dev, int rows, int V, float temperature, uint64_t seed,
                              int32_t iteration, ssd_row_stat* stats_dev, hipStream_t s) {
   CHECK_ARG(logits_dev && stats_dev && rows >= 1 && V >= 1, "bad argument");

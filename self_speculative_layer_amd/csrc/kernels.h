@@ -115,6 +115,10 @@ int launch_verify_prep(DevState* st, const int32_t* drafts, const int32_t* n_dra
 // Copies rows r < (count ? *count : rows) of src [.., D] to dst row r + (dst_off ? *dst_off : 0).
 int launch_copy_rows(const float* src, float* dst, int rows, int D, const int* count, const int* dst_off,
                      const int* stop, hipStream_t s);
+// SpecEE exit features of rows hidden states h [rows, D] for k <= 16 speculative tokens: out [rows][3k] =
+// (logits, local probabilities, variation against prev [rows][k] or 0).
+int launch_specee_features(int dtype, const float* h, int rows, int D, float eps, const float* gain, const void* W,
+                           int V, const int32_t* tokens, int k, const float* prev, float* out, hipStream_t s);
 int launch_score(const ssd_row_stat* stats, const int32_t* window, int n_masks, int gamma, float* scores,
                  int32_t* best, hipStream_t s);
 

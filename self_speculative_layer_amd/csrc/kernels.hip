@@ -1497,6 +1497,84 @@ __global__ void score_kernel(const ssd_row_stat* __restrict__ stats, const int32
   }
 }
 
+// ===========================================================================
+// SpecEE exit features of hidden states (SpecEE notes §4.3.1): for k
+// speculative tokens t_j, z_j = the shared final norm and LM head restricted to
+// the k columns (bf16(h * g) . W[t_j] / rms(h), the LM head's own rounding
+// points), the local probabilities p = softmax(z) over the k, and the variation
+// p - p_prev against the previous layer's (0 without one).  One workgroup per row.
+// ===========================================================================
+
+template <typename T>
+__device__ __forceinline__ float spec_block_sum(float v, float* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void specee_features_kernel(const float* __restrict__ h, int D, float eps,
+                                                              const float* __restrict__ gain, const T* __restrict__ W,
+                                                              int V, const int32_t* __restrict__ tokens, int k,
+                                                              const float* __restrict__ prev, float* __restrict__ out) {
+  constexpr bool BF = sizeof(T) == 2;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const float* hr = h + (size_t)row * D;
+  __shared__ float red[256];
+  __shared__ float zs[16];
+  float ss = 0.f;
+  for (int i = tid; i < D; i += 256) ss = fmaf(hr[i], hr[i], ss);
+  const float inv = inv_rms(spec_block_sum<T>(ss, red), D, eps);
+  for (int j = 0; j < k; ++j) {
+    const int t = min(max(tokens[j], 0), V - 1);
+    float part = 0.f;
+    for (int c = tid; c < D / 8; c += 256) {
+      const int i = 8 * c;
+      const T* wp = BF ? W + wpk_index(t, i, D) : W + (size_t)t * D + i;   // 8 consecutive elements of row t
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = BF ? bf2f(f2bf(hr[i + e] * gain[i + e])) : hr[i + e] * gain[i + e];
+        part = fmaf(x, ld(wp + e), part);
+      }
+    }
+    const float z = spec_block_sum<T>(part, red);
+    if (tid == 0) zs[j] = z * inv;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float m = -INFINITY;
+    for (int j = 0; j < k; ++j) m = fmaxf(m, zs[j]);
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += expf(zs[j] - m);
+    float* o = out + (size_t)row * 3 * k;
+    for (int j = 0; j < k; ++j) {
+      const float p = expf(zs[j] - m) / sum;
+      o[j] = zs[j];
+      o[k + j] = p;
+      o[2 * k + j] = prev ? p - prev[(size_t)row * k + j] : 0.f;
+    }
+  }
+}
+
+int launch_specee_features(int dtype, const float* h, int rows, int D, float eps, const float* gain, const void* W,
+                           int V, const int32_t* tokens, int k, const float* prev, float* out, hipStream_t s) {
+  if (rows <= 0) return 0;
+  if (k < 1 || k > 16 || D % 8 != 0) return SSD_ERR_SHAPE;
+  if (dtype == SSD_DTYPE_BF16)
+    hipLaunchKernelGGL(specee_features_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, h, D, eps, gain,
+                       (const bf16_t*)W, V, tokens, k, prev, out);
+  else
+    hipLaunchKernelGGL(specee_features_kernel<float>, dim3(rows), dim3(256), 0, s, h, D, eps, gain,
+                       (const float*)W, V, tokens, k, prev, out);
+  return last_launch();
+}
+
 int launch_score(const ssd_row_stat* stats, const int32_t* window, int n_masks, int gamma, float* scores,
                  int32_t* best, hipStream_t s) {
   if (n_masks > 1024) return SSD_ERR_CAPACITY;

@@ -455,3 +455,31 @@ def test_decode_exit_matches_oracle(shape):
             assert err < logit_tol(shape), (k, err)
         seq.close()
     g.close()
+
+
+@pytest.mark.parametrize("shape", [BF16_HD64, BF16_HD128, F32_GQA], ids=lambda s: s.name)
+def test_specee_features_match_oracle(shape):
+    """SpecEE exit features (ssd_specee_features) of seeded hidden states against the
+    oracle: logits within the logit tolerance, probabilities and variation within
+    0.005 (their error is the logits' scaled by a probability)."""
+    g = gpu_model(shape)
+    o = omodel.Model.synthetic(shape)
+    rng = np.random.default_rng(17)
+    rows, k = 5, 4
+    h = rng.standard_normal((rows, shape.d_model)) * 0.5
+    toks = np.array([1, shape.vocab - 1, 17, shape.vocab // 2], np.int32)
+    prev = rng.random((rows, k))
+    prev /= prev.sum(axis=1, keepdims=True)
+    hd = torch.from_numpy(h.astype(np.float32)).cuda()
+    td = torch.from_numpy(toks).cuda()
+    pd = torch.from_numpy(prev.astype(np.float32)).cuda()
+    for pv in (None, pd):
+        out = torch.zeros(rows, 3 * k, dtype=torch.float32, device="cuda")
+        B.ssd_specee_features(g.handle, hd, rows, td, k, pv, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        ref = ossd.specee_features(o, h.astype(np.float32).astype(np.float64), toks,
+                                   None if pv is None else prev.astype(np.float32).astype(np.float64))
+        assert np.abs(got[:, :k] - ref[:, :k]).max() < logit_tol(shape)
+        assert np.abs(got[:, k:] - ref[:, k:]).max() < 5e-3
+    g.close()

@@ -407,3 +407,23 @@ def test_exit_generate_equals_truncated_model():
         z = ssd.prefill(trunc, mdl.KVCache(trunc.shape, len(seq) + 1), seq)
         assert np.max(np.abs(z - zs[k])) < 1e-9
         assert ex[k] == int(np.argmax(z))
+
+
+# ---------------------------------------------------------------- SpecEE features
+def test_specee_features_are_the_lm_head_columns():
+    """The speculative-token logits are the final-norm + LM-head logits at those
+    columns; the local probabilities are their softmax; the variation is the
+    difference to the given previous probabilities (zero without them)."""
+    m = _model(synth.TINY)
+    rng = np.random.default_rng(5)
+    h = rng.standard_normal((3, synth.TINY.d_model))
+    toks = [7, 1000, 3, 512]
+    f = ssd.specee_features(m, h, toks)
+    z = mdl.final_logits(m, h)
+    assert np.allclose(f[:, :4], z[:, toks], rtol=0, atol=1e-12)
+    p = np.exp(z[:, toks] - z[:, toks].max(axis=1, keepdims=True))
+    assert np.allclose(f[:, 4:8], p / p.sum(axis=1, keepdims=True), atol=1e-15)
+    assert np.allclose(f[:, 4:8].sum(axis=1), 1.0) and not f[:, 8:].any()
+    prev = rng.random((3, 4))
+    g = ssd.specee_features(m, h, toks, prev)
+    assert np.allclose(g[:, 8:], g[:, 4:8] - prev, atol=0)
