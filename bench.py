@@ -358,6 +358,19 @@ def run_exit(args):
     prof_ms, prof_n, prof_bytes = B.ssd_profile_read()
     achieved = prof_bytes / (prof_ms / 1e3) / 1e9 if prof_ms > 0 else 0.0
     step_bytes = E * shape.layer_param_count() * 2 + shape.vocab * shape.d_model * 2
+    # SpecEE exit features of one hidden row for 4 speculative tokens (latency-bound: 4 x 8 KB of LM-head rows)
+    hrow = torch.randn(1, shape.d_model, device=dev)
+    toks = torch.tensor([5, 77, 1234, 31999], dtype=torch.int32, device=dev)
+    feats = torch.zeros(1, 12, device=dev)
+    for _ in range(3):
+        B.ssd_specee_features(model.handle, hrow, 1, toks, 4, None, feats)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(100):
+        B.ssd_specee_features(model.handle, hrow, 1, toks, 4, None, feats)
+    ev1.record()
+    torch.cuda.synchronize()
+    feat_us = ev0.elapsed_time(ev1) * 10.0
     result = {
         "metric": "lossy early-exit tokens/s (batch 1, exit at layer 8, no verification)",
         "value": round(1e3 / ms, 3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -369,6 +382,7 @@ def run_exit(args):
                      "kernel": DOMINANT + " (decode-block gate/up projection + SwiGLU)", "launches": prof_n,
                      "avg_launch_us": round(prof_ms / max(prof_n, 1) * 1e3, 3)},
         "step_GBps": round(step_bytes / (ms / 1e3) / 1e9, 1),
+        "specee_features_us": round(feat_us, 2),
     }
     seq.close()
     model.close()

@@ -1505,57 +1505,66 @@ __global__ void score_kernel(const ssd_row_stat* __restrict__ stats, const int32
 // p - p_prev against the previous layer's (0 without one).  One workgroup per row.
 // ===========================================================================
 
-template <typename T>
-__device__ __forceinline__ float spec_block_sum(float v, float* red) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  const float r = red[0];
-  __syncthreads();
-  return r;
-}
-
+// One pass over the row: each thread keeps the sum of squares and the k dot products of its 8-element
+// chunks; the wave sums (butterfly) are added in wave order.
 template <typename T>
 __global__ __launch_bounds__(256) void specee_features_kernel(const float* __restrict__ h, int D, float eps,
                                                               const float* __restrict__ gain, const T* __restrict__ W,
                                                               int V, const int32_t* __restrict__ tokens, int k,
                                                               const float* __restrict__ prev, float* __restrict__ out) {
   constexpr bool BF = sizeof(T) == 2;
-  const int row = blockIdx.x, tid = threadIdx.x;
+  constexpr int KM = 16;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* hr = h + (size_t)row * D;
-  __shared__ float red[256];
-  __shared__ float zs[16];
-  float ss = 0.f;
-  for (int i = tid; i < D; i += 256) ss = fmaf(hr[i], hr[i], ss);
-  const float inv = inv_rms(spec_block_sum<T>(ss, red), D, eps);
-  for (int j = 0; j < k; ++j) {
-    const int t = min(max(tokens[j], 0), V - 1);
-    float part = 0.f;
-    for (int c = tid; c < D / 8; c += 256) {
-      const int i = 8 * c;
-      const T* wp = BF ? W + wpk_index(t, i, D) : W + (size_t)t * D + i;   // 8 consecutive elements of row t
+  __shared__ float red[4][KM + 1];
+  int tk[KM];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = BF ? bf2f(f2bf(hr[i + e] * gain[i + e])) : hr[i + e] * gain[i + e];
-        part = fmaf(x, ld(wp + e), part);
-      }
+  for (int j = 0; j < KM; ++j) tk[j] = j < k ? min(max(tokens[j], 0), V - 1) : 0;
+  float ss = 0.f, part[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) part[j] = 0.f;
+  for (int c = tid; c < D / 8; c += 256) {
+    const int i = 8 * c;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ss = fmaf(hr[i + e], hr[i + e], ss);
+      x[e] = BF ? bf2f(f2bf(hr[i + e] * gain[i + e])) : hr[i + e] * gain[i + e];
     }
-    const float z = spec_block_sum<T>(part, red);
-    if (tid == 0) zs[j] = z * inv;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j >= k) break;
+      const T* wp = BF ? W + wpk_index(tk[j], i, D) : W + (size_t)tk[j] * D + i;   // 8 consecutive elements
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[j] = fmaf(x[e], ld(wp + e), part[j]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ss += __shfl_xor(ss, o, 64);
+#pragma unroll
+    for (int j = 0; j < KM; ++j) part[j] += __shfl_xor(part[j], o, 64);
+  }
+  if (lane == 0) {
+    red[wave][KM] = ss;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) red[wave][j] = part[j];
   }
   __syncthreads();
   if (tid == 0) {
+    const float inv = inv_rms(((red[0][KM] + red[1][KM]) + red[2][KM]) + red[3][KM], D, eps);
+    float z[KM];
     float m = -INFINITY;
-    for (int j = 0; j < k; ++j) m = fmaxf(m, zs[j]);
+    for (int j = 0; j < k; ++j) {
+      z[j] = (((red[0][j] + red[1][j]) + red[2][j]) + red[3][j]) * inv;
+      m = fmaxf(m, z[j]);
+    }
     float sum = 0.f;
-    for (int j = 0; j < k; ++j) sum += expf(zs[j] - m);
+    for (int j = 0; j < k; ++j) sum += expf(z[j] - m);
     float* o = out + (size_t)row * 3 * k;
     for (int j = 0; j < k; ++j) {
-      const float p = expf(zs[j] - m) / sum;
-      o[j] = zs[j];
+      const float p = expf(z[j] - m) / sum;
+      o[j] = z[j];
       o[k + j] = p;
       o[2 * k + j] = prev ? p - prev[(size_t)row * k + j] : 0.f;
     }
