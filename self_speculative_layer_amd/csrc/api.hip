@@ -65,6 +65,7 @@ struct Workspace {
   unsigned* dec_ctr;     // attention merge counters [16][KVH], zero between launches
   StatRec* stat_recs;    // row statistics: segment records [rows][segments]
   unsigned* stat_ctr;    //   and per-row counters, zero between launches
+  float* gemm_split;     // quarter sums of K-split projections [4][R][D]
   float* swift_scores;   // layer-set search: one step's scores [64]
   int32_t* swift_best;   //   and its best index
 };
@@ -124,6 +125,7 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.dec_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)16 * d.n_kv_heads);
   t.stat_recs = (StatRec*)take(sizeof(StatRec) * (size_t)R * stat_segments(V));
   t.stat_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)R);
+  t.gemm_split = (float*)take(sizeof(float) * 4 * (size_t)R * D);
   t.swift_scores = (float*)take(sizeof(float) * 64);
   t.swift_best = (int32_t*)take(sizeof(int32_t) * 4);
   if (w) *w = t;
@@ -156,7 +158,7 @@ int attn_sublayer(ssd_seq* q, int l, const Block& b, hipStream_t s) {
   TRY(launch_attention(d.dtype, d.head_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads, d.n_kv_heads, rb,
                        q->max_ctx, b.local_kv, b.local_start, b.group_rows, w.part, w.x, m->q_dim, s));
   TRY(launch_linear(d.dtype, EPI_RESID, lw.w_o, w.x, m->q_dim, rb.M, D, m->q_dim, b.h, D, nullptr, 0, nullptr,
-                    rb.nrows, rb.ymap, rb.stop, s));
+                    rb.nrows, rb.ymap, rb.stop, s, w.gemm_split, 4 * (size_t)q->max_rows * D));
   return 0;
 }
 
@@ -172,7 +174,7 @@ int mlp_sublayer(ssd_seq* q, int l, const Block& b, hipStream_t s) {
   TRY(launch_linear(d.dtype, EPI_SWIGLU, lw.w_gate_up, w.x, D, rb.M, F, D, nullptr, 0, w.x2, F, w.inv, rb.nrows,
                     nullptr, rb.stop, s));
   TRY(launch_linear(d.dtype, EPI_RESID, lw.w_down, w.x2, F, rb.M, D, F, b.h, D, nullptr, 0, nullptr, rb.nrows,
-                    rb.ymap, rb.stop, s));
+                    rb.ymap, rb.stop, s, w.gemm_split, 4 * (size_t)q->max_rows * D));
   return 0;
 }
 

@@ -34,9 +34,11 @@ struct KvView {
 // For EPI_SWIGLU, N = F (output features) and W holds 2F rows (gate, then up).
 // rscale (nullable): per-row factor applied to the product before the
 // epilogue (not for EPI_RESID).
+// split_ws (nullable): at least split_floats floats of workspace, which small many-row problems use to
+// split K by quarter across workgroups (4 x M x N floats).
 int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
                   float* Y, int ldy, void* A, int lda, const float* rscale, const int* nrows, const int* ymap,
-                  const int* stop, hipStream_t s);
+                  const int* stop, hipStream_t s, float* split_ws = nullptr, size_t split_floats = 0);
 
 // Row-major bf16 [N, K] -> packed tile layout (K % 32 == 0).
 int launch_pack_bf16(const void* src, void* dst, int N, int K, hipStream_t s);

@@ -3,6 +3,8 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 #include "attn.h"
 
@@ -205,13 +207,18 @@ __device__ __forceinline__ void tg_barrier() { asm volatile("s_barrier" ::: "mem
 // WI x WJ: MFMA blocks per wave (W row tiles x activation row tiles); the four waves form a 2 x 2 grid,
 // so a workgroup covers 32 WI W rows (SwiGLU: 16 WI gate rows and the same up rows) and 32 WJ
 // activation rows.  4 x 4 for large problems; 2 x 2 when the large tiles would leave CUs idle.
-template <int EPI, int WI, int WJ>
+// SPLIT (plain epilogues only): the grid holds four copies of the tile grid, copy q forming only K
+// quarter q; its quarter sum goes to part[q][row][col] (M x N per quarter), and tg_quarter_reduce_kernel
+// adds the four in quarter order and applies the epilogue.
+template <int EPI, int WI, int WJ, bool SPLIT = false>
 __global__ __launch_bounds__(256) void gemm_bf16_tiled(
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ X, int ldx, int M, int N, int K,
     float* __restrict__ Y, int ldy, bf16_t* __restrict__ A, int lda, int n_mb, const float* __restrict__ rscale,
-    const int* __restrict__ nrows, const int* __restrict__ ymap, const int* __restrict__ stop) {
+    const int* __restrict__ nrows, const int* __restrict__ ymap, const int* __restrict__ stop,
+    float* __restrict__ part = nullptr) {
   if (stop && *stop) return;
   constexpr bool SW = EPI == EPI_SWIGLU;
+  static_assert(!(SPLIT && SW), "quarter split for plain epilogues");
   constexpr int WT = 2 * WI, XT = 2 * WJ;           // W / activation row tiles per workgroup
   constexpr int WSZ = WT * 2 * 512, XSZ = XT * 2 * 512;   // elements of a stage's W / activation tiles
   constexpr int H = WI / 2;
@@ -222,8 +229,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
   const int Ma = active_rows(M, nrows);
   // workgroup i runs on XCD i % 8: consecutive logical blocks (the row blocks of one W tile) are placed
   // on one XCD, so that they share its L2 for the W slabs
-  const int nblk = gridDim.x;
-  const int lb = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int nblk = SPLIT ? gridDim.x / 4 : gridDim.x;
+  const int qsplit = SPLIT ? blockIdx.x / nblk : 0;
+  const int bx = SPLIT ? blockIdx.x % nblk : blockIdx.x;
+  const int lb = (nblk % 8 == 0) ? (bx % 8) * (nblk / 8) + bx / 8 : bx;
   const int mb = lb % n_mb, nb = lb / n_mb;
   const int m0 = mb * 16 * XT;
   if (m0 >= Ma) return;
@@ -274,11 +283,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
     for (int j = 0; j < WJ; ++j) acc[i][j] = sum[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nu = K / TG_KS;                               // slabs (= 64-element units)
+  const int q0 = SPLIT ? qsplit : 0, q1 = SPLIT ? qsplit + 1 : 4;
+  const int sb = (nu * q0) / 4, se = (nu * q1) / 4;       // slabs of this workgroup
 #pragma unroll
   for (int p = 0; p < TG_NST - 1; ++p)
-    if (p < nu) issue(p);
-  int sl = 0;
-  for (int q = 0; q < 4; ++q) {
+    if (sb + p < se) issue(sb + p);
+  int sl = sb;
+  for (int q = q0; q < q1; ++q) {
     const int qe = (nu * (q + 1)) / 4;                    // quarter q: slabs [(nu q) / 4, qe)
     for (; sl < qe; ++sl) {
       if constexpr (ONE_BARRIER) {
@@ -286,9 +297,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
         // slab sl - 1, which the loads of slab sl + 1 then refill
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         tg_barrier();
-        if (sl + 1 < nu) issue(sl + 1);
+        if (sl + 1 < se) issue(sl + 1);
       } else {
-        if (sl + TG_NST - 1 < nu) {
+        if (sl + TG_NST - 1 < se) {
           issue(sl + TG_NST - 1);
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"((WI + WJ) * (TG_NST - 1)) : "memory");   // slab sl has landed
         } else {
@@ -327,6 +338,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
   }
 
   // acc layout: lane (r, g) holds D[feature 4 g + e][row r] of each 16 x 16 block
+  if constexpr (SPLIT) {
+    float* pq = part + (size_t)qsplit * M * N;
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      const int row = m0 + 16 * (WJ * wm + j) + r;
+      if (row >= Ma) continue;
+#pragma unroll
+      for (int i = 0; i < WI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = 16 * WT * nb + 16 * (WI * wn + i) + 4 * g + e;
+          if (col < N) pq[(size_t)row * N + col] = sum[i][j][e];
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
     const int row = m0 + 16 * (WJ * wm + j) + r;
@@ -362,6 +389,32 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
   }
 }
 
+// The four quarter sums of a split projection added in quarter order, then the plain epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void tg_quarter_reduce_kernel(const float* __restrict__ part, int M, int N,
+                                                                float* __restrict__ Y, int ldy,
+                                                                const float* __restrict__ rscale,
+                                                                const int* __restrict__ nrows,
+                                                                const int* __restrict__ ymap,
+                                                                const int* __restrict__ stop) {
+  if (stop && *stop) return;
+  const int Ma = active_rows(M, nrows);
+  const size_t n = (size_t)Ma * N, MN = (size_t)M * N;
+  for (size_t e = blockIdx.x * (size_t)256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
+    const int row = (int)(e / N), col = (int)(e % N);
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v += part[q * MN + e];
+    const int yrow = ymap ? ymap[row] : row;
+    if (EPI == EPI_STORE) {
+      if (rscale) v = __fmul_rn(v, rscale[row]);
+      Y[(size_t)yrow * ldy + col] = v;
+    } else {
+      Y[(size_t)yrow * ldy + col] = __fadd_rn(Y[(size_t)yrow * ldy + col], v);
+    }
+  }
+}
+
 // Workgroups of the tiled projection with WI x WJ blocks per wave.
 static int tg_blocks(int epi, int M, int N, int WI, int WJ) {
   const int n_mb = (M + 32 * WJ - 1) / (32 * WJ);
@@ -378,24 +431,39 @@ static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, 
 
 int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int M, int N, int K,
                   float* Y, int ldy, void* A, int lda, const float* rscale, const int* nrows, const int* ymap,
-                  const int* stop, hipStream_t s) {
+                  const int* stop, hipStream_t s, float* split_ws, size_t split_floats) {
   if (M <= 0 || N <= 0) return 0;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   int* ran = nullptr;
   const bool prof = profile_next(epi, &e0, &e1, &ran);
   int rc;
   if (dtype == SSD_DTYPE_BF16 && M >= TG_MIN_ROWS && K % TG_KS == 0 && (epi != EPI_SWIGLU || N % 64 == 0)) {
-    // large tiles unless they would leave CUs idle
+    // large tiles unless they would leave CUs idle; when even the small tiles leave the CUs with under
+    // two workgroups each, large tiles split by K quarter (plain epilogues, workspace permitting)
     const bool big = tg_blocks(epi, M, N, 4, 4) >= 256;
-    const int WJ = big ? 4 : 2;
+    const bool split = !big && epi != EPI_SWIGLU && split_ws && 4 * (size_t)M * N <= split_floats &&
+                       tg_blocks(epi, M, N, 2, 2) < 512;
+    const int WJ = big || split ? 4 : 2;
     const int n_mb = (M + 32 * WJ - 1) / (32 * WJ);
-    const dim3 grid(big ? tg_blocks(epi, M, N, 4, 4) : tg_blocks(epi, M, N, 2, 2));
+    const dim3 grid(big ? tg_blocks(epi, M, N, 4, 4)
+                        : (split ? 4 * tg_blocks(epi, M, N, 4, 4) : tg_blocks(epi, M, N, 2, 2)));
     const bf16_t* w = (const bf16_t*)W;
     const bf16_t* x = (const bf16_t*)X;
 #define TILED(E, I, J)                                                                                            \
   hipExtLaunchKernelGGL((gemm_bf16_tiled<E, I, J>), grid, dim3(256), 0, s, e0, e1, 0, w, x, ldx, M, N, K, Y, ldy,   \
-                        (bf16_t*)A, lda, n_mb, rscale, nrows, ymap, stop)
-    if (big) {
+                        (bf16_t*)A, lda, n_mb, rscale, nrows, ymap, stop, nullptr)
+#define TSPLIT(E)                                                                                                 \
+  do {                                                                                                            \
+    hipExtLaunchKernelGGL((gemm_bf16_tiled<E, 4, 4, true>), grid, dim3(256), 0, s, e0, e1, 0, w, x, ldx, M, N, K,  \
+                          Y, ldy, (bf16_t*)A, lda, n_mb, rscale, nrows, ymap, stop, split_ws);                     \
+    const size_t nel = (size_t)M * N;                                                                             \
+    hipLaunchKernelGGL(tg_quarter_reduce_kernel<E>, dim3((unsigned)std::min<size_t>((nel + 255) / 256, 2048)),     \
+                       dim3(256), 0, s, split_ws, M, N, Y, ldy, rscale, nrows, ymap, stop);                       \
+  } while (0)
+    if (split) {
+      if (epi == EPI_STORE) TSPLIT(EPI_STORE);
+      else TSPLIT(EPI_RESID);
+    } else if (big) {
       if (epi == EPI_STORE) TILED(EPI_STORE, 4, 4);
       else if (epi == EPI_RESID) TILED(EPI_RESID, 4, 4);
       else TILED(EPI_SWIGLU, 4, 4);
@@ -405,6 +473,7 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
       else TILED(EPI_SWIGLU, 2, 2);
     }
 #undef TILED
+#undef TSPLIT
     rc = last_launch();
   } else {
     const int n_rb = (M + 15) / 16;
