@@ -124,3 +124,17 @@ def test_sublayer_proposals_are_uniform():
             assert m.sum() == n
             counts += m
     assert stats.chisquare(counts).pvalue > 1e-3
+
+
+def test_library_helpers_reject_bad_arguments():
+    from self_speculative_layer_amd import binding as B
+    for args in [(0, 0), (4, 5), (4, -1)]:
+        with pytest.raises(B.SSDError):
+            B.ssd_uniform_mask(*args)
+    with pytest.raises(B.SSDError):
+        B.ssd_swift_propose(4, 5, 1, 0, 0)                 # more layers than there are
+    with pytest.raises(B.SSDError):
+        B.ssd_swift_propose(4, 9, 1, 0, 0, sublayers=True)  # more sub-layers than there are
+    with pytest.raises(B.SSDError):
+        B.ssd_swift_propose(4, 1, 1, -1, 0)
+    assert B.ssd_swift_propose(4, 8, 1, 0, 0, sublayers=True).all()
