@@ -441,8 +441,9 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
     // large tiles unless they would leave CUs idle; when even the small tiles leave the CUs with under
     // two workgroups each, large tiles split by K quarter (plain epilogues, workspace permitting)
     const bool big = tg_blocks(epi, M, N, 4, 4) >= 256;
+    const int small_blocks = tg_blocks(epi, M, N, 2, 2);
     const bool split = !big && epi != EPI_SWIGLU && split_ws && 4 * (size_t)M * N <= split_floats &&
-                       tg_blocks(epi, M, N, 2, 2) < 512;
+                       (small_blocks < 512 || (K >= 8192 && small_blocks <= 1024));   // long K: shorter chains
     const int WJ = big || split ? 4 : 2;
     const int n_mb = (M + 32 * WJ - 1) / (32 * WJ);
     const dim3 grid(big ? tg_blocks(epi, M, N, 4, 4)
