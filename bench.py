@@ -34,7 +34,11 @@ PMC_TRAFFIC = {
                                     "sha1_prefix": "559b8986cd02", "fetch_kib": 88425.7, "write_kib": 61.8,
                                     "fetch_scale": 2.0, "write_scale": 1.0},
 }
+PMC_TRAFFIC["gemm_bf16_tiled<EPI_SWIGLU, 4, 4>"] = {
+    "source": "self_speculative_layer_amd/csrc/kernels.hip", "sha1_prefix": "3b1e3ab39006",
+    "fetch_kib": 187692.9, "write_kib": 6421.7, "fetch_scale": 2.0, "write_scale": 1.0}
 DOMINANT = "dec_gemm_kernel<DEC_SWIGLU>"
+SCORING_DOMINANT = "gemm_bf16_tiled<EPI_SWIGLU, 4, 4>"
 
 
 def pmc_traffic_bytes(kernel):
@@ -483,7 +487,9 @@ def run_scoring(args):
              "frac": round(tflops / 2500.0, 4)} if mfma_bound else
             {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
              "frac": round(gbps / HBM_PEAK_GBPS, 4)})
-    roof.update({"traffic": None, "kernel": "gemm_bf16 gate/up + SwiGLU over the candidates' rows",
+    traffic = pmc_traffic_bytes(SCORING_DOMINANT) if not search else None
+    roof.update({"traffic": None if traffic is None else round(traffic),
+                 "kernel": SCORING_DOMINANT + " (gate/up + SwiGLU over the candidates' rows, 128 x 128 tiles)",
                  "launches": prof_n, "avg_launch_us": round(prof_ms / max(prof_n, 1) * 1e3, 3),
                  "flop_per_step": flops / K, "bytes_per_launch": round(prof_bytes / max(prof_n, 1)),
                  "measured": "dispatch-timestamp events on every launch of the kernel in %d further steps" % K})
