@@ -3,8 +3,8 @@
 A plain, slow, float64 NumPy implementation of what the GPU library computes:
 a Llama-style decoder, layer-skipped / early-exit drafting with a confidence
 stop, a full-depth verify pass that reuses the draft's KV cache, the
-speculative accept/reject rule, and SWIFT matchness scoring of candidate skip
-masks.  It shares no code with the HIP library (the two only share the seeded
+speculative accept/reject rule, SWIFT matchness scoring of candidate skip
+masks, and greedy verification of confidence-sized draft trees.  It shares no code with the HIP library (the two only share the seeded
 input generator in ``synth``) and is the parity authority for it.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg
