@@ -246,6 +246,54 @@ int ssd_accept(ssd_seq* seq, const float* p_logits_dev, const float* q_logits_de
 int ssd_commit(ssd_seq* seq, const int32_t* out_tokens_dev, const int32_t* n_out_dev,
                hipStream_t stream);
 
+/* ---- draft trees: dynamic verification ([SWIFT] §4.2, §3.2.1 Figure 2) ------
+ * The draft's confidence also sets how many candidates each draft step hands to
+ * the verification.  Readings (the page gives no formula): the candidates of
+ * step j are the k_j most probable tokens of softmax(q logits row j-1)
+ * (temperature 1, lowest index first among equal logits), k_j = the least k >= 1
+ * whose top-k mass reaches rho, at most k_max; only the top one (the greedy
+ * draft token y_j) is drafted further, the others are leaves of depth j that sit
+ * at y_j's position and attend to the prefix, y_0..y_{j-1} and themselves.
+ * Greedy decoding only (temperature 0). */
+
+/* Leaves of the last greedy draft (draft_logits_dev / n_drafted_dev as written
+ * by ssd_draft, or any [d, V] float rows): ranks 1..k_j-1 of each step j <= d',
+ * in depth order then rank order, at most max_leaves (<= 15).  k_max in 1..8.
+ * Outputs: leaf_tokens_dev[max_leaves], leaf_depth_dev[max_leaves] (1..d'),
+ * n_leaves_dev[1]. */
+int ssd_tree_candidates(ssd_seq* seq, const float* draft_logits_dev, const int32_t* n_drafted_dev, int d,
+                        float rho, int k_max, int max_leaves, int32_t* leaf_tokens_dev, int32_t* leaf_depth_dev,
+                        int32_t* n_leaves_dev, hipStream_t stream);
+
+/* Tree verify: ssd_verify's chain rows 0..d' plus one row per leaf s (token
+ * leaf_tokens_dev[s] at position kvlen + leaf_depth_dev[s], seeing the cache up
+ * to the position before its own and its own key/value).  The leaves' keys and
+ * values are kept in the workspace; the cache receives only the chain's.  With
+ * reuse, y_d' and the leaves run the layers below the plan's boundary, the
+ * chain rows < d' take the draft's saved residual (as ssd_verify).
+ * Requires a bf16 model, d + 1 + max_leaves <= 16 (and <= max_rows), and a
+ * context of at most 63 * 64 positions (the attention's merge slots).
+ * Output: logits_dev[(d + 1 + max_leaves) * V], rows compact: 0..d' the chain
+ * (bitwise the rows ssd_verify gives), d' + 1 + s leaf s (the full model's
+ * logits for the position after the leaf). */
+int ssd_verify_tree(ssd_seq* seq, const uint8_t* skip_mask_host, int exit_layer, int d,
+                    const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, const int32_t* leaf_tokens_dev,
+                    const int32_t* leaf_depth_dev, const int32_t* n_leaves_dev, int max_leaves, int reuse,
+                    float* logits_dev, hipStream_t stream);
+
+/* Greedy tree acceptance over ssd_verify_tree's rows: for j = 1..d', y_j is
+ * accepted while it is the argmax of chain row j-1; at the first mismatch, if
+ * the argmax is a leaf of depth j, that leaf and the argmax of its own row are
+ * emitted, else the argmax alone; after d' accepted drafts the argmax of row d'
+ * is the bonus.  When a leaf is emitted its keys and values (every layer) are
+ * written into the cache at its position, so ssd_commit's metadata update is
+ * all that remains.  Outputs: out_tokens_dev[d + 1] (first n_out valid),
+ * n_out_dev[1]. */
+int ssd_accept_tree(ssd_seq* seq, const float* logits_dev, const int32_t* draft_tokens_dev,
+                    const int32_t* n_drafted_dev, int d, const int32_t* leaf_tokens_dev, const int32_t* leaf_depth_dev,
+                    const int32_t* n_leaves_dev, int max_leaves, int32_t* out_tokens_dev, int32_t* n_out_dev,
+                    hipStream_t stream);
+
 /* SWIFT matchness scoring (row a6; [SWIFT] §4.1, §4.1.2, §5.3, §D.2).
  * window_dev[gamma + 1] are committed tokens at positions pos0..pos0+gamma, and
  * the cache must hold the full model's keys/values for positions < pos0
@@ -313,7 +361,9 @@ int ssd_row_stats(const float* logits_dev, int rows, int V, float temperature, u
 /* ---- host synchronisation ------------------------------------------------------ */
 
 /* Waits for the stream, then copies the device state.  Returns
- * SSD_ERR_CAPACITY / SSD_ERR_NUMERIC if the device flagged such a condition. */
+ * SSD_ERR_CAPACITY / SSD_ERR_NUMERIC / SSD_ERR_ARG if the device flagged such a
+ * condition (SSD_ERR_ARG: a device-side argument out of range, e.g. a leaf depth
+ * outside 1..d'). */
 int ssd_read_state(ssd_seq* seq, ssd_state* out, hipStream_t stream);
 
 /* Waits for the stream, then copies min(n_out, max_tokens) committed tokens

@@ -16,7 +16,7 @@ ERROR_NAMES = {-1: "SSD_ERR_ARG", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_CAPACITY", -
 EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_packed_bf16_bytes", "ssd_pack_bf16", "ssd_kv_pool_bytes",
            "ssd_workspace_bytes", "ssd_seq_create",
            "ssd_seq_destroy", "ssd_prefill", "ssd_decode_ar", "ssd_decode_exit", "ssd_draft", "ssd_verify",
-           "ssd_accept", "ssd_commit",
+           "ssd_accept", "ssd_commit", "ssd_tree_candidates", "ssd_verify_tree", "ssd_accept_tree",
            "ssd_score_masks", "ssd_uniform_mask", "ssd_swift_propose", "ssd_swift_search", "ssd_specee_features",
            "ssd_row_stats",
            "ssd_read_state", "ssd_read_output", "ssd_last_error",
@@ -84,6 +84,9 @@ def lib():
             "ssd_verify": [P, P, I, I, P, P, I, P, P],
             "ssd_accept": [P, P, P, P, P, I, F, U64, P, P, P],
             "ssd_commit": [P, P, P, P],
+            "ssd_tree_candidates": [P, P, P, I, F, I, I, P, P, P, P],
+            "ssd_verify_tree": [P, P, I, I, P, P, P, P, P, I, I, P, P],
+            "ssd_accept_tree": [P, P, P, P, I, P, P, P, I, P, P, P],
             "ssd_score_masks": [P, P, I, P, I, I, P, P, P],
             "ssd_uniform_mask": [I, I, P],
             "ssd_specee_features": [P, P, I, P, I, P, P, P],
@@ -216,6 +219,27 @@ def ssd_accept(seq, p_logits, q_logits, draft_tokens, n_drafted, d, temperature,
 
 def ssd_commit(seq, out_tokens, n_out, stream=None):
     check(lib().ssd_commit(seq, _ptr(out_tokens), _ptr(n_out), _stream(stream)))
+
+
+def ssd_tree_candidates(seq, draft_logits, n_drafted, d, rho, k_max, max_leaves, leaf_tokens, leaf_depth, n_leaves,
+                        stream=None):
+    check(lib().ssd_tree_candidates(seq, _ptr(draft_logits), _ptr(n_drafted), d, rho, k_max, max_leaves,
+                                    _ptr(leaf_tokens), _ptr(leaf_depth), _ptr(n_leaves), _stream(stream)))
+
+
+def ssd_verify_tree(seq, skip_mask, exit_layer, d, draft_tokens, n_drafted, leaf_tokens, leaf_depth, n_leaves,
+                    max_leaves, reuse, logits, stream=None):
+    keep, mp = _mask_arg(skip_mask)
+    check(lib().ssd_verify_tree(seq, mp, -1 if exit_layer is None else exit_layer, d, _ptr(draft_tokens),
+                                _ptr(n_drafted), _ptr(leaf_tokens), _ptr(leaf_depth), _ptr(n_leaves), max_leaves,
+                                1 if reuse else 0, _ptr(logits), _stream(stream)))
+
+
+def ssd_accept_tree(seq, logits, draft_tokens, n_drafted, d, leaf_tokens, leaf_depth, n_leaves, max_leaves,
+                    out_tokens, n_out, stream=None):
+    check(lib().ssd_accept_tree(seq, _ptr(logits), _ptr(draft_tokens), _ptr(n_drafted), d, _ptr(leaf_tokens),
+                                _ptr(leaf_depth), _ptr(n_leaves), max_leaves, _ptr(out_tokens), _ptr(n_out),
+                                _stream(stream)))
 
 
 def ssd_score_masks(seq, masks, window, pos0, gamma, scores, best, stream=None):
@@ -361,6 +385,11 @@ class Sequence:
         self.n_drafted = torch.zeros(1, dtype=torch.int32, device=device)
         self.out_tokens = torch.zeros(max_draft + 1, dtype=torch.int32, device=device)
         self.n_out = torch.zeros(1, dtype=torch.int32, device=device)
+        # draft trees: at most 15 leaves, 16 verify rows
+        self.leaf_tokens = torch.zeros(16, dtype=torch.int32, device=device)
+        self.leaf_depth = torch.zeros(16, dtype=torch.int32, device=device)
+        self.n_leaves = torch.zeros(1, dtype=torch.int32, device=device)
+        self.tree_logits = torch.zeros(16 * V, dtype=torch.float32, device=device)
 
     def close(self):
         if self.handle is not None:
@@ -377,6 +406,31 @@ class Sequence:
         ssd_accept(self.handle, self.verify_logits, self.draft_logits, self.draft_tokens, self.n_drafted, d,
                    temperature, seed, self.out_tokens, self.n_out, s)
         ssd_commit(self.handle, self.out_tokens, self.n_out, s)
+
+    def tree_iteration(self, skip_mask, exit_layer, d, rho, k_max, max_leaves, conf_thresh=0.0, reuse=True):
+        """Enqueues a greedy draft -> leaves -> tree verify -> tree accept -> commit."""
+        s = self.stream
+        ssd_draft(self.handle, skip_mask, exit_layer, d, conf_thresh, 0.0, 0, self.draft_tokens, self.draft_logits,
+                  self.n_drafted, s)
+        ssd_tree_candidates(self.handle, self.draft_logits, self.n_drafted, d, rho, k_max, max_leaves,
+                            self.leaf_tokens, self.leaf_depth, self.n_leaves, s)
+        ssd_verify_tree(self.handle, skip_mask, exit_layer, d, self.draft_tokens, self.n_drafted, self.leaf_tokens,
+                        self.leaf_depth, self.n_leaves, max_leaves, reuse, self.tree_logits, s)
+        ssd_accept_tree(self.handle, self.tree_logits, self.draft_tokens, self.n_drafted, d, self.leaf_tokens,
+                        self.leaf_depth, self.n_leaves, max_leaves, self.out_tokens, self.n_out, s)
+        ssd_commit(self.handle, self.out_tokens, self.n_out, s)
+
+    def generate_tree(self, prompt, n_gen, skip_mask=None, exit_layer=None, d=4, rho=0.9, k_max=4, max_leaves=3,
+                      conf_thresh=0.0, reuse=True):
+        """Greedy decoding with draft trees; returns (tokens[:n_gen], per-iteration (d', emitted) list)."""
+        ssd_prefill(self.handle, prompt, 0.0, 0, None, self.stream)
+        stats = []
+        st = ssd_read_state(self.handle, self.stream)
+        while st.n_out < n_gen:
+            self.tree_iteration(skip_mask, exit_layer, d, rho, k_max, max_leaves, conf_thresh, reuse)
+            st = ssd_read_state(self.handle, self.stream)
+            stats.append((st.last_n_drafted, st.last_n_emitted))
+        return ssd_read_output(self.handle, n_gen, self.stream)[:n_gen], stats
 
     def generate_ssd(self, prompt, n_gen, skip_mask=None, exit_layer=None, d=4, conf_thresh=0.0, temperature=0.0,
                      seed=0, reuse=True, on_iteration=None):

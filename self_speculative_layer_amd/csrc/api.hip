@@ -68,6 +68,12 @@ struct Workspace {
   float* gemm_split;     // quarter sums of K-split projections [4][R][D]
   float* swift_scores;   // layer-set search: one step's scores [64]
   int32_t* swift_best;   //   and its best index
+  // draft trees
+  bf16_t* tree_kv;       // leaves' keys and values [L][TREE_SLOTS][2][KVH * HD] (not in the cache)
+  float* hp;             // prefix-block residual rows [16][D] (y_d' and the leaves below the boundary)
+  int *tvpos, *tvtok;    // full-block rows [16]
+  int *ppos, *ptok;      // prefix-block rows [16]
+  int *tree_cand, *tree_k;   // per draft row: best tokens [max_draft][TREE_KMAX], candidate count
 };
 
 struct ssd_seq {
@@ -128,6 +134,14 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.gemm_split = (float*)take(sizeof(float) * 4 * (size_t)R * D);
   t.swift_scores = (float*)take(sizeof(float) * 64);
   t.swift_best = (int32_t*)take(sizeof(int32_t) * 4);
+  t.tree_kv = (bf16_t*)take(2 * (size_t)L * TREE_SLOTS * 2 * m->kv_dim);
+  t.hp = (float*)take(sizeof(float) * 16 * (size_t)D);
+  t.tvpos = (int*)take(sizeof(int) * 16);
+  t.tvtok = (int*)take(sizeof(int) * 16);
+  t.ppos = (int*)take(sizeof(int) * 16);
+  t.ptok = (int*)take(sizeof(int) * 16);
+  t.tree_cand = (int*)take(sizeof(int) * (size_t)max_draft * TREE_KMAX);
+  t.tree_k = (int*)take(sizeof(int) * (size_t)max_draft);
   if (w) *w = t;
   return off;
 }
@@ -254,8 +268,10 @@ DecGemm dec_base(const ssd_seq* q, int M, const int* nrows, const int* stop) {
 
 // Entries [e0, e1) of ent on the residual rows h[0, M).
 // copy_last (nullable): the residual rows after the last entry are also written there.
+// side_from (nullable): rows >= *side_from are tree leaves (keys and values in the workspace's tree_kv).
 int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, const std::vector<int>& ent, size_t e0,
-               size_t e1, bool final_lm, const int* stop, hipStream_t s, float* copy_last = nullptr) {
+               size_t e1, bool final_lm, const int* stop, hipStream_t s, float* copy_last = nullptr,
+               const int* side_from = nullptr) {
   const ssd_model* m = q->m;
   const ssd_model_desc& d = m->d;
   const Workspace& w = q->w;
@@ -277,9 +293,11 @@ int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, co
       a.n_lpages = q->kv.n_lpages; a.L = d.n_layers; a.layer = l;
       a.H = d.n_heads; a.KVH = d.n_kv_heads; a.HD = d.head_dim;
       a.pos = pos; a.rope_cs = w.rope_cs; a.err = &w.st->error_flags;
+      a.side_from = side_from;
+      a.side_kv = side_from ? w.tree_kv + (size_t)l * TREE_SLOTS * 2 * m->kv_dim : nullptr;
       TRY(launch_dec_gemm(DEC_QKV, a, s));
       TRY(launch_attention_dec(d.head_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads, d.n_kv_heads, M, nrows,
-                               pos, q->max_ctx, w.part, w.x, m->q_dim, w.dec_ctr, stop, s));
+                               pos, q->max_ctx, w.part, w.x, m->q_dim, w.dec_ctr, stop, s, side_from, a.side_kv));
       r.W = (const bf16_t*)lw.w_o; r.K = m->q_dim; r.X = (const bf16_t*)w.x;
       TRY(launch_dec_gemm(DEC_RESID, r, s));
     } else {
@@ -649,6 +667,89 @@ extern "C" int ssd_commit(ssd_seq* q, const int32_t* out_tokens_dev, const int32
 }
 
 // ---------------------------------------------------------------------------
+// draft trees (dynamic verification)
+
+extern "C" int ssd_tree_candidates(ssd_seq* q, const float* draft_logits_dev, const int32_t* n_drafted_dev, int d_max,
+                                   float rho, int k_max, int max_leaves, int32_t* leaf_tokens_dev,
+                                   int32_t* leaf_depth_dev, int32_t* n_leaves_dev, hipStream_t s) {
+  CHECK_ARG(q && draft_logits_dev && n_drafted_dev && leaf_tokens_dev && leaf_depth_dev && n_leaves_dev,
+            "null argument");
+  CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
+  CHECK_ARG(k_max >= 1 && k_max <= TREE_KMAX && k_max <= q->m->d.vocab, "k_max out of range");
+  CHECK_ARG(max_leaves >= 0 && max_leaves <= TREE_SLOTS, "max_leaves out of range");
+  CHECK_ARG(std::isfinite(rho), "bad rho");
+  const Workspace& w = q->w;
+  TRY(launch_tree_candidates(draft_logits_dev, q->m->d.vocab, d_max, n_drafted_dev, rho, k_max, max_leaves,
+                             w.tree_cand, w.tree_k, leaf_tokens_dev, leaf_depth_dev, n_leaves_dev, s));
+  return SSD_OK;
+}
+
+extern "C" int ssd_verify_tree(ssd_seq* q, const uint8_t* skip_mask_host, int exit_layer, int d_max,
+                               const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev,
+                               const int32_t* leaf_tokens_dev, const int32_t* leaf_depth_dev,
+                               const int32_t* n_leaves_dev, int max_leaves, int reuse, float* logits_dev,
+                               hipStream_t s) {
+  CHECK_ARG(q && draft_tokens_dev && n_drafted_dev && leaf_tokens_dev && leaf_depth_dev && n_leaves_dev && logits_dev,
+            "null argument");
+  CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
+  CHECK_ARG(max_leaves >= 0 && d_max + 1 + max_leaves <= 16, "a tree verify holds at most 16 rows");
+  if (!dec_usable(q, d_max + 1 + max_leaves) || q->max_rows < d_max + 1 + max_leaves)
+    return fail(SSD_ERR_UNSUPPORTED, "tree verification runs bf16 models in 16-row decode blocks");
+  if (!attention_dec_leaves_fit(q->max_ctx))
+    return fail(SSD_ERR_UNSUPPORTED, "context too long for tree verification");
+  const ssd_model_desc& d = q->m->d;
+  const Workspace& w = q->w;
+  std::vector<uint8_t> mask;
+  const int b = plan_mask(q->m, skip_mask_host, exit_layer, mask);
+  CHECK_ARG(b >= 0, "exit_layer out of range");
+  const int M = d_max + 1 + max_leaves, MP = 1 + max_leaves;
+  const int* rows = &w.st->tree_rows;
+  TRY(launch_tree_verify_prep(w.st, draft_tokens_dev, n_drafted_dev, d_max, leaf_tokens_dev, leaf_depth_dev,
+                              n_leaves_dev, max_leaves, w.tvpos, w.tvtok, w.ppos, w.ptok, q->max_ctx, s));
+  std::vector<int> suffix;
+  plan_entries(suffix, reuse ? b : 0, d.n_layers, nullptr);
+  const float* g0 = dec_gain(q->m, suffix, 0, true);
+  if (reuse) {
+    // y_d' and the leaves run the layers below the boundary; the chain rows < d' take the residual
+    // the draft saved there
+    std::vector<int> prefix;
+    plan_entries(prefix, 0, b, nullptr);
+    const int* prows = &w.st->tree_prefix_rows;
+    TRY(dec_entry(q, w.ptok, nullptr, MP, prows, nullptr, w.hp, dec_gain(q->m, prefix, 0, false), nullptr, s));
+    TRY(dec_layers(q, w.hp, MP, prows, w.ppos, prefix, 0, prefix.size(), false, nullptr, s, nullptr,
+                   &w.st->tree_side_prefix));
+    TRY(dec_entry(q, nullptr, w.hb, d_max, n_drafted_dev, nullptr, w.h, g0, nullptr, s));
+    TRY(dec_entry(q, nullptr, w.hp, MP, prows, n_drafted_dev, w.h, g0, nullptr, s));
+  } else {
+    TRY(dec_entry(q, w.tvtok, nullptr, M, rows, nullptr, w.h, g0, nullptr, s));
+  }
+  TRY(dec_layers(q, w.h, M, rows, w.tvpos, suffix, 0, suffix.size(), true, nullptr, s, nullptr,
+                 &w.st->tree_side_full));
+  TRY(dec_logits(q, M, rows, logits_dev, nullptr, s));
+  return SSD_OK;
+}
+
+extern "C" int ssd_accept_tree(ssd_seq* q, const float* logits_dev, const int32_t* draft_tokens_dev,
+                               const int32_t* n_drafted_dev, int d_max, const int32_t* leaf_tokens_dev,
+                               const int32_t* leaf_depth_dev, const int32_t* n_leaves_dev, int max_leaves,
+                               int32_t* out_tokens_dev, int32_t* n_out_dev, hipStream_t s) {
+  CHECK_ARG(q && logits_dev && draft_tokens_dev && n_drafted_dev && leaf_tokens_dev && leaf_depth_dev &&
+                n_leaves_dev && out_tokens_dev && n_out_dev,
+            "null argument");
+  CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
+  CHECK_ARG(max_leaves >= 0 && d_max + 1 + max_leaves <= std::min(16, q->max_rows), "too many tree rows");
+  const ssd_model_desc& d = q->m->d;
+  const Workspace& w = q->w;
+  const int M = d_max + 1 + max_leaves;
+  TRY(launch_row_stats_seg(logits_dev, d.vocab, M, d.vocab, 0.f, 0, nullptr, 0, 0, PURPOSE_SAMPLE, w.stats,
+                           w.stat_recs, w.stat_ctr, nullptr, DraftStep{}, s));
+  TRY(launch_tree_accept(w.stats, draft_tokens_dev, n_drafted_dev, d_max, leaf_tokens_dev, leaf_depth_dev,
+                         n_leaves_dev, max_leaves, w.st, out_tokens_dev, n_out_dev, w.tree_kv, q->kv, d.n_layers,
+                         d.n_kv_heads, d.head_dim, s));
+  return SSD_OK;
+}
+
+// ---------------------------------------------------------------------------
 // SWIFT matchness scoring
 
 extern "C" int ssd_score_masks(ssd_seq* q, const uint8_t* masks_host, int n_masks, const int32_t* window_dev,
@@ -842,6 +943,7 @@ extern "C" int ssd_read_state(ssd_seq* q, ssd_state* out, hipStream_t s) {
   out->last_n_emitted = st.n_emitted;
   if (st.error_flags & ERRF_CAPACITY) return fail(SSD_ERR_CAPACITY, "KV pages or output log exhausted on the device");
   if (st.error_flags & ERRF_NUMERIC) return fail(SSD_ERR_NUMERIC, "non-finite logits seen on the device");
+  if (st.error_flags & ERRF_INPUT) return fail(SSD_ERR_ARG, "a device-side argument was out of range");
   return SSD_OK;
 }
 

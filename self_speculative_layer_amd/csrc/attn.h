@@ -221,7 +221,7 @@ __device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
                                int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
                                const int* __restrict__ pos, int r0, int RB, int g, int s, int nsplit,
                                const bf16_t* __restrict__ local_kv, int local_start, int group_rows,
-                               float* __restrict__ part) {
+                               float* __restrict__ part, int side0 = 0x7fffffff) {
   static_assert(NW == 4, "four waves: 16 keys each");
   constexpr int NT = NW * 64;
   constexpr int KST = SM::KST;
@@ -238,7 +238,9 @@ __device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
   // ---- round 1: active rows, positions, the split's page ids, the queries
   const int na = nrows ? *nrows : M;
   int rp = 0;
-  if (tid < rmax - r0) rp = pos[r0 + tid];
+  // rows >= side0 (tree leaves) see the cache up to the position before their own; their own key is
+  // merged afterwards
+  if (tid < rmax - r0) rp = pos[r0 + tid] - (r0 + tid >= side0 ? 1 : 0);
   const int pg0 = key_beg / PS;
   const int pg = (lane * PS < ATT_CHUNK && pg0 + lane < n_lpages) ? page_table[pg0 + lane] : 0;
   constexpr int QPER = (QT * ATTB_MAXQ * VPR + NT - 1) / NT;
@@ -256,7 +258,9 @@ __device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
   const int Ma = min(M, na);
   const int r1 = min(r0 + RB, Ma);
   if (r1 <= r0) return;
-  const int maxpos = sm.Rpos[r1 - 1 - r0];
+  int maxpos = sm.Rpos[r1 - 1 - r0];                  // positions increase along the rows, except leaf rows
+  if (side0 < r1)
+    for (int i = 0; i < r1 - r0; ++i) maxpos = max(maxpos, sm.Rpos[i]);
   if (key_beg > maxpos) return;
   const int nq = (r1 - r0) * G;
   const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
@@ -447,7 +451,8 @@ __device__ void attn_item_scalar(AttnSmem<T, HD, NW>& sm, const T* __restrict__ 
 }
 
 // One work item: KV head g, split s, the rows r0 .. min(r0 + RB, Ma) - 1 with
-// Ma = min(M, *nrows) (positions increasing).  Keys at positions >= local_start
+// Ma = min(M, *nrows) (positions increasing; rows >= side0, bf16 only, are
+// tree leaves: they see keys up to their position - 1).  Keys at positions >= local_start
 // come from local_kv rows (scoring: the candidate's own keys/values, rows
 // grouped by group_rows).  Requires all NW*64 threads of the block.
 //
@@ -461,10 +466,10 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
                                   int n_lpages, int L, int layer, int H, int KVH, int M,
                                   const int* __restrict__ nrows, const int* __restrict__ pos, int r0, int RB, int g,
                                   int s, int nsplit, const T* __restrict__ local_kv, int local_start, int group_rows,
-                                  float* __restrict__ part) {
+                                  float* __restrict__ part, int side0 = 0x7fffffff) {
   if constexpr (sizeof(T) == 2)
     attn_item_bf16<HD, NW, DEV>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0, RB,
-                                g, s, nsplit, local_kv, local_start, group_rows, part);
+                                g, s, nsplit, local_kv, local_start, group_rows, part, side0);
   else
     attn_item_scalar<T, HD, NW, DEV>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0,
                                      RB, g, s, nsplit, local_kv, local_start, group_rows, part);
@@ -525,9 +530,14 @@ __device__ __forceinline__ float attn_combine_value(const float* __restrict__ pa
 // weighted sums of the splits' o and l in split order, and their quotient.  The o
 // values of the first MP dim pairs per thread are loaded together with (1).
 // The output is in the decode block layout.
+// Rows >= side0 (tree leaves, whose partials cover keys up to their position - 1) have their own key
+// and value side_kv[(row - side0) * 2 + {0, 1}][KVH][HD] as one more split after the last: score
+// (q . k) / sqrt(HD) with q the row's query (q, ldq), sum 1, output v.
 template <int HD, int NW>
 __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __restrict__ part, int nsplit, int r0,
-                                 int r1, int G, int g, int H, bf16_t* __restrict__ out) {
+                                 int r1, int G, int g, int H, bf16_t* __restrict__ out, int side0 = 0x7fffffff,
+                                 const bf16_t* __restrict__ side_kv = nullptr, const bf16_t* __restrict__ q = nullptr,
+                                 int ldq = 0, int KVH = 0) {
   constexpr int NT = NW * 64;
   constexpr int REC = HD + 2;
   constexpr int PR = HD / 2;                          // dim pairs per query
@@ -542,7 +552,19 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
   auto rec = [&](int qq, int sp) -> const float* {
     return part + (((size_t)(r0 + qq / G) * H + g * G + qq % G) * nsplit + sp) * REC;
   };
-  auto nsplits = [&](int qq) { return min(sm.Rpos[qq / G] / ATT_SPLIT + 1, nsplit); };
+  auto nsplits = [&](int qq) { return min(sm.Rpos[qq / G] / ATT_SPLIT + 1, nsplit); };   // stored partials
+  auto leaf = [&](int qq) { return r0 + qq / G >= side0; };
+  auto nterms = [&](int qq) { return nsplits(qq) + (leaf(qq) ? 1 : 0); };                // merged terms
+  // term c of (query qq, dim pair d2): a stored partial's o, or the leaf's own value
+  auto oterm = [&](int qq, int c, int d2) -> float2 {
+    const int ns = nsplits(qq);
+    if (leaf(qq) && c >= ns) {
+      const uint32_t v2 = *(const uint32_t*)(side_kv + ((size_t)(r0 + qq / G - side0) * 2 + 1) * KVH * HD +
+                                             (size_t)g * HD + d2);
+      return make_float2(__uint_as_float(v2 << 16), __uint_as_float(v2 & 0xFFFF0000u));
+    }
+    return *(const float2*)(rec(qq, min(c, ns - 1)) + d2);
+  };
 
   // loads of (1) and of the first round of (3)
   float mv[P1], lv[P1];
@@ -561,9 +583,9 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
   for (int x = 0; x < MP; ++x) {
     const int pi = tid + NT * x;
     if (pi < npair) {
-      const int qq = pi / PR, d2 = (pi % PR) * 2, ns = nsplits(qq);
+      const int qq = pi / PR, d2 = (pi % PR) * 2, ns = nterms(qq);
 #pragma unroll
-      for (int c = 0; c < CH; ++c) ov[x][c] = *(const float2*)(rec(qq, min(c, ns - 1)) + d2);
+      for (int c = 0; c < CH; ++c) ov[x][c] = oterm(qq, min(c, ns - 1), d2);
     }
   }
   // (1)
@@ -576,6 +598,25 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
       Lv[idx] = lv[j];
     }
   }
+  if (side0 < r1) {
+    // the leaves' own terms: one wave per query, lanes over the dimensions, then a butterfly
+    const int lane = tid & 63, wave = tid >> 6;
+    const float scale = 1.0f / sqrtf((float)HD);
+    for (int qq = wave; qq < nq; qq += NW) {
+      if (!leaf(qq)) continue;
+      const int row = r0 + qq / G, head = g * G + qq % G;
+      const bf16_t* qr = q + (size_t)row * ldq + (size_t)head * HD;
+      const bf16_t* kr = side_kv + (size_t)(row - side0) * 2 * KVH * HD + (size_t)g * HD;
+      float acc = 0.f;
+      for (int d = lane; d < HD; d += 64) acc = fmaf(bf2f(qr[d]), bf2f(kr[d]), acc);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      if (lane == 0) {
+        Wt[qq * ATT_MAXW + nsplits(qq)] = __fmul_rn(acc, scale);
+        Lv[qq * ATT_MAXW + nsplits(qq)] = 1.f;
+      }
+    }
+  }
   __syncthreads();
   // (2) per query the maximum of its splits' m and the weights; a wave takes one query at a time
   // (lane = split).  l is accumulated in (3), next to o, in split order.
@@ -583,7 +624,7 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
     const int lane = tid & 63, wave = tid >> 6;
     static_assert(ATT_MAXW <= 64, "one lane per split");
     for (int qq = wave; qq < nq; qq += NW) {
-      const bool on = lane < nsplits(qq);
+      const bool on = lane < nterms(qq);
       const float mv = on ? Wt[qq * ATT_MAXW + lane] : -INFINITY;
       float m = mv;
 #pragma unroll
@@ -599,7 +640,7 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
     for (; c0 < ns; c0 += CH) {
       float2 v[CH];
 #pragma unroll
-      for (int c = 0; c < CH; ++c) v[c] = *(const float2*)(rec(qq, min(c0 + c, ns - 1)) + d2);
+      for (int c = 0; c < CH; ++c) v[c] = oterm(qq, min(c0 + c, ns - 1), d2);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         if (c0 + c < ns) {
@@ -620,7 +661,7 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
   for (int x = 0; x < MP; ++x) {
     const int pi = tid + NT * x;
     if (pi < npair) {
-      const int qq = pi / PR, d2 = (pi % PR) * 2, ns = nsplits(qq);
+      const int qq = pi / PR, d2 = (pi % PR) * 2, ns = nterms(qq);
       const float* w = Wt + qq * ATT_MAXW;
       const float* lw = Lv + qq * ATT_MAXW;
       float2 o = make_float2(0.f, 0.f);
@@ -641,7 +682,7 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
     const int qq = pi / PR, d2 = (pi % PR) * 2;
     float2 o = make_float2(0.f, 0.f);
     float l = 0.f;
-    rest(qq, d2, nsplits(qq), 0, o, l);
+    rest(qq, d2, nterms(qq), 0, o, l);
     store(qq, d2, o, l);
   }
 }

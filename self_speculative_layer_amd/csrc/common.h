@@ -14,6 +14,12 @@ constexpr int WAVE = 64;
 // Flags in DevState::error_flags.
 constexpr int ERRF_CAPACITY = 1;
 constexpr int ERRF_NUMERIC = 2;
+constexpr int ERRF_INPUT = 4;       // a device-side argument out of range (e.g. a tree leaf's depth)
+
+// Draft trees: candidates per draft step, and leaf rows a tree verify can hold (16-row decode blocks
+// with at least one chain row).
+constexpr int TREE_KMAX = 8;
+constexpr int TREE_SLOTS = 15;
 
 // Per-sequence state that lives on the device, so that the host can enqueue
 // a whole decode iteration without reading anything back.
@@ -27,7 +33,10 @@ struct DevState {
   int32_t stop;         // draft early-stop flag (kernels of later draft steps exit at once)
   int32_t n_emitted;    // tokens emitted by the last commit
   int32_t verify_rows;  // d' + 1 of the current verify
-  int32_t pad[7];
+  // tree verify: active rows of the full and prefix blocks, their first leaf row, and the leaf the
+  // acceptance took (-1: none) with its position
+  int32_t tree_rows, tree_prefix_rows, tree_side_full, tree_side_prefix, tree_leaf, tree_leaf_pos;
+  int32_t pad[1];
 };
 
 // ---------------------------------------------------------------------------

@@ -124,7 +124,11 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       eg[j] = gsrc[col];
     }
   }
-  if constexpr (EPI == DEC_QKV) epos = a.pos[erow];
+  int eside = 0x7fffffff;                     // QKV: first tree-leaf row (its keys and values go to side_kv)
+  if constexpr (EPI == DEC_QKV) {
+    epos = a.pos[erow];
+    if (a.side_from) eside = *a.side_from;
+  }
 
   // RMS tile sums of the rows this wave scales: loaded first, summed after the weight loads are issued
   __shared__ float sinv[16];
@@ -274,7 +278,8 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       } else {
         const int kvsel = t.slot < H + KVH ? 0 : 1;
         const int gg = t.slot - H - kvsel * KVH;
-        dst = a.pool + kv_index(epage, a.L, a.layer, kvsel, KVH, gg, a.PS, p % a.PS, HD);
+        dst = row >= eside ? a.side_kv + ((size_t)(row - eside) * 2 + kvsel) * KVH * HD + (size_t)gg * HD
+                           : a.pool + kv_index(epage, a.L, a.layer, kvsel, KVH, gg, a.PS, p % a.PS, HD);
       }
       if (t.slot < H + KVH) {
         float y1, y2;
@@ -356,6 +361,8 @@ int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
 // writes its partial with device-scope stores and counts itself on the
 // (row block, KV head) counter; the item that completes the count merges the
 // rows' partials (in split order) and resets the counter for the next launch.
+// Rows >= *side_from (tree leaves; side_from nullable) see the cache up to
+// their position - 1 and their own key / value from side_kv.
 // ===========================================================================
 
 template <typename T, int HD>
@@ -363,18 +370,23 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(
     const T* __restrict__ q, int ldq, const T* __restrict__ pool, const int* __restrict__ page_table, int PS,
     int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
     const int* __restrict__ pos, int RB, int nsplit, float* __restrict__ part, T* __restrict__ out, int ldo,
-    unsigned* __restrict__ counters, const int* __restrict__ stop) {
+    unsigned* __restrict__ counters, const int* __restrict__ stop, const int* __restrict__ side_from,
+    const T* __restrict__ side_kv) {
   if (stop && *stop) return;
   const int g = blockIdx.x, s = blockIdx.y, rbk = blockIdx.z;
   const int Ma = nrows ? min(M, *nrows) : M;
   const int r0 = rbk * RB, r1 = min(r0 + RB, Ma);
   if (r1 <= r0) return;
-  const int n_act = min(pos[r1 - 1] / ATT_SPLIT + 1, nsplit);   // splits holding a key some row of the block sees
+  const int side0 = side_from ? *side_from : 0x7fffffff;
+  int maxp = pos[r1 - 1];                                        // positions increase, except leaf rows
+  if (side0 < r1)
+    for (int r = r0; r < r1; ++r) maxp = max(maxp, pos[r] - (r >= side0 ? 1 : 0));
+  const int n_act = min(maxp / ATT_SPLIT + 1, nsplit);   // splits holding a key some row of the block sees
   if (s >= n_act) return;
   __shared__ AttnSmem<T, HD, 4> sm;
   __shared__ int is_last;
   attn_partial_item<T, HD, 4, true>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0,
-                                    RB, g, s, nsplit, nullptr, 0, 0, part);
+                                    RB, g, s, nsplit, nullptr, 0, 0, part, side0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -386,17 +398,21 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  attn_merge_block<HD, 4>(sm, part, nsplit, r0, r1, H / KVH, g, H, out);
+  attn_merge_block<HD, 4>(sm, part, nsplit, r0, r1, H / KVH, g, H, out, side0, side_kv, q, ldq, KVH);
 }
+
+bool attention_dec_leaves_fit(int max_ctx) { return attention_nsplit(max_ctx) < ATT_MAXW; }
 
 int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer, int H, int KVH,
                          int M, const int* nrows, const int* pos, int max_ctx, float* part, void* out, int ldo,
-                         unsigned* counters, const int* stop, hipStream_t s) {
+                         unsigned* counters, const int* stop, hipStream_t s, const int* side_from,
+                         const void* side_kv) {
   if (M <= 0) return 0;
   const int G = H / KVH;
   const int RB = ATTB_MAXQ / G;
   if (RB < 1 || M > 16) return SSD_ERR_SHAPE;
   const int nsplit = attention_nsplit(max_ctx);
+  if (side_from && nsplit >= ATT_MAXW) return SSD_ERR_UNSUPPORTED;   // a leaf's own term takes one more slot
   if (nsplit > ATT_MAXW) {
     // longer contexts: partials, then one merge block per (row, head) (the general kernels)
     const RowBlock rb{M, nrows, pos, nullptr, stop};
@@ -407,7 +423,7 @@ int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv,
 #define ATT_DEC(HD)                                                                                             \
   hipLaunchKernelGGL((attn_dec_kernel<bf16_t, HD>), grid, dim3(256), 0, s, (const bf16_t*)q, ldq,                \
                      (const bf16_t*)kv.pool, kv.page_table, kv.page_size, kv.n_lpages, L, layer, H, KVH, M, nrows, \
-                     pos, RB, nsplit, part, (bf16_t*)out, ldo, counters, stop)
+                     pos, RB, nsplit, part, (bf16_t*)out, ldo, counters, stop, side_from, (const bf16_t*)side_kv)
   if (head_dim == 128) ATT_DEC(128); else ATT_DEC(64);
 #undef ATT_DEC
   return dec_ok(hipGetLastError());

@@ -125,6 +125,29 @@ int launch_score(const ssd_row_stat* stats, const int32_t* window, int n_masks, 
                  int32_t* best, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Draft trees (tree.hip).
+
+// Per draft row j < d' (rows of draft_logits): the k_max best tokens into cand[j][TREE_KMAX] and the
+// candidate count into kcount[j]; then the leaves (ranks 1 .. k_j - 1, depth order) into leaf_tok /
+// leaf_depth, their number into n_leaves.
+int launch_tree_candidates(const float* draft_logits, int V, int d, const int32_t* n_drafted, float rho, int k_max,
+                           int max_leaves, int* cand, int* kcount, int32_t* leaf_tok, int32_t* leaf_depth,
+                           int32_t* n_leaves, hipStream_t s);
+// Row positions / tokens of a tree verify's full block (vpos, vtok [d + 1 + max_leaves]) and prefix block
+// (ppos, ptok [1 + max_leaves]); the row counts and first leaf rows in the device state.
+int launch_tree_verify_prep(DevState* st, const int32_t* drafts, const int32_t* n_drafted, int d,
+                            const int32_t* leaf_tok, const int32_t* leaf_depth, const int32_t* n_leaves,
+                            int max_leaves, int* vpos, int* vtok, int* ppos, int* ptok, int max_ctx, hipStream_t s);
+// Greedy tree acceptance from the verify rows' statistics, then the accepted leaf's keys and values
+// (side_kv [L][TREE_SLOTS][2][KVH * HD]) into the cache at its position.
+int launch_tree_accept(const ssd_row_stat* stats, const int32_t* drafts, const int32_t* n_drafted, int d,
+                       const int32_t* leaf_tok, const int32_t* leaf_depth, const int32_t* n_leaves, int max_leaves,
+                       DevState* st, int32_t* out, int32_t* n_out, const bf16_t* side_kv, const KvView& kv, int L,
+                       int KVH, int HD, hipStream_t s);
+// Whether the decode attention can merge a leaf's own term at this context length.
+bool attention_dec_leaves_fit(int max_ctx);
+
+// ---------------------------------------------------------------------------
 // Decode mode (decode.hip): blocks of at most 16 rows, bf16.
 
 enum DecEpilogue {
@@ -152,15 +175,21 @@ struct DecGemm {
   bf16_t* pool; const int* page_table;
   int PS, n_lpages, L, layer, H, KVH, HD;
   const int* pos; const float2* rope_cs; int* err;
+  const int* side_from;             // QKV (nullable): rows >= *side_from are tree leaves; their k, v go to
+  bf16_t* side_kv;                  //   side_kv[(row - *side_from) * 2 + {0, 1}][KVH * HD] instead of the cache
   int n_tiles;                      // set by the launcher
   int* prof_ran;                    // set by the launcher: timing record of a profiled launch (or null)
 };
 int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s);
 
 // Attention with the split merge folded in; counters[n_row_blocks][KVH] start at zero and are left at zero.
+// side_from (nullable): rows >= *side_from are tree leaves, which see the cache up to their position - 1
+// and their own key / value from side_kv[(row - *side_from) * 2 + {0, 1}][KVH * HD] (needs
+// attention_nsplit(max_ctx) < ATT_MAXW).
 int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer, int H, int KVH,
                          int M, const int* nrows, const int* pos, int max_ctx, float* part, void* out, int ldo,
-                         unsigned* counters, const int* stop, hipStream_t s);
+                         unsigned* counters, const int* stop, hipStream_t s, const int* side_from = nullptr,
+                         const void* side_kv = nullptr);
 
 // Draft step j's entry row: position and token from the device state (or the end of the draft when the
 // KV pages are full), then the embedding row and the first consumer's input, as launch_dec_entry.

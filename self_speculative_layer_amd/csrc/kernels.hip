@@ -1410,6 +1410,8 @@ __global__ void state_init_kernel(DevState* st) {
   if (threadIdx.x == 0) {
     st->kvlen = 0; st->last_token = 0; st->iteration = 0; st->n_out = 0; st->error_flags = 0;
     st->n_drafted = 0; st->stop = 0; st->n_emitted = 0; st->verify_rows = 0;
+    st->tree_rows = st->tree_prefix_rows = st->tree_side_full = st->tree_side_prefix = 0;
+    st->tree_leaf = -1; st->tree_leaf_pos = 0;
   }
 }
 
