@@ -62,6 +62,12 @@ WORKLOADS = {
     "13b": dict(shape="llama2-13b-shape", prompt=1024, n_gen=256, random_skip=20, d=8, tau=0.8, T=1.0,
                 desc="LLaMA-2-13B-shaped bf16 decoder, SWIFT skip mask of 20 seeded layers, d<=8, confidence "
                      "stop 0.8, T=1.0 sampling, 1024-token prompt, 256 tokens"),
+    "tree7b": dict(shape="llama2-7b-shape", prompt=512, n_gen=256, exit_layer=8, d=12, tau=0.0, T=0.0,
+                   tree=dict(rho=0.9, k_max=4, max_leaves=3),
+                   desc="LLaMA-2-7B-shaped bf16 decoder, LayerSkip early-exit draft E=8, d=12, greedy, with SWIFT "
+                        "dynamic verification: each draft step's top-k candidates (k from the top-k mass reaching "
+                        "0.9, k <= 4) verified as leaves beside the chain, at most 3 leaves (16 verify rows); "
+                        "512-token random prompt, batch 1"),
     "70b": dict(shape="llama2-70b-shape", prompt=4096, n_gen=128, random_skip=40, d=8, tau=0.0, T=0.0,
                 desc="LLaMA-2-70B-shaped bf16 decoder (GQA 64/8), SWIFT skip mask of 40 seeded layers, d=8, "
                      "greedy, 4096-token prompt, 128 tokens"),
@@ -132,9 +138,19 @@ def cpu_baseline(shape, wl, mask, max_seconds=20.0):
         n = P + len(out)
         drafts, zq, hb = ossd.draft(om, kv, out[-1], n, mask, wl["d"], wl["tau"], wl["T"], synth.SEED_SAMPLING,
                                     iters + 1)
-        zp = ossd.verify(om, kv, out[-1], drafts, n, b, hb)
-        em = ossd.accept_greedy(zp, drafts) if wl["T"] == 0 else ossd.accept_sampled(zp, zq, drafts, wl["T"],
-                                                                                     synth.SEED_SAMPLING, iters + 1)
+        if "tree" in wl:
+            from oracle import tree as otree
+            tr = wl["tree"]
+            leaves = otree.tree_leaves(zq, drafts, tr["rho"], tr["k_max"], tr["max_leaves"])
+            zp, zl = otree.verify_tree(om, kv, out[-1], drafts, leaves, n, b, hb)
+            em, s = otree.accept_tree_greedy(zp, zl, drafts, leaves)
+            if s is not None:
+                j, c = leaves[s]
+                omodel.forward(om, [out[-1]] + [int(t) for t in drafts[: j - 1]] + [c], list(range(n - 1, n + j)), kv)
+        else:
+            zp = ossd.verify(om, kv, out[-1], drafts, n, b, hb)
+            em = ossd.accept_greedy(zp, drafts) if wl["T"] == 0 else ossd.accept_sampled(
+                zp, zq, drafts, wl["T"], synth.SEED_SAMPLING, iters + 1)
         out.extend(em)
         tokens += len(em)
         iters += 1
@@ -215,10 +231,26 @@ def main():
     prefill_ms = ev0.elapsed_time(ev1)
     log("prefill %d tokens: %.1f ms" % (wl["prompt"], prefill_ms))
 
+    tr = wl.get("tree")
+
     def iteration(vev=None):
         h = seq.handle
         B.ssd_draft(h, skip_mask, exit_layer, d, wl["tau"], wl["T"], seed, seq.draft_tokens, seq.draft_logits,
                     seq.n_drafted)
+        if tr is not None:
+            # dynamic verification: leaves from the draft's confidence, one tree verify, tree acceptance
+            B.ssd_tree_candidates(h, seq.draft_logits, seq.n_drafted, d, tr["rho"], tr["k_max"], tr["max_leaves"],
+                                  seq.leaf_tokens, seq.leaf_depth, seq.n_leaves)
+            if vev is not None:
+                vev[0].record()
+            B.ssd_verify_tree(h, skip_mask, exit_layer, d, seq.draft_tokens, seq.n_drafted, seq.leaf_tokens,
+                              seq.leaf_depth, seq.n_leaves, tr["max_leaves"], True, seq.tree_logits)
+            if vev is not None:
+                vev[1].record()
+            B.ssd_accept_tree(h, seq.tree_logits, seq.draft_tokens, seq.n_drafted, d, seq.leaf_tokens,
+                              seq.leaf_depth, seq.n_leaves, tr["max_leaves"], seq.out_tokens, seq.n_out)
+            B.ssd_commit(h, seq.out_tokens, seq.n_out)
+            return
         if vev is not None:
             vev[0].record()
         B.ssd_verify(h, skip_mask, exit_layer, d, seq.draft_tokens, seq.n_drafted, True, seq.verify_logits)
@@ -261,7 +293,8 @@ def main():
     # context during the measured steps (for the verify byte count): its mean kvlen
     kv_mid = (st1.kvlen + st2.kvlen) / 2.0
     b = int(np.argmax(mask.reshape(-1, 2).any(axis=1))) if mask.any() else shape.n_layers
-    vb = verify_bytes(shape, kv_mid, d + 1, b)
+    vrows = d + 1 + (tr["max_leaves"] if tr is not None else 0)
+    vb = verify_bytes(shape, kv_mid, vrows, b)
     vmed = float(np.median(verify_ms))
     log("timed %d steps: %.1f ms (wall %.1f ms), %d tokens -> %.1f tok/s; verify median %.3f ms" %
         (K, elapsed_ms, wall_ms, tokens, value, vmed))
@@ -300,7 +333,9 @@ def main():
         "dtype": "bf16" if shape.dtype == "bf16" else "f32",
         "data": "synthetic (seeded random-init weights and uniform random prompt)",
         "config": {"workload": wl["desc"], "prompt_len": wl["prompt"], "d": d, "conf_thresh": wl["tau"],
-                   "temperature": wl["T"], "batch": 1, "step": "one SSD iteration (draft + verify + accept + commit)"},
+                   "temperature": wl["T"], "batch": 1, "step": "one SSD iteration (draft + verify + accept + commit)"
+                   if tr is None else "one SSD iteration (draft + tree candidates + tree verify + tree accept + "
+                                      "commit)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "measured": "dispatch-timestamp events on every launch of the kernel in %d further steps "
                                  "of the same sequence" % K,
