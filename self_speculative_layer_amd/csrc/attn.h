@@ -215,7 +215,7 @@ __device__ __forceinline__ void attn_tile_bf16(SM& sm, const bf16_t* __restrict_
 
 // bf16 work item (same contract as attn_partial_item below): QT tiles of at most 16 queries each, on
 // the split's keys and values staged once.
-template <int HD, int NW, bool DEV, int QT = 1, typename SM = AttnSmem<bf16_t, HD, NW>>
+template <int HD, int NW, bool DEV, int QT = 1, typename SM = AttnSmem<bf16_t, HD, NW>, bool LEAF = false>
 __device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
                                const bf16_t* __restrict__ pool, const int* __restrict__ page_table, int PS,
                                int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
@@ -240,7 +240,7 @@ __device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
   int rp = 0;
   // rows >= side0 (tree leaves) see the cache up to the position before their own; their own key is
   // merged afterwards
-  if (tid < rmax - r0) rp = pos[r0 + tid] - (r0 + tid >= side0 ? 1 : 0);
+  if (tid < rmax - r0) rp = pos[r0 + tid] - (LEAF && r0 + tid >= side0 ? 1 : 0);
   const int pg0 = key_beg / PS;
   const int pg = (lane * PS < ATT_CHUNK && pg0 + lane < n_lpages) ? page_table[pg0 + lane] : 0;
   constexpr int QPER = (QT * ATTB_MAXQ * VPR + NT - 1) / NT;
@@ -259,7 +259,7 @@ __device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
   const int r1 = min(r0 + RB, Ma);
   if (r1 <= r0) return;
   int maxpos = sm.Rpos[r1 - 1 - r0];                  // positions increase along the rows, except leaf rows
-  if (side0 < r1)
+  if (LEAF && side0 < r1)
     for (int i = 0; i < r1 - r0; ++i) maxpos = max(maxpos, sm.Rpos[i]);
   if (key_beg > maxpos) return;
   const int nq = (r1 - r0) * G;
@@ -460,7 +460,7 @@ __device__ void attn_item_scalar(AttnSmem<T, HD, NW>& sm, const T* __restrict__ 
 // chunk's page ids and the queries; (2) every key and value of the chunk.
 // Items whose split starts past the block's last position return after (1).
 // DEV: partials are written with device-scope stores.
-template <typename T, int HD, int NW, bool DEV = false>
+template <typename T, int HD, int NW, bool DEV = false, bool LEAF = false>
 __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__ q, int ldq,
                                   const T* __restrict__ pool, const int* __restrict__ page_table, int PS,
                                   int n_lpages, int L, int layer, int H, int KVH, int M,
@@ -468,8 +468,10 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
                                   int s, int nsplit, const T* __restrict__ local_kv, int local_start, int group_rows,
                                   float* __restrict__ part, int side0 = 0x7fffffff) {
   if constexpr (sizeof(T) == 2)
-    attn_item_bf16<HD, NW, DEV>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0, RB,
-                                g, s, nsplit, local_kv, local_start, group_rows, part, side0);
+    attn_item_bf16<HD, NW, DEV, 1, AttnSmem<bf16_t, HD, NW>, LEAF>(sm, q, ldq, pool, page_table, PS, n_lpages, L,
+                                                                   layer, H, KVH, M, nrows, pos, r0, RB, g, s,
+                                                                   nsplit, local_kv, local_start, group_rows, part,
+                                                                   side0);
   else
     attn_item_scalar<T, HD, NW, DEV>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0,
                                      RB, g, s, nsplit, local_kv, local_start, group_rows, part);
@@ -533,7 +535,7 @@ __device__ __forceinline__ float attn_combine_value(const float* __restrict__ pa
 // Rows >= side0 (tree leaves, whose partials cover keys up to their position - 1) have their own key
 // and value side_kv[(row - side0) * 2 + {0, 1}][KVH][HD] as one more split after the last: score
 // (q . k) / sqrt(HD) with q the row's query (q, ldq), sum 1, output v.
-template <int HD, int NW>
+template <int HD, int NW, bool LEAF = false>
 __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __restrict__ part, int nsplit, int r0,
                                  int r1, int G, int g, int H, bf16_t* __restrict__ out, int side0 = 0x7fffffff,
                                  const bf16_t* __restrict__ side_kv = nullptr, const bf16_t* __restrict__ q = nullptr,
@@ -553,12 +555,12 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
     return part + (((size_t)(r0 + qq / G) * H + g * G + qq % G) * nsplit + sp) * REC;
   };
   auto nsplits = [&](int qq) { return min(sm.Rpos[qq / G] / ATT_SPLIT + 1, nsplit); };   // stored partials
-  auto leaf = [&](int qq) { return r0 + qq / G >= side0; };
+  auto leaf = [&](int qq) { return LEAF && r0 + qq / G >= side0; };
   auto nterms = [&](int qq) { return nsplits(qq) + (leaf(qq) ? 1 : 0); };                // merged terms
   // term c of (query qq, dim pair d2): a stored partial's o, or the leaf's own value
   auto oterm = [&](int qq, int c, int d2) -> float2 {
     const int ns = nsplits(qq);
-    if (leaf(qq) && c >= ns) {
+    if (LEAF && leaf(qq) && c >= ns) {
       const uint32_t v2 = *(const uint32_t*)(side_kv + ((size_t)(r0 + qq / G - side0) * 2 + 1) * KVH * HD +
                                              (size_t)g * HD + d2);
       return make_float2(__uint_as_float(v2 << 16), __uint_as_float(v2 & 0xFFFF0000u));
@@ -598,7 +600,7 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
       Lv[idx] = lv[j];
     }
   }
-  if (side0 < r1) {
+  if (LEAF && side0 < r1) {
     // the leaves' own terms: one wave per query, lanes over the dimensions, then a butterfly
     const int lane = tid & 63, wave = tid >> 6;
     const float scale = 1.0f / sqrtf((float)HD);

@@ -365,7 +365,7 @@ int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
 // their position - 1 and their own key / value from side_kv.
 // ===========================================================================
 
-template <typename T, int HD>
+template <typename T, int HD, bool LEAF>
 __global__ __launch_bounds__(256) void attn_dec_kernel(
     const T* __restrict__ q, int ldq, const T* __restrict__ pool, const int* __restrict__ page_table, int PS,
     int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
@@ -377,15 +377,15 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(
   const int Ma = nrows ? min(M, *nrows) : M;
   const int r0 = rbk * RB, r1 = min(r0 + RB, Ma);
   if (r1 <= r0) return;
-  const int side0 = side_from ? *side_from : 0x7fffffff;
+  const int side0 = LEAF ? *side_from : 0x7fffffff;
   int maxp = pos[r1 - 1];                                        // positions increase, except leaf rows
-  if (side0 < r1)
+  if (LEAF && side0 < r1)
     for (int r = r0; r < r1; ++r) maxp = max(maxp, pos[r] - (r >= side0 ? 1 : 0));
   const int n_act = min(maxp / ATT_SPLIT + 1, nsplit);   // splits holding a key some row of the block sees
   if (s >= n_act) return;
   __shared__ AttnSmem<T, HD, 4> sm;
   __shared__ int is_last;
-  attn_partial_item<T, HD, 4, true>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0,
+  attn_partial_item<T, HD, 4, true, LEAF>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0,
                                     RB, g, s, nsplit, nullptr, 0, 0, part, side0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores are complete
   __syncthreads();
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  attn_merge_block<HD, 4>(sm, part, nsplit, r0, r1, H / KVH, g, H, out, side0, side_kv, q, ldq, KVH);
+  attn_merge_block<HD, 4, LEAF>(sm, part, nsplit, r0, r1, H / KVH, g, H, out, side0, side_kv, q, ldq, KVH);
 }
 
 bool attention_dec_leaves_fit(int max_ctx) { return attention_nsplit(max_ctx) < ATT_MAXW; }
@@ -420,11 +420,16 @@ int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv,
                             out, ldo, s, true);
   }
   const dim3 grid(KVH, nsplit, (M + RB - 1) / RB);
-#define ATT_DEC(HD)                                                                                             \
-  hipLaunchKernelGGL((attn_dec_kernel<bf16_t, HD>), grid, dim3(256), 0, s, (const bf16_t*)q, ldq,                \
+#define ATT_DEC(HD, LF)                                                                                         \
+  hipLaunchKernelGGL((attn_dec_kernel<bf16_t, HD, LF>), grid, dim3(256), 0, s, (const bf16_t*)q, ldq,            \
                      (const bf16_t*)kv.pool, kv.page_table, kv.page_size, kv.n_lpages, L, layer, H, KVH, M, nrows, \
                      pos, RB, nsplit, part, (bf16_t*)out, ldo, counters, stop, side_from, (const bf16_t*)side_kv)
-  if (head_dim == 128) ATT_DEC(128); else ATT_DEC(64);
+  // leaf rows are a separate instantiation: the chain's launches keep the plain merge
+  if (side_from) {
+    if (head_dim == 128) ATT_DEC(128, true); else ATT_DEC(64, true);
+  } else {
+    if (head_dim == 128) ATT_DEC(128, false); else ATT_DEC(64, false);
+  }
 #undef ATT_DEC
   return dec_ok(hipGetLastError());
 }
