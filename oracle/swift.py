@@ -5,8 +5,7 @@ candidate layer sets are proposed by random search, scored by matchness on the
 last context window (the scoring of oracle/ssd.py), and the best one is kept;
 the phase ends at a step limit, after a number of steps without improvement, or
 once the matchness passes a target (the digest's settings: 1000 steps, 300
-unimproved steps, 0.95).  The periodic Bayesian-optimisation step of the pages
-is not part of this search.
+unimproved steps, 0.95, and a Bayesian-optimisation step every 25 steps).
 
 Readings taken (the pages give no procedure beyond the above):
   * a candidate skips n_skip whole layers (both sub-layers), or n_skip of the
@@ -23,7 +22,19 @@ Readings taken (the pages give no procedure beyond the above):
     proposals) is replaced by the step's best proposal (lowest index on ties)
     only when that proposal scores strictly higher; a step without replacement
     counts as unimproved; the search stops when the incumbent's score exceeds
-    the target, after `patience` unimproved steps in a row, or after max_steps.
+    the target, after `patience` unimproved steps in a row, or after max_steps;
+  * the Bayesian-optimisation step (every bo_every-th step, t > 0; SWIFT digest
+    §4.1.2 "periodic Bayesian optimization", §B.2 every 25 steps, §5.3 the
+    interval beta): a Gaussian process over the mask vectors x in {0,1}^{2L} of
+    the most recent bo_window scored plans (zero-mean after subtracting the
+    scores' mean and dividing by their standard deviation; squared-exponential
+    kernel exp(-|x - x'|^2 / (2 l^2)) with l^2 = the number of skipped entries,
+    unit signal variance, 1e-6 noise) ranks a pool of pool_factor * n_cand
+    random proposals (counter (step, candidate) as above, candidates 0..pool-1)
+    by expected improvement over the incumbent's score; the n_cand best (lower
+    pool index first among equal values) are scored, in that order.  When the
+    scores seen so far are all equal there is nothing to model and the step
+    proposes at random like the others.
 """
 import numpy as np
 
@@ -63,22 +74,85 @@ def propose_mask(L, n_skip, seed, step, cand, sublayers=False):
     return layers_to_mask(L, propose_layers(L, n_skip, seed, step, cand))
 
 
-def search(score_fn, L, init_mask, n_skip, n_cand, max_steps, patience, target, seed, sublayers=False):
-    """Random search.  score_fn(list of masks) -> scores.  Returns the final
-    incumbent mask, its score, the number of steps run and the per-step
-    history [(proposal masks, their scores, incumbent score after the step)]."""
+def gp_posterior(X, y, Xq, ell2, noise=1e-6):
+    """Posterior mean and standard deviation at Xq of a zero-mean Gaussian
+    process with kernel exp(-|x - x'|^2 / (2 ell2)) (unit signal variance) and
+    observation noise `noise`, conditioned on (X, y)."""
+    X = np.asarray(X, np.float64)
+    Xq = np.asarray(Xq, np.float64)
+    def kern(A, B):
+        d2 = ((A[:, None, :] - B[None, :, :]) ** 2).sum(-1)
+        return np.exp(-d2 / (2.0 * ell2))
+    Kxx = kern(X, X) + noise * np.eye(len(X))
+    Kqx = kern(Xq, X)
+    alpha = np.linalg.solve(Kxx, np.asarray(y, np.float64))
+    mu = Kqx @ alpha
+    v = np.linalg.solve(Kxx, Kqx.T)
+    var = np.maximum(1.0 - np.sum(Kqx * v.T, axis=1), 0.0)
+    return mu, np.sqrt(var)
+
+
+def expected_improvement(mu, sd, best):
+    """E[max(Y - best, 0)] for Y ~ N(mu, sd^2); max(mu - best, 0) where sd = 0."""
+    from math import erfc, exp, pi, sqrt
+    out = []
+    for m, s in zip(np.atleast_1d(mu), np.atleast_1d(sd)):
+        if s <= 1e-12:
+            out.append(max(m - best, 0.0))
+            continue
+        z = (m - best) / s
+        cdf = 0.5 * erfc(-z / sqrt(2.0))
+        pdf = exp(-0.5 * z * z) / sqrt(2.0 * pi)
+        out.append((m - best) * cdf + s * pdf)
+    return np.array(out)
+
+
+def bo_proposals(obs_masks, obs_scores, inc_score, pool, n_cand):
+    """The n_cand pool plans with the highest expected improvement under the GP
+    of the observed (mask, score) pairs (the module's reading), best first,
+    lower pool index first among equal values; None when the observed scores
+    are all equal."""
+    y = np.asarray(obs_scores, np.float64)
+    sd = y.std()
+    if not sd > 0:
+        return None
+    mean = y.mean()
+    ell2 = float(np.asarray(pool[0]).sum())
+    mu, s = gp_posterior(obs_masks, (y - mean) / sd, pool, ell2)
+    ei = expected_improvement(mu, s, (inc_score - mean) / sd)
+    order = sorted(range(len(pool)), key=lambda i: (-ei[i], i))
+    return [pool[i] for i in order[:n_cand]]
+
+
+def search(score_fn, L, init_mask, n_skip, n_cand, max_steps, patience, target, seed, sublayers=False, bo_every=0,
+           pool_factor=8, bo_window=256):
+    """Random search with the periodic Bayesian-optimisation step.  score_fn(list
+    of masks) -> scores.  Returns the final incumbent mask, its score, the
+    number of steps run and the per-step history [(proposal masks, their
+    scores, incumbent score after the step)]."""
     inc = np.asarray(init_mask, np.uint8).copy()
     inc_score = None
     unimproved = 0
     history = []
+    obs_m, obs_s = [], []
     t = 0
     while t < max_steps:
-        props = [propose_mask(L, n_skip, seed, t, c, sublayers) for c in range(n_cand)]
+        props = None
+        if bo_every > 0 and t > 0 and t % bo_every == 0:
+            pool = [propose_mask(L, n_skip, seed, t, c, sublayers) for c in range(pool_factor * n_cand)]
+            props = bo_proposals(obs_m[-bo_window:], obs_s[-bo_window:], inc_score, pool, n_cand)
+        if props is None:
+            props = [propose_mask(L, n_skip, seed, t, c, sublayers) for c in range(n_cand)]
         if t == 0:
             sc = list(score_fn([inc] + props))
             inc_score, sc = sc[0], sc[1:]
         else:
             sc = list(score_fn(props))
+        if t == 0:
+            obs_m.append(inc.copy())
+            obs_s.append(inc_score)
+        obs_m.extend(p.copy() for p in props)
+        obs_s.extend(sc)
         k = int(np.argmax(sc))                      # lowest index among the maxima
         if sc[k] > inc_score:
             inc, inc_score = props[k].copy(), sc[k]

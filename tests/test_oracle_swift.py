@@ -138,3 +138,66 @@ def test_library_helpers_reject_bad_arguments():
     with pytest.raises(B.SSDError):
         B.ssd_swift_propose(4, 1, 1, -1, 0)
     assert B.ssd_swift_propose(4, 8, 1, 0, 0, sublayers=True).all()
+
+
+# ---------------------------------------------------------------- Bayesian-optimisation step
+def test_gp_posterior_matches_sklearn():
+    """The GP of the BO step against scikit-learn's Gaussian-process regressor with
+    the same fixed kernel (RBF, length scale sqrt(ell2)) and noise."""
+    from sklearn.gaussian_process import GaussianProcessRegressor
+    from sklearn.gaussian_process.kernels import RBF
+    rng = np.random.default_rng(5)
+    X = (rng.random((40, 16)) < 0.5).astype(np.float64)
+    y = rng.standard_normal(40)
+    Xq = (rng.random((25, 16)) < 0.5).astype(np.float64)
+    ell2 = 8.0
+    mu, sd = swift.gp_posterior(X, y, Xq, ell2, noise=1e-6)
+    ref = GaussianProcessRegressor(kernel=RBF(length_scale=np.sqrt(ell2), length_scale_bounds="fixed"), alpha=1e-6,
+                                   optimizer=None, normalize_y=False).fit(X, y)
+    rmu, rsd = ref.predict(Xq, return_std=True)
+    np.testing.assert_allclose(mu, rmu, rtol=0, atol=1e-8)
+    np.testing.assert_allclose(sd, rsd, rtol=0, atol=1e-6)
+    # interpolation: at a training point the mean is the observation and the spread vanishes
+    m0, s0 = swift.gp_posterior(X, y, X[:3], ell2, noise=1e-10)
+    np.testing.assert_allclose(m0, y[:3], atol=1e-6)
+    assert np.all(s0 < 1e-3)
+
+
+@pytest.mark.parametrize("mu,sd,best", [(0.3, 0.7, 0.1), (-1.0, 0.5, 0.2), (2.0, 1e-3, 0.5), (0.0, 2.0, 0.0),
+                                        (0.4, 0.0, 0.1), (0.1, 0.0, 0.4)])
+def test_expected_improvement_is_the_integral(mu, sd, best):
+    from scipy import integrate, stats
+    got = swift.expected_improvement([mu], [sd], best)[0]
+    if sd == 0:
+        assert got == max(mu - best, 0.0)
+        return
+    ref, _ = integrate.quad(lambda v: (v - best) * stats.norm.pdf(v, mu, sd), best, mu + 12 * sd, limit=200)
+    assert abs(got - ref) < 1e-9 * max(1.0, abs(ref))
+
+
+def test_bo_step_prefers_plans_the_model_expects_to_score_higher():
+    """On a score that counts the skipped layers of a hidden good set, the BO
+    step's picks score far above the pool they come from (a sign error in the
+    improvement, a transposed kernel or a wrong ordering would not)."""
+    L, n_skip, n_cand = 24, 8, 6
+    good = set(range(0, 24, 2))
+    score = lambda m: sum(1 for l in range(L) if m[2 * l] and l in good) / n_skip
+    obs = [swift.propose_mask(L, n_skip, 9, 0, c) for c in range(60)]
+    ys = [score(m) for m in obs]
+    pool = [swift.propose_mask(L, n_skip, 9, 1, c) for c in range(8 * n_cand)]
+    picks = swift.bo_proposals(obs, ys, max(ys), pool, n_cand)
+    assert np.mean([score(m) for m in picks]) > np.mean([score(m) for m in pool]) + 0.15
+    assert swift.bo_proposals(obs, [0.5] * len(obs), 0.5, pool, n_cand) is None   # nothing to model
+
+
+def test_search_without_a_bo_step_in_range_is_random_search():
+    L, n_skip = 12, 4
+    fn = lambda ms: [float(m[::2][:6].sum()) / n_skip for m in ms]
+    init = swift.layers_to_mask(L, swift.uniform_skip_layers(L, n_skip))
+    a = swift.search(fn, L, init, n_skip, 5, 6, 100, 2.0, 3)
+    b = swift.search(fn, L, init, n_skip, 5, 6, 100, 2.0, 3, bo_every=7)
+    assert a[1] == b[1] and a[2] == b[2] and np.array_equal(a[0], b[0])
+    c = swift.search(fn, L, init, n_skip, 5, 6, 100, 2.0, 3, bo_every=2)
+    same = lambda ha, hb: all(np.array_equal(x, y) for x, y in zip(ha[0], hb[0]))
+    assert same(a[3][0], c[3][0]) and same(a[3][1], c[3][1])   # steps 0, 1: random proposals
+    assert not same(a[3][2], c[3][2])                           # step 2: the BO step's picks
