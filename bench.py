@@ -540,6 +540,18 @@ def run_scoring(args):
         "best": (np.nonzero(search_out["best"][::2])[0].tolist() if search else int(best.item())),
         "prefill_ms": round(prefill_ms, 2),
     }
+    if search:
+        # a 26-step search with and without its Bayesian-optimisation step at step 25 (the pages' interval):
+        # the difference is the host's GP fit and ranking of the 120-plan pool on 256 observations
+        times = {}
+        for bo in (0, 25):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            B.ssd_swift_search(seq.handle, window, P - 1, gamma, init, n_skip, nm - 1, 26, 1000, 2.0,
+                               synth.SEED_MASKS, shape.n_layers, bo_every=bo)
+            times[bo] = (time.perf_counter() - t0) * 1e3
+        result["search_26_steps_ms"] = {"random": round(times[0], 2), "with_bo_step_25": round(times[25], 2)}
+        log("26-step search: %.1f ms random, %.1f ms with the BO step" % (times[0], times[25]))
     seq.close()
     model.close()
     print(json.dumps(result), flush=True)

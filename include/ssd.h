@@ -335,12 +335,19 @@ int ssd_swift_propose(int n_layers, int n_skip, int sublayers, uint64_t seed, in
  * ssd_swift_propose with the same sublayers flag.  Step t scores its
  * n_cand proposals (step 0 also the starting plan init_mask_host) in one batched scoring pass; the
  * search stops after max_steps steps, after `patience` consecutive steps without improvement, or as
- * soon as the incumbent's score exceeds `target`.  Requires (n_cand + 1) * gamma <= max_rows and
+ * soon as the incumbent's score exceeds `target`.  Every bo_every-th step (t > 0; 0 = never) is a
+ * Bayesian-optimisation step ([SWIFT] §4.1.2 "periodic Bayesian optimization", §B.2 every 25 steps):
+ * a Gaussian process over the mask vectors of the most recent 256 scored plans (scores standardised,
+ * kernel exp(-|x - x'|^2 / (2 l^2)) with l^2 = the number of skipped entries, unit signal variance,
+ * 1e-6 noise; double precision on the host) ranks a pool of 8 * n_cand proposals (candidates
+ * 0..8 n_cand - 1 of the step's counter) by expected improvement over the incumbent, and the n_cand
+ * best (lower pool index first among equal values) are scored, best first; when every score seen
+ * so far is equal the step proposes at random.  Requires (n_cand + 1) * gamma <= max_rows and
  * n_cand + 1 <= 64.  Out: best_mask_host[2L] (the incumbent), *best_score, *n_steps.  Synchronises
  * the stream once per step (the scores decide the next step). */
 int ssd_swift_search(ssd_seq* seq, const int32_t* window_dev, int pos0, int gamma, const uint8_t* init_mask_host,
                      int n_skip, int sublayers, int n_cand, int max_steps, int patience, float target, uint64_t seed,
-                     uint8_t* best_mask_host, float* best_score, int* n_steps, hipStream_t stream);
+                     int bo_every, uint8_t* best_mask_host, float* best_score, int* n_steps, hipStream_t stream);
 
 /* SpecEE exit features (next row f4; [SpecEE] §4.3.1) of rows hidden states h_dev [rows][D] (fp32, a
  * layer's output in the residual stream) for k speculative tokens tokens_dev[k] (1 <= k <= 16):

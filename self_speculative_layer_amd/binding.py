@@ -91,7 +91,7 @@ def lib():
             "ssd_uniform_mask": [I, I, P],
             "ssd_specee_features": [P, P, I, P, I, P, P, P],
             "ssd_swift_propose": [I, I, I, U64, I, I, P],
-            "ssd_swift_search": [P, P, I, I, P, I, I, I, I, I, F, U64, P, ctypes.POINTER(F), ctypes.POINTER(I), P],
+            "ssd_swift_search": [P, P, I, I, P, I, I, I, I, I, F, U64, I, P, ctypes.POINTER(F), ctypes.POINTER(I), P],
             "ssd_row_stats": [P, I, I, F, U64, ctypes.c_int32, P, P],
             "ssd_read_state": [P, ctypes.POINTER(ssd_state), P],
             "ssd_read_output": [P, P, I, ctypes.POINTER(I), P],
@@ -265,14 +265,14 @@ def ssd_swift_propose(n_layers, n_skip, seed, step, cand, sublayers=False):
 
 
 def ssd_swift_search(seq, window, pos0, gamma, init_mask, n_skip, n_cand, max_steps, patience, target, seed,
-                     n_layers, sublayers=False, stream=None):
+                     n_layers, sublayers=False, bo_every=0, stream=None):
     """Returns (best mask, best score, steps run)."""
     import numpy as np
     im = np.ascontiguousarray(np.asarray(init_mask, dtype=np.uint8))
     out = np.zeros(2 * n_layers, np.uint8)
     sc, ns = F(0.0), I(0)
     check(lib().ssd_swift_search(seq, _ptr(window), pos0, gamma, im.ctypes.data_as(ctypes.c_void_p), n_skip,
-                                 1 if sublayers else 0, n_cand, max_steps, patience, target, seed,
+                                 1 if sublayers else 0, n_cand, max_steps, patience, target, seed, bo_every,
                                  out.ctypes.data_as(ctypes.c_void_p),
                                  ctypes.byref(sc), ctypes.byref(ns), _stream(stream)))
     return out, float(sc.value), int(ns.value)

@@ -839,6 +839,80 @@ void propose_layers(int L, int n_skip, int sublayers, uint64_t seed, int step, i
   }
 }
 
+// The search's Bayesian-optimisation step: a Gaussian process over the mask vectors of the observed
+// plans (scores standardised; kernel exp(-|x - x'|^2 / (2 l^2)), l^2 = the number of skipped entries of a
+// pool plan, unit signal variance, 1e-6 noise) ranks the pool's plans by expected improvement over the
+// incumbent; picks = the n_cand best, lower pool index first among equal values.  Returns false when the
+// observed scores are all equal (nothing to model).
+bool bo_rank(const uint8_t* obs, const double* ys, int n, double inc_score, const uint8_t* pool, int P, size_t ML,
+             int n_cand, std::vector<int>& picks) {
+  double mean = 0.0;
+  for (int i = 0; i < n; ++i) mean += ys[i];
+  mean /= n;
+  double var = 0.0;
+  for (int i = 0; i < n; ++i) var += (ys[i] - mean) * (ys[i] - mean);
+  const double sd = std::sqrt(var / n);
+  if (!(sd > 0.0)) return false;
+  double ell2 = 0.0;
+  for (size_t e = 0; e < ML; ++e) ell2 += pool[e] ? 1.0 : 0.0;
+  if (!(ell2 > 0.0)) ell2 = 1.0;
+  auto kern = [&](const uint8_t* a, const uint8_t* b) {
+    double d2 = 0.0;
+    for (size_t e = 0; e < ML; ++e) d2 += (a[e] != 0) != (b[e] != 0) ? 1.0 : 0.0;
+    return std::exp(-d2 / (2.0 * ell2));
+  };
+  // Cholesky factor C (lower) of K + 1e-6 I, then alpha = K^-1 y
+  std::vector<double> C((size_t)n * n, 0.0), y(n), alpha(n), k(n), v(n);
+  for (int i = 0; i < n; ++i) y[i] = (ys[i] - mean) / sd;
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j <= i; ++j) {
+      double a = kern(obs + i * ML, obs + j * ML) + (i == j ? 1e-6 : 0.0);
+      for (int t = 0; t < j; ++t) a -= C[(size_t)i * n + t] * C[(size_t)j * n + t];
+      C[(size_t)i * n + j] = i == j ? std::sqrt(std::max(a, 1e-300)) : a / C[(size_t)j * n + j];
+    }
+  auto lower_solve = [&](const std::vector<double>& b, std::vector<double>& x) {
+    for (int i = 0; i < n; ++i) {
+      double a = b[i];
+      for (int t = 0; t < i; ++t) a -= C[(size_t)i * n + t] * x[t];
+      x[i] = a / C[(size_t)i * n + i];
+    }
+  };
+  std::vector<double> z(n);
+  lower_solve(y, z);
+  for (int i = n - 1; i >= 0; --i) {
+    double a = z[i];
+    for (int t = i + 1; t < n; ++t) a -= C[(size_t)t * n + i] * alpha[t];
+    alpha[i] = a / C[(size_t)i * n + i];
+  }
+  const double best = (inc_score - mean) / sd;
+  std::vector<double> ei(P);
+  for (int p = 0; p < P; ++p) {
+    double mu = 0.0;
+    for (int i = 0; i < n; ++i) {
+      k[i] = kern(pool + p * ML, obs + i * ML);
+      mu += k[i] * alpha[i];
+    }
+    lower_solve(k, v);
+    double vv = 0.0;
+    for (int i = 0; i < n; ++i) vv += v[i] * v[i];
+    const double sg = std::sqrt(std::max(1.0 - vv, 0.0));
+    if (sg <= 1e-12) {
+      ei[p] = std::max(mu - best, 0.0);
+    } else {
+      const double zz = (mu - best) / sg;
+      ei[p] = (mu - best) * 0.5 * std::erfc(-zz / std::sqrt(2.0)) + sg * std::exp(-0.5 * zz * zz) / std::sqrt(2.0 * M_PI);
+    }
+  }
+  std::vector<int> order(P);
+  for (int p = 0; p < P; ++p) order[p] = p;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return ei[a] > ei[b]; });
+  picks.assign(order.begin(), order.begin() + std::min(n_cand, P));
+  return true;
+}
+
+constexpr int BO_POOL_FACTOR = 8;     // pool = 8 n_cand random proposals
+constexpr int BO_WINDOW = 256;        // the GP sees the most recent 256 scored plans
+
 }  // namespace
 
 extern "C" int ssd_uniform_mask(int n_layers, int n_skip, uint8_t* mask_host) {
@@ -862,17 +936,20 @@ extern "C" int ssd_swift_propose(int n_layers, int n_skip, int sublayers, uint64
 
 extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0, int gamma,
                                 const uint8_t* init_mask_host, int n_skip, int sublayers, int n_cand, int max_steps,
-                                int patience, float target, uint64_t seed, uint8_t* best_mask_host,
+                                int patience, float target, uint64_t seed, int bo_every, uint8_t* best_mask_host,
                                 float* best_score, int* n_steps, hipStream_t s) {
   CHECK_ARG(q && window_dev && init_mask_host && best_mask_host && best_score && n_steps, "null argument");
   const int L = q->m->d.n_layers;
   CHECK_ARG(n_skip >= 0 && n_skip <= (sublayers ? 2 : 1) * L && n_cand >= 1 && n_cand + 1 <= 64 && max_steps >= 1 &&
-                patience >= 1,
+                patience >= 1 && bo_every >= 0,
             "bad search parameters");
   if ((n_cand + 1) * gamma > q->max_rows) return fail(SSD_ERR_CAPACITY, "(n_cand + 1) * gamma exceeds max_rows");
   const size_t ML = 2 * (size_t)L;
   std::vector<uint8_t> inc(init_mask_host, init_mask_host + ML), masks((n_cand + 1) * ML);
   std::vector<float> sc(n_cand + 1);
+  std::vector<uint8_t> obs_m, pool;     // every scored plan, in scoring order, and a BO step's pool
+  std::vector<double> obs_s;
+  std::vector<int> picks;
   float inc_score = 0.f;
   int unimproved = 0, t = 0;
   while (t < max_steps) {
@@ -881,12 +958,27 @@ extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0,
       std::copy(inc.begin(), inc.end(), masks.begin());
       off = 1;
     }
-    for (int c = 0; c < n_cand; ++c) propose_layers(L, n_skip, sublayers, seed, t, c, masks.data() + (off + c) * ML);
+    bool bo = false;
+    if (bo_every > 0 && t > 0 && t % bo_every == 0) {
+      const int P = BO_POOL_FACTOR * n_cand;
+      pool.resize((size_t)P * ML);
+      for (int c = 0; c < P; ++c) propose_layers(L, n_skip, sublayers, seed, t, c, pool.data() + c * ML);
+      const int n = std::min((int)obs_s.size(), BO_WINDOW);
+      const size_t first = obs_s.size() - n;
+      bo = bo_rank(obs_m.data() + first * ML, obs_s.data() + first, n, inc_score, pool.data(), P, ML, n_cand, picks);
+      if (bo)
+        for (int c = 0; c < n_cand; ++c)
+          std::copy(pool.begin() + picks[c] * ML, pool.begin() + (picks[c] + 1) * ML, masks.begin() + (off + c) * ML);
+    }
+    if (!bo)
+      for (int c = 0; c < n_cand; ++c) propose_layers(L, n_skip, sublayers, seed, t, c, masks.data() + (off + c) * ML);
     const int nm = n_cand + off;
     TRY(ssd_score_masks(q, masks.data(), nm, window_dev, pos0, gamma, q->w.swift_scores, q->w.swift_best, s));
     if (hipMemcpy(sc.data(), q->w.swift_scores, sizeof(float) * nm, hipMemcpyDeviceToHost) != hipSuccess)
       return fail(SSD_ERR_HIP, "read scores");
     if (t == 0) inc_score = sc[0];
+    obs_m.insert(obs_m.end(), masks.begin(), masks.begin() + nm * ML);
+    for (int c = 0; c < nm; ++c) obs_s.push_back((double)sc[c]);
     int k = off;
     for (int c = off + 1; c < nm; ++c)
       if (sc[c] > sc[k]) k = c;
