@@ -179,3 +179,38 @@ def test_tree_arguments_rejected():
     assert e.value.code == B.SSD_ERR_ARG
     seq.close()
     g.close()
+
+
+@pytest.mark.parametrize("page_size", [16, 32])
+def test_paged_layouts_give_identical_results(page_size):
+    """Row a5's paged cache: SSD and tree decoding with small pages scattered by a
+    permuted page table give the same tokens, and the same verify logits bit for
+    bit, as the contiguous 64-key pages (keys are addressed per position; the
+    attention's 64-key splits do not depend on the page size).  The tree run
+    accepts leaves, so the repair of an accepted leaf's keys and values goes
+    through the scattered pages too."""
+    shape = BF16_HD64
+    plan = TREE_PLANS[shape.name]
+    mask, d, ml = plan["mask"], plan["d"], plan["max_leaves"]
+    g = gpu_model(shape)
+    P, n_gen = 70, 48
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    max_ctx = P + n_gen + 2 * d + 16
+    n_lp = (max_ctx + page_size - 1) // page_size
+    perm = [(7 * i + 3) % n_lp for i in range(n_lp)]
+    assert sorted(perm) == list(range(n_lp))
+    runs = []
+    for ps, pt in ((64, None), (page_size, perm)):
+        seq = B.Sequence(g, max_ctx=max_ctx, max_rows=16, max_draft=d, page_size=ps, page_table=pt)
+        out, stats = seq.generate_ssd(dev(prompt), n_gen, skip_mask=mask, d=d)
+        vz = seq.verify_logits.clone()
+        seq.close()
+        seq = B.Sequence(g, max_ctx=max_ctx, max_rows=16, max_draft=d, page_size=ps, page_table=pt)
+        tout, tstats = seq.generate_tree(dev(prompt), n_gen, skip_mask=mask, d=d, rho=RHO, k_max=K_MAX, max_leaves=ml)
+        tz = seq.tree_logits.clone()
+        seq.close()
+        runs.append(([int(x) for x in out], stats, vz, [int(x) for x in tout], tstats, tz))
+    a, b = runs
+    assert a[0] == b[0] and a[1] == b[1] and torch.equal(a[2], b[2])
+    assert a[3] == b[3] and a[4] == b[4] and torch.equal(a[5], b[5])
+    g.close()
