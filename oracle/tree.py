@@ -26,13 +26,33 @@ notes):
       the target's argmax, and stop.  After d' accepted drafts the target's
       argmax after y_d' is the bonus.  Every emitted token is the full
       model's greedy choice, so the output equals greedy AR decoding.
-      Only temperature 0 is covered.
+  R5  Sampling (temperature T > 0).  The top-k tokens are not draws from q,
+      and the p/q rule preserves the target distribution only for drawn
+      candidates, so at T > 0: k_j from R1 on softmax(z_j / T); the draft token
+      y_j is the chain's draw; the leaves of depth j are k_j - 1 further
+      independent draws from q_j (race keys z/T + Gumbel, purpose "leaf",
+      counter row (j - 1) + 256 r for the r-th extra draw); the verify is R2's.
+      Acceptance at depth j takes the candidates in order c_0 = y_j, then the
+      leaves of depth j: with p' = p_j, candidate c_i is accepted when
+      u_i q_j(c_i) < p'(c_i) (u_i: purpose "accept", row (j - 1) + 256 i), else
+      p' becomes norm(max(0, p' - q_j)) (p' kept when that is all zero).  c_0
+      accepted: go on to depth j + 1.  A leaf accepted: emit it and a draw from
+      the full model after it (purpose "sample", row (j - 1) + 256 i).  All
+      rejected: emit a draw from p' (purpose "sample", row j - 1).  This is the
+      multi-candidate form of the speculative-sampling rule (SpecInfer, Miao et
+      al. 2024): with candidates drawn independently from q_j the emitted token
+      follows p_j.  Without leaves it is the chain rule of ssd.accept_sampled,
+      draw for draw.
 """
 import numpy as np
 
 from . import model as mdl
+from . import philox
 from . import ssd
 from .numerics import argmax_lowest, softmax
+
+PURPOSE_LEAF = 4
+ROW_STRIDE = 256       # counter row of the r-th candidate of draft step j: (j - 1) + 256 r
 
 
 def topk_lowest(z, k):
@@ -42,10 +62,10 @@ def topk_lowest(z, k):
     return [int(i) for i in np.argsort(-z, kind="stable")[:k]]
 
 
-def candidate_count(z, rho, k_max):
+def candidate_count(z, rho, k_max, T=0.0):
     """R1: the least k >= 1 such that the k most probable tokens of softmax(z)
-    hold at least rho of the mass, capped at k_max."""
-    q = softmax(np.asarray(z, np.float64))
+    (softmax(z / T) when T > 0, R5) hold at least rho of the mass, capped at k_max."""
+    q = softmax(np.asarray(z, np.float64) / (T if T > 0 else 1.0))
     top = topk_lowest(z, k_max)
     cum = np.cumsum(q[top])
     hit = np.nonzero(cum >= rho)[0]
@@ -65,6 +85,59 @@ def tree_leaves(zq, drafts, rho, k_max, budget):
             if len(leaves) < budget:
                 leaves.append((j, t))
     return leaves
+
+
+def tree_leaves_sampled(zq, drafts, T, rho, k_max, budget, seed, it):
+    """R5: leaves (depth j, token) of a sampled draft, in depth order then draw
+    order, at most `budget`: k_j - 1 independent draws from softmax(zq[j-1] / T)."""
+    leaves = []
+    for j in range(1, len(drafts) + 1):
+        k = candidate_count(zq[j - 1], rho, k_max, T)
+        for r in range(1, k):
+            if len(leaves) < budget:
+                t = ssd.sample_logits(zq[j - 1], T, seed, it, (j - 1) + ROW_STRIDE * r, PURPOSE_LEAF)
+                leaves.append((j, t))
+    return leaves
+
+
+def accept_tree_sampled(zp, zq, zl, drafts, leaves, T, seed, it):
+    """R5: (emitted tokens, index of the accepted leaf or None).  Decisions on
+    float32 quantities, as ssd.accept_sampled; the final draw at a depth uses the
+    last nonzero max(0, p' - q) unnormalised (log p when there was none), so that
+    a depth without leaves draws exactly as the chain rule."""
+    dp = len(drafts)
+    for j in range(1, dp + 1):
+        lp = ssd.log_softmax(zp[j - 1], T).astype(np.float32)
+        lq = ssd.log_softmax(zq[j - 1], T).astype(np.float32)
+        q32 = np.exp(lq)
+        cur = np.exp(lp)                      # p' (float32 probabilities)
+        last_r = None                         # the last nonzero residual, unnormalised
+        cands = [(int(drafts[j - 1]), None)] + [(int(c), s) for s, (dj, c) in enumerate(leaves) if dj == j]
+        accepted = False
+        for i, (c, s) in enumerate(cands):
+            u = philox.uniforms(seed, it, (j - 1) + ROW_STRIDE * i, philox.PURPOSE_ACCEPT, 1)[0]
+            lpc = lp[c] if last_r is None else (np.log(cur[c]) if cur[c] > 0 else -np.inf)
+            if np.log(u) + lq[c] < lpc:
+                if s is None:
+                    accepted = True           # the chain goes on
+                    break
+                bonus = ssd.sample_logits(zl[s], T, seed, it, (j - 1) + ROW_STRIDE * i, philox.PURPOSE_SAMPLE)
+                return [int(t) for t in drafts[: j - 1]] + [c, bonus], s
+            r = np.maximum(np.float32(0), cur - q32)
+            tot = np.float32(r.sum(dtype=np.float64))
+            if tot > 0:
+                last_r = r
+                cur = (r / tot).astype(np.float32)
+        if accepted:
+            continue
+        g = philox.gumbel(seed, it, j - 1, philox.PURPOSE_SAMPLE, cur.shape[0])
+        if last_r is None:
+            keys = lp + g
+        else:
+            with np.errstate(divide="ignore"):
+                keys = np.log(last_r) + g
+        return [int(t) for t in drafts[: j - 1]] + [ssd.race_sample(keys)], None
+    return [int(t) for t in drafts] + [ssd.sample_logits(zp[dp], T, seed, it, dp, philox.PURPOSE_SAMPLE)], None
 
 
 def verify_tree(model, kv, y0, drafts, leaves, n, b, hb=None):
@@ -98,25 +171,32 @@ def accept_tree_greedy(zp, zl, drafts, leaves):
 
 
 def tree_generate(model, prompt, n_gen, mask, d, rho, k_max, budget, tau=0.0, reuse=True, capacity=None,
-                  on_iteration=None):
-    """Greedy self-speculative decoding with confidence-sized draft trees:
-    draft (ssd.draft, T = 0), leaves (R1-R3), one tree verify, tree acceptance
-    (R4).  The cache ends each iteration holding the full model's keys and
-    values of every committed token: when a leaf is accepted its path is run
-    through the full model into the cache.  Output truncated to n_gen tokens."""
+                  on_iteration=None, T=0.0, seed=3):
+    """Self-speculative decoding with confidence-sized draft trees: draft
+    (ssd.draft), leaves (R1-R3, or R5 at T > 0), one tree verify, tree
+    acceptance (R4, or R5).  The cache ends each iteration holding the full
+    model's keys and values of every committed token: when a leaf is accepted
+    its path is run through the full model into the cache.  Output truncated
+    to n_gen tokens."""
     P = len(prompt)
     b = mdl.first_skipped_layer(mask, model.L)
     kv = mdl.KVCache(model.shape, capacity or (P + n_gen + d + 2))
-    out = [argmax_lowest(ssd.prefill(model, kv, prompt))]
+    out = [ssd.pick(ssd.prefill(model, kv, prompt), T, seed, 0, 0, philox.PURPOSE_SAMPLE)]
     stats = {"drafted": [], "leaves": [], "emitted": [], "leaf_accepted": []}
     it = 1
     while len(out) < n_gen:
         n = P + len(out)
         y0 = out[-1]
-        drafts, zq, hb = ssd.draft(model, kv, y0, n, mask, d, tau, 0.0, 0, it)
-        leaves = tree_leaves(zq, drafts, rho, k_max, budget)
+        drafts, zq, hb = ssd.draft(model, kv, y0, n, mask, d, tau, T, seed, it)
+        if T == 0:
+            leaves = tree_leaves(zq, drafts, rho, k_max, budget)
+        else:
+            leaves = tree_leaves_sampled(zq, drafts, T, rho, k_max, budget, seed, it)
         zp, zl = verify_tree(model, kv, y0, drafts, leaves, n, b, hb if reuse else None)
-        emitted, s = accept_tree_greedy(zp, zl, drafts, leaves)
+        if T == 0:
+            emitted, s = accept_tree_greedy(zp, zl, drafts, leaves)
+        else:
+            emitted, s = accept_tree_sampled(zp, zq, zl, drafts, leaves, T, seed, it)
         if s is not None:
             j, c = leaves[s]
             path = [int(y0)] + [int(t) for t in drafts[: j - 1]] + [int(c)]

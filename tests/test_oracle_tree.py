@@ -169,3 +169,85 @@ def test_no_leaves_is_the_chain_loop(k_max, budget):
     assert out == ref
     assert st["emitted"] == rst["emitted"]
     assert not any(st["leaf_accepted"])
+
+
+# ---------------------------------------------------------------- R5: sampled trees
+def test_sampled_tree_without_leaves_is_the_chain_loop():
+    """k_max = 1: no leaves, and the sampled tree loop is ssd_generate's at T = 1,
+    draw for draw (same tokens, same per-iteration yields)."""
+    m = mdl.Model.synthetic(synth.TINY)
+    prompt = synth.prompt_tokens(24, synth.TINY.vocab)
+    mask = PLANS["skip2"]
+    out, st, _ = tree.tree_generate(m, prompt, 40, mask, 4, 0.9, 1, 6, tau=0.002, T=1.0, seed=77)
+    ref, rst, _ = ssd.ssd_generate(m, prompt, 40, mask, 4, tau=0.002, T=1.0, seed=77)
+    assert out == ref
+    assert st["emitted"] == rst["emitted"]
+
+
+def _first_token_counts(accept_fn, leaf_fn, n, T=1.0, V=8):
+    """First emitted token of one depth-1 tree (the draft's draw plus two more
+    candidates) over n seeds, and the target law p_1 = softmax(zp[0] / T)."""
+    from oracle import philox
+    from oracle.numerics import softmax as sm
+    rng = np.random.default_rng(0)
+    zp = rng.standard_normal((2, V)) * 1.5
+    zq = rng.standard_normal((1, V)) * 1.5
+    zl = np.zeros((4, V))
+    counts = np.zeros(V)
+    for seed in range(n):
+        y1 = ssd.sample_logits(zq[0], T, seed, 1, 0, philox.PURPOSE_DRAFT)
+        leaves = leaf_fn(zq, [y1], T, seed)
+        em, _ = accept_fn(zp, zq, zl, [y1], leaves, T, seed, 1)
+        counts[em[0]] += 1
+    return counts, sm(zp[0] / T)
+
+
+def _drawn_leaves(zq, drafts, T, seed):
+    return tree.tree_leaves_sampled(zq, drafts, T, 1.01, 3, 4, seed, 1)   # rho > 1: k = k_max = 3
+
+
+def _mutated_accept(old, new):
+    """tree.accept_tree_sampled with one planted mistake (source edit, on the CPU)."""
+    import inspect
+    src = inspect.getsource(tree.accept_tree_sampled)
+    assert old in src
+    ns = dict(tree.__dict__)
+    exec(src.replace(old, new), ns)
+    return ns["accept_tree_sampled"]
+
+
+def test_sampled_tree_first_token_follows_the_target():
+    """R5's multi-candidate rule with drawn leaves emits the target law (chi-square,
+    6000 seeds); a missing residual update between candidates, a leaf tested
+    against p instead of the residual, or top-k leaves instead of drawn ones each
+    break it (p < 1e-6)."""
+    from scipy import stats
+    n = 6000
+    c, p = _first_token_counts(tree.accept_tree_sampled, _drawn_leaves, n)
+    assert stats.chisquare(c, n * p).pvalue > 1e-4
+    no_update = _mutated_accept("cur = (r / tot).astype(np.float32)", "cur = cur")
+    c, p = _first_token_counts(no_update, _drawn_leaves, n)
+    assert stats.chisquare(c, n * p).pvalue < 1e-6
+    against_p = _mutated_accept("lpc = lp[c] if last_r is None else", "lpc = lp[c] if True else")
+    c, p = _first_token_counts(against_p, _drawn_leaves, n)
+    assert stats.chisquare(c, n * p).pvalue < 1e-6
+    topk = lambda zq, drafts, T, seed: [(1, t) for t in tree.topk_lowest(zq[0], 3)[:2]]
+    c, p = _first_token_counts(tree.accept_tree_sampled, topk, n)
+    assert stats.chisquare(c, n * p).pvalue < 1e-6
+
+
+def test_sampled_tree_leaves_are_draws_of_q():
+    """The extra candidates of a step are independent draws of softmax(z / T)
+    (chi-square over seeds), k_j - 1 of them, depth order."""
+    from scipy import stats
+    from oracle.numerics import softmax as sm
+    rng = np.random.default_rng(4)
+    V, T = 6, 0.7
+    zq = rng.standard_normal((2, V))
+    counts = np.zeros(V)
+    n = 4000
+    for seed in range(n):
+        lv = tree.tree_leaves_sampled(zq, [0, 1], T, 1.01, 3, 10, seed, 5)
+        assert [j for j, _ in lv] == [1, 1, 2, 2]
+        counts[lv[2][1]] += 1
+    assert stats.chisquare(counts, n * sm(zq[1] / T)).pvalue > 1e-4
