@@ -240,7 +240,7 @@ def main():
         if tr is not None:
             # dynamic verification: leaves from the draft's confidence, one tree verify, tree acceptance
             B.ssd_tree_candidates(h, seq.draft_logits, seq.n_drafted, d, tr["rho"], tr["k_max"], tr["max_leaves"],
-                                  seq.leaf_tokens, seq.leaf_depth, seq.n_leaves)
+                                  seq.leaf_tokens, seq.leaf_depth, seq.n_leaves, wl["T"], seed)
             if vev is not None:
                 vev[0].record()
             B.ssd_verify_tree(h, skip_mask, exit_layer, d, seq.draft_tokens, seq.n_drafted, seq.leaf_tokens,
@@ -248,7 +248,8 @@ def main():
             if vev is not None:
                 vev[1].record()
             B.ssd_accept_tree(h, seq.tree_logits, seq.draft_tokens, seq.n_drafted, d, seq.leaf_tokens,
-                              seq.leaf_depth, seq.n_leaves, tr["max_leaves"], seq.out_tokens, seq.n_out)
+                              seq.leaf_depth, seq.n_leaves, tr["max_leaves"], seq.out_tokens, seq.n_out,
+                              seq.draft_logits, wl["T"], seed)
             B.ssd_commit(h, seq.out_tokens, seq.n_out)
             return
         if vev is not None:

@@ -254,16 +254,25 @@ int ssd_commit(ssd_seq* seq, const int32_t* out_tokens_dev, const int32_t* n_out
  * whose top-k mass reaches rho, at most k_max; only the top one (the greedy
  * draft token y_j) is drafted further, the others are leaves of depth j that sit
  * at y_j's position and attend to the prefix, y_0..y_{j-1} and themselves.
- * Greedy decoding only (temperature 0). */
+ * At temperature T > 0 the top-k tokens are not draws of q, so the leaves of step
+ * j are k_j - 1 further independent draws of softmax(z_j / T) (k_j from the same
+ * rule at T), and acceptance is the multi-candidate form of the speculative
+ * sampling rule (SpecInfer, Miao et al.), which keeps the target distribution
+ * for drawn candidates. */
 
-/* Leaves of the last greedy draft (draft_logits_dev / n_drafted_dev as written
- * by ssd_draft, or any [d, V] float rows): ranks 1..k_j-1 of each step j <= d',
- * in depth order then rank order, at most max_leaves (<= 15).  k_max in 1..8.
+/* Leaves of the last draft (draft_logits_dev / n_drafted_dev as written by
+ * ssd_draft with the same temperature, or any [d, V] float rows).  Temperature 0:
+ * ranks 1..k_j-1 of each step j <= d'.  T > 0: k_j - 1 draws of softmax(row / T)
+ * (race keys z / T + Gumbel; Philox counter (iteration, (j - 1) + 256 r,
+ * purpose 4 "leaf", v / 4) for the r-th extra draw, the iteration read from the
+ * sequence's device state).  Depth order, then rank (draw) order, at most
+ * max_leaves (<= 15).  k_max in 1..8, d <= 256.
  * Outputs: leaf_tokens_dev[max_leaves], leaf_depth_dev[max_leaves] (1..d'),
  * n_leaves_dev[1]. */
 int ssd_tree_candidates(ssd_seq* seq, const float* draft_logits_dev, const int32_t* n_drafted_dev, int d,
-                        float rho, int k_max, int max_leaves, int32_t* leaf_tokens_dev, int32_t* leaf_depth_dev,
-                        int32_t* n_leaves_dev, hipStream_t stream);
+                        float temperature, uint64_t seed, float rho, int k_max, int max_leaves,
+                        int32_t* leaf_tokens_dev, int32_t* leaf_depth_dev, int32_t* n_leaves_dev,
+                        hipStream_t stream);
 
 /* Tree verify: ssd_verify's chain rows 0..d' plus one row per leaf s (token
  * leaf_tokens_dev[s] at position kvlen + leaf_depth_dev[s], seeing the cache up
@@ -281,17 +290,28 @@ int ssd_verify_tree(ssd_seq* seq, const uint8_t* skip_mask_host, int exit_layer,
                     const int32_t* leaf_depth_dev, const int32_t* n_leaves_dev, int max_leaves, int reuse,
                     float* logits_dev, hipStream_t stream);
 
-/* Greedy tree acceptance over ssd_verify_tree's rows: for j = 1..d', y_j is
- * accepted while it is the argmax of chain row j-1; at the first mismatch, if
- * the argmax is a leaf of depth j, that leaf and the argmax of its own row are
- * emitted, else the argmax alone; after d' accepted drafts the argmax of row d'
- * is the bonus.  When a leaf is emitted its keys and values (every layer) are
- * written into the cache at its position, so ssd_commit's metadata update is
- * all that remains.  Outputs: out_tokens_dev[d + 1] (first n_out valid),
- * n_out_dev[1]. */
-int ssd_accept_tree(ssd_seq* seq, const float* logits_dev, const int32_t* draft_tokens_dev,
-                    const int32_t* n_drafted_dev, int d, const int32_t* leaf_tokens_dev, const int32_t* leaf_depth_dev,
-                    const int32_t* n_leaves_dev, int max_leaves, int32_t* out_tokens_dev, int32_t* n_out_dev,
+/* Tree acceptance over ssd_verify_tree's rows (logits_dev; q_logits_dev: the
+ * draft's logits, needed at T > 0).
+ * Temperature 0: for j = 1..d', y_j is accepted while it is the argmax of chain
+ * row j-1; at the first mismatch, if the argmax is a leaf of depth j, that leaf
+ * and the argmax of its own row are emitted, else the argmax alone; after d'
+ * accepted drafts the argmax of row d' is the bonus.
+ * T > 0: the chain rule of ssd_accept per depth; at the first rejected depth j
+ * that has leaves, the leaves are tried in order: with p' the target after the
+ * rejections so far (p' <- norm(max(0, p' - q_j)) after each, kept when that is
+ * all zero), leaf c (the k-th candidate of the depth, the draft token being the
+ * 0-th) is accepted when u q_j(c) < p'(c) (u: counter (iteration, (j - 1) + 256 k,
+ * "accept")), and then emitted with a draw from its own row (counter
+ * (iteration, (j - 1) + 256 k, "sample")); when all are rejected, a draw from the
+ * last nonzero max(0, p' - q_j) (or p_j) with the chain rule's counter.  Without
+ * leaves this is ssd_accept's rule draw for draw.
+ * When a leaf is emitted its keys and values (every layer) are written into the
+ * cache at its position, so ssd_commit's metadata update is all that remains.
+ * Outputs: out_tokens_dev[d + 1] (first n_out valid), n_out_dev[1]. */
+int ssd_accept_tree(ssd_seq* seq, const float* logits_dev, const float* q_logits_dev,
+                    const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, int d,
+                    const int32_t* leaf_tokens_dev, const int32_t* leaf_depth_dev, const int32_t* n_leaves_dev,
+                    int max_leaves, float temperature, uint64_t seed, int32_t* out_tokens_dev, int32_t* n_out_dev,
                     hipStream_t stream);
 
 /* SWIFT matchness scoring (row a6; [SWIFT] §4.1, §4.1.2, §5.3, §D.2).

@@ -84,9 +84,9 @@ def lib():
             "ssd_verify": [P, P, I, I, P, P, I, P, P],
             "ssd_accept": [P, P, P, P, P, I, F, U64, P, P, P],
             "ssd_commit": [P, P, P, P],
-            "ssd_tree_candidates": [P, P, P, I, F, I, I, P, P, P, P],
+            "ssd_tree_candidates": [P, P, P, I, F, U64, F, I, I, P, P, P, P],
             "ssd_verify_tree": [P, P, I, I, P, P, P, P, P, I, I, P, P],
-            "ssd_accept_tree": [P, P, P, P, I, P, P, P, I, P, P, P],
+            "ssd_accept_tree": [P, P, P, P, P, I, P, P, P, I, F, U64, P, P, P],
             "ssd_score_masks": [P, P, I, P, I, I, P, P, P],
             "ssd_uniform_mask": [I, I, P],
             "ssd_specee_features": [P, P, I, P, I, P, P, P],
@@ -222,9 +222,10 @@ def ssd_commit(seq, out_tokens, n_out, stream=None):
 
 
 def ssd_tree_candidates(seq, draft_logits, n_drafted, d, rho, k_max, max_leaves, leaf_tokens, leaf_depth, n_leaves,
-                        stream=None):
-    check(lib().ssd_tree_candidates(seq, _ptr(draft_logits), _ptr(n_drafted), d, rho, k_max, max_leaves,
-                                    _ptr(leaf_tokens), _ptr(leaf_depth), _ptr(n_leaves), _stream(stream)))
+                        temperature=0.0, seed=0, stream=None):
+    check(lib().ssd_tree_candidates(seq, _ptr(draft_logits), _ptr(n_drafted), d, temperature, seed, rho, k_max,
+                                    max_leaves, _ptr(leaf_tokens), _ptr(leaf_depth), _ptr(n_leaves),
+                                    _stream(stream)))
 
 
 def ssd_verify_tree(seq, skip_mask, exit_layer, d, draft_tokens, n_drafted, leaf_tokens, leaf_depth, n_leaves,
@@ -236,10 +237,10 @@ def ssd_verify_tree(seq, skip_mask, exit_layer, d, draft_tokens, n_drafted, leaf
 
 
 def ssd_accept_tree(seq, logits, draft_tokens, n_drafted, d, leaf_tokens, leaf_depth, n_leaves, max_leaves,
-                    out_tokens, n_out, stream=None):
-    check(lib().ssd_accept_tree(seq, _ptr(logits), _ptr(draft_tokens), _ptr(n_drafted), d, _ptr(leaf_tokens),
-                                _ptr(leaf_depth), _ptr(n_leaves), max_leaves, _ptr(out_tokens), _ptr(n_out),
-                                _stream(stream)))
+                    out_tokens, n_out, q_logits=None, temperature=0.0, seed=0, stream=None):
+    check(lib().ssd_accept_tree(seq, _ptr(logits), _ptr(q_logits), _ptr(draft_tokens), _ptr(n_drafted), d,
+                                _ptr(leaf_tokens), _ptr(leaf_depth), _ptr(n_leaves), max_leaves, temperature, seed,
+                                _ptr(out_tokens), _ptr(n_out), _stream(stream)))
 
 
 def ssd_score_masks(seq, masks, window, pos0, gamma, scores, best, stream=None):
@@ -407,27 +408,30 @@ class Sequence:
                    temperature, seed, self.out_tokens, self.n_out, s)
         ssd_commit(self.handle, self.out_tokens, self.n_out, s)
 
-    def tree_iteration(self, skip_mask, exit_layer, d, rho, k_max, max_leaves, conf_thresh=0.0, reuse=True):
-        """Enqueues a greedy draft -> leaves -> tree verify -> tree accept -> commit."""
+    def tree_iteration(self, skip_mask, exit_layer, d, rho, k_max, max_leaves, conf_thresh=0.0, reuse=True,
+                       temperature=0.0, seed=0):
+        """Enqueues draft -> leaves -> tree verify -> tree accept -> commit."""
         s = self.stream
-        ssd_draft(self.handle, skip_mask, exit_layer, d, conf_thresh, 0.0, 0, self.draft_tokens, self.draft_logits,
-                  self.n_drafted, s)
+        ssd_draft(self.handle, skip_mask, exit_layer, d, conf_thresh, temperature, seed, self.draft_tokens,
+                  self.draft_logits, self.n_drafted, s)
         ssd_tree_candidates(self.handle, self.draft_logits, self.n_drafted, d, rho, k_max, max_leaves,
-                            self.leaf_tokens, self.leaf_depth, self.n_leaves, s)
+                            self.leaf_tokens, self.leaf_depth, self.n_leaves, temperature, seed, s)
         ssd_verify_tree(self.handle, skip_mask, exit_layer, d, self.draft_tokens, self.n_drafted, self.leaf_tokens,
                         self.leaf_depth, self.n_leaves, max_leaves, reuse, self.tree_logits, s)
         ssd_accept_tree(self.handle, self.tree_logits, self.draft_tokens, self.n_drafted, d, self.leaf_tokens,
-                        self.leaf_depth, self.n_leaves, max_leaves, self.out_tokens, self.n_out, s)
+                        self.leaf_depth, self.n_leaves, max_leaves, self.out_tokens, self.n_out, self.draft_logits,
+                        temperature, seed, s)
         ssd_commit(self.handle, self.out_tokens, self.n_out, s)
 
     def generate_tree(self, prompt, n_gen, skip_mask=None, exit_layer=None, d=4, rho=0.9, k_max=4, max_leaves=3,
-                      conf_thresh=0.0, reuse=True):
-        """Greedy decoding with draft trees; returns (tokens[:n_gen], per-iteration (d', emitted) list)."""
-        ssd_prefill(self.handle, prompt, 0.0, 0, None, self.stream)
+                      conf_thresh=0.0, reuse=True, temperature=0.0, seed=0):
+        """Decoding with draft trees; returns (tokens[:n_gen], per-iteration (d', emitted) list)."""
+        ssd_prefill(self.handle, prompt, temperature, seed, None, self.stream)
         stats = []
         st = ssd_read_state(self.handle, self.stream)
         while st.n_out < n_gen:
-            self.tree_iteration(skip_mask, exit_layer, d, rho, k_max, max_leaves, conf_thresh, reuse)
+            self.tree_iteration(skip_mask, exit_layer, d, rho, k_max, max_leaves, conf_thresh, reuse, temperature,
+                                seed)
             st = ssd_read_state(self.handle, self.stream)
             stats.append((st.last_n_drafted, st.last_n_emitted))
         return ssd_read_output(self.handle, n_gen, self.stream)[:n_gen], stats

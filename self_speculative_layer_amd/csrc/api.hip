@@ -670,17 +670,20 @@ extern "C" int ssd_commit(ssd_seq* q, const int32_t* out_tokens_dev, const int32
 // draft trees (dynamic verification)
 
 extern "C" int ssd_tree_candidates(ssd_seq* q, const float* draft_logits_dev, const int32_t* n_drafted_dev, int d_max,
-                                   float rho, int k_max, int max_leaves, int32_t* leaf_tokens_dev,
-                                   int32_t* leaf_depth_dev, int32_t* n_leaves_dev, hipStream_t s) {
+                                   float temperature, uint64_t seed, float rho, int k_max, int max_leaves,
+                                   int32_t* leaf_tokens_dev, int32_t* leaf_depth_dev, int32_t* n_leaves_dev,
+                                   hipStream_t s) {
   CHECK_ARG(q && draft_logits_dev && n_drafted_dev && leaf_tokens_dev && leaf_depth_dev && n_leaves_dev,
             "null argument");
   CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
   CHECK_ARG(k_max >= 1 && k_max <= TREE_KMAX && k_max <= q->m->d.vocab, "k_max out of range");
   CHECK_ARG(max_leaves >= 0 && max_leaves <= TREE_SLOTS, "max_leaves out of range");
   CHECK_ARG(std::isfinite(rho), "bad rho");
+  CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
   const Workspace& w = q->w;
-  TRY(launch_tree_candidates(draft_logits_dev, q->m->d.vocab, d_max, n_drafted_dev, rho, k_max, max_leaves,
-                             w.tree_cand, w.tree_k, leaf_tokens_dev, leaf_depth_dev, n_leaves_dev, s));
+  TRY(launch_tree_candidates(draft_logits_dev, q->m->d.vocab, d_max, n_drafted_dev, temperature, seed, w.st, rho,
+                             k_max, max_leaves, w.tree_cand, w.tree_k, leaf_tokens_dev, leaf_depth_dev, n_leaves_dev,
+                             s));
   return SSD_OK;
 }
 
@@ -729,23 +732,32 @@ extern "C" int ssd_verify_tree(ssd_seq* q, const uint8_t* skip_mask_host, int ex
   return SSD_OK;
 }
 
-extern "C" int ssd_accept_tree(ssd_seq* q, const float* logits_dev, const int32_t* draft_tokens_dev,
-                               const int32_t* n_drafted_dev, int d_max, const int32_t* leaf_tokens_dev,
-                               const int32_t* leaf_depth_dev, const int32_t* n_leaves_dev, int max_leaves,
+extern "C" int ssd_accept_tree(ssd_seq* q, const float* logits_dev, const float* q_logits_dev,
+                               const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, int d_max,
+                               const int32_t* leaf_tokens_dev, const int32_t* leaf_depth_dev,
+                               const int32_t* n_leaves_dev, int max_leaves, float temperature, uint64_t seed,
                                int32_t* out_tokens_dev, int32_t* n_out_dev, hipStream_t s) {
   CHECK_ARG(q && logits_dev && draft_tokens_dev && n_drafted_dev && leaf_tokens_dev && leaf_depth_dev &&
                 n_leaves_dev && out_tokens_dev && n_out_dev,
             "null argument");
+  CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
+  CHECK_ARG(temperature == 0.f || q_logits_dev, "sampled acceptance needs the draft's logits");
   CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
   CHECK_ARG(max_leaves >= 0 && d_max + 1 + max_leaves <= std::min(16, q->max_rows), "too many tree rows");
   const ssd_model_desc& d = q->m->d;
   const Workspace& w = q->w;
   const int M = d_max + 1 + max_leaves;
-  TRY(launch_row_stats_seg(logits_dev, d.vocab, M, d.vocab, 0.f, 0, nullptr, 0, 0, PURPOSE_SAMPLE, w.stats,
-                           w.stat_recs, w.stat_ctr, nullptr, DraftStep{}, s));
-  TRY(launch_tree_accept(w.stats, draft_tokens_dev, n_drafted_dev, d_max, leaf_tokens_dev, leaf_depth_dev,
-                         n_leaves_dev, max_leaves, w.st, out_tokens_dev, n_out_dev, w.tree_kv, q->kv, d.n_layers,
-                         d.n_kv_heads, d.head_dim, s));
+  if (temperature > 0.f) {
+    TRY(launch_tree_accept_sampled(logits_dev, q_logits_dev, d.vocab, draft_tokens_dev, n_drafted_dev, d_max,
+                                   leaf_tokens_dev, leaf_depth_dev, n_leaves_dev, max_leaves, temperature, seed,
+                                   w.st, w.dec, w.corr, out_tokens_dev, n_out_dev, s));
+  } else {
+    TRY(launch_row_stats_seg(logits_dev, d.vocab, M, d.vocab, 0.f, 0, nullptr, 0, 0, PURPOSE_SAMPLE, w.stats,
+                             w.stat_recs, w.stat_ctr, nullptr, DraftStep{}, s));
+    TRY(launch_tree_accept(w.stats, draft_tokens_dev, n_drafted_dev, d_max, leaf_tokens_dev, leaf_depth_dev,
+                           n_leaves_dev, max_leaves, w.st, out_tokens_dev, n_out_dev, s));
+  }
+  TRY(launch_tree_kv_fix(w.st, w.tree_kv, q->kv, d.n_layers, d.n_kv_heads, d.head_dim, s));
   return SSD_OK;
 }
 

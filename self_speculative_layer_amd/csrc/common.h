@@ -94,6 +94,8 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 constexpr uint32_t PURPOSE_DRAFT = 0;
 constexpr uint32_t PURPOSE_ACCEPT = 1;
 constexpr uint32_t PURPOSE_SAMPLE = 2;
+constexpr uint32_t PURPOSE_LEAF = 4;           // draft trees: the extra candidates of a draft step
+constexpr int TREE_ROW_STRIDE = 256;           //   candidate r of draft row i: counter row i + 256 r
 
 struct U4 { uint32_t x, y, z, w; };
 

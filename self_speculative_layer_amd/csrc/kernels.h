@@ -130,20 +130,27 @@ int launch_score(const ssd_row_stat* stats, const int32_t* window, int n_masks, 
 // Per draft row j < d' (rows of draft_logits): the k_max best tokens into cand[j][TREE_KMAX] and the
 // candidate count into kcount[j]; then the leaves (ranks 1 .. k_j - 1, depth order) into leaf_tok /
 // leaf_depth, their number into n_leaves.
-int launch_tree_candidates(const float* draft_logits, int V, int d, const int32_t* n_drafted, float rho, int k_max,
-                           int max_leaves, int* cand, int* kcount, int32_t* leaf_tok, int32_t* leaf_depth,
-                           int32_t* n_leaves, hipStream_t s);
+int launch_tree_candidates(const float* draft_logits, int V, int d, const int32_t* n_drafted, float T, uint64_t seed,
+                           const DevState* st, float rho, int k_max, int max_leaves, int* cand, int* kcount,
+                           int32_t* leaf_tok, int32_t* leaf_depth, int32_t* n_leaves, hipStream_t s);
 // Row positions / tokens of a tree verify's full block (vpos, vtok [d + 1 + max_leaves]) and prefix block
 // (ppos, ptok [1 + max_leaves]); the row counts and first leaf rows in the device state.
 int launch_tree_verify_prep(DevState* st, const int32_t* drafts, const int32_t* n_drafted, int d,
                             const int32_t* leaf_tok, const int32_t* leaf_depth, const int32_t* n_leaves,
                             int max_leaves, int* vpos, int* vtok, int* ppos, int* ptok, int max_ctx, hipStream_t s);
-// Greedy tree acceptance from the verify rows' statistics, then the accepted leaf's keys and values
-// (side_kv [L][TREE_SLOTS][2][KVH * HD]) into the cache at its position.
+// Greedy tree acceptance from the verify rows' statistics.
 int launch_tree_accept(const ssd_row_stat* stats, const int32_t* drafts, const int32_t* n_drafted, int d,
                        const int32_t* leaf_tok, const int32_t* leaf_depth, const int32_t* n_leaves, int max_leaves,
-                       DevState* st, int32_t* out, int32_t* n_out, const bf16_t* side_kv, const KvView& kv, int L,
-                       int KVH, int HD, hipStream_t s);
+                       DevState* st, int32_t* out, int32_t* n_out, hipStream_t s);
+// Sampled (T > 0) tree acceptance (kernels.hip): the chain rule per row, then the multi-candidate rule at
+// the first rejected depth when it has leaves.
+int launch_tree_accept_sampled(const float* zp, const float* zq, int V, const int32_t* drafts,
+                               const int32_t* n_drafted, int d, const int32_t* leaf_tok, const int32_t* leaf_depth,
+                               const int32_t* n_leaves, int max_leaves, float T, uint64_t seed, DevState* st,
+                               int* dec, int* corr, int32_t* out, int32_t* n_out, hipStream_t s);
+// The accepted leaf's keys and values (side_kv [L][TREE_SLOTS][2][KVH * HD]) into the cache at its position.
+int launch_tree_kv_fix(const DevState* st, const bf16_t* side_kv, const KvView& kv, int L, int KVH, int HD,
+                       hipStream_t s);
 // Whether the decode attention can merge a leaf's own term at this context length.
 bool attention_dec_leaves_fit(int max_ctx);
 

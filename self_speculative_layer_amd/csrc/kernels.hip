@@ -1351,6 +1351,148 @@ __global__ void accept_emit_kernel(const int32_t* __restrict__ drafts, const int
   *n_out = k + 1;
 }
 
+// Sampled tree acceptance (T > 0), after accept_rows_kernel on the chain rows (dec[i]: the chain's
+// candidate of depth i + 1 accepted, corr[i]: the chain rule's draw at row i).  At the first rejected
+// depth, if it has leaves, its candidates are taken in order (the chain's token, then the leaves in
+// leaf order): with p' = p_j, candidate c_k (k >= 1) is accepted when u_k q(c_k) < p'(c_k) (u_k:
+// counter (iteration, i + 256 k, accept)); after each rejection p' becomes norm(max(0, p' - q)) (kept
+// when that is all zero).  A leaf accepted: it and a draw from its own row (counter (iteration, i + 256 k,
+// sample)) are emitted.  All rejected: a draw from the last nonzero residual, unnormalised, or from p
+// when there was none (counter (iteration, i, sample)).  Tree rows: chain rows 0..d', leaf s at d' + 1 + s.
+__global__ __launch_bounds__(1024) void tree_accept_sampled_kernel(
+    const float* __restrict__ zp, const float* __restrict__ zq, int V, const int32_t* __restrict__ drafts,
+    const int32_t* __restrict__ n_drafted, int d, const int32_t* __restrict__ leaf_tok,
+    const int32_t* __restrict__ leaf_depth, const int32_t* __restrict__ n_leaves, int max_leaves, float T,
+    uint64_t seed, DevState* st, const int* __restrict__ dec, const int* __restrict__ corr, int32_t* __restrict__ out,
+    int32_t* __restrict__ n_out) {
+  __shared__ int s_i, s_nd, s_acc;
+  __shared__ float tots[TREE_KMAX + TREE_SLOTS + 1];
+  const int tid = threadIdx.x;
+  const int dp = max(min(*n_drafted, d), 0);
+  const int nl = max(min(*n_leaves, max_leaves), 0);
+  if (tid == 0) {
+    st->tree_leaf = -1;
+    int i = 0;
+    while (i < dp && dec[i]) { out[i] = drafts[i]; ++i; }
+    int nd = 0;
+    if (i < dp)
+      for (int s = 0; s < nl; ++s) nd += leaf_depth[s] == i + 1;
+    s_i = i;
+    s_nd = nd;
+    if (i == dp || nd == 0) { out[i] = corr[i]; *n_out = i + 1; }
+  }
+  __syncthreads();
+  const int i = s_i;
+  if (i == dp || s_nd == 0) return;
+  const float* p = zp + (size_t)i * V;
+  const float* q = zq + (size_t)i * V;
+  const float lse_p = block_lse(p, V, T);
+  const float lse_q = block_lse(q, V, T);
+  const int iter = st->iteration;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  int nu = 0;                                     // residual updates with a nonzero sum so far
+  // p'(v) after the first u updates
+  auto cur = [&](float pv, float qv, int u) {
+    float x = expf(pv / T - lse_p);
+    const float qq = expf(qv / T - lse_q);
+    for (int t = 0; t < u; ++t) x = fmaxf(0.f, x - qq) / tots[t];
+    return x;
+  };
+  auto update = [&]() {                           // after a rejection: the sum of max(0, p' - q)
+    float acc = 0.f;
+    for_quads<1024>(p, q, V, [&](int v4, const float* pq, const float* qq4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (v4 + e < V) acc += fmaxf(0.f, cur(pq[e], qq4[e], nu) - expf(qq4[e] / T - lse_q));
+    });
+    const float tot = block_sum_1024(acc);
+    if (tot > 0.f) {
+      if (tid == 0) tots[nu] = tot;
+      __syncthreads();
+      ++nu;
+    }
+  };
+  update();                                       // the chain's candidate was rejected
+  int k = 0;
+  for (int s = 0; s < nl; ++s) {
+    if (leaf_depth[s] != i + 1) continue;
+    ++k;
+    const int c = min(max(leaf_tok[s], 0), V - 1);
+    if (tid == 0) {
+      const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)(i + TREE_ROW_STRIDE * k), PURPOSE_ACCEPT, 0u, k0, k1);
+      const float u = word_to_uniform(w.x);
+      const float lqc = q[c] / T - lse_q;
+      float lpc = p[c] / T - lse_p;
+      if (nu > 0) {
+        const float x = cur(p[c], q[c], nu);
+        lpc = x > 0.f ? logf(x) : -INFINITY;
+      }
+      s_acc = (logf(u) + lqc) < lpc;
+    }
+    __syncthreads();
+    if (s_acc) {
+      // the leaf and a draw from its own row
+      const float* zl = zp + (size_t)(dp + 1 + s) * V;
+      float kb = -INFINITY;
+      int ib = 0x7fffffff;
+      const uint32_t row = (uint32_t)(i + TREE_ROW_STRIDE * k);
+      for_quads<1024>(zl, zl, V, [&](int v4, const float* a, const float*) {
+        const U4 w = philox4x32_10((uint32_t)iter, row, PURPOSE_SAMPLE, (uint32_t)(v4 >> 2), k0, k1);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (v4 + e < V) argmax_merge(kb, ib, a[e] / T + word_to_gumbel(ws[e]), v4 + e);
+      });
+      const int b = block_argmax_1024(kb, ib);
+      if (tid == 0) {
+        out[i] = c;
+        out[i + 1] = b;
+        *n_out = i + 2;
+        st->tree_leaf = s;
+        st->tree_leaf_pos = st->kvlen + i + 1;
+      }
+      return;
+    }
+    update();
+  }
+  // every candidate rejected: a draw from the last nonzero residual (or from p)
+  float kb = -INFINITY;
+  int ib = 0x7fffffff;
+  for_quads<1024>(p, q, V, [&](int v4, const float* pq, const float* qq4) {
+    const U4 w = philox4x32_10((uint32_t)iter, (uint32_t)i, PURPOSE_SAMPLE, (uint32_t)(v4 >> 2), k0, k1);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (v4 + e >= V) continue;
+      float key;
+      if (nu == 0) {
+        key = (pq[e] / T - lse_p) + word_to_gumbel(ws[e]);
+      } else {
+        const float r = fmaxf(0.f, cur(pq[e], qq4[e], nu - 1) - expf(qq4[e] / T - lse_q));
+        if (!(r > 0.f)) continue;
+        key = logf(r) + word_to_gumbel(ws[e]);
+      }
+      argmax_merge(kb, ib, key, v4 + e);
+    }
+  });
+  const int b = block_argmax_1024(kb, ib);
+  if (tid == 0) {
+    out[i] = b;
+    *n_out = i + 1;
+  }
+}
+
+int launch_tree_accept_sampled(const float* zp, const float* zq, int V, const int32_t* drafts,
+                               const int32_t* n_drafted, int d, const int32_t* leaf_tok, const int32_t* leaf_depth,
+                               const int32_t* n_leaves, int max_leaves, float T, uint64_t seed, DevState* st,
+                               int* dec, int* corr, int32_t* out, int32_t* n_out, hipStream_t s) {
+  hipLaunchKernelGGL(accept_rows_kernel, dim3(d + 1), dim3(1024), 0, s, zp, zq, V, drafts, n_drafted, T, seed, st,
+                     dec, corr);
+  hipLaunchKernelGGL(tree_accept_sampled_kernel, dim3(1), dim3(1024), 0, s, zp, zq, V, drafts, n_drafted, d, leaf_tok,
+                     leaf_depth, n_leaves, max_leaves, T, seed, st, dec, corr, out, n_out);
+  return last_launch();
+}
+
 int launch_accept(const float* zp, const float* zq, int V, const int32_t* drafts, const int32_t* n_drafted, int d,
                   float T, uint64_t seed, const DevState* st, int* dec, int* corr, int32_t* out_tokens,
                   int32_t* n_out, hipStream_t s) {

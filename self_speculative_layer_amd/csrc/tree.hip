@@ -29,10 +29,13 @@ __device__ __forceinline__ bool tree_before(float v, int i, float tv, int ti) {
 }
 
 // One block per draft row j < d': the row's k_max best tokens, their
-// softmax probabilities and the candidate count k_j.  cand[j][TREE_KMAX],
-// kcount[j].
+// softmax(z / T) probabilities (T = 1 when T is 0) and the candidate count
+// k_j.  cand[j][TREE_KMAX]: at T = 0 the ranks 0..k_max-1; at T > 0 entry r >= 1
+// is the r-th extra draw of softmax(z / T) (race keys z / T + Gumbel, counter
+// (iteration, j + 256 r, purpose leaf)); kcount[j].
 __global__ __launch_bounds__(256) void tree_topk_kernel(const float* __restrict__ z, int V, int d,
                                                         const int32_t* __restrict__ n_drafted, float rho, int k_max,
+                                                        float T, uint64_t seed, const DevState* __restrict__ st,
                                                         int* __restrict__ cand, int* __restrict__ kcount) {
   constexpr int K = TREE_KMAX;
   const int j = blockIdx.x;
@@ -86,23 +89,54 @@ __global__ __launch_bounds__(256) void tree_topk_kernel(const float* __restrict_
     }
     if (pop) { tv[K - 1] = -INFINITY; ti[K - 1] = 0x7fffffff; }
   }
-  // softmax normaliser: sum of exp(z - max), each thread's terms in index order, then wave and block
+  // softmax normaliser: sum of exp((z - max) / T), each thread's terms in index order, then wave and block
   const float m = topv[0];
+  const float Tn = T > 0.f ? T : 1.f;
   float se = 0.f;
-  for (int v = tid; v < V; v += 256) se += expf(__fsub_rn(zr[v], m));
+  for (int v = tid; v < V; v += 256) se += expf(__fdiv_rn(__fsub_rn(zr[v], m), Tn));
   se = wave_sum(se);
   if (lane == 0) wsum[wave] = se;
   __syncthreads();
+  __shared__ int s_k;
   if (tid == 0) {
     const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
     float cum = 0.f;
     int k = k_max;
     for (int r = 0; r < k_max; ++r) {
-      cum += __fdiv_rn(expf(__fsub_rn(topv[r], m)), tot);
+      cum += __fdiv_rn(expf(__fdiv_rn(__fsub_rn(topv[r], m), Tn)), tot);
       if (cum >= rho) { k = r + 1; break; }
     }
     for (int r = 0; r < K; ++r) cand[(size_t)j * K + r] = r < k_max ? topi[r] : -1;
     kcount[j] = k;
+    s_k = k;
+  }
+  if (!(T > 0.f)) return;
+  __syncthreads();
+  // T > 0: the extra candidates are draws of softmax(z / T), one race per draw
+  const int k = s_k;
+  const int iter = st->iteration;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  for (int r = 1; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    const uint32_t row = (uint32_t)(j + TREE_ROW_STRIDE * r);
+    for (int v4 = 4 * tid; v4 < V; v4 += 4 * 256) {
+      const U4 w = philox4x32_10((uint32_t)iter, row, PURPOSE_LEAF, (uint32_t)(v4 >> 2), k0, k1);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (v4 + e < V) argmax_merge(bv, bi, zr[v4 + e] / T + word_to_gumbel(ws[e]), v4 + e);
+    }
+    wave_argmax(bv, bi);
+    if (lane == 0) { wv[wave] = bv; wi[wave] = bi; }
+    __syncthreads();
+    if (tid == 0) {
+      float v = wv[0];
+      int i = wi[0];
+      for (int w = 1; w < 4; ++w) argmax_merge(v, i, wv[w], wi[w]);
+      cand[(size_t)j * K + r] = i;
+    }
+    __syncthreads();
   }
 }
 
@@ -122,12 +156,12 @@ __global__ void tree_plan_kernel(const int* __restrict__ cand, const int* __rest
   *n_leaves = nl;
 }
 
-int launch_tree_candidates(const float* draft_logits, int V, int d, const int32_t* n_drafted, float rho, int k_max,
-                           int max_leaves, int* cand, int* kcount, int32_t* leaf_tok, int32_t* leaf_depth,
-                           int32_t* n_leaves, hipStream_t s) {
-  if (k_max < 1 || k_max > TREE_KMAX || k_max > V || d < 1) return SSD_ERR_ARG;
-  hipLaunchKernelGGL(tree_topk_kernel, dim3(d), dim3(256), 0, s, draft_logits, V, d, n_drafted, rho, k_max, cand,
-                     kcount);
+int launch_tree_candidates(const float* draft_logits, int V, int d, const int32_t* n_drafted, float T, uint64_t seed,
+                           const DevState* st, float rho, int k_max, int max_leaves, int* cand, int* kcount,
+                           int32_t* leaf_tok, int32_t* leaf_depth, int32_t* n_leaves, hipStream_t s) {
+  if (k_max < 1 || k_max > TREE_KMAX || k_max > V || d < 1 || d > TREE_ROW_STRIDE) return SSD_ERR_ARG;
+  hipLaunchKernelGGL(tree_topk_kernel, dim3(d), dim3(256), 0, s, draft_logits, V, d, n_drafted, rho, k_max, T, seed,
+                     st, cand, kcount);
   hipLaunchKernelGGL(tree_plan_kernel, dim3(1), dim3(64), 0, s, cand, kcount, d, n_drafted, max_leaves, leaf_tok,
                      leaf_depth, n_leaves);
   return tree_ok(hipGetLastError());
@@ -226,10 +260,14 @@ __global__ void tree_kv_fix_kernel(const DevState* __restrict__ st, const bf16_t
 
 int launch_tree_accept(const ssd_row_stat* stats, const int32_t* drafts, const int32_t* n_drafted, int d,
                        const int32_t* leaf_tok, const int32_t* leaf_depth, const int32_t* n_leaves, int max_leaves,
-                       DevState* st, int32_t* out, int32_t* n_out, const bf16_t* side_kv, const KvView& kv, int L,
-                       int KVH, int HD, hipStream_t s) {
+                       DevState* st, int32_t* out, int32_t* n_out, hipStream_t s) {
   hipLaunchKernelGGL(tree_accept_kernel, dim3(1), dim3(64), 0, s, stats, drafts, n_drafted, d, leaf_tok, leaf_depth,
                      n_leaves, max_leaves, st, out, n_out);
+  return tree_ok(hipGetLastError());
+}
+
+int launch_tree_kv_fix(const DevState* st, const bf16_t* side_kv, const KvView& kv, int L, int KVH, int HD,
+                       hipStream_t s) {
   hipLaunchKernelGGL(tree_kv_fix_kernel, dim3(L, 2 * KVH), dim3(64), 0, s, st, side_kv, (bf16_t*)kv.pool,
                      kv.page_table, kv.page_size, kv.n_lpages, L, KVH, HD);
   return tree_ok(hipGetLastError());

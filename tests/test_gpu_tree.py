@@ -214,3 +214,81 @@ def test_paged_layouts_give_identical_results(page_size):
     assert a[0] == b[0] and a[1] == b[1] and torch.equal(a[2], b[2])
     assert a[3] == b[3] and a[4] == b[4] and torch.equal(a[5], b[5])
     g.close()
+
+
+# ---------------------------------------------------------------- sampled trees (T > 0)
+SAMPLED = dict(mask=synth.mask_exit(4, 2), d=4, max_leaves=6, T=0.5, seed=12345)   # z / 0.5 is exact on both sides
+
+
+def test_sampled_candidates_match_oracle():
+    """At T > 0 the leaves are draws of softmax(z / T) with the leaf purpose and the
+    sequence's iteration (1 after a prefill): the same tokens as the oracle's."""
+    from oracle import philox as ophilox
+    V, T, seed, k_max, rho, ml = 1000, 0.5, 99, 4, 0.6, 15
+    shape = synth.ModelShape("vocab-%d" % V, 1, 64, 1, 1, 64, 64, V, "bf16")
+    g = gpu_model(shape)
+    d, dp = 6, 5
+    z = _candidate_rows(V, d, seed=7) * 0.25
+    assert _boundary_gap(z[:dp] / T, rho, k_max) > 1e-5
+    ref = otree.tree_leaves_sampled(z[:dp], [0] * dp, T, rho, k_max, ml, seed, 1)
+    for j, _ in ref:                         # no race decided within rounding: the two best keys apart
+        for r in range(1, k_max):
+            keys = np.sort((np.asarray(z[j - 1], np.float64) / T).astype(np.float32) +
+                           ophilox.gumbel(seed, 1, (j - 1) + 256 * r, 4, V))
+            assert keys[-1] - keys[-2] > 1e-5
+    seq = B.Sequence(g, max_ctx=128, max_rows=16, max_draft=d)
+    B.ssd_prefill(seq.handle, dev(synth.prompt_tokens(8, V)))
+    B.ssd_tree_candidates(seq.handle, dev(z.reshape(-1), torch.float32), dev([dp]), d, rho, k_max, ml,
+                          seq.leaf_tokens, seq.leaf_depth, seq.n_leaves, T, seed)
+    torch.cuda.synchronize()
+    nl = int(seq.n_leaves.item())
+    got = list(zip(seq.leaf_depth[:nl].cpu().tolist(), seq.leaf_tokens[:nl].cpu().tolist()))
+    print("sampled leaves: %s" % got)
+    assert got == ref and nl > 0
+    seq.close()
+    g.close()
+
+
+def test_sampled_tree_without_leaves_is_the_chain():
+    """k_max = 1: no leaves, and sampled tree decoding emits ssd_accept's tokens
+    draw for draw (same tokens, same per-iteration record)."""
+    shape = BF16_HD64
+    g = gpu_model(shape)
+    P, n_gen = 24, 40
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    kw = dict(skip_mask=SAMPLED["mask"], d=SAMPLED["d"], temperature=SAMPLED["T"], seed=SAMPLED["seed"])
+    seq = B.Sequence(g, max_ctx=P + n_gen + 32, max_rows=16, max_draft=8)
+    a, sa = seq.generate_tree(dev(prompt), n_gen, k_max=1, max_leaves=SAMPLED["max_leaves"], **kw)
+    seq.close()
+    seq = B.Sequence(g, max_ctx=P + n_gen + 32, max_rows=16, max_draft=8)
+    b, sb = seq.generate_ssd(dev(prompt), n_gen, **kw)
+    seq.close()
+    assert [int(x) for x in a] == [int(x) for x in b] and sa == sb
+    g.close()
+
+
+def test_sampled_tree_generation_matches_oracle():
+    """T = 0.5 with drawn leaves: the same Philox draws on both sides, so the tokens
+    agree except at decisions within rounding of flipping; the oracle's run
+    accepts leaves."""
+    shape = BF16_HD64
+    g = gpu_model(shape)
+    o = omodel.Model.synthetic(shape)
+    P, n_gen = 24, 40
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    c = SAMPLED
+    ref, ost, _ = otree.tree_generate(o, prompt, n_gen, c["mask"], c["d"], RHO, K_MAX, c["max_leaves"], T=c["T"],
+                                      seed=c["seed"])
+    assert sum(ost["leaf_accepted"]) >= 2
+    seq = B.Sequence(g, max_ctx=P + n_gen + 32, max_rows=16, max_draft=8)
+    out, stats = seq.generate_tree(dev(prompt), n_gen, skip_mask=c["mask"], d=c["d"], rho=RHO, k_max=K_MAX,
+                                   max_leaves=c["max_leaves"], temperature=c["T"], seed=c["seed"])
+    seq.close()
+    got = [int(x) for x in out]
+    n_match = next((i for i, (a, b) in enumerate(zip(got, ref)) if a != b), len(ref))
+    print("sampled tree: %d/%d tokens match; oracle leaf acceptances %d" % (n_match, n_gen,
+                                                                          sum(ost["leaf_accepted"])))
+    assert n_match >= n_gen // 2
+    if n_match == n_gen:
+        assert [e for _, e in stats] == ost["emitted"]
+    g.close()
