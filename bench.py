@@ -68,6 +68,12 @@ WORKLOADS = {
                         "dynamic verification: each draft step's top-k candidates (k from the top-k mass reaching "
                         "0.9, k <= 4) verified as leaves beside the chain, at most 3 leaves (16 verify rows); "
                         "512-token random prompt, batch 1"),
+    "tree13b": dict(shape="llama2-13b-shape", prompt=1024, n_gen=256, random_skip=20, d=8, tau=0.8, T=1.0,
+                    tree=dict(rho=0.9, k_max=4, max_leaves=7),
+                    desc="LLaMA-2-13B-shaped bf16 decoder, SWIFT skip mask of 20 seeded layers, d<=8, confidence "
+                         "stop 0.8, T=1.0 sampling, with sampled draft trees: each draft step's extra candidates "
+                         "(k from the top-k mass of softmax(z/T) reaching 0.9, k <= 4) drawn from the draft "
+                         "distribution and verified as leaves, at most 7 leaves (16 verify rows); 1024-token prompt"),
     "70b": dict(shape="llama2-70b-shape", prompt=4096, n_gen=128, random_skip=40, d=8, tau=0.0, T=0.0,
                 desc="LLaMA-2-70B-shaped bf16 decoder (GQA 64/8), SWIFT skip mask of 40 seeded layers, d=8, "
                      "greedy, 4096-token prompt, 128 tokens"),
