@@ -3,7 +3,7 @@
 // the parallel verification; §3.2.1 and Figure 2 — top-k drafts raise the
 // acceptance).  Readings taken where the page gives no formula:
 //   * the candidates of draft step j are the k_j most probable tokens of
-//     softmax(z_j) (temperature 1; lowest index first among equal logits),
+//     softmax(z_j) (temperature 1 when greedy; lowest index first among equal logits),
 //     k_j = the least k >= 1 whose top-k mass reaches rho, at most k_max;
 //   * only the top candidate is drafted further; the others are leaves at its
 //     position, attending to the prefix and themselves;
@@ -11,7 +11,11 @@
 //     pass's free rows;
 //   * greedy acceptance walks the chain; where the target's choice differs
 //     from the draft it may be a leaf of that depth, which is then emitted
-//     with the target's choice after it.
+//     with the target's choice after it;
+//   * when sampling (T > 0) the leaves are further draws of softmax(z / T),
+//     since the speculative-sampling rule keeps the target distribution only
+//     for drawn candidates; their acceptance (the multi-candidate rule) is in
+//     kernels.hip next to the chain's.
 // The kernels here are control-sized (one block per draft row, or one wave);
 // the verify rows themselves run through the decode-block kernels.
 #include <math.h>
