@@ -38,6 +38,16 @@ int ssd_profile_disable(void);
  * their algorithmic bytes. */
 int ssd_profile_read(double* total_ms, int* n_launches, double* total_bytes);
 
+/* A streaming-read probe, for a measured bandwidth ceiling to set the kernels
+ * against: one launch reads src_dev[0, bytes) once (2048 workgroups of 256
+ * threads, each workgroup one contiguous slice, 16-byte loads, eight per thread
+ * in flight)
+ * and writes one word per workgroup to sink_dev[2048] (a fold of what it read,
+ * so that the loads are not removed).  bytes must be a positive multiple of 64
+ * and src_dev 16-byte aligned.  Enqueued on `stream` (a hipStream_t, nullable);
+ * returns 0, SSD_ERR_ARG (-1) or SSD_ERR_HIP (-4). */
+int ssd_probe_read(const void* src_dev, uint64_t bytes, uint32_t* sink_dev, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_packed_bf16_bytes", "ss
            "ssd_score_masks", "ssd_uniform_mask", "ssd_swift_propose", "ssd_swift_search", "ssd_specee_features",
            "ssd_row_stats",
            "ssd_read_state", "ssd_read_output", "ssd_last_error",
-           "ssd_profile_enable", "ssd_profile_disable", "ssd_profile_read"]
+           "ssd_profile_enable", "ssd_profile_disable", "ssd_profile_read", "ssd_probe_read"]
 
 
 class SSDError(RuntimeError):
@@ -98,6 +98,7 @@ def lib():
             "ssd_profile_enable": [I, I],
             "ssd_profile_disable": [],
             "ssd_profile_read": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I), ctypes.POINTER(ctypes.c_double)],
+            "ssd_probe_read": [P, U64, P, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -323,6 +324,10 @@ def ssd_profile_read():
     n = ctypes.c_int()
     check(lib().ssd_profile_read(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(by)))
     return ms.value, n.value, by.value
+
+
+def ssd_probe_read(src, nbytes, sink, stream=None):
+    check(lib().ssd_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
 
 
 

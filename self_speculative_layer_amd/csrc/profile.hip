@@ -101,3 +101,45 @@ extern "C" int ssd_profile_read(double* total_ms, int* n_launches, double* total
   *total_bytes = by;
   return SSD_OK;
 }
+
+// ---------------------------------------------------------------------------
+// streaming-read probe
+
+namespace {
+
+__global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ src, uint64_t n16,
+                                                         uint32_t* __restrict__ sink) {
+  // each workgroup reads one contiguous slice, eight 4 KB runs in flight per step
+  const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const uint64_t beg = min((uint64_t)blockIdx.x * per, n16), end = min(beg + per, n16);
+  uint32_t acc = 0;
+  uint64_t i = beg + threadIdx.x;
+  for (; i + 7 * 256 < end; i += 8 * 256) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[i + k * 256];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < end; i += 256) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int k = 0; k < 256; ++k) t ^= red[k];
+    sink[blockIdx.x] = t;
+  }
+}
+
+}  // namespace
+
+extern "C" int ssd_probe_read(const void* src_dev, uint64_t bytes, uint32_t* sink_dev, void* stream) {
+  if (!src_dev || !sink_dev || bytes == 0 || bytes % 64 != 0 || ((uintptr_t)src_dev & 15) != 0) return SSD_ERR_ARG;
+  hipLaunchKernelGGL(probe_read_kernel, dim3(2048), dim3(256), 0, (hipStream_t)stream, (const uint4*)src_dev,
+                     bytes / 16, sink_dev);
+  return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
