@@ -59,3 +59,28 @@ def check_greedy_tokens(gpu, ref, ref_logits, margin=1e-2):
 
 def dev(a, dtype=torch.int32):
     return torch.as_tensor(np.asarray(a), dtype=dtype).cuda()
+
+
+def check_greedy_with_resync(generate, prompt, ref, ref_logits, margin=1e-2, max_events=2):
+    """Greedy parity with re-synchronisation: generate(prefix, n) runs the GPU path
+    from a prompt of committed tokens and returns n tokens.  A token may differ
+    from the oracle's only where the oracle's top-2 margin is below `margin`; after
+    such an allowed mismatch the GPU path restarts from the oracle's committed
+    prefix (a fresh prefill) and the comparison goes on.  Returns the number of
+    re-synchronisations (at most max_events)."""
+    prompt = [int(t) for t in prompt]
+    ref = [int(t) for t in ref]
+    done, events = 0, 0
+    while done < len(ref):
+        got = [int(x) for x in generate(prompt + ref[:done], len(ref) - done)]
+        mismatch = next((i for i, (a, b) in enumerate(zip(got, ref[done:])) if a != b), None)
+        if mismatch is None:
+            assert len(got) == len(ref) - done
+            return events
+        k = done + mismatch
+        mg = top2_margin(ref_logits[k])
+        assert mg < margin, "token %d: gpu %d oracle %d, oracle margin %.3g" % (k, got[mismatch], ref[k], mg)
+        events += 1
+        assert events <= max_events, "too many near-tie re-synchronisations"
+        done = k + 1
+    return events

@@ -10,8 +10,8 @@ from oracle import philox as ophilox
 from oracle import ssd as ossd
 
 from synth import device as sdev
-from gpu_util import (BF16_HD64, BF16_HD128, F32_GQA, check_greedy_tokens, dev, gpu_model, logit_tol,
-                      oracle_ar_with_logits)
+from gpu_util import (BF16_HD64, BF16_HD128, F32_GQA, check_greedy_tokens, check_greedy_with_resync, dev, gpu_model,
+                      logit_tol, oracle_ar_with_logits)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,10 +103,19 @@ def test_greedy_ssd_matches_oracle_and_ar(pair):
                                   exit_layer=plan.get("exit_layer"), d=plan["d"])
     print("iterations %d, mean emitted %.2f" % (len(stats), np.mean([e for _, e in stats])))
     assert all(1 <= e <= dp + 1 for dp, e in stats)
-    check_greedy_tokens(out, ref, ref_z)
     ar = seq.generate_ar(dev(prompt), n_gen)
     assert [int(x) for x in ar] == [int(x) for x in out]
     seq.close()
+
+    def gen(prefix, n):
+        s2 = B.Sequence(g, max_ctx=len(prefix) + n + 2 * plan["d"] + 8, max_rows=64, max_draft=8)
+        toks, _ = s2.generate_ssd(dev(prefix), n, skip_mask=plan.get("skip_mask"), exit_layer=plan.get("exit_layer"),
+                                  d=plan["d"])
+        s2.close()
+        return toks
+
+    events = check_greedy_with_resync(gen, prompt, ref, ref_z)
+    print("near-tie re-synchronisations: %d" % events)
 
 
 def test_verify_logits_match_oracle_per_iteration(pair):

@@ -11,8 +11,8 @@ from oracle import ssd as ossd
 from oracle import tree as otree
 from oracle.numerics import softmax
 
-from gpu_util import BF16_HD64, BF16_HD128, F32_GQA, check_greedy_tokens, dev, gpu_model, logit_tol, \
-    oracle_ar_with_logits
+from gpu_util import BF16_HD64, BF16_HD128, F32_GQA, check_greedy_tokens, check_greedy_with_resync, dev, gpu_model, \
+    logit_tol, oracle_ar_with_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -147,6 +147,14 @@ def test_tree_generation_matches_oracle(pair):
     if first is None:
         assert [e for _, e in stats] == ost["emitted"] and [dp for dp, _ in stats] == ost["drafted"]
     seq.close()
+
+    def gen(prefix, n):
+        s2 = B.Sequence(g, max_ctx=len(prefix) + n + 2 * d + 8, max_rows=16, max_draft=d)
+        toks, _ = s2.generate_tree(dev(prefix), n, skip_mask=mask, d=d, rho=RHO, k_max=K_MAX, max_leaves=ml)
+        s2.close()
+        return toks
+
+    print("near-tie re-synchronisations: %d" % check_greedy_with_resync(gen, prompt, ref, ref_z))
 
 
 def test_tree_arguments_rejected():
