@@ -35,8 +35,8 @@ PMC_TRAFFIC = {
                                     "fetch_scale": 2.0, "write_scale": 1.0},
 }
 PMC_TRAFFIC["gemm_bf16_tiled<EPI_SWIGLU, 4, 4>"] = {
-    "source": "self_speculative_layer_amd/csrc/kernels.hip", "sha1_prefix": "83ddb57518b1",
-    "fetch_kib": 187800.0, "write_kib": 6422.5, "fetch_scale": 2.0, "write_scale": 1.0}
+    "source": "self_speculative_layer_amd/csrc/kernels.hip", "sha1_prefix": "cf269fe21ae0",
+    "fetch_kib": 187621.0, "write_kib": 6420.7, "fetch_scale": 2.0, "write_scale": 1.0}
 DOMINANT = "dec_gemm_kernel<DEC_SWIGLU>"
 SCORING_DOMINANT = "gemm_bf16_tiled<EPI_SWIGLU, 4, 4>"
 
