@@ -300,3 +300,32 @@ def test_sampled_tree_generation_matches_oracle():
     if n_match == n_gen:
         assert [e for _, e in stats] == ost["emitted"]
     g.close()
+
+
+@pytest.mark.parametrize("plan", ["empty", "skip-layer0-attention"])
+def test_tree_decoding_edge_plans(plan):
+    """Reuse-boundary edge cases of the tree verify: the empty plan (b = L: y_d' and
+    the leaves run every layer in the prefix block, no suffix) and a plan whose
+    first sub-layer is skipped (b = 0: no prefix block).  With the empty plan
+    every draft is accepted and the tokens are the GPU's AR tokens exactly; with
+    the other plan the tokens are the oracle's greedy ones (margin rule)."""
+    shape = BF16_HD64
+    g = gpu_model(shape)
+    P, n_gen, d = 24, 40, 4
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    mask = np.zeros(2 * shape.n_layers, np.uint8)
+    if plan != "empty":
+        mask[0] = 1
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=16, max_draft=d)
+    out, stats = seq.generate_tree(dev(prompt), n_gen, skip_mask=mask, d=d, rho=0.99, k_max=4, max_leaves=3)
+    seq.close()
+    seq = B.Sequence(g, max_ctx=P + n_gen + 8, max_rows=16, max_draft=2)
+    ar = seq.generate_ar(dev(prompt), n_gen)
+    seq.close()
+    g.close()
+    if plan == "empty":
+        assert all(e == dp + 1 for dp, e in stats)
+        assert [int(x) for x in out] == [int(x) for x in ar]
+    else:
+        ref, ref_z = oracle_ar_with_logits(omodel.Model.synthetic(shape), prompt, n_gen)
+        check_greedy_tokens(out, ref, ref_z)
