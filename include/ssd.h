@@ -9,7 +9,9 @@
  *            draft's state below the first skipped layer, then the shared LM head;
  *   accept — min(1, p/q) accept/reject with resampling from norm(max(0, p - q))
  *            and a bonus token when every draft is accepted;
- * plus SWIFT's matchness scoring of candidate skip plans against committed context.
+ * plus SWIFT's matchness scoring of candidate skip plans against committed context
+ * and its layer-set search, dynamic verification with confidence-sized draft
+ * trees, lossy early-exit decoding, and SpecEE's speculative-token features.
  *
  * Sources (web pages, cited by title and section):
  *   [SWIFT]     "SWIFT: On-the-Fly Self-Speculative Decoding for LLM Inference
@@ -33,8 +35,9 @@
  *   - Return value: SSD_OK (0) or a negative ssd_status.  ssd_last_error()
  *     gives a message for the calling thread's last failure.  Nothing aborts
  *     and nothing throws across this boundary.  Conditions found on the device
- *     (KV capacity exceeded, non-finite logits) set a sticky flag in the
- *     sequence, reported by ssd_read_state() / ssd_sync().
+ *     (KV capacity exceeded, non-finite logits, a device-side argument out of
+ *     range) set a sticky flag in the sequence, reported by ssd_read_state()
+ *     and ssd_read_output().
  *
  * Sequence state kept on the device (so that a whole iteration can be enqueued
  * without a host round trip, and captured in a HIP graph):
