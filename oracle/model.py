@@ -17,23 +17,27 @@ layers are marked separately): uint8[2L], entry 2l = skip the attention
 sub-layer of layer l, entry 2l+1 = skip its MLP sub-layer.  A LayerSkip exit at
 E (LayerSkip blog §3.1) is the plan that skips every sub-layer of layers E..L-1.
 
-RMSNorm before a projection is applied as  y = (rnd(h * gain) . W^T) / rms(h)
-with rms(h) = sqrt(mean(h^2) + eps): the same function as
-rnd(h / rms(h) * gain) . W^T before rounding, with the 1/rms scale applied to
-the projection's output.
+RMSNorm before a projection is the plain definition: the projection input is
+x = rnd(h / rms(h) * gain) with rms(h) = sqrt(mean(h^2) + eps), and the
+projection is x . W^T.
 
 Precision (bf16 models): the model stores bf16 tensors at these points and
 rounds to nearest-even there; everything else is float64 here —
-the gain-scaled residual entering a projection, RoPE'd q, the cached k and v,
-the attention output entering Wo, the SwiGLU product entering Wdown.  fp32
-models are computed in float64 with no rounding.
+the normalised residual entering a projection (after the gain), RoPE'd q, the
+cached k and v, the attention output entering Wo, the SwiGLU product entering
+Wdown.  fp32 models are computed in float64 with no rounding.
+
+Tracing: a callable ``trace(name, layer, value)`` passed to the functions below
+receives each rounding point's tensor and the residual it was formed from
+(names "h_attn", "x_attn", "q", "k", "v", "o", "h_mlp", "x_mlp", "a", "h_final",
+"x_final"), so that tests can check every rounding point on its own.
 """
 import dataclasses
 
 import numpy as np
 
 import synth
-from .numerics import bf16_round, rms, rope, silu, softmax
+from .numerics import bf16_round, rmsnorm, rope, silu, softmax
 
 
 @dataclasses.dataclass
@@ -122,7 +126,17 @@ def first_skipped_layer(mask, n_layers):
     return n_layers
 
 
-def attention_sublayer(model, l, h, positions, kv):
+def norm_input(model, h, gain):
+    """Projection input of an RMSNorm sub-layer: rnd(RMSNorm(h) * gain), per row."""
+    return model.rnd(rmsnorm(h, gain, model.shape.rms_eps))
+
+
+def _tr(trace, name, l, v):
+    if trace is not None:
+        trace(name, l, v)
+
+
+def attention_sublayer(model, l, h, positions, kv, trace=None):
     """One attention sub-layer over rows h[M, D] at absolute positions (increasing).
 
     Writes the rows' keys and values at their positions, then each row attends
@@ -132,14 +146,18 @@ def attention_sublayer(model, l, h, positions, kv):
     lw = model.layers[l]
     M = h.shape[0]
     H, KVH, hd = s.n_heads, s.n_kv_heads, s.head_dim
-    x = model.rnd(h * lw.attn_norm)
-    r = rms(h, s.rms_eps)
-    q = ((x @ lw.wq.T) / r).reshape(M, H, hd)
-    k = ((x @ lw.wk.T) / r).reshape(M, KVH, hd)
-    v = ((x @ lw.wv.T) / r).reshape(M, KVH, hd)
+    x = norm_input(model, h, lw.attn_norm)
+    _tr(trace, "h_attn", l, h)
+    _tr(trace, "x_attn", l, x)
+    q = (x @ lw.wq.T).reshape(M, H, hd)
+    k = (x @ lw.wk.T).reshape(M, KVH, hd)
+    v = (x @ lw.wv.T).reshape(M, KVH, hd)
     q = model.rnd(rope(q, positions, s.rope_theta))
     k = model.rnd(rope(k, positions, s.rope_theta))
     v = model.rnd(v)
+    _tr(trace, "q", l, q)
+    _tr(trace, "k", l, k)
+    _tr(trace, "v", l, v)
     for i, p in enumerate(positions):
         kv.K[l, p] = k[i]
         kv.V[l, p] = v[i]
@@ -154,26 +172,28 @@ def attention_sublayer(model, l, h, positions, kv):
         pr = softmax(sc)
         o[i] = np.einsum("gjk,kgd->gjd", pr, Vc).reshape(H, hd)
     o = model.rnd(o.reshape(M, H * hd))
+    _tr(trace, "o", l, o)
     return h + o @ lw.wo.T
 
 
-def mlp_sublayer(model, l, h):
-    s = model.shape
+def mlp_sublayer(model, l, h, trace=None):
     lw = model.layers[l]
-    x = model.rnd(h * lw.mlp_norm)
-    r = rms(h, s.rms_eps)
-    a = model.rnd(silu((x @ lw.wgate.T) / r) * ((x @ lw.wup.T) / r))
+    x = norm_input(model, h, lw.mlp_norm)
+    _tr(trace, "h_mlp", l, h)
+    _tr(trace, "x_mlp", l, x)
+    a = model.rnd(silu(x @ lw.wgate.T) * (x @ lw.wup.T))
+    _tr(trace, "a", l, a)
     return h + a @ lw.wdown.T
 
 
-def run_layers(model, h, positions, kv, mask=None, l_begin=0, l_end=None):
+def run_layers(model, h, positions, kv, mask=None, l_begin=0, l_end=None, trace=None):
     """Layers l_begin..l_end-1 over rows h, skipping the sub-layers the plan marks."""
     l_end = model.L if l_end is None else l_end
     for l in range(l_begin, l_end):
         if not skip_attn(mask, l):
-            h = attention_sublayer(model, l, h, positions, kv)
+            h = attention_sublayer(model, l, h, positions, kv, trace)
         if not skip_mlp(mask, l):
-            h = mlp_sublayer(model, l, h)
+            h = mlp_sublayer(model, l, h, trace)
     return h
 
 
@@ -181,14 +201,16 @@ def embed(model, tokens):
     return model.embed[np.asarray(tokens, dtype=np.int64)].astype(np.float64)
 
 
-def final_logits(model, h):
+def final_logits(model, h, trace=None):
     """Shared final RMSNorm and shared LM head: logits [M, V] (LayerSkip blog §2)."""
-    s = model.shape
-    return (model.rnd(h * model.final_norm) @ model.lm_head.T) / rms(h, s.rms_eps)
+    x = norm_input(model, h, model.final_norm)
+    _tr(trace, "h_final", model.L, h)
+    _tr(trace, "x_final", model.L, x)
+    return x @ model.lm_head.T
 
 
-def forward(model, tokens, positions, kv, mask=None):
+def forward(model, tokens, positions, kv, mask=None, trace=None):
     """Embed + every (non-skipped) layer + final norm + LM head for a block of rows."""
     h = embed(model, tokens)
-    h = run_layers(model, h, list(positions), kv, mask)
-    return final_logits(model, h)
+    h = run_layers(model, h, list(positions), kv, mask, trace=trace)
+    return final_logits(model, h, trace)

@@ -26,7 +26,7 @@ import numpy as np
 
 from . import model as mdl
 from . import philox
-from .numerics import argmax_lowest, rms, softmax
+from .numerics import argmax_lowest, softmax
 
 
 # --------------------------------------------------------------------------
@@ -273,7 +273,7 @@ def specee_features(model, h, tokens, prev_probs=None):
     is none).  Returns [rows, 3k]."""
     h = np.atleast_2d(np.asarray(h, np.float64))
     w = model.lm_head[[int(t) for t in tokens]]
-    z = (model.rnd(h * model.final_norm) @ w.T) / rms(h, model.shape.rms_eps)
+    z = mdl.norm_input(model, h, model.final_norm) @ w.T
     p = softmax(z)
     var = np.zeros_like(p) if prev_probs is None else p - np.asarray(prev_probs, np.float64)
     return np.concatenate([z, p, var], axis=1)
