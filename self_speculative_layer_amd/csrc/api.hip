@@ -60,7 +60,7 @@ struct Workspace {
   int *dec, *corr, *rowmaps;
   int32_t* log;
   // decode blocks (<= 16 rows)
-  bf16_t* xg;            // next RMSNorm consumer's input bf16(h * g), decode block layout [16][max(D, q_dim)]
+  float* xg;             // next RMSNorm consumer's input h * g (fp32), decode block layout [16][max(D, q_dim)]
   float* ss;             // its 16-feature tile sums of h^2 [16][D / 16]
   unsigned* dec_ctr;     // attention merge counters [16][KVH], zero between launches
   StatRec* stat_recs;    // row statistics: segment records [rows][segments]
@@ -126,7 +126,7 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.corr = (int*)take(sizeof(int) * (max_draft + 1));
   t.rowmaps = (int*)take(sizeof(int) * (size_t)2 * L * R);
   t.log = (int32_t*)take(sizeof(int32_t) * (size_t)max_ctx);
-  t.xg = (bf16_t*)take(2 * (size_t)16 * std::max(D, m->q_dim));
+  t.xg = (float*)take(sizeof(float) * (size_t)16 * std::max(D, m->q_dim));
   t.ss = (float*)take(sizeof(float) * (size_t)16 * (D / 16 + 1));
   t.dec_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)16 * d.n_kv_heads);
   t.stat_recs = (StatRec*)take(sizeof(StatRec) * (size_t)R * stat_segments(V));
@@ -165,8 +165,8 @@ int attn_sublayer(ssd_seq* q, int l, const Block& b, hipStream_t s) {
   const int D = d.d_model;
   TRY(launch_rowprep(d.dtype, b.h, D, lw.attn_norm, w.x, D, w.inv, rb.M, D, d.rms_eps, rb.nrows, rb.ymap, rb.stop,
                      s));
-  TRY(launch_linear(d.dtype, EPI_STORE, lw.w_qkv, w.x, D, rb.M, m->qkv_dim, D, w.qkv, m->qkv_dim, nullptr, 0, w.inv,
-                    rb.nrows, nullptr, rb.stop, s));
+  TRY(launch_linear(d.dtype, EPI_STORE, lw.w_qkv, w.x, D, rb.M, m->qkv_dim, D, w.qkv, m->qkv_dim, nullptr, 0,
+                    nullptr, rb.nrows, nullptr, rb.stop, s));
   TRY(launch_rope_kv(d.dtype, d.head_dim, w.qkv, m->qkv_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads,
                      d.n_kv_heads, rb, w.rope_cs, b.local_kv, &w.st->error_flags, s));
   TRY(launch_attention(d.dtype, d.head_dim, w.qb, m->q_dim, q->kv, d.n_layers, l, d.n_heads, d.n_kv_heads, rb,
@@ -185,7 +185,7 @@ int mlp_sublayer(ssd_seq* q, int l, const Block& b, hipStream_t s) {
   const int D = d.d_model, F = d.ffn_dim;
   TRY(launch_rowprep(d.dtype, b.h, D, lw.mlp_norm, w.x, D, w.inv, rb.M, D, d.rms_eps, rb.nrows, rb.ymap, rb.stop,
                      s));
-  TRY(launch_linear(d.dtype, EPI_SWIGLU, lw.w_gate_up, w.x, D, rb.M, F, D, nullptr, 0, w.x2, F, w.inv, rb.nrows,
+  TRY(launch_linear(d.dtype, EPI_SWIGLU, lw.w_gate_up, w.x, D, rb.M, F, D, nullptr, 0, w.x2, F, nullptr, rb.nrows,
                     nullptr, rb.stop, s));
   TRY(launch_linear(d.dtype, EPI_RESID, lw.w_down, w.x2, F, rb.M, D, F, b.h, D, nullptr, 0, nullptr, rb.nrows,
                     rb.ymap, rb.stop, s, w.gemm_split, 4 * (size_t)q->max_rows * D));
@@ -211,7 +211,7 @@ int final_logits(ssd_seq* q, const float* h, int M, const int* nrows, float* log
   TRY(launch_rowprep(d.dtype, h, d.d_model, d.final_norm, q->w.x, d.d_model, q->w.inv, M, d.d_model, d.rms_eps,
                      nrows, nullptr, stop, s));
   TRY(launch_linear(d.dtype, EPI_STORE, d.lm_head, q->w.x, d.d_model, M, d.vocab, d.d_model, logits, d.vocab,
-                    nullptr, 0, q->w.inv, nrows, nullptr, stop, s));
+                    nullptr, 0, nullptr, nrows, nullptr, stop, s));
   return 0;
 }
 
@@ -287,7 +287,7 @@ int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, co
     if (ent[e] % 2 == 0) {
       DecGemm a = dec_base(q, M, nrows, stop);
       a.W = (const bf16_t*)lw.w_qkv; a.N = m->qkv_dim; a.K = D;
-      a.X = w.xg;
+      a.Xf = w.xg;
       a.q = (bf16_t*)w.qb; a.ldq = m->q_dim;
       a.pool = (bf16_t*)q->kv.pool; a.page_table = q->kv.page_table; a.PS = q->kv.page_size;
       a.n_lpages = q->kv.n_lpages; a.L = d.n_layers; a.layer = l;
@@ -303,7 +303,7 @@ int dec_layers(ssd_seq* q, float* h, int M, const int* nrows, const int* pos, co
     } else {
       DecGemm a = dec_base(q, M, nrows, stop);
       a.W = (const bf16_t*)lw.w_gate_up; a.N = F; a.K = D;
-      a.X = w.xg;
+      a.Xf = w.xg;
       a.A = (bf16_t*)w.x2;
       TRY(launch_dec_gemm(DEC_SWIGLU, a, s));
       r.W = (const bf16_t*)lw.w_down; r.K = F; r.X = (const bf16_t*)w.x2;
@@ -318,7 +318,7 @@ int dec_logits(ssd_seq* q, int M, const int* nrows, float* logits, const int* st
   const ssd_model_desc& d = q->m->d;
   DecGemm a = dec_base(q, M, nrows, stop);
   a.W = (const bf16_t*)d.lm_head; a.N = d.vocab; a.K = d.d_model;
-  a.X = q->w.xg;
+  a.Xf = q->w.xg;
   a.Y = logits; a.ldy = d.vocab;
   TRY(launch_dec_gemm(DEC_STORE, a, s));
   return 0;

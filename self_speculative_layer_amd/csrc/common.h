@@ -185,6 +185,30 @@ __device__ __forceinline__ size_t dec_act_index(int row, int col) {
   return (size_t)(col >> 5) * 512 + (size_t)row * 32 + (col & 31);
 }
 
+// fp32 rows of a decode block (the h * gain inputs of RMSNorm consumers): the
+// same 32-column blocks of 16 rows, each split into two 1 KB halves so that a
+// matrix-core step's operand (lane = 16 g + row takes k = 8g .. 8g + 7) is two
+// loads of 16 contiguous bytes per lane, each load one contiguous 1 KB run:
+// half 0 holds k = 8g .. 8g + 3, half 1 k = 8g + 4 .. 8g + 7.
+__device__ __forceinline__ size_t dec_actf_index(int row, int col) {
+  const int kk = col & 31;
+  return (size_t)(col >> 5) * 512 + (size_t)((kk >> 2) & 1) * 256 + (size_t)((kk >> 3) * 16 + row) * 4 + (kk & 3);
+}
+
+// Projection input of an RMSNorm: bf16 (round to nearest even, the matrix
+// cores' conversion) of (h * gain) * inv_rms.  The residual's product with the
+// gain is formed by whichever kernel last updated h; the consumer applies the
+// row's 1 / rms before rounding, so the stored value is RMSNorm(h) * gain
+// rounded once.  Every kernel that forms such an input uses these functions.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t norm_pack2(float hg0, float hg1, float inv) {
+  const bf16x2_t v = {(__bf16)__fmul_rn(hg0, inv), (__bf16)__fmul_rn(hg1, inv)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bf16_t norm_bf16(float hg, float inv) {
+  return (bf16_t)(norm_pack2(hg, 0.f, inv) & 0xFFFFu);
+}
+
 __device__ __forceinline__ float swiglu(float g, float u) {
   return __fmul_rn(__fdiv_rn(g, __fadd_rn(1.0f, expf(-g))), u);
 }

@@ -2,13 +2,14 @@
 // d' + 1 rows of a verify pass) through the decoder with the small steps
 // folded into the projections, so that a layer takes five launches:
 //
-//   QKV projection    row scale from the RMSNorm tile sums, RoPE, q store and
+//   QKV projection    normalised input bf16(h * gain / rms) from the RMSNorm
+//                     tile sums, RoPE, q store and
 //                     K/V append to the paged cache in the epilogue
 //   attention         split partials; the last split of a (row block, KV head)
 //                     to finish merges them
 //   O projection      residual add, then the next RMSNorm consumer's input
-//                     (x = bf16(h * gain) and the 16-feature tile sums of h^2)
-//   gate/up           row scale, SwiGLU
+//                     (h * gain in fp32 and the 16-feature tile sums of h^2)
+//   gate/up           normalised input, SwiGLU
 //   down projection   residual add, next consumer's input
 //
 // The arithmetic of every output element is the same as in the general
@@ -18,12 +19,21 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 #include "attn.h"
 
 namespace ssd {
 
 typedef uint32_t dec_u32x4 __attribute__((ext_vector_type(4)));
+typedef float dec_f32x8 __attribute__((ext_vector_type(8)));
+
+// B operand (8 consecutive k of one row) of a normalised input: bf16((h * gain) * inv_rms).
+__device__ __forceinline__ dec_u32x4 norm_operand(const dec_f32x8& v, float inv) {
+  return dec_u32x4{norm_pack2(v[0], v[1], inv), norm_pack2(v[2], v[3], inv), norm_pack2(v[4], v[5], inv),
+                   norm_pack2(v[6], v[7], inv)};
+}
 
 static inline int dec_ok(hipError_t e) { return e == hipSuccess ? 0 : SSD_ERR_HIP; }
 
@@ -33,6 +43,7 @@ constexpr int DEC_U = 8;      // 32-element K steps each wave keeps in flight
 // 7B shapes, 4 was fastest for every matrix.
 constexpr int DEC_NW = 4;
 constexpr int DEC_SSP = 8;    // RMS tile sums per lane and row: K <= 64 * 16 * DEC_SSP
+constexpr int DEC_AX = 4;     // activation steps in flight (fp32 normalised inputs)
 
 // ===========================================================================
 // Projection Y[M, N] = X[M, K] . W[N, K]^T for M <= 16, bf16 operands, fp32
@@ -43,10 +54,16 @@ constexpr int DEC_SSP = 8;    // RMS tile sums per lane and row: K <= 64 * 16 * 
 // SwiGLU and QKV epilogues) and all of K.  Its NW waves take contiguous
 // 64-element slices of K; each wave keeps DEC_U steps (one contiguous 1 KB
 // tile of each weight set per step, packed layout) in flight in registers and
-// reloads a step's
-// registers as soon as its MFMA has been issued.  The per-wave tiles are
-// reduced through LDS in wave order.  Rows >= M repeat the last row's
-// activations (no masking on the load path); their outputs are not stored.
+// reloads a step's registers as soon as its MFMA has been issued.  The
+// per-wave tiles are reduced through LDS in wave order.  Rows >= M repeat the
+// last row's activations (no masking on the load path); their outputs are not
+// stored.
+//
+// RMSNorm consumers (QKV, gate/up, LM head) read the fp32 rows h * gain and
+// the rows' tile sums of h^2: the row scale 1 / rms is formed before the
+// stream starts (while the first weight steps are in flight), and each step's
+// B operand is bf16(h * gain * inv), so the projection sees the normalised
+// input rounded once, as the plain definition has it.
 // ===========================================================================
 
 // Per-tile output rows: f0 + i (and f1 + i for the two-set epilogues); for QKV also the head slot and
@@ -107,7 +124,12 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
     wp[j * SPT] = a.W + wpk_index(wrow, g * 8, K);                  // step t: + 512 t
     if (DUAL) wp[j * SPT + 1] = a.W + wpk_index(t.f1 + r, g * 8, K);
   }
-  const bf16_t* xp = a.X + dec_act_index(min(r, Ma - 1), g * 8);   // step t: xp + 512 t
+  // activations of row r (clamped), k = 8g..8g+7 of each step: step t at + 512 t
+  typedef typename std::conditional<NORM, float, bf16_t>::type XT;
+  typedef typename std::conditional<NORM, dec_f32x8, dec_u32x4>::type XR;
+  const XT* xp;
+  if constexpr (NORM) xp = a.Xf + dec_actf_index(min(r, Ma - 1), g * 8);   // + 256: k = 8g + 4 .. 8g + 7
+  else xp = a.X + dec_act_index(min(r, Ma - 1), g * 8);
 
   // Epilogue operands that do not depend on the product (the residual element and the next gain; the
   // row's position) are loaded ahead of the weight stream, so that the tail after the reduction holds
@@ -146,15 +168,29 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   const int nu = K >> 6;
   const int s0 = 2 * ((nu * wave) / NW);
   const int n = 2 * ((nu * (wave + 1)) / NW) - s0;   // 32-element steps of this wave (>= 2)
-  dec_u32x4 w[NS][U], xa[U];
-  auto reload = [&](int u, int step) {
+  // activation steps in flight: the fp32 rows of a normalised input come from the L2 (the previous
+  // kernel wrote them), so a few steps ahead cover their latency and keep the registers for the weights
+  constexpr int AX = NORM && DEC_AX < U ? DEC_AX : U;
+  static_assert(U % AX == 0, "activation slots divide the weight slots");
+  dec_u32x4 w[NS][U];
+  XR xa[AX];
+  auto wload = [&](int u, int step) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) w[j][u] = *(const dec_u32x4*)(wp[j] + (size_t)(s0 + step) * 512);
-    xa[u] = *(const dec_u32x4*)(xp + (size_t)(s0 + step) * 512);
+  };
+  auto xload = [&](int slot, int step) {
+    if constexpr (NORM) {
+      const f32x4 lo = *(const f32x4*)(xp + (size_t)(s0 + step) * 512);
+      const f32x4 hi = *(const f32x4*)(xp + (size_t)(s0 + step) * 512 + 256);
+      xa[slot] = dec_f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      xa[slot] = *(const XR*)(xp + (size_t)(s0 + step) * 512);
+    }
   };
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    reload(u, min(u, n - 1));
+    wload(u, min(u, n - 1));
+    if (u < AX) xload(u, min(u, n - 1));
     __builtin_amdgcn_sched_barrier(0);       // same load order as the steady loop
   }
 
@@ -171,6 +207,11 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, WAVE);
       if (row < Ma && lane == 0) sinv[row] = inv_rms(acc, K, a.eps);
     }
+  }
+  float xinv = 1.f;                             // the scale of this lane's activation row
+  if constexpr (NORM) {
+    __syncthreads();
+    xinv = sinv[min(r, Ma - 1)];
   }
   // QKV: the row's page and rotation, issued behind the first weight steps (only the position load
   // is waited for here)
@@ -191,20 +232,25 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
 #pragma unroll
   for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // steps are consumed in increasing order; the steady loop has no branches, so the compiler's
-  // wait before each step's MFMAs leaves the later steps' loads in flight
+  // wait before each step's MFMAs leaves the later steps' loads in flight.  Step t sits in weight
+  // slot t % U and activation slot t % AX.
   auto consume = [&](int u) {
+    dec_u32x4 xb;
+    if constexpr (NORM) xb = norm_operand(xa[u % AX], xinv);
+    else xb = xa[u % AX];
 #pragma unroll
     for (int j = 0; j < NS; ++j)
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[j][u]),
-                                                       __builtin_bit_cast(bf16x8, xa[u]), acc[j], 0, 0, 0);
+                                                       __builtin_bit_cast(bf16x8, xb), acc[j], 0, 0, 0);
   };
   const int nfull = n / U, rem = n - nfull * U;
   for (int b = 1; b < nfull; ++b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      consume(u);
-      reload(u, b * U + u);
-      __builtin_amdgcn_sched_barrier(0);     // keep the issue order: one step's MFMAs, then its reload
+      consume(u);                                // step (b - 1) U + u
+      xload(u % AX, (b - 1) * U + u + AX);       // < n: AX <= U
+      wload(u, b * U + u);
+      __builtin_amdgcn_sched_barrier(0);     // keep the issue order: one step's MFMAs, then its reloads
     }
   }
   if (nfull > 0) {
@@ -212,16 +258,23 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         consume(u);
-        reload(u, min(nfull * U + u, n - 1));
+        xload(u % AX, min((nfull - 1) * U + u + AX, n - 1));
+        wload(u, min(nfull * U + u, n - 1));
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) consume(u);
+      for (int u = 0; u < U; ++u) {
+        consume(u);
+        if (u + AX < U) xload(u % AX, (nfull - 1) * U + u + AX);
+      }
     }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    if (u < rem) consume(u);
+    if (u < rem) {
+      consume(u);                                // step nfull U + u
+      if constexpr (AX < U) xload(u % AX, min(nfull * U + u + AX, n - 1));
+    }
 
   // acc[j][i] holds D[feature 4g + i][row r] of set j
   __shared__ float red[NS][NW][16][17];
@@ -247,23 +300,21 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       if (HALF) s2 += red[j][ww][nn + 8][row];
     }
     if constexpr (EPI == DEC_STORE) {
-      if (t.f0 + nn < a.N) a.Y[(size_t)row * a.ldy + t.f0 + nn] = __fmul_rn(s, sinv[row]);
+      if (t.f0 + nn < a.N) a.Y[(size_t)row * a.ldy + t.f0 + nn] = s;
     } else if constexpr (EPI == DEC_RESID) {
       const int col = t.f0 + nn;
       const float hn = __fadd_rn(eh[j], s);
       a.Y[(size_t)row * a.ldy + col] = hn;
       if (a.y_copy) a.y_copy[(size_t)row * a.ldy + col] = hn;
       if (a.gain_next) {
-        st(a.xg_next + dec_act_index(row, col), __fmul_rn(hn, eg[j]));
+        a.xg_next[dec_actf_index(row, col)] = __fmul_rn(hn, eg[j]);
         const float tt = tile16_ss_lanes(hn);
         if (nn == 0) a.ss_next[(size_t)row * (a.N / 16) + col / 16] = tt;
       }
     } else if constexpr (EPI == DEC_SWIGLU) {
-      const float inv = sinv[row];
-      st(a.A + dec_act_index(row, t.f0 + nn), swiglu(__fmul_rn(s, inv), __fmul_rn(s2, inv)));
+      st(a.A + dec_act_index(row, t.f0 + nn), swiglu(s, s2));
     } else {
-      const float inv = sinv[row];
-      const float x1 = __fmul_rn(s, inv), x2 = __fmul_rn(s2, inv);
+      const float x1 = s, x2 = s2;
       const int HD = a.HD, H = a.H, KVH = a.KVH;
       const int i = t.d0 + nn;                  // pair index
       const int p = epos;                       // row == erow here (row < Ma)
@@ -349,7 +400,7 @@ int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
     // algorithmic bytes: weights once, activations in once, results out once (residual: read + write)
     const double M = a.M, N = a.N, K = a.K;
     const double wrows = epi == DEC_SWIGLU ? 2.0 * N : N;
-    double by = wrows * K * 2.0 + M * K * 2.0;
+    double by = wrows * K * 2.0 + M * K * (epi == DEC_RESID ? 2.0 : 4.0);
     by += epi == DEC_STORE ? 4.0 * M * N : (epi == DEC_RESID ? 8.0 * M * N : 2.0 * M * N);
     profile_done(by, a.stop, true, s);
   }
@@ -440,11 +491,11 @@ int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv,
 // ===========================================================================
 
 // Row r of the entry: h[dr] from the embedding row e (EMB) or from sr, and with NORM the first consumer's
-// input xg[dr] = bf16(h * gain) and the tile sums ss[dr].
+// input xg[dr] = h * gain (fp32) and the tile sums ss[dr].
 template <bool EMB, bool NORM>
 __device__ __forceinline__ void dec_entry_row(const bf16_t* __restrict__ e, const float* __restrict__ sr, int dr,
                                               float* __restrict__ h, int D, const float* __restrict__ gain,
-                                              bf16_t* __restrict__ xg, float* __restrict__ ss) {
+                                              float* __restrict__ xg, float* __restrict__ ss) {
   float* hr = h + (size_t)dr * D;
   // D % 16 == 0: each group of 16 lanes is entirely inside or outside the row.  Loads are issued in
   // batches of 8 per thread before their first use.
@@ -465,7 +516,7 @@ __device__ __forceinline__ void dec_entry_row(const bf16_t* __restrict__ e, cons
       if (NORM) {
         const float t = tile16_ss_lanes(v[j]);
         if (i < D) {
-          st(xg + dec_act_index(dr, i), __fmul_rn(v[j], gv[j]));
+          xg[dec_actf_index(dr, i)] = __fmul_rn(v[j], gv[j]);
           if ((threadIdx.x & 15) == 0) ss[(size_t)dr * (D / 16) + i / 16] = t;
         }
       }
@@ -478,7 +529,7 @@ __global__ __launch_bounds__(256) void dec_entry_kernel(const bf16_t* __restrict
                                                         int V, const float* __restrict__ src, int rows,
                                                         const int* __restrict__ count, const int* __restrict__ dst_off,
                                                         float* __restrict__ h, int D, const float* __restrict__ gain,
-                                                        bf16_t* __restrict__ xg, float* __restrict__ ss,
+                                                        float* __restrict__ xg, float* __restrict__ ss,
                                                         const int* __restrict__ stop) {
   if (stop && *stop) return;
   const int r = blockIdx.x;
@@ -500,7 +551,7 @@ __global__ __launch_bounds__(256) void dec_draft_entry_kernel(DevState* __restri
                                                               const bf16_t* __restrict__ emb, int V,
                                                               float* __restrict__ h, int D,
                                                               const float* __restrict__ gain,
-                                                              bf16_t* __restrict__ xg, float* __restrict__ ss) {
+                                                              float* __restrict__ xg, float* __restrict__ ss) {
   __shared__ int s_tok, s_ok;
   if (threadIdx.x == 0) {
     int ok = !st->stop, tok = 0;
@@ -532,7 +583,7 @@ int launch_dec_draft_entry(DevState* st, const int32_t* drafts, int j, int* pos1
   if (D % 16 != 0) return SSD_ERR_SHAPE;
 #define DENTRY(N)                                                                                                 \
   hipLaunchKernelGGL((dec_draft_entry_kernel<N>), dim3(1), dim3(256), 0, s, st, drafts, j, pos1, tok1, max_ctx,  \
-                     n_drafted_out, (const bf16_t*)emb, V, h, D, gain, (bf16_t*)xg, ss)
+                     n_drafted_out, (const bf16_t*)emb, V, h, D, gain, (float*)xg, ss)
   if (gain) DENTRY(true); else DENTRY(false);
 #undef DENTRY
   return dec_ok(hipGetLastError());
@@ -545,7 +596,7 @@ int launch_dec_entry(const void* emb, const int* tokens, int V, const float* src
   if (D % 16 != 0) return SSD_ERR_SHAPE;
 #define ENTRY(E, N)                                                                                              \
   hipLaunchKernelGGL((dec_entry_kernel<E, N>), dim3(rows), dim3(256), 0, s, (const bf16_t*)emb, tokens, V, src,  \
-                     rows, count, dst_off, h, D, gain, (bf16_t*)xg, ss, stop)
+                     rows, count, dst_off, h, D, gain, (float*)xg, ss, stop)
   if (tokens) {
     if (gain) ENTRY(true, true); else ENTRY(true, false);
   } else {

@@ -43,7 +43,8 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
 // Row-major bf16 [N, K] -> packed tile layout (K % 32 == 0).
 int launch_pack_bf16(const void* src, void* dst, int N, int K, hipStream_t s);
 
-// x[m] = act(h[hmap[m]] * gain), inv[m] = 1 / sqrt(mean(h^2) + eps).
+// x[m] = act(h[hmap[m]] * gain / sqrt(mean(h^2) + eps)) (the projection input of an RMSNorm, rounded once);
+// inv (nullable) receives the rows' 1 / sqrt(mean(h^2) + eps).
 int launch_rowprep(int dtype, const float* h, int ldh, const float* gain, void* x, int ldx, float* inv, int M, int D,
                    float eps, const int* nrows, const int* hmap, const int* stop, hipStream_t s);
 
@@ -158,24 +159,26 @@ bool attention_dec_leaves_fit(int max_ctx);
 // Decode mode (decode.hip): blocks of at most 16 rows, bf16.
 
 enum DecEpilogue {
-  DEC_STORE = 0,    // Y[m, n] = acc * inv[m]                                  (LM head, fp32 logits)
+  DEC_STORE = 0,    // Y[m, n] = acc                                            (LM head, fp32 logits)
   DEC_RESID = 1,    // Y[m, n] += acc; then xg_next, ss_next of the new row (when gain_next)
-  DEC_SWIGLU = 2,   // A[m, f] = bf16(silu(acc_gate * inv[m]) * acc_up * inv[m])
-  DEC_QKV = 3       // (acc * inv[m]) rotated (q, k), stored to q / the paged cache
+  DEC_SWIGLU = 2,   // A[m, f] = bf16(silu(acc_gate) * acc_up)
+  DEC_QKV = 3       // acc rotated (q, k), stored to q / the paged cache
 };
 
-// inv[m] = 1 / sqrt(mean(h^2) + eps) from the rows' 16-feature tile sums ss[m][K/16].
-// Activations (X, and the A / xg_next outputs) are in the decode block layout
-// (dec_act_index in common.h).
+// STORE, SWIGLU and QKV consume an RMSNorm: their input is Xf = h * gain (fp32) with the rows' 16-feature
+// tile sums of h^2 in ss[m][K/16]; the product is taken with bf16(Xf[m] / sqrt(mean(h^2) + eps)).
+// Activations are in the decode block layouts of common.h: X and A (bf16) by dec_act_index, Xf and
+// xg_next (fp32) by dec_actf_index.
 struct DecGemm {
   const bf16_t* W; int N, K;        // W [N rows (SWIGLU: 2N), K]
-  const bf16_t* X;                  // activations [M <= 16, K], decode block layout
+  const bf16_t* X;                  // RESID: activations [M <= 16, K], decode block layout
+  const float* Xf;                  // STORE, SWIGLU, QKV: rows h * gain [M <= 16, K], decode block layout
   int M; const int* nrows; const int* stop;
-  const float* ss; float eps;       // STORE, SWIGLU, QKV: tile sums of the normalised rows
+  const float* ss; float eps;       // STORE, SWIGLU, QKV: tile sums of h^2 of the normalised rows
   float* Y; int ldy;                // STORE: output; RESID: residual stream
   bf16_t* A;                        // SWIGLU output [M, N], decode block layout
   const float* gain_next;           // RESID: gain of the next RMSNorm consumer (nullable: none)
-  bf16_t* xg_next;                  //   its input bf16(h * gain) [M, N], decode block layout
+  float* xg_next;                   //   its input h * gain [M, N] (fp32), decode block layout
   float* ss_next;                   //   tile sums of h^2 [M, N/16]
   float* y_copy;                    //   (nullable) second destination of the new residual rows (stride ldy)
   bf16_t* q; int ldq;               // QKV: rotated queries [M, H*HD]
@@ -205,7 +208,7 @@ int launch_dec_draft_entry(DevState* st, const int32_t* drafts, int j, int* pos1
                            void* xg, float* ss, hipStream_t s);
 
 // h[dst] = embedding row of tokens[r] (tokens != nullptr) or src[r], for r < (count ? *count : rows),
-// dst = r + (dst_off ? *dst_off : 0); with gain, also xg[dst] = bf16(h * gain) and ss[dst] tile sums.
+// dst = r + (dst_off ? *dst_off : 0); with gain, also xg[dst] = h * gain (fp32) and ss[dst] tile sums.
 int launch_dec_entry(const void* emb, const int* tokens, int V, const float* src, int rows, const int* count,
                      const int* dst_off, float* h, int D, const float* gain, void* xg, float* ss, const int* stop,
                      hipStream_t s);

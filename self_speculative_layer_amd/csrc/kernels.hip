@@ -539,9 +539,10 @@ static int launch_linear_impl(int dtype, int epi, const void* W, const void* X, 
 // RMSNorm: x[m] = act(h[hmap[m]] / sqrt(mean(h^2) + eps) * gain), fp32 sums.
 // ===========================================================================
 
-// Row preparation for a projection: x[m] = act(h[hmap[m]] * gain) and
-// inv[m] = 1 / sqrt(mean(h^2) + eps) (the RMS scale is applied to the
-// projection's output).  One workgroup per row.
+// Row preparation for a projection: x[m] = act(h[hmap[m]] * gain * inv) with
+// inv = 1 / sqrt(mean(h^2) + eps), the RMSNorm's output rounded once (the same
+// bits as the decode projections' operands: norm_bf16 of h * gain and inv from
+// the canonical tile sums).  One workgroup per row.
 template <typename T>
 __global__ __launch_bounds__(1024) void rowprep_kernel(const float* __restrict__ h, int ldh,
                                                        const float* __restrict__ gain, T* __restrict__ x,
@@ -554,6 +555,7 @@ __global__ __launch_bounds__(1024) void rowprep_kernel(const float* __restrict__
   const float* hr = h + (size_t)(hmap ? hmap[row] : row) * ldh;
   T* xr = x + (size_t)row * ldx;
   __shared__ float tss[1024];                  // group sums, D <= 16384
+  __shared__ float s_inv;
   constexpr int PER = 16;                      // D / 1024 elements per thread at most
   float v[PER], gv[PER];
 #pragma unroll
@@ -567,15 +569,27 @@ __global__ __launch_bounds__(1024) void rowprep_kernel(const float* __restrict__
     const int i = j * 1024 + threadIdx.x;
     if (j * 1024 >= D) break;                  // uniform: D is a multiple of 16
     const float s = tile16_ss_lanes(v[j]);
-    if (i < D) {
-      if ((threadIdx.x & 15) == 0) tss[i >> 4] = s;
-      st(xr + i, __fmul_rn(v[j], gv[j]));
-    }
+    if (i < D && (threadIdx.x & 15) == 0) tss[i >> 4] = s;
   }
   __syncthreads();
   if (threadIdx.x < 64) {
     const float tot = row_ss_total(tss, 1, D / 16);
-    if (threadIdx.x == 0) inv[row] = inv_rms(tot, D, eps);
+    if (threadIdx.x == 0) {
+      s_inv = inv_rms(tot, D, eps);
+      if (inv) inv[row] = s_inv;
+    }
+  }
+  __syncthreads();
+  const float iv = s_inv;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = j * 1024 + threadIdx.x;
+    if (j * 1024 >= D) break;
+    if (i < D) {
+      const float hg = __fmul_rn(v[j], gv[j]);
+      if constexpr (sizeof(T) == 2) xr[i] = norm_bf16(hg, iv);
+      else xr[i] = __fmul_rn(hg, iv);
+    }
   }
 }
 
@@ -1727,13 +1741,14 @@ __global__ void score_kernel(const ssd_row_stat* __restrict__ stats, const int32
 // ===========================================================================
 // SpecEE exit features of hidden states (SpecEE notes §4.3.1): for k
 // speculative tokens t_j, z_j = the shared final norm and LM head restricted to
-// the k columns (bf16(h * g) . W[t_j] / rms(h), the LM head's own rounding
-// points), the local probabilities p = softmax(z) over the k, and the variation
+// the k columns (bf16(h / rms(h) * g) . W[t_j], the LM head's own rounding
+// point), the local probabilities p = softmax(z) over the k, and the variation
 // p - p_prev against the previous layer's (0 without one).  One workgroup per row.
 // ===========================================================================
 
-// One pass over the row: each thread keeps the sum of squares and the k dot products of its 8-element
-// chunks; the wave sums (butterfly) are added in wave order.
+// Two passes over the row: the sum of squares (canonical tile order) gives the row's 1 / rms; then each
+// thread keeps the k dot products of its 8-element chunks of x = rnd(h * gain * inv), and the wave sums
+// (butterfly) are added in wave order.
 template <typename T>
 __global__ __launch_bounds__(256) void specee_features_kernel(const float* __restrict__ h, int D, float eps,
                                                               const float* __restrict__ gain, const T* __restrict__ W,
@@ -1743,11 +1758,25 @@ __global__ __launch_bounds__(256) void specee_features_kernel(const float* __res
   constexpr int KM = 16;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* hr = h + (size_t)row * D;
-  __shared__ float red[4][KM + 1];
+  __shared__ float red[4][KM];
+  __shared__ float tss[1024];                  // 16-feature tile sums, D <= 16384
+  __shared__ float s_inv;
   int tk[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) tk[j] = j < k ? min(max(tokens[j], 0), V - 1) : 0;
-  float ss = 0.f, part[KM];
+  for (int i0 = 0; i0 < D; i0 += 256) {        // D % 16 == 0: each 16-lane group is inside or outside the row
+    const int i = i0 + tid;
+    const float t = tile16_ss_lanes(i < D ? hr[i] : 0.f);
+    if (i < D && (tid & 15) == 0) tss[i >> 4] = t;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const float tot = row_ss_total(tss, 1, D / 16);
+    if (tid == 0) s_inv = inv_rms(tot, D, eps);
+  }
+  __syncthreads();
+  const float inv = s_inv;
+  float part[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) part[j] = 0.f;
   for (int c = tid; c < D / 8; c += 256) {
@@ -1755,8 +1784,8 @@ __global__ __launch_bounds__(256) void specee_features_kernel(const float* __res
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      ss = fmaf(hr[i + e], hr[i + e], ss);
-      x[e] = BF ? bf2f(f2bf(hr[i + e] * gain[i + e])) : hr[i + e] * gain[i + e];
+      const float hg = __fmul_rn(hr[i + e], gain[i + e]);
+      x[e] = BF ? bf2f(norm_bf16(hg, inv)) : __fmul_rn(hg, inv);
     }
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
@@ -1768,22 +1797,19 @@ __global__ __launch_bounds__(256) void specee_features_kernel(const float* __res
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    ss += __shfl_xor(ss, o, 64);
 #pragma unroll
     for (int j = 0; j < KM; ++j) part[j] += __shfl_xor(part[j], o, 64);
   }
   if (lane == 0) {
-    red[wave][KM] = ss;
 #pragma unroll
     for (int j = 0; j < KM; ++j) red[wave][j] = part[j];
   }
   __syncthreads();
   if (tid == 0) {
-    const float inv = inv_rms(((red[0][KM] + red[1][KM]) + red[2][KM]) + red[3][KM], D, eps);
     float z[KM];
     float m = -INFINITY;
     for (int j = 0; j < k; ++j) {
-      z[j] = (((red[0][j] + red[1][j]) + red[2][j]) + red[3][j]) * inv;
+      z[j] = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
       m = fmaxf(m, z[j]);
     }
     float sum = 0.f;
@@ -1801,7 +1827,7 @@ __global__ __launch_bounds__(256) void specee_features_kernel(const float* __res
 int launch_specee_features(int dtype, const float* h, int rows, int D, float eps, const float* gain, const void* W,
                            int V, const int32_t* tokens, int k, const float* prev, float* out, hipStream_t s) {
   if (rows <= 0) return 0;
-  if (k < 1 || k > 16 || D % 8 != 0) return SSD_ERR_SHAPE;
+  if (k < 1 || k > 16 || D % 16 != 0 || D > 16384) return SSD_ERR_SHAPE;
   if (dtype == SSD_DTYPE_BF16)
     hipLaunchKernelGGL(specee_features_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, h, D, eps, gain,
                        (const bf16_t*)W, V, tokens, k, prev, out);
