@@ -23,9 +23,12 @@
  *
  * Conventions
  *   - Every pointer named *_dev is device memory of the GPU current when the
- *     object was created; the caller allocates and owns it (the library never
- *     allocates device memory).  *_host pointers are host memory, read during
- *     the call only.
+ *     object was created; the caller allocates and owns it.  No entry point of
+ *     this header allocates device memory; the library's own device memory is
+ *     the fixed scratch array of ssd_accept_noalloc (part of its code object)
+ *     and, only while profiling is enabled, the timing records of
+ *     ssd_profile_enable (ssd_profile.h).  *_host pointers are host memory,
+ *     read during the call only.
  *   - Weights are row-major [out_features, in_features] ("[N, K]"), in the
  *     model dtype (SSD_DTYPE_F32: float, SSD_DTYPE_BF16: bfloat16 bits).  Norm
  *     gains are float32.
@@ -241,6 +244,27 @@ int ssd_verify(ssd_seq* seq, const uint8_t* skip_mask_host, int exit_layer, int 
 int ssd_accept(ssd_seq* seq, const float* p_logits_dev, const float* q_logits_dev,
                const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, int d, float temperature,
                uint64_t seed, int32_t* out_tokens_dev, int32_t* n_out_dev, hipStream_t stream);
+
+/* Allocation-free acceptance, for callers that cannot allocate device memory
+ * or hand over a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the rule and the random draws of
+ * ssd_accept, without a sequence.  p_logits_dev [d + 1, vocab],
+ * q_logits_dev [d, vocab] (fp32, row-major), draft_tokens_dev [d] and
+ * n_drafted_dev[1] (d' in 1..d; values outside 0..d are clamped) are as in
+ * ssd_accept; iteration addresses the draws (a sequence's iteration counter
+ * reproduces ssd_accept's draws exactly).  Outputs: out_tokens_dev[d + 1]
+ * (first n_out valid), n_out_dev[1].
+ * Scratch: the per-row decisions and draws passed between the two kernels sit
+ * in a library-owned device array of 2 x (SSD_ACCEPT_NOALLOC_MAX_DRAFT + 1)
+ * int32 per GPU, created with the library's code object and held until the
+ * process ends; the call itself allocates nothing.  Every call on one GPU
+ * shares that array: calls that overlap on one GPU (e.g. on two streams) race
+ * and must be ordered by the caller.  d > SSD_ACCEPT_NOALLOC_MAX_DRAFT returns
+ * SSD_ERR_CAPACITY. */
+#define SSD_ACCEPT_NOALLOC_MAX_DRAFT 32
+int ssd_accept_noalloc(const float* p_logits_dev, const float* q_logits_dev, const int32_t* draft_tokens_dev,
+                       const int32_t* n_drafted_dev, int d, int vocab, float temperature, uint64_t seed,
+                       int32_t iteration, int32_t* out_tokens_dev, int32_t* n_out_dev, hipStream_t stream);
 
 /* Commit (row a5): appends out_tokens_dev[0..n_out-1] to the output log,
  * kvlen += n_out, last_token = the last emitted token, iteration += 1.  Keys and

@@ -16,7 +16,7 @@ ERROR_NAMES = {-1: "SSD_ERR_ARG", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_CAPACITY", -
 EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_packed_bf16_bytes", "ssd_pack_bf16", "ssd_kv_pool_bytes",
            "ssd_workspace_bytes", "ssd_seq_create",
            "ssd_seq_destroy", "ssd_prefill", "ssd_decode_ar", "ssd_decode_exit", "ssd_draft", "ssd_verify",
-           "ssd_accept", "ssd_commit", "ssd_tree_candidates", "ssd_verify_tree", "ssd_accept_tree",
+           "ssd_accept", "ssd_accept_noalloc", "ssd_commit", "ssd_tree_candidates", "ssd_verify_tree", "ssd_accept_tree",
            "ssd_score_masks", "ssd_uniform_mask", "ssd_swift_propose", "ssd_swift_search", "ssd_specee_features",
            "ssd_row_stats",
            "ssd_read_state", "ssd_read_output", "ssd_last_error",
@@ -83,6 +83,7 @@ def lib():
             "ssd_draft": [P, P, I, I, F, F, U64, P, P, P, P],
             "ssd_verify": [P, P, I, I, P, P, I, P, P],
             "ssd_accept": [P, P, P, P, P, I, F, U64, P, P, P],
+            "ssd_accept_noalloc": [P, P, P, P, I, I, F, U64, ctypes.c_int32, P, P, P],
             "ssd_commit": [P, P, P, P],
             "ssd_tree_candidates": [P, P, P, I, F, U64, F, I, I, P, P, P, P],
             "ssd_verify_tree": [P, P, I, I, P, P, P, P, P, I, I, P, P],
@@ -216,6 +217,12 @@ def ssd_accept(seq, p_logits, q_logits, draft_tokens, n_drafted, d, temperature,
                stream=None):
     check(lib().ssd_accept(seq, _ptr(p_logits), _ptr(q_logits), _ptr(draft_tokens), _ptr(n_drafted), d, temperature,
                            seed, _ptr(out_tokens), _ptr(n_out), _stream(stream)))
+
+
+def ssd_accept_noalloc(p_logits, q_logits, draft_tokens, n_drafted, d, vocab, temperature, seed, iteration,
+                       out_tokens, n_out, stream=None):
+    check(lib().ssd_accept_noalloc(_ptr(p_logits), _ptr(q_logits), _ptr(draft_tokens), _ptr(n_drafted), d, vocab,
+                                   temperature, seed, iteration, _ptr(out_tokens), _ptr(n_out), _stream(stream)))
 
 
 def ssd_commit(seq, out_tokens, n_out, stream=None):

@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssd.so")
-SOURCES = ["kernels.hip", "decode.hip", "tree.hip", "api.hip", "profile.hip"]
+SOURCES = ["kernels.hip", "decode.hip", "tree.hip", "api.hip", "profile.hip", "noalloc.hip"]
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

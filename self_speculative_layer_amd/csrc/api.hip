@@ -39,6 +39,8 @@ static int fail(int code, const std::string& msg) {
 
 extern "C" const char* ssd_last_error(void) { return g_err.c_str(); }
 
+int ssd::set_last_error(int code, const char* msg) { return fail(code, msg); }
+
 // ---------------------------------------------------------------------------
 // handles
 
@@ -656,7 +658,7 @@ extern "C" int ssd_accept(ssd_seq* q, const float* p_logits_dev, const float* q_
   CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
   CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
   TRY(launch_accept(p_logits_dev, q_logits_dev, q->m->d.vocab, draft_tokens_dev, n_drafted_dev, d_max, temperature,
-                    seed, q->w.st, q->w.dec, q->w.corr, out_tokens_dev, n_out_dev, s));
+                    seed, &q->w.st->iteration, 0, q->w.dec, q->w.corr, out_tokens_dev, n_out_dev, s));
   return SSD_OK;
 }
 

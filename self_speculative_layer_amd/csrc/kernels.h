@@ -8,6 +8,9 @@
 
 namespace ssd {
 
+// Records msg as the calling thread's last error (ssd_last_error) and returns code.
+int set_last_error(int code, const char* msg);
+
 // GEMM epilogues: Y = X . W^T then
 enum Epilogue {
   EPI_STORE = 0,    // Y[m, n] = acc                          (float)
@@ -94,8 +97,10 @@ int launch_row_stats_seg(const float* z, int ldz, int rows, int V, float T, uint
                          unsigned* ctr, const int* stop, const DraftStep& ds, hipStream_t s);
 
 
+// Accept / reject of a chain (d + 1 verify rows): dec, corr [d + 1] hold the per-row decisions and draws
+// between the two kernels; the draws are addressed by iteration *iter_ptr (or iter_const when null).
 int launch_accept(const float* zp, const float* zq, int V, const int32_t* drafts, const int32_t* n_drafted,
-                  int d, float T, uint64_t seed, const DevState* st, int* dec, int* corr,
+                  int d, float T, uint64_t seed, const int* iter_ptr, int iter_const, int* dec, int* corr,
                   int32_t* out_tokens, int32_t* n_out, hipStream_t s);
 
 int launch_commit(DevState* st, const int32_t* out_tokens, const int32_t* n_out, int32_t* log,

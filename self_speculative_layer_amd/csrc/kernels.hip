@@ -1271,10 +1271,11 @@ __device__ float block_lse(const float* z, int V, float T) {
 __global__ __launch_bounds__(1024) void accept_rows_kernel(const float* __restrict__ zp, const float* __restrict__ zq,
                                                            int V, const int32_t* __restrict__ drafts,
                                                            const int32_t* __restrict__ n_drafted, float T,
-                                                           uint64_t seed, const DevState* __restrict__ st,
-                                                           int* __restrict__ dec, int* __restrict__ corr) {
+                                                           uint64_t seed, const int* __restrict__ iter_ptr,
+                                                           int iter_const, int* __restrict__ dec,
+                                                           int* __restrict__ corr) {
   const int i = blockIdx.x;
-  const int dp = *n_drafted;
+  const int dp = min(max(*n_drafted, 0), (int)gridDim.x - 1);   // d' (the grid has d + 1 rows)
   if (i > dp) return;
   const float* p = zp + (size_t)i * V;
   const int tid = threadIdx.x;
@@ -1294,7 +1295,7 @@ __global__ __launch_bounds__(1024) void accept_rows_kernel(const float* __restri
     if (tid == 0) { corr[i] = am; dec[i] = (i < dp) && (am == drafts[i]); }
     return;
   }
-  const int iter = st->iteration;
+  const int iter = iter_ptr ? *iter_ptr : iter_const;
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const float lse_p = block_lse(p, V, T);
   float kbest = -INFINITY;
@@ -1354,11 +1355,11 @@ __global__ __launch_bounds__(1024) void accept_rows_kernel(const float* __restri
   }
 }
 
-__global__ void accept_emit_kernel(const int32_t* __restrict__ drafts, const int32_t* __restrict__ n_drafted,
+__global__ void accept_emit_kernel(const int32_t* __restrict__ drafts, const int32_t* __restrict__ n_drafted, int d,
                                    const int* __restrict__ dec, const int* __restrict__ corr,
                                    int32_t* __restrict__ out, int32_t* __restrict__ n_out) {
   if (threadIdx.x != 0) return;
-  const int dp = *n_drafted;
+  const int dp = min(max(*n_drafted, 0), d);
   int k = 0;
   while (k < dp && dec[k]) { out[k] = drafts[k]; ++k; }
   out[k] = corr[k];
@@ -1500,19 +1501,20 @@ int launch_tree_accept_sampled(const float* zp, const float* zq, int V, const in
                                const int32_t* n_drafted, int d, const int32_t* leaf_tok, const int32_t* leaf_depth,
                                const int32_t* n_leaves, int max_leaves, float T, uint64_t seed, DevState* st,
                                int* dec, int* corr, int32_t* out, int32_t* n_out, hipStream_t s) {
-  hipLaunchKernelGGL(accept_rows_kernel, dim3(d + 1), dim3(1024), 0, s, zp, zq, V, drafts, n_drafted, T, seed, st,
-                     dec, corr);
+  hipLaunchKernelGGL(accept_rows_kernel, dim3(d + 1), dim3(1024), 0, s, zp, zq, V, drafts, n_drafted, T, seed,
+                     &st->iteration, 0, dec, corr);
   hipLaunchKernelGGL(tree_accept_sampled_kernel, dim3(1), dim3(1024), 0, s, zp, zq, V, drafts, n_drafted, d, leaf_tok,
                      leaf_depth, n_leaves, max_leaves, T, seed, st, dec, corr, out, n_out);
   return last_launch();
 }
 
 int launch_accept(const float* zp, const float* zq, int V, const int32_t* drafts, const int32_t* n_drafted, int d,
-                  float T, uint64_t seed, const DevState* st, int* dec, int* corr, int32_t* out_tokens,
-                  int32_t* n_out, hipStream_t s) {
-  hipLaunchKernelGGL(accept_rows_kernel, dim3(d + 1), dim3(1024), 0, s, zp, zq, V, drafts, n_drafted, T, seed, st,
-                     dec, corr);
-  hipLaunchKernelGGL(accept_emit_kernel, dim3(1), dim3(64), 0, s, drafts, n_drafted, dec, corr, out_tokens, n_out);
+                  float T, uint64_t seed, const int* iter_ptr, int iter_const, int* dec, int* corr,
+                  int32_t* out_tokens, int32_t* n_out, hipStream_t s) {
+  hipLaunchKernelGGL(accept_rows_kernel, dim3(d + 1), dim3(1024), 0, s, zp, zq, V, drafts, n_drafted, T, seed,
+                     iter_ptr, iter_const, dec, corr);
+  hipLaunchKernelGGL(accept_emit_kernel, dim3(1), dim3(64), 0, s, drafts, n_drafted, d, dec, corr, out_tokens,
+                     n_out);
   return last_launch();
 }
 

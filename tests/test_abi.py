@@ -84,3 +84,19 @@ def test_null_arguments_are_errors():
     assert b"null" in lib.ssd_last_error()
     assert lib.ssd_draft(None, None, 1, 4, 0.0, 0.0, 0, None, None, None, None) == B.SSD_ERR_ARG
     assert lib.ssd_accept(None, None, None, None, None, 4, 0.0, 0, None, None, None) == B.SSD_ERR_ARG
+
+
+def test_accept_noalloc_rejects_bad_arguments_on_the_host():
+    """The allocation-free acceptance checks its arguments before touching the device: null pointers,
+    non-positive sizes and a bad temperature are SSD_ERR_ARG, a chain longer than its scratch array
+    SSD_ERR_CAPACITY."""
+    L = B.lib()
+    p = ctypes.c_void_p(0x1000)
+    args = lambda d=4, vocab=100, T=1.0, ptr=p: (ptr, p, p, p, d, vocab, T, 3, 1, p, p, None)
+    assert L.ssd_accept_noalloc(*args(ptr=None)) == B.SSD_ERR_ARG
+    assert L.ssd_accept_noalloc(*args(d=0)) == B.SSD_ERR_ARG
+    assert L.ssd_accept_noalloc(*args(vocab=0)) == B.SSD_ERR_ARG
+    assert L.ssd_accept_noalloc(*args(T=-1.0)) == B.SSD_ERR_ARG
+    assert L.ssd_accept_noalloc(*args(T=float("nan"))) == B.SSD_ERR_ARG
+    assert L.ssd_accept_noalloc(*args(d=33)) == B.SSD_ERR_CAPACITY
+    assert b"SSD_ACCEPT_NOALLOC_MAX_DRAFT" in L.ssd_last_error()
