@@ -349,14 +349,16 @@ int ssd_accept_tree(ssd_seq* seq, const float* logits_dev, const float* q_logits
  * the candidate's own keys/values at the window positions (kept in the
  * workspace; the cache is not modified); row i predicts argmax of its logits.
  * scores_dev[c] = #(prediction i == window[i+1]) / gamma; best_dev[0] = the
- * highest-scoring candidate (lowest index on ties).
+ * highest-scoring candidate (lowest index on ties); row_pred_dev (nullable)
+ * [n_masks * gamma] receives each row's prediction (candidate-major).
  * Requires n_masks * gamma <= max_rows. */
 int ssd_score_masks(ssd_seq* seq, const uint8_t* masks_host, int n_masks, const int32_t* window_dev,
-                    int pos0, int gamma, float* scores_dev, int32_t* best_dev, hipStream_t stream);
+                    int pos0, int gamma, float* scores_dev, int32_t* best_dev, int32_t* row_pred_dev,
+                    hipStream_t stream);
 
 /* ---- SWIFT layer-set search (next row f1; [SWIFT] §1, §4.1.1, §4.1.2, §5.3, §B.2) ----
  * The pages' optimisation phase proposes candidate layer sets by random search
- * (with a periodic Bayesian step, not implemented here), scores them by
+ * (with a periodic Bayesian step: bo_every below), scores them by
  * matchness on the last context window and keeps the best, stopping at a step
  * limit, after a run of steps without improvement, or above a matchness target.
  * Readings: candidates skip n_skip whole layers (both bits of a layer) or, with

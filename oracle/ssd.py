@@ -39,18 +39,39 @@ def race_sample(keys_f32):
     return argmax_lowest(keys_f32)
 
 
-def sample_logits(z, T, seed, it, row, purpose):
+def top2_gap(keys):
+    """How far a maximum-taking decision is from flipping: the largest key minus
+    the second largest (inf with a single finite key).  For race keys this is the
+    log-gap of the two best candidates; for logits, the top-2 margin."""
+    k = np.sort(np.asarray(keys, np.float64).ravel())
+    if k.size < 2 or not np.isfinite(k[-2]):
+        return float("inf")
+    return float(k[-1] - k[-2])
+
+
+def _log(log, kind, row, margin):
+    if log is not None:
+        log.append((kind, int(row), float(margin)))
+
+
+def sample_logits(z, T, seed, it, row, purpose, log=None, kind="sample"):
     """Sample from softmax(z / T) by the race over float32 keys z/T + Gumbel."""
     g = philox.gumbel(seed, it, row, purpose, z.shape[-1])
     keys = (np.asarray(z, np.float64) / T).astype(np.float32) + g
+    _log(log, kind, row, top2_gap(keys))
     return race_sample(keys)
 
 
-def pick(z, T, seed, it, row, purpose):
-    """Greedy argmax at T == 0, otherwise a sample from softmax(z / T)."""
+def pick(z, T, seed, it, row, purpose, log=None, kind="sample"):
+    """Greedy argmax at T == 0, otherwise a sample from softmax(z / T).
+
+    log (optional list): receives (kind, row, margin) for the decision, the
+    margin being how far it is from flipping (top-2 logit gap when greedy,
+    top-2 race-key gap when sampling)."""
     if T == 0:
+        _log(log, kind, row, top2_gap(z))
         return argmax_lowest(z)
-    return sample_logits(z, T, seed, it, row, purpose)
+    return sample_logits(z, T, seed, it, row, purpose, log, kind)
 
 
 def log_softmax(z, T):
@@ -86,17 +107,19 @@ def accept_greedy(p_logits, drafts):
     return [int(t) for t in drafts[:k]] + [argmax_lowest(p_logits[k])]
 
 
-def accept_sampled(p_logits, q_logits, drafts, T, seed, it):
+def accept_sampled(p_logits, q_logits, drafts, T, seed, it, log=None):
     """T > 0 accept/reject (LayerSkip blog §3.3): for i = 1..d', accept y_i when
     u_i * q_i(y_i) < p_i(y_i) (probability min(1, p/q)); at the first rejection
     emit a sample of norm(max(0, p_i - q_i)); if all are accepted, emit a bonus
-    sample of p_{d'+1}.  Decisions are taken on float32 quantities."""
+    sample of p_{d'+1}.  Decisions are taken on float32 quantities.  log: as in
+    pick; an accept decision's margin is |ln(u q(y) / p(y))|."""
     dp = len(drafts)
     for i in range(dp):
         y = int(drafts[i])
         lp = log_softmax(p_logits[i], T).astype(np.float32)
         lq = log_softmax(q_logits[i], T).astype(np.float32)
         u = philox.uniforms(seed, it, i, philox.PURPOSE_ACCEPT, 1)[0]
+        _log(log, "accept", i, abs(float(np.log(u) + lq[y]) - float(lp[y])))
         if np.log(u) + lq[y] < lp[y]:
             continue
         p32 = np.exp(lp)
@@ -108,8 +131,9 @@ def accept_sampled(p_logits, q_logits, drafts, T, seed, it):
                 keys = np.log(r) + g
         else:
             keys = lp + g
+        _log(log, "sample", i, top2_gap(keys))
         return [int(t) for t in drafts[:i]] + [race_sample(keys)]
-    return [int(t) for t in drafts] + [sample_logits(p_logits[dp], T, seed, it, dp, philox.PURPOSE_SAMPLE)]
+    return [int(t) for t in drafts] + [sample_logits(p_logits[dp], T, seed, it, dp, philox.PURPOSE_SAMPLE, log)]
 
 
 # --------------------------------------------------------------------------
@@ -122,13 +146,15 @@ def prefill(model, kv, prompt):
     return z[-1]
 
 
-def draft(model, kv, y0, n, mask, d, tau, T, seed, it):
+def draft(model, kv, y0, n, mask, d, tau, T, seed, it, log=None):
     """Draft phase (LayerSkip blog §3.1; SWIFT digest §3.1, §4.2).
 
     Feeds y0 at position n-1, then each new draft token at the next position,
     through the sub-layers the plan keeps, the shared final norm and LM head.
     Stops after step j when confidence < tau (or at j = d).  Returns
     (drafts, draft logits [d', V], hidden states entering layer b [d', D]).
+    log: as in pick (kind "draft"), plus each confidence-stop decision (kind
+    "stop", margin |ln conf - ln tau|) when tau > 0.
     """
     b = mdl.first_skipped_layer(mask, model.L)
     drafts, zs, hb = [], [], []
@@ -140,10 +166,13 @@ def draft(model, kv, y0, n, mask, d, tau, T, seed, it):
         hb.append(h[0].copy())
         h = mdl.run_layers(model, h, pos, kv, mask, b, model.L)
         z = mdl.final_logits(model, h)[0]
-        y = pick(z, T, seed, it, j - 1, philox.PURPOSE_DRAFT)
+        y = pick(z, T, seed, it, j - 1, philox.PURPOSE_DRAFT, log, "draft")
         drafts.append(y)
         zs.append(z)
-        if np.float32(confidence(z, T)) < np.float32(tau):
+        conf = np.float32(confidence(z, T))
+        if tau > 0:
+            _log(log, "stop", j - 1, abs(np.log(float(conf)) - np.log(float(np.float32(tau)))))
+        if conf < np.float32(tau):
             break
     return drafts, np.array(zs), np.array(hb)
 
@@ -213,26 +242,31 @@ def exit_generate(model, prompt, n_gen, mask, T=0.0, seed=3, capacity=None):
 def ssd_generate(model, prompt, n_gen, mask, d, tau=0.0, T=0.0, seed=3, reuse=True, capacity=None,
                  on_iteration=None):
     """Self-speculative decoding loop (LayerSkip blog §3.3): draft, verify, accept,
-    append the emitted tokens; output truncated to exactly n_gen tokens."""
+    append the emitted tokens; output truncated to exactly n_gen tokens.
+    stats["decisions"][k]: the (kind, row, margin) log of iteration k (0: the
+    prefill's token) at T > 0."""
     P = len(prompt)
     L = model.L
     b = mdl.first_skipped_layer(mask, L)
     kv = mdl.KVCache(model.shape, capacity or (P + n_gen + d + 2))
-    out = [pick(prefill(model, kv, prompt), T, seed, 0, 0, philox.PURPOSE_SAMPLE)]
-    stats = {"drafted": [], "accepted": [], "emitted": []}
+    log0 = []
+    out = [pick(prefill(model, kv, prompt), T, seed, 0, 0, philox.PURPOSE_SAMPLE, log0)]
+    stats = {"drafted": [], "accepted": [], "emitted": [], "decisions": [log0]}
     it = 1
     while len(out) < n_gen:
         n = P + len(out)
         y0 = out[-1]
-        drafts, zq, hb = draft(model, kv, y0, n, mask, d, tau, T, seed, it)
+        log = []
+        drafts, zq, hb = draft(model, kv, y0, n, mask, d, tau, T, seed, it, log)
         zp = verify(model, kv, y0, drafts, n, b, hb if reuse else None)
         if T == 0:
             emitted = accept_greedy(zp, drafts)
         else:
-            emitted = accept_sampled(zp, zq, drafts, T, seed, it)
+            emitted = accept_sampled(zp, zq, drafts, T, seed, it, log)
         stats["drafted"].append(len(drafts))
         stats["accepted"].append(len(emitted) - 1)
         stats["emitted"].append(len(emitted))
+        stats["decisions"].append(log)
         if on_iteration is not None:
             on_iteration(it, n, drafts, zq, zp, emitted, kv)
         out.extend(emitted)
@@ -240,7 +274,7 @@ def ssd_generate(model, prompt, n_gen, mask, d, tau=0.0, T=0.0, seed=3, reuse=Tr
     return out[:n_gen], stats, kv
 
 
-def score_masks(model, kv, window, pos0, masks):
+def score_masks(model, kv, window, pos0, masks, detail=False):
     """SWIFT matchness scoring (SWIFT digest §4.1, §4.1.2, §5.3).
 
     window = gamma+1 committed tokens at positions pos0..pos0+gamma; the cache
@@ -249,19 +283,24 @@ def score_masks(model, kv, window, pos0, masks):
     keys/values at the window positions, the full model's before them) and
     predicts every next token by argmax; its score is the fraction of rows whose
     prediction equals window[i+1].  Returns (scores, index of the best plan,
-    lowest index on ties).
+    lowest index on ties), and with detail=True also each row's prediction and
+    its top-2 logit margin ([n_masks, gamma] each).
     """
     gamma = len(window) - 1
     rows = [int(t) for t in window[:-1]]
     targets = np.asarray(window[1:], dtype=np.int64)
     positions = list(range(pos0, pos0 + gamma))
-    scores = []
+    scores, preds, margins = [], [], []
     for mask in masks:
         kvm = kv.copy()
         z = mdl.forward(model, rows, positions, kvm, mask)
         pred = np.array([argmax_lowest(r) for r in z])
         scores.append(float(np.sum(pred == targets)) / gamma)
+        preds.append(pred)
+        margins.append([top2_gap(r) for r in z])
     scores = np.array(scores)
+    if detail:
+        return scores, int(np.argmax(scores)), np.array(preds), np.array(margins)
     return scores, int(np.argmax(scores))
 
 

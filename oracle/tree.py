@@ -87,24 +87,30 @@ def tree_leaves(zq, drafts, rho, k_max, budget):
     return leaves
 
 
-def tree_leaves_sampled(zq, drafts, T, rho, k_max, budget, seed, it):
+def tree_leaves_sampled(zq, drafts, T, rho, k_max, budget, seed, it, log=None):
     """R5: leaves (depth j, token) of a sampled draft, in depth order then draw
-    order, at most `budget`: k_j - 1 independent draws from softmax(zq[j-1] / T)."""
+    order, at most `budget`: k_j - 1 independent draws from softmax(zq[j-1] / T).
+    log: as ssd.pick, each draw logged at row j - 1 (kind "leaf")."""
     leaves = []
     for j in range(1, len(drafts) + 1):
         k = candidate_count(zq[j - 1], rho, k_max, T)
         for r in range(1, k):
             if len(leaves) < budget:
                 t = ssd.sample_logits(zq[j - 1], T, seed, it, (j - 1) + ROW_STRIDE * r, PURPOSE_LEAF)
+                if log is not None:
+                    g = philox.gumbel(seed, it, (j - 1) + ROW_STRIDE * r, PURPOSE_LEAF, zq.shape[-1])
+                    keys = (np.asarray(zq[j - 1], np.float64) / T).astype(np.float32) + g
+                    log.append(("leaf", j - 1, ssd.top2_gap(keys)))
                 leaves.append((j, t))
     return leaves
 
 
-def accept_tree_sampled(zp, zq, zl, drafts, leaves, T, seed, it):
+def accept_tree_sampled(zp, zq, zl, drafts, leaves, T, seed, it, log=None):
     """R5: (emitted tokens, index of the accepted leaf or None).  Decisions on
     float32 quantities, as ssd.accept_sampled; the final draw at a depth uses the
     last nonzero max(0, p' - q) unnormalised (log p when there was none), so that
-    a depth without leaves draws exactly as the chain rule."""
+    a depth without leaves draws exactly as the chain rule.  log: as
+    ssd.accept_sampled, every decision at depth j logged at row j - 1."""
     dp = len(drafts)
     for j in range(1, dp + 1):
         lp = ssd.log_softmax(zp[j - 1], T).astype(np.float32)
@@ -117,11 +123,17 @@ def accept_tree_sampled(zp, zq, zl, drafts, leaves, T, seed, it):
         for i, (c, s) in enumerate(cands):
             u = philox.uniforms(seed, it, (j - 1) + ROW_STRIDE * i, philox.PURPOSE_ACCEPT, 1)[0]
             lpc = lp[c] if last_r is None else (np.log(cur[c]) if cur[c] > 0 else -np.inf)
+            if log is not None:
+                log.append(("accept", j - 1, abs(float(np.log(u) + lq[c]) - float(lpc))))
             if np.log(u) + lq[c] < lpc:
                 if s is None:
                     accepted = True           # the chain goes on
                     break
                 bonus = ssd.sample_logits(zl[s], T, seed, it, (j - 1) + ROW_STRIDE * i, philox.PURPOSE_SAMPLE)
+                if log is not None:
+                    g = philox.gumbel(seed, it, (j - 1) + ROW_STRIDE * i, philox.PURPOSE_SAMPLE, zl.shape[-1])
+                    log.append(("sample", j - 1, ssd.top2_gap((np.asarray(zl[s], np.float64) / T).astype(np.float32)
+                                                             + g)))
                 return [int(t) for t in drafts[: j - 1]] + [c, bonus], s
             r = np.maximum(np.float32(0), cur - q32)
             tot = np.float32(r.sum(dtype=np.float64))
@@ -136,8 +148,10 @@ def accept_tree_sampled(zp, zq, zl, drafts, leaves, T, seed, it):
         else:
             with np.errstate(divide="ignore"):
                 keys = np.log(last_r) + g
+        if log is not None:
+            log.append(("sample", j - 1, ssd.top2_gap(keys)))
         return [int(t) for t in drafts[: j - 1]] + [ssd.race_sample(keys)], None
-    return [int(t) for t in drafts] + [ssd.sample_logits(zp[dp], T, seed, it, dp, philox.PURPOSE_SAMPLE)], None
+    return [int(t) for t in drafts] + [ssd.sample_logits(zp[dp], T, seed, it, dp, philox.PURPOSE_SAMPLE, log)], None
 
 
 def verify_tree(model, kv, y0, drafts, leaves, n, b, hb=None):
@@ -181,22 +195,25 @@ def tree_generate(model, prompt, n_gen, mask, d, rho, k_max, budget, tau=0.0, re
     P = len(prompt)
     b = mdl.first_skipped_layer(mask, model.L)
     kv = mdl.KVCache(model.shape, capacity or (P + n_gen + d + 2))
-    out = [ssd.pick(ssd.prefill(model, kv, prompt), T, seed, 0, 0, philox.PURPOSE_SAMPLE)]
-    stats = {"drafted": [], "leaves": [], "emitted": [], "leaf_accepted": []}
+    log0 = []
+    out = [ssd.pick(ssd.prefill(model, kv, prompt), T, seed, 0, 0, philox.PURPOSE_SAMPLE, log0)]
+    stats = {"drafted": [], "leaves": [], "emitted": [], "leaf_accepted": [], "decisions": [log0]}
     it = 1
     while len(out) < n_gen:
         n = P + len(out)
         y0 = out[-1]
-        drafts, zq, hb = ssd.draft(model, kv, y0, n, mask, d, tau, T, seed, it)
+        log = []
+        drafts, zq, hb = ssd.draft(model, kv, y0, n, mask, d, tau, T, seed, it, log)
         if T == 0:
             leaves = tree_leaves(zq, drafts, rho, k_max, budget)
         else:
-            leaves = tree_leaves_sampled(zq, drafts, T, rho, k_max, budget, seed, it)
+            leaves = tree_leaves_sampled(zq, drafts, T, rho, k_max, budget, seed, it, log)
         zp, zl = verify_tree(model, kv, y0, drafts, leaves, n, b, hb if reuse else None)
         if T == 0:
             emitted, s = accept_tree_greedy(zp, zl, drafts, leaves)
         else:
-            emitted, s = accept_tree_sampled(zp, zq, zl, drafts, leaves, T, seed, it)
+            emitted, s = accept_tree_sampled(zp, zq, zl, drafts, leaves, T, seed, it, log)
+        stats["decisions"].append(log)
         if s is not None:
             j, c = leaves[s]
             path = [int(y0)] + [int(t) for t in drafts[: j - 1]] + [int(c)]

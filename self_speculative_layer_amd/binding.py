@@ -88,7 +88,7 @@ def lib():
             "ssd_tree_candidates": [P, P, P, I, F, U64, F, I, I, P, P, P, P],
             "ssd_verify_tree": [P, P, I, I, P, P, P, P, P, I, I, P, P],
             "ssd_accept_tree": [P, P, P, P, P, I, P, P, P, I, F, U64, P, P, P],
-            "ssd_score_masks": [P, P, I, P, I, I, P, P, P],
+            "ssd_score_masks": [P, P, I, P, I, I, P, P, P, P],
             "ssd_uniform_mask": [I, I, P],
             "ssd_specee_features": [P, P, I, P, I, P, P, P],
             "ssd_swift_propose": [I, I, I, U64, I, I, P],
@@ -251,11 +251,11 @@ def ssd_accept_tree(seq, logits, draft_tokens, n_drafted, d, leaf_tokens, leaf_d
                                 _ptr(out_tokens), _ptr(n_out), _stream(stream)))
 
 
-def ssd_score_masks(seq, masks, window, pos0, gamma, scores, best, stream=None):
+def ssd_score_masks(seq, masks, window, pos0, gamma, scores, best, row_pred=None, stream=None):
     import numpy as np
     m = np.ascontiguousarray(np.asarray(masks, dtype=np.uint8))
     check(lib().ssd_score_masks(seq, m.ctypes.data_as(ctypes.c_void_p), m.shape[0], _ptr(window), pos0, gamma,
-                                _ptr(scores), _ptr(best), _stream(stream)))
+                                _ptr(scores), _ptr(best), _ptr(row_pred), _stream(stream)))
 
 
 def ssd_uniform_mask(n_layers, n_skip):

@@ -767,7 +767,8 @@ extern "C" int ssd_accept_tree(ssd_seq* q, const float* logits_dev, const float*
 // SWIFT matchness scoring
 
 extern "C" int ssd_score_masks(ssd_seq* q, const uint8_t* masks_host, int n_masks, const int32_t* window_dev,
-                               int pos0, int gamma, float* scores_dev, int32_t* best_dev, hipStream_t s) {
+                               int pos0, int gamma, float* scores_dev, int32_t* best_dev, int32_t* row_pred_dev,
+                               hipStream_t s) {
   CHECK_ARG(q && masks_host && window_dev && scores_dev && best_dev, "null argument");
   CHECK_ARG(n_masks >= 1 && gamma >= 1, "empty scoring problem");
   CHECK_ARG(pos0 >= 0, "negative pos0");
@@ -805,7 +806,7 @@ extern "C" int ssd_score_masks(ssd_seq* q, const uint8_t* masks_host, int n_mask
   TRY(final_logits(q, w.h, R, nullptr, w.logits_rows, nullptr, s));
   TRY(launch_row_stats_seg(w.logits_rows, d.vocab, R, d.vocab, 0.f, 0, nullptr, 0, 0, PURPOSE_DRAFT, w.stats,
                            w.stat_recs, w.stat_ctr, nullptr, DraftStep{}, s));
-  TRY(launch_score(w.stats, window_dev, n_masks, gamma, scores_dev, best_dev, s));
+  TRY(launch_score(w.stats, window_dev, n_masks, gamma, scores_dev, best_dev, row_pred_dev, s));
   // the host row lists must outlive the copy
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(SSD_ERR_HIP, "stream sync");
@@ -987,7 +988,8 @@ extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0,
     if (!bo)
       for (int c = 0; c < n_cand; ++c) propose_layers(L, n_skip, sublayers, seed, t, c, masks.data() + (off + c) * ML);
     const int nm = n_cand + off;
-    TRY(ssd_score_masks(q, masks.data(), nm, window_dev, pos0, gamma, q->w.swift_scores, q->w.swift_best, s));
+    TRY(ssd_score_masks(q, masks.data(), nm, window_dev, pos0, gamma, q->w.swift_scores, q->w.swift_best, nullptr,
+                        s));
     if (hipMemcpy(sc.data(), q->w.swift_scores, sizeof(float) * nm, hipMemcpyDeviceToHost) != hipSuccess)
       return fail(SSD_ERR_HIP, "read scores");
     if (t == 0) inc_score = sc[0];

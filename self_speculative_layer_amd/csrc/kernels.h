@@ -128,7 +128,7 @@ int launch_copy_rows(const float* src, float* dst, int rows, int D, const int* c
 int launch_specee_features(int dtype, const float* h, int rows, int D, float eps, const float* gain, const void* W,
                            int V, const int32_t* tokens, int k, const float* prev, float* out, hipStream_t s);
 int launch_score(const ssd_row_stat* stats, const int32_t* window, int n_masks, int gamma, float* scores,
-                 int32_t* best, hipStream_t s);
+                 int32_t* best, int32_t* row_pred, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Draft trees (tree.hip).

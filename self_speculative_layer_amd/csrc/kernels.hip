@@ -1722,12 +1722,17 @@ int launch_pack_bf16(const void* src, void* dst, int N, int K, hipStream_t s) {
 // Matchness: per candidate the fraction of rows whose argmax equals the next
 // window token; best = highest score, lowest index on ties.
 __global__ void score_kernel(const ssd_row_stat* __restrict__ stats, const int32_t* __restrict__ window,
-                             int n_masks, int gamma, float* __restrict__ scores, int32_t* __restrict__ best) {
+                             int n_masks, int gamma, float* __restrict__ scores, int32_t* __restrict__ best,
+                             int32_t* __restrict__ row_pred) {
   __shared__ int hits[1024];
   const int c = threadIdx.x;
   if (c < n_masks) {
     int h = 0;
-    for (int i = 0; i < gamma; ++i) h += stats[c * gamma + i].argmax == window[i + 1];
+    for (int i = 0; i < gamma; ++i) {
+      const int pr = stats[c * gamma + i].argmax;
+      h += pr == window[i + 1];
+      if (row_pred) row_pred[c * gamma + i] = pr;
+    }
     hits[c] = h;
     scores[c] = (float)h / (float)gamma;
   }
@@ -1840,9 +1845,10 @@ int launch_specee_features(int dtype, const float* h, int rows, int D, float eps
 }
 
 int launch_score(const ssd_row_stat* stats, const int32_t* window, int n_masks, int gamma, float* scores,
-                 int32_t* best, hipStream_t s) {
+                 int32_t* best, int32_t* row_pred, hipStream_t s) {
   if (n_masks > 1024) return SSD_ERR_CAPACITY;
-  hipLaunchKernelGGL(score_kernel, dim3(1), dim3(1024), 0, s, stats, window, n_masks, gamma, scores, best);
+  hipLaunchKernelGGL(score_kernel, dim3(1), dim3(1024), 0, s, stats, window, n_masks, gamma, scores, best,
+                     row_pred);
   return last_launch();
 }
 

@@ -1,12 +1,13 @@
 """Full-size parity: the 32-layer LLaMA-2-7B-shaped model of the bench, in the
 bench's launch configuration (512-token prompt, exit at layer 8, d = 12,
-greedy).  At this size the oracle cannot follow a 512-token context in seconds,
-so the checks are (a) properties of the path that hold at any size — greedy
+greedy).  Checked (a) as properties of the path that hold at any size — greedy
 SSD tokens equal AR tokens, the verify with the draft's saved state equals the
 verify that recomputes every row, a decode step equals the last row of a
-prefill, all bit for bit — and (b) sampled outputs the oracle computes one by
-one: the logits of the first four generated tokens after an 8-token prompt,
-against the float64 oracle at full width and depth."""
+prefill, all bit for bit — and (b) against the float64 oracle at full width and
+depth: the first token's logits and every draft and verify row of two SSD
+iterations after the 512-token prompt (beside the oracle's float32-accumulation
+twin on the same rows), 64 generated tokens against the oracle's greedy AR
+tokens, and the logits of the first four tokens after an 8-token prompt."""
 import numpy as np
 import pytest
 import torch
@@ -73,6 +74,117 @@ def test_fullsize_bench_config_properties(model7b):
     seq.close()
     assert t == ar[1]
     assert torch.equal(lg, lg2)
+
+
+def _rel_rows(a, b):
+    """Per row: max |a - b| / max |b|."""
+    a, b = np.atleast_2d(a), np.atleast_2d(b)
+    return np.abs(a - b).max(axis=1) / np.abs(b).max(axis=1)
+
+
+def test_fullsize_bench_prompt_parity(model7b):
+    """The bench configuration itself (512-token prompt, exit 8, d = 12, greedy) against the float64
+    oracle: the first token's logits and every draft and verify row of the first two SSD iterations, row
+    by row, beside the same rows of the oracle's float32-accumulation twin (same rounding points; its
+    drift from the oracle is what accumulation order alone does at this depth); then 64 generated tokens
+    against the oracle's greedy AR tokens with re-synchronisation at near-ties."""
+    from gpu_util import acc32_twin, check_greedy_with_resync
+    from oracle import ssd as ossd
+    g = model7b
+    P, d, E, n_iter, n_gen = 512, 12, 8, 2, 64
+    V = SHAPE.vocab
+    prompt = synth.prompt_tokens(P, V)
+    mask = synth.mask_exit(SHAPE.n_layers, E)
+    print("[gpu] full-size 7B, 512-token prompt: float64 oracle prefill", flush=True)
+    o = omodel.Model.synthetic(SHAPE)
+    kv = omodel.KVCache(SHAPE, P + n_gen + 2 * d + 4)
+    z0 = ossd.prefill(o, kv, prompt)
+    kv_ar = kv.copy()
+    out = [int(np.argmax(z0))]
+    iters = []                                     # (y0, n, drafts, zq, zp)
+    for it in range(1, n_iter + 1):
+        n = P + len(out)
+        y0 = out[-1]
+        drafts, zq, hb = ossd.draft(o, kv, y0, n, mask, d, 0.0, 0.0, 0, it)
+        zp = ossd.verify(o, kv, y0, drafts, n, E, hb)
+        iters.append((y0, n, drafts, zq, zp))
+        out += ossd.accept_greedy(zp, drafts)
+        print("[gpu]   oracle iteration %d: %d drafts, emitted %d" % (it, len(drafts), len(out) - 1), flush=True)
+    # the twin on the same rows (teacher-forced with the oracle's tokens)
+    print("[gpu] float32-accumulation twin", flush=True)
+    tw = acc32_twin(o)
+    kvt = omodel.KVCache(SHAPE, P + n_gen + 2 * d + 4)
+    tw_rows = [ossd.prefill(tw, kvt, prompt)[None]]
+    for y0, n, drafts, zq, zp in iters:
+        pos = list(range(n - 1, n - 1 + len(drafts) + 1))
+        tw_rows.append(omodel.forward(tw, [y0] + drafts[:-1], pos[:-1], kvt.copy(), mask))
+        tw_rows.append(omodel.forward(tw, [y0] + drafts, pos, kvt))
+    del tw, kvt
+    # the GPU path on the same steps
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 16, max_rows=64, max_draft=d)
+    lg0 = torch.zeros(V, dtype=torch.float32, device="cuda")
+    B.ssd_prefill(seq.handle, dev(prompt), 0.0, 0, lg0)
+    gpu_rows = [lg0.cpu().numpy()[None]]
+    ref_rows = [z0[None]]
+    tw_cmp = [tw_rows[0]]
+    same_path = True
+    for k_it, (y0, n, drafts, zq, zp) in enumerate(iters):
+        seq.ssd_iteration(None, E, d)
+        st = B.ssd_read_state(seq.handle)
+        assert st.error_flags == 0
+        dp = st.last_n_drafted
+        gd = seq.draft_tokens[:dp].cpu().numpy().tolist()
+        gq = seq.draft_logits[: dp * V].view(dp, V).cpu().numpy()
+        if gd != list(drafts):
+            # a draft token differs: only at an oracle near-tie; rows up to it saw the same inputs
+            i = next(j for j, (a, b) in enumerate(zip(gd, drafts)) if a != b)
+            assert np.sort(zq[i])[-1] - np.sort(zq[i])[-2] < 1e-2, "draft %d differs away from a near-tie" % i
+            gpu_rows.append(gq[: i + 1])
+            ref_rows.append(zq[: i + 1])
+            tw_cmp.append(tw_rows[1 + 2 * k_it][: i + 1])
+            same_path = False
+            break
+        gpu_rows += [gq, seq.verify_logits[: (dp + 1) * V].view(dp + 1, V).cpu().numpy()]
+        ref_rows += [zq, zp]
+        tw_cmp += [tw_rows[1 + 2 * k_it], tw_rows[2 + 2 * k_it]]
+    seq.close()
+    g_rel = np.concatenate([_rel_rows(a, b) for a, b in zip(gpu_rows, ref_rows)])
+    t_rel = np.concatenate([_rel_rows(a, b) for a, b in zip(tw_cmp, ref_rows)])
+    g_abs = np.concatenate([np.abs(np.atleast_2d(a) - np.atleast_2d(b)).max(axis=1) for a, b in zip(gpu_rows, ref_rows)])
+    q = lambda x: "median %.3g p90 %.3g max %.3g" % (np.median(x), np.quantile(x, 0.9), x.max())
+    print("rows compared: %d (same draft path: %s)" % (len(g_rel), same_path))
+    print("GPU  - oracle, max|dz| / max|z| per row: %s" % q(g_rel))
+    print("twin - oracle, max|dz| / max|z| per row: %s" % q(t_rel))
+    print("GPU  - oracle, max|dz| absolute per row: %s (max|z| %.3g)" % (q(g_abs), np.abs(z0).max()))
+    assert len(g_rel) >= 2
+    # the GPU accumulates in float32 in a different order from the twin (and keeps its softmax, attention
+    # and RoPE table in float32): its drift is bounded by 1.5 times the twin's, row set against row set
+    # (measured: median 1.08x, max 1.15x)
+    assert np.median(g_rel) <= 1.5 * np.median(t_rel)
+    assert g_rel.max() <= 1.5 * t_rel.max()
+    # how far an implementation as accurate as the twin can move the difference of two logits: twice its
+    # largest per-logit drift on these rows.  A greedy token may differ from the oracle's only where the
+    # oracle puts the two tokens closer than that (the 1e-2 margin holds at two layers, not at 32: the
+    # twin itself drifts by about 0.1 per logit here)
+    t_abs = np.concatenate([np.abs(np.atleast_2d(a) - np.atleast_2d(b)).max(axis=1) for a, b in zip(tw_cmp, ref_rows)])
+    near = 2.0 * t_abs.max()
+    print("token excuse margin from the twin: %.3g" % near)
+    # 64 tokens: the GPU's SSD loop against the oracle's greedy AR
+    print("[gpu] oracle greedy AR, %d tokens" % n_gen, flush=True)
+    ref, ref_z = [out[0]], [z0]
+    while len(ref) < n_gen:
+        z = omodel.forward(o, [ref[-1]], [P + len(ref) - 1], kv_ar)[0]
+        ref.append(int(np.argmax(z)))
+        ref_z.append(z)
+        if len(ref) % 16 == 0:
+            print("[gpu]   %d tokens" % len(ref), flush=True)
+    del o
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 16, max_rows=64, max_draft=d)
+    events = check_greedy_with_resync(lambda pre, n: seq.generate_ssd(dev(pre), n, exit_layer=E, d=d)[0], prompt,
+                                      ref, np.array(ref_z), margin=near, max_events=n_gen // 4)
+    seq.close()
+    print("64 greedy SSD tokens: %d re-synchronisations where the oracle puts the two tokens within %.3g" %
+          (events, near))
 
 
 def test_fullsize_logits_match_oracle(model7b):

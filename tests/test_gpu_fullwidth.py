@@ -18,16 +18,9 @@ from self_speculative_layer_amd import binding as B
 from oracle import model as omodel
 from oracle import ssd as ossd
 
-from gpu_util import dev, gpu_model
+from gpu_util import acc32_twin, dev, gpu_model, max_abs_rows, teacher_rows
 
 pytestmark = pytest.mark.gpu
-
-# Logit error bound relative to the largest logit magnitude of the compared rows.  bf16 storage makes
-# the decoder sensitive to the accumulation precision before each rounding: the oracle with its
-# matrix products accumulated in float32 instead of float64 (same rounding points) already differs
-# from itself by up to 0.47% of max|z| at 7B width over two layers; the bound is 2^-6 (1.56%).
-REL_TOL = 2.0 ** -6
-
 
 def two_layer(shape):
     return dataclasses.replace(shape, name=shape.name + "-2l", n_layers=2)
@@ -59,37 +52,48 @@ def _mask(shape, plan):
 
 
 def test_fullwidth_iterations_match_oracle(case):
+    """Each iteration's draft and verify logits against the oracle, row by row, beside the oracle's
+    float32-accumulation twin on the same rows: the GPU's drift from the oracle is bounded by 1.5 times the
+    twin's (what accumulation in float32 alone does at this width), and reported in absolute terms against
+    the 2e-2 bf16 target."""
     shape, P, d, plan, g, o = case
     n_iter = 2
     prompt = synth.prompt_tokens(P, shape.vocab)
+    mask = _mask(shape, plan)
     records = []
-    ossd.ssd_generate(o, prompt, 1 + n_iter, _mask(shape, plan), d,
-                      on_iteration=lambda it, n, dr, zq, zp, em, kv: records.append((list(dr), zq, zp, em)))
+    ossd.ssd_generate(o, prompt, 1 + n_iter, mask, d,
+                      on_iteration=lambda it, n, dr, zq, zp, em, kv: records.append((n, list(dr), zq, zp, em)))
     seq = B.Sequence(g, max_ctx=P + 4 * d + 16, max_rows=64, max_draft=d)
     B.ssd_prefill(seq.handle, dev(prompt))
     V = shape.vocab
-    worst, compared = 0.0, 0
-    for dr, zq, zp, em in records[:n_iter]:
+    ref, gpu, iters = [], [], []
+    y0 = None
+    for n, dr, zq, zp, em in records[:n_iter]:
+        y0 = int(B.ssd_read_output(seq.handle, n - P)[-1])
         seq.ssd_iteration(plan.get("skip_mask"), plan.get("exit_layer"), d)
         st = B.ssd_read_state(seq.handle)
         assert st.error_flags == 0
         dp = st.last_n_drafted
         if seq.draft_tokens[:dp].cpu().numpy().tolist() != dr:
             break          # a near-tie changed the path
-        gz = seq.verify_logits[: (dp + 1) * V].view(dp + 1, V).cpu().numpy()
-        gq = seq.draft_logits[: dp * V].view(dp, V).cpu().numpy()
-        ev, ed = np.abs(gz - zp), np.abs(gq - zq)
-        print("  verify max %.3g (row %s) p99.9 %.3g |z| %.3g; draft max %.3g (row %s) |z| %.3g" % (
-            ev.max(), np.unravel_index(ev.argmax(), ev.shape), np.quantile(ev, 0.999), np.abs(zp).max(),
-            ed.max(), np.unravel_index(ed.argmax(), ed.shape), np.abs(zq).max()))
-        worst = max(worst, ev.max() / max(1.0, np.abs(zp).max()), ed.max() / max(1.0, np.abs(zq).max()))
-        compared += 1
+        gpu += [seq.draft_logits[: dp * V].view(dp, V).cpu().numpy(),
+                seq.verify_logits[: (dp + 1) * V].view(dp + 1, V).cpu().numpy()]
+        ref += [zq, zp]
+        iters.append((y0, n, dr))
         if seq.out_tokens[: st.last_n_emitted].cpu().numpy().tolist() != em:
             break
-    print("%s: worst |dz| / max|z| over %d iterations %.3g" % (shape.name, compared, worst))
-    assert compared >= 1
-    assert worst < REL_TOL
     seq.close()
+    assert len(iters) >= 1
+    tw = teacher_rows(acc32_twin(o), prompt, iters, mask, P + 4 * d + 16)[1:]
+    e_gpu = np.concatenate([max_abs_rows(a, b) for a, b in zip(gpu, ref)])
+    e_tw = np.concatenate([max_abs_rows(a, b) for a, b in zip(tw, ref)])
+    zmax = np.concatenate([np.abs(np.atleast_2d(b)).max(axis=1) for b in ref])
+    print("%s, %d iterations: |dz| GPU - oracle median %.3g max %.3g; twin - oracle median %.3g max %.3g; "
+          "max|z| %.3g; 2e-2 absolute holds on %d of %d rows" % (
+              shape.name, len(iters), np.median(e_gpu), e_gpu.max(), np.median(e_tw), e_tw.max(), zmax.max(),
+              int((e_gpu <= 2e-2).sum()), len(e_gpu)))
+    assert np.median(e_gpu) <= 1.5 * np.median(e_tw)
+    assert e_gpu.max() <= 1.5 * e_tw.max()
 
 
 def test_fullwidth_reuse_and_greedy_properties(case):
@@ -134,3 +138,48 @@ def test_fullwidth_decode_step_equals_prefill_row(case):
     torch.cuda.synchronize()
     seq.close()
     assert torch.equal(lg, lg2)
+
+
+def test_fullwidth_13b_sampled_matches_oracle():
+    """The 13B sampling workload's path at full width (two layers): a skip plan, d <= 8 with the confidence
+    stop at 0.8, temperature 1 with rejection-sampling acceptance; the GPU's tokens against the oracle's with
+    the sampled parity rule (a token may differ only where a decision of the oracle lies within 1e-2 of
+    flipping, then both restart from the oracle's prefix)."""
+    from gpu_util import check_sampled_with_resync
+    shape, P, _, plan = CASES["13b"]
+    d, tau, T, seed, n_gen = 8, 0.8, 1.0, 3, 40
+    print("[gpu] full-width 13B, sampled with the confidence stop: building weights", flush=True)
+    g = gpu_model(shape)
+    o = omodel.Model.synthetic(shape)
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 16, max_rows=64, max_draft=d)
+    drafted = []
+
+    def gpu_run(prefix, n):
+        out, stats = seq.generate_ssd(dev(prefix), n, skip_mask=plan["skip_mask"], d=d, conf_thresh=tau,
+                                      temperature=T, seed=seed)
+        drafted.extend(s[0] for s in stats)
+        return out
+
+    def oracle_run(prefix, n):
+        toks, st, _ = ossd.ssd_generate(o, prefix, n, plan["skip_mask"], d, tau=tau, T=T, seed=seed)
+        return toks, st
+
+    # how far float32 accumulation alone moves a logit here (the twin on the first iteration's rows); an
+    # accept decision ln u + ln q(y) - ln p(y) can move by four times that, a draw's key gap or a stop's
+    # ln conf by twice
+    recs = []
+    toks, _, _ = ossd.ssd_generate(o, prompt, 2, plan["skip_mask"], d, tau=tau, T=T, seed=seed,
+                                   on_iteration=lambda it, n, dr, zq, zp, em, kv: recs.append((n, list(dr))))
+    iters = [(int(toks[0]), recs[0][0], recs[0][1])]
+    cap = P + 4 * d + 16
+    rows_o = teacher_rows(o, prompt, iters, plan["skip_mask"], cap)
+    rows_t = teacher_rows(acc32_twin(o), prompt, iters, plan["skip_mask"], cap)
+    drift = max(max_abs_rows(a, b).max() for a, b in zip(rows_t, rows_o))
+    margin = 4.0 * drift / T
+    print("twin drift %.3g per logit: decision margin %.3g" % (drift, margin))
+    events = check_sampled_with_resync(gpu_run, oracle_run, prompt, n_gen, margin=margin, max_events=n_gen // 4)
+    print("13B width, tau 0.8, T 1: %d re-synchronisations over %d tokens; d' histogram %s" %
+          (events, n_gen, np.bincount(drafted).tolist()))
+    seq.close()
+    g.close()

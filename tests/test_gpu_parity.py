@@ -10,7 +10,8 @@ from oracle import philox as ophilox
 from oracle import ssd as ossd
 
 from synth import device as sdev
-from gpu_util import (BF16_HD64, BF16_HD128, F32_GQA, check_greedy_tokens, check_greedy_with_resync, dev, gpu_model,
+from gpu_util import (BF16_HD64, BF16_HD128, F32_GQA, check_greedy_tokens, check_greedy_with_resync,
+                      check_sampled_with_resync, check_scores, dev, gpu_model,
                       logit_tol, oracle_ar_with_logits)
 
 pytestmark = pytest.mark.gpu
@@ -187,22 +188,31 @@ def test_empty_plan_accepts_everything(pair):
 
 def test_sampled_ssd_matches_oracle(pair):
     """T = 1 with a confidence stop: same Philox draws on both sides, so the emitted
-    tokens agree except at decisions within 1e-2 (log units) of flipping."""
+    tokens agree except where a decision of the oracle lies within 1e-2 (log units)
+    of flipping; after such a token both sides restart from the oracle's prefix
+    and the comparison runs to the end."""
     shape, g, o = pair
     plan = PLANS[shape.name]
     mask = _mask_of(shape, plan)
     d, tau, T, seed = plan["d"], 0.002, 1.0, 12345
     P, n_gen = 24, 40
     prompt = synth.prompt_tokens(P, shape.vocab)
-    ref, ost, _ = ossd.ssd_generate(o, prompt, n_gen, mask, d, tau=tau, T=T, seed=seed)
     seq = B.Sequence(g, max_ctx=P + n_gen + 2 * d + 8, max_rows=64, max_draft=8)
-    out, stats = seq.generate_ssd(dev(prompt), n_gen, skip_mask=plan.get("skip_mask"),
-                                  exit_layer=plan.get("exit_layer"), d=d, conf_thresh=tau, temperature=T, seed=seed)
-    got = [int(x) for x in out]
-    n_match = next((i for i, (a, b) in enumerate(zip(got, ref)) if a != b), len(ref))
-    print("sampled: %d/%d tokens match before the first divergence; oracle drafted %s, gpu %s" %
-          (n_match, n_gen, ost["drafted"][:8], [s[0] for s in stats[:8]]))
-    assert n_match >= n_gen // 2
+    drafted = []
+
+    def gpu_run(prefix, n):
+        out, stats = seq.generate_ssd(dev(prefix), n, skip_mask=plan.get("skip_mask"),
+                                      exit_layer=plan.get("exit_layer"), d=d, conf_thresh=tau, temperature=T,
+                                      seed=seed)
+        drafted.extend(s[0] for s in stats)
+        return out
+
+    def oracle_run(prefix, n):
+        toks, st, _ = ossd.ssd_generate(o, prefix, n, mask, d, tau=tau, T=T, seed=seed)
+        return toks, st
+
+    events = check_sampled_with_resync(gpu_run, oracle_run, prompt, n_gen)
+    print("sampled: %d re-synchronisations over %d tokens; gpu drafted %s" % (events, n_gen, drafted[:10]))
     seq.close()
 
 
@@ -283,19 +293,20 @@ def test_score_masks_match_oracle():
     window = (list(prompt) + ref)[P - 1: P + gamma]
     masks = [np.zeros(8, np.uint8), synth.mask_from_layers(4, [1]), synth.mask_from_layers(4, [0, 2]),
              synth.mask_exit(4, 2), np.array([0, 1, 1, 0, 0, 0, 0, 1], np.uint8)]
-    oscores, obest = ossd.score_masks(o, kv, window, P - 1, masks)
+    oscores, obest, opred, omargin = ossd.score_masks(o, kv, window, P - 1, masks, detail=True)
     seq = B.Sequence(g, max_ctx=P + gamma + 64, max_rows=len(masks) * gamma, max_draft=4)
-    gout = seq.generate_ar(dev(prompt), gamma)
-    assert [int(x) for x in gout] == ref
+    seq.generate_ar(dev(prompt), gamma)            # the cache before the window: the prompt's keys/values
     scores = torch.zeros(len(masks), dtype=torch.float32, device="cuda")
     best = torch.zeros(1, dtype=torch.int32, device="cuda")
-    B.ssd_score_masks(seq.handle, np.stack(masks), dev(window), P - 1, gamma, scores, best)
+    pred = torch.zeros(len(masks) * gamma, dtype=torch.int32, device="cuda")
+    B.ssd_score_masks(seq.handle, np.stack(masks), dev(window), P - 1, gamma, scores, best, pred)
     torch.cuda.synchronize()
     gs = scores.cpu().numpy()
     print("scores gpu %s oracle %s" % (gs, oscores))
     assert gs[0] == 1.0
-    assert np.abs(gs - oscores).max() <= 2.0 / gamma
-    assert int(best.item()) == int(np.argmax(gs))
+    nd = check_scores(gs, int(best.item()), pred.cpu().numpy().reshape(len(masks), gamma), window, oscores, obest,
+                      opred, omargin)
+    print("rows differing from the oracle (all near-ties): %d" % nd)
     seq.close()
     g.close()
 
@@ -447,7 +458,9 @@ def test_swift_search_matches_oracle(shape, sublayers, bo_every, n_sub, seed):
     print("gpu: %d steps, score %.4f, best %s" % (gsteps, gscore, gbest[::2]))
     assert gsteps == osteps
     assert np.array_equal(gbest, obest)
-    assert abs(gscore - oscore) <= 2.0 / gamma
+    # the final plan's score may differ only by its rows that are oracle near-ties (top-2 margin < 1e-2)
+    _, _, _, om = ossd.score_masks(o, kv, window, P - 1, [obest], detail=True)
+    assert abs(gscore - oscore) <= int((om < 1e-2).sum()) / gamma + 1e-7
     seq.close()
     g.close()
 

@@ -427,3 +427,82 @@ def test_specee_features_are_the_lm_head_columns():
     prev = rng.random((3, 4))
     g = ssd.specee_features(m, h, toks, prev)
     assert np.allclose(g[:, 8:], g[:, 4:8] - prev, atol=0)
+
+
+# ---------------------------------------------------------------- decision margins (parity rule)
+def test_top2_gap():
+    assert ssd.top2_gap([0.0, 3.0, 1.0]) == 2.0
+    assert ssd.top2_gap([5.0, -np.inf]) == float("inf")
+    assert ssd.top2_gap([1.0, 1.0]) == 0.0
+
+
+def test_accept_margin_is_the_distance_to_flipping():
+    """The logged margin of an accept decision is |ln(u q(y) / p(y))|: moving p(y)'s logit by 0.9 of it
+    toward the threshold keeps the decision, by 1.1 of it flips it."""
+    rng = np.random.default_rng(3)
+    V, T, seed, it = 16, 1.0, 9, 4
+    for trial in range(20):
+        zp = rng.standard_normal((2, V))
+        zq = rng.standard_normal((1, V))
+        y = int(rng.integers(V))
+        log = []
+        out = ssd.accept_sampled(zp, zq, [y], T, seed, it + trial, log)
+        kind, row, m = log[0]
+        assert (kind, row) == ("accept", 0)
+        accepted = out[0] == y and len(out) == 2
+        u = philox.uniforms(seed, it + trial, 0, philox.PURPOSE_ACCEPT, 1)[0]
+        lp = ssd.log_softmax(zp[0], T)[y]
+        lq = ssd.log_softmax(zq[0], T)[y]
+        assert abs(m - abs(np.log(u) + lq - lp)) < 1e-5
+        # shift the target's log-probability of y by s (renormalising keeps the others' ratios)
+        for frac, flips in ((0.9, False), (1.1, True)):
+            s = (-1 if accepted else 1) * frac * m
+            if lp + s >= -1e-6:
+                continue                  # p'(y) would reach 1
+            zs = zp.copy()
+            # log p'(y) = lp + s, the other entries scaled equally
+            p = np.exp(ssd.log_softmax(zp[0], T))
+            pn = p.copy()
+            pn[y] = np.exp(lp + s)
+            others = np.arange(V) != y
+            pn[others] *= (1 - pn[y]) / p[others].sum()
+            zs[0] = np.log(pn)
+            out2 = ssd.accept_sampled(zs, zq, [y], T, seed, it + trial)
+            acc2 = out2[0] == y and len(out2) == 2
+            if m > 1e-3:
+                assert acc2 == (accepted != flips)
+
+
+def test_race_gap_is_the_distance_to_flipping():
+    """A race sample's logged margin is the top-2 key gap: raising the runner-up's logit by 1.1 gaps
+    (T = 1) hands it the draw, by 0.9 gaps does not."""
+    rng = np.random.default_rng(8)
+    V, seed = 40, 5
+    for it in range(15):
+        z = rng.standard_normal(V)
+        log = []
+        t = ssd.pick(z, 1.0, seed, it, 2, philox.PURPOSE_SAMPLE, log)
+        kind, row, m = log[0]
+        g = philox.gumbel(seed, it, 2, philox.PURPOSE_SAMPLE, V)
+        keys = z.astype(np.float32) + g
+        second = int(np.argsort(-keys, kind="stable")[1])
+        for frac, winner in ((0.9, t), (1.1, second)):
+            zz = z.copy()
+            zz[second] += frac * m
+            assert ssd.pick(zz, 1.0, seed, it, 2, philox.PURPOSE_SAMPLE) == winner
+
+
+def test_sampled_generation_logs_every_decision():
+    """Per iteration: one draft draw per draft row, one stop decision per row when tau > 0, an accept
+    decision per tested draft, one final draw (correction or bonus)."""
+    m = _model(synth.TINY)
+    prompt = synth.prompt_tokens(12, synth.TINY.vocab)
+    out, st, _ = ssd.ssd_generate(m, prompt, 20, synth.mask_from_layers(4, [2]), 4, tau=0.01, T=1.0, seed=7)
+    assert [k for k, _, _ in st["decisions"][0]] == ["sample"]
+    for k, log in enumerate(st["decisions"][1:]):
+        dp, e = st["drafted"][k], st["emitted"][k]
+        kinds = [x[0] for x in log]
+        assert kinds.count("draft") == dp and kinds.count("stop") == dp
+        assert kinds.count("accept") == min(e, dp)
+        assert kinds.count("sample") == 1
+        assert all(mg >= 0 for _, _, mg in log)
