@@ -27,24 +27,20 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 
 # HBM traffic of the dominant kernel from rocprofv3 counter runs (FETCH_SIZE and
-# WRITE_SIZE in KiB per decode dispatch, scaled by the factors a plain 1 GiB copy
-# reads on the same counters); valid only for the kernel source they were taken on.
-PMC_TRAFFIC = {
-    "dec_gemm_kernel<DEC_SWIGLU>": {"source": "self_speculative_layer_amd/csrc/decode.hip",
-                                    "sha1_prefix": "a2443541c93a", "fetch_kib": 88428.0, "write_kib": 61.8,
-                                    "fetch_scale": 2.0, "write_scale": 1.0},
-}
-PMC_TRAFFIC["gemm_bf16_tiled<EPI_SWIGLU, 4, 4>"] = {
-    "source": "self_speculative_layer_amd/csrc/kernels.hip", "sha1_prefix": "cf269fe21ae0",
-    "fetch_kib": 187621.0, "write_kib": 6420.7, "fetch_scale": 2.0, "write_scale": 1.0}
+# WRITE_SIZE in KiB per dispatch, averaged over the kernel's dispatches in the
+# run, scaled by the factors a plain 1 GiB copy reads on the same counters).
+# Keyed by (kernel, workload): a record holds only for the workload (shapes and
+# row counts) it was taken on, and only while the kernel source is the one it
+# was taken on; otherwise the line reports null.
+PMC_TRAFFIC = {}
 DOMINANT = "dec_gemm_kernel<DEC_SWIGLU>"
 SCORING_DOMINANT = "gemm_bf16_tiled<EPI_SWIGLU, 4, 4>"
 
 
-def pmc_traffic_bytes(kernel):
-    """Measured HBM bytes per launch, or None when the kernel source has changed."""
+def pmc_traffic_bytes(kernel, workload):
+    """Measured HBM bytes per launch, or None (no record for this kernel and workload, or the source changed)."""
     import hashlib
-    rec = PMC_TRAFFIC.get(kernel)
+    rec = PMC_TRAFFIC.get((kernel, workload))
     if rec is None:
         return None
     with open(os.path.join(ROOT, rec["source"]), "rb") as f:
@@ -136,38 +132,70 @@ def read_ceiling_gbps(torch, B, nbytes=1 << 33, reps=5):
     return nbytes / (best / 1e3) / 1e9
 
 
+def host_cpu():
+    """The host's CPU model, its logical CPU count, and the threads the oracle's BLAS runs."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    return model, os.cpu_count(), threads
+
+
 def cpu_baseline(shape, wl, mask, max_seconds=20.0):
-    """The oracle as it stands on a bounded sample: SSD iterations of the same
-    model after a 16-token prompt (weights float64 on the host)."""
+    """The oracle as it stands, timed on this host on the workload itself: the prefill of the workload's own
+    prompt (timed apart), then SSD iterations of the same plan from there until about max_seconds have
+    passed (at most 64)."""
     import numpy as np
     import synth
     from oracle import model as omodel
     from oracle import ssd as ossd
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count()
+    cpu_model, n_cpus, threads = host_cpu()
+    need = shape.param_count() * 8
+    mem = os.sysconf("SC_PAGE_SIZE") * os.sysconf("SC_PHYS_PAGES")
+    if need > 0.6 * mem:
+        return {"value": None, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model,
+                "sample": "not run: the oracle's float64 weights (%.0f GB) exceed 60%% of host RAM (%.0f GB)"
+                          % (need / 1e9, mem / 1e9)}
     t0 = time.time()
     om = omodel.Model.synthetic(shape)
     log("oracle weights built in %.1fs" % (time.time() - t0))
-    P = 16
-    prompt = synth.prompt_tokens(P, shape.vocab)
-    kv = omodel.KVCache(shape, P + 64 * (wl["d"] + 2))
-    out = [ossd.pick(ossd.prefill(om, kv, prompt), wl["T"], synth.SEED_SAMPLING, 0, 0, 2)]
+    P, d = wl["prompt"], wl["d"]
+    prompt = synth.prompt_tokens(P, shape.vocab)            # the GPU run's prompt
+    kv = omodel.KVCache(shape, P + 64 * (d + 2) + 8)
+    t0 = time.time()
+    z = ossd.prefill(om, kv, prompt)
+    prefill_s = time.time() - t0
+    log("oracle prefill of %d tokens: %.1f s" % (P, prefill_s))
+    out = [ossd.pick(z, wl["T"], synth.SEED_SAMPLING, 0, 0, 2)]
     b = omodel.first_skipped_layer(mask, shape.n_layers)
     tokens, iters = 0, 0
     t0 = time.time()
     while True:
         n = P + len(out)
-        drafts, zq, hb = ossd.draft(om, kv, out[-1], n, mask, wl["d"], wl["tau"], wl["T"], synth.SEED_SAMPLING,
-                                    iters + 1)
+        drafts, zq, hb = ossd.draft(om, kv, out[-1], n, mask, d, wl["tau"], wl["T"], synth.SEED_SAMPLING, iters + 1)
         if "tree" in wl:
             from oracle import tree as otree
             tr = wl["tree"]
-            leaves = otree.tree_leaves(zq, drafts, tr["rho"], tr["k_max"], tr["max_leaves"])
+            if wl["T"] == 0:
+                leaves = otree.tree_leaves(zq, drafts, tr["rho"], tr["k_max"], tr["max_leaves"])
+            else:
+                leaves = otree.tree_leaves_sampled(zq, drafts, wl["T"], tr["rho"], tr["k_max"], tr["max_leaves"],
+                                                   synth.SEED_SAMPLING, iters + 1)
             zp, zl = otree.verify_tree(om, kv, out[-1], drafts, leaves, n, b, hb)
-            em, s = otree.accept_tree_greedy(zp, zl, drafts, leaves)
+            if wl["T"] == 0:
+                em, s = otree.accept_tree_greedy(zp, zl, drafts, leaves)
+            else:
+                em, s = otree.accept_tree_sampled(zp, zq, zl, drafts, leaves, wl["T"], synth.SEED_SAMPLING, iters + 1)
             if s is not None:
                 j, c = leaves[s]
                 omodel.forward(om, [out[-1]] + [int(t) for t in drafts[: j - 1]] + [c], list(range(n - 1, n + j)), kv)
@@ -181,9 +209,11 @@ def cpu_baseline(shape, wl, mask, max_seconds=20.0):
         if time.time() - t0 > max_seconds or iters >= 64:
             break
     dt = time.time() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%d SSD iterations (%d committed tokens) of the same %s model and plan after a 16-token "
-                      "prompt, float64 NumPy oracle, %.1f s" % (iters, tokens, shape.name, dt)}
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d SSD iterations (%d committed tokens) of the same %s model, plan and seeded %d-token prompt "
+                      "as the GPU run, right after the prompt's prefill (%.1f s, not counted), float64 NumPy oracle "
+                      "with %d BLAS threads, %.1f s" % (iters, tokens, shape.name, P, prefill_s, threads, dt),
+            "prefill_s": round(prefill_s, 2), "cpu_model": cpu_model, "host_logical_cpus": n_cpus}
 
 
 def main():
@@ -243,7 +273,7 @@ def main():
     skip_mask, exit_layer, mask = plan_of(wl, shape)
     d = wl["d"]
     K, W = args.steps, args.warmup
-    max_ctx = wl["prompt"] + (2 * K + W + 2) * (d + 1) + 64
+    max_ctx = wl["prompt"] + (3 * K + W + 2) * (d + 1) + 64
     seq = B.Sequence(model, max_ctx=max_ctx, max_rows=512, max_draft=max(d, 1), device=dev)
     prompt = torch.from_numpy(synth.prompt_tokens(wl["prompt"], shape.vocab)).to(dev)
     seed = synth.SEED_SAMPLING
@@ -257,10 +287,14 @@ def main():
 
     tr = wl.get("tree")
 
-    def iteration(vev=None):
+    def iteration(vev=None, dev_=None):
         h = seq.handle
+        if dev_ is not None:
+            dev_[0].record()
         B.ssd_draft(h, skip_mask, exit_layer, d, wl["tau"], wl["T"], seed, seq.draft_tokens, seq.draft_logits,
                     seq.n_drafted)
+        if dev_ is not None:
+            dev_[1].record()
         if tr is not None:
             # dynamic verification: leaves from the draft's confidence, one tree verify, tree acceptance
             B.ssd_tree_candidates(h, seq.draft_logits, seq.n_drafted, d, tr["rho"], tr["k_max"], tr["max_leaves"],
@@ -325,6 +359,19 @@ def main():
         (K, elapsed_ms, wall_ms, tokens, value, vmed))
     achieved = prof_bytes / (prof_ms / 1e3) / 1e9 if prof_ms > 0 else 0.0
 
+    # statistics pass: K more steps, each followed by a state read (d' and the emitted count), with the draft
+    # phase bracketed by events (SWIFT digest §B.3: M = tokens per verify, alpha = accepted-draft fraction)
+    dps, ems, draft_ms = [], [], []
+    for k in range(K):
+        dv = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        iteration(dev_=dv)
+        st = B.ssd_read_state(seq.handle)
+        dps.append(st.last_n_drafted)
+        ems.append(st.last_n_emitted)
+        draft_ms.append(dv[0].elapsed_time(dv[1]))
+    dps, ems, draft_ms = np.array(dps), np.array(ems), np.array(draft_ms)
+    acc = np.minimum(ems - 1, dps)
+
     # same-kernel AR decode baseline
     ar_tps = None
     if args.ar_steps > 0:
@@ -341,7 +388,7 @@ def main():
         ar_tps = args.ar_steps / (ev0.elapsed_time(ev1) / 1e3)
         seq2.close()
 
-    traffic = pmc_traffic_bytes(DOMINANT)
+    traffic = pmc_traffic_bytes(DOMINANT, args.workload)
     if traffic is not None:
         traffic = round(traffic)
     ceiling = read_ceiling_gbps(torch, B)
@@ -377,6 +424,15 @@ def main():
                    "GBps": round(vb / (vmed / 1e3) / 1e9, 1),
                    "frac_of_peak": round(vb / (vmed / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "mean_tokens_per_step": round(tokens / K, 4),
+        "ssd_stats": {"steps": K, "M_tokens_per_verify": round(float(ems.mean()), 4),
+                      "alpha_accepted_fraction": round(float(acc.sum() / max(dps.sum(), 1)), 4),
+                      "d_prime_histogram": np.bincount(dps, minlength=d + 1).tolist(),
+                      "draft_phase_ms_median": round(float(np.median(draft_ms)), 4),
+                      "draft_ms_per_drafted_token": round(float(np.median(draft_ms / np.maximum(dps, 1))), 4),
+                      "c_draft_token_over_ar_token": (None if ar_tps is None else
+                                                      round(float(np.median(draft_ms / np.maximum(dps, 1)))
+                                                            / (1e3 / ar_tps), 4)),
+                      "measured": "%d further steps of the same sequence, a state read after each" % K},
         "ar_tokens_per_s": None if ar_tps is None else round(ar_tps, 3),
         "prefill_ms": round(prefill_ms, 2),
         "wall_ms_timed": round(wall_ms, 2),
@@ -552,7 +608,7 @@ def run_scoring(args):
              "frac": round(tflops / 2500.0, 4)} if mfma_bound else
             {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
              "frac": round(gbps / HBM_PEAK_GBPS, 4)})
-    traffic = pmc_traffic_bytes(SCORING_DOMINANT) if not search else None
+    traffic = pmc_traffic_bytes(SCORING_DOMINANT, args.workload)
     roof.update({"traffic": None if traffic is None else round(traffic),
                  "kernel": SCORING_DOMINANT + " (gate/up + SwiGLU over the candidates' rows, 128 x 128 tiles)",
                  "launches": prof_n, "avg_launch_us": round(prof_ms / max(prof_n, 1) * 1e3, 3),

@@ -210,6 +210,12 @@ int ssd_decode_exit(ssd_seq* seq, const uint8_t* skip_mask_host, int exit_layer,
  * final norm and LM head; y_j = argmax (temperature 0) or a draw from
  * softmax(z / T) (purpose "draft"); conf_j = max softmax.  Drafting stops after
  * step j when conf_j < conf_thresh or j = d; d' = j.
+ * With conf_thresh <= 0 no step can stop early: all d steps are enqueued and
+ * the call returns at once.  With conf_thresh > 0 the call waits after each
+ * step j < d for the stop decision (it synchronises the stream and reads 4
+ * bytes) and enqueues no later step once drafting has stopped, so a stopped
+ * draft costs no further launches; such a call cannot be captured into a HIP
+ * graph.
  * Outputs: draft_tokens_dev[d] (first d' valid), draft_logits_dev[d * V]
  * (rows 0..d'-1 valid: the q logits), n_drafted_dev[1] = d'.
  * Also saves, for each step, the residual entering the reuse boundary b (the

@@ -547,6 +547,20 @@ extern "C" int ssd_decode_exit(ssd_seq* q, const uint8_t* skip_mask_host, int ex
 // ---------------------------------------------------------------------------
 // draft / verify / accept / commit
 
+namespace {
+
+// Waits for the work queued on s and reads the draft's stop flag (a 4-byte copy).
+int draft_stopped(ssd_seq* q, hipStream_t s, int* stopped) {
+  int v = 0;
+  hipError_t e = hipMemcpyAsync(&v, &q->w.st->stop, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  *stopped = v;
+  return 0;
+}
+
+}  // namespace
+
 extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_layer, int d_max, float conf_thresh,
                          float temperature, uint64_t seed, int32_t* draft_tokens_dev, float* draft_logits_dev,
                          int32_t* n_drafted_dev, hipStream_t s) {
@@ -579,6 +593,11 @@ extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_lay
       TRY(launch_row_stats_seg(lg, d.vocab, 1, d.vocab, temperature, seed, nullptr, 0, 0, PURPOSE_DRAFT, nullptr,
                                w.stat_recs, w.stat_ctr, nullptr,
                                DraftStep{w.st, j, d_max, conf_thresh, draft_tokens_dev, n_drafted_dev}, s));
+      if (conf_thresh > 0.f && j < d_max) {
+        int stopped = 0;
+        TRY(draft_stopped(q, s, &stopped));
+        if (stopped) break;
+      }
     }
     return SSD_OK;
   }
@@ -594,6 +613,11 @@ extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_lay
     TRY(launch_row_stats_seg(lg, d.vocab, 1, d.vocab, temperature, seed, nullptr, 0, 0, PURPOSE_DRAFT, nullptr,
                              w.stat_recs, w.stat_ctr, nullptr,
                              DraftStep{w.st, j, d_max, conf_thresh, draft_tokens_dev, n_drafted_dev}, s));
+    if (conf_thresh > 0.f && j < d_max) {
+      int stopped = 0;
+      TRY(draft_stopped(q, s, &stopped));
+      if (stopped) break;
+    }
   }
   return SSD_OK;
 }
