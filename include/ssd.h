@@ -246,7 +246,9 @@ int ssd_verify(ssd_seq* seq, const uint8_t* skip_mask_host, int exit_layer, int 
  * rejection a draw from norm(max(0, p_i - q_i)) (purpose "sample", row i-1) is
  * emitted; when all d' are accepted a bonus draw from p_{d'+1} (row d').
  * Outputs: out_tokens_dev[d + 1] (first n_out valid), n_out_dev[1] = k + 1.
- * Does not change the sequence (see ssd_commit). */
+ * A verify row 0..d' or draft row with NaN or +inf logits decides nothing:
+ * n_out = 0 and the sequence's numeric flag is raised (ssd_read_state returns
+ * SSD_ERR_NUMERIC).  Does not change the sequence otherwise (see ssd_commit). */
 int ssd_accept(ssd_seq* seq, const float* p_logits_dev, const float* q_logits_dev,
                const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, int d, float temperature,
                uint64_t seed, int32_t* out_tokens_dev, int32_t* n_out_dev, hipStream_t stream);
@@ -259,7 +261,8 @@ int ssd_accept(ssd_seq* seq, const float* p_logits_dev, const float* q_logits_de
  * n_drafted_dev[1] (d' in 1..d; values outside 0..d are clamped) are as in
  * ssd_accept; iteration addresses the draws (a sequence's iteration counter
  * reproduces ssd_accept's draws exactly).  Outputs: out_tokens_dev[d + 1]
- * (first n_out valid), n_out_dev[1].
+ * (first n_out valid), n_out_dev[1]; n_out = 0 when a row holds NaN or +inf
+ * logits.
  * Scratch: the per-row decisions and draws passed between the two kernels sit
  * in a library-owned device array of 2 x (SSD_ACCEPT_NOALLOC_MAX_DRAFT + 1)
  * int32 per GPU, created with the library's code object and held until the
@@ -275,7 +278,9 @@ int ssd_accept_noalloc(const float* p_logits_dev, const float* q_logits_dev, con
 /* Commit (row a5): appends out_tokens_dev[0..n_out-1] to the output log,
  * kvlen += n_out, last_token = the last emitted token, iteration += 1.  Keys and
  * values at positions >= the new kvlen are dead (rejected drafts) and are
- * overwritten by later steps: roll-back is this metadata update only. */
+ * overwritten by later steps: roll-back is this metadata update only.
+ * n_out = 0 commits nothing (iteration += 1); n_out < 0 or > max_draft + 1
+ * commits nothing and raises the input flag (ssd_read_state: SSD_ERR_ARG). */
 int ssd_commit(ssd_seq* seq, const int32_t* out_tokens_dev, const int32_t* n_out_dev,
                hipStream_t stream);
 

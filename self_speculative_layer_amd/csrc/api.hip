@@ -8,8 +8,10 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <new>
 #include <string>
+#include <unordered_set>
 #include <vector>
 
 #include "kernels.h"
@@ -38,6 +40,29 @@ static int fail(int code, const std::string& msg) {
   } while (0)
 
 extern "C" const char* ssd_last_error(void) { return g_err.c_str(); }
+
+// ---------------------------------------------------------------------------
+// live handles: every entry point checks that the handle it is given was created here and not destroyed
+
+static std::mutex g_handles_mu;
+static std::unordered_set<const void*> g_models, g_seqs;
+
+static bool is_live(const std::unordered_set<const void*>& set, const void* h) {
+  std::lock_guard<std::mutex> lock(g_handles_mu);
+  return set.count(h) != 0;
+}
+
+#define CHECK_MODEL(m)                                                                                   \
+  do {                                                                                                   \
+    if (!(m)) return fail(SSD_ERR_ARG, "null model handle");                                             \
+    if (!is_live(g_models, (m))) return fail(SSD_ERR_ARG, "not a live model handle (destroyed or never created)"); \
+  } while (0)
+
+#define CHECK_SEQ(q)                                                                                     \
+  do {                                                                                                   \
+    if (!(q)) return fail(SSD_ERR_ARG, "null sequence handle");                                          \
+    if (!is_live(g_seqs, (q))) return fail(SSD_ERR_ARG, "not a live sequence handle (destroyed or never created)"); \
+  } while (0)
 
 int ssd::set_last_error(int code, const char* msg) { return fail(code, msg); }
 
@@ -369,6 +394,10 @@ extern "C" int ssd_model_create(const ssd_model_desc* desc, ssd_model** out_mode
   m->kv_dim = d.n_kv_heads * d.head_dim;
   m->qkv_dim = m->q_dim + 2 * m->kv_dim;
   m->elt = d.dtype == SSD_DTYPE_BF16 ? 2 : 4;
+  {
+    std::lock_guard<std::mutex> lock(g_handles_mu);
+    g_models.insert(m);
+  }
   *out_model = m;
   return SSD_OK;
 }
@@ -388,17 +417,26 @@ extern "C" int ssd_pack_bf16(const void* src, void* dst, int N, int K, hipStream
 }
 
 extern "C" int ssd_model_destroy(ssd_model* model) {
+  CHECK_MODEL(model);
+  {
+    std::lock_guard<std::mutex> lock(g_handles_mu);
+    for (const void* h : g_seqs)
+      if (((const ssd_seq*)h)->m == model) return fail(SSD_ERR_ARG, "a live sequence still uses this model");
+    g_models.erase(model);
+  }
   delete model;
   return SSD_OK;
 }
 
 extern "C" int ssd_kv_pool_bytes(const ssd_model* m, int n_pages, int page_size, size_t* bytes) {
+  CHECK_MODEL(m);
   CHECK_ARG(m && bytes && n_pages > 0 && page_size > 0, "bad argument");
   *bytes = (size_t)n_pages * m->d.n_layers * 2 * m->kv_dim * page_size * m->elt;
   return SSD_OK;
 }
 
 extern "C" int ssd_workspace_bytes(const ssd_model* m, int max_rows, int max_draft, int max_ctx, size_t* bytes) {
+  CHECK_MODEL(m);
   CHECK_ARG(m && bytes, "null argument");
   CHECK_ARG(max_rows >= 1 && max_rows <= 1024, "max_rows must be in 1..1024");
   CHECK_ARG(max_draft >= 1 && max_draft <= 32, "max_draft must be in 1..32");
@@ -414,6 +452,7 @@ extern "C" int ssd_seq_create(const ssd_model* m, void* kv_pool_dev, int n_pages
                               const int32_t* page_table_host, int n_logical_pages, void* workspace_dev,
                               size_t workspace_bytes, int max_rows, int max_draft, hipStream_t stream,
                               ssd_seq** out_seq) {
+  CHECK_MODEL(m);
   CHECK_ARG(m && kv_pool_dev && page_table_host && workspace_dev && out_seq, "null argument");
   CHECK_ARG(page_size == 16 || page_size == 32 || page_size == 64, "page_size must be 16, 32 or 64");
   CHECK_ARG(n_pages > 0 && n_logical_pages > 0, "no pages");
@@ -462,11 +501,20 @@ extern "C" int ssd_seq_create(const ssd_model* m, void* kv_pool_dev, int n_pages
     delete q;
     return fail(SSD_ERR_HIP, "state init failed");
   }
+  {
+    std::lock_guard<std::mutex> lock(g_handles_mu);
+    g_seqs.insert(q);
+  }
   *out_seq = q;
   return SSD_OK;
 }
 
 extern "C" int ssd_seq_destroy(ssd_seq* seq) {
+  CHECK_SEQ(seq);
+  {
+    std::lock_guard<std::mutex> lock(g_handles_mu);
+    g_seqs.erase(seq);
+  }
   delete seq;
   return SSD_OK;
 }
@@ -476,6 +524,7 @@ extern "C" int ssd_seq_destroy(ssd_seq* seq) {
 
 extern "C" int ssd_prefill(ssd_seq* q, const int32_t* tokens_dev, int n, float temperature, uint64_t seed,
                            float* last_logits_dev, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && tokens_dev, "null argument");
   CHECK_ARG(n >= 1, "empty prompt");
   CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
@@ -530,6 +579,7 @@ int decode_one(ssd_seq* q, const uint8_t* mask, float temperature, uint64_t seed
 }  // namespace
 
 extern "C" int ssd_decode_ar(ssd_seq* q, float temperature, uint64_t seed, float* logits_dev, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q, "null argument");
   CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
   return decode_one(q, nullptr, temperature, seed, logits_dev, s);
@@ -537,6 +587,7 @@ extern "C" int ssd_decode_ar(ssd_seq* q, float temperature, uint64_t seed, float
 
 extern "C" int ssd_decode_exit(ssd_seq* q, const uint8_t* skip_mask_host, int exit_layer, float temperature,
                                uint64_t seed, float* logits_dev, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q, "null argument");
   CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
   std::vector<uint8_t> mask;
@@ -564,6 +615,7 @@ int draft_stopped(ssd_seq* q, hipStream_t s, int* stopped) {
 extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_layer, int d_max, float conf_thresh,
                          float temperature, uint64_t seed, int32_t* draft_tokens_dev, float* draft_logits_dev,
                          int32_t* n_drafted_dev, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && draft_tokens_dev && draft_logits_dev && n_drafted_dev, "null argument");
   CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
   CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
@@ -625,6 +677,7 @@ extern "C" int ssd_draft(ssd_seq* q, const uint8_t* skip_mask_host, int exit_lay
 extern "C" int ssd_verify(ssd_seq* q, const uint8_t* skip_mask_host, int exit_layer, int d_max,
                           const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, int reuse,
                           float* logits_dev, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && draft_tokens_dev && n_drafted_dev && logits_dev, "null argument");
   CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
   const ssd_model_desc& d = q->m->d;
@@ -677,18 +730,21 @@ extern "C" int ssd_verify(ssd_seq* q, const uint8_t* skip_mask_host, int exit_la
 extern "C" int ssd_accept(ssd_seq* q, const float* p_logits_dev, const float* q_logits_dev,
                           const int32_t* draft_tokens_dev, const int32_t* n_drafted_dev, int d_max, float temperature,
                           uint64_t seed, int32_t* out_tokens_dev, int32_t* n_out_dev, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && p_logits_dev && q_logits_dev && draft_tokens_dev && n_drafted_dev && out_tokens_dev && n_out_dev,
             "null argument");
   CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
   CHECK_ARG(temperature >= 0.f && std::isfinite(temperature), "bad temperature");
   TRY(launch_accept(p_logits_dev, q_logits_dev, q->m->d.vocab, draft_tokens_dev, n_drafted_dev, d_max, temperature,
-                    seed, &q->w.st->iteration, 0, q->w.dec, q->w.corr, out_tokens_dev, n_out_dev, s));
+                    seed, &q->w.st->iteration, 0, q->w.dec, q->w.corr, out_tokens_dev, n_out_dev,
+                    &q->w.st->error_flags, s));
   return SSD_OK;
 }
 
 extern "C" int ssd_commit(ssd_seq* q, const int32_t* out_tokens_dev, const int32_t* n_out_dev, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && out_tokens_dev && n_out_dev, "null argument");
-  TRY(launch_commit(q->w.st, out_tokens_dev, n_out_dev, q->w.log, q->log_cap, s));
+  TRY(launch_commit(q->w.st, out_tokens_dev, n_out_dev, q->w.log, q->log_cap, q->max_draft + 1, s));
   return SSD_OK;
 }
 
@@ -699,6 +755,7 @@ extern "C" int ssd_tree_candidates(ssd_seq* q, const float* draft_logits_dev, co
                                    float temperature, uint64_t seed, float rho, int k_max, int max_leaves,
                                    int32_t* leaf_tokens_dev, int32_t* leaf_depth_dev, int32_t* n_leaves_dev,
                                    hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && draft_logits_dev && n_drafted_dev && leaf_tokens_dev && leaf_depth_dev && n_leaves_dev,
             "null argument");
   CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
@@ -718,6 +775,7 @@ extern "C" int ssd_verify_tree(ssd_seq* q, const uint8_t* skip_mask_host, int ex
                                const int32_t* leaf_tokens_dev, const int32_t* leaf_depth_dev,
                                const int32_t* n_leaves_dev, int max_leaves, int reuse, float* logits_dev,
                                hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && draft_tokens_dev && n_drafted_dev && leaf_tokens_dev && leaf_depth_dev && n_leaves_dev && logits_dev,
             "null argument");
   CHECK_ARG(d_max >= 1 && d_max <= q->max_draft, "d out of range");
@@ -763,6 +821,7 @@ extern "C" int ssd_accept_tree(ssd_seq* q, const float* logits_dev, const float*
                                const int32_t* leaf_tokens_dev, const int32_t* leaf_depth_dev,
                                const int32_t* n_leaves_dev, int max_leaves, float temperature, uint64_t seed,
                                int32_t* out_tokens_dev, int32_t* n_out_dev, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && logits_dev && draft_tokens_dev && n_drafted_dev && leaf_tokens_dev && leaf_depth_dev &&
                 n_leaves_dev && out_tokens_dev && n_out_dev,
             "null argument");
@@ -793,6 +852,7 @@ extern "C" int ssd_accept_tree(ssd_seq* q, const float* logits_dev, const float*
 extern "C" int ssd_score_masks(ssd_seq* q, const uint8_t* masks_host, int n_masks, const int32_t* window_dev,
                                int pos0, int gamma, float* scores_dev, int32_t* best_dev, int32_t* row_pred_dev,
                                hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && masks_host && window_dev && scores_dev && best_dev, "null argument");
   CHECK_ARG(n_masks >= 1 && gamma >= 1, "empty scoring problem");
   CHECK_ARG(pos0 >= 0, "negative pos0");
@@ -977,6 +1037,7 @@ extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0,
                                 const uint8_t* init_mask_host, int n_skip, int sublayers, int n_cand, int max_steps,
                                 int patience, float target, uint64_t seed, int bo_every, uint8_t* best_mask_host,
                                 float* best_score, int* n_steps, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && window_dev && init_mask_host && best_mask_host && best_score && n_steps, "null argument");
   const int L = q->m->d.n_layers;
   CHECK_ARG(n_skip >= 0 && n_skip <= (sublayers ? 2 : 1) * L && n_cand >= 1 && n_cand + 1 <= 64 && max_steps >= 1 &&
@@ -1040,6 +1101,7 @@ extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0,
 
 extern "C" int ssd_specee_features(const ssd_model* m, const float* h_dev, int rows, const int32_t* tokens_dev, int k,
                                    const float* prev_probs_dev, float* features_dev, hipStream_t s) {
+  CHECK_MODEL(m);
   CHECK_ARG(m && h_dev && tokens_dev && features_dev && rows >= 0, "bad argument");
   if (k < 1 || k > 16) return fail(SSD_ERR_SHAPE, "k must be 1..16");
   const ssd_model_desc& d = m->d;
@@ -1061,6 +1123,7 @@ extern "C" int ssd_row_stats(const float* logits_dev, int rows, int V, float tem
 // host synchronisation
 
 extern "C" int ssd_read_state(ssd_seq* q, ssd_state* out, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && out, "null argument");
   DevState st;
   hipError_t e = hipStreamSynchronize(s);
@@ -1080,6 +1143,7 @@ extern "C" int ssd_read_state(ssd_seq* q, ssd_state* out, hipStream_t s) {
 }
 
 extern "C" int ssd_read_output(ssd_seq* q, int32_t* tokens_host, int max_tokens, int* n_tokens, hipStream_t s) {
+  CHECK_SEQ(q);
   CHECK_ARG(q && tokens_host && n_tokens && max_tokens >= 0, "bad argument");
   ssd_state st;
   int rc = ssd_read_state(q, &st, s);

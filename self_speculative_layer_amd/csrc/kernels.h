@@ -99,12 +99,14 @@ int launch_row_stats_seg(const float* z, int ldz, int rows, int V, float T, uint
 
 // Accept / reject of a chain (d + 1 verify rows): dec, corr [d + 1] hold the per-row decisions and draws
 // between the two kernels; the draws are addressed by iteration *iter_ptr (or iter_const when null).
+// Rows with NaN or +inf logits emit nothing (n_out = 0) and raise ERRF_NUMERIC in *err_flags (nullable).
 int launch_accept(const float* zp, const float* zq, int V, const int32_t* drafts, const int32_t* n_drafted,
                   int d, float T, uint64_t seed, const int* iter_ptr, int iter_const, int* dec, int* corr,
-                  int32_t* out_tokens, int32_t* n_out, hipStream_t s);
+                  int32_t* out_tokens, int32_t* n_out, int* err_flags, hipStream_t s);
 
+// Commits n_out tokens (at most max_n; 0 commits nothing).
 int launch_commit(DevState* st, const int32_t* out_tokens, const int32_t* n_out, int32_t* log,
-                  int log_cap, hipStream_t s);
+                  int log_cap, int max_n, hipStream_t s);
 
 // Pick one token from a row's stats and commit it (prefill / AR step).
 int launch_pick_commit(const ssd_row_stat* stat, DevState* st, int32_t* log, int log_cap, int set_kvlen,

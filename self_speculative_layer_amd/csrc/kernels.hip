@@ -1168,6 +1168,7 @@ __global__ __launch_bounds__(256) void row_stats_seg_kernel(const float* __restr
       *ds.n_drafted_out = ds.j;
     }
   } else {
+    if (bb) o.max = __int_as_float(0x7fc00000);          // non-finite logits: the row's max reads NaN
     out[row] = o;
   }
 }
@@ -1279,25 +1280,41 @@ __global__ __launch_bounds__(1024) void accept_rows_kernel(const float* __restri
   if (i > dp) return;
   const float* p = zp + (size_t)i * V;
   const int tid = threadIdx.x;
+  // a row holding NaN or +inf decides nothing: corr[i] = -1 marks it for the emit step
   if (T == 0.f) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
+    int bad = 0;
     if (V <= 1024 * ROWREG) {
       float r[ROWREG];
       load_row_strided(p, V, r);
 #pragma unroll
       for (int k = 0; k < ROWREG; ++k)
-        if (tid + 1024 * k < V) argmax_merge(bv, bi, r[k], tid + 1024 * k);
+        if (tid + 1024 * k < V) {
+          argmax_merge(bv, bi, r[k], tid + 1024 * k);
+          bad |= isnan(r[k]) || r[k] == INFINITY;
+        }
     } else {
-      for_strided<1024>(p, V, [&](int v, float pv) { argmax_merge(bv, bi, pv, v); });
+      for_strided<1024>(p, V, [&](int v, float pv) {
+        argmax_merge(bv, bi, pv, v);
+        bad |= isnan(pv) || pv == INFINITY;
+      });
     }
     const int am = block_argmax_1024(bv, bi);
-    if (tid == 0) { corr[i] = am; dec[i] = (i < dp) && (am == drafts[i]); }
+    const int anybad = __syncthreads_or(bad);
+    if (tid == 0) {
+      corr[i] = anybad ? -1 : am;
+      dec[i] = !anybad && (i < dp) && (am == drafts[i]);
+    }
     return;
   }
   const int iter = iter_ptr ? *iter_ptr : iter_const;
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const float lse_p = block_lse(p, V, T);
+  if (!isfinite(lse_p) || (i < dp && !isfinite(block_lse(zq + (size_t)i * V, V, T)))) {
+    if (tid == 0) { corr[i] = -1; dec[i] = 0; }
+    return;
+  }
   float kbest = -INFINITY;
   int ibest = 0x7fffffff;
   if (i == dp) {
@@ -1355,11 +1372,18 @@ __global__ __launch_bounds__(1024) void accept_rows_kernel(const float* __restri
   }
 }
 
+// Rows marked non-finite (corr = -1) emit nothing: n_out = 0 and ERRF_NUMERIC in *err (nullable).
 __global__ void accept_emit_kernel(const int32_t* __restrict__ drafts, const int32_t* __restrict__ n_drafted, int d,
                                    const int* __restrict__ dec, const int* __restrict__ corr,
-                                   int32_t* __restrict__ out, int32_t* __restrict__ n_out) {
+                                   int32_t* __restrict__ out, int32_t* __restrict__ n_out, int* __restrict__ err) {
   if (threadIdx.x != 0) return;
   const int dp = min(max(*n_drafted, 0), d);
+  for (int r = 0; r <= dp; ++r)
+    if (corr[r] < 0) {
+      *n_out = 0;
+      if (err) atomicOr(err, ERRF_NUMERIC);
+      return;
+    }
   int k = 0;
   while (k < dp && dec[k]) { out[k] = drafts[k]; ++k; }
   out[k] = corr[k];
@@ -1387,18 +1411,22 @@ __global__ __launch_bounds__(1024) void tree_accept_sampled_kernel(
   const int nl = max(min(*n_leaves, max_leaves), 0);
   if (tid == 0) {
     st->tree_leaf = -1;
-    int i = 0;
-    while (i < dp && dec[i]) { out[i] = drafts[i]; ++i; }
+    int bad = 0;
+    for (int r = 0; r <= dp; ++r) bad |= corr[r] < 0;
+    if (bad) st->error_flags |= ERRF_NUMERIC;
+    int i = bad ? -1 : 0;
+    while (i >= 0 && i < dp && dec[i]) { out[i] = drafts[i]; ++i; }
     int nd = 0;
     if (i < dp)
       for (int s = 0; s < nl; ++s) nd += leaf_depth[s] == i + 1;
     s_i = i;
     s_nd = nd;
-    if (i == dp || nd == 0) { out[i] = corr[i]; *n_out = i + 1; }
+    if (i < 0) *n_out = 0;                                 // non-finite logits: nothing is emitted
+    else if (i == dp || nd == 0) { out[i] = corr[i]; *n_out = i + 1; }
   }
   __syncthreads();
   const int i = s_i;
-  if (i == dp || s_nd == 0) return;
+  if (i < 0 || i == dp || s_nd == 0) return;
   const float* p = zp + (size_t)i * V;
   const float* q = zq + (size_t)i * V;
   const float lse_p = block_lse(p, V, T);
@@ -1510,11 +1538,11 @@ int launch_tree_accept_sampled(const float* zp, const float* zq, int V, const in
 
 int launch_accept(const float* zp, const float* zq, int V, const int32_t* drafts, const int32_t* n_drafted, int d,
                   float T, uint64_t seed, const int* iter_ptr, int iter_const, int* dec, int* corr,
-                  int32_t* out_tokens, int32_t* n_out, hipStream_t s) {
+                  int32_t* out_tokens, int32_t* n_out, int* err_flags, hipStream_t s) {
   hipLaunchKernelGGL(accept_rows_kernel, dim3(d + 1), dim3(1024), 0, s, zp, zq, V, drafts, n_drafted, T, seed,
                      iter_ptr, iter_const, dec, corr);
   hipLaunchKernelGGL(accept_emit_kernel, dim3(1), dim3(64), 0, s, drafts, n_drafted, d, dec, corr, out_tokens,
-                     n_out);
+                     n_out, err_flags);
   return last_launch();
 }
 
@@ -1522,10 +1550,22 @@ int launch_accept(const float* zp, const float* zq, int V, const int32_t* drafts
 // Commit and control kernels (single wave).
 // ===========================================================================
 
+// n_out outside 0..max_n: ERRF_INPUT, nothing committed; n_out = 0 (an acceptance that saw non-finite
+// logits): nothing committed, the iteration counter still moves on.
 __global__ void commit_kernel(DevState* st, const int32_t* __restrict__ out_tokens, const int32_t* __restrict__ n_out,
-                              int32_t* __restrict__ log, int log_cap) {
+                              int32_t* __restrict__ log, int log_cap, int max_n) {
   if (threadIdx.x != 0) return;
   const int n = *n_out;
+  if (n < 0 || n > max_n) {
+    st->error_flags |= ERRF_INPUT;
+    st->n_emitted = 0;
+    return;
+  }
+  if (n == 0) {
+    st->iteration += 1;
+    st->n_emitted = 0;
+    return;
+  }
   for (int t = 0; t < n; ++t) {
     const int idx = st->n_out + t;
     if (idx < log_cap) log[idx] = out_tokens[t];
@@ -1538,9 +1578,9 @@ __global__ void commit_kernel(DevState* st, const int32_t* __restrict__ out_toke
   st->n_emitted = n;
 }
 
-int launch_commit(DevState* st, const int32_t* out_tokens, const int32_t* n_out, int32_t* log, int log_cap,
+int launch_commit(DevState* st, const int32_t* out_tokens, const int32_t* n_out, int32_t* log, int log_cap, int max_n,
                   hipStream_t s) {
-  hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, s, st, out_tokens, n_out, log, log_cap);
+  hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, s, st, out_tokens, n_out, log, log_cap, max_n);
   return last_launch();
 }
 

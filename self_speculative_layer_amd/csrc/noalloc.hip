@@ -63,7 +63,7 @@ extern "C" int ssd_accept_noalloc(const float* p_logits_dev, const float* q_logi
   int rc = scratch_ptr(&sc);
   if (rc != SSD_OK) return rc;
   rc = launch_accept(p_logits_dev, q_logits_dev, vocab, draft_tokens_dev, n_drafted_dev, d_max, temperature, seed,
-                     nullptr, iteration, sc, sc + NA_ROWS, out_tokens_dev, n_out_dev, stream);
+                     nullptr, iteration, sc, sc + NA_ROWS, out_tokens_dev, n_out_dev, nullptr, stream);
   if (rc != 0) return na_fail(rc, "kernel launch failed");
   return SSD_OK;
 }

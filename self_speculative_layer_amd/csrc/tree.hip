@@ -227,6 +227,12 @@ __global__ void tree_accept_kernel(const ssd_row_stat* __restrict__ stats, const
   const int dp = max(min(*n_drafted, d), 0);
   const int nl = max(min(*n_leaves, max_leaves), 0);
   st->tree_leaf = -1;
+  for (int r = 0; r <= dp + nl; ++r)
+    if (isnan(stats[r].max)) {          // a row with non-finite logits: nothing is emitted
+      st->error_flags |= ERRF_NUMERIC;
+      *n_out = 0;
+      return;
+    }
   for (int j = 1; j <= dp; ++j) {
     const int a = stats[j - 1].argmax;
     out[j - 1] = a;

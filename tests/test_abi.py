@@ -100,3 +100,18 @@ def test_accept_noalloc_rejects_bad_arguments_on_the_host():
     assert L.ssd_accept_noalloc(*args(T=float("nan"))) == B.SSD_ERR_ARG
     assert L.ssd_accept_noalloc(*args(d=33)) == B.SSD_ERR_CAPACITY
     assert b"SSD_ACCEPT_NOALLOC_MAX_DRAFT" in L.ssd_last_error()
+
+
+def test_unknown_handles_are_rejected_on_the_host():
+    """Handles the library did not create (or has destroyed) are refused before any device work."""
+    L = B.lib()
+    bogus = ctypes.c_void_p(0x12345678)
+    st = B.ssd_state()
+    assert L.ssd_read_state(bogus, ctypes.byref(st), None) == B.SSD_ERR_ARG
+    assert b"live sequence" in L.ssd_last_error()
+    assert L.ssd_seq_destroy(bogus) == B.SSD_ERR_ARG
+    assert L.ssd_commit(bogus, bogus, bogus, None) == B.SSD_ERR_ARG
+    assert L.ssd_model_destroy(bogus) == B.SSD_ERR_ARG
+    assert b"live model" in L.ssd_last_error()
+    size = ctypes.c_size_t()
+    assert L.ssd_workspace_bytes(bogus, 16, 4, 64, ctypes.byref(size)) == B.SSD_ERR_ARG
