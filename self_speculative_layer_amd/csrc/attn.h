@@ -25,6 +25,10 @@ constexpr int ATT_MAXQ = 64;     // queries (rows x heads of a group) per fp32 w
 constexpr int ATTB_MAXQ = 16;    // queries per bf16 work item (one matrix-core query tile)
 constexpr int ATT_MAXW = 64;     // splits a block merge can hold (contexts up to 4096 positions)
 
+// A split's partial for one query: o[HD], then m and l, then two unused floats, so that every record
+// (and its (m, l) pair) starts 16-byte aligned.
+__host__ __device__ constexpr int att_rec(int hd) { return hd + 4; }
+
 // Queries (rows x heads of a KV group) one work item takes for storage type T.
 template <typename T>
 constexpr int att_maxq() { return sizeof(T) == 2 ? ATTB_MAXQ : ATT_MAXQ; }
@@ -86,6 +90,13 @@ template <bool DEV>
 __device__ __forceinline__ void part_store(float* p, float v) {
   if constexpr (DEV) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else *p = v;
+}
+// Two adjacent floats (p 8-byte aligned) in one store.
+template <bool DEV>
+__device__ __forceinline__ void part_store2(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  if constexpr (DEV) __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *(uint64_t*)p = v;
 }
 
 // Scores, softmax partials, P.V and the partial stores of one tile of at most 16 queries: queries
@@ -200,13 +211,11 @@ __device__ __forceinline__ void attn_tile_bf16(SM& sm, const bf16_t* __restrict_
         ohi += w == wave ? o[a][j][1] : Opw[w][qq][2 * dp + 1];
       }
       const int row = r0 + qi / G, head = g * G + qi % G;
-      float* dstp = part + (((size_t)row * H + head) * nsplit + s) * (HD + 2);
-      part_store<DEV>(dstp + 2 * dp, olo);
-      part_store<DEV>(dstp + 2 * dp + 1, ohi);
+      float* dstp = part + (((size_t)row * H + head) * nsplit + s) * att_rec(HD);
+      part_store2<DEV>(dstp + 2 * dp, olo, ohi);
       if (dp == 0) {
         const float l = ((sm.Sw[0][qq] + sm.Sw[1][qq]) + sm.Sw[2][qq]) + sm.Sw[3][qq];
-        part_store<DEV>(dstp + HD, sm.Mx[qq]);
-        part_store<DEV>(dstp + HD + 1, l);
+        part_store2<DEV>(dstp + HD, sm.Mx[qq], l);
       }
     }
   }
@@ -215,13 +224,17 @@ __device__ __forceinline__ void attn_tile_bf16(SM& sm, const bf16_t* __restrict_
 
 // bf16 work item (same contract as attn_partial_item below): QT tiles of at most 16 queries each, on
 // the split's keys and values staged once.
+// Returns the largest position the block's rows see (-1: the item had nothing to do) and sets *r1_out
+// (nullable) to the block's end row.  stop (nullable): a flag read with the first loads; set, the item
+// does nothing.
 template <int HD, int NW, bool DEV, int QT = 1, typename SM = AttnSmem<bf16_t, HD, NW>, bool LEAF = false>
-__device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
-                               const bf16_t* __restrict__ pool, const int* __restrict__ page_table, int PS,
-                               int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
-                               const int* __restrict__ pos, int r0, int RB, int g, int s, int nsplit,
-                               const bf16_t* __restrict__ local_kv, int local_start, int group_rows,
-                               float* __restrict__ part, int side0 = 0x7fffffff) {
+__device__ int attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
+                              const bf16_t* __restrict__ pool, const int* __restrict__ page_table, int PS,
+                              int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
+                              const int* __restrict__ pos, int r0, int RB, int g, int s, int nsplit,
+                              const bf16_t* __restrict__ local_kv, int local_start, int group_rows,
+                              float* __restrict__ part, int side0 = 0x7fffffff, const int* __restrict__ stop = nullptr,
+                              int* r1_out = nullptr) {
   static_assert(NW == 4, "four waves: 16 keys each");
   constexpr int NT = NW * 64;
   constexpr int KST = SM::KST;
@@ -235,7 +248,8 @@ __device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rmax = min(r0 + RB, M);
 
-  // ---- round 1: active rows, positions, the split's page ids, the queries
+  // ---- round 1: the stop flag, active rows, positions, the split's page ids, the queries
+  const int stopv = stop ? *stop : 0;
   const int na = nrows ? *nrows : M;
   int rp = 0;
   // rows >= side0 (tree leaves) see the cache up to the position before their own; their own key is
@@ -257,11 +271,12 @@ __device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
   __syncthreads();
   const int Ma = min(M, na);
   const int r1 = min(r0 + RB, Ma);
-  if (r1 <= r0) return;
+  if (stopv || r1 <= r0) return -1;
   int maxpos = sm.Rpos[r1 - 1 - r0];                  // positions increase along the rows, except leaf rows
   if (LEAF && side0 < r1)
     for (int i = 0; i < r1 - r0; ++i) maxpos = max(maxpos, sm.Rpos[i]);
-  if (key_beg > maxpos) return;
+  if (key_beg > maxpos) return -1;
+  if (r1_out) *r1_out = r1;
   const int nq = (r1 - r0) * G;
   const int key_end = min(key_beg + ATT_SPLIT, maxpos + 1);
   const int grp_base = group_rows > 0 ? (r0 / group_rows) * group_rows : 0;
@@ -304,6 +319,7 @@ __device__ void attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
   for (int t = 0; t * ATTB_MAXQ < nq; ++t)
     attn_tile_bf16<HD, NW, DEV>(sm, sm.Qs + t * ATTB_MAXQ * KST, sm.Op, t * ATTB_MAXQ, nq, G, r0, g, H, s, nsplit,
                                 key_beg, key_end, part);
+  return maxpos;
 }
 
 // fp32 work item (FMAs throughout).
@@ -423,7 +439,7 @@ __device__ void attn_item_scalar(AttnSmem<T, HD, NW>& sm, const T* __restrict__ 
       const float psum = wave_sum(pexp);
       sm.Pw[wave][lane] = pexp;
       __builtin_amdgcn_wave_barrier();
-      float* dstp = part + (((size_t)row * H + head) * nsplit + s) * (HD + 2);
+      float* dstp = part + (((size_t)row * H + head) * nsplit + s) * att_rec(HD);
       for (int d = lane; d < HD; d += 64) {
         float o = 0.f;
         // 16 keys' values are read before their 16 multiply-adds (one LDS round trip per 16 keys)
@@ -468,10 +484,10 @@ __device__ void attn_partial_item(AttnSmem<T, HD, NW>& sm, const T* __restrict__
                                   int s, int nsplit, const T* __restrict__ local_kv, int local_start, int group_rows,
                                   float* __restrict__ part, int side0 = 0x7fffffff) {
   if constexpr (sizeof(T) == 2)
-    attn_item_bf16<HD, NW, DEV, 1, AttnSmem<bf16_t, HD, NW>, LEAF>(sm, q, ldq, pool, page_table, PS, n_lpages, L,
-                                                                   layer, H, KVH, M, nrows, pos, r0, RB, g, s,
-                                                                   nsplit, local_kv, local_start, group_rows, part,
-                                                                   side0);
+    (void)attn_item_bf16<HD, NW, DEV, 1, AttnSmem<bf16_t, HD, NW>, LEAF>(sm, q, ldq, pool, page_table, PS, n_lpages,
+                                                                         L, layer, H, KVH, M, nrows, pos, r0, RB, g, s,
+                                                                         nsplit, local_kv, local_start, group_rows,
+                                                                         part, side0);
   else
     attn_item_scalar<T, HD, NW, DEV>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0,
                                      RB, g, s, nsplit, local_kv, local_start, group_rows, part);
@@ -482,7 +498,7 @@ template <int HD>
 __device__ __forceinline__ float attn_combine_value(const float* __restrict__ part, int nsplit, int row, int head,
                                                    int H, int p, int d) {
   const int ns = p / ATT_SPLIT + 1;
-  const float* pr = part + ((size_t)row * H + head) * nsplit * (HD + 2);
+  const float* pr = part + ((size_t)row * H + head) * nsplit * att_rec(HD);
   constexpr int B = 16;
   if (ns <= B) {
     // one round of loads
@@ -492,9 +508,9 @@ __device__ __forceinline__ float attn_combine_value(const float* __restrict__ pa
       mv[s] = -INFINITY;
       lv[s] = ov[s] = 0.f;
       if (s < ns) {
-        mv[s] = pr[s * (HD + 2) + HD];
-        lv[s] = pr[s * (HD + 2) + HD + 1];
-        ov[s] = pr[s * (HD + 2) + d];
+        mv[s] = pr[s * att_rec(HD) + HD];
+        lv[s] = pr[s * att_rec(HD) + HD + 1];
+        ov[s] = pr[s * att_rec(HD) + d];
       }
     }
     float m = -INFINITY;
@@ -513,95 +529,56 @@ __device__ __forceinline__ float attn_combine_value(const float* __restrict__ pa
   }
   float m = -INFINITY;
 #pragma unroll 16
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, pr[s * (HD + 2) + HD]);
+  for (int s = 0; s < ns; ++s) m = fmaxf(m, pr[s * att_rec(HD) + HD]);
   float l = 0.f, o = 0.f;
 #pragma unroll 16
   for (int s = 0; s < ns; ++s) {
-    const float w = expf(__fsub_rn(pr[s * (HD + 2) + HD], m));
-    l = fmaf(pr[s * (HD + 2) + HD + 1], w, l);
-    o = fmaf(pr[s * (HD + 2) + d], w, o);
+    const float w = expf(__fsub_rn(pr[s * att_rec(HD) + HD], m));
+    l = fmaf(pr[s * att_rec(HD) + HD + 1], w, l);
+    o = fmaf(pr[s * att_rec(HD) + d], w, o);
   }
   return __fdiv_rn(o, l);
 }
 
 // Merge by one block of the partials of rows r0 .. r1 - 1 (all G query heads
 // of KV head g), once every split has stored its partial (positions from
-// sm.Rpos, at most ATT_MAXW splits).  Same arithmetic as attn_combine_value,
-// with each (query, split) weight formed once: (1) every pair's m and l,
-// (2) per query the maximum and the weights, (3) per output element the
-// weighted sums of the splits' o and l in split order, and their quotient.  The o
-// values of the first MP dim pairs per thread are loaded together with (1).
-// The output is in the decode block layout.
+// sm.Rpos, at most ATT_MAXW splits).  Same arithmetic as attn_combine_value:
+// per query the maximum M of its splits' m, each split's weight
+// exp(m_s - M), then l and o as fma chains in split order, and o / l.
+// A group of 16 lanes (inside one wave) takes one query: lane j loads the
+// (m, l) of splits j, j + 16, ... and HD / 16 consecutive dimensions of o of
+// every split, all in one round of loads for contexts up to 64 * MCH
+// positions; the maximum is a butterfly over the group, and the weights pass
+// between the group's lanes through LDS, so the merge has no workgroup
+// barrier.  The output is in the decode block layout.
 // Rows >= side0 (tree leaves, whose partials cover keys up to their position - 1) have their own key
 // and value side_kv[(row - side0) * 2 + {0, 1}][KVH][HD] as one more split after the last: score
 // (q . k) / sqrt(HD) with q the row's query (q, ldq), sum 1, output v.
 template <int HD, int NW, bool LEAF = false>
-__device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __restrict__ part, int nsplit, int r0,
-                                 int r1, int G, int g, int H, bf16_t* __restrict__ out, int side0 = 0x7fffffff,
-                                 const bf16_t* __restrict__ side_kv = nullptr, const bf16_t* __restrict__ q = nullptr,
-                                 int ldq = 0, int KVH = 0) {
-  constexpr int NT = NW * 64;
-  constexpr int REC = HD + 2;
-  constexpr int PR = HD / 2;                          // dim pairs per query
-  constexpr int CH = 16;                              // splits per load round of (3)
-  constexpr int MP = 4;                               // dim pairs per thread in the first round
-  constexpr int P1 = ATTB_MAXQ * ATT_MAXW / NT;
+__device__ __forceinline__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __restrict__ part,
+                                                 int nsplit, int r0, int r1, int G, int g, int H,
+                                                 bf16_t* __restrict__ out, int side0 = 0x7fffffff,
+                                                 const bf16_t* __restrict__ side_kv = nullptr,
+                                                 const bf16_t* __restrict__ q = nullptr, int ldq = 0, int KVH = 0) {
+  static_assert(NW * 64 == 16 * ATTB_MAXQ, "one 16-lane group per query");
+  constexpr int REC = att_rec(HD);
+  constexpr int DPT = HD / 16;                        // dimensions per lane
+  constexpr int NV = DPT / 4;                         // 16-byte o loads per split
+  constexpr int MCH = HD == 128 ? 12 : 16;            // splits whose o comes with the first round
+  constexpr int MLR = ATT_MAXW / 16;                  // (m, l) pairs per lane
+  static_assert(DPT % 4 == 0 && ATT_MAXW % 16 == 0, "merge layout");
   const int tid = threadIdx.x;
   const int nq = (r1 - r0) * G;
-  const int npair = nq * PR;
-  float* Wt = sm.Wm;                                  // [query][split]: m, then the weight
-  float* Lv = sm.Wm + ATTB_MAXQ * ATT_MAXW;           // [query][split]: l
+  float* Wt = sm.Wm;                                  // [query][term]: the weights (leaves: first the score)
+  float* Lv = sm.Wm + ATTB_MAXQ * ATT_MAXW;           // [query][term]: l
   auto rec = [&](int qq, int sp) -> const float* {
     return part + (((size_t)(r0 + qq / G) * H + g * G + qq % G) * nsplit + sp) * REC;
   };
   auto nsplits = [&](int qq) { return min(sm.Rpos[qq / G] / ATT_SPLIT + 1, nsplit); };   // stored partials
   auto leaf = [&](int qq) { return LEAF && r0 + qq / G >= side0; };
-  auto nterms = [&](int qq) { return nsplits(qq) + (leaf(qq) ? 1 : 0); };                // merged terms
-  // term c of (query qq, dim pair d2): a stored partial's o, or the leaf's own value
-  auto oterm = [&](int qq, int c, int d2) -> float2 {
-    const int ns = nsplits(qq);
-    if (LEAF && leaf(qq) && c >= ns) {
-      const uint32_t v2 = *(const uint32_t*)(side_kv + ((size_t)(r0 + qq / G - side0) * 2 + 1) * KVH * HD +
-                                             (size_t)g * HD + d2);
-      return make_float2(__uint_as_float(v2 << 16), __uint_as_float(v2 & 0xFFFF0000u));
-    }
-    return *(const float2*)(rec(qq, min(c, ns - 1)) + d2);
-  };
 
-  // loads of (1) and of the first round of (3)
-  float mv[P1], lv[P1];
-#pragma unroll
-  for (int j = 0; j < P1; ++j) {
-    const int idx = tid + NT * j;
-    const int qq = idx / ATT_MAXW, sp = idx % ATT_MAXW;
-    if (qq < nq && sp < nsplits(qq)) {
-      const float* pr = rec(qq, sp);
-      mv[j] = pr[HD];
-      lv[j] = pr[HD + 1];
-    }
-  }
-  float2 ov[MP][CH];
-#pragma unroll
-  for (int x = 0; x < MP; ++x) {
-    const int pi = tid + NT * x;
-    if (pi < npair) {
-      const int qq = pi / PR, d2 = (pi % PR) * 2, ns = nterms(qq);
-#pragma unroll
-      for (int c = 0; c < CH; ++c) ov[x][c] = oterm(qq, min(c, ns - 1), d2);
-    }
-  }
-  // (1)
-#pragma unroll
-  for (int j = 0; j < P1; ++j) {
-    const int idx = tid + NT * j;
-    const int qq = idx / ATT_MAXW, sp = idx % ATT_MAXW;
-    if (qq < nq && sp < nsplits(qq)) {
-      Wt[idx] = mv[j];
-      Lv[idx] = lv[j];
-    }
-  }
   if (LEAF && side0 < r1) {
-    // the leaves' own terms: one wave per query, lanes over the dimensions, then a butterfly
+    // the leaves' own scores: one wave per query, lanes over the dimensions, then a butterfly
     const int lane = tid & 63, wave = tid >> 6;
     const float scale = 1.0f / sqrtf((float)HD);
     for (int qq = wave; qq < nq; qq += NW) {
@@ -613,80 +590,96 @@ __device__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, const float* __re
       for (int d = lane; d < HD; d += 64) acc = fmaf(bf2f(qr[d]), bf2f(kr[d]), acc);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      if (lane == 0) {
-        Wt[qq * ATT_MAXW + nsplits(qq)] = __fmul_rn(acc, scale);
-        Lv[qq * ATT_MAXW + nsplits(qq)] = 1.f;
-      }
+      if (lane == 0) Wt[qq * ATT_MAXW + nsplits(qq)] = __fmul_rn(acc, scale);
     }
+    __syncthreads();
   }
-  __syncthreads();
-  // (2) per query the maximum of its splits' m and the weights; a wave takes one query at a time
-  // (lane = split).  l is accumulated in (3), next to o, in split order.
-  {
-    const int lane = tid & 63, wave = tid >> 6;
-    static_assert(ATT_MAXW <= 64, "one lane per split");
-    for (int qq = wave; qq < nq; qq += NW) {
-      const bool on = lane < nterms(qq);
-      const float mv = on ? Wt[qq * ATT_MAXW + lane] : -INFINITY;
-      float m = mv;
+  const int qq = tid >> 4, j = tid & 15;
+  if (qq >= nq) return;                               // whole groups; no barrier follows
+  const int ns = nsplits(qq);
+  const bool lf = leaf(qq);
+  const int nt = ns + (lf ? 1 : 0);                   // merged terms
+  const int d0 = j * DPT;
+  // term c's o at dimensions d0 .. d0 + DPT - 1: a stored partial's, or the leaf's own value
+  auto oload = [&](int c, f32x4 (&v)[NV]) {
+    if (LEAF && c >= ns) {
+      const bf16_t* vr = side_kv + ((size_t)(r0 + qq / G - side0) * 2 + 1) * KVH * HD + (size_t)g * HD + d0;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      if (on) Wt[qq * ATT_MAXW + lane] = expf(__fsub_rn(mv, m));
-    }
-  }
-  __syncthreads();
-  // (3): splits [c0, ns) of one dim pair accumulated into o, and l; then the store
-  auto rest = [&](int qq, int d2, int ns, int c0, float2& o, float& l) {
-    const float* w = Wt + qq * ATT_MAXW;
-    const float* lw = Lv + qq * ATT_MAXW;
-    for (; c0 < ns; c0 += CH) {
-      float2 v[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) v[c] = oterm(qq, min(c0 + c, ns - 1), d2);
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        if (c0 + c < ns) {
-          l = fmaf(lw[c0 + c], w[c0 + c], l);
-          o.x = fmaf(v[c].x, w[c0 + c], o.x);
-          o.y = fmaf(v[c].y, w[c0 + c], o.y);
-        }
+      for (int x = 0; x < NV; ++x) {
+        const uint2 u = *(const uint2*)(vr + 4 * x);
+        v[x] = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xFFFF0000u)};
       }
+      return;
     }
+#pragma unroll
+    for (int x = 0; x < NV; ++x) v[x] = *(const f32x4*)(rec(qq, c) + d0 + 4 * x);
   };
-  auto store = [&](int qq, int d2, float2 o, float l) {
-    const int row = r0 + qq / G, head = g * G + qq % G;
-    bf16_t* dst = out + dec_act_index(row, head * HD + d2);   // d2 even: d2 + 1 is the next element
-    st(dst, __fdiv_rn(o.x, l));
-    st(dst + 1, __fdiv_rn(o.y, l));
-  };
+
+  // one round of loads: (m, l) of the lane's terms, o of the first MCH terms (clamped to the last)
+  float2 ml[MLR];
 #pragma unroll
-  for (int x = 0; x < MP; ++x) {
-    const int pi = tid + NT * x;
-    if (pi < npair) {
-      const int qq = pi / PR, d2 = (pi % PR) * 2, ns = nterms(qq);
-      const float* w = Wt + qq * ATT_MAXW;
-      const float* lw = Lv + qq * ATT_MAXW;
-      float2 o = make_float2(0.f, 0.f);
-      float l = 0.f;
+  for (int r = 0; r < MLR; ++r) {
+    const int c = j + 16 * r;
+    ml[r] = make_float2(-INFINITY, 0.f);
+    if (c < ns) ml[r] = *(const float2*)(rec(qq, c) + HD);
+    else if (LEAF && c < nt) ml[r] = make_float2(Wt[qq * ATT_MAXW + c], 1.f);
+  }
+  f32x4 ov[MCH][NV];
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        if (c < ns) {
-          l = fmaf(lw[c], w[c], l);
-          o.x = fmaf(ov[x][c].x, w[c], o.x);
-          o.y = fmaf(ov[x][c].y, w[c], o.y);
-        }
-      }
-      rest(qq, d2, ns, CH, o, l);
-      store(qq, d2, o, l);
+  for (int c = 0; c < MCH; ++c) oload(min(c, nt - 1), ov[c]);
+  // the maximum over the query's terms, then each lane's terms' weights (and l) into LDS
+  float m = ml[0].x;
+#pragma unroll
+  for (int r = 1; r < MLR; ++r) m = fmaxf(m, ml[r].x);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+#pragma unroll
+  for (int r = 0; r < MLR; ++r) {
+    const int c = j + 16 * r;
+    if (c < nt) {
+      Wt[qq * ATT_MAXW + c] = expf(__fsub_rn(ml[r].x, m));
+      Lv[qq * ATT_MAXW + c] = ml[r].y;
     }
   }
-  for (int pi = tid + NT * MP; pi < npair; pi += NT) {
-    const int qq = pi / PR, d2 = (pi % PR) * 2;
-    float2 o = make_float2(0.f, 0.f);
-    float l = 0.f;
-    rest(qq, d2, nterms(qq), 0, o, l);
-    store(qq, d2, o, l);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // o and l in term order, then o / l
+  const float* w = Wt + qq * ATT_MAXW;
+  const float* lw = Lv + qq * ATT_MAXW;
+  f32x4 o[NV];
+#pragma unroll
+  for (int x = 0; x < NV; ++x) o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  auto add = [&](int c, const f32x4 (&v)[NV]) {
+    const float wc = w[c];
+    l = fmaf(lw[c], wc, l);
+#pragma unroll
+    for (int x = 0; x < NV; ++x)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[x][i] = fmaf(v[x][i], wc, o[x][i]);
+  };
+#pragma unroll
+  for (int c = 0; c < MCH; ++c)
+    if (c < nt) add(c, ov[c]);
+  for (int c0 = MCH; c0 < nt; c0 += MCH) {            // contexts past 64 * MCH positions
+#pragma unroll
+    for (int c = 0; c < MCH; ++c) oload(min(c0 + c, nt - 1), ov[c]);
+#pragma unroll
+    for (int c = 0; c < MCH; ++c)
+      if (c0 + c < nt) add(c0 + c, ov[c]);
   }
+  const int row = r0 + qq / G, head = g * G + qq % G;
+  bf16_t* dst = out + dec_act_index(row, head * HD + d0);   // d0 % DPT == 0: DPT contiguous elements
+  uint32_t pk[DPT / 2];
+#pragma unroll
+  for (int x = 0; x < NV; ++x) {
+    pk[2 * x] = (uint32_t)f2bf(__fdiv_rn(o[x][0], l)) | ((uint32_t)f2bf(__fdiv_rn(o[x][1], l)) << 16);
+    pk[2 * x + 1] = (uint32_t)f2bf(__fdiv_rn(o[x][2], l)) | ((uint32_t)f2bf(__fdiv_rn(o[x][3], l)) << 16);
+  }
+  if constexpr (DPT == 8) *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  else *(uint2*)dst = make_uint2(pk[0], pk[1]);
 }
 
 // blocked: out in the decode block layout (ldo unused), else rows of stride ldo.

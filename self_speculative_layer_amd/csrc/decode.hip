@@ -423,21 +423,21 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(
     const int* __restrict__ pos, int RB, int nsplit, float* __restrict__ part, T* __restrict__ out, int ldo,
     unsigned* __restrict__ counters, const int* __restrict__ stop, const int* __restrict__ side_from,
     const T* __restrict__ side_kv) {
-  if (stop && *stop) return;
+  static_assert(sizeof(T) == 2, "bf16 items");
   const int g = blockIdx.x, s = blockIdx.y, rbk = blockIdx.z;
-  const int Ma = nrows ? min(M, *nrows) : M;
-  const int r0 = rbk * RB, r1 = min(r0 + RB, Ma);
-  if (r1 <= r0) return;
+  const int r0 = rbk * RB;
+  if (r0 >= M) return;
   const int side0 = LEAF ? *side_from : 0x7fffffff;
-  int maxp = pos[r1 - 1];                                        // positions increase, except leaf rows
-  if (LEAF && side0 < r1)
-    for (int r = r0; r < r1; ++r) maxp = max(maxp, pos[r] - (r >= side0 ? 1 : 0));
-  const int n_act = min(maxp / ATT_SPLIT + 1, nsplit);   // splits holding a key some row of the block sees
-  if (s >= n_act) return;
   __shared__ AttnSmem<T, HD, 4> sm;
   __shared__ int is_last;
-  attn_partial_item<T, HD, 4, true, LEAF>(sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0,
-                                    RB, g, s, nsplit, nullptr, 0, 0, part, side0);
+  // the stop flag, the active-row count, the positions, the page ids and the queries arrive in one round
+  // of loads; maxp: the largest position a row of the block sees (-1: nothing to do)
+  int r1 = r0;
+  const int maxp = attn_item_bf16<HD, 4, true, 1, AttnSmem<bf16_t, HD, 4>, LEAF>(
+      sm, q, ldq, pool, page_table, PS, n_lpages, L, layer, H, KVH, M, nrows, pos, r0, RB, g, s, nsplit, nullptr, 0,
+      0, part, side0, stop, &r1);
+  if (maxp < 0) return;
+  const int n_act = min(maxp / ATT_SPLIT + 1, nsplit);   // splits holding a key some row of the block sees
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {

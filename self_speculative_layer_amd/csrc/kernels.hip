@@ -712,7 +712,7 @@ int attention_nsplit(int max_ctx) { return (max_ctx + ATT_SPLIT - 1) / ATT_SPLIT
 
 size_t attention_partial_floats(int max_rows, int H, int head_dim, int max_ctx) {
   const int nsplit = attention_nsplit(max_ctx);
-  return (size_t)max_rows * H * nsplit * (head_dim + 2);
+  return (size_t)max_rows * H * nsplit * att_rec(head_dim);
 }
 
 template <typename T, int HD>
