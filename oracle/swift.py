@@ -125,27 +125,35 @@ def bo_proposals(obs_masks, obs_scores, inc_score, pool, n_cand):
 
 
 def search(score_fn, L, init_mask, n_skip, n_cand, max_steps, patience, target, seed, sublayers=False, bo_every=0,
-           pool_factor=8, bo_window=256):
+           pool_factor=8, bo_window=256, step0=0, unimproved0=0, out=None):
     """Random search with the periodic Bayesian-optimisation step.  score_fn(list
     of masks) -> scores.  Returns the final incumbent mask, its score, the
     number of steps run and the per-step history [(proposal masks, their
-    scores, incumbent score after the step)]."""
+    scores, incumbent score after the step)].
+
+    A search that continues earlier ones (the on-the-fly alternation below)
+    numbers its steps from step0 (proposal counters and the Bayesian schedule
+    use step0 + t) and starts its run of unimproved steps at unimproved0; the
+    run at the end goes to out["unimproved"] when out is a dict (and the
+    starting plan's score to out["score0"])."""
     inc = np.asarray(init_mask, np.uint8).copy()
     inc_score = None
-    unimproved = 0
+    unimproved = unimproved0
     history = []
     obs_m, obs_s = [], []
     t = 0
     while t < max_steps:
+        st = step0 + t
         props = None
-        if bo_every > 0 and t > 0 and t % bo_every == 0:
-            pool = [propose_mask(L, n_skip, seed, t, c, sublayers) for c in range(pool_factor * n_cand)]
+        if bo_every > 0 and st > 0 and st % bo_every == 0 and obs_s:
+            pool = [propose_mask(L, n_skip, seed, st, c, sublayers) for c in range(pool_factor * n_cand)]
             props = bo_proposals(obs_m[-bo_window:], obs_s[-bo_window:], inc_score, pool, n_cand)
         if props is None:
-            props = [propose_mask(L, n_skip, seed, t, c, sublayers) for c in range(n_cand)]
+            props = [propose_mask(L, n_skip, seed, st, c, sublayers) for c in range(n_cand)]
         if t == 0:
             sc = list(score_fn([inc] + props))
             inc_score, sc = sc[0], sc[1:]
+            score0 = inc_score
         else:
             sc = list(score_fn(props))
         if t == 0:
@@ -163,4 +171,92 @@ def search(score_fn, L, init_mask, n_skip, n_cand, max_steps, patience, target, 
         t += 1
         if inc_score > target or unimproved >= patience:
             break
+    if out is not None and t > 0:
+        out["unimproved"] = unimproved
+        out["score0"] = score0
     return inc, inc_score, t, history
+
+
+def swift_generate(model, prompt, n_gen, n_skip, gamma, n_cand, steps_per_phase, max_steps, patience, target, d,
+                   tau=0.0, T=0.0, seed=3, bo_every=0, sublayers=False, accumulate=None, init_mask=None,
+                   capacity=None):
+    """SWIFT's on-the-fly alternation of context accumulation and layer-set
+    optimisation during generation (SWIFT digest §4, §4.1.1, §4.1.2, §5.3,
+    §B.2, §D.2).
+
+    Readings (the pages name the phases and their stopping rules, not the
+    schedule between them):
+      * generation starts with init_mask (default: the uniform plan of n_skip
+        whole layers; a sub-layer search must be given one) and
+        runs self-speculative iterations (oracle.ssd: draft, verify, accept)
+        with the plan in use;
+      * once `accumulate` tokens (default gamma) have been committed since the
+        previous optimisation phase (for the first phase: since the prefill's
+        token), and optimisation is not over, a phase runs on the window of the
+        last gamma + 1 committed tokens: `search` with the plan in use as the
+        starting incumbent (scored afresh on this window together with the
+        phase's first proposals), steps numbered on from the earlier phases
+        (proposal counters and the Bayesian schedule), the run of unimproved
+        steps carried over, at most steps_per_phase steps;
+      * the plan in use becomes the phase's final incumbent, which differs
+        from it only when some proposal scored strictly higher on the window;
+      * optimisation is over for good once max_steps steps have run in all
+        phases, once the run of unimproved steps reaches patience, or once the
+        incumbent's score exceeds target; generation goes on with the last plan.
+    With accumulate = steps_per_phase = 1 this is one optimisation step after
+    every iteration on a window that slides with the generated text.
+
+    Returns (tokens [n_gen], trace): trace["phases"] holds, per phase, n_out
+    (committed tokens when it ran), pos0, the plan before and after, the
+    incumbent's score, the steps run and the per-step history;
+    trace["plans"][k] is the plan iteration k (1-based) drafted with and
+    trace["n_out"][k] the committed count after it; trace also has the final
+    state (steps, unimproved, done).
+    """
+    from . import model as mdl
+    from . import ssd as ossd
+    P = len(prompt)
+    L = model.L
+    acc = gamma if accumulate is None else accumulate
+    if init_mask is None:
+        if sublayers:
+            raise ValueError("a sub-layer search needs its starting plan")
+        init_mask = layers_to_mask(L, uniform_skip_layers(L, n_skip))
+    plan = np.asarray(init_mask, np.uint8).copy()
+    kv = mdl.KVCache(model.shape, capacity or (P + n_gen + d + 2))
+    out = [ossd.pick(ossd.prefill(model, kv, prompt), T, seed, 0, 0, philox.PURPOSE_SAMPLE)]
+    trace = {"phases": [], "plans": [None], "n_out": [1]}
+    steps, unimproved, done, last = 0, 0, max_steps <= 0, 1
+    it = 1
+    while len(out) < n_gen:
+        n = P + len(out)
+        b = mdl.first_skipped_layer(plan, L)
+        y0 = out[-1]
+        drafts, zq, hb = ossd.draft(model, kv, y0, n, plan, d, tau, T, seed, it)
+        zp = ossd.verify(model, kv, y0, drafts, n, b, hb)
+        emitted = ossd.accept_greedy(zp, drafts) if T == 0 else ossd.accept_sampled(zp, zq, drafts, T, seed, it)
+        trace["plans"].append(plan.copy())
+        out.extend(emitted)
+        trace["n_out"].append(len(out))
+        it += 1
+        if not done and len(out) - last >= acc and len(out) >= gamma + 1:
+            n_out = len(out)
+            pos0 = P + n_out - 1 - gamma
+            window = out[n_out - 1 - gamma:n_out]
+
+            def score_fn(masks):
+                return ossd.score_masks(model, kv, window, pos0, masks)[0]
+            st = {}
+            inc, sc, ran, hist = search(score_fn, L, plan, n_skip, n_cand, min(steps_per_phase, max_steps - steps),
+                                        patience, target, seed, sublayers, bo_every, step0=steps,
+                                        unimproved0=unimproved, out=st)
+            trace["phases"].append({"n_out": n_out, "pos0": pos0, "before": plan.copy(), "after": inc.copy(),
+                                    "score0": st["score0"], "score": sc, "steps": ran, "history": hist,
+                                    "unimproved0": unimproved, "step0": steps})
+            plan = inc.copy()
+            steps += ran
+            unimproved = st["unimproved"]
+            done = steps >= max_steps or unimproved >= patience or sc > target
+            last = n_out
+    trace.update(steps=steps, unimproved=unimproved, done=done)
+    return out[:n_gen], trace
