@@ -221,7 +221,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="default 64 (SSD steps), 8 (scoring steps)")
     ap.add_argument("--warmup", type=int, default=None, help="default 8 (SSD steps), 2 (scoring steps)")
-    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS) + sorted(SCORING) + ["exit7b"])
+    ap.add_argument("--workload", default="7b",
+                    choices=sorted(WORKLOADS) + sorted(SCORING) + ["exit7b", "swiftotf13b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ar-steps", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -248,6 +249,11 @@ def main():
     from synth import device as sdev
     from self_speculative_layer_amd import binding as B
 
+    if args.workload == "swiftotf13b":
+        args.steps = 8 if args.steps is None else args.steps
+        args.warmup = 0 if args.warmup is None else args.warmup
+        run_swift_otf(args)
+        return
     if args.workload == "exit7b":
         args.steps = 64 if args.steps is None else args.steps
         args.warmup = 8 if args.warmup is None else args.warmup
@@ -508,6 +514,72 @@ def run_exit(args):
                      "avg_launch_us": round(prof_ms / max(prof_n, 1) * 1e3, 3)},
         "step_GBps": round(step_bytes / (ms / 1e3) / 1e9, 1),
         "specee_features_us": round(feat_us, 2),
+    }
+    seq.close()
+    model.close()
+    print(json.dumps(result), flush=True)
+
+
+def run_swift_otf(args):
+    """SWIFT on the fly (ssd_swift_generate): self-speculative iterations with the plan in use and, after every
+    32 committed tokens, an optimisation phase of at most 8 search steps (15 proposals each) on the last 33
+    committed tokens; one step = one call generating 32 tokens (its iterations and the phase that follows)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import device as sdev
+    from self_speculative_layer_amd import binding as B
+
+    shape = synth.LLAMA13B
+    L = shape.n_layers
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    tensors = sdev.build_weights(shape)
+    model = B.Model(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
+                    shape.vocab, shape.dtype, tensors)
+    K, W, P, gamma, n_skip, n_cand, per, d = args.steps, args.warmup, 1024, 32, 20, 15, 8, 8
+    n_gen = (K + W) * gamma
+    seq = B.Sequence(model, max_ctx=P + n_gen + 64, max_rows=(n_cand + 1) * gamma, max_draft=d, device=dev)
+    B.ssd_prefill(seq.handle, torch.from_numpy(synth.prompt_tokens(P, shape.vocab)).to(dev), 1.0,
+                  synth.SEED_SAMPLING)
+    cfg = B.swift_config(gamma, n_skip, n_cand, per, 1000, 300, 0.95, d, synth.SEED_SAMPLING, bo_every=25,
+                         conf_thresh=0.8, temperature=1.0)
+    st = B.ssd_swift_begin(seq.handle, cfg)
+    plan = np.ascontiguousarray(B.ssd_uniform_mask(L, n_skip))
+
+    def call():
+        B.ssd_swift_generate(seq.handle, cfg, st, plan, gamma, seq.draft_tokens, seq.draft_logits, seq.n_drafted,
+                             seq.verify_logits, seq.out_tokens, seq.n_out)
+
+    for _ in range(W):
+        call()
+    s0 = B.ssd_read_state(seq.handle)
+    it0, ph0, steps0 = st.iterations, st.phases, st.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s1 = B.ssd_read_state(seq.handle)
+    tokens = s1.n_out - s0.n_out
+    result = {
+        "metric": "committed tokens/s (batch 1) with SWIFT's on-the-fly layer-set optimisation",
+        "value": round(tokens / wall, 3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(wall * 1e3 / K, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded random-init weights and uniform random prompt)",
+        "config": {"workload": "LLaMA-2-13B-shaped bf16 decoder, SWIFT on the fly: uniform start plan of 20 skipped "
+                               "layers, a phase of <= 8 search steps (15 proposals of 20 layers, Bayesian step "
+                               "every 25 steps) after every 32 committed tokens on the last 33, d<=8, confidence "
+                               "stop 0.8, T=1.0, 1024-token random prompt",
+                   "step": "one ssd_swift_generate call of 32 tokens (its iterations and the phase after them)"},
+        "timing": "wall clock around the calls (each iteration and each optimisation step synchronises the stream)",
+        "tokens": tokens, "iterations": st.iterations - it0,
+        "M_tokens_per_iteration": round(tokens / max(st.iterations - it0, 1), 3),
+        "phases": st.phases - ph0, "optimisation_steps": st.steps - steps0, "switches": st.switches,
+        "final_score": None if st.score != st.score else round(float(st.score), 4), "optimisation_done": bool(st.done),
+        "final_plan_layers": [int(l) for l in np.nonzero(plan[::2])[0]],
     }
     seq.close()
     model.close()

@@ -409,6 +409,63 @@ int ssd_swift_search(ssd_seq* seq, const int32_t* window_dev, int pos0, int gamm
                      int n_skip, int sublayers, int n_cand, int max_steps, int patience, float target, uint64_t seed,
                      int bo_every, uint8_t* best_mask_host, float* best_score, int* n_steps, hipStream_t stream);
 
+/* ---- SWIFT on the fly (next row f1; [SWIFT] §4, §4.1.1, §4.1.2, §5.3, §B.2, §D.2) ----
+ * Generation alternates self-speculative iterations (ssd_draft, ssd_verify with reuse, ssd_accept,
+ * ssd_commit) with the plan in use and optimisation phases (steps of ssd_swift_search) on the most recent
+ * context window.  Readings (the pages name the phases and their stopping rules, not the schedule between
+ * them): a phase runs once `accumulate` tokens (<= 0: gamma) have been committed since the previous phase
+ * (the first: since ssd_swift_begin), optimisation is not over and at least gamma + 1 tokens have been
+ * generated; its window is the last gamma + 1 committed tokens (the newest at position kvlen).  The phase
+ * is ssd_swift_search with the plan in use as the starting incumbent (scored afresh on the window), at most
+ * steps_per_phase steps numbered on from the earlier phases (proposal counters and the Bayesian schedule
+ * bo_every count every phase's steps; the Gaussian process sees the current phase's plans), and the run of
+ * unimproved steps carried over.  The plan becomes the phase's final incumbent (a different plan only when
+ * a proposal scored strictly higher on the window).  Optimisation ends for good once max_steps steps have
+ * run in all, once the unimproved run reaches patience, or once a phase ends with a score above target;
+ * generation goes on with the last plan.  The pages' settings: gamma 32, max_steps 1000, patience 300,
+ * target 0.95, bo_every 25.  With accumulate = steps_per_phase = 1 the window slides: one optimisation
+ * step after every iteration. */
+typedef struct ssd_swift_config {
+  int32_t gamma;             /* window: tokens each candidate predicts */
+  int32_t accumulate;        /* committed tokens between phases (<= 0: gamma) */
+  int32_t n_skip, sublayers; /* candidate size, as ssd_swift_propose */
+  int32_t n_cand;            /* proposals per step; (n_cand + 1) * gamma <= max_rows, n_cand + 1 <= 64 */
+  int32_t steps_per_phase;   /* >= 1 */
+  int32_t max_steps;         /* in all phases; 0 = never optimise */
+  int32_t patience;          /* >= 1 */
+  float target;
+  int32_t bo_every;          /* 0 = no Bayesian steps */
+  int32_t d;                 /* drafts per iteration, 1..max_draft */
+  float conf_thresh, temperature;
+  uint64_t seed;             /* the proposals' and the iterations' draws */
+} ssd_swift_config;
+
+typedef struct ssd_swift_state {
+  int32_t steps;             /* optimisation steps run so far */
+  int32_t unimproved;        /* the current run of steps without improvement */
+  int32_t done;              /* 1: optimisation is over */
+  int32_t last_phase_n_out;  /* n_out when the last phase ran (at ssd_swift_begin: the n_out then) */
+  int32_t phases, switches;  /* phases run, and how many of them changed the plan */
+  float score;               /* the plan's matchness on the last phase's window (NaN before the first) */
+  int32_t iterations;        /* self-speculative iterations run by ssd_swift_generate */
+} ssd_swift_state;
+
+/* Starts the controller on a prefilled sequence: *state = no steps, no phases, windows counted from the
+ * sequence's current n_out (the call synchronises the stream to read it); done = 1 when max_steps is 0.
+ * The starting plan is the caller's plan_host[2L] (e.g. ssd_uniform_mask). */
+int ssd_swift_begin(ssd_seq* seq, const ssd_swift_config* cfg, ssd_swift_state* state, hipStream_t stream);
+
+/* Runs iterations with plan_host[2L] (in: the plan in use; out: the plan after the last phase) until at
+ * least n_tokens more tokens are committed (an iteration commits 1..d + 1), with the phases above in
+ * between; *state is updated.  The iterations' buffers are the caller's, as in ssd_draft / ssd_verify /
+ * ssd_accept: draft_tokens_dev[d], draft_logits_dev[d * V], n_drafted_dev[1], verify_logits_dev[(d + 1) * V],
+ * out_tokens_dev[d + 1], n_out_dev[1].  Synchronises the stream after every iteration (4-byte state read:
+ * the committed count decides when a phase is due) and once per optimisation step.  An iteration that
+ * commits nothing (non-finite logits) ends the call with SSD_ERR_NUMERIC. */
+int ssd_swift_generate(ssd_seq* seq, const ssd_swift_config* cfg, ssd_swift_state* state, uint8_t* plan_host,
+                       int n_tokens, int32_t* draft_tokens_dev, float* draft_logits_dev, int32_t* n_drafted_dev,
+                       float* verify_logits_dev, int32_t* out_tokens_dev, int32_t* n_out_dev, hipStream_t stream);
+
 /* SpecEE exit features (next row f4; [SpecEE] §4.3.1) of rows hidden states h_dev [rows][D] (fp32, a
  * layer's output in the residual stream) for k speculative tokens tokens_dev[k] (1 <= k <= 16):
  * features_dev[r][0..k) = speculative-token logits z_j = bf16(h * g_final) . W_lm[t_j] / rms(h) (the shared

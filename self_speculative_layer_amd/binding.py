@@ -17,7 +17,8 @@ EXPORTS = ["ssd_model_create", "ssd_model_destroy", "ssd_packed_bf16_bytes", "ss
            "ssd_workspace_bytes", "ssd_seq_create",
            "ssd_seq_destroy", "ssd_prefill", "ssd_decode_ar", "ssd_decode_exit", "ssd_draft", "ssd_verify",
            "ssd_accept", "ssd_accept_noalloc", "ssd_commit", "ssd_tree_candidates", "ssd_verify_tree", "ssd_accept_tree",
-           "ssd_score_masks", "ssd_uniform_mask", "ssd_swift_propose", "ssd_swift_search", "ssd_specee_features",
+           "ssd_score_masks", "ssd_uniform_mask", "ssd_swift_propose", "ssd_swift_search", "ssd_swift_begin",
+           "ssd_swift_generate", "ssd_specee_features",
            "ssd_row_stats",
            "ssd_read_state", "ssd_read_output", "ssd_last_error",
            "ssd_profile_enable", "ssd_profile_disable", "ssd_profile_read", "ssd_probe_read"]
@@ -45,6 +46,20 @@ class ssd_model_desc(ctypes.Structure):
 class ssd_row_stat(ctypes.Structure):
     _fields_ = [("max", ctypes.c_float), ("argmax", ctypes.c_int32), ("max2", ctypes.c_float),
                 ("lse", ctypes.c_float), ("conf", ctypes.c_float), ("sample", ctypes.c_int32)]
+
+
+class ssd_swift_config(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_int32), ("accumulate", ctypes.c_int32), ("n_skip", ctypes.c_int32),
+                ("sublayers", ctypes.c_int32), ("n_cand", ctypes.c_int32), ("steps_per_phase", ctypes.c_int32),
+                ("max_steps", ctypes.c_int32), ("patience", ctypes.c_int32), ("target", ctypes.c_float),
+                ("bo_every", ctypes.c_int32), ("d", ctypes.c_int32), ("conf_thresh", ctypes.c_float),
+                ("temperature", ctypes.c_float), ("seed", ctypes.c_uint64)]
+
+
+class ssd_swift_state(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int32), ("unimproved", ctypes.c_int32), ("done", ctypes.c_int32),
+                ("last_phase_n_out", ctypes.c_int32), ("phases", ctypes.c_int32), ("switches", ctypes.c_int32),
+                ("score", ctypes.c_float), ("iterations", ctypes.c_int32)]
 
 
 class ssd_state(ctypes.Structure):
@@ -93,6 +108,9 @@ def lib():
             "ssd_specee_features": [P, P, I, P, I, P, P, P],
             "ssd_swift_propose": [I, I, I, U64, I, I, P],
             "ssd_swift_search": [P, P, I, I, P, I, I, I, I, I, F, U64, I, P, ctypes.POINTER(F), ctypes.POINTER(I), P],
+            "ssd_swift_begin": [P, ctypes.POINTER(ssd_swift_config), ctypes.POINTER(ssd_swift_state), P],
+            "ssd_swift_generate": [P, ctypes.POINTER(ssd_swift_config), ctypes.POINTER(ssd_swift_state), P, I, P, P, P,
+                                   P, P, P, P],
             "ssd_row_stats": [P, I, I, F, U64, ctypes.c_int32, P, P],
             "ssd_read_state": [P, ctypes.POINTER(ssd_state), P],
             "ssd_read_output": [P, P, I, ctypes.POINTER(I), P],
@@ -285,6 +303,28 @@ def ssd_swift_search(seq, window, pos0, gamma, init_mask, n_skip, n_cand, max_st
                                  out.ctypes.data_as(ctypes.c_void_p),
                                  ctypes.byref(sc), ctypes.byref(ns), _stream(stream)))
     return out, float(sc.value), int(ns.value)
+
+
+def swift_config(gamma, n_skip, n_cand, steps_per_phase, max_steps, patience, target, d, seed, accumulate=0,
+                 sublayers=False, bo_every=0, conf_thresh=0.0, temperature=0.0):
+    return ssd_swift_config(gamma, accumulate, n_skip, 1 if sublayers else 0, n_cand, steps_per_phase, max_steps,
+                            patience, target, bo_every, d, conf_thresh, temperature, seed)
+
+
+def ssd_swift_begin(seq, cfg, stream=None):
+    st = ssd_swift_state()
+    check(lib().ssd_swift_begin(seq, ctypes.byref(cfg), ctypes.byref(st), _stream(stream)))
+    return st
+
+
+def ssd_swift_generate(seq, cfg, state, plan, n_tokens, draft_tokens, draft_logits, n_drafted, verify_logits,
+                       out_tokens, n_out, stream=None):
+    """plan: a C-contiguous uint8 numpy array [2L], updated in place; state: updated in place."""
+    import numpy as np
+    assert isinstance(plan, np.ndarray) and plan.dtype == np.uint8 and plan.flags["C_CONTIGUOUS"]
+    check(lib().ssd_swift_generate(seq, ctypes.byref(cfg), ctypes.byref(state), plan.ctypes.data_as(ctypes.c_void_p),
+                                   n_tokens, _ptr(draft_tokens), _ptr(draft_logits), _ptr(n_drafted),
+                                   _ptr(verify_logits), _ptr(out_tokens), _ptr(n_out), _stream(stream)))
 
 
 def ssd_specee_features(model, h, rows, tokens, k, prev_probs, features, stream=None):

@@ -12,6 +12,7 @@
 #include <new>
 #include <string>
 #include <unordered_set>
+#include <limits>
 #include <vector>
 
 #include "kernels.h"
@@ -945,6 +946,7 @@ void propose_layers(int L, int n_skip, int sublayers, uint64_t seed, int step, i
 // observed scores are all equal (nothing to model).
 bool bo_rank(const uint8_t* obs, const double* ys, int n, double inc_score, const uint8_t* pool, int P, size_t ML,
              int n_cand, std::vector<int>& picks) {
+  if (n < 1) return false;
   double mean = 0.0;
   for (int i = 0; i < n; ++i) mean += ys[i];
   mean /= n;
@@ -1033,36 +1035,33 @@ extern "C" int ssd_swift_propose(int n_layers, int n_skip, int sublayers, uint64
   return SSD_OK;
 }
 
-extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0, int gamma,
-                                const uint8_t* init_mask_host, int n_skip, int sublayers, int n_cand, int max_steps,
-                                int patience, float target, uint64_t seed, int bo_every, uint8_t* best_mask_host,
-                                float* best_score, int* n_steps, hipStream_t s) {
-  CHECK_SEQ(q);
-  CHECK_ARG(q && window_dev && init_mask_host && best_mask_host && best_score && n_steps, "null argument");
+// One run of the search on a window: steps numbered step0, step0 + 1, ... (proposal counters and the
+// Bayesian schedule), the run of unimproved steps starting at unimproved0.  inc: the starting plan in, the
+// final incumbent out.
+int swift_phase(ssd_seq* q, const int32_t* window_dev, int pos0, int gamma, std::vector<uint8_t>& inc, int n_skip,
+                int sublayers, int n_cand, int max_steps, int patience, float target, uint64_t seed, int bo_every,
+                int step0, int unimproved0, float* score, int* n_steps, int* unimproved_out, hipStream_t s) {
   const int L = q->m->d.n_layers;
-  CHECK_ARG(n_skip >= 0 && n_skip <= (sublayers ? 2 : 1) * L && n_cand >= 1 && n_cand + 1 <= 64 && max_steps >= 1 &&
-                patience >= 1 && bo_every >= 0,
-            "bad search parameters");
-  if ((n_cand + 1) * gamma > q->max_rows) return fail(SSD_ERR_CAPACITY, "(n_cand + 1) * gamma exceeds max_rows");
   const size_t ML = 2 * (size_t)L;
-  std::vector<uint8_t> inc(init_mask_host, init_mask_host + ML), masks((n_cand + 1) * ML);
+  std::vector<uint8_t> masks((n_cand + 1) * ML);
   std::vector<float> sc(n_cand + 1);
   std::vector<uint8_t> obs_m, pool;     // every scored plan, in scoring order, and a BO step's pool
   std::vector<double> obs_s;
   std::vector<int> picks;
   float inc_score = 0.f;
-  int unimproved = 0, t = 0;
+  int unimproved = unimproved0, t = 0;
   while (t < max_steps) {
+    const int st = step0 + t;
     int off = 0;
     if (t == 0) {
       std::copy(inc.begin(), inc.end(), masks.begin());
       off = 1;
     }
     bool bo = false;
-    if (bo_every > 0 && t > 0 && t % bo_every == 0) {
+    if (bo_every > 0 && st > 0 && st % bo_every == 0) {
       const int P = BO_POOL_FACTOR * n_cand;
       pool.resize((size_t)P * ML);
-      for (int c = 0; c < P; ++c) propose_layers(L, n_skip, sublayers, seed, t, c, pool.data() + c * ML);
+      for (int c = 0; c < P; ++c) propose_layers(L, n_skip, sublayers, seed, st, c, pool.data() + c * ML);
       const int n = std::min((int)obs_s.size(), BO_WINDOW);
       const size_t first = obs_s.size() - n;
       bo = bo_rank(obs_m.data() + first * ML, obs_s.data() + first, n, inc_score, pool.data(), P, ML, n_cand, picks);
@@ -1071,7 +1070,7 @@ extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0,
           std::copy(pool.begin() + picks[c] * ML, pool.begin() + (picks[c] + 1) * ML, masks.begin() + (off + c) * ML);
     }
     if (!bo)
-      for (int c = 0; c < n_cand; ++c) propose_layers(L, n_skip, sublayers, seed, t, c, masks.data() + (off + c) * ML);
+      for (int c = 0; c < n_cand; ++c) propose_layers(L, n_skip, sublayers, seed, st, c, masks.data() + (off + c) * ML);
     const int nm = n_cand + off;
     TRY(ssd_score_masks(q, masks.data(), nm, window_dev, pos0, gamma, q->w.swift_scores, q->w.swift_best, nullptr,
                         s));
@@ -1093,9 +1092,106 @@ extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0,
     ++t;
     if (inc_score > target || unimproved >= patience) break;
   }
-  std::copy(inc.begin(), inc.end(), best_mask_host);
-  *best_score = inc_score;
+  *score = inc_score;
   *n_steps = t;
+  *unimproved_out = unimproved;
+  return SSD_OK;
+}
+
+extern "C" int ssd_swift_search(ssd_seq* q, const int32_t* window_dev, int pos0, int gamma,
+                                const uint8_t* init_mask_host, int n_skip, int sublayers, int n_cand, int max_steps,
+                                int patience, float target, uint64_t seed, int bo_every, uint8_t* best_mask_host,
+                                float* best_score, int* n_steps, hipStream_t s) {
+  CHECK_SEQ(q);
+  CHECK_ARG(q && window_dev && init_mask_host && best_mask_host && best_score && n_steps, "null argument");
+  const int L = q->m->d.n_layers;
+  CHECK_ARG(n_skip >= 0 && n_skip <= (sublayers ? 2 : 1) * L && n_cand >= 1 && n_cand + 1 <= 64 && max_steps >= 1 &&
+                patience >= 1 && bo_every >= 0,
+            "bad search parameters");
+  if ((n_cand + 1) * gamma > q->max_rows) return fail(SSD_ERR_CAPACITY, "(n_cand + 1) * gamma exceeds max_rows");
+  std::vector<uint8_t> inc(init_mask_host, init_mask_host + 2 * (size_t)L);
+  int unimproved = 0;
+  TRY(swift_phase(q, window_dev, pos0, gamma, inc, n_skip, sublayers, n_cand, max_steps, patience, target, seed,
+                  bo_every, 0, 0, best_score, n_steps, &unimproved, s));
+  std::copy(inc.begin(), inc.end(), best_mask_host);
+  return SSD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// SWIFT on the fly: self-speculative iterations with the plan in use, and after every `accumulate`
+// committed tokens (while optimisation is not over) a phase of search steps on the last gamma + 1
+// committed tokens; the plan becomes the phase's incumbent.
+
+namespace {
+bool swift_config_ok(const ssd_seq* q, const ssd_swift_config* c) {
+  const int L = q->m->d.n_layers;
+  return c->gamma >= 1 && c->n_skip >= 0 && c->n_skip <= (c->sublayers ? 2 : 1) * L && c->n_cand >= 1 &&
+         c->n_cand + 1 <= 64 && c->steps_per_phase >= 1 && c->max_steps >= 0 && c->patience >= 1 &&
+         c->bo_every >= 0 && c->d >= 1 && c->d <= q->max_draft && std::isfinite(c->target) &&
+         std::isfinite(c->conf_thresh) && c->temperature >= 0.f && std::isfinite(c->temperature) &&
+         (c->n_cand + 1) * c->gamma <= q->max_rows;
+}
+}  // namespace
+
+extern "C" int ssd_swift_begin(ssd_seq* q, const ssd_swift_config* cfg, ssd_swift_state* st, hipStream_t s) {
+  CHECK_SEQ(q);
+  CHECK_ARG(q && cfg && st, "null argument");
+  if (!swift_config_ok(q, cfg)) return fail(SSD_ERR_ARG, "bad SWIFT configuration");
+  ssd_state ds;
+  TRY(ssd_read_state(q, &ds, s));
+  *st = ssd_swift_state{};
+  st->done = cfg->max_steps == 0 ? 1 : 0;
+  st->last_phase_n_out = ds.n_out;
+  st->score = std::numeric_limits<float>::quiet_NaN();
+  return SSD_OK;
+}
+
+extern "C" int ssd_swift_generate(ssd_seq* q, const ssd_swift_config* cfg, ssd_swift_state* st, uint8_t* plan_host,
+                                  int n_tokens, int32_t* draft_tokens_dev, float* draft_logits_dev,
+                                  int32_t* n_drafted_dev, float* verify_logits_dev, int32_t* out_tokens_dev,
+                                  int32_t* n_out_dev, hipStream_t s) {
+  CHECK_SEQ(q);
+  CHECK_ARG(q && cfg && st && plan_host && draft_tokens_dev && draft_logits_dev && n_drafted_dev &&
+                verify_logits_dev && out_tokens_dev && n_out_dev && n_tokens >= 0,
+            "null argument");
+  if (!swift_config_ok(q, cfg)) return fail(SSD_ERR_ARG, "bad SWIFT configuration");
+  const int L = q->m->d.n_layers;
+  const int acc = cfg->accumulate > 0 ? cfg->accumulate : cfg->gamma;
+  ssd_state ds;
+  TRY(ssd_read_state(q, &ds, s));
+  const int n_end = ds.n_out + n_tokens;
+  std::vector<uint8_t> inc(plan_host, plan_host + 2 * (size_t)L);
+  while (ds.n_out < n_end) {
+    TRY(ssd_draft(q, plan_host, -1, cfg->d, cfg->conf_thresh, cfg->temperature, cfg->seed, draft_tokens_dev,
+                  draft_logits_dev, n_drafted_dev, s));
+    TRY(ssd_verify(q, plan_host, -1, cfg->d, draft_tokens_dev, n_drafted_dev, 1, verify_logits_dev, s));
+    TRY(ssd_accept(q, verify_logits_dev, draft_logits_dev, draft_tokens_dev, n_drafted_dev, cfg->d,
+                   cfg->temperature, cfg->seed, out_tokens_dev, n_out_dev, s));
+    TRY(ssd_commit(q, out_tokens_dev, n_out_dev, s));
+    const int before = ds.n_out;
+    TRY(ssd_read_state(q, &ds, s));
+    ++st->iterations;
+    if (ds.n_out == before) return fail(SSD_ERR_NUMERIC, "an iteration committed no token");
+    if (st->done || ds.n_out - st->last_phase_n_out < acc || ds.n_out < cfg->gamma + 1) continue;
+    // the window: the last gamma + 1 committed tokens, the newest at position kvlen
+    const int32_t* window = q->w.log + (ds.n_out - 1 - cfg->gamma);
+    const int pos0 = ds.kvlen - cfg->gamma;
+    if (ds.n_out > q->log_cap) return fail(SSD_ERR_CAPACITY, "the output log no longer holds the window");
+    std::copy(plan_host, plan_host + 2 * (size_t)L, inc.begin());
+    float score = 0.f;
+    int ran = 0, unimproved = 0;
+    TRY(swift_phase(q, window, pos0, cfg->gamma, inc, cfg->n_skip, cfg->sublayers, cfg->n_cand,
+                    std::min(cfg->steps_per_phase, cfg->max_steps - st->steps), cfg->patience, cfg->target, cfg->seed,
+                    cfg->bo_every, st->steps, st->unimproved, &score, &ran, &unimproved, s));
+    if (!std::equal(inc.begin(), inc.end(), plan_host)) ++st->switches;
+    std::copy(inc.begin(), inc.end(), plan_host);
+    st->steps += ran;
+    st->unimproved = unimproved;
+    st->score = score;
+    ++st->phases;
+    st->done = (st->steps >= cfg->max_steps || unimproved >= cfg->patience || score > cfg->target) ? 1 : 0;
+    st->last_phase_n_out = ds.n_out;
+  }
   return SSD_OK;
 }
 
