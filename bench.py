@@ -32,7 +32,12 @@ HBM_PEAK_GBPS = 8000.0
 # Keyed by (kernel, workload): a record holds only for the workload (shapes and
 # row counts) it was taken on, and only while the kernel source is the one it
 # was taken on; otherwise the line reports null.
-PMC_TRAFFIC = {}
+PMC_TRAFFIC = {
+    ("dec_gemm_kernel<DEC_SWIGLU>", "7b"): dict(
+        source="self_speculative_layer_amd/csrc/decode.hip", sha1_prefix="c62f1a6fd6b7",
+        fetch_kib=89412.0, fetch_scale=2.0, write_kib=63.8, write_scale=1.0,
+        profile="profiles/dec_7b_hbm_counters.md"),
+}
 DOMINANT = "dec_gemm_kernel<DEC_SWIGLU>"
 SCORING_DOMINANT = "gemm_bf16_tiled<EPI_SWIGLU, 4, 4>"
 
