@@ -55,9 +55,9 @@ constexpr int DEC_AX = 4;     // activation steps in flight (fp32 normalised inp
 // 64-element slices of K; each wave keeps DEC_U steps (one contiguous 1 KB
 // tile of each weight set per step, packed layout) in flight in registers and
 // reloads a step's registers as soon as its MFMA has been issued.  The
-// per-wave tiles are reduced through LDS in wave order.  Rows >= M repeat the
-// last row's activations (no masking on the load path); their outputs are not
-// stored.
+// per-wave tiles are reduced through LDS in wave order.  Rows >= M repeat row
+// M - 1's activations and rows past the active count read what their rows
+// hold (no masking on the load path); neither is stored.
 //
 // RMSNorm consumers (QKV, gate/up, LM head) read the fp32 rows h * gain and
 // the rows' tile sums of h^2: the row scale 1 / rms is formed before the
@@ -94,10 +94,10 @@ __device__ __forceinline__ DecTile dec_tile(const DecGemm& a, int tile) {
 // depend on TPW.
 template <int EPI, int NW, bool HALF, int TPW>
 __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
-  if (a.stop && *a.stop) return;
+  // The stop flag and the active-row count travel with the first weight steps: no load issued before the
+  // first wait depends on them (rows are clamped to the block's capacity M; only rows < Ma are stored).
+  const int stopv = a.stop ? *a.stop : 0;
   const int Ma = a.nrows ? min(a.M, *a.nrows) : a.M;
-  if (Ma <= 0) return;
-  if (a.prof_ran && blockIdx.x == 0 && threadIdx.x == 0) *a.prof_ran = 1;   // timing record: this launch ran
   constexpr bool TWO = EPI == DEC_SWIGLU || EPI == DEC_QKV;   // outputs combine two W row sets
   constexpr bool DUAL = TWO && !HALF;                           // 16 + 16 rows: two accumulators
   static_assert(!HALF || TWO, "half tiles pair two row sets");
@@ -128,13 +128,13 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   typedef typename std::conditional<NORM, float, bf16_t>::type XT;
   typedef typename std::conditional<NORM, dec_f32x8, dec_u32x4>::type XR;
   const XT* xp;
-  if constexpr (NORM) xp = a.Xf + dec_actf_index(min(r, Ma - 1), g * 8);   // + 256: k = 8g + 4 .. 8g + 7
-  else xp = a.X + dec_act_index(min(r, Ma - 1), g * 8);
+  if constexpr (NORM) xp = a.Xf + dec_actf_index(min(r, a.M - 1), g * 8);   // + 256: k = 8g + 4 .. 8g + 7
+  else xp = a.X + dec_act_index(min(r, a.M - 1), g * 8);
 
   // Epilogue operands that do not depend on the product (the residual element and the next gain; the
   // row's position) are loaded ahead of the weight stream, so that the tail after the reduction holds
   // no dependent global loads.  Thread (erow, enn) of the epilogue; clamped rows are not stored.
-  const int erow = min((int)threadIdx.x >> 4, Ma - 1), enn = threadIdx.x & 15;
+  const int erow = min((int)threadIdx.x >> 4, a.M - 1), enn = threadIdx.x & 15;
   float eh[TPW], eg[TPW];
   int epos = 0;
   if constexpr (EPI == DEC_RESID) {
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   if constexpr (NORM) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-      const int row = min(wave + i * NW, Ma - 1);
+      const int row = min(wave + i * NW, a.M - 1);
 #pragma unroll
       for (int j = 0; j < DEC_SSP; ++j) ssv[i][j] = a.ss[(size_t)row * nts + min(lane + 64 * j, nts - 1)];
     }
@@ -193,6 +193,11 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
     if (u < AX) xload(u, min(u, n - 1));
     __builtin_amdgcn_sched_barrier(0);       // same load order as the steady loop
   }
+  if (stopv || Ma <= 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no wave ends with loads in flight
+    return;
+  }
+  if (a.prof_ran && blockIdx.x == 0 && threadIdx.x == 0) *a.prof_ran = 1;   // timing record: this launch ran
 
   if constexpr (NORM) {
     // canonical order: lane j adds tiles j, j + 64, ... then a butterfly over the wave
@@ -205,13 +210,13 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
         acc += __fmul_rn(ssv[i][j], lane + 64 * j < nts ? 1.f : 0.f);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, WAVE);
-      if (row < Ma && lane == 0) sinv[row] = inv_rms(acc, K, a.eps);
+      if (row < a.M && lane == 0) sinv[row] = inv_rms(acc, K, a.eps);
     }
   }
   float xinv = 1.f;                             // the scale of this lane's activation row
   if constexpr (NORM) {
     __syncthreads();
-    xinv = sinv[min(r, Ma - 1)];
+    xinv = sinv[min(r, a.M - 1)];
   }
   // QKV: the row's page and rotation, issued behind the first weight steps (only the position load
   // is waited for here)
