@@ -34,8 +34,8 @@ HBM_PEAK_GBPS = 8000.0
 # was taken on; otherwise the line reports null.
 PMC_TRAFFIC = {
     ("dec_gemm_kernel<DEC_SWIGLU>", "7b"): dict(
-        source="self_speculative_layer_amd/csrc/decode.hip", sha1_prefix="c62f1a6fd6b7",
-        fetch_kib=89412.0, fetch_scale=2.0, write_kib=63.8, write_scale=1.0,
+        source="self_speculative_layer_amd/csrc/decode.hip", sha1_prefix="3724176308ff",
+        fetch_kib=89403.7, fetch_scale=2.0, write_kib=63.8, write_scale=1.0,
         profile="profiles/dec_7b_hbm_counters.md"),
 }
 DOMINANT = "dec_gemm_kernel<DEC_SWIGLU>"
