@@ -92,12 +92,14 @@ __device__ __forceinline__ DecTile dec_tile(const DecGemm& a, int tile) {
 // TPW tiles per workgroup share each activation load (fewer activation reads
 // per weight byte when M > 1); the arithmetic of an output element does not
 // depend on TPW.
-template <int EPI, int NW, bool HALF, int TPW>
+// DEVROWS: the active-row count is a device value (a.nrows); otherwise all M rows are active.
+template <int EPI, int NW, bool HALF, int TPW, bool DEVROWS>
 __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
-  // The stop flag and the active-row count travel with the first weight steps: no load issued before the
-  // first wait depends on them (rows are clamped to the block's capacity M; only rows < Ma are stored).
+  // The stop flag and the active-row count travel with the first weight steps: the weight loads are
+  // issued before anything waits for them.  Activation rows are clamped to the active rows (rows past
+  // them would only add distinct lines to every step's loads); only rows < Ma are stored.
   const int stopv = a.stop ? *a.stop : 0;
-  const int Ma = a.nrows ? min(a.M, *a.nrows) : a.M;
+  const int Ma = DEVROWS ? min(a.M, *a.nrows) : a.M;
   constexpr bool TWO = EPI == DEC_SWIGLU || EPI == DEC_QKV;   // outputs combine two W row sets
   constexpr bool DUAL = TWO && !HALF;                           // 16 + 16 rows: two accumulators
   static_assert(!HALF || TWO, "half tiles pair two row sets");
@@ -124,12 +126,9 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
     wp[j * SPT] = a.W + wpk_index(wrow, g * 8, K);                  // step t: + 512 t
     if (DUAL) wp[j * SPT + 1] = a.W + wpk_index(t.f1 + r, g * 8, K);
   }
-  // activations of row r (clamped), k = 8g..8g+7 of each step: step t at + 512 t
   typedef typename std::conditional<NORM, float, bf16_t>::type XT;
   typedef typename std::conditional<NORM, dec_f32x8, dec_u32x4>::type XR;
-  const XT* xp;
-  if constexpr (NORM) xp = a.Xf + dec_actf_index(min(r, a.M - 1), g * 8);   // + 256: k = 8g + 4 .. 8g + 7
-  else xp = a.X + dec_act_index(min(r, a.M - 1), g * 8);
+  const XT* xp = nullptr;                       // this lane's activation row (set once Ma is known)
 
   // Epilogue operands that do not depend on the product (the residual element and the next gain; the
   // row's position) are loaded ahead of the weight stream, so that the tail after the reduction holds
@@ -152,18 +151,9 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
     if (a.side_from) eside = *a.side_from;
   }
 
-  // RMS tile sums of the rows this wave scales: loaded first, summed after the weight loads are issued
   __shared__ float sinv[16];
   const int nts = K / 16;
   float ssv[RPW][DEC_SSP];
-  if constexpr (NORM) {
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int row = min(wave + i * NW, a.M - 1);
-#pragma unroll
-      for (int j = 0; j < DEC_SSP; ++j) ssv[i][j] = a.ss[(size_t)row * nts + min(lane + 64 * j, nts - 1)];
-    }
-  }
 
   const int nu = K >> 6;
   const int s0 = 2 * ((nu * wave) / NW);
@@ -187,11 +177,42 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       xa[slot] = *(const XR*)(xp + (size_t)(s0 + step) * 512);
     }
   };
+  // Activations of row r (clamped to the active rows), k = 8g..8g+7 of each step (step t at + 512 t), and
+  // the RMS tile sums of the rows this wave scales.
+  auto act_setup = [&]() {
+    if constexpr (NORM) xp = a.Xf + dec_actf_index(min(r, Ma - 1), g * 8);   // + 256: k = 8g + 4 .. 8g + 7
+    else xp = a.X + dec_act_index(min(r, Ma - 1), g * 8);
+    if constexpr (NORM) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    wload(u, min(u, n - 1));
-    if (u < AX) xload(u, min(u, n - 1));
-    __builtin_amdgcn_sched_barrier(0);       // same load order as the steady loop
+      for (int i = 0; i < RPW; ++i) {
+        const int row = min(wave + i * NW, Ma - 1);
+#pragma unroll
+        for (int j = 0; j < DEC_SSP; ++j) ssv[i][j] = a.ss[(size_t)row * nts + min(lane + 64 * j, nts - 1)];
+      }
+    }
+  };
+  if constexpr (DEVROWS) {
+    // the active-row count is a device value: every weight step is issued before its load is waited for
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      wload(u, min(u, n - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    act_setup();
+#pragma unroll
+    for (int u = 0; u < AX; ++u) {
+      xload(u, min(u, n - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // all M rows are active: the steady loop's load order from the first step
+    act_setup();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      wload(u, min(u, n - 1));
+      if (u < AX) xload(u, min(u, n - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   if (stopv || Ma <= 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no wave ends with loads in flight
@@ -210,13 +231,13 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
         acc += __fmul_rn(ssv[i][j], lane + 64 * j < nts ? 1.f : 0.f);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, WAVE);
-      if (row < a.M && lane == 0) sinv[row] = inv_rms(acc, K, a.eps);
+      if (row < Ma && lane == 0) sinv[row] = inv_rms(acc, K, a.eps);
     }
   }
   float xinv = 1.f;                             // the scale of this lane's activation row
   if constexpr (NORM) {
     __syncthreads();
-    xinv = sinv[min(r, a.M - 1)];
+    xinv = sinv[min(r, Ma - 1)];
   }
   // QKV: the row's page and rotation, issued behind the first weight steps (only the position load
   // is waited for here)
@@ -371,14 +392,21 @@ static int dec_tpw(int epi, int M) {
 }
 
 // e0, e1: events taking the dispatch's begin and end timestamps (profiling), or null.
-template <int EPI, bool HALF>
+template <int EPI, bool HALF, bool DEVROWS>
 static void dec_launch(const DecGemm& a, int tpw, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
   const dim3 block(DEC_NW * 64);
   if (tpw == 2)
-    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 2>), dim3((a.n_tiles + 1) / 2), block, 0, s, e0, e1, 0,
-                          a);
+    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 2, DEVROWS>), dim3((a.n_tiles + 1) / 2), block, 0, s,
+                          e0, e1, 0, a);
   else
-    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 1>), dim3(a.n_tiles), block, 0, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 1, DEVROWS>), dim3(a.n_tiles), block, 0, s, e0, e1, 0,
+                          a);
+}
+
+template <int EPI, bool HALF>
+static void dec_launch(const DecGemm& a, int tpw, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
+  if (a.nrows) dec_launch<EPI, HALF, true>(a, tpw, e0, e1, s);
+  else dec_launch<EPI, HALF, false>(a, tpw, e0, e1, s);
 }
 
 int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
