@@ -104,7 +104,10 @@ __device__ __forceinline__ void part_store2(float* p, float a, float b) {
 // staged in sm.Ks / sm.Vs and the tile's queries at Qs.  Opw ([NW][16][HD] floats) takes the waves'
 // P.V sums handed over; it may alias sm.Ks when no later tile needs the keys (the scores are formed
 // before the barrier that precedes its first write).  Ends with a workgroup barrier.
-template <int HD, int NW, bool DEV, typename SM>
+// NQA: quad groups of P.V per lane (the tile's first 4 * (64 / (HD / 2)) * NQA queries); fewer than all
+// when the tile holds only that many queries (one-row blocks); the queries it covers get the same
+// arithmetic either way.
+template <int HD, int NW, bool DEV, typename SM, int NQA = ATTB_MAXQ / 4 / (64 / (HD / 2))>
 __device__ __forceinline__ void attn_tile_bf16(SM& sm, const bf16_t* __restrict__ Qs,
                                                float (*Opw)[ATTB_MAXQ][HD], int qbase, int nq, int G, int r0,
                                                int g, int H, int s, int nsplit, int key_beg, int key_end,
@@ -160,7 +163,8 @@ __device__ __forceinline__ void attn_tile_bf16(SM& sm, const bf16_t* __restrict_
   // the query quads qh, qh + QS, ...; waves 1..3 hand their sums to wave 0, which adds them in wave order
   constexpr int DP = HD / 2;                          // dim pairs
   constexpr int QS = 64 / DP;                         // quad groups per wave (1 at hd 128, 2 at hd 64)
-  constexpr int NQ4 = ATTB_MAXQ / 4 / QS;             // quads per lane
+  constexpr int NQ4 = NQA;                            // quads per lane (all: ATTB_MAXQ / 4 / QS)
+  static_assert(NQA >= 1 && NQA <= ATTB_MAXQ / 4 / QS, "quad groups");
   const int dp = lane % DP, qh = lane / DP;
   float o[NQ4][4][2];
 #pragma unroll
@@ -316,9 +320,13 @@ __device__ int attn_item_bf16(SM& sm, const bf16_t* __restrict__ q, int ldq,
   }
   __syncthreads();
 
-  for (int t = 0; t * ATTB_MAXQ < nq; ++t)
-    attn_tile_bf16<HD, NW, DEV>(sm, sm.Qs + t * ATTB_MAXQ * KST, sm.Op, t * ATTB_MAXQ, nq, G, r0, g, H, s, nsplit,
-                                key_beg, key_end, part);
+  constexpr int QS1 = 64 / (HD / 2);                  // quads one P.V pass per lane covers
+  if (nq <= 4 * QS1)
+    attn_tile_bf16<HD, NW, DEV, SM, 1>(sm, sm.Qs, sm.Op, 0, nq, G, r0, g, H, s, nsplit, key_beg, key_end, part);
+  else
+    for (int t = 0; t * ATTB_MAXQ < nq; ++t)
+      attn_tile_bf16<HD, NW, DEV>(sm, sm.Qs + t * ATTB_MAXQ * KST, sm.Op, t * ATTB_MAXQ, nq, G, r0, g, H, s, nsplit,
+                                  key_beg, key_end, part);
   return maxpos;
 }
 
