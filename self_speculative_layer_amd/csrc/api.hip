@@ -353,11 +353,12 @@ int dec_logits(ssd_seq* q, int M, const int* nrows, float* logits, const int* st
 }
 
 // Rows entering a pass: h[dst] from tokens (embedding) or src rows, with the first consumer's input.
+// block_rows: the rows of the block they enter (a one-row block's input is stored row-major).
 int dec_entry(ssd_seq* q, const int* tokens, const float* src, int rows, const int* count, const int* dst_off,
-              float* h, const float* gain, const int* stop, hipStream_t s) {
+              float* h, const float* gain, const int* stop, hipStream_t s, int block_rows) {
   const ssd_model_desc& d = q->m->d;
   TRY(launch_dec_entry(d.embed, tokens, d.vocab, src, rows, count, dst_off, h, d.d_model, gain, q->w.xg,
-                       q->w.ss, stop, s));
+                       q->w.ss, stop, block_rows, s));
   return 0;
 }
 
@@ -562,7 +563,7 @@ int decode_one(ssd_seq* q, const uint8_t* mask, float temperature, uint64_t seed
   if (dec_usable(q, 1)) {
     std::vector<int> ent;
     plan_entries(ent, 0, d.n_layers, mask);
-    TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, dec_gain(q->m, ent, 0, true), nullptr, s));
+    TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, dec_gain(q->m, ent, 0, true), nullptr, s, 1));
     TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, ent, 0, ent.size(), true, nullptr, s));
     TRY(dec_logits(q, 1, nullptr, lg, nullptr, s));
   } else {
@@ -699,12 +700,12 @@ extern "C" int ssd_verify(ssd_seq* q, const uint8_t* skip_mask_host, int exit_la
       // normalised-input buffers); then the rows < d' take the residual the draft saved there
       std::vector<int> prefix;
       plan_entries(prefix, 0, b, nullptr);
-      TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, dec_gain(q->m, prefix, 0, false), nullptr, s));
+      TRY(dec_entry(q, w.tok1, nullptr, 1, nullptr, nullptr, w.h1, dec_gain(q->m, prefix, 0, false), nullptr, s, 1));
       TRY(dec_layers(q, w.h1, 1, nullptr, w.pos1, prefix, 0, prefix.size(), false, nullptr, s));
-      TRY(dec_entry(q, nullptr, w.hb, d_max, n_drafted_dev, nullptr, w.h, g0, nullptr, s));
-      TRY(dec_entry(q, nullptr, w.h1, 1, nullptr, n_drafted_dev, w.h, g0, nullptr, s));
+      TRY(dec_entry(q, nullptr, w.hb, d_max, n_drafted_dev, nullptr, w.h, g0, nullptr, s, M));
+      TRY(dec_entry(q, nullptr, w.h1, 1, nullptr, n_drafted_dev, w.h, g0, nullptr, s, M));
     } else {
-      TRY(dec_entry(q, w.vtok, nullptr, M, rows, nullptr, w.h, g0, nullptr, s));
+      TRY(dec_entry(q, w.vtok, nullptr, M, rows, nullptr, w.h, g0, nullptr, s, M));
     }
     TRY(dec_layers(q, w.h, M, rows, w.vpos, suffix, 0, suffix.size(), true, nullptr, s));
     TRY(dec_logits(q, M, rows, logits_dev, nullptr, s));
@@ -803,13 +804,13 @@ extern "C" int ssd_verify_tree(ssd_seq* q, const uint8_t* skip_mask_host, int ex
     std::vector<int> prefix;
     plan_entries(prefix, 0, b, nullptr);
     const int* prows = &w.st->tree_prefix_rows;
-    TRY(dec_entry(q, w.ptok, nullptr, MP, prows, nullptr, w.hp, dec_gain(q->m, prefix, 0, false), nullptr, s));
+    TRY(dec_entry(q, w.ptok, nullptr, MP, prows, nullptr, w.hp, dec_gain(q->m, prefix, 0, false), nullptr, s, MP));
     TRY(dec_layers(q, w.hp, MP, prows, w.ppos, prefix, 0, prefix.size(), false, nullptr, s, nullptr,
                    &w.st->tree_side_prefix));
-    TRY(dec_entry(q, nullptr, w.hb, d_max, n_drafted_dev, nullptr, w.h, g0, nullptr, s));
-    TRY(dec_entry(q, nullptr, w.hp, MP, prows, n_drafted_dev, w.h, g0, nullptr, s));
+    TRY(dec_entry(q, nullptr, w.hb, d_max, n_drafted_dev, nullptr, w.h, g0, nullptr, s, M));
+    TRY(dec_entry(q, nullptr, w.hp, MP, prows, n_drafted_dev, w.h, g0, nullptr, s, M));
   } else {
-    TRY(dec_entry(q, w.tvtok, nullptr, M, rows, nullptr, w.h, g0, nullptr, s));
+    TRY(dec_entry(q, w.tvtok, nullptr, M, rows, nullptr, w.h, g0, nullptr, s, M));
   }
   TRY(dec_layers(q, w.h, M, rows, w.tvpos, suffix, 0, suffix.size(), true, nullptr, s, nullptr,
                  &w.st->tree_side_full));

@@ -93,7 +93,9 @@ __device__ __forceinline__ DecTile dec_tile(const DecGemm& a, int tile) {
 // per weight byte when M > 1); the arithmetic of an output element does not
 // depend on TPW.
 // DEVROWS: the active-row count is a device value (a.nrows); otherwise all M rows are active.
-template <int EPI, int NW, bool HALF, int TPW, bool DEVROWS>
+// ROW1 (a one-row block, M = 1): the fp32 normalised input is stored row-major (a step's 32 elements are
+// one 128-byte line instead of four 16-byte pieces 256 bytes apart).
+template <int EPI, int NW, bool HALF, int TPW, bool DEVROWS, bool ROW1>
 __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   // The stop flag and the active-row count travel with the first weight steps: the weight loads are
   // issued before anything waits for them.  Activation rows are clamped to the active rows (rows past
@@ -170,8 +172,9 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   };
   auto xload = [&](int slot, int step) {
     if constexpr (NORM) {
-      const f32x4 lo = *(const f32x4*)(xp + (size_t)(s0 + step) * 512);
-      const f32x4 hi = *(const f32x4*)(xp + (size_t)(s0 + step) * 512 + 256);
+      constexpr int STEP = ROW1 ? 32 : 512, HI = ROW1 ? 4 : 256;
+      const f32x4 lo = *(const f32x4*)(xp + (size_t)(s0 + step) * STEP);
+      const f32x4 hi = *(const f32x4*)(xp + (size_t)(s0 + step) * STEP + HI);
       xa[slot] = dec_f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     } else {
       xa[slot] = *(const XR*)(xp + (size_t)(s0 + step) * 512);
@@ -180,7 +183,8 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
   // Activations of row r (clamped to the active rows), k = 8g..8g+7 of each step (step t at + 512 t), and
   // the RMS tile sums of the rows this wave scales.
   auto act_setup = [&]() {
-    if constexpr (NORM) xp = a.Xf + dec_actf_index(min(r, Ma - 1), g * 8);   // + 256: k = 8g + 4 .. 8g + 7
+    if constexpr (NORM && ROW1) xp = a.Xf + g * 8;                            // + 4: k = 8g + 4 .. 8g + 7
+    else if constexpr (NORM) xp = a.Xf + dec_actf_index(min(r, Ma - 1), g * 8);   // + 256: k = 8g + 4 .. 8g + 7
     else xp = a.X + dec_act_index(min(r, Ma - 1), g * 8);
     if constexpr (NORM) {
 #pragma unroll
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       a.Y[(size_t)row * a.ldy + col] = hn;
       if (a.y_copy) a.y_copy[(size_t)row * a.ldy + col] = hn;
       if (a.gain_next) {
-        a.xg_next[dec_actf_index(row, col)] = __fmul_rn(hn, eg[j]);
+        a.xg_next[a.M == 1 ? col : dec_actf_index(row, col)] = __fmul_rn(hn, eg[j]);   // one-row blocks: row-major
         const float tt = tile16_ss_lanes(hn);
         if (nn == 0) a.ss_next[(size_t)row * (a.N / 16) + col / 16] = tt;
       }
@@ -395,12 +399,15 @@ static int dec_tpw(int epi, int M) {
 template <int EPI, bool HALF, bool DEVROWS>
 static void dec_launch(const DecGemm& a, int tpw, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
   const dim3 block(DEC_NW * 64);
-  if (tpw == 2)
-    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 2, DEVROWS>), dim3((a.n_tiles + 1) / 2), block, 0, s,
-                          e0, e1, 0, a);
+  if (EPI != DEC_RESID && a.M == 1)
+    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 1, DEVROWS, true>), dim3(a.n_tiles), block, 0, s, e0,
+                          e1, 0, a);
+  else if (tpw == 2)
+    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 2, DEVROWS, false>), dim3((a.n_tiles + 1) / 2), block,
+                          0, s, e0, e1, 0, a);
   else
-    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 1, DEVROWS>), dim3(a.n_tiles), block, 0, s, e0, e1, 0,
-                          a);
+    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 1, DEVROWS, false>), dim3(a.n_tiles), block, 0, s, e0,
+                          e1, 0, a);
 }
 
 template <int EPI, bool HALF>
@@ -526,9 +533,10 @@ int launch_attention_dec(int head_dim, const void* q, int ldq, const KvView& kv,
 // Row r of the entry: h[dr] from the embedding row e (EMB) or from sr, and with NORM the first consumer's
 // input xg[dr] = h * gain (fp32) and the tile sums ss[dr].
 template <bool EMB, bool NORM>
+// row1: the row enters a one-row block (its consumer input is stored row-major).
 __device__ __forceinline__ void dec_entry_row(const bf16_t* __restrict__ e, const float* __restrict__ sr, int dr,
                                               float* __restrict__ h, int D, const float* __restrict__ gain,
-                                              float* __restrict__ xg, float* __restrict__ ss) {
+                                              float* __restrict__ xg, float* __restrict__ ss, bool row1) {
   float* hr = h + (size_t)dr * D;
   // D % 16 == 0: each group of 16 lanes is entirely inside or outside the row.  Loads are issued in
   // batches of 8 per thread before their first use.
@@ -549,7 +557,7 @@ __device__ __forceinline__ void dec_entry_row(const bf16_t* __restrict__ e, cons
       if (NORM) {
         const float t = tile16_ss_lanes(v[j]);
         if (i < D) {
-          xg[dec_actf_index(dr, i)] = __fmul_rn(v[j], gv[j]);
+          xg[row1 ? i : dec_actf_index(dr, i)] = __fmul_rn(v[j], gv[j]);   // one-row blocks: row-major
           if ((threadIdx.x & 15) == 0) ss[(size_t)dr * (D / 16) + i / 16] = t;
         }
       }
@@ -563,14 +571,14 @@ __global__ __launch_bounds__(256) void dec_entry_kernel(const bf16_t* __restrict
                                                         const int* __restrict__ count, const int* __restrict__ dst_off,
                                                         float* __restrict__ h, int D, const float* __restrict__ gain,
                                                         float* __restrict__ xg, float* __restrict__ ss,
-                                                        const int* __restrict__ stop) {
+                                                        const int* __restrict__ stop, int block_rows) {
   if (stop && *stop) return;
   const int r = blockIdx.x;
   const int n = count ? min(rows, *count) : rows;
   if (r >= n) return;
   const int dr = r + (dst_off ? *dst_off : 0);
   const bf16_t* e = EMB ? emb + (size_t)min(max(tokens[r], 0), V - 1) * D : nullptr;   // ids are produced in range
-  dec_entry_row<EMB, NORM>(e, EMB ? nullptr : src + (size_t)r * D, dr, h, D, gain, xg, ss);
+  dec_entry_row<EMB, NORM>(e, EMB ? nullptr : src + (size_t)r * D, dr, h, D, gain, xg, ss, block_rows == 1);
 }
 
 // Draft step j (1-based): the row y_{j-1} at position kvlen + j - 1 (y_0 = the last committed token).
@@ -607,7 +615,7 @@ __global__ __launch_bounds__(256) void dec_draft_entry_kernel(DevState* __restri
   }
   __syncthreads();
   if (!s_ok) return;
-  dec_entry_row<true, NORM>(emb + (size_t)min(max(s_tok, 0), V - 1) * D, nullptr, 0, h, D, gain, xg, ss);
+  dec_entry_row<true, NORM>(emb + (size_t)min(max(s_tok, 0), V - 1) * D, nullptr, 0, h, D, gain, xg, ss, true);
 }
 
 int launch_dec_draft_entry(DevState* st, const int32_t* drafts, int j, int* pos1, int* tok1, int max_ctx,
@@ -624,12 +632,12 @@ int launch_dec_draft_entry(DevState* st, const int32_t* drafts, int j, int* pos1
 
 int launch_dec_entry(const void* emb, const int* tokens, int V, const float* src, int rows, const int* count,
                      const int* dst_off, float* h, int D, const float* gain, void* xg, float* ss, const int* stop,
-                     hipStream_t s) {
+                     int block_rows, hipStream_t s) {
   if (rows <= 0) return 0;
   if (D % 16 != 0) return SSD_ERR_SHAPE;
 #define ENTRY(E, N)                                                                                              \
   hipLaunchKernelGGL((dec_entry_kernel<E, N>), dim3(rows), dim3(256), 0, s, (const bf16_t*)emb, tokens, V, src,  \
-                     rows, count, dst_off, h, D, gain, (float*)xg, ss, stop)
+                     rows, count, dst_off, h, D, gain, (float*)xg, ss, stop, block_rows)
   if (tokens) {
     if (gain) ENTRY(true, true); else ENTRY(true, false);
   } else {

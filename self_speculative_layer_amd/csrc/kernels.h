@@ -216,8 +216,9 @@ int launch_dec_draft_entry(DevState* st, const int32_t* drafts, int j, int* pos1
 
 // h[dst] = embedding row of tokens[r] (tokens != nullptr) or src[r], for r < (count ? *count : rows),
 // dst = r + (dst_off ? *dst_off : 0); with gain, also xg[dst] = h * gain (fp32) and ss[dst] tile sums.
+// block_rows: the rows of the block the rows enter (a one-row block stores its consumer input row-major).
 int launch_dec_entry(const void* emb, const int* tokens, int V, const float* src, int rows, const int* count,
                      const int* dst_off, float* h, int D, const float* gain, void* xg, float* ss, const int* stop,
-                     hipStream_t s);
+                     int block_rows, hipStream_t s);
 
 }  // namespace ssd
