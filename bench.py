@@ -27,16 +27,20 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 
 # HBM traffic of the dominant kernel from rocprofv3 counter runs (FETCH_SIZE and
-# WRITE_SIZE in KiB per dispatch, averaged over the kernel's dispatches in the
-# run, scaled by the factors a plain 1 GiB copy reads on the same counters).
-# Keyed by (kernel, workload): a record holds only for the workload (shapes and
-# row counts) it was taken on, and only while the kernel source is the one it
-# was taken on; otherwise the line reports null.
+# WRITE_SIZE in KiB per dispatch, scaled by the factors a plain 1 GiB copy reads
+# on the same counters).  Keyed by (kernel, workload): a record holds only for
+# the workload (shapes and row counts) it was taken on, and only while the
+# kernel source is the one it was taken on; otherwise the line reports null.
+# The 7B gate/up launches are two instantiations, one-row blocks (104 per SSD
+# step: 12 draft passes and the verify's last row over 8 layers) and 13-row
+# verify blocks (24 per step, layers 8..31); the record holds each one's mean
+# and the per-launch figure is their mean weighted by that mix.
 PMC_TRAFFIC = {
     ("dec_gemm_kernel<DEC_SWIGLU>", "7b"): dict(
-        source="self_speculative_layer_amd/csrc/decode.hip", sha1_prefix="3724176308ff",
-        fetch_kib=89403.7, fetch_scale=2.0, write_kib=63.8, write_scale=1.0,
-        profile="profiles/dec_7b_hbm_counters.md"),
+        source="self_speculative_layer_amd/csrc/decode.hip", sha1_prefix="52aa25bb9f24",
+        parts=[dict(launches=104, fetch_kib=88261.6, write_kib=21.5),
+               dict(launches=24, fetch_kib=90205.4, write_kib=279.5)],
+        fetch_scale=2.0, write_scale=1.0, profile="profiles/dec_7b_hbm_counters.md"),
 }
 DOMINANT = "dec_gemm_kernel<DEC_SWIGLU>"
 SCORING_DOMINANT = "gemm_bf16_tiled<EPI_SWIGLU, 4, 4>"
@@ -51,7 +55,10 @@ def pmc_traffic_bytes(kernel, workload):
     with open(os.path.join(ROOT, rec["source"]), "rb") as f:
         if hashlib.sha1(f.read()).hexdigest()[:12] != rec["sha1_prefix"]:
             return None
-    return 1024.0 * (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"])
+    parts = rec.get("parts") or [dict(launches=1, fetch_kib=rec["fetch_kib"], write_kib=rec["write_kib"])]
+    n = sum(p["launches"] for p in parts)
+    return 1024.0 * sum(p["launches"] * (p["fetch_kib"] * rec["fetch_scale"] + p["write_kib"] * rec["write_scale"])
+                        for p in parts) / n
 
 WORKLOADS = {
     "7b": dict(shape="llama2-7b-shape", prompt=512, n_gen=256, exit_layer=8, d=12, tau=0.0, T=0.0,
