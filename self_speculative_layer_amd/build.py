@@ -5,14 +5,15 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssd.so")
-SOURCES = ["kernels.hip", "decode.hip", "tree.hip", "api.hip", "profile.hip", "noalloc.hip"]
+SOURCES = ["kernels.hip", "attn_group.hip", "decode.hip", "tree.hip", "api.hip", "profile.hip", "noalloc.hip"]
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 # Kernels that must not use scratch (private) memory: the decode-block
 # projections and attention keep every value in registers / LDS.
-NO_SCRATCH = {"decode.hip": ("dec_gemm_kernel", "attn_dec_kernel"), "kernels.hip": ("gemm_bf16_tiled",)}
+NO_SCRATCH = {"decode.hip": ("dec_gemm_kernel", "attn_dec_kernel"), "kernels.hip": ("gemm_bf16_tiled",),
+              "attn_group.hip": ("attn_group_kernel",)}
 
 
 def _check_no_scratch(src, remarks):

@@ -68,6 +68,12 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
                      int H, int KVH, const RowBlock& rb, int max_ctx, const void* local_kv,
                      int local_start, int group_rows, float* part, void* out, int ldo, hipStream_t s,
                      bool out_blocked = false);
+// The mask-scoring pass's attention (attn_group.hip): rows in groups of group_rows consecutive rows, each
+// group one candidate whose positions >= local_start come from its own keys and values in local_kv; bf16,
+// head_dim 64 or 128, H / KVH <= 64.  Output rows of stride ldo.
+int launch_attention_groups(int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer, int H, int KVH,
+                            const RowBlock& rb, const void* local_kv, int local_start, int group_rows, void* out,
+                            int ldo, hipStream_t s);
 size_t attention_partial_floats(int max_rows, int H, int head_dim, int max_ctx);
 // Number of fixed key splits covering max_ctx positions (the partial buffer's split dimension).
 int attention_nsplit(int max_ctx);
