@@ -7,12 +7,14 @@
 // records and no merge launch are needed:
 //   S = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16, K as A: 16 keys
 //   x 32 dims, the queries as B), the chunk's maxima and probabilities in
-//   fp32 registers, and O += P V on the matrix cores too, with V transposed
-//   into LDS while it is staged and each probability split into two bf16
-//   parts (hi + lo), so the products keep ~16 bits of the probability.
+//   fp32 registers (base 2), and O += P V on the matrix cores too, each
+//   probability split into two bf16 parts (hi + lo) so that the products keep
+//   ~16 bits of it.
 // Each wave owns 16 queries and all 64 keys of a chunk, so the softmax needs
-// no exchange between waves; keys are staged double-buffered (K straight into
-// LDS by global_load_lds, V through registers).
+// no exchange between waves (the four lanes of a query exchange through
+// permlane swaps).  Keys and values go straight into LDS (global_load_lds,
+// double-buffered) as 1 KB tiles of 16 rows x 32 dims; the value tiles are
+// read transposed (ds_read_b64_tr_b16) as the A operand of P V.
 // Arithmetic differs from the split-item attention of the decode and prefill
 // paths (order of the key sums, online rescaling); the scoring pass compares
 // candidates with one another, never with those paths' bits.
@@ -26,16 +28,26 @@ namespace ssd {
 namespace {
 
 constexpr int GA_CHUNK = 64;       // keys per chunk
-constexpr int GA_VTS = 72;         // row stride (elements) of the transposed V tile: conflict-light writes and reads
 
 typedef uint32_t ga_u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t ga_u32x2 __attribute__((ext_vector_type(2)));
+typedef short ga_s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void ga_lds_t;
+typedef __attribute__((address_space(3))) ga_s16x4 ga_lds_s16x4;
 typedef __attribute__((address_space(1))) const void ga_gbl_t;
 
-// Value of the lane's pair partner (lane ^ 1).
-__device__ __forceinline__ uint32_t ga_swap_pair(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);   // quad_perm [1, 0, 3, 2]
+// Reductions over the four lanes r, r + 16, r + 32, r + 48 (the 16-lane rows of a wave).
+__device__ __forceinline__ float ga_row4_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));          // rows (0, 1) and (2, 3)
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));       // halves
+}
+__device__ __forceinline__ float ga_row4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int HD, int NW, int PS>
@@ -44,15 +56,16 @@ __global__ __launch_bounds__(NW * 64) void attn_group_kernel(
     int n_lpages, int L, int layer, int H, int KVH, int M, const int* __restrict__ nrows,
     const int* __restrict__ pos, int RB, const bf16_t* __restrict__ local_kv, int local_start, int group_rows,
     bf16_t* __restrict__ out, int ldo, const int* __restrict__ stop) {
-  constexpr int NDS = HD / 32;               // 32-dim slices of a key row
-  constexpr int NKT = 4 * NDS;               // K tiles (16 keys x 32 dims, 1 KB) per chunk
+  constexpr int NDS = HD / 32;               // 32-dim slices of a row
+  constexpr int NT = 4 * NDS;                // tiles (16 keys x 32 dims, 1 KB) per chunk, of K and of V each
   constexpr int NDB = HD / 16;               // 16-dim blocks of the output
-  constexpr int DG = HD / 8;                 // 16-byte groups of a row
-  constexpr int KPI = 64 / DG;               // keys per V load instruction of a wave
-  constexpr int NVI = GA_CHUNK / KPI;        // V load instructions per chunk
-  static_assert(HD % 32 == 0 && NKT % NW == 0 && NVI % NW == 0, "tile split over the waves");
-  __shared__ alignas(16) bf16_t Ks[2][NKT * 512];
-  __shared__ alignas(16) bf16_t Vt[2][HD * GA_VTS];
+  constexpr int NPG = GA_CHUNK / PS;         // pages per chunk
+  static_assert(HD % 32 == 0 && NT % NW == 0, "tile split over the waves");
+  // tile t = kb * NDS + ds holds keys 16 kb .. + 15, dims 32 ds .. + 31; row R (key 16 kb + R) is 64 bytes of
+  // four 16-byte chunks; K tiles keep the chunks in order, V tiles put dim chunk C at position
+  // C ^ (R / 4) (two-way bank conflicts for the transposed reads)
+  __shared__ alignas(16) bf16_t Ks[2][NT * 512];
+  __shared__ alignas(16) bf16_t Vs[2][NT * 512];
 
   if (stop && *stop) return;
   const int g = blockIdx.x;
@@ -95,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) void attn_group_kernel(
   const int n_fast = min(lstart, maxpos + 1) / GA_CHUNK;
 
   // page ids of chunk c: lane i < 64 / PS holds that of the chunk's i-th page (pages of 16, 32 or 64
-  // positions, so the 4 to 16 aligned keys of one load instruction share a page)
+  // positions, so the 16 keys of a tile share a page)
   auto pages = [&](int c) -> int {
     const int i = min(c * GA_CHUNK / PS + lane, n_lpages - 1);
     return lane * PS < GA_CHUNK ? page_table[i] : 0;
@@ -103,25 +116,18 @@ __global__ __launch_bounds__(NW * 64) void attn_group_kernel(
   const size_t page_stride = (size_t)L * 2 * KVH * PS * HD;
   const bf16_t* pool_k = pool + (((size_t)layer * 2 + 0) * KVH + g) * PS * HD;
   const size_t vdelta = (size_t)KVH * PS * HD;         // value rows follow the key rows of a page's layer
+  const size_t lrow = (size_t)2 * KVH * HD;             // local buffer: [row][K, V][KVH][HD]
 
-  // Loads.  K tile t = kb * NDS + ds (16 keys x 32 dims): lane -> key 16 kb + lane / 4, dims 32 ds + 8 (lane % 4),
-  // written to LDS at 16 * lane, so a fragment read is one contiguous 1 KB.  V: lane = key parity | 16-byte
-  // group << 1 | key pair << (1 + log2 DG), 16 bytes each.  Offsets within a page (elements) are the same
-  // for every chunk.
-  const int par = lane & 1, dg = (lane >> 1) % DG, kq = (lane >> 1) / DG;
-  uint32_t koff[NKT / NW], voff[NVI / NW];
+  // Tile loads: lane -> row R = lane / 4 (key 16 kb + R), position lane % 4 (16 bytes, written to LDS at
+  // 16 * lane).  Offsets within a page (elements) are the same for every chunk.
+  const int kR = lane >> 2;
+  const int kdim = 8 * (lane & 3), vdim = 8 * ((lane & 3) ^ ((lane >> 4) & 3));
+  uint32_t toff[NT / NW];
 #pragma unroll
-  for (int j = 0; j < NKT / NW; ++j) {
-    const int t = wave + NW * j, kb = t / NDS, ds = t % NDS;
-    koff[j] = (uint32_t)(((16 * kb + (lane >> 2)) & (PS - 1)) * HD + 32 * ds + 8 * (lane & 3));
+  for (int j = 0; j < NT / NW; ++j) {
+    const int kb = (wave + NW * j) / NDS;
+    toff[j] = (uint32_t)(((16 * kb + kR) & (PS - 1)) * HD);
   }
-#pragma unroll
-  for (int i = 0; i < NVI / NW; ++i) {
-    const int ii = wave + NW * i;
-    voff[i] = (uint32_t)(((KPI * ii + 2 * kq + par) & (PS - 1)) * HD + 8 * dg);
-  }
-  ga_u32x4 vreg[NVI / NW];
-  constexpr int NPG = GA_CHUNK / PS;                    // pages per chunk
   auto issue = [&](int c, int pgc, int b) {
     const bf16_t* pk[NPG];                              // the chunk's pages: key rows of (layer, head g)
 #pragma unroll
@@ -129,73 +135,38 @@ __global__ __launch_bounds__(NW * 64) void attn_group_kernel(
     if (c < n_fast) {
       // every key of the chunk is a prefix key of the paged cache
 #pragma unroll
-      for (int j = 0; j < NKT / NW; ++j) {
-        const int t = wave + NW * j, kb = t / NDS;
-        __builtin_amdgcn_global_load_lds((ga_gbl_t*)(pk[16 * kb / PS] + koff[j]), (ga_lds_t*)(&Ks[b][t * 512]), 16,
-                                         0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < NVI / NW; ++i) {
-        const int ii = wave + NW * i;
-        vreg[i] = *(const ga_u32x4*)(pk[KPI * ii / PS] + vdelta + voff[i]);
+      for (int j = 0; j < NT / NW; ++j) {
+        const int t = wave + NW * j, kb = t / NDS, ds = t % NDS;
+        const bf16_t* row = pk[16 * kb / PS] + toff[j] + 32 * ds;
+        __builtin_amdgcn_global_load_lds((ga_gbl_t*)(row + kdim), (ga_lds_t*)(&Ks[b][t * 512]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((ga_gbl_t*)(row + vdelta + vdim), (ga_lds_t*)(&Vs[b][t * 512]), 16, 0, 0);
       }
     } else {
       // prefix keys, the candidate's own keys (positions >= local_start: row grp_base + kp - local_start of
-      // the local buffer), and positions past maxpos (the group's last local row, or some row of a valid
-      // page): their scores are masked and their values zeroed
-      const size_t lrow = (size_t)2 * KVH * HD;
+      // the local buffer), and positions past maxpos, which read the row of maxpos: their scores are masked
+      // and their probabilities are zero
 #pragma unroll
-      for (int j = 0; j < NKT / NW; ++j) {
+      for (int j = 0; j < NT / NW; ++j) {
         const int t = wave + NW * j, kb = t / NDS, ds = t % NDS;
-        const int kp = c * GA_CHUNK + 16 * kb + (lane >> 2);
-        const bf16_t* pr = pk[16 * kb / PS] + koff[j];
-        const bf16_t* lr = local_kv + (size_t)(grp_base + min(kp, maxpos) - local_start) * lrow + (size_t)g * HD +
-                           32 * ds + 8 * (lane & 3);
-        __builtin_amdgcn_global_load_lds((ga_gbl_t*)(kp >= lstart ? lr : pr), (ga_lds_t*)(&Ks[b][t * 512]), 16, 0,
-                                         0);
-      }
-#pragma unroll
-      for (int i = 0; i < NVI / NW; ++i) {
-        const int ii = wave + NW * i;
-        const int kp = c * GA_CHUNK + KPI * ii + 2 * kq + par;
-        const bf16_t* pr = pk[KPI * ii / PS] + vdelta + voff[i];
-        const bf16_t* lr = local_kv + (size_t)(grp_base + min(kp, maxpos) - local_start) * lrow + (size_t)KVH * HD +
-                           (size_t)g * HD + 8 * dg;
-        vreg[i] = *(const ga_u32x4*)(kp >= lstart ? lr : pr);
-        if (kp > maxpos) vreg[i] = ga_u32x4{0u, 0u, 0u, 0u};
+        const int kp = min(c * GA_CHUNK + 16 * kb + kR, maxpos);
+        const int page = __shfl(pgc, (kp - c * GA_CHUNK) / PS, 64);
+        const bf16_t* pr = pool_k + (size_t)page * page_stride + (size_t)(kp & (PS - 1)) * HD;
+        const bf16_t* lr = local_kv + (size_t)(grp_base + kp - local_start) * lrow + (size_t)g * HD;
+        const bf16_t* kr = (kp >= lstart ? lr : pr) + 32 * ds;
+        const size_t vd = kp >= lstart ? (size_t)KVH * HD : vdelta;
+        __builtin_amdgcn_global_load_lds((ga_gbl_t*)(kr + kdim), (ga_lds_t*)(&Ks[b][t * 512]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((ga_gbl_t*)(kr + vd + vdim), (ga_lds_t*)(&Vs[b][t * 512]), 16, 0, 0);
       }
     }
   };
-  // V rows of a chunk into Vt[b] as [dim][key]: the two lanes of a key pair swap halves, so each writes
-  // 4 dims x 2 keys as four 32-bit words, in a lane-rotated row order (fewer bank conflicts)
-  const int rot = (dg >> 1) & 3;
-  uint32_t vtaddr[4];                                   // byte offsets in a Vt buffer of the lane's four rows
+
+  // transposed reads of V for the P V operand: lane (r, g4) of output block d takes dim 16 d + r of keys
+  // 32 kk + 4 g4 + 0..3 (tile 2 kk) and 32 kk + 16 + 4 g4 + 0..3 (tile 2 kk + 1); as a source it reads 8 bytes
+  // of row 4 g4 + r / 4, dims 16 (d % 2) + 4 (r % 4), chunk C = 2 (d % 2) + (r % 4) / 2 at position C ^ g4
+  uint32_t voff2[2];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) vtaddr[jj] = (uint32_t)(((8 * dg + 4 * par + ((jj + rot) & 3)) * GA_VTS + 2 * kq) * 2);
-  auto put_v = [&](int b) {
-    char* vt = (char*)Vt[b];
-#pragma unroll
-    for (int i = 0; i < NVI / NW; ++i) {
-      const int ii = wave + NW * i;
-      const ga_u32x4 u = vreg[i];
-      const uint32_t s0 = par ? u[0] : u[2], s1 = par ? u[1] : u[3];
-      const uint32_t x0 = ga_swap_pair(s0), x1 = ga_swap_pair(s1);
-      const uint32_t e0 = par ? x0 : u[0], e1 = par ? x1 : u[1];   // even key of the pair
-      const uint32_t o0 = par ? u[2] : x0, o1 = par ? u[3] : x1;   // odd key
-      uint32_t w[4];
-      w[0] = __builtin_amdgcn_perm(o0, e0, 0x05040100u);          // dims 4 par + 0 .. 3: (even, odd) key
-      w[1] = __builtin_amdgcn_perm(o0, e0, 0x07060302u);
-      w[2] = __builtin_amdgcn_perm(o1, e1, 0x05040100u);
-      w[3] = __builtin_amdgcn_perm(o1, e1, 0x07060302u);
-      uint32_t y[4], z[4];                                // z[jj] = w[(jj + rot) & 3]
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) y[jj] = (rot & 1) ? w[(jj + 1) & 3] : w[jj];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) z[jj] = (rot & 2) ? y[(jj + 2) & 3] : y[jj];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) *(uint32_t*)(vt + vtaddr[jj] + 2 * KPI * ii) = z[jj];
-    }
-  };
+  for (int h = 0; h < 2; ++h)
+    voff2[h] = (uint32_t)((4 * g4 + (r >> 2)) * 32 + ((2 * h + ((r & 3) >> 1)) ^ g4) * 8 + 4 * (r & 1));
 
   // softmax in base 2: scores scaled by log2(e) / sqrt(HD)
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
@@ -207,8 +178,7 @@ __global__ __launch_bounds__(NW * 64) void attn_group_kernel(
   int pg_next = pages(0);
   issue(0, pg_next, 0);
   if (nch > 1) pg_next = pages(1);
-  put_v(0);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
@@ -248,8 +218,7 @@ __global__ __launch_bounds__(NW * 64) void attn_group_kernel(
           mloc = fmaxf(mloc, s[kb][e]);
         }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    mloc = ga_row4_max(mloc);
     const float m_new = fmaxf(m_run, mloc);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -268,38 +237,28 @@ __global__ __launch_bounds__(NW * 64) void attn_group_kernel(
         const float q0 = p0 - __uint_as_float(u0 & 0xFFFF0000u), q1 = p1 - __uint_as_float(u1 & 0xFFFF0000u);
         pl[kb][e / 2] = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x07060302u);
       }
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    lsum = ga_row4_sum(lsum);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) o[d] *= alpha;
     // ---- O[dim][query] += V^T P^T: k slots 8 g4 + t hold keys 32 kk + 4 g4 + t (t < 4) and
     // 32 kk + 16 + 4 g4 + (t - 4), the keys this lane's probabilities belong to
-    const bf16_t* vt = Vt[b];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const ga_u32x4 bh = {ph[2 * kk][0], ph[2 * kk][1], ph[2 * kk + 1][0], ph[2 * kk + 1][1]};
       const ga_u32x4 bl = {pl[2 * kk][0], pl[2 * kk][1], pl[2 * kk + 1][0], pl[2 * kk + 1][1]};
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        const bf16_t* row = vt + (16 * d + r) * GA_VTS + 32 * kk + 4 * g4;
-        const ga_u32x2 a0 = *(const ga_u32x2*)row, a1 = *(const ga_u32x2*)(row + 16);
-        const ga_u32x4 av = {a0[0], a0[1], a1[0], a1[1]};
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bh),
-                                                      o[d], 0, 0, 0);
-      }
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const bf16_t* row = vt + (16 * d + r) * GA_VTS + 32 * kk + 4 * g4;
-        const ga_u32x2 a0 = *(const ga_u32x2*)row, a1 = *(const ga_u32x2*)(row + 16);
-        const ga_u32x4 av = {a0[0], a0[1], a1[0], a1[1]};
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bl),
-                                                      o[d], 0, 0, 0);
+        const bf16_t* t0 = &Vs[b][((2 * kk) * NDS + d / 2) * 512 + voff2[d & 1]];
+        const ga_s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ga_lds_s16x4*)t0);
+        const ga_s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ga_lds_s16x4*)(t0 + NDS * 512));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh), o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), o[d], 0, 0, 0);
       }
     }
-    if (c + 1 < nch) put_v(b ^ 1);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
