@@ -1,4 +1,6 @@
 """GPU path (through the C ABI) against the CPU oracle on the same seeded inputs."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -311,15 +313,17 @@ def test_score_masks_match_oracle():
     g.close()
 
 
-@pytest.mark.parametrize("shape,P,gamma", [(BF16_HD64, 200, 12), (BF16_HD128, 150, 32)],
-                         ids=["hd64-gqa-P200-g12", "hd128-P150-g32"])
+@pytest.mark.parametrize("shape,P,gamma", [(BF16_HD64, 200, 12), (BF16_HD128, 150, 32), (BF16_HD64, 131, 32),
+                                           (BF16_HD128, 257, 8)],
+                         ids=["hd64-gqa-P200-g12", "hd128-P150-g32", "hd64-gqa-P131-g32", "hd128-P257-g8"])
 def test_score_masks_long_prefix_any_pages(shape, P, gamma):
     """Mask scoring over a prompt of several 64-key chunks (the attention walks the
     cached prefix chunk by chunk before the candidates' own window keys; windows of
-    12 and 32 rows, grouped-query heads): the scores and predictions match the
-    oracle's up to its near-ties, and pages of 16 or 32 positions scattered by a
-    permuted page table give the same scores and predictions bit for bit as
-    contiguous 64-position pages."""
+    8, 12 and 32 rows; grouped-query heads: 24 and 64 queries per block, one, two
+    and four waves): the scores and predictions match the oracle's up to its
+    near-ties, and pages of 16 or 32 positions scattered by a permuted page table
+    give the same scores and predictions bit for bit as contiguous 64-position
+    pages."""
     g = gpu_model(shape)
     o = omodel.Model.synthetic(shape)
     L = shape.n_layers
@@ -333,7 +337,8 @@ def test_score_masks_long_prefix_any_pages(shape, P, gamma):
     results = []
     for ps in (64, 16, 32):
         n_lp = (max_ctx + ps - 1) // ps
-        perm = None if ps == 64 else [(7 * i + 3) % n_lp for i in range(n_lp)]
+        mul = next(m for m in range(7, 64) if math.gcd(m, n_lp) == 1)   # (mul i + 3) mod n: a permutation
+        perm = None if ps == 64 else [(mul * i + 3) % n_lp for i in range(n_lp)]
         assert perm is None or sorted(perm) == list(range(n_lp))
         seq = B.Sequence(g, max_ctx=max_ctx, max_rows=len(masks) * gamma, max_draft=4, page_size=ps, page_table=perm)
         seq.generate_ar(dev(prompt), gamma)
