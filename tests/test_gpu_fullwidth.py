@@ -183,3 +183,48 @@ def test_fullwidth_13b_sampled_matches_oracle():
           (events, n_gen, np.bincount(drafted).tolist()))
     seq.close()
     g.close()
+
+
+@pytest.mark.parametrize("name,P,gamma", [("13b", 96, 32), ("70b", 80, 16)], ids=["13b-g32", "70b-gqa-g16"])
+def test_fullwidth_score_masks_match_oracle(name, P, gamma):
+    """Mask scoring at the 13B and 70B decoder widths (two layers): all 16 attention / MLP skip patterns of
+    the two layers as the candidate plans (512 and 256 rows through the batched projections; at 70B eight
+    query heads per KV head, so a block of the scoring attention holds 64 queries), over a prompt of two
+    64-key chunks.  Scores and predictions against the oracle's: a row may differ only where the oracle's
+    top-2 logit margin is within what the arithmetic moves a logit at this width, measured as in the other
+    full-width tests: three times the largest distance between the oracle's window logits and those of its
+    float32-accumulation twin (1.5 times the twin's drift for each of the two logits), and at least 1e-2.
+    (At these widths the 1e-2 rule alone is too tight for any bf16 path: the decode kernels' split-item
+    attention also predicts a 13B-width row differently at an oracle margin of 0.03.)"""
+    from gpu_util import check_scores
+    shape = CASES[name][0]
+    L = shape.n_layers
+    print("[gpu] full-width %s scoring: building weights" % shape.name, flush=True)
+    g = gpu_model(shape)
+    o = omodel.Model.synthetic(shape)
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    ref, kv = ossd.ar_generate(o, prompt, gamma)
+    window = (list(prompt) + ref)[P - 1: P + gamma]
+    masks = [np.array([(m >> i) & 1 for i in range(2 * L)], np.uint8) for m in range(2 ** (2 * L))]
+    oscores, obest, opred, omargin = ossd.score_masks(o, kv, window, P - 1, masks, detail=True)
+    twin = acc32_twin(o)
+    rows, positions = [int(t) for t in window[:-1]], list(range(P - 1, P - 1 + gamma))
+    drift = max(max_abs_rows(omodel.forward(twin, rows, positions, kv.copy(), m),
+                             omodel.forward(o, rows, positions, kv.copy(), m)).max() for m in masks)
+    margin = max(1e-2, 3.0 * drift)
+    print("twin drift %.3g per logit: decision margin %.3g" % (drift, margin))
+    seq = B.Sequence(g, max_ctx=P + gamma + 64, max_rows=len(masks) * gamma, max_draft=4)
+    seq.generate_ar(dev(prompt), gamma)
+    scores = torch.zeros(len(masks), dtype=torch.float32, device="cuda")
+    best = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pred = torch.zeros(len(masks) * gamma, dtype=torch.int32, device="cuda")
+    B.ssd_score_masks(seq.handle, np.stack(masks), dev(window), P - 1, gamma, scores, best, pred)
+    torch.cuda.synchronize()
+    assert B.ssd_read_state(seq.handle).error_flags == 0
+    gs = scores.cpu().numpy()
+    print("scores gpu %s\n       oracle %s" % (gs, oscores))
+    nd = check_scores(gs, int(best.item()), pred.cpu().numpy().reshape(len(masks), gamma), window, oscores, obest,
+                      opred, omargin, margin=margin)
+    print("rows differing from the oracle (all within the margin): %d of %d" % (nd, len(masks) * gamma))
+    seq.close()
+    g.close()
