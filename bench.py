@@ -41,13 +41,13 @@ PMC_TRAFFIC = {
         parts=[dict(launches=104, fetch_kib=88261.6, write_kib=21.5),
                dict(launches=24, fetch_kib=90205.4, write_kib=279.5)],
         fetch_scale=2.0, write_scale=1.0, profile="profiles/dec_7b_hbm_counters.md"),
-    # 13B scoring gate/up: per step 23 launches of 256 rows, 15 of 384 and 2 of 512 (the same masks
+    # 13B scoring gate/up: per step 23 launches of 256 rows, 15 of 384 and 2 of 128 (the same masks
     # every step)
     ("gemm_bf16_tiled<EPI_SWIGLU, 4, 4>", "score13b"): dict(
-        source="self_speculative_layer_amd/csrc/kernels.hip", sha1_prefix="d6be512243bf",
-        parts=[dict(launches=23, fetch_kib=166886.2, write_kib=5409.6),
-               dict(launches=15, fetch_kib=216328.9, write_kib=8410.5),
-               dict(launches=2, fetch_kib=160261.1, write_kib=3146.2)],
+        source="self_speculative_layer_amd/csrc/kernels.hip", sha1_prefix="7b01a014b998",
+        parts=[dict(launches=23, fetch_kib=166564.3, write_kib=5409.6),
+               dict(launches=15, fetch_kib=213456.2, write_kib=8410.6),
+               dict(launches=2, fetch_kib=142826.9, write_kib=3024.0)],
         fetch_scale=2.0, write_scale=1.0, profile="profiles/gemm_tiled_score13b_kernel_trace.md"),
 }
 DOMINANT = "dec_gemm_kernel<DEC_SWIGLU>"

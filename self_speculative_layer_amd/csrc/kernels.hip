@@ -438,18 +438,22 @@ int launch_linear(int dtype, int epi, const void* W, const void* X, int ldx, int
   const bool prof = profile_next(epi, &e0, &e1, &ran);
   int rc;
   if (dtype == SSD_DTYPE_BF16 && M >= TG_MIN_ROWS && K % TG_KS == 0 && (epi != EPI_SWIGLU || N % 64 == 0)) {
-    // large tiles unless they would leave CUs idle; plain epilogues with few small tiles take large tiles
-    // split by K quarter (workspace permitting): below 192 small tiles, or up to 1024 of them for long K
-    // (K >= 8192), where the split measured faster than the small tiles on the 13B shapes in spite of its
-    // partial sums and reduce launch (K = 5120 at 192 - 512 small tiles: 10-20 % slower split)
-    const bool big = tg_blocks(epi, M, N, 4, 4) >= 256;
+    // Tile choice (all three give the same bits), measured on the 13B shapes over M = 96 - 512:
+    // - large tiles from 256 of them, or from 192 when the last 128-row block is at least three quarters
+    //   full (QKV at M = 224 - 256, gate/up at M = 96 - 128: 4-20 % faster than the small tiles);
+    // - otherwise plain epilogues with few small tiles take the large tiles split by K quarter (workspace
+    //   permitting): below 192 small tiles, or up to 1024 of them for long K (K >= 8192), where the split
+    //   wins in spite of its partial sums and reduce launch (K = 5120 at 192 - 512 small tiles: 10-20 %
+    //   slower than the small tiles);
+    // - otherwise the small tiles.
+    const int big_blocks = tg_blocks(epi, M, N, 4, 4);
+    const bool big = big_blocks >= 256 || (big_blocks >= 192 && (M % 128 == 0 || M % 128 >= 96));
     const int small_blocks = tg_blocks(epi, M, N, 2, 2);
     const bool split = !big && epi != EPI_SWIGLU && split_ws && 4 * (size_t)M * N <= split_floats &&
                        (K >= 8192 ? small_blocks <= 1024 : small_blocks < 192);
     const int WJ = big || split ? 4 : 2;
     const int n_mb = (M + 32 * WJ - 1) / (32 * WJ);
-    const dim3 grid(big ? tg_blocks(epi, M, N, 4, 4)
-                        : (split ? 4 * tg_blocks(epi, M, N, 4, 4) : tg_blocks(epi, M, N, 2, 2)));
+    const dim3 grid(big ? big_blocks : (split ? 4 * big_blocks : tg_blocks(epi, M, N, 2, 2)));
     const bf16_t* w = (const bf16_t*)W;
     const bf16_t* x = (const bf16_t*)X;
 #define TILED(E, I, J)                                                                                            \
