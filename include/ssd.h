@@ -403,8 +403,11 @@ int ssd_swift_propose(int n_layers, int n_skip, int sublayers, uint64_t seed, in
  * 0..8 n_cand - 1 of the step's counter) by expected improvement over the incumbent, and the n_cand
  * best (lower pool index first among equal values) are scored, best first; when every score seen
  * so far is equal the step proposes at random.  Requires (n_cand + 1) * gamma <= max_rows and
- * n_cand + 1 <= 64.  Out: best_mask_host[2L] (the incumbent), *best_score, *n_steps.  Synchronises
- * the stream once per step (the scores decide the next step). */
+ * n_cand + 1 <= 64.  Random proposals do not depend on earlier scores, so a step and the random steps
+ * after it (up to the next Bayesian step, as many as max_rows / gamma window rows hold) are scored in
+ * one batched pass and then applied in order; a stop drops the later steps' scores.  The results are
+ * those of one pass per step, bit for bit.  Out: best_mask_host[2L] (the incumbent), *best_score,
+ * *n_steps (the steps applied).  Synchronises the stream once per scoring pass. */
 int ssd_swift_search(ssd_seq* seq, const int32_t* window_dev, int pos0, int gamma, const uint8_t* init_mask_host,
                      int n_skip, int sublayers, int n_cand, int max_steps, int patience, float target, uint64_t seed,
                      int bo_every, uint8_t* best_mask_host, float* best_score, int* n_steps, hipStream_t stream);

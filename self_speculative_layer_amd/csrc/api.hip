@@ -94,7 +94,7 @@ struct Workspace {
   StatRec* stat_recs;    // row statistics: segment records [rows][segments]
   unsigned* stat_ctr;    //   and per-row counters, zero between launches
   float* gemm_split;     // quarter sums of K-split projections [4][R][D]
-  float* swift_scores;   // layer-set search: one step's scores [64]
+  float* swift_scores;   // layer-set search: the scores of one scoring pass [max(64, R)]
   int32_t* swift_best;   //   and its best index
   // draft trees
   bf16_t* tree_kv;       // leaves' keys and values [L][TREE_SLOTS][2][KVH * HD] (not in the cache)
@@ -160,7 +160,7 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.stat_recs = (StatRec*)take(sizeof(StatRec) * (size_t)R * stat_segments(V));
   t.stat_ctr = (unsigned*)take(sizeof(unsigned) * (size_t)R);
   t.gemm_split = (float*)take(sizeof(float) * 4 * (size_t)R * D);
-  t.swift_scores = (float*)take(sizeof(float) * 64);
+  t.swift_scores = (float*)take(sizeof(float) * std::max(64, R));
   t.swift_best = (int32_t*)take(sizeof(int32_t) * 4);
   t.tree_kv = (bf16_t*)take(2 * (size_t)L * TREE_SLOTS * 2 * m->kv_dim);
   t.hp = (float*)take(sizeof(float) * 16 * (size_t)D);
@@ -1039,59 +1039,85 @@ extern "C" int ssd_swift_propose(int n_layers, int n_skip, int sublayers, uint64
 // One run of the search on a window: steps numbered step0, step0 + 1, ... (proposal counters and the
 // Bayesian schedule), the run of unimproved steps starting at unimproved0.  inc: the starting plan in, the
 // final incumbent out.
+// Search steps step0 .. step0 + max_steps - 1 from the incumbent `inc`.  The proposals of a random step
+// depend only on (seed, step, candidate), so a step and the random steps after it (up to the next
+// Bayesian step, within the sequence's row limit) are scored in one pass; the steps are then taken in
+// order as if scored one by one (a row's scores do not depend on the rows batched with it), and the
+// passes' extra steps after a stop are discarded.
 int swift_phase(ssd_seq* q, const int32_t* window_dev, int pos0, int gamma, std::vector<uint8_t>& inc, int n_skip,
                 int sublayers, int n_cand, int max_steps, int patience, float target, uint64_t seed, int bo_every,
                 int step0, int unimproved0, float* score, int* n_steps, int* unimproved_out, hipStream_t s) {
   const int L = q->m->d.n_layers;
   const size_t ML = 2 * (size_t)L;
-  std::vector<uint8_t> masks((n_cand + 1) * ML);
-  std::vector<float> sc(n_cand + 1);
-  std::vector<uint8_t> obs_m, pool;     // every scored plan, in scoring order, and a BO step's pool
+  const int max_masks = std::max(n_cand + 1, q->max_rows / gamma);   // masks one scoring pass can hold
+  std::vector<uint8_t> masks;
+  std::vector<float> sc;
+  std::vector<int> first;               // a pass's steps: index of each one's first mask, then the end
+  std::vector<uint8_t> obs_m, pool;     // every scored plan of the steps taken, in scoring order, and a BO pool
   std::vector<double> obs_s;
   std::vector<int> picks;
   float inc_score = 0.f;
   int unimproved = unimproved0, t = 0;
-  while (t < max_steps) {
-    const int st = step0 + t;
-    int off = 0;
-    if (t == 0) {
-      std::copy(inc.begin(), inc.end(), masks.begin());
-      off = 1;
+  bool stop = false;
+  auto is_bo = [&](int st) { return bo_every > 0 && st > 0 && st % bo_every == 0; };
+  while (t < max_steps && !stop) {
+    // ---- the pass: step t, then random steps while they fit
+    masks.clear();
+    first.clear();
+    for (int u = t; u < max_steps; ++u) {
+      const int st = step0 + u;
+      const int off = u == 0 ? 1 : 0;
+      const int nm = (int)(masks.size() / ML);
+      if (u > t && (is_bo(st) || nm + n_cand + off > max_masks)) break;
+      first.push_back(nm);
+      masks.resize((size_t)(nm + n_cand + off) * ML);
+      uint8_t* m = masks.data() + (size_t)nm * ML;
+      if (off) std::copy(inc.begin(), inc.end(), m);
+      bool bo = false;
+      if (is_bo(st)) {                  // only the pass's first step: the history is complete
+        const int P = BO_POOL_FACTOR * n_cand;
+        pool.resize((size_t)P * ML);
+        for (int c = 0; c < P; ++c) propose_layers(L, n_skip, sublayers, seed, st, c, pool.data() + c * ML);
+        const int n = std::min((int)obs_s.size(), BO_WINDOW);
+        const size_t f0 = obs_s.size() - n;
+        bo = bo_rank(obs_m.data() + f0 * ML, obs_s.data() + f0, n, inc_score, pool.data(), P, ML, n_cand, picks);
+        if (bo)
+          for (int c = 0; c < n_cand; ++c)
+            std::copy(pool.begin() + picks[c] * ML, pool.begin() + (picks[c] + 1) * ML, m + (off + c) * ML);
+      }
+      if (!bo)
+        for (int c = 0; c < n_cand; ++c) propose_layers(L, n_skip, sublayers, seed, st, c, m + (off + c) * ML);
     }
-    bool bo = false;
-    if (bo_every > 0 && st > 0 && st % bo_every == 0) {
-      const int P = BO_POOL_FACTOR * n_cand;
-      pool.resize((size_t)P * ML);
-      for (int c = 0; c < P; ++c) propose_layers(L, n_skip, sublayers, seed, st, c, pool.data() + c * ML);
-      const int n = std::min((int)obs_s.size(), BO_WINDOW);
-      const size_t first = obs_s.size() - n;
-      bo = bo_rank(obs_m.data() + first * ML, obs_s.data() + first, n, inc_score, pool.data(), P, ML, n_cand, picks);
-      if (bo)
-        for (int c = 0; c < n_cand; ++c)
-          std::copy(pool.begin() + picks[c] * ML, pool.begin() + (picks[c] + 1) * ML, masks.begin() + (off + c) * ML);
-    }
-    if (!bo)
-      for (int c = 0; c < n_cand; ++c) propose_layers(L, n_skip, sublayers, seed, st, c, masks.data() + (off + c) * ML);
-    const int nm = n_cand + off;
-    TRY(ssd_score_masks(q, masks.data(), nm, window_dev, pos0, gamma, q->w.swift_scores, q->w.swift_best, nullptr,
-                        s));
-    if (hipMemcpy(sc.data(), q->w.swift_scores, sizeof(float) * nm, hipMemcpyDeviceToHost) != hipSuccess)
+    const int total = (int)(masks.size() / ML);
+    first.push_back(total);
+    sc.resize(total);
+    TRY(ssd_score_masks(q, masks.data(), total, window_dev, pos0, gamma, q->w.swift_scores, q->w.swift_best,
+                        nullptr, s));
+    if (hipMemcpy(sc.data(), q->w.swift_scores, sizeof(float) * total, hipMemcpyDeviceToHost) != hipSuccess)
       return fail(SSD_ERR_HIP, "read scores");
-    if (t == 0) inc_score = sc[0];
-    obs_m.insert(obs_m.end(), masks.begin(), masks.begin() + nm * ML);
-    for (int c = 0; c < nm; ++c) obs_s.push_back((double)sc[c]);
-    int k = off;
-    for (int c = off + 1; c < nm; ++c)
-      if (sc[c] > sc[k]) k = c;
-    if (sc[k] > inc_score) {
-      std::copy(masks.begin() + k * ML, masks.begin() + (k + 1) * ML, inc.begin());
-      inc_score = sc[k];
-      unimproved = 0;
-    } else {
-      ++unimproved;
+    // ---- the pass's steps in order
+    for (size_t i = 0; i + 1 < first.size(); ++i) {
+      const int b = first[i], e = first[i + 1];
+      const int off = t == 0 ? 1 : 0;
+      if (t == 0) inc_score = sc[b];
+      obs_m.insert(obs_m.end(), masks.begin() + (size_t)b * ML, masks.begin() + (size_t)e * ML);
+      for (int c = b; c < e; ++c) obs_s.push_back((double)sc[c]);
+      int k = b + off;
+      for (int c = b + off + 1; c < e; ++c)
+        if (sc[c] > sc[k]) k = c;
+      if (sc[k] > inc_score) {
+        std::copy(masks.begin() + (size_t)k * ML, masks.begin() + (size_t)(k + 1) * ML, inc.begin());
+        inc_score = sc[k];
+        unimproved = 0;
+      } else {
+        ++unimproved;
+      }
+      ++t;
+      if (inc_score > target || unimproved >= patience) {
+        stop = true;
+        break;
+      }
     }
-    ++t;
-    if (inc_score > target || unimproved >= patience) break;
   }
   *score = inc_score;
   *n_steps = t;

@@ -470,13 +470,14 @@ def test_long_context_attention_paths_agree(shape):
                               "f32-gqa-sublayers-bo2", "bf16-hd128-sublayers-bo2"])
 def test_swift_search_matches_oracle(shape, sublayers, bo_every, n_sub, seed):
     """SWIFT search (ssd_swift_search: proposals and the Bayesian-optimisation
-    step on the host, one batched scoring pass per step) against the oracle's
+    step on the host, batched scoring passes) against the oracle's
     search with its own scoring: same number of steps, same final plan, score
     within the scoring tolerance.  The target is out of reach, so the search runs
     until its patience ends.  In the bo2 cases (n_sub sub-layers skipped, evenly
     spaced at the start) every second step is a BO step, and on these inputs the
     BO steps change the oracle's path (final plan and score) against plain
-    random search."""
+    random search.  With rows for several steps per pass (a step and the random
+    steps after it scored together) the search is the same bit for bit."""
     from oracle import swift
     g = gpu_model(shape)
     o = omodel.Model.synthetic(shape)
@@ -512,6 +513,14 @@ def test_swift_search_matches_oracle(shape, sublayers, bo_every, n_sub, seed):
     # the final plan's score may differ only by its rows that are oracle near-ties (top-2 margin < 1e-2)
     _, _, _, om = ossd.score_masks(o, kv, window, P - 1, [obest], detail=True)
     assert abs(gscore - oscore) <= int((om < 1e-2).sum()) / gamma + 1e-7
+    seq.close()
+    # room for several steps per scoring pass (the random steps after a step, up to the next BO step, are
+    # scored with it): the same search, bit for bit
+    seq = B.Sequence(g, max_ctx=P + gamma + 64, max_rows=4 * (n_cand + 1) * gamma, max_draft=4)
+    seq.generate_ar(dev(prompt), gamma)
+    bbest, bscore, bsteps = B.ssd_swift_search(seq.handle, dev(window), P - 1, gamma, init, n_skip, n_cand, steps,
+                                               patience, 1.5, seed, L, sublayers=sublayers, bo_every=bo_every)
+    assert bsteps == gsteps and bscore == gscore and np.array_equal(bbest, gbest)
     seq.close()
     g.close()
 

@@ -19,10 +19,12 @@ from gpu_util import BF16_HD64, F32_GQA, check_greedy_tokens, dev, gpu_model, or
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_run(g, shape, prompt, cfg, init, n_gen):
+def _gpu_run(g, shape, prompt, cfg, init, n_gen, rows_factor=1):
     """One iteration per call; returns (tokens, n_out after each iteration, plan each iteration drafted with,
-    per-phase records)."""
-    seq = B.Sequence(g, max_ctx=len(prompt) + n_gen + 64, max_rows=(cfg.n_cand + 1) * cfg.gamma, max_draft=cfg.d)
+    per-phase records).  rows_factor: the sequence's row limit in units of one search step's rows (above 1 a
+    scoring pass takes several steps)."""
+    seq = B.Sequence(g, max_ctx=len(prompt) + n_gen + 64, max_rows=rows_factor * (cfg.n_cand + 1) * cfg.gamma,
+                     max_draft=cfg.d)
     B.ssd_prefill(seq.handle, dev(prompt))
     st = B.ssd_swift_begin(seq.handle, cfg)
     assert st.last_phase_n_out == 1 and st.phases == 0
@@ -87,6 +89,15 @@ def test_swift_generate_matches_oracle(shape, n_skip, acc, per, max_steps, patie
         assert np.array_equal(plans[k], otr["plans"][k]), k
     assert (st.steps, st.unimproved, bool(st.done)) == (otr["steps"], otr["unimproved"], otr["done"])
     assert st.switches == sum(1 for p in otr["phases"] if not np.array_equal(p["before"], p["after"]))
+    # rows for several search steps per scoring pass: the same run, bit for bit
+    toks2, nouts2, plans2, phases2, st2 = _gpu_run(g, shape, prompt, cfg, init, n_gen, rows_factor=3)
+    assert toks2 == toks and nouts2 == nouts
+    assert all(np.array_equal(a, b) for a, b in zip(plans2[1:], plans[1:]))
+    assert len(phases2) == len(phases)
+    for a, b in zip(phases2, phases):
+        assert np.array_equal(a["after"], b["after"]) and a["score"] == b["score"] and a["steps"] == b["steps"]
+        assert (a["n_out"], a["unimproved"], a["done"]) == (b["n_out"], b["unimproved"], b["done"])
+    assert (st2.steps, st2.unimproved, st2.done, st2.switches) == (st.steps, st.unimproved, st.done, st.switches)
     g.close()
 
 
