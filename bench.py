@@ -245,6 +245,8 @@ def main():
                     choices=sorted(WORKLOADS) + sorted(SCORING) + ["exit7b", "swiftotf13b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ar-steps", type=int, default=16)
+    ap.add_argument("--search-steps-per-pass", type=int, default=8,
+                    help="swift13b / swiftotf13b: search steps scored together in one pass (the rows allotted)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -560,8 +562,9 @@ def run_swift_otf(args):
                     shape.vocab, shape.dtype, tensors)
     K, W, P, gamma, n_skip, n_cand, per, d = args.steps, args.warmup, 1024, 32, 20, 15, 8, 8
     n_gen = (K + W) * gamma
-    # rows for two search steps per scoring pass
-    seq = B.Sequence(model, max_ctx=P + n_gen + 64, max_rows=2 * (n_cand + 1) * gamma, max_draft=d, device=dev)
+    # rows for the search steps scored together in one pass
+    spp = args.search_steps_per_pass
+    seq = B.Sequence(model, max_ctx=P + n_gen + 64, max_rows=(spp * n_cand + 1) * gamma, max_draft=d, device=dev)
     B.ssd_prefill(seq.handle, torch.from_numpy(synth.prompt_tokens(P, shape.vocab)).to(dev), 1.0,
                   synth.SEED_SAMPLING)
     cfg = B.swift_config(gamma, n_skip, n_cand, per, 1000, 300, 0.95, d, synth.SEED_SAMPLING, bo_every=25,
@@ -594,7 +597,8 @@ def run_swift_otf(args):
                                "layers, a phase of <= 8 search steps (15 proposals of 20 layers, Bayesian step "
                                "every 25 steps) after every 32 committed tokens on the last 33, d<=8, confidence "
                                "stop 0.8, T=1.0, 1024-token random prompt",
-                   "step": "one ssd_swift_generate call of 32 tokens (its iterations and the phase after them)"},
+                   "step": "one ssd_swift_generate call of 32 tokens (its iterations and the phase after them)",
+                   "search_steps_per_pass": spp},
         "timing": "wall clock around the calls (each iteration and each optimisation step synchronises the stream)",
         "tokens": tokens, "iterations": st.iterations - it0,
         "M_tokens_per_iteration": round(tokens / max(st.iterations - it0, 1), 3),
@@ -633,10 +637,11 @@ def run_scoring(args):
     P, gamma, nm = wl["prompt"], wl["gamma"], wl["n_masks"]
     masks = synth.scoring_masks(shape.n_layers, nm, wl["skip_lo"], wl["skip_hi"])
     search = wl.get("search", False)
-    # the search scores a step together with the random steps after it while the rows allow: room for two
-    # steps per scoring pass
-    per_call = 2 if search else 1
-    seq = B.Sequence(model, max_ctx=P + gamma + 64, max_rows=per_call * nm * gamma, max_draft=1, device=dev)
+    # the search scores a step together with the random steps after it while the rows allow: room for
+    # --search-steps-per-pass steps per scoring pass, and one call runs that many steps
+    per_call = args.search_steps_per_pass if search else 1
+    seq = B.Sequence(model, max_ctx=P + gamma + 64, max_rows=(per_call * (nm - 1) + 1) * gamma, max_draft=1,
+                     device=dev)
     prompt = torch.from_numpy(synth.prompt_tokens(P, shape.vocab)).to(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
@@ -659,8 +664,8 @@ def run_scoring(args):
 
     def step():
         if search:
-            # two search steps per call, scored in one pass (step 0: the starting plan and 15 proposals, step 1:
-            # 15 more; a new seed each call; no stop rule can end the call early)
+            # per_call search steps per call, scored in one pass (step 0: the starting plan and 15 proposals,
+            # each later step 15 more; a new seed each call; no stop rule can end the call early)
             sd = synth.SEED_MASKS + len(used)
             bm, bs, ns = B.ssd_swift_search(seq.handle, window, P - 1, gamma, init, n_skip, nm - 1, per_call, 1000,
                                             2.0, sd, shape.n_layers)
@@ -713,8 +718,8 @@ def run_scoring(args):
                  "flop_per_step": flops / K / per_call, "bytes_per_launch": round(prof_bytes / max(prof_n, 1)),
                  "measured": "dispatch-timestamp events on every launch of the kernel in %d further steps" % K})
     result = {
-        "metric": ("SWIFT search steps/s (15 proposals x 32-token window; two steps per call and scoring pass)"
-                   if search else
+        "metric": ("SWIFT search steps/s (15 proposals x 32-token window; %d steps per call and scoring pass)"
+                   % per_call if search else
                    "mask-scoring steps/s (16 candidate plans x 32-token window)"),
         "value": round(1e3 / ms, 4), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

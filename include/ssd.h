@@ -158,10 +158,14 @@ int ssd_model_destroy(ssd_model* model);
 int ssd_kv_pool_bytes(const ssd_model* model, int n_pages, int page_size, size_t* bytes);
 
 /* Bytes of the per-sequence device workspace.
- *   max_rows   largest row block processed at once: prefill chunk, d + 1 for
- *              verify, n_masks * gamma for scoring (<= 1024);
+ *   max_rows   largest row block processed at once: d + 1 for verify, n_masks * gamma
+ *              for scoring, the prefill chunk (prefill takes at most 1024 rows at a
+ *              time); 1..SSD_MAX_ROWS.  Scoring more than 1024 rows needs a bf16 model
+ *              with head_dim 64 or 128 and at most 64 query heads per KV head
+ *              (SSD_ERR_UNSUPPORTED otherwise);
  *   max_draft  largest d passed to ssd_draft (<= 32);
  *   max_ctx    page_size * n_logical_pages of the sequence. */
+#define SSD_MAX_ROWS 4096
 int ssd_workspace_bytes(const ssd_model* model, int max_rows, int max_draft, int max_ctx,
                         size_t* bytes);
 
@@ -179,7 +183,7 @@ int ssd_seq_create(const ssd_model* model, void* kv_pool_dev, int n_pages, int p
 int ssd_seq_destroy(ssd_seq* seq);
 
 /* Prefill (row a7): the n prompt tokens tokens_dev[0..n-1] at positions 0..n-1
- * through the full model (in chunks of max_rows rows); then the first
+ * through the full model (in chunks of min(max_rows, 1024) rows); then the first
  * generated token is picked from the last row's logits (argmax at temperature
  * 0, else a draw with iteration 0) and committed.  After it: kvlen = n,
  * n_out = 1.  last_logits_dev[V] (nullable) receives the last row's logits. */

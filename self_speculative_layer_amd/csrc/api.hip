@@ -140,7 +140,8 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.h1 = (float*)take(sizeof(float) * D);
   t.inv = (float*)take(sizeof(float) * R);
   t.qkv = (float*)take(sizeof(float) * (size_t)R * m->qkv_dim);
-  t.part = (float*)take(sizeof(float) * attention_partial_floats(R, d.n_heads, d.head_dim, max_ctx));
+  t.part = (float*)take(sizeof(float) * attention_partial_floats(std::min(R, SPLIT_ATTN_MAX_ROWS), d.n_heads,
+                                                                 d.head_dim, max_ctx));
   t.hb = (float*)take(sizeof(float) * (size_t)max_draft * D);
   t.logits1 = (float*)take(sizeof(float) * V);
   t.logits_rows = (float*)take(sizeof(float) * (size_t)R * V);
@@ -440,7 +441,7 @@ extern "C" int ssd_kv_pool_bytes(const ssd_model* m, int n_pages, int page_size,
 extern "C" int ssd_workspace_bytes(const ssd_model* m, int max_rows, int max_draft, int max_ctx, size_t* bytes) {
   CHECK_MODEL(m);
   CHECK_ARG(m && bytes, "null argument");
-  CHECK_ARG(max_rows >= 1 && max_rows <= 1024, "max_rows must be in 1..1024");
+  CHECK_ARG(max_rows >= 1 && max_rows <= SSD_MAX_ROWS, "max_rows must be in 1..4096");
   CHECK_ARG(max_draft >= 1 && max_draft <= 32, "max_draft must be in 1..32");
   CHECK_ARG(max_ctx >= 1, "max_ctx must be positive");
   *bytes = carve(m, std::max(max_rows, max_draft + 1), max_draft, max_ctx, nullptr, nullptr);
@@ -458,7 +459,7 @@ extern "C" int ssd_seq_create(const ssd_model* m, void* kv_pool_dev, int n_pages
   CHECK_ARG(m && kv_pool_dev && page_table_host && workspace_dev && out_seq, "null argument");
   CHECK_ARG(page_size == 16 || page_size == 32 || page_size == 64, "page_size must be 16, 32 or 64");
   CHECK_ARG(n_pages > 0 && n_logical_pages > 0, "no pages");
-  CHECK_ARG(max_rows >= 1 && max_rows <= 1024 && max_draft >= 1 && max_draft <= 32, "bad row limits");
+  CHECK_ARG(max_rows >= 1 && max_rows <= SSD_MAX_ROWS && max_draft >= 1 && max_draft <= 32, "bad row limits");
   for (int i = 0; i < n_logical_pages; ++i)
     CHECK_ARG(page_table_host[i] >= 0 && page_table_host[i] < n_pages, "page table entry out of range");
   const int R = std::max(max_rows, max_draft + 1);
@@ -535,8 +536,9 @@ extern "C" int ssd_prefill(ssd_seq* q, const int32_t* tokens_dev, int n, float t
   const Workspace& w = q->w;
   TRY(launch_state_init(w.st, s));
   int last_rows = 0;
-  for (int c0 = 0; c0 < n; c0 += q->max_rows) {
-    const int M = std::min(q->max_rows, n - c0);
+  const int chunk = std::min(q->max_rows, SPLIT_ATTN_MAX_ROWS);
+  for (int c0 = 0; c0 < n; c0 += chunk) {
+    const int M = std::min(chunk, n - c0);
     TRY(launch_fill_positions(w.pos, M, c0, s));
     TRY(launch_embed(d.dtype, d.embed, tokens_dev + c0, d.vocab, w.h, d.d_model, M, d.d_model, nullptr, nullptr,
                      s));
@@ -862,6 +864,8 @@ extern "C" int ssd_score_masks(ssd_seq* q, const uint8_t* masks_host, int n_mask
   const int L = d.n_layers;
   const int R = n_masks * gamma;
   if (R > q->max_rows) return fail(SSD_ERR_CAPACITY, "n_masks * gamma exceeds max_rows");
+  if (R > SPLIT_ATTN_MAX_ROWS && !attention_groups_usable(d.dtype, d.head_dim, d.n_heads, d.n_kv_heads))
+    return fail(SSD_ERR_UNSUPPORTED, "more than 1024 scoring rows need a bf16 model with head_dim 64 or 128");
   if (pos0 + gamma > q->max_ctx) return fail(SSD_ERR_CAPACITY, "window beyond the KV pages");
   const Workspace& w = q->w;
   // compact row lists per sub-layer: rows of the candidates that run it
@@ -1049,7 +1053,11 @@ int swift_phase(ssd_seq* q, const int32_t* window_dev, int pos0, int gamma, std:
                 int step0, int unimproved0, float* score, int* n_steps, int* unimproved_out, hipStream_t s) {
   const int L = q->m->d.n_layers;
   const size_t ML = 2 * (size_t)L;
-  const int max_masks = std::max(n_cand + 1, q->max_rows / gamma);   // masks one scoring pass can hold
+  // masks one scoring pass can hold (beyond 1024 rows only where the scoring attention takes them)
+  const ssd_model_desc& d = q->m->d;
+  const int row_cap = attention_groups_usable(d.dtype, d.head_dim, d.n_heads, d.n_kv_heads)
+                          ? q->max_rows : std::min(q->max_rows, SPLIT_ATTN_MAX_ROWS);
+  const int max_masks = std::max(n_cand + 1, row_cap / gamma);
   std::vector<uint8_t> masks;
   std::vector<float> sc;
   std::vector<int> first;               // a pass's steps: index of each one's first mask, then the end

@@ -74,6 +74,13 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
 int launch_attention_groups(int head_dim, const void* q, int ldq, const KvView& kv, int L, int layer, int H, int KVH,
                             const RowBlock& rb, const void* local_kv, int local_start, int group_rows, void* out,
                             int ldo, hipStream_t s);
+// Whether launch_attention takes launch_attention_groups for candidate groups of this model shape.
+inline bool attention_groups_usable(int dtype, int head_dim, int H, int KVH) {
+  return dtype == SSD_DTYPE_BF16 && (head_dim == 64 || head_dim == 128) && H / KVH <= 64;
+}
+// Rows one launch of the split-key attention takes (the partial buffer holds this many rows); prefill
+// chunks are at most this long.
+constexpr int SPLIT_ATTN_MAX_ROWS = 1024;
 size_t attention_partial_floats(int max_rows, int H, int head_dim, int max_ctx);
 // Number of fixed key splits covering max_ctx positions (the partial buffer's split dimension).
 int attention_nsplit(int max_ctx);

@@ -767,10 +767,10 @@ int launch_attention(int dtype, int head_dim, const void* q, int ldq, const KvVi
   if (out_blocked && rb.M > 16) return SSD_ERR_SHAPE;
   const int G = H / KVH;
   // candidate groups of the scoring pass: one online-softmax walk over the keys per group and head
-  if (dtype == SSD_DTYPE_BF16 && local_kv && group_rows > 0 && !out_blocked && G <= 64 &&
-      (head_dim == 64 || head_dim == 128))
+  if (local_kv && group_rows > 0 && !out_blocked && attention_groups_usable(dtype, head_dim, H, KVH))
     return launch_attention_groups(head_dim, q, ldq, kv, L, layer, H, KVH, rb, local_kv, local_start, group_rows,
                                    out, ldo, s);
+  if (rb.M > SPLIT_ATTN_MAX_ROWS) return SSD_ERR_SHAPE;   // the partial buffer's row capacity
   int RB = (dtype == SSD_DTYPE_BF16 ? ATTB_MAXQ : ATT_MAXQ) / G;
   if (RB < 1) return SSD_ERR_SHAPE;
   // bf16 rows beyond a decode block: several 16-query tiles per item (the rows of an item share one

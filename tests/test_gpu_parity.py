@@ -526,6 +526,36 @@ def test_swift_search_matches_oracle(shape, sublayers, bo_every, n_sub, seed):
 
 
 @pytest.mark.parametrize("shape", [BF16_HD64, BF16_HD128, F32_GQA], ids=lambda s: s.name)
+def test_swift_search_passes_beyond_1024_rows(shape):
+    """Eight random search steps of 15 proposals on a 32-token window with rows
+    for all of them in one scoring pass (1 + 8 * 15 plans, 3872 rows; f32 models
+    keep their passes within 1024 rows, the split attention's capacity) and with
+    one step per pass: the same steps, score and plan, bit for bit.  The row
+    invariance of the projections and of the scoring attention makes a candidate's
+    rows independent of the pass they run in."""
+    g = gpu_model(shape)
+    o = omodel.Model.synthetic(shape)
+    P, gamma, n_cand, steps = 40, 32, 15, 8
+    L = shape.n_layers
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    ref, _ = ossd.ar_generate(o, prompt, gamma)
+    window = (list(prompt) + ref)[P - 1: P + gamma]
+    init = B.ssd_uniform_mask(L, 1)
+    out = []
+    for max_rows in ((n_cand + 1) * gamma, (steps * n_cand + 1) * gamma):
+        print("[gpu] %s: search with max_rows %d" % (shape.name, max_rows), flush=True)
+        seq = B.Sequence(g, max_ctx=P + gamma + 64, max_rows=max_rows, max_draft=4)
+        seq.generate_ar(dev(prompt), gamma)      # the cache holds the full model's keys and values
+        out.append(B.ssd_swift_search(seq.handle, dev(window), P - 1, gamma, init, 1, n_cand, steps, 100, 1.5, 11,
+                                      L, sublayers=True))
+        seq.close()
+    (b0, s0, n0), (b1, s1, n1) = out
+    assert n0 == n1 == steps
+    assert s0 == s1 and np.array_equal(b0, b1)
+    g.close()
+
+
+@pytest.mark.parametrize("shape", [BF16_HD64, BF16_HD128, F32_GQA], ids=lambda s: s.name)
 def test_decode_exit_matches_oracle(shape):
     """Lossy early-exit decoding (ssd_decode_exit, exit at layer 1 and a skip mask)
     against the oracle's exit_generate: tokens by the margin rule, each step's
