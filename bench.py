@@ -698,8 +698,10 @@ def run_scoring(args):
     D, F = shape.d_model, shape.ffn_dim
     flops = 0.0
     for mk in used[n_before:]:
-        keep_mlp = (mk[:, 1::2] == 0).sum(axis=0)         # candidates running each layer's MLP
-        flops += float(sum(2.0 * (c * gamma) * 2 * F * D for c in keep_mlp if c > 0))
+        # a sub-layer runs once per class of candidates that run it with equal plans before it
+        for sl in range(1, mk.shape[1], 2):               # each layer's MLP
+            classes = {mk[c, :sl].tobytes() for c in range(mk.shape[0]) if mk[c, sl] == 0}
+            flops += 2.0 * (len(classes) * gamma) * 2 * F * D
     gu_ms = prof_ms
     tflops = flops / (gu_ms / 1e3) / 1e12 if gu_ms > 0 else 0.0
     gbps = prof_bytes / (gu_ms / 1e3) / 1e9 if gu_ms > 0 else 0.0

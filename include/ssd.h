@@ -366,6 +366,9 @@ int ssd_accept_tree(ssd_seq* seq, const float* logits_dev, const float* q_logits
  * scores_dev[c] = #(prediction i == window[i+1]) / gamma; best_dev[0] = the
  * highest-scoring candidate (lowest index on ties); row_pred_dev (nullable)
  * [n_masks * gamma] receives each row's prediction (candidate-major).
+ * Candidates whose plans agree on the sub-layers before a sub-layer share its
+ * computation (it runs once for them); each candidate's results are those it
+ * gets when scored alone, bit for bit.
  * Requires n_masks * gamma <= max_rows. */
 int ssd_score_masks(ssd_seq* seq, const uint8_t* masks_host, int n_masks, const int32_t* window_dev,
                     int pos0, int gamma, float* scores_dev, int32_t* best_dev, int32_t* row_pred_dev,

@@ -153,7 +153,7 @@ size_t carve(const ssd_model* m, int max_rows, int max_draft, int max_ctx, char*
   t.stats = (ssd_row_stat*)take(sizeof(ssd_row_stat) * R);
   t.dec = (int*)take(sizeof(int) * (max_draft + 1));
   t.corr = (int*)take(sizeof(int) * (max_draft + 1));
-  t.rowmaps = (int*)take(sizeof(int) * (size_t)2 * L * R);
+  t.rowmaps = (int*)take(sizeof(int) * ((size_t)2 * L * R + 4 * (size_t)R));   // row lists + copy pairs
   t.log = (int32_t*)take(sizeof(int32_t) * (size_t)max_ctx);
   t.xg = (float*)take(sizeof(float) * (size_t)16 * std::max(D, m->q_dim));
   t.ss = (float*)take(sizeof(float) * (size_t)16 * (D / 16 + 1));
@@ -868,31 +868,79 @@ extern "C" int ssd_score_masks(ssd_seq* q, const uint8_t* masks_host, int n_mask
     return fail(SSD_ERR_UNSUPPORTED, "more than 1024 scoring rows need a bf16 model with head_dim 64 or 128");
   if (pos0 + gamma > q->max_ctx) return fail(SSD_ERR_CAPACITY, "window beyond the KV pages");
   const Workspace& w = q->w;
-  // compact row lists per sub-layer: rows of the candidates that run it
-  std::vector<int> maps((size_t)2 * L * R);
+  // Candidates whose plans agree on every sub-layer before sl carry the same residual rows into sl, so a
+  // sub-layer runs once per class of such candidates, on the rows of one member (its holder).  Where a
+  // class splits at sl (some members run it, the others skip it), the part without the holder becomes a
+  // new class whose first member takes a copy of the holder's rows before sl runs.  Every candidate's
+  // rows thus go through the same computation as when scored alone (a row's result does not depend on
+  // the other rows of its launch).
+  const size_t ML = 2 * (size_t)L;
+  std::vector<int> cls(n_masks, 0), hold(1, 0);   // class of each candidate; holder of each class
+  std::vector<int> maps, copies;                   // row lists of the sub-layers; (src, dst) holder pairs
+  std::vector<size_t> map_off(2 * L), copy_off(2 * L + 2);
   std::vector<int> counts(2 * L);
   for (int sl = 0; sl < 2 * L; ++sl) {
-    int n = 0;
-    for (int c = 0; c < n_masks; ++c)
-      if (!masks_host[(size_t)c * 2 * L + sl])
-        for (int i = 0; i < gamma; ++i) maps[(size_t)sl * R + n++] = c * gamma + i;
-    counts[sl] = n;
+    auto runs = [&](int c) { return masks_host[(size_t)c * ML + sl] == 0; };
+    const int nc = (int)hold.size();
+    std::vector<int> first_run(nc, -1), first_skip(nc, -1);
+    for (int c = 0; c < n_masks; ++c) {
+      int& f = runs(c) ? first_run[cls[c]] : first_skip[cls[c]];
+      if (f < 0) f = c;
+    }
+    copy_off[sl] = copies.size();
+    for (int k = 0; k < nc; ++k) {
+      if (first_run[k] < 0 || first_skip[k] < 0) continue;
+      const bool holder_runs = runs(hold[k]);
+      const int nh = holder_runs ? first_skip[k] : first_run[k];
+      for (int c = 0; c < n_masks; ++c)
+        if (cls[c] == k && runs(c) != holder_runs) cls[c] = (int)hold.size();
+      copies.push_back(hold[k]);
+      copies.push_back(nh);
+      hold.push_back(nh);
+    }
+    // every class now runs sl or skips it as a whole: the rows of the running classes' holders
+    std::vector<int> hs;
+    for (int hc : hold)
+      if (runs(hc)) hs.push_back(hc);
+    std::sort(hs.begin(), hs.end());
+    map_off[sl] = maps.size();
+    for (int hc : hs)
+      for (int i = 0; i < gamma; ++i) maps.push_back(hc * gamma + i);
+    counts[sl] = (int)(maps.size() - map_off[sl]);
   }
+  // before the logits every candidate takes its class's rows
+  copy_off[2 * L] = copies.size();
+  for (int c = 0; c < n_masks; ++c)
+    if (hold[cls[c]] != c) {
+      copies.push_back(hold[cls[c]]);
+      copies.push_back(c);
+    }
+  copy_off[2 * L + 1] = copies.size();
+  const size_t n_maps = maps.size();
+  maps.insert(maps.end(), copies.begin(), copies.end());
   hipError_t e = hipMemcpyAsync(w.rowmaps, maps.data(), sizeof(int) * maps.size(), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return fail(SSD_ERR_HIP, "rowmap upload");
+  const int* dev_copies = w.rowmaps + n_maps;
+  auto copy_rows = [&](int i) {
+    return launch_copy_candidate_rows(w.h, d.d_model, dev_copies + copy_off[i],
+                                      (int)(copy_off[i + 1] - copy_off[i]) / 2, gamma, s);
+  };
   TRY(launch_window_rows(window_dev, R, gamma, pos0, w.pos, w.tok, s));
-  TRY(launch_embed(d.dtype, d.embed, w.tok, d.vocab, w.h, d.d_model, R, d.d_model, nullptr, nullptr, s));
+  // the window's embedding in candidate 0's rows (the first class's holder); the others are copied
+  TRY(launch_embed(d.dtype, d.embed, w.tok, d.vocab, w.h, d.d_model, gamma, d.d_model, nullptr, nullptr, s));
   for (int l = 0; l < L; ++l) {
     for (int sub = 0; sub < 2; ++sub) {
       const int sl = 2 * l + sub;
+      TRY(copy_rows(sl));
       const int M = counts[sl];
       if (M == 0) continue;
       // compact row j is window row j % gamma: positions come from w.pos (filled for all R rows)
-      Block b{w.h, RowBlock{M, nullptr, w.pos, w.rowmaps + (size_t)sl * R, nullptr}, w.local_kv, pos0, gamma};
+      Block b{w.h, RowBlock{M, nullptr, w.pos, w.rowmaps + map_off[sl], nullptr}, w.local_kv, pos0, gamma};
       if (sub == 0) TRY(attn_sublayer(q, l, b, s));
       else TRY(mlp_sublayer(q, l, b, s));
     }
   }
+  TRY(copy_rows(2 * L));
   TRY(final_logits(q, w.h, R, nullptr, w.logits_rows, nullptr, s));
   TRY(launch_row_stats_seg(w.logits_rows, d.vocab, R, d.vocab, 0.f, 0, nullptr, 0, 0, PURPOSE_DRAFT, w.stats,
                            w.stat_recs, w.stat_ctr, nullptr, DraftStep{}, s));

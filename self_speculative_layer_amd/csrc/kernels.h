@@ -129,6 +129,8 @@ int launch_pick_commit(const ssd_row_stat* stat, DevState* st, int32_t* log, int
 int launch_state_init(DevState* st, hipStream_t s);
 int launch_fill_positions(int* pos, int M, int start, hipStream_t s);
 int launch_window_rows(const int32_t* window, int R, int gamma, int pos0, int* pos, int* tok, hipStream_t s);
+// h rows dst * gamma + i = rows src * gamma + i (i < gamma) for each of the n_pairs (src, dst) pairs.
+int launch_copy_candidate_rows(float* h, int D, const int* pairs, int n_pairs, int gamma, hipStream_t s);
 int launch_single_row_prep(DevState* st, int* pos1, int* tok1, int max_ctx, hipStream_t s);
 int launch_draft_begin(DevState* st, hipStream_t s);
 int launch_draft_step_prep(DevState* st, const int32_t* drafts, int j, int* pos1, int* tok1, int max_ctx,

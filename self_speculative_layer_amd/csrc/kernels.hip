@@ -1651,6 +1651,22 @@ int launch_window_rows(const int32_t* window, int R, int gamma, int pos0, int* p
   return last_launch();
 }
 
+// Residual rows of candidate pairs (src, dst): rows dst * gamma + i take rows src * gamma + i, i < gamma.
+// One block per copied row.
+__global__ __launch_bounds__(256) void copy_candidate_rows_kernel(float* __restrict__ h, int D,
+                                                                  const int* __restrict__ pairs, int gamma) {
+  const int p = blockIdx.x / gamma, i = blockIdx.x % gamma;
+  const float* src = h + ((size_t)pairs[2 * p] * gamma + i) * D;
+  float* dst = h + ((size_t)pairs[2 * p + 1] * gamma + i) * D;
+  for (int k = threadIdx.x; k < D; k += 256) dst[k] = src[k];
+}
+
+int launch_copy_candidate_rows(float* h, int D, const int* pairs, int n_pairs, int gamma, hipStream_t s) {
+  if (n_pairs <= 0) return 0;
+  hipLaunchKernelGGL(copy_candidate_rows_kernel, dim3(n_pairs * gamma), dim3(256), 0, s, h, D, pairs, gamma);
+  return last_launch();
+}
+
 // AR step: the newest token at position kvlen.
 __global__ void single_row_prep_kernel(DevState* st, int* pos1, int* tok1, int max_ctx) {
   if (threadIdx.x != 0) return;

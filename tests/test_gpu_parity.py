@@ -313,6 +313,48 @@ def test_score_masks_match_oracle():
     g.close()
 
 
+@pytest.mark.parametrize("shape", [BF16_HD64, BF16_HD128, F32_GQA], ids=lambda s: s.name)
+def test_score_masks_shared_prefixes_equal_alone(shape):
+    """Plans that agree on their first sub-layers share those sub-layers' rows in a
+    scoring pass (one launch per class of equal prefixes, copies where a class
+    splits).  A set with long shared prefixes, splits at the first and the last
+    sub-layer, a duplicate plan and the empty plan, scored together, gives every
+    plan the predictions and score it gets when scored alone, bit for bit."""
+    g = gpu_model(shape)
+    o = omodel.Model.synthetic(shape)
+    L = shape.n_layers
+    P, gamma = 40, 16
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    ref, _ = ossd.ar_generate(o, prompt, gamma)
+    window = (list(prompt) + ref)[P - 1: P + gamma]
+    z = np.zeros(2 * L, np.uint8)
+    def sk(*i):
+        m = z.copy()
+        m[list(i)] = 1
+        return m
+    masks = [sk(2 * L - 1), z.copy(), sk(0), sk(2 * L - 1), sk(1, 2 * L - 2), sk(1), sk(0, 3), sk(0, 2 * L - 1),
+             sk(*range(2 * L)), sk(2, 3), sk(2, 4)]
+    seq = B.Sequence(g, max_ctx=P + gamma + 64, max_rows=len(masks) * gamma, max_draft=4)
+    seq.generate_ar(dev(prompt), gamma)
+    def score(ms):
+        sc = torch.zeros(len(ms), dtype=torch.float32, device="cuda")
+        best = torch.zeros(1, dtype=torch.int32, device="cuda")
+        pred = torch.zeros(len(ms) * gamma, dtype=torch.int32, device="cuda")
+        B.ssd_score_masks(seq.handle, np.stack(ms), dev(window), P - 1, gamma, sc, best, pred)
+        torch.cuda.synchronize()
+        return sc.cpu().numpy(), pred.cpu().numpy().reshape(len(ms), gamma)
+    print("[gpu] %s: %d plans together" % (shape.name, len(masks)), flush=True)
+    gs, gp = score(masks)
+    for c, m in enumerate(masks):
+        s1, p1 = score([m])
+        assert s1[0] == gs[c] and np.array_equal(p1[0], gp[c]), c
+    assert gs[0] == gs[3] and np.array_equal(gp[0], gp[3])
+    assert B.ssd_read_state(seq.handle).error_flags == 0
+    print("scores %s" % gs)
+    seq.close()
+    g.close()
+
+
 @pytest.mark.parametrize("shape,P,gamma", [(BF16_HD64, 200, 12), (BF16_HD128, 150, 32), (BF16_HD64, 131, 32),
                                            (BF16_HD128, 257, 8)],
                          ids=["hd64-gqa-P200-g12", "hd128-P150-g32", "hd64-gqa-P131-g32", "hd128-P257-g8"])
