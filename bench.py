@@ -41,13 +41,14 @@ PMC_TRAFFIC = {
         parts=[dict(launches=104, fetch_kib=88261.6, write_kib=21.5),
                dict(launches=24, fetch_kib=90205.4, write_kib=279.5)],
         fetch_scale=2.0, write_scale=1.0, profile="profiles/dec_7b_hbm_counters.md"),
-    # 13B scoring gate/up: per step 23 launches of 256 rows, 15 of 384 and 2 of 128 (the same masks
-    # every step)
+    # 13B scoring gate/up, every launch of a step (the same masks every step): 23 of 129-256 rows, 12 of
+    # 257-384 and 3 of 96-128 (128 x 128 tiles), 2 of at most 64 (64 x 64 tiles)
     ("gemm_bf16_tiled<EPI_SWIGLU, 4, 4>", "score13b"): dict(
-        source="self_speculative_layer_amd/csrc/kernels.hip", sha1_prefix="7b01a014b998",
-        parts=[dict(launches=23, fetch_kib=166564.3, write_kib=5409.6),
-               dict(launches=15, fetch_kib=213456.2, write_kib=8410.6),
-               dict(launches=2, fetch_kib=142826.9, write_kib=3024.0)],
+        source="self_speculative_layer_amd/csrc/kernels.hip", sha1_prefix="20b4129517c5",
+        parts=[dict(launches=23, fetch_kib=165637.6, write_kib=5484.7),
+               dict(launches=12, fetch_kib=214621.0, write_kib=8425.1),
+               dict(launches=3, fetch_kib=142613.2, write_kib=2880.0),
+               dict(launches=2, fetch_kib=140602.3, write_kib=1300.4)],
         fetch_scale=2.0, write_scale=1.0, profile="profiles/gemm_tiled_score13b_kernel_trace.md"),
 }
 DOMINANT = "dec_gemm_kernel<DEC_SWIGLU>"
@@ -715,7 +716,8 @@ def run_scoring(args):
              "frac": round(gbps / HBM_PEAK_GBPS, 4)})
     traffic = pmc_traffic_bytes(SCORING_DOMINANT, args.workload)
     roof.update({"traffic": None if traffic is None else round(traffic),
-                 "kernel": SCORING_DOMINANT + " (gate/up + SwiGLU over the candidates' rows, 128 x 128 tiles)",
+                 "kernel": SCORING_DOMINANT + " (gate/up + SwiGLU over the candidates' rows: 128 x 128 tiles, 64 x 64 below "
+                           "96 rows)",
                  "launches": prof_n, "avg_launch_us": round(prof_ms / max(prof_n, 1) * 1e3, 3),
                  "flop_per_step": flops / K / per_call, "bytes_per_launch": round(prof_bytes / max(prof_n, 1)),
                  "measured": "dispatch-timestamp events on every launch of the kernel in %d further steps" % K})
