@@ -75,6 +75,10 @@ def test_workspace_limits():
         B.ssd_workspace_bytes(m, 0, 8, 512)
     with pytest.raises(B.SSDError):
         B.ssd_workspace_bytes(m, 64, 33, 512)
+    # up to 4096 rows (scoring passes); the split-key attention's partial buffer stays at 1024 rows
+    assert B.ssd_workspace_bytes(m, 4096, 8, 512) > B.ssd_workspace_bytes(m, 1024, 8, 512)
+    with pytest.raises(B.SSDError):
+        B.ssd_workspace_bytes(m, 4097, 8, 512)
     B.ssd_model_destroy(m)
 
 
