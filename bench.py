@@ -465,6 +465,13 @@ def main():
         "ar_tokens_per_s": None if ar_tps is None else round(ar_tps, 3),
         "prefill_ms": round(prefill_ms, 2),
         "wall_ms_timed": round(wall_ms, 2),
+        # what the pages report for trained models (context, not the target); under random weights the full
+        # model almost never repeats a draft, so SSD runs below AR here
+        "pages_context": {
+            "swift_speedup_over_ar": "1.3-1.6x, LLaMA-2 and CodeLLaMA (SWIFT digest, section 5.2 and Table 2)",
+            "layerskip_speedup_over_ar": "up to 2.16x (LayerSkip blog, title)",
+            "hardware": "not named in the pages' text",
+            "measured_ssd_over_ar": None if ar_tps is None else round(value / ar_tps, 4)},
     }
     seq.close()
     model.close()
