@@ -5,8 +5,9 @@ plan's sub-layers, shared final norm + LM head, confidence stop), one verify
 pass over the d'+1 rows, accept/reject, commit.  Inputs (weights, prompt, KV
 cache after the prefill) are resident in HBM before the timed region.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7b|tiny|13b|70b|score13b]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload 7b|tiny|13b|70b|tree7b|tree13b|score13b|swift13b|swiftotf13b|exit7b]
+                    [--search-steps-per-pass N] [--no-cpu-baseline]
 
 Prints one JSON line.  value = committed tokens per second over the K timed
 steps (nothing else queued).  roofline = the dominant kernel (the decode-block
