@@ -106,3 +106,26 @@ def test_destroyed_handles_are_rejected():
     with pytest.raises(B.SSDError) as e:
         B.ssd_model_destroy(m)
     assert e.value.code == B.SSD_ERR_ARG and "live model" in str(e.value)
+
+
+def test_scoring_beyond_1024_rows_needs_the_group_attention():
+    """A scoring pass of more than 1024 rows runs only where the candidate-group attention takes it (bf16,
+    head_dim 64 or 128): on an fp32 model the call is refused on the host, before any device work, and a
+    pass within 1024 rows still runs."""
+    shape = F32_GQA
+    g = gpu_model(shape)
+    L, gamma = shape.n_layers, 32
+    seq = B.Sequence(g, max_ctx=128, max_rows=2048, max_draft=4)
+    seq.generate_ar(dev(synth.prompt_tokens(40, shape.vocab)), gamma)
+    window = dev(np.arange(gamma + 1, dtype=np.int32) % shape.vocab)
+    masks = np.zeros((33, 2 * L), np.uint8)                 # 33 x 32 = 1056 rows
+    scores = torch.zeros(33, dtype=torch.float32, device="cuda")
+    best = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(B.SSDError) as e:
+        B.ssd_score_masks(seq.handle, masks, window, 39, gamma, scores, best)
+    assert e.value.code == B.SSD_ERR_UNSUPPORTED
+    B.ssd_score_masks(seq.handle, masks[:32], window, 39, gamma, scores, best)
+    torch.cuda.synchronize()
+    assert np.all(scores[:32].cpu().numpy() == scores[0].item())   # equal plans score alike
+    seq.close()
+    g.close()
