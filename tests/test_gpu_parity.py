@@ -443,6 +443,33 @@ def test_decode_step_equals_prefill_row(shape):
     g.close()
 
 
+@pytest.mark.parametrize("shape", [BF16_HD64, F32_GQA], ids=lambda s: s.name)
+def test_prefill_chunkings_agree(shape):
+    """A 1100-token prompt prefilled in chunks of 64 rows, of 1024 + 76 rows (a
+    sequence of 4096 rows takes at most 1024 per prefill chunk, the split-key
+    attention's capacity) and of 700 + 400 rows gives the same last-row logits
+    and the same next AR step, bit for bit: a row's result does not depend on
+    the rows it is processed with."""
+    g = gpu_model(shape)
+    P = 1100
+    prompt = synth.prompt_tokens(P, shape.vocab)
+    out = []
+    for max_rows in (64, 4096, 700):
+        print("[gpu] %s: prefill of %d tokens, max_rows %d" % (shape.name, P, max_rows), flush=True)
+        seq = B.Sequence(g, max_ctx=P + 64, max_rows=max_rows, max_draft=4)
+        lp = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
+        la = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
+        B.ssd_prefill(seq.handle, dev(prompt), 0.0, 0, lp)
+        B.ssd_decode_ar(seq.handle, 0.0, 0, la)
+        torch.cuda.synchronize()
+        assert B.ssd_read_state(seq.handle).error_flags == 0
+        out.append((lp.clone(), la.clone(), B.ssd_read_output(seq.handle, 2)))
+        seq.close()
+    for lp, la, toks in out[1:]:
+        assert torch.equal(lp, out[0][0]) and torch.equal(la, out[0][1]) and list(toks) == list(out[0][2])
+    g.close()
+
+
 @pytest.mark.parametrize("N,K", [(16, 32), (1000, 256), (2003, 512), (48, 4096)])
 def test_pack_bf16_layout(N, K):
     """ssd_pack_bf16 (device kernel) against the layout definition (element (n, k) at
