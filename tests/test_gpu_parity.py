@@ -499,19 +499,22 @@ def test_pack_bf16_rejects_bad_k():
     assert e.value.code == B.SSD_ERR_SHAPE
 
 
-@pytest.mark.parametrize("shape", [BF16_HD64, BF16_HD128], ids=lambda s: s.name)
-def test_long_context_attention_paths_agree(shape):
-    """A 2100-token context (33 active 64-key splits): the decode attention with
-    the merge folded in (KV pages for 2240 positions: 35 splits) and the general
-    partial + combine kernels (pages for 4224 positions: 66 splits) give the same
-    draft and verify logits, bit for bit; the AR step's logits match the oracle."""
+@pytest.mark.parametrize("shape,P,ctxs", [(BF16_HD64, 2100, (2240, 4224, 8320)), (BF16_HD128, 2100, (2240, 8320)),
+                                          (BF16_HD64, 4200, (4352, 8320)), (BF16_HD128, 4200, (4352, 8320))],
+                         ids=["hd64-gqa-P2100", "hd128-P2100", "hd64-gqa-P4200", "hd128-P4200"])
+def test_long_context_attention_paths_agree(shape, P, ctxs):
+    """Contexts of 2100 and 4200 tokens (33 and 66 active 64-key splits): the
+    decode attention with the merge folded in (KV pages for 2240 positions: 35
+    splits; it holds up to 64) and the general partial + combine kernels (pages
+    for 4224, 4352 and 8320 positions: 66, 68 and 130 splits) give the same draft
+    and verify logits, bit for bit; the AR step's logits match the oracle."""
     g = gpu_model(shape)
     o = omodel.Model.synthetic(shape)
-    P, d = 2100, 4
+    d = 4
     prompt = synth.prompt_tokens(P, shape.vocab)
     plan = PLANS[shape.name]
     runs = []
-    for max_ctx in (2240, 4224):
+    for max_ctx in ctxs:
         print("[gpu] %s: max_ctx %d" % (shape.name, max_ctx), flush=True)
         seq = B.Sequence(g, max_ctx=max_ctx, max_rows=64, max_draft=d)
         B.ssd_prefill(seq.handle, dev(prompt))
@@ -522,9 +525,10 @@ def test_long_context_attention_paths_agree(shape):
         assert st.error_flags == 0
         runs.append((lg.clone(), seq.draft_logits.clone(), seq.verify_logits.clone(), st.last_n_drafted))
         seq.close()
-    (a0, a1, a2, n0), (b0, b1, b2, n1) = runs
-    assert n0 == n1
-    assert torch.equal(a0, b0) and torch.equal(a1, b1) and torch.equal(a2, b2)
+    a0, a1, a2, n0 = runs[0]
+    for b0, b1, b2, n1 in runs[1:]:
+        assert n0 == n1
+        assert torch.equal(a0, b0) and torch.equal(a1, b1) and torch.equal(a2, b2)
     _, ref_z = oracle_ar_with_logits(o, prompt, 2)
     err = np.abs(a0.cpu().numpy() - ref_z[1]).max()
     print("AR step at position %d: max |dz| = %.3g" % (P, err))
