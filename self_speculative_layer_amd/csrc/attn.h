@@ -138,7 +138,7 @@ __device__ __forceinline__ void attn_tile_bf16(SM& sm, const bf16_t* __restrict_
   for (int i = 0; i < 4; ++i) {
     const int kp = key_beg + 16 * wave + 4 * g4 + i;
     const bool valid = kp < key_end && kp <= prow;
-    sc[i] = valid ? __fmul_rn(acc[i], scale) : -INFINITY;
+    sc[i] = valid ? fmul_nc(acc[i], scale) : -INFINITY;
     mx = fmaxf(mx, sc[i]);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -149,7 +149,7 @@ __device__ __forceinline__ void attn_tile_bf16(SM& sm, const bf16_t* __restrict_
   float ps = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float pe = sc[i] == -INFINITY ? 0.f : expf(__fsub_rn(sc[i], mx));
+    const float pe = sc[i] == -INFINITY ? 0.f : expf(fsub_nc(sc[i], mx));
     sm.P[(16 * wave + 4 * g4 + i) * ATTB_MAXQ + ql] = pe;
     ps += pe;
   }
@@ -440,10 +440,10 @@ __device__ void attn_item_scalar(AttnSmem<T, HD, NW>& sm, const T* __restrict__ 
 #pragma unroll 16
           for (int d = 0; d < HD; ++d) acc = fmaf(ld(qr + d), ld(kr + d), acc);
         }
-        sc = __fmul_rn(acc, scale);
+        sc = fmul_nc(acc, scale);
       }
       const float mx = wave_max(sc);
-      const float pexp = valid ? expf(__fsub_rn(sc, mx)) : 0.f;
+      const float pexp = valid ? expf(fsub_nc(sc, mx)) : 0.f;
       const float psum = wave_sum(pexp);
       sm.Pw[wave][lane] = pexp;
       __builtin_amdgcn_wave_barrier();
@@ -528,7 +528,7 @@ __device__ __forceinline__ float attn_combine_value(const float* __restrict__ pa
 #pragma unroll
     for (int s = 0; s < B; ++s) {
       if (s < ns) {
-        const float w = expf(__fsub_rn(mv[s], m));
+        const float w = expf(fsub_nc(mv[s], m));
         l = fmaf(lv[s], w, l);
         o = fmaf(ov[s], w, o);
       }
@@ -541,7 +541,7 @@ __device__ __forceinline__ float attn_combine_value(const float* __restrict__ pa
   float l = 0.f, o = 0.f;
 #pragma unroll 16
   for (int s = 0; s < ns; ++s) {
-    const float w = expf(__fsub_rn(pr[s * att_rec(HD) + HD], m));
+    const float w = expf(fsub_nc(pr[s * att_rec(HD) + HD], m));
     l = fmaf(pr[s * att_rec(HD) + HD + 1], w, l);
     o = fmaf(pr[s * att_rec(HD) + d], w, o);
   }
@@ -598,7 +598,7 @@ __device__ __forceinline__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, c
       for (int d = lane; d < HD; d += 64) acc = fmaf(bf2f(qr[d]), bf2f(kr[d]), acc);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      if (lane == 0) Wt[qq * ATT_MAXW + nsplits(qq)] = __fmul_rn(acc, scale);
+      if (lane == 0) Wt[qq * ATT_MAXW + nsplits(qq)] = fmul_nc(acc, scale);
     }
     __syncthreads();
   }
@@ -646,7 +646,7 @@ __device__ __forceinline__ void attn_merge_block(AttnSmem<bf16_t, HD, NW>& sm, c
   for (int r = 0; r < MLR; ++r) {
     const int c = j + 16 * r;
     if (c < nt) {
-      Wt[qq * ATT_MAXW + c] = expf(__fsub_rn(ml[r].x, m));
+      Wt[qq * ATT_MAXW + c] = expf(fsub_nc(ml[r].x, m));
       Lv[qq * ATT_MAXW + c] = ml[r].y;
     }
   }

@@ -137,13 +137,31 @@ namespace ssd {
 // kernel that needs a row's RMS uses these functions, so the result is the
 // same bits whichever kernel produced or consumes it.
 
+// Single-rounding float operations the compiler never fuses with a
+// neighbouring operation.  The toolchain's __fmul_rn / __fadd_rn are plain
+// operators that may still be contracted into a fused multiply-add, and the
+// compiler chooses which product to fuse kernel by kernel; steps that several
+// kernels must perform with the same bits use these instead.
+__device__ __forceinline__ float fmul_nc(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ __forceinline__ float fadd_nc(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+__device__ __forceinline__ float fsub_nc(float a, float b) {
+#pragma clang fp contract(off)
+  return a - b;
+}
+
 // (1) with the 16 values held by 16 consecutive lanes; every lane gets the sum.
 __device__ __forceinline__ float tile16_ss_lanes(float v) {
-  float s = __fmul_rn(v, v);
-  s += __shfl_xor(s, 8, 16);
-  s += __shfl_xor(s, 4, 16);
-  s += __shfl_xor(s, 2, 16);
-  s += __shfl_xor(s, 1, 16);
+  float s = fmul_nc(v, v);
+  s = fadd_nc(s, __shfl_xor(s, 8, 16));
+  s = fadd_nc(s, __shfl_xor(s, 4, 16));
+  s = fadd_nc(s, __shfl_xor(s, 2, 16));
+  s = fadd_nc(s, __shfl_xor(s, 1, 16));
   return s;
 }
 
@@ -158,17 +176,17 @@ __device__ __forceinline__ float row_ss_total(const float* tiles, int stride, in
 }
 
 __device__ __forceinline__ float inv_rms(float ss_total, int D, float eps) {
-  return __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(ss_total, (float)D), eps)));
+  return __fdiv_rn(1.0f, __fsqrt_rn(fadd_nc(__fdiv_rn(ss_total, (float)D), eps)));
 }
 
-// Elementwise steps shared by every kernel that performs them, with explicit
-// round-to-nearest operations so that no kernel contracts them differently.
+// Elementwise steps shared by every kernel that performs them, each written
+// with the operations above so that every kernel rounds them the same way.
 // Rotation of the pair (x1, x2) by the angle whose (cos, sin) is cs.  The
 // table of (cos, sin)(pos * theta^(-2i/hd)) is formed in fp64 and rounded to
 // fp32 when a sequence is created.
 __device__ __forceinline__ void rope_apply(float x1, float x2, float2 cs, float& y1, float& y2) {
-  y1 = __fsub_rn(__fmul_rn(x1, cs.x), __fmul_rn(x2, cs.y));
-  y2 = __fadd_rn(__fmul_rn(x2, cs.x), __fmul_rn(x1, cs.y));
+  y1 = fsub_nc(fmul_nc(x1, cs.x), fmul_nc(x2, cs.y));
+  y2 = fadd_nc(fmul_nc(x2, cs.x), fmul_nc(x1, cs.y));
 }
 
 // Packed bf16 projection weights: element (n, k) of an [N, K] matrix, in
@@ -202,7 +220,7 @@ __device__ __forceinline__ size_t dec_actf_index(int row, int col) {
 // rounded once.  Every kernel that forms such an input uses these functions.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t norm_pack2(float hg0, float hg1, float inv) {
-  const bf16x2_t v = {(__bf16)__fmul_rn(hg0, inv), (__bf16)__fmul_rn(hg1, inv)};
+  const bf16x2_t v = {(__bf16)fmul_nc(hg0, inv), (__bf16)fmul_nc(hg1, inv)};
   return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ bf16_t norm_bf16(float hg, float inv) {
@@ -210,7 +228,7 @@ __device__ __forceinline__ bf16_t norm_bf16(float hg, float inv) {
 }
 
 __device__ __forceinline__ float swiglu(float g, float u) {
-  return __fmul_rn(__fdiv_rn(g, __fadd_rn(1.0f, expf(-g))), u);
+  return fmul_nc(__fdiv_rn(g, fadd_nc(1.0f, expf(-g))), u);
 }
 
 }  // namespace ssd

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < DEC_SSP; ++j)   // tiles past the row end add an exact 0 (keeps every load unconditional)
-        acc += __fmul_rn(ssv[i][j], lane + 64 * j < nts ? 1.f : 0.f);
+        acc += fmul_nc(ssv[i][j], lane + 64 * j < nts ? 1.f : 0.f);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, WAVE);
       if (row < Ma && lane == 0) sinv[row] = inv_rms(acc, K, a.eps);
@@ -333,11 +333,11 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(const DecGemm a) {
       if (t.f0 + nn < a.N) a.Y[(size_t)row * a.ldy + t.f0 + nn] = s;
     } else if constexpr (EPI == DEC_RESID) {
       const int col = t.f0 + nn;
-      const float hn = __fadd_rn(eh[j], s);
+      const float hn = fadd_nc(eh[j], s);
       a.Y[(size_t)row * a.ldy + col] = hn;
       if (a.y_copy) a.y_copy[(size_t)row * a.ldy + col] = hn;
       if (a.gain_next) {
-        a.xg_next[a.M == 1 ? col : dec_actf_index(row, col)] = __fmul_rn(hn, eg[j]);   // one-row blocks: row-major
+        a.xg_next[a.M == 1 ? col : dec_actf_index(row, col)] = fmul_nc(hn, eg[j]);   // one-row blocks: row-major
         const float tt = tile16_ss_lanes(hn);
         if (nn == 0) a.ss_next[(size_t)row * (a.N / 16) + col / 16] = tt;
       }
@@ -388,11 +388,37 @@ static int dec_tiles(int epi, int N) {
   return (N + 15) / 16;
 }
 
-// Tiles per workgroup: one (most workgroups in flight), except for the LM head
-// with several rows: its 2000 tiles keep the chip busy at two per workgroup,
-// and each activation load then feeds twice the weights.
-static int dec_tpw(int epi, int M) {
-  return epi == DEC_STORE && M > 1 ? 2 : 1;
+// Compute units of the current device (cached per device).
+static int dec_device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
+// Tiles per workgroup.  One-row blocks: one (most workgroups in flight; the
+// row's activation loads are one line per step and cost next to nothing).
+// Blocks of several rows fetch a 16-row fp32 activation step (2 KB) for every
+// 1 KB weight step, so the normalised-input projections (QKV, gate/up) let each
+// activation load feed 3 or 4 tiles when that still leaves at most one
+// workgroup per compute unit (7B at 13 rows: QKV 768 tiles -> 256 workgroups,
+// 28.2 -> 23.6 us; gate/up 688 -> 230, 37.5 -> 36.2 us); with more tiles than
+// four per unit (70B gate/up) the grid stays one tile per workgroup.  The LM
+// head with several rows takes two tiles per workgroup (its 2000 tiles keep
+// the chip busy).
+static int dec_tpw(int epi, int M, int n_tiles) {
+  if (M <= 1) return 1;
+  if (epi == DEC_STORE) return 2;
+  if (epi == DEC_QKV || epi == DEC_SWIGLU) {
+    const int ncu = dec_device_cus();
+    const int t = (n_tiles + ncu - 1) / ncu;
+    if (t == 3 || t == 4) return t;
+  }
+  return 1;
 }
 
 // e0, e1: events taking the dispatch's begin and end timestamps (profiling), or null.
@@ -405,6 +431,17 @@ static void dec_launch(const DecGemm& a, int tpw, hipEvent_t e0, hipEvent_t e1, 
   else if (tpw == 2)
     hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 2, DEVROWS, false>), dim3((a.n_tiles + 1) / 2), block,
                           0, s, e0, e1, 0, a);
+  else if (EPI != DEC_QKV && EPI != DEC_SWIGLU)
+    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 1, DEVROWS, false>), dim3(a.n_tiles), block, 0, s, e0,
+                          e1, 0, a);
+  else if (tpw == 3)
+    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, (EPI == DEC_QKV || EPI == DEC_SWIGLU) ? 3 : 1, DEVROWS,
+                                           false>),
+                          dim3((a.n_tiles + 2) / 3), block, 0, s, e0, e1, 0, a);
+  else if (tpw == 4)
+    hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, (EPI == DEC_QKV || EPI == DEC_SWIGLU) ? 4 : 1, DEVROWS,
+                                           false>),
+                          dim3((a.n_tiles + 3) / 4), block, 0, s, e0, e1, 0, a);
   else
     hipExtLaunchKernelGGL((dec_gemm_kernel<EPI, DEC_NW, HALF, 1, DEVROWS, false>), dim3(a.n_tiles), block, 0, s, e0,
                           e1, 0, a);
@@ -425,7 +462,7 @@ int launch_dec_gemm(int epi, const DecGemm& a, hipStream_t s) {
   if (epi == DEC_SWIGLU && a.N % (DEC_HALF_SWIGLU ? 8 : 16) != 0) return SSD_ERR_SHAPE;
   DecGemm b = a;
   b.n_tiles = dec_tiles(epi, a.N);
-  const int tpw = dec_tpw(epi, a.M);
+  const int tpw = dec_tpw(epi, a.M, b.n_tiles);
   // profile classes: 0 plain-store projections (QKV, LM head), 1 residual, 2 gate/up
   const int cls = epi == DEC_RESID ? 1 : (epi == DEC_SWIGLU ? 2 : 0);
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -557,7 +594,7 @@ __device__ __forceinline__ void dec_entry_row(const bf16_t* __restrict__ e, cons
       if (NORM) {
         const float t = tile16_ss_lanes(v[j]);
         if (i < D) {
-          xg[row1 ? i : dec_actf_index(dr, i)] = __fmul_rn(v[j], gv[j]);   // one-row blocks: row-major
+          xg[row1 ? i : dec_actf_index(dr, i)] = fmul_nc(v[j], gv[j]);   // one-row blocks: row-major
           if ((threadIdx.x & 15) == 0) ss[(size_t)dr * (D / 16) + i / 16] = t;
         }
       }

@@ -111,10 +111,10 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_rows16(
         s += red[0][w][nn][mm];
         if (EPI == EPI_SWIGLU) s2 += red[NT - 1][w][nn][mm];
       }
-      if (rscale && EPI != EPI_RESID) { s = __fmul_rn(s, rscale[row]); s2 = __fmul_rn(s2, rscale[row]); }
+      if (rscale && EPI != EPI_RESID) { s = fmul_nc(s, rscale[row]); s2 = fmul_nc(s2, rscale[row]); }
       const int yrow = ymap ? ymap[row] : row;
       if (EPI == EPI_STORE) Y[(size_t)yrow * ldy + col] = s;
-      else if (EPI == EPI_RESID) Y[(size_t)yrow * ldy + col] = __fadd_rn(Y[(size_t)yrow * ldy + col], s);
+      else if (EPI == EPI_RESID) Y[(size_t)yrow * ldy + col] = fadd_nc(Y[(size_t)yrow * ldy + col], s);
       else A[(size_t)row * lda + col] = f2bf(swiglu(s, s2));
     }
   }
@@ -163,10 +163,10 @@ __global__ __launch_bounds__(256) void gemm_f32_rows16(
         float s2 = (EPI == EPI_SWIGLU) ? wave_sum(acc2[i]) : 0.f;
         if (lane == 0) {
           const int row = m0 + i;
-          if (rscale && EPI != EPI_RESID) { s = __fmul_rn(s, rscale[row]); s2 = __fmul_rn(s2, rscale[row]); }
+          if (rscale && EPI != EPI_RESID) { s = fmul_nc(s, rscale[row]); s2 = fmul_nc(s2, rscale[row]); }
           const int yrow = ymap ? ymap[row] : row;
           if (EPI == EPI_STORE) Y[(size_t)yrow * ldy + col] = s;
-          else if (EPI == EPI_RESID) Y[(size_t)yrow * ldy + col] = __fadd_rn(Y[(size_t)yrow * ldy + col], s);
+          else if (EPI == EPI_RESID) Y[(size_t)yrow * ldy + col] = fadd_nc(Y[(size_t)yrow * ldy + col], s);
           else A[(size_t)row * lda + col] = swiglu(s, s2);
         }
       }
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
         for (int e = 0; e < 4; ++e) {
           const int col = 16 * WI * nb + 16 * (H * wn + i) + 4 * g + e;
           float s1 = sum[i][j][e], s2 = sum[i + H][j][e];
-          if (rscale) { s1 = __fmul_rn(s1, rs); s2 = __fmul_rn(s2, rs); }
+          if (rscale) { s1 = fmul_nc(s1, rs); s2 = fmul_nc(s2, rs); }
           A[(size_t)row * lda + col] = f2bf(swiglu(s1, s2));
         }
     } else {
@@ -381,10 +381,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_tiled(
           if (col >= N) continue;
           float v = sum[i][j][e];
           if (EPI == EPI_STORE) {
-            if (rscale) v = __fmul_rn(v, rs);
+            if (rscale) v = fmul_nc(v, rs);
             Y[(size_t)yrow * ldy + col] = v;
           } else {
-            Y[(size_t)yrow * ldy + col] = __fadd_rn(Y[(size_t)yrow * ldy + col], v);
+            Y[(size_t)yrow * ldy + col] = fadd_nc(Y[(size_t)yrow * ldy + col], v);
           }
         }
     }
@@ -409,10 +409,10 @@ __global__ __launch_bounds__(256) void tg_quarter_reduce_kernel(const float* __r
     for (int q = 0; q < 4; ++q) v += part[q * MN + e];
     const int yrow = ymap ? ymap[row] : row;
     if (EPI == EPI_STORE) {
-      if (rscale) v = __fmul_rn(v, rscale[row]);
+      if (rscale) v = fmul_nc(v, rscale[row]);
       Y[(size_t)yrow * ldy + col] = v;
     } else {
-      Y[(size_t)yrow * ldy + col] = __fadd_rn(Y[(size_t)yrow * ldy + col], v);
+      Y[(size_t)yrow * ldy + col] = fadd_nc(Y[(size_t)yrow * ldy + col], v);
     }
   }
 }
@@ -594,9 +594,9 @@ __global__ __launch_bounds__(1024) void rowprep_kernel(const float* __restrict__
     const int i = j * 1024 + threadIdx.x;
     if (j * 1024 >= D) break;
     if (i < D) {
-      const float hg = __fmul_rn(v[j], gv[j]);
+      const float hg = fmul_nc(v[j], gv[j]);
       if constexpr (sizeof(T) == 2) xr[i] = norm_bf16(hg, iv);
-      else xr[i] = __fmul_rn(hg, iv);
+      else xr[i] = fmul_nc(hg, iv);
     }
   }
 }
@@ -1860,8 +1860,8 @@ __global__ __launch_bounds__(256) void specee_features_kernel(const float* __res
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float hg = __fmul_rn(hr[i + e], gain[i + e]);
-      x[e] = BF ? bf2f(norm_bf16(hg, inv)) : __fmul_rn(hg, inv);
+      const float hg = fmul_nc(hr[i + e], gain[i + e]);
+      x[e] = BF ? bf2f(norm_bf16(hg, inv)) : fmul_nc(hg, inv);
     }
 #pragma unroll
     for (int j = 0; j < KM; ++j) {

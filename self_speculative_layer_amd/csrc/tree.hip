@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void tree_topk_kernel(const float* __restrict_
   const float m = topv[0];
   const float Tn = T > 0.f ? T : 1.f;
   float se = 0.f;
-  for (int v = tid; v < V; v += 256) se += expf(__fdiv_rn(__fsub_rn(zr[v], m), Tn));
+  for (int v = tid; v < V; v += 256) se += expf(__fdiv_rn(fsub_nc(zr[v], m), Tn));
   se = wave_sum(se);
   if (lane == 0) wsum[wave] = se;
   __syncthreads();
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void tree_topk_kernel(const float* __restrict_
     float cum = 0.f;
     int k = k_max;
     for (int r = 0; r < k_max; ++r) {
-      cum += __fdiv_rn(expf(__fdiv_rn(__fsub_rn(topv[r], m), Tn)), tot);
+      cum += __fdiv_rn(expf(__fdiv_rn(fsub_nc(topv[r], m), Tn)), tot);
       if (cum >= rho) { k = r + 1; break; }
     }
     for (int r = 0; r < K; ++r) cand[(size_t)j * K + r] = r < k_max ? topi[r] : -1;
