@@ -38,18 +38,18 @@ HBM_PEAK_GBPS = 8000.0
 # and the per-launch figure is their mean weighted by that mix.
 PMC_TRAFFIC = {
     ("dec_gemm_kernel<DEC_SWIGLU>", "7b"): dict(
-        source="self_speculative_layer_amd/csrc/decode.hip", sha1_prefix="52aa25bb9f24",
-        parts=[dict(launches=104, fetch_kib=88261.6, write_kib=21.5),
-               dict(launches=24, fetch_kib=90205.4, write_kib=279.5)],
+        source="self_speculative_layer_amd/csrc/decode.hip", sha1_prefix="a643b1a908b3",
+        parts=[dict(launches=104, fetch_kib=88271.4, write_kib=21.5),
+               dict(launches=24, fetch_kib=89262.7, write_kib=279.5)],
         fetch_scale=2.0, write_scale=1.0, profile="profiles/dec_7b_hbm_counters.md"),
     # 13B scoring gate/up, every launch of a step (the same masks every step): 23 of 129-256 rows, 12 of
     # 257-384 and 3 of 96-128 (128 x 128 tiles), 2 of at most 64 (64 x 64 tiles)
     ("gemm_bf16_tiled<EPI_SWIGLU, 4, 4>", "score13b"): dict(
-        source="self_speculative_layer_amd/csrc/kernels.hip", sha1_prefix="20b4129517c5",
-        parts=[dict(launches=23, fetch_kib=165637.6, write_kib=5484.7),
-               dict(launches=12, fetch_kib=214621.0, write_kib=8425.1),
-               dict(launches=3, fetch_kib=142613.2, write_kib=2880.0),
-               dict(launches=2, fetch_kib=140602.3, write_kib=1300.4)],
+        source="self_speculative_layer_amd/csrc/kernels.hip", sha1_prefix="fa9187ef4828",
+        parts=[dict(launches=23, fetch_kib=165991.8, write_kib=5484.7),
+               dict(launches=12, fetch_kib=215410.4, write_kib=8425.0),
+               dict(launches=3, fetch_kib=142613.1, write_kib=2880.0),
+               dict(launches=2, fetch_kib=140571.9, write_kib=1301.0)],
         fetch_scale=2.0, write_scale=1.0, profile="profiles/gemm_tiled_score13b_kernel_trace.md"),
 }
 DOMINANT = "dec_gemm_kernel<DEC_SWIGLU>"
