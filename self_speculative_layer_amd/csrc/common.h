@@ -129,14 +129,6 @@ __device__ __forceinline__ float word_to_gumbel(uint32_t x) {
 
 namespace ssd {
 
-// ---------------------------------------------------------------------------
-// Canonical RMS reductions.  The residual stream's sum of squares is formed
-// as (1) per group of 16 consecutive features, a butterfly over 16 lanes
-// (xor 8, 4, 2, 1), then (2) over the groups: lane j of one wave adds groups
-// j, j + 64, j + 128, ... in order, then a butterfly over 64 lanes.  Every
-// kernel that needs a row's RMS uses these functions, so the result is the
-// same bits whichever kernel produced or consumes it.
-
 // Single-rounding float operations the compiler never fuses with a
 // neighbouring operation.  The toolchain's __fmul_rn / __fadd_rn are plain
 // operators that may still be contracted into a fused multiply-add, and the
@@ -154,6 +146,14 @@ __device__ __forceinline__ float fsub_nc(float a, float b) {
 #pragma clang fp contract(off)
   return a - b;
 }
+
+// ---------------------------------------------------------------------------
+// Canonical RMS reductions.  The residual stream's sum of squares is formed
+// as (1) per group of 16 consecutive features, a butterfly over 16 lanes
+// (xor 8, 4, 2, 1), then (2) over the groups: lane j of one wave adds groups
+// j, j + 64, j + 128, ... in order, then a butterfly over 64 lanes.  Every
+// kernel that needs a row's RMS uses these functions, so the result is the
+// same bits whichever kernel produced or consumes it.
 
 // (1) with the 16 values held by 16 consecutive lanes; every lane gets the sum.
 __device__ __forceinline__ float tile16_ss_lanes(float v) {
